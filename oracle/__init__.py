@@ -1,0 +1,229 @@
+"""CPU oracle for the symmetric W8A8 INT8 linear layer (test infrastructure).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never loads it and
+shares no code with it.  The arithmetic lives in ``qk_oracle.c`` (plain C
+loops, one step per statement); this module only marshals numpy arrays into
+it and offers the composite ``linear`` that chains the steps in the order the
+pages state them:
+
+  per-token quantization  -- "kernels: fused silu_and_mul + dynamic per-token
+                             FP8 quantization", Algorithm (absmax, guarded
+                             scale) with the symmetric [-127, 127] range of
+                             "Skill: Write an INT8 Quantized Kernel", Inputs.
+  INT8 GEMM, INT32 acc    -- "16. Deploying Custom Kernels", C++ Kernel
+                             Interface (GemmConfig), and "KV-cache kernels",
+                             02 Scales and dequantization.
+  dequant epilogue        -- the same two passages: acc * scale_a * scale_b.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qk_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16, F16 = 0, 1, 2
+B_KN, B_NK = 0, 1
+
+_CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+           "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile qk_oracle.c into liboracle.so with gcc (no GPU toolchain)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.or_widen.argtypes = [ctypes.c_int, I64, P, P]
+    lib.or_widen.restype = ctypes.c_int
+    lib.or_quant_rows.argtypes = [I64, I64, P, P, P]
+    lib.or_quant_rows.restype = None
+    lib.or_spec_expf.argtypes = [ctypes.c_float]
+    lib.or_spec_expf.restype = ctypes.c_float
+    lib.or_expf_array.argtypes = [I64, P, P]
+    lib.or_expf_array.restype = None
+    lib.or_spec_taylor.argtypes = [P]
+    lib.or_spec_reduction_constants.argtypes = [P]
+    lib.or_silu_mul.argtypes = [I64, I64, P, P]
+    lib.or_silu_mul.restype = None
+    lib.or_gemm_i32.argtypes = [I64, I64, I64, P, P, ctypes.c_int, P]
+    lib.or_gemm_i32.restype = I64
+    lib.or_gemm_entries.argtypes = [I64, P, P, I64, I64, P, P, ctypes.c_int, P]
+    lib.or_gemm_entries.restype = I64
+    lib.or_dequant.argtypes = [I64, I64, P, P, P, ctypes.c_float, P]
+    lib.or_dequant.restype = None
+    lib.or_bf16_nearest.argtypes = [I64, P, P]
+    lib.or_bf16_nearest.restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _contig(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# --------------------------------------------------------------------------
+# step wrappers
+# --------------------------------------------------------------------------
+
+def widen(bits: np.ndarray, dtype: int) -> np.ndarray:
+    """Widen fp32 / bf16 bits / fp16 bits to binary32 (exact)."""
+    lib = _load()
+    if dtype == F32:
+        src = _contig(bits, np.float32)
+    else:
+        src = _contig(bits.view(np.uint16) if bits.dtype != np.uint16 else bits, np.uint16)
+    out = np.empty(src.shape, dtype=np.float32)
+    rc = lib.or_widen(dtype, src.size, _ptr(src), _ptr(out))
+    if rc:
+        raise ValueError("unknown dtype")
+    return out
+
+
+def quant_per_token(x32: np.ndarray):
+    """x32: [m, k] float32 -> (codes int8 [m, k], scale float32 [m])."""
+    lib = _load()
+    x = _contig(x32, np.float32)
+    m, k = x.shape
+    q = np.empty((m, k), dtype=np.int8)
+    s = np.empty((m,), dtype=np.float32)
+    lib.or_quant_rows(m, k, _ptr(x), _ptr(q), _ptr(s))
+    return q, s
+
+
+def spec_expf(x: np.ndarray) -> np.ndarray:
+    lib = _load()
+    xs = _contig(x, np.float32)
+    y = np.empty_like(xs)
+    lib.or_expf_array(xs.size, _ptr(xs), _ptr(y))
+    return y
+
+
+def spec_taylor() -> np.ndarray:
+    out = np.empty(8, dtype=np.float32)
+    _load().or_spec_taylor(_ptr(out))
+    return out
+
+
+def spec_reduction_constants() -> np.ndarray:
+    out = np.empty(3, dtype=np.float32)
+    _load().or_spec_reduction_constants(_ptr(out))
+    return out
+
+
+def silu_mul(h32: np.ndarray) -> np.ndarray:
+    """h32: [m, 2d] float32 (gate | up) -> silu(gate) * up, float32 [m, d]."""
+    lib = _load()
+    h = _contig(h32, np.float32)
+    m, two_d = h.shape
+    if two_d % 2:
+        raise ValueError("last dimension of h must be even")
+    d = two_d // 2
+    out = np.empty((m, d), dtype=np.float32)
+    lib.or_silu_mul(m, d, _ptr(h), _ptr(out))
+    return out
+
+
+def gemm_i32(a: np.ndarray, b: np.ndarray, layout: int = B_KN) -> np.ndarray:
+    """Exact int32 accumulators of a [m,k] x b ([k,n] if B_KN, [n,k] if B_NK)."""
+    lib = _load()
+    a = _contig(a, np.int8)
+    b = _contig(b, np.int8)
+    m, k = a.shape
+    n = b.shape[1] if layout == B_KN else b.shape[0]
+    kb = b.shape[0] if layout == B_KN else b.shape[1]
+    if kb != k:
+        raise ValueError("inner dimensions differ")
+    c = np.empty((m, n), dtype=np.int32)
+    ovf = lib.or_gemm_i32(m, n, k, _ptr(a), _ptr(b), layout, _ptr(c))
+    if ovf:
+        raise OverflowError(f"{ovf} accumulators exceed int32")
+    return c
+
+
+def gemm_entries(a: np.ndarray, b: np.ndarray, rows, cols, layout: int = B_KN) -> np.ndarray:
+    """Exact int32 accumulators at the listed (row, col) pairs."""
+    lib = _load()
+    a = _contig(a, np.int8)
+    b = _contig(b, np.int8)
+    rows = _contig(rows, np.int64)
+    cols = _contig(cols, np.int64)
+    k = a.shape[1]
+    n = b.shape[1] if layout == B_KN else b.shape[0]
+    c = np.empty(rows.shape, dtype=np.int32)
+    ovf = lib.or_gemm_entries(rows.size, _ptr(rows), _ptr(cols), n, k, _ptr(a), _ptr(b),
+                              layout, _ptr(c))
+    if ovf:
+        raise OverflowError(f"{ovf} accumulators exceed int32")
+    return c
+
+
+def dequant(c: np.ndarray, scale_a: np.ndarray, scale_b: np.ndarray,
+            output_scale: float = 1.0) -> np.ndarray:
+    """acc * scale_a[row] * scale_b[col] * output_scale in float64."""
+    lib = _load()
+    c = _contig(c, np.int32)
+    sa = _contig(scale_a, np.float32)
+    sb = _contig(scale_b, np.float32)
+    m, n = c.shape
+    out = np.empty((m, n), dtype=np.float64)
+    lib.or_dequant(m, n, _ptr(c), _ptr(sa), _ptr(sb), float(output_scale), _ptr(out))
+    return out
+
+
+def bf16_nearest(v: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns nearest to the float64 values (ties to even)."""
+    lib = _load()
+    v = _contig(v, np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib.or_bf16_nearest(v.size, _ptr(v), _ptr(out))
+    return out
+
+
+# --------------------------------------------------------------------------
+# composites (the layer, step by step)
+# --------------------------------------------------------------------------
+
+def quantize_input(x_bits: np.ndarray, dtype: int):
+    """Widen then quantize per token: returns (codes, scales)."""
+    return quant_per_token(widen(x_bits, dtype))
+
+
+def silu_mul_quantize(h_bits: np.ndarray, dtype: int):
+    """silu(gate) * up, then per-token quantization: returns (codes, scales)."""
+    return quant_per_token(silu_mul(widen(h_bits, dtype)))
+
+
+def linear(x_bits: np.ndarray, dtype: int, w: np.ndarray, scale_b: np.ndarray,
+           layout: int = B_KN, output_scale: float = 1.0):
+    """Whole layer: returns (codes, scales, acc int32, out float64)."""
+    q, s = quantize_input(x_bits, dtype)
+    c = gemm_i32(q, w, layout)
+    return q, s, c, dequant(c, s, scale_b, output_scale)

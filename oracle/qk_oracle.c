@@ -1,0 +1,304 @@
+/*
+ * CPU oracle for the symmetric W8A8 INT8 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is loaded by the test suite, by the
+ * package smoke check and by the benchmark's CPU-baseline leg, and by nothing
+ * else.  It shares no code, header, table or constant with the GPU library;
+ * the two are written independently from the same source pages.
+ *
+ * It is deliberately plain: straight loops, one step per statement, in the
+ * order the pages state the method, so that a reader can check it by eye.
+ * OpenMP only splits independent rows across threads; no step is blocked,
+ * fused or reordered.
+ *
+ * Sources (cited by page title and section):
+ *   [GEMM-IF]  "16. Deploying Custom Kernels", C++ Kernel Interface -- the
+ *              problem statement: m, n, k, int8 A and B, int32 C, fp32
+ *              per-row scale_a, per-column scale_b, scalar output_scale.
+ *   [SKILL]    "Skill: Write an INT8 Quantized Kernel", Inputs the agent
+ *              should gather first -- symmetric range [-127, 127] with zero
+ *              point 0; INT32 accumulation is mandatory; per-token and
+ *              per-channel granularity; fp32 or fp16 output after dequant.
+ *   [DAY25]    "KV-cache kernels" (a quantization lesson), 02 Scales and
+ *              dequantization -- int8 dot products accumulate in int32 and
+ *              the result is multiplied by the activation and weight scales.
+ *   [PR]       "kernels: fused silu_and_mul + dynamic per-token FP8
+ *              quantization", Purpose and Algorithm -- one scale per token
+ *              from the row absmax, scale = max(absmax, 1e-12) / qmax, the
+ *              value quantized is silu(gate) * up.
+ *
+ * Precision.  Quantization and the SiLU gate run in IEEE binary32: their
+ * results decide integer codes, and the per-token scale is an fp32 value in
+ * the interface [GEMM-IF].  The integer product is exact (int64 accumulation,
+ * range-checked against int32).  The dequant epilogue is evaluated in
+ * binary64 as the reference value an fp32/bf16 result is compared against.
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *   - x / scale is a true IEEE binary32 division (not a reciprocal product),
+ *     rounded to an integer with round-half-to-even, then clamped to +-127.
+ *   - the 1e-12 guard is the binary32 value nearest 1e-12, applied to the
+ *     absmax before the division by 127.
+ *   - silu(g) = g / (1 + exp(-g)) with exp evaluated by the fixed binary32
+ *     algorithm spec_expf below (Cody-Waite reduction by ln 2, degree-7
+ *     Taylor polynomial in Horner form with fused multiply-adds, scaling by
+ *     2^n); every other step is one correctly rounded binary32 operation.
+ *   - gate is the first half of each row of H, up the second half.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -fPIC -shared
+ * (-ffp-contract=off: no multiply-add is fused unless written as fmaf).
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+#define OR_F16 2
+
+#define OR_B_KN 0 /* weight stored [k][n], n contiguous */
+#define OR_B_NK 1 /* weight stored [n][k], k contiguous */
+
+/* ------------------------------------------------------------------ */
+/* Step 0: widen the input element to binary32 (exact for all three).  */
+/* ------------------------------------------------------------------ */
+
+static float widen_bf16(uint16_t bits)
+{
+    /* bfloat16 is the upper half of a binary32 word. */
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static float widen_f16(uint16_t bits)
+{
+    /* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+    int sign = bits >> 15;
+    int e = (bits >> 10) & 31;
+    int f = bits & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24); /* subnormal: f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25); /* (1 + f/1024) * 2^(e-15) */
+    return (float)(sign ? -v : v);
+}
+
+int or_widen(int dtype, int64_t count, const void *src, float *dst)
+{
+    if (dtype == OR_F32) {
+        memcpy(dst, src, (size_t)count * sizeof(float));
+        return 0;
+    }
+    if (dtype != OR_BF16 && dtype != OR_F16)
+        return 1;
+    const uint16_t *s = (const uint16_t *)src;
+    for (int64_t i = 0; i < count; ++i)
+        dst[i] = dtype == OR_BF16 ? widen_bf16(s[i]) : widen_f16(s[i]);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Steps 1-3: dynamic per-token symmetric quantization [PR], [SKILL].   */
+/* ------------------------------------------------------------------ */
+
+/* x: [m][k] binary32, q: [m][k] int8, scale: [m] binary32. */
+void or_quant_rows(int64_t m, int64_t k, const float *x, int8_t *q, float *scale)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i) {
+        const float *row = x + i * k;
+
+        /* 1. row absmax (exact: max is order independent) */
+        float amax = 0.0f;
+        for (int64_t j = 0; j < k; ++j) {
+            float a = fabsf(row[j]);
+            if (a > amax)
+                amax = a;
+        }
+
+        /* 2. scale = max(absmax, 1e-12) / 127 */
+        float guarded = fmaxf(amax, 1e-12f);
+        float s = guarded / 127.0f;
+        scale[i] = s;
+
+        /* 3. code = clamp(rint(x / scale), -127, 127) */
+        for (int64_t j = 0; j < k; ++j) {
+            float ratio = row[j] / s;
+            float r = nearbyintf(ratio); /* default rounding mode: to nearest, ties to even */
+            if (r > 127.0f)
+                r = 127.0f;
+            if (r < -127.0f)
+                r = -127.0f;
+            q[i * k + j] = (int8_t)r;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Step 0': silu(gate) * up [PR], with the binary32 exp spec.           */
+/* ------------------------------------------------------------------ */
+
+/* Constants of spec_expf, each the binary32 value nearest the quantity named. */
+static const float SPEC_LOG2E = 0x1.715476p+0f;      /* 1 / ln 2 */
+static const float SPEC_LN2_HI = 0x1.62e400p-1f;     /* 0.693145751953125, ln 2 cut to 16 bits */
+static const float SPEC_LN2_LO = 0x1.7f7d1cp-20f;    /* ln 2 - SPEC_LN2_HI */
+static const float SPEC_TAYLOR[8] = {                /* 1 / j! for j = 0..7 */
+    0x1.000000p+0f, 0x1.000000p+0f, 0x1.000000p-1f,  0x1.555556p-3f,
+    0x1.555556p-5f, 0x1.111112p-7f, 0x1.6c16c2p-10f, 0x1.a01a02p-13f,
+};
+
+float or_spec_expf(float x)
+{
+    if (x > 88.0f)
+        return INFINITY;
+    if (x < -87.0f)
+        return 0.0f;
+    float n = nearbyintf(x * SPEC_LOG2E);  /* x = n ln2 + r */
+    float r = fmaf(-n, SPEC_LN2_HI, x);
+    r = fmaf(-n, SPEC_LN2_LO, r);
+    float p = SPEC_TAYLOR[7];              /* e^r by Horner's rule */
+    for (int j = 6; j >= 0; --j)
+        p = fmaf(p, r, SPEC_TAYLOR[j]);
+    return ldexpf(p, (int)n);              /* exact: the result is a normal number */
+}
+
+void or_spec_taylor(float *out8)
+{
+    for (int j = 0; j < 8; ++j)
+        out8[j] = SPEC_TAYLOR[j];
+}
+
+void or_spec_reduction_constants(float *out3)
+{
+    out3[0] = SPEC_LOG2E;
+    out3[1] = SPEC_LN2_HI;
+    out3[2] = SPEC_LN2_LO;
+}
+
+void or_expf_array(int64_t count, const float *x, float *y)
+{
+    for (int64_t i = 0; i < count; ++i)
+        y[i] = or_spec_expf(x[i]);
+}
+
+/* h: [m][2d] binary32 with gate = h[:, :d], up = h[:, d:]; out: [m][d]. */
+void or_silu_mul(int64_t m, int64_t d, const float *h, float *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t j = 0; j < d; ++j) {
+            float g = h[i * 2 * d + j];
+            float u = h[i * 2 * d + d + j];
+            float e = or_spec_expf(-g);
+            float t = 1.0f + e;
+            float sg = g / t; /* silu(g) = g / (1 + exp(-g)) */
+            out[i * d + j] = sg * u;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Step 4: INT8 x INT8 -> INT32 GEMM [GEMM-IF], [SKILL], [DAY25].       */
+/* ------------------------------------------------------------------ */
+
+static int8_t weight_at(const int8_t *b, int layout, int64_t n, int64_t k, int64_t kk, int64_t j)
+{
+    return layout == OR_B_KN ? b[kk * n + j] : b[j * k + kk];
+}
+
+/* Returns the number of accumulators that do not fit in int32 (0 = all fit). */
+int64_t or_gemm_i32(int64_t m, int64_t n, int64_t k, const int8_t *a, const int8_t *b,
+                    int layout, int32_t *c)
+{
+    int64_t overflow = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : overflow)
+    for (int64_t i = 0; i < m; ++i) {
+        int64_t *acc = (int64_t *)calloc((size_t)(n > 0 ? n : 1), sizeof(int64_t));
+        if (layout == OR_B_KN) {
+            for (int64_t kk = 0; kk < k; ++kk) {
+                int64_t av = a[i * k + kk];
+                for (int64_t j = 0; j < n; ++j)
+                    acc[j] += av * (int64_t)b[kk * n + j];
+            }
+        } else {
+            for (int64_t j = 0; j < n; ++j)
+                for (int64_t kk = 0; kk < k; ++kk)
+                    acc[j] += (int64_t)a[i * k + kk] * (int64_t)b[j * k + kk];
+        }
+        for (int64_t j = 0; j < n; ++j) {
+            if (acc[j] > INT32_MAX || acc[j] < INT32_MIN)
+                ++overflow;
+            c[i * n + j] = (int32_t)acc[j];
+        }
+        free(acc);
+    }
+    return overflow;
+}
+
+/* Accumulators for the listed (row, col) pairs only, one dot product each. */
+int64_t or_gemm_entries(int64_t count, const int64_t *rows, const int64_t *cols, int64_t n,
+                        int64_t k, const int8_t *a, const int8_t *b, int layout, int32_t *c)
+{
+    int64_t overflow = 0;
+#pragma omp parallel for schedule(static) reduction(+ : overflow)
+    for (int64_t e = 0; e < count; ++e) {
+        int64_t acc = 0;
+        for (int64_t kk = 0; kk < k; ++kk)
+            acc += (int64_t)a[rows[e] * k + kk] * (int64_t)weight_at(b, layout, n, k, kk, cols[e]);
+        if (acc > INT32_MAX || acc < INT32_MIN)
+            ++overflow;
+        c[e] = (int32_t)acc;
+    }
+    return overflow;
+}
+
+/* ------------------------------------------------------------------ */
+/* Step 5: dequant epilogue [GEMM-IF], [DAY25], in binary64.            */
+/* ------------------------------------------------------------------ */
+
+/* out[i][j] = acc[i][j] * scale_a[i] * scale_b[j] * output_scale */
+void or_dequant(int64_t m, int64_t n, const int32_t *c, const float *scale_a,
+                const float *scale_b, float output_scale, double *out)
+{
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            out[i * n + j] = (double)c[i * n + j] * (double)scale_a[i] * (double)scale_b[j] *
+                             (double)output_scale;
+}
+
+/* bfloat16 (8 significant bits, binary32 exponent range) nearest v, ties to even. */
+static uint16_t bf16_nearest(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v))
+        return 0x7fc0;
+    if (a == 0.0)
+        return sign;
+    if (isinf(v))
+        return sign | 0x7f80;
+    int e;
+    frexp(a, &e);             /* a = f * 2^e, 0.5 <= f < 1: leading bit is 2^(e-1) */
+    int lsb = (e - 1) - 7;    /* weight of the last of 8 significant bits */
+    if (lsb < -133)
+        lsb = -133;           /* subnormal spacing 2^-133 */
+    double r = ldexp(nearbyint(ldexp(a, -lsb)), lsb); /* exact scalings around one RNE */
+    if (r >= 0x1p128)
+        return sign | 0x7f80;
+    float f = (float)r;       /* exact: at most 8 significant bits, in range */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return sign | (uint16_t)(u >> 16);
+}
+
+void or_bf16_nearest(int64_t count, const double *v, uint16_t *out)
+{
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = bf16_nearest(v[i]);
+}
