@@ -1,0 +1,249 @@
+"""Benchmark of the W8A8 INT8 linear layer on one MI355X.
+
+Headline: INT8 TOPS of one step = per-token quantization + INT8 GEMM with the
+dequant epilogue on the prefill workload with outlier channels (X bf16
+[2048, 4096], W int8 [4096, 4096], bf16 out); ops = 2 M N K per step.  Also
+measured in the same run: HBM GB/s of the decode linear at M = 1 (X bf16
+[1, 4096], W int8 [4096, 14336]; bytes = W + s_ch + X + out per call).
+
+Inputs are seeded synthetic tensors resident in HBM before timing starts.
+Each step uses the next of R buffer sets (R x ~59 MB > the 256 MB Infinity
+Cache plus L2), so weights and activations come from HBM, not cache.
+
+Prints one JSON line (rank 0; one GPU only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0     # MI355X dense INT8 MFMA, published
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_prefill_outliers_traffic.txt")
+GEMM_SRC = os.path.join(ROOT, "w8a8_int8_quantized_qk_amd", "csrc", "gemm_mfma.hip")
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--ring", type=int, default=8, help="buffer sets cycled through")
+    p.add_argument("--decode-calls", type=int, default=400)
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target duration of the CPU oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain copy kernel of known size (for counter scaling)")
+    return p.parse_args()
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic_from_profile():
+    """HBM bytes per GEMM launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != _sha(GEMM_SRC):
+        return None
+    return float(t.group(1))
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+              f"--gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import w8a8_int8_quantized_qk_amd as qk
+    from w8a8_int8_quantized_qk_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = qk.library()
+
+    # ---------------- prefill: quant + GEMM (headline) ----------------
+    wcfg = wl.WORKLOADS["prefill_outliers"]
+    m, k, n = wcfg.m, wcfg.k, wcfg.n
+    sets = []
+    for r in range(args.ring):
+        d = wl.generate(wcfg, seed=r)
+        sets.append({
+            "x": d["x"].to(dev), "w": torch.from_numpy(d["w"]).to(dev),
+            "s_ch": torch.from_numpy(d["s_ch"]).to(dev),
+            "q": torch.empty((m, k), dtype=torch.int8, device=dev),
+            "s": torch.empty((m,), dtype=torch.float32, device=dev),
+            "out": torch.empty((m, n), dtype=torch.bfloat16, device=dev),
+        })
+    stream = torch.cuda.current_stream(dev)
+
+    def step(bs, ev=None):
+        qk.quant_per_token(bs["x"], bs["q"], bs["s"])
+        if ev is not None:
+            ev[0].record(stream)
+        qk.gemm_i8_scaled(bs["q"], bs["w"], bs["s"], bs["s_ch"], out=bs["out"])
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % args.ring])
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % args.ring], events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    ms_per_step = wall * 1e3 / args.steps
+    ops = 2.0 * m * n * k
+    tops = ops / (ms_per_step * 1e-3) / 1e12
+    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
+    traffic = _traffic_from_profile()
+
+    result = {
+        "metric": "INT8 TOPS (quant+GEMM) at M=2048,K=N=4096; HBM GB/s at decode M=1",
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "prefill_outliers", "m": m, "k": k, "n": n, "x_dtype": "bf16",
+                   "w_layout": "[K,N]", "out_dtype": "bf16", "outlier_cols": wcfg.outlier_cols,
+                   "ring_sets": args.ring, "step": "qk_quant_per_token + qk_gemm_i8_scaled"},
+        "roofline": {"bound": "mfma", "kernel": "gemm_i8_mfma_kernel",
+                     "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                     "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+                     "traffic": traffic, "avg_launch_us": round(gemm_ms * 1e3, 3),
+                     "algorithmic_ops_per_launch": ops},
+        "step_frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+    }
+
+    # ---------------- decode: M = 1 linear (second metric) ----------------
+    if not args.no_decode:
+        dcfg = wl.WORKLOADS["decode_m1"]
+        dm, dk, dn = dcfg.m, dcfg.k, dcfg.n
+        dsets = []
+        for r in range(args.ring):
+            d = wl.generate(dcfg, seed=r)
+            dsets.append({
+                "x": d["x"].to(dev), "w": torch.from_numpy(d["w"]).to(dev),
+                "s_ch": torch.from_numpy(d["s_ch"]).to(dev),
+                "q": torch.empty((dm, dk), dtype=torch.int8, device=dev),
+                "s": torch.empty((dm,), dtype=torch.float32, device=dev),
+                "out": torch.empty((dm, dn), dtype=torch.bfloat16, device=dev),
+            })
+        ws = torch.zeros(qk.gemm_workspace_size(dm, dn, dk), dtype=torch.uint8, device=dev)
+
+        def dstep(bs, ev=None):
+            qk.quant_per_token(bs["x"], bs["q"], bs["s"])
+            if ev is not None:
+                ev[0].record(stream)
+            qk.gemm_i8_scaled(bs["q"], bs["w"], bs["s"], bs["s_ch"], out=bs["out"], workspace=ws)
+            if ev is not None:
+                ev[1].record(stream)
+
+        for i in range(args.warmup):
+            dstep(dsets[i % args.ring])
+        torch.cuda.synchronize()
+        dev_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(args.decode_calls)]
+        t0 = time.perf_counter()
+        for i in range(args.decode_calls):
+            dstep(dsets[i % args.ring], dev_events[i])
+        torch.cuda.synchronize()
+        dwall = time.perf_counter() - t0
+        gemv_ms = float(np.mean([a.elapsed_time(b) for a, b in dev_events]))
+        call_us = dwall * 1e6 / args.decode_calls
+        dbytes = dk * dn + 4 * dn + 2 * dm * dk + 2 * dm * dn
+        gemv_bytes = dk * dn + 4 * dn + dm * dk + 4 * dm + 2 * dm * dn
+        result["decode"] = {
+            "metric": "HBM GB/s at decode M=1 (quant + GEMV call)",
+            "workload": "decode_m1", "m": dm, "k": dk, "n": dn,
+            "value": round(dbytes / (call_us * 1e-6) / 1e9, 1), "unit": "GB/s",
+            "us_per_call": round(call_us, 3), "algorithmic_bytes_per_call": dbytes,
+            "frac_of_hbm_peak": round(dbytes / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "roofline": {"bound": "hbm", "kernel": "gemv_i8_splitk_kernel",
+                         "achieved": round(gemv_bytes / (gemv_ms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gemv_bytes / (gemv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "avg_launch_us": round(gemv_ms * 1e3, 3),
+                         "algorithmic_bytes_per_launch": gemv_bytes, "traffic": None},
+        }
+
+    if args.copy_calibration:
+        nbytes = 256 << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes_each_way"] = nbytes
+
+    # ---------------- CPU oracle baseline (reported, not the target) ----------------
+    if not args.no_cpu_baseline:
+        cores = len(os.sched_getaffinity(0))
+        os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+        import oracle
+
+        d0 = wl.generate(wcfg, seed=0)
+        xb = wl.bits(d0["x"])
+
+        def run_rows(rows):
+            t = time.perf_counter()
+            oracle.linear(xb[:rows], oracle.BF16, d0["w"], d0["s_ch"])
+            return time.perf_counter() - t
+
+        probe_rows = 32
+        tp = run_rows(probe_rows)
+        rows = int(min(m, max(probe_rows, probe_rows * args.cpu_seconds / max(tp, 1e-3))))
+        rows = max(16, rows // 16 * 16)
+        tc = run_rows(rows)
+        cpu_tops = 2.0 * rows * n * k / tc / 1e12
+        result["cpu_baseline"] = {
+            "value": round(cpu_tops, 5), "unit": "TOPS", "cores": int(os.environ["OMP_NUM_THREADS"]),
+            "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of prefill_outliers ({rows}x{k}x{n}): widen, per-token "
+                      f"quant, int8 GEMM, float64 dequant; {tc:.2f} s",
+            "seconds": round(tc, 3), "gpu_speedup": round(tops / cpu_tops, 1),
+        }
+
+    props = torch.cuda.get_device_properties(dev)
+    result["env"] = {"gpu": getattr(props, "gcnArchName", props.name), "cus": props.multi_processor_count,
+                     "torch": torch.__version__, "hip": torch.version.hip,
+                     "host_cpu": platform.processor() or platform.machine(),
+                     "host_cores": len(os.sched_getaffinity(0)), "lib": qk.build_info()}
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * qk.h -- C ABI of libqk, an MI355X (gfx950) W8A8 INT8 linear layer.
+ *
+ * The layer (all steps on the GPU, in HIP kernels of this library):
+ *   1. per-token dynamic INT8 quantization of the activations, optionally of
+ *      silu(gate) * up;
+ *   2. an INT8 x INT8 product accumulated in INT32;
+ *   3. a dequant epilogue  out = acc * scale_a[row] * scale_b[col] * output_scale.
+ *
+ * Sources, cited by page title and section:
+ *   "16. Deploying Custom Kernels", C++ Kernel Interface: the GEMM problem
+ *     statement (GemmConfig: m, n, k, int8 a and b, int32 c, fp32 scale_a and
+ *     scale_b, float output_scale, stream) and a status return;
+ *     Python Bindings: the argument order of the flat call.
+ *   "Skill: Write an INT8 Quantized Kernel", Inputs the agent should gather
+ *     first: symmetric [-127, 127] codes with zero point 0, INT32
+ *     accumulation, per-token and per-channel scales, fp32/fp16 output,
+ *     row- or column-major weights.
+ *   "KV-cache kernels", 02 Scales and dequantization: int8 products
+ *     accumulate in int32, then acc * a_scale * b_scale.
+ *   "kernels: fused silu_and_mul + dynamic per-token FP8 quantization",
+ *     Purpose and Algorithm: one scale per token from the row absmax,
+ *     scale = max(absmax, 1e-12) / qmax, optionally of silu(gate) * up.
+ *   "dynquant-kernels", Variants: an ABI number checked by the loader.
+ *
+ * Conventions (every function):
+ *   - Pointers to tensors are DEVICE pointers on the current HIP device;
+ *     every tensor is dense and row-major.  The caller allocates and owns all
+ *     memory; the library allocates nothing and keeps no pointer after a call
+ *     returns.  Outputs must not alias inputs.
+ *   - Work is enqueued on `stream` (0 = the null stream) and runs
+ *     asynchronously; a fault during execution surfaces at the caller's next
+ *     synchronisation.
+ *   - The return value is a status: QK_OK (0) on success; QK_ERR_* (>= 1000)
+ *     for an argument error detected on the host before anything is
+ *     enqueued; otherwise the hipError_t of a failed launch.  Nothing aborts
+ *     and no C++ exception crosses this interface.
+ *   - Dimensions are int; m == 0 or n == 0 is a successful no-op.
+ */
+#ifndef QK_H
+#define QK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QK_ABI_VERSION 1
+
+/* element types */
+#define QK_F32 0
+#define QK_BF16 1
+#define QK_F16 2
+
+/* weight layouts */
+#define QK_B_KN 0 /* b is [k][n], n contiguous (the default) */
+#define QK_B_NK 1 /* b is [n][k], k contiguous */
+
+/* GEMM kernel choice for qk_gemm_i8_scaled_ex */
+#define QK_KERNEL_AUTO 0 /* by shape: decode GEMV for m <= 16, MFMA tiles otherwise */
+#define QK_KERNEL_MFMA 1 /* LDS-tiled INT8 MFMA kernel, any m */
+#define QK_KERNEL_GEMV 2 /* split-K decode kernel, m <= 16 only */
+
+/* status codes */
+#define QK_OK 0
+#define QK_ERR_INVALID_VALUE 1001 /* negative size, NULL pointer, unknown enum */
+#define QK_ERR_UNSUPPORTED 1002   /* a size or alignment this library does not handle */
+#define QK_ERR_WORKSPACE 1003     /* workspace missing or smaller than required */
+
+/* Largest reduction length accepted: 131071 * 128 * 128 < 2^31, so no int32
+ * accumulator can overflow even for -128 operands ("Skill: Write an INT8
+ * Quantized Kernel", Inputs: INT32 accumulation is mandatory). */
+#define QK_MAX_K 131071
+
+/* Compiled-in ABI number.  A loader must refuse the library when it differs
+ * from the number it was written for ("dynquant-kernels", Variants). */
+int qk_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *qk_status_string(int status);
+
+/* Static text: code-object architectures, HIP version, ABI number
+ * (after "dynquant-kernels", Diagnosing an install). */
+const char *qk_build_info(void);
+
+/*
+ * Per-token dynamic INT8 quantization ("kernels: fused silu_and_mul + dynamic
+ * per-token FP8 quantization", Algorithm, with the symmetric [-127, 127]
+ * range of "Skill: Write an INT8 Quantized Kernel", Inputs):
+ *   scale[i] = max(max_j |x[i][j]|, 1e-12f) / 127       (binary32 division)
+ *   q[i][j]  = clamp(rint(x[i][j] / scale[i]), -127, 127) (binary32 division,
+ *                                                          ties to even)
+ *   x       [m][k] of x_dtype (QK_F32, QK_BF16 or QK_F16), read only.
+ *   q       [m][k] int8, written.
+ *   scale   [m] float, written.
+ * Any k >= 0 (k == 0 gives scale = 1e-12f / 127).  Errors: m or k negative,
+ * m*k > 2^62, NULL pointer with m*k > 0 (QK_ERR_INVALID_VALUE); unknown
+ * dtype (QK_ERR_INVALID_VALUE).
+ */
+int qk_quant_per_token(int m, int k, const void *x, int x_dtype, int8_t *q, float *scale,
+                       hipStream_t stream);
+
+/*
+ * silu(gate) * up followed by per-token INT8 quantization, one pass over h
+ * ("kernels: fused silu_and_mul + dynamic per-token FP8 quantization",
+ * Purpose and Algorithm):
+ *   g = h[i][j], u = h[i][d + j];  a[i][j] = (g / (1 + exp(-g))) * u  (binary32)
+ *   then scale[i] and q[i][j] as qk_quant_per_token on a.
+ *   exp is the library's fixed binary32 algorithm (reduction by ln 2, degree-7
+ *   Taylor polynomial with fused multiply-adds, scaling by 2^n; inputs above
+ *   88 give +inf, below -87 give 0), so results are reproducible bit for bit.
+ *   h       [m][2d] of h_dtype, gate = first half of each row, up = second.
+ *   q       [m][d] int8;  scale [m] float.
+ * Errors as qk_quant_per_token.
+ */
+int qk_silu_mul_quant_per_token(int m, int d, const void *h, int h_dtype, int8_t *q,
+                                float *scale, hipStream_t stream);
+
+/* Bytes of workspace qk_gemm_i8_scaled needs for this shape (0 if none).  The
+ * decode kernel (m <= 16) keeps exact INT32 split-K partial sums and arrival
+ * counters there. */
+size_t qk_gemm_workspace_size(int m, int n, int k);
+
+/*
+ * INT8 GEMM with INT32 accumulation and the dequant epilogue
+ * ("16. Deploying Custom Kernels", C++ Kernel Interface and Python Bindings
+ * for the first nine arguments; "KV-cache kernels", 02 Scales and
+ * dequantization for the epilogue):
+ *   acc[i][j] = sum_t a[i][t] * B(t, j)              (exact, INT32)
+ *   c[i][j]   = acc[i][j]                            (if c != NULL; raw)
+ *   out[i][j] = (float)acc * scale_a[i] * scale_b[j] * output_scale
+ *                                                    (if out != NULL; binary32
+ *                                                    arithmetic, stored as fp32
+ *                                                    or bf16 rounded to nearest even)
+ *   a        [m][k] int8 (the quantized activations).
+ *   b        [k][n] int8 (QK_B_KN) or [n][k] int8 (QK_B_NK).
+ *   c        [m][n] int32 or NULL.
+ *   scale_a  [m] float (per token), scale_b [n] float (per output channel);
+ *            both may be NULL only when out is NULL.
+ *   out      [m][n] of out_dtype (QK_F32 or QK_BF16) or NULL; c and out may
+ *            not both be NULL.
+ *   workspace / workspace_bytes: device memory of at least
+ *            qk_gemm_workspace_size(m, n, k) bytes, 256-byte aligned, zero
+ *            filled before its first use by this library; every call returns
+ *            it to all zeros when it completes.  Two calls in flight at the
+ *            same time must not share one workspace.
+ * Requirements: 0 <= k <= QK_MAX_K and k % 16 == 0; a, b 16-byte aligned
+ * (QK_ERR_UNSUPPORTED otherwise).  k == 0 gives acc = 0.
+ */
+int qk_gemm_i8_scaled(int m, int n, int k, const int8_t *a, const int8_t *b, int32_t *c,
+                      const float *scale_a, const float *scale_b, float output_scale, void *out,
+                      int out_dtype, int b_layout, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* As qk_gemm_i8_scaled with an explicit kernel choice (QK_KERNEL_*), so that
+ * both kernels can be checked at any shape.  QK_KERNEL_GEMV requires
+ * m <= 16 (QK_ERR_UNSUPPORTED otherwise). */
+int qk_gemm_i8_scaled_ex(int m, int n, int k, const int8_t *a, const int8_t *b, int32_t *c,
+                         const float *scale_a, const float *scale_b, float output_scale,
+                         void *out, int out_dtype, int b_layout, void *workspace,
+                         size_t workspace_bytes, int kernel, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QK_H */

@@ -74,6 +74,8 @@ def _load():
     lib.or_gemm_entries.restype = I64
     lib.or_dequant.argtypes = [I64, I64, P, P, P, ctypes.c_float, P]
     lib.or_dequant.restype = None
+    lib.or_dequant_entries.argtypes = [I64, P, P, P, ctypes.c_float, P]
+    lib.or_dequant_entries.restype = None
     lib.or_bf16_nearest.argtypes = [I64, P, P]
     lib.or_bf16_nearest.restype = None
     _lib = lib
@@ -195,6 +197,20 @@ def dequant(c: np.ndarray, scale_a: np.ndarray, scale_b: np.ndarray,
     m, n = c.shape
     out = np.empty((m, n), dtype=np.float64)
     lib.or_dequant(m, n, _ptr(c), _ptr(sa), _ptr(sb), float(output_scale), _ptr(out))
+    return out
+
+
+def dequant_entries(c: np.ndarray, scale_a: np.ndarray, scale_b: np.ndarray,
+                    output_scale: float = 1.0) -> np.ndarray:
+    """Per-entry acc[e] * scale_a[e] * scale_b[e] * output_scale in float64."""
+    lib = _load()
+    c = _contig(c, np.int32).ravel()
+    sa = _contig(scale_a, np.float32).ravel()
+    sb = _contig(scale_b, np.float32).ravel()
+    if not (c.size == sa.size == sb.size):
+        raise ValueError("entry arrays differ in length")
+    out = np.empty(c.shape, dtype=np.float64)
+    lib.or_dequant_entries(c.size, _ptr(c), _ptr(sa), _ptr(sb), float(output_scale), _ptr(out))
     return out
 
 

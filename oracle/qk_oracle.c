@@ -272,6 +272,14 @@ void or_dequant(int64_t m, int64_t n, const int32_t *c, const float *scale_a,
                              (double)output_scale;
 }
 
+/* The same product for listed entries: out[e] = acc[e] * sa[e] * sb[e] * output_scale. */
+void or_dequant_entries(int64_t count, const int32_t *c, const float *scale_a,
+                        const float *scale_b, float output_scale, double *out)
+{
+    for (int64_t e = 0; e < count; ++e)
+        out[e] = (double)c[e] * (double)scale_a[e] * (double)scale_b[e] * (double)output_scale;
+}
+
 /* bfloat16 (8 significant bits, binary32 exponent range) nearest v, ties to even. */
 static uint16_t bf16_nearest(double v)
 {

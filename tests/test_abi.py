@@ -1,0 +1,138 @@
+"""The C-ABI library loads, exports every symbol include/qk.h declares, and
+rejects bad arguments on the host before anything reaches a GPU.
+
+None of these calls launches a kernel: each returns from host-side checks, so
+they run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w8a8_int8_quantized_qk_amd as qk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qk.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qk_[a-z0-9_]+)\s*\(", text)))
+
+
+def _header_constants():
+    consts = {}
+    for name, val in re.findall(r"#define\s+(QK_[A-Z0-9_]+)\s+(-?\d+)", open(HEADER).read()):
+        consts[name] = int(val)
+    return consts
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return qk.library()
+
+
+def test_every_declared_function_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(qk.EXPORTED)
+
+
+def test_binding_constants_match_header():
+    c = _header_constants()
+    assert c["QK_ABI_VERSION"] == qk.ABI_VERSION
+    assert (c["QK_F32"], c["QK_BF16"], c["QK_F16"]) == (qk.F32, qk.BF16, qk.F16)
+    assert (c["QK_B_KN"], c["QK_B_NK"]) == (qk.B_KN, qk.B_NK)
+    assert (c["QK_KERNEL_AUTO"], c["QK_KERNEL_MFMA"], c["QK_KERNEL_GEMV"]) == (
+        qk.KERNEL_AUTO, qk.KERNEL_MFMA, qk.KERNEL_GEMV)
+
+
+def test_abi_version_and_build_info(lib):
+    assert lib.qk_abi_version() == qk.ABI_VERSION
+    info = qk.build_info()
+    assert "gfx950" in info and f"ABI {qk.ABI_VERSION}" in info
+
+
+def test_status_strings(lib):
+    c = _header_constants()
+    for code in ("QK_OK", "QK_ERR_INVALID_VALUE", "QK_ERR_UNSUPPORTED", "QK_ERR_WORKSPACE"):
+        s = qk.status_string(c[code])
+        assert s.startswith(code)
+
+
+def test_abi_mismatch_refuses_to_load(monkeypatch):
+    monkeypatch.setattr(qk, "ABI_VERSION", qk.ABI_VERSION + 1)
+    with pytest.raises(ImportError, match="ABI"):
+        qk.load_library()
+
+
+def test_missing_library_raises(tmp_path):
+    with pytest.raises(ImportError, match="missing"):
+        qk.load_library(str(tmp_path / "libqk.so"))
+
+
+def test_workspace_size(lib):
+    assert qk.gemm_workspace_size(2048, 4096, 4096) == 0        # MFMA path needs none
+    ws = qk.gemm_workspace_size(1, 14336, 4096)
+    assert ws >= 8 * 14336 * 4 and ws % 256 == 0
+    assert qk.gemm_workspace_size(16, 100, 16) > 0
+    assert qk.gemm_workspace_size(0, 100, 16) == 0
+
+
+NULL = ctypes.c_void_p(0)
+FAKE = ctypes.c_void_p(0x100000)      # 16-byte aligned; never dereferenced by these calls
+FAKE_ODD = ctypes.c_void_p(0x100001)
+
+
+def _gemm(lib, m, n, k, a=FAKE, b=FAKE, c=FAKE, sa=FAKE, sb=FAKE, out=FAKE, out_dtype=0,
+          layout=0, ws=NULL, ws_bytes=0, kernel=0):
+    return lib.qk_gemm_i8_scaled_ex(m, n, k, a, b, c, sa, sb, 1.0, out, out_dtype, layout, ws,
+                                    ws_bytes, kernel, NULL)
+
+
+def test_gemm_argument_errors_are_reported_before_launch(lib):
+    c = _header_constants()
+    INVALID, UNSUP, WS = c["QK_ERR_INVALID_VALUE"], c["QK_ERR_UNSUPPORTED"], c["QK_ERR_WORKSPACE"]
+    assert _gemm(lib, -1, 4, 16) == INVALID
+    assert _gemm(lib, 4, -1, 16) == INVALID
+    assert _gemm(lib, 4, 4, -16) == INVALID
+    assert _gemm(lib, 4, 4, 131072) == INVALID            # beyond QK_MAX_K
+    assert _gemm(lib, 4, 4, 24) == UNSUP                  # k % 16 != 0
+    assert _gemm(lib, 4, 4, 16, c=NULL, out=NULL) == INVALID
+    assert _gemm(lib, 4, 4, 16, out_dtype=2) == INVALID   # fp16 out not offered
+    assert _gemm(lib, 4, 4, 16, layout=7) == INVALID
+    assert _gemm(lib, 4, 4, 16, kernel=9) == INVALID
+    assert _gemm(lib, 40, 4, 16, a=NULL) == INVALID
+    assert _gemm(lib, 40, 4, 16, sa=NULL) == INVALID      # out needs both scales
+    assert _gemm(lib, 40, 4, 16, a=FAKE_ODD) == UNSUP     # 128-bit loads need alignment
+    assert _gemm(lib, 17, 4, 16, kernel=2) == UNSUP       # decode kernel takes m <= 16
+    assert _gemm(lib, 4, 4, 16, layout=1, kernel=2) == UNSUP
+    assert _gemm(lib, 4, 4, 16, kernel=2) == WS           # decode kernel without workspace
+    assert _gemm(lib, 4, 4, 16, ws=FAKE, ws_bytes=16) == WS
+    # empty problems succeed without touching memory
+    assert _gemm(lib, 0, 4, 16, a=NULL, b=NULL) == 0
+    assert _gemm(lib, 4, 0, 16, a=NULL, b=NULL) == 0
+
+
+def test_quant_argument_errors_are_reported_before_launch(lib):
+    c = _header_constants()
+    INVALID = c["QK_ERR_INVALID_VALUE"]
+    assert lib.qk_quant_per_token(-1, 4, FAKE, 0, FAKE, FAKE, NULL) == INVALID
+    assert lib.qk_quant_per_token(4, -4, FAKE, 0, FAKE, FAKE, NULL) == INVALID
+    assert lib.qk_quant_per_token(4, 4, FAKE, 5, FAKE, FAKE, NULL) == INVALID
+    assert lib.qk_quant_per_token(4, 4, NULL, 0, FAKE, FAKE, NULL) == INVALID
+    assert lib.qk_quant_per_token(4, 4, FAKE, 0, FAKE, NULL, NULL) == INVALID
+    assert lib.qk_quant_per_token(0, 4, NULL, 0, NULL, NULL, NULL) == 0
+    assert lib.qk_silu_mul_quant_per_token(4, 4, FAKE, 3, FAKE, FAKE, NULL) == INVALID
+    assert lib.qk_silu_mul_quant_per_token(0, 4, NULL, 1, NULL, NULL, NULL) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(2, 16)
+    with pytest.raises(ValueError, match="GPU"):
+        qk.quant_per_token(x)

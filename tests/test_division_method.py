@@ -1,0 +1,21 @@
+"""The quantization kernel's reciprocal-corrected quotient gives the IEEE codes.
+
+The kernel forms x / s as fma(e, r, y) with y = x * r, e = fma(-y, s, x) and
+r = RN(1 / s) (Markstein's correction).  This test runs that recipe on the
+CPU against true binary32 division over every bf16 input for a spread of row
+maxima and over random binary32 inputs, including inputs next to the
+half-integer multiples of s where a wrong quotient would change the code.
+"""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def test_markstein_quotient_gives_ieee_codes(tmp_path):
+    exe = tmp_path / "division_method_check"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+                           os.path.join(HERE, "division_method_check.c"), "-o", str(exe), "-lm"])
+    res = subprocess.run([str(exe), "20000000"], capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "mismatches 0" in res.stdout

@@ -1,0 +1,336 @@
+"""GPU parity: every libqk kernel against the CPU oracle, element by element.
+
+Codes, scales and INT32 accumulators must match bit for bit; fp32 outputs
+within 1e-6 relative and bf16 outputs within one ulp of the oracle's float64
+dequant value.  Inputs are seeded and synthetic (w8a8_int8_quantized_qk_amd
+.workloads); nothing expected here comes from the GPU.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w8a8_int8_quantized_qk_amd as qk
+from tests.gpu_compare import (DTYPE_CODE, TORCH_OUT, assert_equal_exact, assert_out_close,
+                               host)
+from w8a8_int8_quantized_qk_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qk.library()  # raises when the HIP library is missing
+
+
+def _seed(*parts) -> int:
+    s = 0
+    for p in parts:
+        s = (s * 1000003 + (p if isinstance(p, int) else sum(map(ord, str(p))))) % (2**32)
+    return s
+
+
+def _check_quant(x_cpu: torch.Tensor, dtype: str, x_dev: torch.Tensor | None = None, what=""):
+    x_dev = x_cpu.to(DEV) if x_dev is None else x_dev
+    q, s = qk.quant_per_token(x_dev)
+    q_ref, s_ref = oracle.quantize_input(wl.bits(x_cpu), DTYPE_CODE[dtype])
+    assert_equal_exact(host(s), s_ref, f"{what} scale")
+    assert_equal_exact(host(q), q_ref, f"{what} codes")
+
+
+def _check_silu_quant(h_cpu: torch.Tensor, dtype: str, what=""):
+    q, s = qk.silu_mul_quant_per_token(h_cpu.to(DEV))
+    q_ref, s_ref = oracle.silu_mul_quantize(wl.bits(h_cpu), DTYPE_CODE[dtype])
+    assert_equal_exact(host(s), s_ref, f"{what} scale")
+    assert_equal_exact(host(q), q_ref, f"{what} codes")
+
+
+# --------------------------------------------------------------------------
+# per-token quantization
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("tokens", [1, 7, 64, 256])
+@pytest.mark.parametrize("hidden", [64, 512, 4096])
+def test_quant_token_hidden_grid(dtype, tokens, hidden):
+    rng = np.random.default_rng(_seed("q", dtype, tokens, hidden))
+    x = wl.random_activations(rng, tokens, hidden, dtype, outlier_cols=max(1, hidden // 100))
+    _check_quant(x, dtype, what=f"{dtype} {tokens}x{hidden}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("k", [0, 1, 3, 8, 100, 1000, 4104, 8200, 16392, 33000])
+def test_quant_ragged_and_long_rows(dtype, k):
+    rng = np.random.default_rng(_seed("qr", dtype, k))
+    x = wl.random_activations(rng, 5, k, dtype)
+    _check_quant(x, dtype, what=f"{dtype} k={k}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quant_misaligned_input_takes_the_two_pass_kernel(dtype):
+    rng = np.random.default_rng(_seed("qm", dtype))
+    m, k = 9, 1024
+    x = wl.random_activations(rng, m, k, dtype)
+    buf = torch.empty(m * k + 1, dtype=x.dtype, device=DEV)
+    xd = buf[1:].view(m, k)
+    xd.copy_(x.to(DEV))
+    _check_quant(x, dtype, x_dev=xd, what="misaligned")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("k", [64, 333, 4096])
+def test_quant_edge_rows(dtype, k):
+    _check_quant(wl.edge_rows(k, dtype), dtype, what=f"edge {dtype} k={k}")
+
+
+def test_quant_rounding_discriminators():
+    # inputs next to half-integer multiples of the row scale, where a
+    # reciprocal product or a different rounding would change the code
+    rng = np.random.default_rng(_seed("disc"))
+    rows = []
+    for amax in rng.uniform(0.01, 300, 64).astype(np.float32):
+        s = np.float32(max(amax, np.float32(1e-12))) / np.float32(127)
+        j = rng.integers(-126, 126, 255)
+        base = ((j + 0.5) * s).astype(np.float32)
+        steps = rng.integers(-2, 3, 255)
+        x = base.copy()
+        for i in range(255):
+            for _ in range(abs(int(steps[i]))):
+                x[i] = np.nextafter(x[i], np.float32(np.inf) if steps[i] > 0 else np.float32(-np.inf))
+        x = np.clip(x, -amax, amax)
+        rows.append(np.concatenate([[amax], x]).astype(np.float32))
+    xt = torch.from_numpy(np.stack(rows))
+    _check_quant(xt, "f32", what="discriminators")
+
+
+@pytest.mark.parametrize("name", ["prefill_outliers", "mlp_up", "decode_m8"])
+def test_quant_full_workload(name):
+    d = wl.generate(name)
+    _check_quant(d["x"], d["workload"].x_dtype, what=name)
+
+
+def test_quant_repeatable():
+    rng = np.random.default_rng(_seed("rep"))
+    x = wl.random_activations(rng, 300, 4096, "bf16", outlier_cols=41).to(DEV)
+    q1, s1 = qk.quant_per_token(x)
+    q2, s2 = qk.quant_per_token(x)
+    assert torch.equal(q1, q2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
+# --------------------------------------------------------------------------
+# silu(gate) * up fused with per-token quantization
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("tokens", [1, 7, 64, 256])
+@pytest.mark.parametrize("hidden", [64, 512, 4096])
+def test_silu_quant_token_hidden_grid(dtype, tokens, hidden):
+    rng = np.random.default_rng(_seed("s", dtype, tokens, hidden))
+    h = wl.random_activations(rng, tokens, 2 * hidden, dtype)
+    _check_silu_quant(h, dtype, what=f"silu {dtype} {tokens}x{hidden}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [1, 3, 100, 14336, 16392])
+def test_silu_quant_ragged_and_long_rows(dtype, d):
+    rng = np.random.default_rng(_seed("sr", dtype, d))
+    h = wl.random_activations(rng, 3, 2 * d, dtype)
+    _check_silu_quant(h, dtype, what=f"silu {dtype} d={d}")
+
+
+def test_silu_quant_extreme_gates():
+    # gates across the exp limits (|g| up to 120) and exact zeros
+    rng = np.random.default_rng(_seed("se"))
+    g = rng.uniform(-120, 120, (16, 2048)).astype(np.float32)
+    g[:, :16] = 0.0
+    g[:, 16:32] = np.float32(-88.0)
+    g[:, 32:48] = np.float32(87.5)
+    u = rng.standard_normal((16, 2048)).astype(np.float32)
+    for dt in ("f32", "bf16"):
+        _check_silu_quant(wl.cast(np.concatenate([g, u], axis=1), dt), dt, what=f"extreme {dt}")
+
+
+def test_silu_quant_full_workload():
+    d = wl.generate("gated_down")
+    _check_silu_quant(d["h"], "bf16", what="gated_down")
+
+
+# --------------------------------------------------------------------------
+# INT8 GEMM + dequant epilogue
+# --------------------------------------------------------------------------
+
+GEMM_SHAPES = [(1, 1, 16), (1, 512, 256), (2, 1000, 512), (3, 100, 64), (7, 63, 48),
+               (8, 1040, 4096), (16, 77, 32), (33, 130, 272), (65, 257, 400),
+               (256, 128, 128), (300, 385, 1040), (513, 200, 0)]
+
+
+def _gemm_inputs(m, n, k, layout, seed):
+    rng = np.random.default_rng(seed)
+    a = rng.integers(-128, 128, size=(m, k), dtype=np.int8)
+    b_kn = rng.integers(-128, 128, size=(k, n), dtype=np.int8)
+    sa = rng.uniform(1e-4, 1e-1, m).astype(np.float32)
+    sb = rng.uniform(1e-3, 1e-2, n).astype(np.float32)
+    b = b_kn if layout == "kn" else np.ascontiguousarray(b_kn.T)
+    return a, b, sa, sb
+
+
+def _run_gemm_case(m, n, k, layout, kernel, out_dtype, output_scale=1.0):
+    a, b, sa, sb = _gemm_inputs(m, n, k, layout, _seed("g", m, n, k, layout))
+    out, c = qk.gemm_i8_scaled(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV),
+                               torch.from_numpy(sa).to(DEV), torch.from_numpy(sb).to(DEV),
+                               output_scale, TORCH_OUT[out_dtype], layout, return_acc=True,
+                               kernel=kernel)
+    c_ref = oracle.gemm_i32(a, b, oracle.B_KN if layout == "kn" else oracle.B_NK)
+    what = f"{m}x{n}x{k} {layout} {kernel} {out_dtype}"
+    assert_equal_exact(host(c), c_ref, f"{what} acc")
+    assert_out_close(host(out), oracle.dequant(c_ref, sa, sb, output_scale), out_dtype, what)
+    # the launch without raw accumulators gives the same outputs
+    out2 = qk.gemm_i8_scaled(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV),
+                             torch.from_numpy(sa).to(DEV), torch.from_numpy(sb).to(DEV),
+                             output_scale, TORCH_OUT[out_dtype], layout, kernel=kernel)
+    assert np.array_equal(host(out2).view(np.uint8), host(out).view(np.uint8))
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_mfma_kernel(m, n, k, layout, out_dtype):
+    _run_gemm_case(m, n, k, layout, "mfma", out_dtype)
+
+
+@pytest.mark.parametrize("m,n,k", [s for s in GEMM_SHAPES if s[0] <= 16])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_decode_kernel(m, n, k, out_dtype):
+    _run_gemm_case(m, n, k, "kn", "gemv", out_dtype)
+
+
+@pytest.mark.parametrize("kernel", ["auto", "mfma", "gemv"])
+def test_gemm_output_scale(kernel):
+    _run_gemm_case(4, 96, 64, "kn", kernel, "f32", output_scale=-0.375)
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "gemv"])
+def test_gemm_int32_closed_forms(kernel):
+    # K * 127 * 127 at K = 65536, and K * (-128) * (-128) at the largest
+    # K (multiple of 16) the library accepts: both fit in int32 exactly
+    for k, av, bv in ((65536, 127, 127), (65536, 127, -127), (131056, -128, -128)):
+        a = torch.full((2, k), av, dtype=torch.int8, device=DEV)
+        b = torch.full((k, 64), bv, dtype=torch.int8, device=DEV)
+        c = qk.gemm_i8_scaled(a, b, out_dtype=None, kernel=kernel)
+        assert bool((c == k * av * bv).all()), (kernel, k, av, bv)
+
+
+def test_gemm_empty_and_zero_k():
+    a = torch.empty((0, 32), dtype=torch.int8, device=DEV)
+    b = torch.zeros((32, 8), dtype=torch.int8, device=DEV)
+    out = qk.gemm_i8_scaled(a, b, torch.empty(0, device=DEV), torch.ones(8, device=DEV),
+                            out_dtype=torch.float32)
+    assert out.shape == (0, 8)
+    for kernel in ("mfma", "gemv"):
+        a = torch.empty((5, 0), dtype=torch.int8, device=DEV)
+        b = torch.empty((0, 40), dtype=torch.int8, device=DEV)
+        out, c = qk.gemm_i8_scaled(a, b, torch.ones(5, device=DEV), torch.ones(40, device=DEV),
+                                   out_dtype=torch.float32, return_acc=True, kernel=kernel)
+        assert not c.any() and not out.any()
+
+
+def test_gemm_rejects_k_not_multiple_of_16():
+    a = torch.zeros((4, 24), dtype=torch.int8, device=DEV)
+    b = torch.zeros((24, 8), dtype=torch.int8, device=DEV)
+    with pytest.raises(qk.QKError):
+        qk.gemm_i8_scaled(a, b, out_dtype=None)
+
+
+def test_gemm_repeatable_and_workspace_left_zero():
+    d = wl.generate("decode_m8")
+    x = d["x"].to(DEV)
+    w = torch.from_numpy(d["w"]).to(DEV)
+    s_ch = torch.from_numpy(d["s_ch"]).to(DEV)
+    q, s = qk.quant_per_token(x)
+    ws = torch.zeros(qk.gemm_workspace_size(8, w.shape[1], w.shape[0]), dtype=torch.uint8,
+                     device=DEV)
+    outs = [qk.gemm_i8_scaled(q, w, s, s_ch, return_acc=True, kernel="gemv", workspace=ws)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    assert not ws.any()
+    for o, c in outs[1:]:
+        assert torch.equal(c, outs[0][1]) and torch.equal(o.view(torch.int16),
+                                                          outs[0][0].view(torch.int16))
+    o_mfma, c_mfma = qk.gemm_i8_scaled(q, w, s, s_ch, return_acc=True, kernel="mfma")
+    assert torch.equal(c_mfma, outs[0][1])
+
+
+def test_gemm_on_a_side_stream():
+    a, b, sa, sb = _gemm_inputs(300, 200, 256, "kn", 5)
+    side = torch.cuda.Stream(DEV)
+    with torch.cuda.stream(side):
+        c = qk.gemm_i8_scaled(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV),
+                              out_dtype=None)
+    side.synchronize()
+    assert_equal_exact(host(c), oracle.gemm_i32(a, b), "side stream acc")
+
+
+# --------------------------------------------------------------------------
+# the named workloads, end to end, in the launch configuration of bench.py
+# --------------------------------------------------------------------------
+
+def _sample_entries(m, n, rng, count=4096):
+    rows = np.concatenate([rng.integers(0, m, count), [0, m - 1, m - 1, 0]])
+    cols = np.concatenate([rng.integers(0, n, count), [0, n - 1, 0, n - 1]])
+    return rows.astype(np.int64), cols.astype(np.int64)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "decode_m1", "decode_m8", "prefill_outliers",
+                                  "gated_down", "mlp_up"])
+def test_workload_end_to_end(name):
+    d = wl.generate(name)
+    w_cfg = d["workload"]
+    w_host = d["w"]
+    w = torch.from_numpy(w_host).to(DEV)
+    s_ch = torch.from_numpy(d["s_ch"]).to(DEV)
+    if w_cfg.gated:
+        q, s = qk.silu_mul_quant_per_token(d["h"].to(DEV))
+        q_ref, s_ref = oracle.silu_mul_quantize(wl.bits(d["h"]), DTYPE_CODE[w_cfg.x_dtype])
+    else:
+        q, s = qk.quant_per_token(d["x"].to(DEV))
+        q_ref, s_ref = oracle.quantize_input(wl.bits(d["x"]), DTYPE_CODE[w_cfg.x_dtype])
+    assert_equal_exact(host(s), s_ref, f"{name} scale")
+    assert_equal_exact(host(q), q_ref, f"{name} codes")
+
+    out = qk.gemm_i8_scaled(q, w, s, s_ch, out_dtype=TORCH_OUT[w_cfg.out_dtype])
+    out_acc, c = qk.gemm_i8_scaled(q, w, s, s_ch, out_dtype=TORCH_OUT[w_cfg.out_dtype],
+                                   return_acc=True)
+    out_h = host(out)
+    assert np.array_equal(out_h.view(np.uint8), host(out_acc).view(np.uint8))
+    c_h = host(c)
+    m, n = w_cfg.m, w_cfg.n
+    rng = np.random.default_rng(_seed("e2e", name))
+    if m * n * w_cfg.k <= 2**28:
+        c_ref = oracle.gemm_i32(q_ref, w_host)
+        assert_equal_exact(c_h, c_ref, f"{name} acc")
+        assert_out_close(out_h, oracle.dequant(c_ref, s_ref, d["s_ch"]), w_cfg.out_dtype, name)
+        return
+    # full rows at a few positions (tile edges included) ...
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, m - 1], rng.integers(0, m, 7)]))
+    rows = rows[rows < m]
+    c_rows = oracle.gemm_i32(q_ref[rows], w_host)
+    assert_equal_exact(c_h[rows], c_rows, f"{name} acc rows")
+    assert_out_close(out_h[rows], oracle.dequant(c_rows, s_ref[rows], d["s_ch"]),
+                     w_cfg.out_dtype, f"{name} rows")
+    # ... and scattered single entries
+    r, cc = _sample_entries(m, n, rng)
+    c_ent = oracle.gemm_entries(q_ref, w_host, r, cc)
+    assert_equal_exact(c_h[r, cc], c_ent, f"{name} acc entries")
+    assert_out_close(out_h[r, cc], oracle.dequant_entries(c_ent, s_ref[r], d["s_ch"][cc]),
+                     w_cfg.out_dtype, f"{name} entries")
+    # and a property over every entry: |out| is bounded by |acc| s_a s_b (1 + 1e-6)
+    bound = np.abs(c_h.astype(np.float64)) * s_ref[:, None].astype(np.float64) \
+        * d["s_ch"][None, :].astype(np.float64)
+    outf = torch.from_numpy(out_h.view(np.int16)).view(torch.bfloat16).float().numpy() \
+        if w_cfg.out_dtype == "bf16" else out_h
+    assert np.all(np.abs(outf.astype(np.float64)) <= bound * (1 + 2.0 ** -7) + 1e-30)

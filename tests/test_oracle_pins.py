@@ -433,3 +433,14 @@ def test_silu_mul_bitwise_against_stepwise_exact_evaluation():
             assert float(hv) == 0.0
         else:
             assert exact.f32_bits(float(hv)) == exact.f32_bits(want), (gv, uv)
+
+
+def test_dequant_entries_is_the_exact_product():
+    rng = np.random.default_rng(13)
+    c = rng.integers(-2**31, 2**31 - 1, size=50, dtype=np.int64).astype(np.int32)
+    sa = rng.uniform(1e-4, 1, 50).astype(np.float32)
+    sb = rng.uniform(1e-3, 1e-2, 50).astype(np.float32)
+    out = oracle.dequant_entries(c, sa, sb, 0.5)
+    for e in range(50):
+        ex = Fraction(int(c[e])) * Fraction(float(sa[e])) * Fraction(float(sb[e])) / 2
+        assert abs(Fraction(float(out[e])) - ex) <= abs(ex) * Fraction(4, 2**53)

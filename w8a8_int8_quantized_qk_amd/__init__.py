@@ -1,1 +1,269 @@
-"""MI355X-native W8A8 INT8 linear layer (placeholder; the binding follows)."""
+"""MI355X-native W8A8 INT8 linear layer: Python binding of libqk.
+
+Every step runs in the HIP kernels of ``libqk.so`` (built for gfx950 by
+``build.py``); this module only checks tensors, passes raw device pointers
+and the current HIP stream through the C ABI of ``include/qk.h``, and raises
+on a nonzero status.  PyTorch provides device memory and streams.  There is no
+fallback: if the library is missing or was built for another ABI, every call
+raises.
+
+Layer (per-token dynamic INT8 activations, per-channel INT8 weights):
+  q, s     = quant_per_token(x)                 # or silu_mul_quant_per_token(h)
+  out      = gemm_i8_scaled(q, w, s, s_ch)       # INT32 accumulate + dequant
+  out      = linear_w8a8(x, w, s_ch)             # both steps
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+ABI_VERSION = 1
+F32, BF16, F16 = 0, 1, 2
+B_KN, B_NK = 0, 1
+KERNEL_AUTO, KERNEL_MFMA, KERNEL_GEMV = 0, 1, 2
+QK_OK = 0
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqk.so")
+
+_IN_DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+_OUT_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+_LAYOUTS = {"kn": B_KN, "nk": B_NK}
+_KERNELS = {"auto": KERNEL_AUTO, "mfma": KERNEL_MFMA, "gemv": KERNEL_GEMV}
+
+EXPORTED = (
+    "qk_abi_version", "qk_status_string", "qk_build_info", "qk_quant_per_token",
+    "qk_silu_mul_quant_per_token", "qk_gemm_workspace_size", "qk_gemm_i8_scaled",
+    "qk_gemm_i8_scaled_ex",
+)
+
+
+class QKError(RuntimeError):
+    """A nonzero status from libqk."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libqk status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def _declare(lib):
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.qk_abi_version.argtypes = []
+    lib.qk_abi_version.restype = I
+    lib.qk_status_string.argtypes = [I]
+    lib.qk_status_string.restype = ctypes.c_char_p
+    lib.qk_build_info.argtypes = []
+    lib.qk_build_info.restype = ctypes.c_char_p
+    lib.qk_quant_per_token.argtypes = [I, I, P, I, P, P, P]
+    lib.qk_quant_per_token.restype = I
+    lib.qk_silu_mul_quant_per_token.argtypes = [I, I, P, I, P, P, P]
+    lib.qk_silu_mul_quant_per_token.restype = I
+    lib.qk_gemm_workspace_size.argtypes = [I, I, I]
+    lib.qk_gemm_workspace_size.restype = ctypes.c_size_t
+    gemm = [I, I, I, P, P, P, P, P, F, P, I, I, P, ctypes.c_size_t]
+    lib.qk_gemm_i8_scaled.argtypes = gemm + [P]
+    lib.qk_gemm_i8_scaled.restype = I
+    lib.qk_gemm_i8_scaled_ex.argtypes = gemm + [I, P]
+    lib.qk_gemm_i8_scaled_ex.restype = I
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libqk and check its ABI number; raises if absent or mismatched."""
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m w8a8_int8_quantized_qk_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(path)
+    for name in EXPORTED:
+        if not hasattr(lib, name):
+            raise ImportError(f"{path} does not export {name}")
+    _declare(lib)
+    got = lib.qk_abi_version()
+    if got != ABI_VERSION:
+        raise ImportError(
+            f"{path} has ABI {got}, this binding expects ABI {ABI_VERSION}: rebuild the "
+            "library from this source tree")
+    return lib
+
+
+def library() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                _lib = load_library()
+    return _lib
+
+
+def build_info() -> str:
+    return library().qk_build_info().decode()
+
+
+def status_string(status: int) -> str:
+    return library().qk_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != QK_OK:
+        raise QKError(status, status_string(status))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def quant_per_token(x: torch.Tensor, q: torch.Tensor | None = None,
+                    scale: torch.Tensor | None = None):
+    """Per-token INT8 codes and fp32 scales of x [m, k] (fp32, bf16 or fp16)."""
+    _need(x, "x", ndim=2)
+    if x.dtype not in _IN_DTYPES:
+        raise TypeError(f"x dtype {x.dtype} not supported")
+    m, k = x.shape
+    q = torch.empty((m, k), dtype=torch.int8, device=x.device) if q is None else q
+    scale = torch.empty((m,), dtype=torch.float32, device=x.device) if scale is None else scale
+    _need(q, "q", torch.int8, 2, x.device)
+    _need(scale, "scale", torch.float32, 1, x.device)
+    if tuple(q.shape) != (m, k) or scale.shape[0] != m:
+        raise ValueError("q must be [m, k] and scale [m]")
+    _check(library().qk_quant_per_token(m, k, _ptr(x), _IN_DTYPES[x.dtype], _ptr(q),
+                                        _ptr(scale), _stream(x.device)))
+    return q, scale
+
+
+def silu_mul_quant_per_token(h: torch.Tensor, q: torch.Tensor | None = None,
+                             scale: torch.Tensor | None = None):
+    """Codes and scales of silu(h[:, :d]) * h[:, d:] for h [m, 2d]."""
+    _need(h, "h", ndim=2)
+    if h.dtype not in _IN_DTYPES:
+        raise TypeError(f"h dtype {h.dtype} not supported")
+    m, two_d = h.shape
+    if two_d % 2:
+        raise ValueError("h must have an even number of columns (gate | up)")
+    d = two_d // 2
+    q = torch.empty((m, d), dtype=torch.int8, device=h.device) if q is None else q
+    scale = torch.empty((m,), dtype=torch.float32, device=h.device) if scale is None else scale
+    _need(q, "q", torch.int8, 2, h.device)
+    _need(scale, "scale", torch.float32, 1, h.device)
+    if tuple(q.shape) != (m, d) or scale.shape[0] != m:
+        raise ValueError("q must be [m, d] and scale [m]")
+    _check(library().qk_silu_mul_quant_per_token(m, d, _ptr(h), _IN_DTYPES[h.dtype], _ptr(q),
+                                                 _ptr(scale), _stream(h.device)))
+    return q, scale
+
+
+def gemm_workspace_size(m: int, n: int, k: int) -> int:
+    return int(library().qk_gemm_workspace_size(m, n, k))
+
+
+_workspaces: dict = {}
+
+
+def workspace_for(device: torch.device, stream_handle: int, nbytes: int) -> torch.Tensor | None:
+    """A zero-filled workspace of at least nbytes for one (device, stream).
+
+    libqk leaves the workspace zero after every call, so one buffer serves all
+    calls issued in order on that stream.
+    """
+    if nbytes == 0:
+        return None
+    key = (device, stream_handle)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def gemm_i8_scaled(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor | None = None,
+                   scale_b: torch.Tensor | None = None, output_scale: float = 1.0,
+                   out_dtype: torch.dtype | None = torch.bfloat16, b_layout: str = "kn",
+                   return_acc: bool = False, out: torch.Tensor | None = None,
+                   c: torch.Tensor | None = None, kernel: str = "auto",
+                   workspace: torch.Tensor | None = None):
+    """INT8 GEMM, INT32 accumulation, dequant epilogue.
+
+    a [m, k] int8; b [k, n] ("kn") or [n, k] ("nk") int8; scale_a [m] and
+    scale_b [n] fp32.  Returns out [m, n] (out_dtype fp32 or bf16), or
+    (out, c) with the raw int32 accumulators when return_acc; out_dtype None
+    returns only c.
+    """
+    _need(a, "a", torch.int8, 2)
+    dev = a.device
+    _need(b, "b", torch.int8, 2, dev)
+    layout = _LAYOUTS[b_layout]
+    m, k = a.shape
+    n, kb = (b.shape[1], b.shape[0]) if layout == B_KN else (b.shape[0], b.shape[1])
+    if kb != k:
+        raise ValueError(f"inner dimensions differ: a has k={k}, b has {kb}")
+    want_out = out is not None or out_dtype is not None
+    if want_out:
+        out_dtype = out.dtype if out is not None else out_dtype
+        if out_dtype not in _OUT_DTYPES:
+            raise TypeError(f"out dtype {out_dtype} not supported")
+        if out is None:
+            out = torch.empty((m, n), dtype=out_dtype, device=dev)
+        _need(out, "out", out_dtype, 2, dev)
+        _need(scale_a, "scale_a", torch.float32, 1, dev)
+        _need(scale_b, "scale_b", torch.float32, 1, dev)
+        if scale_a.shape[0] != m or scale_b.shape[0] != n or tuple(out.shape) != (m, n):
+            raise ValueError("scale_a must be [m], scale_b [n], out [m, n]")
+    if return_acc or not want_out:
+        if c is None:
+            c = torch.empty((m, n), dtype=torch.int32, device=dev)
+        _need(c, "c", torch.int32, 2, dev)
+    else:
+        c = None
+    stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = workspace_for(dev, stream.cuda_stream, gemm_workspace_size(m, n, k))
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(library().qk_gemm_i8_scaled_ex(
+        m, n, k, _ptr(a), _ptr(b), _ptr(c), _ptr(scale_a if want_out else None),
+        _ptr(scale_b if want_out else None), float(output_scale), _ptr(out if want_out else None),
+        _OUT_DTYPES[out_dtype] if want_out else F32, layout, _ptr(workspace), ws_bytes,
+        _KERNELS[kernel], ctypes.c_void_p(stream.cuda_stream)))
+    if not want_out:
+        return c
+    return (out, c) if return_acc else out
+
+
+def linear_w8a8(x: torch.Tensor, w: torch.Tensor, s_ch: torch.Tensor,
+                out_dtype: torch.dtype = torch.bfloat16, b_layout: str = "kn",
+                output_scale: float = 1.0, kernel: str = "auto"):
+    """Per-token quantization of x, then the INT8 GEMM with dequant."""
+    q, s = quant_per_token(x)
+    return gemm_i8_scaled(q, w, s, s_ch, output_scale, out_dtype, b_layout, kernel=kernel)
+
+
+def gated_linear_w8a8(h: torch.Tensor, w: torch.Tensor, s_ch: torch.Tensor,
+                      out_dtype: torch.dtype = torch.bfloat16, b_layout: str = "kn",
+                      output_scale: float = 1.0, kernel: str = "auto"):
+    """silu(gate) * up with per-token quantization, then the INT8 GEMM."""
+    q, s = silu_mul_quant_per_token(h)
+    return gemm_i8_scaled(q, w, s, s_ch, output_scale, out_dtype, b_layout, kernel=kernel)

@@ -1,0 +1,127 @@
+// C ABI of libqk: argument validation, kernel choice by shape, launches on the
+// caller's stream.  Declarations and the contract of each call are in qk.h.
+#include <cstdint>
+
+#include "qk_internal.h"
+
+#define QK_STR2(x) #x
+#define QK_STR(x) QK_STR2(x)
+
+namespace {
+
+bool aligned(const void* p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; }
+
+bool known_input_dtype(int dt) { return dt == QK_F32 || dt == QK_BF16 || dt == QK_F16; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? QK_OK : static_cast<int>(e); }
+
+int check_rows(int m, int k, const void* src, const void* q, const void* scale, int dtype) {
+  if (m < 0 || k < 0) return QK_ERR_INVALID_VALUE;
+  if (!known_input_dtype(dtype)) return QK_ERR_INVALID_VALUE;
+  if (m > 0 && (!scale || (k > 0 && (!src || !q)))) return QK_ERR_INVALID_VALUE;
+  return QK_OK;
+}
+
+int gemm_common(int m, int n, int k, const int8_t* a, const int8_t* b, int32_t* c,
+                const float* scale_a, const float* scale_b, float output_scale, void* out,
+                int out_dtype, int b_layout, void* workspace, size_t workspace_bytes, int kernel,
+                hipStream_t stream) {
+  if (m < 0 || n < 0 || k < 0 || k > QK_MAX_K) return QK_ERR_INVALID_VALUE;
+  if (b_layout != QK_B_KN && b_layout != QK_B_NK) return QK_ERR_INVALID_VALUE;
+  if (kernel != QK_KERNEL_AUTO && kernel != QK_KERNEL_MFMA && kernel != QK_KERNEL_GEMV)
+    return QK_ERR_INVALID_VALUE;
+  if (k % 16 != 0) return QK_ERR_UNSUPPORTED;
+  if (m == 0 || n == 0) return QK_OK;  // empty tensors may have NULL data pointers
+  if (!c && !out) return QK_ERR_INVALID_VALUE;
+  if (out && out_dtype != QK_F32 && out_dtype != QK_BF16) return QK_ERR_INVALID_VALUE;
+  if (k > 0 && (!a || !b)) return QK_ERR_INVALID_VALUE;
+  if (out && (!scale_a || !scale_b)) return QK_ERR_INVALID_VALUE;
+  if (!aligned(a, 16) || !aligned(b, 16)) return QK_ERR_UNSUPPORTED;
+  if (c && !aligned(c, 4)) return QK_ERR_UNSUPPORTED;
+  if (out && !aligned(out, out_dtype == QK_BF16 ? 2 : 4)) return QK_ERR_UNSUPPORTED;
+
+  bool gemv;
+  if (kernel == QK_KERNEL_GEMV) {
+    if (m > qk::kGemvMaxM || b_layout != QK_B_KN) return QK_ERR_UNSUPPORTED;
+    gemv = true;
+  } else if (kernel == QK_KERNEL_MFMA) {
+    gemv = false;
+  } else {
+    gemv = m <= qk::kGemvMaxRows && b_layout == QK_B_KN;
+  }
+
+  qk::GemmArgs g{m, n, k, a, b, c, scale_a, scale_b, output_scale, out, out_dtype, b_layout,
+                 workspace, workspace_bytes};
+  if (gemv) {
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < qk::gemv_workspace_bytes(n))
+      return QK_ERR_WORKSPACE;
+    return status_of(qk::launch_gemv(g, stream));
+  }
+  return status_of(qk::launch_gemm_mfma(g, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int qk_abi_version(void) { return QK_ABI_VERSION; }
+
+const char* qk_status_string(int status) {
+  switch (status) {
+    case QK_OK: return "QK_OK: success";
+    case QK_ERR_INVALID_VALUE:
+      return "QK_ERR_INVALID_VALUE: negative size, NULL pointer, or unknown dtype/layout/kernel";
+    case QK_ERR_UNSUPPORTED:
+      return "QK_ERR_UNSUPPORTED: k not a multiple of 16, misaligned pointer, or kernel/shape "
+             "combination not provided";
+    case QK_ERR_WORKSPACE:
+      return "QK_ERR_WORKSPACE: workspace missing, misaligned, or smaller than "
+             "qk_gemm_workspace_size()";
+    default: return hipGetErrorString(static_cast<hipError_t>(status));
+  }
+}
+
+const char* qk_build_info(void) {
+  return "libqk ABI " QK_STR(QK_ABI_VERSION) "; code objects: gfx950; HIP " QK_STR(
+      HIP_VERSION_MAJOR) "." QK_STR(HIP_VERSION_MINOR) "." QK_STR(HIP_VERSION_PATCH) "; built " __DATE__
+                                                                                       " " __TIME__;
+}
+
+int qk_quant_per_token(int m, int k, const void* x, int x_dtype, int8_t* q, float* scale,
+                       hipStream_t stream) {
+  const int rc = check_rows(m, k, x, q, scale, x_dtype);
+  if (rc != QK_OK || m == 0) return rc;
+  return status_of(qk::launch_quant_rows(m, k, x, x_dtype, q, scale, stream));
+}
+
+int qk_silu_mul_quant_per_token(int m, int d, const void* h, int h_dtype, int8_t* q,
+                                float* scale, hipStream_t stream) {
+  const int rc = check_rows(m, d, h, q, scale, h_dtype);
+  if (rc != QK_OK || m == 0) return rc;
+  if (static_cast<long long>(d) * 2 > 0x7fffffffLL) return QK_ERR_UNSUPPORTED;
+  return status_of(qk::launch_silu_quant_rows(m, d, h, h_dtype, q, scale, stream));
+}
+
+size_t qk_gemm_workspace_size(int m, int n, int k) {
+  (void)k;
+  if (m <= 0 || n <= 0 || m > qk::kGemvMaxM) return 0;
+  return qk::gemv_workspace_bytes(n);
+}
+
+int qk_gemm_i8_scaled(int m, int n, int k, const int8_t* a, const int8_t* b, int32_t* c,
+                      const float* scale_a, const float* scale_b, float output_scale, void* out,
+                      int out_dtype, int b_layout, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  return gemm_common(m, n, k, a, b, c, scale_a, scale_b, output_scale, out, out_dtype, b_layout,
+                     workspace, workspace_bytes, QK_KERNEL_AUTO, stream);
+}
+
+int qk_gemm_i8_scaled_ex(int m, int n, int k, const int8_t* a, const int8_t* b, int32_t* c,
+                         const float* scale_a, const float* scale_b, float output_scale,
+                         void* out, int out_dtype, int b_layout, void* workspace,
+                         size_t workspace_bytes, int kernel, hipStream_t stream) {
+  return gemm_common(m, n, k, a, b, c, scale_a, scale_b, output_scale, out, out_dtype, b_layout,
+                     workspace, workspace_bytes, kernel, stream);
+}
+
+}  // extern "C"

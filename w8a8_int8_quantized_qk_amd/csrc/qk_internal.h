@@ -1,0 +1,64 @@
+// Internal interface between the C ABI (qk_api.hip) and the kernel files.
+// Nothing here is exported; every launcher returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <tuple>
+#include <utility>
+
+#include "qk.h"
+
+namespace qk {
+
+// Launch `kernel` with arguments converted to its exact parameter types and
+// return the launch status (hipLaunchKernel reports it directly, so no
+// thread-global error state is read or cleared).
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds_bytes,
+                  hipStream_t stream, Args&&... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count mismatch");
+  std::tuple<KArgs...> typed(std::forward<Args>(args)...);
+  return std::apply(
+      [&](auto&... a) {
+        void* argv[] = {static_cast<void*>(&a)...};
+        return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv,
+                               lds_bytes, stream);
+      },
+      typed);
+}
+
+struct GemmArgs {
+  int m, n, k;
+  const int8_t* a;
+  const int8_t* b;
+  int32_t* c;
+  const float* scale_a;
+  const float* scale_b;
+  float output_scale;
+  void* out;
+  int out_dtype;  // QK_F32 | QK_BF16 (ignored when out == nullptr)
+  int b_layout;   // QK_B_KN | QK_B_NK
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+// Per-token quantization, one workgroup per row (quant.hip).
+hipError_t launch_quant_rows(int m, int k, const void* x, int dtype, int8_t* q, float* scale,
+                             hipStream_t stream);
+// silu(gate) * up then per-token quantization, one workgroup per row (quant.hip).
+hipError_t launch_silu_quant_rows(int m, int d, const void* h, int dtype, int8_t* q,
+                                  float* scale, hipStream_t stream);
+
+// LDS-tiled INT8 MFMA GEMM with fused epilogue (gemm_mfma.hip).
+hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
+
+// Split-K decode GEMV for m <= kGemvMaxRows per launch (gemv.hip).
+constexpr int kGemvMaxRows = 8;
+constexpr int kGemvMaxM = 16;  // larger m is split into row groups of kGemvMaxRows
+size_t gemv_workspace_bytes(int n);
+hipError_t launch_gemv(const GemmArgs& g, hipStream_t stream);
+
+}  // namespace qk
