@@ -148,8 +148,9 @@ size_t qk_gemm_workspace_size(int m, int n, int k);
  *            filled before its first use by this library; every call returns
  *            it to all zeros when it completes.  Two calls in flight at the
  *            same time must not share one workspace.
- * Requirements: 0 <= k <= QK_MAX_K and k % 16 == 0; a, b 16-byte aligned
- * (QK_ERR_UNSUPPORTED otherwise).  k == 0 gives acc = 0.
+ * Requirements: 0 <= k <= QK_MAX_K and k % 16 == 0; a, b 16-byte aligned;
+ * for the tiled (m > 8) kernel m*k and n*k below 2^32 (QK_ERR_UNSUPPORTED
+ * otherwise).  k == 0 gives acc = 0.
  */
 int qk_gemm_i8_scaled(int m, int n, int k, const int8_t *a, const int8_t *b, int32_t *c,
                       const float *scale_a, const float *scale_b, float output_scale, void *out,

@@ -5,40 +5,51 @@
 // "Skill: Write an INT8 Quantized Kernel", Inputs):
 //   acc[i][j] = sum_t a[i][t] * B(t, j)        exact INT32
 //   c[i][j]   = acc                            (optional)
-//   out[i][j] = ((float)acc * scale_a[i]) * scale_b[j] * output_scale   (optional)
+//   out[i][j] = ((float)acc * scale_a[i]) * (scale_b[j] * output_scale)   (optional)
 //
 // Design for gfx950:
-//   * Workgroup tile 256 (M) x 128 (N), reduction step 128 bytes of K.  Four
-//     wave64s in a 2 x 2 grid each own a 128 x 64 sub-tile computed with
-//     v_mfma_i32_32x32x32_i8 (4 x 2 instructions per 32-deep k slice, 128
-//     INT32 accumulators per lane).  One tile per CU covers M=2048, N=4096 in
-//     a single wave of 256 workgroups.
-//   * Both operands are staged through LDS, double buffered (2 x 48 KiB):
-//     the next k slice is fetched into registers with 128-bit (A) loads while
-//     the matrix cores work on the current one.
-//   * LDS rows are 128 bytes; the 16-byte chunk index is XORed with a function
-//     of the row so that the eight lanes served together by a 128-bit LDS
-//     access touch eight different chunks, both when a row is written and
-//     when eight consecutive rows are read as MFMA operands.
-//   * MFMA wants 16 consecutive k values per lane for both operands.  A is
-//     [M][K] (k contiguous) and is copied as is.  A weight stored [K][N]
-//     (n contiguous) is loaded as 4-column x 16-row byte blocks and transposed
-//     in registers with v_perm_b32 before it is written to LDS as [N][K];
-//     a weight stored [N][K] is copied like A.
-//   * Rows past M or N re-read the last valid row (results discarded); k past
-//     K loads zeros, so partial k slices add nothing.
+//   * Workgroup tile 256 (M) x 128 (N), k slice 128 bytes.  Four wave64s in a
+//     2 x 2 grid each own a 128 x 64 sub-tile computed with
+//     v_mfma_i32_32x32x32_i8 (4 x 2 instructions per 32-deep k step, 128
+//     INT32 accumulators per lane).  M=2048, N=4096 is 256 tiles: one per CU.
+//   * Operands go from global memory straight into LDS with 128-bit
+//     global_load_lds (no register staging): lane l of a wave writes LDS
+//     bytes [16 l, 16 l + 16) above the wave's base address, so each lane
+//     fetches the global chunk that belongs at its LDS slot.  Three LDS
+//     slices (3 x 48 KiB) let slice s + 2 stream in while slice s is
+//     multiplied; one barrier per slice.
+//   * A (and a weight stored [N][K]) is kept k-contiguous, 128-byte rows with
+//     the 16-byte chunk index XORed by (row & 7) ^ ((row >> 2) & 7): the eight
+//     lanes served together by a 128-bit LDS read see eight distinct chunks.
+//   * A weight stored [K][N] (n contiguous) stays [k][n] in LDS (chunk index
+//     XORed by k & 7) and is read with ds_read_b64_tr_b8: a 16-lane group
+//     reads an 8 (k) x 16 (n) byte block and lane j receives column j's eight
+//     k values, which is the k-contiguous MFMA operand; two such reads give
+//     the 16 bytes of a lane.  No VALU transposes are needed.
+//   * For a [K][N] weight whose N is not a multiple of 16, B falls back to
+//     register staging (dword or byte loads, 4 x 4 byte transposes with
+//     v_perm_b32, LDS writes in the [n][k] layout).
+//   * Rows past M or N re-read a valid row (those outputs are never stored).
+//     When K is not a multiple of 128 the final slice's A chunks at k >= K are
+//     zeroed in LDS before use, so they add nothing.
+//   * Workgroups are dispatched to the 8 XCDs round robin; tiles are renumbered
+//     so the ones running together on one XCD form a compact 4 x 8 block that
+//     shares A rows and B columns in that XCD's L2.
 //   * The epilogue converts each accumulator to binary32 in registers,
 //     multiplies by the per-token and per-channel scales, and stores fp32 or
 //     bf16 (round to nearest even); raw accumulators are stored when asked.
+//   * Operands are addressed with 32-bit offsets (m*k, n*k < 2^32).
 #include "qk_internal.h"
 
 namespace qk {
 namespace {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr int BM = 256;
 constexpr int BN = 128;
 constexpr int BK = 128;
@@ -46,46 +57,83 @@ constexpr int WTM = 128;       // wave tile rows
 constexpr int WTN = 64;        // wave tile columns
 constexpr int FM = WTM / 32;   // 32x32 fragments per wave along M
 constexpr int FN = WTN / 32;   // ... along N
+constexpr int kStages = 3;     // LDS k slices in flight
 constexpr int A_STAGE = BM * BK;
 constexpr int B_STAGE = BN * BK;
-constexpr int A_CHUNKS = BM * BK / 16 / kThreads;  // 16-byte chunks per thread: 8
-constexpr int BNK_CHUNKS = BN * BK / 16 / kThreads;  // 4
+constexpr int STAGE = A_STAGE + B_STAGE;
 
-__device__ __forceinline__ int lds_offset(int row, int chunk) {
-  const int swz = (row & 7) ^ ((row >> 2) & 7);
-  return row * BK + ((chunk ^ swz) << 4);
-}
-
-// ---- A (and a [N][K] weight): 16-byte chunks, 8 consecutive lanes per row ----
-template <int ROWS>
-struct RowTile {
-  static constexpr int kChunks = ROWS * BK / 16 / kThreads;
-  uint4 v[kChunks];
-
-  __device__ void load(const int8_t* __restrict__ p, int rows_valid, int K, int r0, int k0) {
-    const int t = threadIdx.x;
-    const int gk = k0 + (t & 7) * 16;
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int row = (t >> 3) + 32 * i;
-      const int gr = min(r0 + row, rows_valid - 1);
-      if (gk < K)
-        v[i] = *reinterpret_cast<const uint4*>(p + static_cast<size_t>(gr) * K + gk);
-      else
-        v[i] = make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ void store(char* lds) const {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-      const int row = (t >> 3) + 32 * i;
-      *reinterpret_cast<uint4*>(lds + lds_offset(row, t & 7)) = v[i];
-    }
-  }
+enum BMode {
+  kBnkDma = 0,    // weight [N][K], DMA, read like A
+  kBknDma = 1,    // weight [K][N], N % 16 == 0: DMA into [k][n], transpose reads
+  kBknReg4 = 2,   // weight [K][N], N % 4 == 0: dword loads, register transpose
+  kBknReg1 = 3,   // weight [K][N], other N: byte loads, register transpose
 };
 
-// ---- a [K][N] weight: each thread loads 16 k-rows x 4 columns ----
+// k-contiguous tiles (A, [N][K] weight): 128-byte rows
+__device__ __forceinline__ int rowk_offset(int row, int chunk) {
+  return row * BK + ((chunk ^ ((row & 7) ^ ((row >> 2) & 7))) << 4);
+}
+// [k][n] weight tile: 128-byte rows of n
+__device__ __forceinline__ int kn_offset(int k, int chunk) {
+  return k * BN + ((chunk ^ (k & 7)) << 4);
+}
+
+// One 128-bit global-to-LDS load: this lane's 16 bytes at g go to LDS byte
+// lds_base + 16 * lane (lds_base is the wave-uniform LDS address in m0).
+// Written as inline assembly so that the compiler does not treat every later
+// LDS read as possibly aliasing the transfer (which makes it wait for all
+// outstanding loads before each read); completion is tracked explicitly with
+// wait_vmcnt before the barrier that publishes the slice.  The instruction
+// has no register results.  m0 is written here and nowhere else in the kernel.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p)));
+}
+
+// DMA of a k-contiguous tile of ROWS rows x 128 bytes (global rows clamped to
+// rows_valid - 1, k offset clamped into the row).
+template <int ROWS>
+__device__ __forceinline__ void dma_rowk(const int8_t* __restrict__ g, char* lds, int rows_valid,
+                                         int K, int r0, int k0) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  constexpr int kPerWave = ROWS * BK / 1024 / kWaves;
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) {
+    const int blk = wave * kPerWave + i;  // 1 KiB = 8 rows
+    const int row = blk * 8 + (lane >> 3);
+    const int lchunk = (lane & 7) ^ ((row & 7) ^ ((row >> 2) & 7));
+    const uint32_t gr = static_cast<uint32_t>(min(r0 + row, rows_valid - 1));
+    const uint32_t gk = static_cast<uint32_t>(min(k0 + 16 * lchunk, K - 16));
+    lds_dma16(g + (gr * static_cast<uint32_t>(K) + gk), lds_addr(lds + blk * 1024));
+  }
+}
+
+// DMA of a [K][N] weight tile: 128 k rows x 128 bytes of n.
+__device__ __forceinline__ void dma_kn(const int8_t* __restrict__ b, char* lds, int N, int K,
+                                       int n0, int k0) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  constexpr int kPerWave = BK * BN / 1024 / kWaves;
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) {
+    const int blk = wave * kPerWave + i;
+    const int k = blk * 8 + (lane >> 3);
+    const int lchunk = (lane & 7) ^ (k & 7);
+    const uint32_t gk = static_cast<uint32_t>(min(k0 + k, K - 1));
+    const uint32_t gn = static_cast<uint32_t>(min(n0 + 16 * lchunk, N - 16));
+    lds_dma16(b + (gk * static_cast<uint32_t>(N) + gn), lds_addr(lds + blk * 1024));
+  }
+}
+
+// ---- register-staged [K][N] weight (N not a multiple of 16) ----
 __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
                                              uint32_t& c0, uint32_t& c1, uint32_t& c2,
                                              uint32_t& c3) {
@@ -101,31 +149,31 @@ __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c,
 }
 
 template <bool N4>
-struct KnTile {
-  uint32_t v[16];  // v[r] = columns 4cg..4cg+3 of k row 16rg + r
+struct KnRegTile {
+  uint32_t v[16];  // v[r] = columns 4cg..4cg+3 of k row 16rg + r; thread = (cg, rg) = (t%32, t/32)
 
-  __device__ void load(const int8_t* __restrict__ b, int N, int K, int n0, int k0) {
+  __device__ __forceinline__ void load(const int8_t* __restrict__ b, int N, int K, int n0, int k0) {
     const int t = threadIdx.x;
     const int gn = n0 + 4 * (t & 31);
     const int kb = k0 + 16 * (t >> 5);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int gk = kb + r;
-      const int8_t* row = b + static_cast<size_t>(gk) * N;
+      const uint32_t gk = static_cast<uint32_t>(min(kb + r, K - 1));
       if constexpr (N4) {
-        v[r] = (gk < K && gn < N) ? *reinterpret_cast<const uint32_t*>(row + gn) : 0u;
+        const uint32_t gnc = static_cast<uint32_t>(min(gn, N - 4));
+        v[r] = *reinterpret_cast<const uint32_t*>(b + (gk * static_cast<uint32_t>(N) + gnc));
       } else {
+        const int8_t* row = b + gk * static_cast<uint32_t>(N);
         uint32_t w = 0;
-        if (gk < K) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (gn + j < N) w |= (static_cast<uint32_t>(static_cast<uint8_t>(row[gn + j]))) << (8 * j);
-        }
+        for (int j = 0; j < 4; ++j)
+          w |= static_cast<uint32_t>(static_cast<uint8_t>(row[min(gn + j, N - 1)])) << (8 * j);
         v[r] = w;
       }
     }
   }
-  __device__ void store(char* lds) const {
+  // written as k-contiguous [n][k] rows (read like A)
+  __device__ __forceinline__ void store(char* lds) const {
     const int t = threadIdx.x;
     const int cg = t & 31;
     const int rg = t >> 5;
@@ -136,41 +184,104 @@ struct KnTile {
                    col[2][d], col[3][d]);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint4*>(lds + lds_offset(4 * cg + j, rg)) =
+      *reinterpret_cast<uint4*>(lds + rowk_offset(4 * cg + j, rg)) =
           make_uint4(col[j][0], col[j][1], col[j][2], col[j][3]);
   }
+};
+
+struct NoRegTile {
+  __device__ __forceinline__ void load(const int8_t*, int, int, int, int) {}
+  __device__ __forceinline__ void store(char*) const {}
 };
 
 __device__ __forceinline__ uint16_t to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-template <bool B_NK, bool N4>
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  Global-to-LDS loads complete on
+// this counter, so this is how a wave knows its DMA into LDS has landed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+constexpr int kGroupM = 4;
+
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  int b = blockIdx.x;
+  if (T % 8 == 0) b = (b % 8) * (T / 8) + b / 8;
+  const int group_tiles = kGroupM * tiles_n;
+  const int g = b / group_tiles;
+  const int first_m = g * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int r = b - g * group_tiles;
+  tm = first_m + r % gm;
+  tn = r / gm;
+}
+
+template <int MODE, bool KTAIL>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
     const int8_t* __restrict__ a, const int8_t* __restrict__ b, int32_t* __restrict__ c,
     const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
-    void* __restrict__ out, int out_dtype, int M, int N, int K, int tiles_m) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * (A_STAGE + B_STAGE)];
-  char* const As0 = smem;
-  char* const Bs0 = smem + 2 * A_STAGE;
+    void* __restrict__ out, int out_dtype, int M, int N, int K, int tiles_m, int tiles_n) {
+  constexpr bool kRegB = MODE == kBknReg4 || MODE == kBknReg1;
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * STAGE];
 
-  const int tile = blockIdx.x;
-  const int m0 = (tile % tiles_m) * BM;
-  const int n0 = (tile / tiles_m) * BN;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
   const int t = threadIdx.x;
-  const int wave = t >> 6;
   const int lane = t & 63;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = (t >> 6) >> 1;
+  const int wn = (t >> 6) & 1;
 
-  RowTile<BM> at;
-  using BTile = std::conditional_t<B_NK, RowTile<BN>, KnTile<N4>>;
-  BTile bt;
-  auto load_b = [&](int k0) {
-    if constexpr (B_NK)
-      bt.load(b, N, K, n0, k0);
-    else
-      bt.load(b, N, K, n0, k0);
+  auto a_lds = [&](int s) { return smem + (s % kStages) * STAGE; };
+  auto b_lds = [&](int s) { return smem + (s % kStages) * STAGE + A_STAGE; };
+
+  using RegTile = std::conditional_t<MODE == kBknReg4, KnRegTile<true>,
+                                     std::conditional_t<MODE == kBknReg1, KnRegTile<false>, NoRegTile>>;
+  RegTile breg;
+
+  // issue the global reads of k slice s (DMA: straight into its LDS slice)
+  auto fetch = [&](int s) {
+    dma_rowk<BM>(a, a_lds(s), M, K, m0, s * BK);
+    if constexpr (MODE == kBnkDma) dma_rowk<BN>(b, b_lds(s), N, K, n0, s * BK);
+    if constexpr (MODE == kBknDma) dma_kn(b, b_lds(s), N, K, n0, s * BK);
+  };
+  constexpr int kFetchOps = BM * BK / 1024 / kWaves + (kRegB ? 0 : BN * BK / 1024 / kWaves);
+
+  // fragment reads: A (and [N][K] / register-staged B) with 128-bit reads;
+  // a DMA'd [K][N] B with two transpose reads per lane
+  const int a_row = wm * WTM + (lane & 31);
+  const int b_row = wn * WTN + (lane & 31);
+  auto read_frags = [&](const char* As, const char* Bs, int kk, v4i* fa, v4i* fb) {
+    const int chunk = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[i] = *reinterpret_cast<const v4i*>(As + rowk_offset(a_row + i * 32, chunk));
+    if constexpr (MODE == kBknDma) {
+      const int g = lane >> 4;        // 16-lane group
+      const int i16 = lane & 15;
+      const int kr = 32 * kk + 16 * (g >> 1) + (i16 >> 1);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int cb = (wn * WTN + j * 32 + 16 * (g & 1)) >> 4;  // chunk of 16 columns
+        const int half = 8 * (i16 & 1);
+        const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(Bs + kn_offset(kr, cb) + half));
+        const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(Bs + kn_offset(kr + 8, cb) + half));
+        fb[j] = v4i{lo.x, lo.y, hi.x, hi.y};
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        fb[j] = *reinterpret_cast<const v4i*>(Bs + rowk_offset(b_row + j * 32, chunk));
+    }
   };
 
   v16i acc[FM][FN];
@@ -179,75 +290,185 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
 
-  const int KT = (K + BK - 1) / BK;
-  if (KT > 0) {
-    at.load(a, M, K, m0, 0);
-    load_b(0);
-    at.store(As0);
-    bt.store(Bs0);
-  }
-  __syncthreads();
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const char* As = As0 + (kt & 1) * A_STAGE;
-    const char* Bs = Bs0 + (kt & 1) * B_STAGE;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      at.load(a, M, K, m0, (kt + 1) * BK);
-      load_b((kt + 1) * BK);
+  const int KT = (K + BK - 1) / BK;
+
+  // Zero the A chunks of slice s that lie at k >= K (final slice of a K that
+  // is not a multiple of BK), then publish with a barrier.
+  auto zero_tail = [&](int s) {
+    char* Az = a_lds(s);
+#pragma unroll
+    for (int i = 0; i < BM * 8 / kThreads; ++i) {
+      const int row = (t >> 3) + 32 * i;
+      if (s * BK + 16 * (t & 7) >= K)
+        *reinterpret_cast<uint4*>(Az + rowk_offset(row, t & 7)) = make_uint4(0, 0, 0, 0);
     }
+    __syncthreads();
+  };
+
+  v4i af[2][FM], bf[2][FN];
+  if (KT > 0) {
+    fetch(0);
+    if constexpr (kRegB) breg.load(b, N, K, n0, 0);
+    if (KT > 1) fetch(1);
+    if constexpr (kRegB) {
+      wait_vmcnt<0>();
+      breg.store(b_lds(0));
+    } else {
+      if (KT > 1) wait_vmcnt<kFetchOps>(); else wait_vmcnt<0>();
+    }
+    __syncthreads();
+    if (KTAIL && KT == 1) zero_tail(0);
+    read_frags(a_lds(0), b_lds(0), 0, af[0], bf[0]);
+  }
+
+  // Software pipeline, one k slice per iteration (4 MFMA steps of 32 k):
+  //   top:       issue the DMA of slice kt + 2 (its LDS slice was last read
+  //              in iteration kt - 1, before that iteration's barrier);
+  //   steps 0-2: 8 MFMAs on the fragments in registers, interleaved with the
+  //              LDS reads of the next step's fragments;
+  //   step 3:    wait for this wave's DMA of slice kt + 1, barrier (all waves'
+  //              DMA has landed and all reads of slice kt are done), then the
+  //              last 8 MFMAs interleaved with the reads of slice kt + 1's
+  //              first step.
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 2 < KT) fetch(kt + 2);
+    if constexpr (kRegB) {
+      if (kt + 1 < KT) breg.load(b, N, K, n0, (kt + 1) * BK);
+    }
+    const char* As = a_lds(kt);
+    const char* Bs = b_lds(kt);
 #pragma unroll
     for (int kk = 0; kk < BK / 32; ++kk) {
-      const int chunk = 2 * kk + (lane >> 5);
-      v4i af[FM], bf[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const v4i*>(As + lds_offset(wm * WTM + i * 32 + (lane & 31), chunk));
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bf[j] = *reinterpret_cast<const v4i*>(Bs + lds_offset(wn * WTN + j * 32 + (lane & 31), chunk));
+      const int cur = kk & 1;
+      const int nxt = cur ^ 1;
+      if (kk + 1 < BK / 32) {
+        read_frags(As, Bs, kk + 1, af[nxt], bf[nxt]);
+      } else if (kt + 1 < KT) {
+        if constexpr (kRegB) {
+          wait_vmcnt<0>();
+          breg.store(b_lds(kt + 1));
+        } else {
+          if (kt + 2 < KT) wait_vmcnt<kFetchOps>(); else wait_vmcnt<0>();
+        }
+        __syncthreads();
+        if (KTAIL && kt + 1 == KT - 1) zero_tail(kt + 1);
+        read_frags(a_lds(kt + 1), b_lds(kt + 1), 0, af[nxt], bf[nxt]);
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[cur][j], acc[i][j], 0,
+                                                            0, 0);
+      // issue order: two LDS reads, one MFMA, ... then the remaining MFMAs
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    if (more) {
-      at.store(As0 + ((kt + 1) & 1) * A_STAGE);
-      bt.store(Bs0 + ((kt + 1) & 1) * B_STAGE);
-    }
-    __syncthreads();
   }
 
-  // epilogue: lane owns column (lane & 31) of each fragment and rows
-  // 8 * (r / 4) + 4 * (lane / 32) + r % 4 for accumulator register r
+  // ---- epilogue ----
+  // Each wave stages its raw 128 x 64 INT32 tile in LDS (row stride padded by
+  // 16 bytes), then streams it out row by row: eight lanes cover one row's 64
+  // columns, each converting 8 accumulators with the per-token and
+  // per-channel scales and writing 16 (bf16) or 32 (fp32) contiguous bytes.
+  constexpr int kRowStride = WTN * 4 + 16;
+  static_assert(kWaves * WTM * kRowStride <= kStages * STAGE, "epilogue staging fits in LDS");
+  __syncthreads();  // every wave is done with the k slices
+  char* stage = smem + (t >> 6) * (WTM * kRowStride);
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int col = n0 + wn * WTN + j * 32 + (lane & 31);
-    if (col >= N) continue;
-    const float sb = out ? scale_b[col] * output_scale : 0.0f;
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= M) continue;
-        const int v = acc[i][j][r];
-        const size_t idx = static_cast<size_t>(row) * N + col;
-        if (c) c[idx] = v;
-        if (out) {
-          const float f = (static_cast<float>(v) * scale_a[row]) * sb;
-          if (out_dtype == QK_BF16)
-            static_cast<uint16_t*>(out)[idx] = to_bf16(f);
-          else
-            static_cast<float*>(out)[idx] = f;
+        const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = j * 32 + (lane & 31);
+        *reinterpret_cast<int*>(stage + row * kRowStride + col * 4) = acc[i][j][r];
+      }
+  // a wave reads back only what it wrote; waiting on its own LDS writes suffices
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  const int tile_r0 = m0 + wm * WTM;
+  const int cg = lane & 7;  // 8-column group
+  const int gcol = n0 + wn * WTN + 8 * cg;
+  const bool vec_ok = (N % 8 == 0) && (gcol + 8 <= N);
+  float sb[8];
+  if (out) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sb[e] = gcol + e < N ? scale_b[gcol + e] * output_scale : 0.0f;
+  }
+#pragma unroll 4
+  for (int it = 0; it < WTM * 8 / 64; ++it) {
+    const int row = 8 * it + (lane >> 3);
+    const int grow = tile_r0 + row;
+    if (grow >= M) continue;
+    const int4 v0 = *reinterpret_cast<const int4*>(stage + row * kRowStride + cg * 32);
+    const int4 v1 = *reinterpret_cast<const int4*>(stage + row * kRowStride + cg * 32 + 16);
+    const int v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const size_t base = static_cast<size_t>(grow) * N + gcol;
+    if (c) {
+      if (vec_ok) {
+        *reinterpret_cast<int4*>(c + base) = v0;
+        *reinterpret_cast<int4*>(c + base + 4) = v1;
+      } else {
+        for (int e = 0; e < 8; ++e)
+          if (gcol + e < N) c[base + e] = v[e];
+      }
+    }
+    if (out) {
+      const float sa = scale_a[grow];
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = (static_cast<float>(v[e]) * sa) * sb[e];
+      if (out_dtype == QK_BF16) {
+        uint16_t* o = static_cast<uint16_t*>(out) + base;
+        if (vec_ok) {
+          uint4 w;
+          w.x = to_bf16(f[0]) | (static_cast<uint32_t>(to_bf16(f[1])) << 16);
+          w.y = to_bf16(f[2]) | (static_cast<uint32_t>(to_bf16(f[3])) << 16);
+          w.z = to_bf16(f[4]) | (static_cast<uint32_t>(to_bf16(f[5])) << 16);
+          w.w = to_bf16(f[6]) | (static_cast<uint32_t>(to_bf16(f[7])) << 16);
+          *reinterpret_cast<uint4*>(o) = w;
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (gcol + e < N) o[e] = to_bf16(f[e]);
+        }
+      } else {
+        float* o = static_cast<float*>(out) + base;
+        if (vec_ok) {
+          *reinterpret_cast<float4*>(o) = make_float4(f[0], f[1], f[2], f[3]);
+          *reinterpret_cast<float4*>(o + 4) = make_float4(f[4], f[5], f[6], f[7]);
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (gcol + e < N) o[e] = f[e];
         }
       }
     }
   }
 }
 
+template <int MODE>
+hipError_t launch_mode(const GemmArgs& g, dim3 grid, int tiles_m, int tiles_n,
+                       hipStream_t stream) {
+  if (g.k % BK != 0)
+    return launch(gemm_i8_mfma_kernel<MODE, true>, grid, dim3(kThreads), 0, stream, g.a, g.b, g.c,
+                  g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k,
+                  tiles_m, tiles_n);
+  return launch(gemm_i8_mfma_kernel<MODE, false>, grid, dim3(kThreads), 0, stream, g.a, g.b, g.c,
+                g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k, tiles_m,
+                tiles_n);
+}
+
 }  // namespace
+
+bool gemm_mfma_supported(int m, int n, int k) {
+  return static_cast<unsigned long long>(m) * k < (1ull << 32) &&
+         static_cast<unsigned long long>(n) * k < (1ull << 32);
+}
 
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream) {
   const int tiles_m = (g.m + BM - 1) / BM;
@@ -255,15 +476,10 @@ hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream) {
   const long long tiles = static_cast<long long>(tiles_m) * tiles_n;
   if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(tiles));
-  const dim3 block(kThreads);
-  if (g.b_layout == QK_B_NK)
-    return launch(gemm_i8_mfma_kernel<true, true>, grid, block, 0, stream, g.a, g.b, g.c,
-                  g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k, tiles_m);
-  if (g.n % 4 == 0)
-    return launch(gemm_i8_mfma_kernel<false, true>, grid, block, 0, stream, g.a, g.b, g.c,
-                  g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k, tiles_m);
-  return launch(gemm_i8_mfma_kernel<false, false>, grid, block, 0, stream, g.a, g.b, g.c,
-                g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k, tiles_m);
+  if (g.b_layout == QK_B_NK) return launch_mode<kBnkDma>(g, grid, tiles_m, tiles_n, stream);
+  if (g.n % 16 == 0) return launch_mode<kBknDma>(g, grid, tiles_m, tiles_n, stream);
+  if (g.n % 4 == 0) return launch_mode<kBknReg4>(g, grid, tiles_m, tiles_n, stream);
+  return launch_mode<kBknReg1>(g, grid, tiles_m, tiles_n, stream);
 }
 
 }  // namespace qk

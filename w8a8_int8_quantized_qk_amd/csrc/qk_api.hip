@@ -57,6 +57,7 @@ int gemm_common(int m, int n, int k, const int8_t* a, const int8_t* b, int32_t* 
       return QK_ERR_WORKSPACE;
     return status_of(qk::launch_gemv(g, stream));
   }
+  if (!qk::gemm_mfma_supported(m, n, k)) return QK_ERR_UNSUPPORTED;
   return status_of(qk::launch_gemm_mfma(g, stream));
 }
 

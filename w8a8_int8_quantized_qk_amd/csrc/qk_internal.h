@@ -52,7 +52,9 @@ hipError_t launch_quant_rows(int m, int k, const void* x, int dtype, int8_t* q, 
 hipError_t launch_silu_quant_rows(int m, int d, const void* h, int dtype, int8_t* q,
                                   float* scale, hipStream_t stream);
 
-// LDS-tiled INT8 MFMA GEMM with fused epilogue (gemm_mfma.hip).
+// LDS-tiled INT8 MFMA GEMM with fused epilogue (gemm_mfma.hip).  Operands
+// are addressed with 32-bit offsets: m*k and n*k must stay below 2^32.
+bool gemm_mfma_supported(int m, int n, int k);
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
 
 // Split-K decode GEMV for m <= kGemvMaxRows per launch (gemv.hip).
