@@ -8,7 +8,10 @@ measured in the same run: HBM GB/s of the decode linear at M = 1 (X bf16
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 Each step uses the next of R buffer sets (R x ~59 MB > the 256 MB Infinity
-Cache plus L2), so weights and activations come from HBM, not cache.
+Cache plus L2), so weights and activations come from HBM, not cache.  Steps
+are captured in HIP graphs and replayed, so the GPU is not left waiting for
+per-launch Python work; exactly K steps are timed with HIP events on the
+replay stream.
 
 Prints one JSON line (rank 0; one GPU only).
 """
@@ -82,7 +85,48 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    lib = qk.library()
+    qk.library()
+    stream = torch.cuda.Stream(dev)  # default priority (capture needs a non-default stream)
+
+    def timed_replays(step_fns, k_steps, warmup):
+        """Capture one HIP graph per buffer set (one step each) plus one graph of
+        a whole ring, then run exactly k_steps steps by replay and time them with
+        HIP events on the replay stream.  Returns (ms per step, wall seconds)."""
+        R = len(step_fns)
+        with torch.cuda.stream(stream):
+            for f in step_fns:  # eager warm-up: first-use setup stays out of capture
+                f()
+        torch.cuda.synchronize()
+        singles = []
+        for f in step_fns:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                f()
+            singles.append(g)
+        ring = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ring, stream=stream):
+            for f in step_fns:
+                f()
+        torch.cuda.synchronize()
+
+        def run(n):
+            with torch.cuda.stream(stream):
+                for _ in range(n // R):
+                    ring.replay()
+                for i in range(n % R):
+                    singles[i].replay()
+
+        run(warmup)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        run(k_steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / k_steps, wall
 
     # ---------------- prefill: quant + GEMM (headline) ----------------
     wcfg = wl.WORKLOADS["prefill_outliers"]
@@ -97,28 +141,22 @@ def main():
             "s": torch.empty((m,), dtype=torch.float32, device=dev),
             "out": torch.empty((m, n), dtype=torch.bfloat16, device=dev),
         })
-    stream = torch.cuda.current_stream(dev)
 
-    def step(bs, ev=None):
-        qk.quant_per_token(bs["x"], bs["q"], bs["s"])
-        if ev is not None:
-            ev[0].record(stream)
-        qk.gemm_i8_scaled(bs["q"], bs["w"], bs["s"], bs["s_ch"], out=bs["out"])
-        if ev is not None:
-            ev[1].record(stream)
+    def step_fn(bs):
+        def f():
+            qk.quant_per_token(bs["x"], bs["q"], bs["s"])
+            qk.gemm_i8_scaled(bs["q"], bs["w"], bs["s"], bs["s_ch"], out=bs["out"])
+        return f
 
-    for i in range(args.warmup):
-        step(sets[i % args.ring])
-    torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(sets[i % args.ring], events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
-    ms_per_step = wall * 1e3 / args.steps
+    def gemm_fn(bs):
+        return lambda: qk.gemm_i8_scaled(bs["q"], bs["w"], bs["s"], bs["s_ch"], out=bs["out"])
+
+    def quant_fn(bs):
+        return lambda: qk.quant_per_token(bs["x"], bs["q"], bs["s"])
+
+    ms_per_step, wall = timed_replays([step_fn(b) for b in sets], args.steps, args.warmup)
+    gemm_ms, _ = timed_replays([gemm_fn(b) for b in sets], args.steps, args.warmup)
+    quant_ms, _ = timed_replays([quant_fn(b) for b in sets], args.steps, args.warmup)
     ops = 2.0 * m * n * k
     tops = ops / (ms_per_step * 1e-3) / 1e12
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
@@ -139,65 +177,49 @@ def main():
         "data": "synthetic",
         "config": {"workload": "prefill_outliers", "m": m, "k": k, "n": n, "x_dtype": "bf16",
                    "w_layout": "[K,N]", "out_dtype": "bf16", "outlier_cols": wcfg.outlier_cols,
-                   "ring_sets": args.ring, "step": "qk_quant_per_token + qk_gemm_i8_scaled"},
+                   "ring_sets": args.ring,
+                   "step": "qk_quant_per_token + qk_gemm_i8_scaled, replayed from HIP graphs"},
         "roofline": {"bound": "mfma", "kernel": "gemm_i8_mfma_kernel",
                      "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                      "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
                      "traffic": traffic, "avg_launch_us": round(gemm_ms * 1e3, 3),
                      "algorithmic_ops_per_launch": ops},
         "step_frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+        "quant_kernel_us": round(quant_ms * 1e3, 3),
+        "wall_s_timed_region": round(wall, 4),
     }
 
     # ---------------- decode: M = 1 linear (second metric) ----------------
     if not args.no_decode:
         dcfg = wl.WORKLOADS["decode_m1"]
         dm, dk, dn = dcfg.m, dcfg.k, dcfg.n
+        ws = torch.zeros(qk.gemm_workspace_size(dm, dn, dk), dtype=torch.uint8, device=dev)
         dsets = []
         for r in range(args.ring):
             d = wl.generate(dcfg, seed=r)
             dsets.append({
                 "x": d["x"].to(dev), "w": torch.from_numpy(d["w"]).to(dev),
                 "s_ch": torch.from_numpy(d["s_ch"]).to(dev),
-                "q": torch.empty((dm, dk), dtype=torch.int8, device=dev),
-                "s": torch.empty((dm,), dtype=torch.float32, device=dev),
                 "out": torch.empty((dm, dn), dtype=torch.bfloat16, device=dev),
             })
-        ws = torch.zeros(qk.gemm_workspace_size(dm, dn, dk), dtype=torch.uint8, device=dev)
 
-        def dstep(bs, ev=None):
-            qk.quant_per_token(bs["x"], bs["q"], bs["s"])
-            if ev is not None:
-                ev[0].record(stream)
-            qk.gemm_i8_scaled(bs["q"], bs["w"], bs["s"], bs["s_ch"], out=bs["out"], workspace=ws)
-            if ev is not None:
-                ev[1].record(stream)
+        def dstep_fn(bs):
+            return lambda: qk.linear_w8a8(bs["x"], bs["w"], bs["s_ch"], out=bs["out"], workspace=ws)
 
-        for i in range(args.warmup):
-            dstep(dsets[i % args.ring])
-        torch.cuda.synchronize()
-        dev_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                      for _ in range(args.decode_calls)]
-        t0 = time.perf_counter()
-        for i in range(args.decode_calls):
-            dstep(dsets[i % args.ring], dev_events[i])
-        torch.cuda.synchronize()
-        dwall = time.perf_counter() - t0
-        gemv_ms = float(np.mean([a.elapsed_time(b) for a, b in dev_events]))
-        call_us = dwall * 1e6 / args.decode_calls
+        dms, _ = timed_replays([dstep_fn(b) for b in dsets], args.decode_calls, args.warmup)
         dbytes = dk * dn + 4 * dn + 2 * dm * dk + 2 * dm * dn
-        gemv_bytes = dk * dn + 4 * dn + dm * dk + 4 * dm + 2 * dm * dn
+        gbs = dbytes / (dms * 1e-3) / 1e9
         result["decode"] = {
-            "metric": "HBM GB/s at decode M=1 (quant + GEMV call)",
+            "metric": "HBM GB/s at decode M=1 (quantization + GEMV in one launch)",
             "workload": "decode_m1", "m": dm, "k": dk, "n": dn,
-            "value": round(dbytes / (call_us * 1e-6) / 1e9, 1), "unit": "GB/s",
-            "us_per_call": round(call_us, 3), "algorithmic_bytes_per_call": dbytes,
-            "frac_of_hbm_peak": round(dbytes / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "roofline": {"bound": "hbm", "kernel": "gemv_i8_splitk_kernel",
-                         "achieved": round(gemv_bytes / (gemv_ms * 1e-3) / 1e9, 1),
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gemv_bytes / (gemv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                         "avg_launch_us": round(gemv_ms * 1e3, 3),
-                         "algorithmic_bytes_per_launch": gemv_bytes, "traffic": None},
+            "value": round(gbs, 1), "unit": "GB/s",
+            "us_per_call": round(dms * 1e3, 3), "algorithmic_bytes_per_call": dbytes,
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "roofline": {"bound": "hbm", "kernel": "gemv_kernel (fused quantization)",
+                         "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "avg_launch_us": round(dms * 1e3, 3),
+                         "algorithmic_bytes_per_launch": dbytes, "traffic": None},
         }
 
     if args.copy_calibration:

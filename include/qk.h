@@ -61,15 +61,15 @@ extern "C" {
 #define QK_B_NK 1 /* b is [n][k], k contiguous */
 
 /* GEMM kernel choice for qk_gemm_i8_scaled_ex */
-#define QK_KERNEL_AUTO 0 /* by shape: decode GEMV for m <= 16, MFMA tiles otherwise */
+#define QK_KERNEL_AUTO 0 /* by shape: decode GEMV for m <= 8, MFMA tiles otherwise */
 #define QK_KERNEL_MFMA 1 /* LDS-tiled INT8 MFMA kernel, any m */
-#define QK_KERNEL_GEMV 2 /* split-K decode kernel, m <= 16 only */
+#define QK_KERNEL_GEMV 2 /* split-K decode GEMV: m <= 16, [k][n] weight */
 
 /* status codes */
 #define QK_OK 0
 #define QK_ERR_INVALID_VALUE 1001 /* negative size, NULL pointer, unknown enum */
 #define QK_ERR_UNSUPPORTED 1002   /* a size or alignment this library does not handle */
-#define QK_ERR_WORKSPACE 1003     /* workspace missing or smaller than required */
+#define QK_ERR_WORKSPACE 1003     /* workspace missing, misaligned or too small */
 
 /* Largest reduction length accepted: 131071 * 128 * 128 < 2^31, so no int32
  * accumulator can overflow even for -128 operands ("Skill: Write an INT8
@@ -120,9 +120,9 @@ int qk_quant_per_token(int m, int k, const void *x, int x_dtype, int8_t *q, floa
 int qk_silu_mul_quant_per_token(int m, int d, const void *h, int h_dtype, int8_t *q,
                                 float *scale, hipStream_t stream);
 
-/* Bytes of workspace qk_gemm_i8_scaled needs for this shape (0 if none).  The
- * decode kernel (m <= 16) keeps exact INT32 split-K partial sums and arrival
- * counters there. */
+/* Bytes of workspace qk_gemm_i8_scaled / qk_linear_w8a8 need for this shape
+ * (0 if none).  The decode kernel (m <= 16) adds exact INT32 split-K partial
+ * sums there and counts arriving workgroups; the tiled kernel needs none. */
 size_t qk_gemm_workspace_size(int m, int n, int k);
 
 /*
@@ -145,9 +145,11 @@ size_t qk_gemm_workspace_size(int m, int n, int k);
  *            not both be NULL.
  *   workspace / workspace_bytes: device memory of at least
  *            qk_gemm_workspace_size(m, n, k) bytes, 256-byte aligned, zero
- *            filled before its first use by this library; every call returns
- *            it to all zeros when it completes.  Two calls in flight at the
- *            same time must not share one workspace.
+ *            filled before its first use by this library; every call
+ *            returns it to all zeros when it completes, so one buffer serves
+ *            all calls issued in order on a stream.  Calls that can run at
+ *            the same time must not share one.  May be NULL when the size is 0
+ *            (QK_ERR_WORKSPACE otherwise).
  * Requirements: 0 <= k <= QK_MAX_K and k % 16 == 0; a, b 16-byte aligned;
  * for the tiled (m > 8) kernel m*k and n*k below 2^32 (QK_ERR_UNSUPPORTED
  * otherwise).  k == 0 gives acc = 0.
@@ -158,12 +160,35 @@ int qk_gemm_i8_scaled(int m, int n, int k, const int8_t *a, const int8_t *b, int
                       hipStream_t stream);
 
 /* As qk_gemm_i8_scaled with an explicit kernel choice (QK_KERNEL_*), so that
- * both kernels can be checked at any shape.  QK_KERNEL_GEMV requires
- * m <= 16 (QK_ERR_UNSUPPORTED otherwise). */
+ * both kernels can be checked at any shape.  QK_KERNEL_GEMV requires m <= 16
+ * and a [k][n] weight (QK_ERR_UNSUPPORTED otherwise). */
 int qk_gemm_i8_scaled_ex(int m, int n, int k, const int8_t *a, const int8_t *b, int32_t *c,
                          const float *scale_a, const float *scale_b, float output_scale,
                          void *out, int out_dtype, int b_layout, void *workspace,
                          size_t workspace_bytes, int kernel, hipStream_t stream);
+
+/*
+ * The whole layer: per-token quantization of x, the INT8 GEMM and the
+ * dequant epilogue (same arithmetic as qk_quant_per_token followed by
+ * qk_gemm_i8_scaled with scale_a = the per-token scales).
+ *   x        [m][k] of x_dtype (QK_F32, QK_BF16, QK_F16).
+ *   b        [k][n] (QK_B_KN) or [n][k] (QK_B_NK) int8; scale_b [n] float.
+ *   out      [m][n] of out_dtype (QK_F32 or QK_BF16).
+ *   q_out, scale_out: [m][k] int8 codes and [m] scales.  Optional when the
+ *            call runs as one fused decode launch (m <= 8, [k][n] weight,
+ *            x 16-byte aligned, kernel AUTO or GEMV); then they receive the
+ *            codes and scales if given.  Required otherwise: they hold the
+ *            intermediate between the two launches.
+ *   workspace / workspace_bytes: as for qk_gemm_i8_scaled (used by the
+ *            fused decode launch).
+ *   kernel   QK_KERNEL_AUTO, QK_KERNEL_GEMV (fused, m <= 16) or
+ *            QK_KERNEL_MFMA (quantization launch + tiled GEMM).
+ * Requirements and errors as qk_quant_per_token and qk_gemm_i8_scaled.
+ */
+int qk_linear_w8a8(int m, int n, int k, const void *x, int x_dtype, const int8_t *b,
+                   const float *scale_b, float output_scale, void *out, int out_dtype,
+                   int b_layout, int8_t *q_out, float *scale_out, void *workspace,
+                   size_t workspace_bytes, int kernel, hipStream_t stream);
 
 #ifdef __cplusplus
 }

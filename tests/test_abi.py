@@ -76,10 +76,11 @@ def test_missing_library_raises(tmp_path):
 
 
 def test_workspace_size(lib):
-    assert qk.gemm_workspace_size(2048, 4096, 4096) == 0        # MFMA path needs none
+    assert qk.gemm_workspace_size(2048, 4096, 4096) == 0        # tiled kernel needs none
     ws = qk.gemm_workspace_size(1, 14336, 4096)
     assert ws >= 8 * 14336 * 4 and ws % 256 == 0
     assert qk.gemm_workspace_size(16, 100, 16) > 0
+    assert qk.gemm_workspace_size(17, 100, 16) == 0
     assert qk.gemm_workspace_size(0, 100, 16) == 0
 
 
@@ -129,6 +130,29 @@ def test_quant_argument_errors_are_reported_before_launch(lib):
     assert lib.qk_quant_per_token(0, 4, NULL, 0, NULL, NULL, NULL) == 0
     assert lib.qk_silu_mul_quant_per_token(4, 4, FAKE, 3, FAKE, FAKE, NULL) == INVALID
     assert lib.qk_silu_mul_quant_per_token(0, 4, NULL, 1, NULL, NULL, NULL) == 0
+
+
+def _linear(lib, m, n, k, x=FAKE, xdt=1, b=FAKE, sb=FAKE, out=FAKE, odt=1, layout=0, q=NULL,
+            s=NULL, ws=NULL, ws_bytes=0, kernel=0):
+    return lib.qk_linear_w8a8(m, n, k, x, xdt, b, sb, 1.0, out, odt, layout, q, s, ws, ws_bytes,
+                              kernel, NULL)
+
+
+def test_linear_argument_errors_are_reported_before_launch(lib):
+    c = _header_constants()
+    INVALID, UNSUP = c["QK_ERR_INVALID_VALUE"], c["QK_ERR_UNSUPPORTED"]
+    assert _linear(lib, -1, 4, 16) == INVALID
+    assert _linear(lib, 4, 4, 16, xdt=7) == INVALID
+    assert _linear(lib, 4, 4, 16, odt=2) == INVALID
+    assert _linear(lib, 4, 4, 24) == UNSUP
+    assert _linear(lib, 4, 4, 16, out=NULL) == INVALID
+    assert _linear(lib, 4, 4, 16, sb=NULL) == INVALID
+    assert _linear(lib, 4, 4, 16, b=FAKE_ODD) == UNSUP
+    assert _linear(lib, 64, 4, 16) == INVALID              # tiled path needs q and scale
+    assert _linear(lib, 4, 4, 16, layout=1) == INVALID     # [n][k] weight: tiled path too
+    assert _linear(lib, 17, 4, 16, kernel=2) == UNSUP
+    assert _linear(lib, 4, 4, 16) == c["QK_ERR_WORKSPACE"]  # fused decode launch needs one
+    assert _linear(lib, 0, 4, 16, x=NULL, b=NULL) == 0
 
 
 def test_binding_rejects_cpu_tensors():

@@ -216,10 +216,12 @@ def test_gemm_output_scale(kernel):
 
 @pytest.mark.parametrize("kernel", ["mfma", "gemv"])
 def test_gemm_int32_closed_forms(kernel):
-    # K * 127 * 127 at K = 65536, and K * (-128) * (-128) at the largest
-    # K (multiple of 16) the library accepts: both fit in int32 exactly
-    for k, av, bv in ((65536, 127, 127), (65536, 127, -127), (131056, -128, -128)):
-        a = torch.full((2, k), av, dtype=torch.int8, device=DEV)
+    # K * a * b with constant operands: K = 65536 at |q| <= 127, and -128 * -128
+    # at the largest K accepted (the largest multiple of 16 below QK_MAX_K)
+    kmax = 131056
+    m = 2
+    for k, av, bv in ((65536, 127, 127), (65536, 127, -127), (kmax, -128, -128)):
+        a = torch.full((m, k), av, dtype=torch.int8, device=DEV)
         b = torch.full((k, 64), bv, dtype=torch.int8, device=DEV)
         c = qk.gemm_i8_scaled(a, b, out_dtype=None, kernel=kernel)
         assert bool((c == k * av * bv).all()), (kernel, k, av, bv)
@@ -257,7 +259,7 @@ def test_gemm_repeatable_and_workspace_left_zero():
     outs = [qk.gemm_i8_scaled(q, w, s, s_ch, return_acc=True, kernel="gemv", workspace=ws)
             for _ in range(3)]
     torch.cuda.synchronize()
-    assert not ws.any()
+    assert not ws.any()  # the decode kernel leaves its workspace zero
     for o, c in outs[1:]:
         assert torch.equal(c, outs[0][1]) and torch.equal(o.view(torch.int16),
                                                           outs[0][0].view(torch.int16))
@@ -334,3 +336,78 @@ def test_workload_end_to_end(name):
     outf = torch.from_numpy(out_h.view(np.int16)).view(torch.bfloat16).float().numpy() \
         if w_cfg.out_dtype == "bf16" else out_h
     assert np.all(np.abs(outf.astype(np.float64)) <= bound * (1 + 2.0 ** -7) + 1e-30)
+
+
+# --------------------------------------------------------------------------
+# the whole layer in one call (fused decode launch, or quantization + tiled GEMM)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,k,n", [(1, 64, 64), (1, 4096, 1000), (3, 272, 130), (8, 512, 2048),
+                                   (11, 1024, 320), (16, 256, 64), (40, 512, 256)])
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("kernel", ["auto", "gemv", "mfma"])
+def test_linear_entry_point(m, k, n, x_dtype, kernel):
+    if kernel == "gemv" and m > 16:
+        pytest.skip("decode kernel takes m <= 16")
+    rng = np.random.default_rng(_seed("lin", m, k, n, x_dtype))
+    x = wl.random_activations(rng, m, k, x_dtype, outlier_cols=max(1, k // 100))
+    w = wl.random_weight(rng, k, n)
+    s_ch = wl.random_channel_scales(rng, n)
+    out_dtype = "f32" if m % 2 else "bf16"
+    out, q, s = qk.linear_w8a8(x.to(DEV), torch.from_numpy(w).to(DEV), torch.from_numpy(s_ch).to(DEV),
+                               TORCH_OUT[out_dtype], kernel=kernel, return_codes=True)
+    q_ref, s_ref, c_ref, out_ref = oracle.linear(wl.bits(x), DTYPE_CODE[x_dtype], w, s_ch)
+    what = f"linear {m}x{k}x{n} {x_dtype} {kernel}"
+    assert_equal_exact(host(s), s_ref, f"{what} scale")
+    assert_equal_exact(host(q), q_ref, f"{what} codes")
+    assert_out_close(host(out), out_ref, out_dtype, what)
+    # without the optional code outputs (the fused launch then writes none)
+    out2 = qk.linear_w8a8(x.to(DEV), torch.from_numpy(w).to(DEV), torch.from_numpy(s_ch).to(DEV),
+                          TORCH_OUT[out_dtype], kernel=kernel)
+    assert np.array_equal(host(out2).view(np.uint8), host(out).view(np.uint8))
+
+
+@pytest.mark.parametrize("name", ["decode_m1", "decode_m8"])
+def test_linear_decode_workloads(name):
+    d = wl.generate(name)
+    wcfg = d["workload"]
+    out = qk.linear_w8a8(d["x"].to(DEV), torch.from_numpy(d["w"]).to(DEV),
+                         torch.from_numpy(d["s_ch"]).to(DEV), TORCH_OUT[wcfg.out_dtype])
+    q_ref, s_ref, c_ref, out_ref = oracle.linear(wl.bits(d["x"]), DTYPE_CODE[wcfg.x_dtype], d["w"],
+                                                 d["s_ch"])
+    assert_out_close(host(out), out_ref, wcfg.out_dtype, name)
+
+
+def test_hip_graph_replays_match_eager():
+    # capture the decode linear (which uses the self-cleaning workspace) and a
+    # prefill quant + GEMM; replay several times with eager work in between
+    dec = wl.generate("decode_m8")
+    pre = wl.generate(wl.Workload("pre_small", 300, 1024, 512, "bf16", "bf16", outlier_cols=10))
+    xd, wd, sd = dec["x"].to(DEV), torch.from_numpy(dec["w"]).to(DEV), torch.from_numpy(dec["s_ch"]).to(DEV)
+    xp, wp, sp = pre["x"].to(DEV), torch.from_numpy(pre["w"]).to(DEV), torch.from_numpy(pre["s_ch"]).to(DEV)
+    ws = torch.zeros(qk.gemm_workspace_size(8, wd.shape[1], wd.shape[0]), dtype=torch.uint8, device=DEV)
+    out_d = torch.empty((8, wd.shape[1]), dtype=torch.bfloat16, device=DEV)
+    q = torch.empty((300, 1024), dtype=torch.int8, device=DEV)
+    s = torch.empty((300,), dtype=torch.float32, device=DEV)
+    out_p = torch.empty((300, 512), dtype=torch.bfloat16, device=DEV)
+    ref_d = qk.linear_w8a8(xd, wd, sd, workspace=ws).clone()
+    qr, sr = qk.quant_per_token(xp)
+    ref_p = qk.gemm_i8_scaled(qr, wp, sr, sp).clone()
+    stream = torch.cuda.Stream(DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        qk.linear_w8a8(xd, wd, sd, out=out_d, workspace=ws)
+        qk.quant_per_token(xp, q, s)
+        qk.gemm_i8_scaled(q, wp, s, sp, out=out_p)
+    for rep in range(4):
+        out_d.zero_()
+        out_p.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_d.view(torch.int16), ref_d.view(torch.int16)), rep
+        assert torch.equal(out_p.view(torch.int16), ref_p.view(torch.int16)), rep
+        # eager work on the same workspace between replays
+        again = qk.linear_w8a8(xd, wd, sd, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16), ref_d.view(torch.int16))
+    assert not ws.any()

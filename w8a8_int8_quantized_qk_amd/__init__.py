@@ -37,7 +37,7 @@ _KERNELS = {"auto": KERNEL_AUTO, "mfma": KERNEL_MFMA, "gemv": KERNEL_GEMV}
 EXPORTED = (
     "qk_abi_version", "qk_status_string", "qk_build_info", "qk_quant_per_token",
     "qk_silu_mul_quant_per_token", "qk_gemm_workspace_size", "qk_gemm_i8_scaled",
-    "qk_gemm_i8_scaled_ex",
+    "qk_gemm_i8_scaled_ex", "qk_linear_w8a8",
 )
 
 
@@ -72,6 +72,8 @@ def _declare(lib):
     lib.qk_gemm_i8_scaled.restype = I
     lib.qk_gemm_i8_scaled_ex.argtypes = gemm + [I, P]
     lib.qk_gemm_i8_scaled_ex.restype = I
+    lib.qk_linear_w8a8.argtypes = [I, I, I, P, I, P, P, F, P, I, I, P, P, P, ctypes.c_size_t, I, P]
+    lib.qk_linear_w8a8.restype = I
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -255,10 +257,48 @@ def gemm_i8_scaled(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor | Non
 
 def linear_w8a8(x: torch.Tensor, w: torch.Tensor, s_ch: torch.Tensor,
                 out_dtype: torch.dtype = torch.bfloat16, b_layout: str = "kn",
-                output_scale: float = 1.0, kernel: str = "auto"):
-    """Per-token quantization of x, then the INT8 GEMM with dequant."""
-    q, s = quant_per_token(x)
-    return gemm_i8_scaled(q, w, s, s_ch, output_scale, out_dtype, b_layout, kernel=kernel)
+                output_scale: float = 1.0, kernel: str = "auto", out: torch.Tensor | None = None,
+                q: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                return_codes: bool = False, workspace: torch.Tensor | None = None):
+    """The whole layer in one call: per-token quantization of x, INT8 GEMM, dequant.
+
+    Decode shapes (m <= 8, [k, n] weight) run as one fused launch.  Otherwise
+    the codes and scales go through q / scale (allocated when not given).
+    Returns out, or (out, q, scale) when return_codes.
+    """
+    _need(x, "x", ndim=2)
+    if x.dtype not in _IN_DTYPES:
+        raise TypeError(f"x dtype {x.dtype} not supported")
+    dev = x.device
+    _need(w, "w", torch.int8, 2, dev)
+    _need(s_ch, "s_ch", torch.float32, 1, dev)
+    layout = _LAYOUTS[b_layout]
+    m, k = x.shape
+    n, kb = (w.shape[1], w.shape[0]) if layout == B_KN else (w.shape[0], w.shape[1])
+    if kb != k:
+        raise ValueError(f"inner dimensions differ: x has k={k}, w has {kb}")
+    if out_dtype not in _OUT_DTYPES:
+        raise TypeError(f"out dtype {out_dtype} not supported")
+    out = torch.empty((m, n), dtype=out_dtype, device=dev) if out is None else out
+    _need(out, "out", out_dtype, 2, dev)
+    fused = (m <= 8 and layout == B_KN and kernel != "mfma") or kernel == "gemv"
+    if (return_codes or not fused) and q is None:
+        q = torch.empty((m, k), dtype=torch.int8, device=dev)
+    if (return_codes or not fused) and scale is None:
+        scale = torch.empty((m,), dtype=torch.float32, device=dev)
+    if q is not None:
+        _need(q, "q", torch.int8, 2, dev)
+    if scale is not None:
+        _need(scale, "scale", torch.float32, 1, dev)
+    stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = workspace_for(dev, stream.cuda_stream, gemm_workspace_size(m, n, k))
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(library().qk_linear_w8a8(
+        m, n, k, _ptr(x), _IN_DTYPES[x.dtype], _ptr(w), _ptr(s_ch), float(output_scale),
+        _ptr(out), _OUT_DTYPES[out_dtype], layout, _ptr(q), _ptr(scale), _ptr(workspace),
+        ws_bytes, _KERNELS[kernel], ctypes.c_void_p(stream.cuda_stream)))
+    return (out, q, scale) if return_codes else out
 
 
 def gated_linear_w8a8(h: torch.Tensor, w: torch.Tensor, s_ch: torch.Tensor,

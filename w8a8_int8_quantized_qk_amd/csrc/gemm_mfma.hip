@@ -48,8 +48,9 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;   // 8: two per SIMD
+constexpr int kGroups = 2;              // wave groups splitting each k slice
 constexpr int BM = 256;
 constexpr int BN = 128;
 constexpr int BK = 128;
@@ -154,6 +155,7 @@ struct KnRegTile {
 
   __device__ __forceinline__ void load(const int8_t* __restrict__ b, int N, int K, int n0, int k0) {
     const int t = threadIdx.x;
+    if (t >= 256) return;  // waves 0-3 stage the 128 x 128 tile
     const int gn = n0 + 4 * (t & 31);
     const int kb = k0 + 16 * (t >> 5);
 #pragma unroll
@@ -175,6 +177,7 @@ struct KnRegTile {
   // written as k-contiguous [n][k] rows (read like A)
   __device__ __forceinline__ void store(char* lds) const {
     const int t = threadIdx.x;
+    if (t >= 256) return;
     const int cg = t & 31;
     const int rg = t >> 5;
     uint32_t col[4][4];
@@ -236,8 +239,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
   const int n0 = tn * BN;
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wm = (t >> 6) >> 1;
-  const int wn = (t >> 6) & 1;
+  const int grp = (t >> 6) / 4;       // which k steps of a slice this wave multiplies
+  const int wsub = (t >> 6) % 4;      // which 128 x 64 sub-tile it owns
+  const int wm = wsub >> 1;
+  const int wn = wsub & 1;
 
   auto a_lds = [&](int s) { return smem + (s % kStages) * STAGE; };
   auto b_lds = [&](int s) { return smem + (s % kStages) * STAGE + A_STAGE; };
@@ -299,13 +304,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
     char* Az = a_lds(s);
 #pragma unroll
     for (int i = 0; i < BM * 8 / kThreads; ++i) {
-      const int row = (t >> 3) + 32 * i;
+      const int row = (t >> 3) + (kThreads / 8) * i;
       if (s * BK + 16 * (t & 7) >= K)
         *reinterpret_cast<uint4*>(Az + rowk_offset(row, t & 7)) = make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
   };
 
+  constexpr int kSteps = BK / 32 / kGroups;  // MFMA steps per wave per slice
   v4i af[2][FM], bf[2][FN];
   if (KT > 0) {
     fetch(0);
@@ -319,18 +325,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
     }
     __syncthreads();
     if (KTAIL && KT == 1) zero_tail(0);
-    read_frags(a_lds(0), b_lds(0), 0, af[0], bf[0]);
+    read_frags(a_lds(0), b_lds(0), kSteps * grp, af[0], bf[0]);
   }
 
-  // Software pipeline, one k slice per iteration (4 MFMA steps of 32 k):
-  //   top:       issue the DMA of slice kt + 2 (its LDS slice was last read
-  //              in iteration kt - 1, before that iteration's barrier);
-  //   steps 0-2: 8 MFMAs on the fragments in registers, interleaved with the
-  //              LDS reads of the next step's fragments;
-  //   step 3:    wait for this wave's DMA of slice kt + 1, barrier (all waves'
-  //              DMA has landed and all reads of slice kt are done), then the
-  //              last 8 MFMAs interleaved with the reads of slice kt + 1's
-  //              first step.
+  // Software pipeline, one k slice per iteration.  A slice has 4 MFMA steps
+  // of 32 k; wave group g multiplies steps 2g and 2g + 1 (both groups cover
+  // the same output sub-tiles, their sums are added at the end).  Per slice:
+  //   top:      issue the DMA of slice kt + 2 (its LDS slice was last read in
+  //             iteration kt - 1, before that iteration's barrier);
+  //   step 1st: 8 MFMAs on the fragments in registers, interleaved with the
+  //             LDS reads of the second step's fragments;
+  //   step 2nd: wait for this wave's DMA of slice kt + 1, barrier (all DMA
+  //             landed, all reads of slice kt done), then 8 MFMAs interleaved
+  //             with the reads of slice kt + 1's first step.
   for (int kt = 0; kt < KT; ++kt) {
     if (kt + 2 < KT) fetch(kt + 2);
     if constexpr (kRegB) {
@@ -339,11 +346,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
     const char* As = a_lds(kt);
     const char* Bs = b_lds(kt);
 #pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      const int cur = kk & 1;
+    for (int st = 0; st < kSteps; ++st) {
+      const int cur = st & 1;
       const int nxt = cur ^ 1;
-      if (kk + 1 < BK / 32) {
-        read_frags(As, Bs, kk + 1, af[nxt], bf[nxt]);
+      if (st + 1 < kSteps) {
+        read_frags(As, Bs, kSteps * grp + st + 1, af[nxt], bf[nxt]);
       } else if (kt + 1 < KT) {
         if constexpr (kRegB) {
           wait_vmcnt<0>();
@@ -353,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
         }
         __syncthreads();
         if (KTAIL && kt + 1 == KT - 1) zero_tail(kt + 1);
-        read_frags(a_lds(kt + 1), b_lds(kt + 1), 0, af[nxt], bf[nxt]);
+        read_frags(a_lds(kt + 1), b_lds(kt + 1), kSteps * grp, af[nxt], bf[nxt]);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -372,38 +379,60 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
   }
 
   // ---- epilogue ----
-  // Each wave stages its raw 128 x 64 INT32 tile in LDS (row stride padded by
-  // 16 bytes), then streams it out row by row: eight lanes cover one row's 64
-  // columns, each converting 8 accumulators with the per-token and
-  // per-channel scales and writing 16 (bf16) or 32 (fp32) contiguous bytes.
+  // The two wave groups' INT32 tiles are summed in LDS (row stride padded by
+  // 16 bytes): group 1 stages its accumulators, group 0 adds its own and
+  // writes the sum back in place (each element has the same owner lane in
+  // both groups).  Then all eight waves stream the 128 x 64 sub-tiles out row
+  // by row: eight lanes cover one row's 64 columns, each converting 8
+  // accumulators with the per-token and per-channel scales and writing 16
+  // (bf16) or 32 (fp32) contiguous bytes.
   constexpr int kRowStride = WTN * 4 + 16;
-  static_assert(kWaves * WTM * kRowStride <= kStages * STAGE, "epilogue staging fits in LDS");
+  static_assert(4 * WTM * kRowStride + 4 * (BM + BN) <= kStages * STAGE,
+                "epilogue staging fits in LDS");
   __syncthreads();  // every wave is done with the k slices
-  char* stage = smem + (t >> 6) * (WTM * kRowStride);
+  char* stage = smem + wsub * (WTM * kRowStride);
+  float* s_sa = reinterpret_cast<float*>(smem + 4 * WTM * kRowStride);
+  float* s_sb = s_sa + BM;
+  if (out) {
+    if (t < BM) s_sa[t] = m0 + t < M ? scale_a[m0 + t] : 0.0f;
+    else if (t - BM < BN) s_sb[t - BM] = n0 + t - BM < N ? scale_b[n0 + t - BM] * output_scale : 0.0f;
+  }
+  auto stage_at = [&](int i, int j, int r) -> int* {
+    const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    const int col = j * 32 + (lane & 31);
+    return reinterpret_cast<int*>(stage + row * kRowStride + col * 4);
+  };
+  if (grp == 1) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int col = j * 32 + (lane & 31);
-        *reinterpret_cast<int*>(stage + row * kRowStride + col * 4) = acc[i][j][r];
-      }
-  // a wave reads back only what it wrote; waiting on its own LDS writes suffices
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        for (int r = 0; r < 16; ++r) *stage_at(i, j, r) = acc[i][j][r];
+  }
+  __syncthreads();
+  if (grp == 0) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          int* p = stage_at(i, j, r);
+          *p = *p + acc[i][j][r];
+        }
+  }
+  __syncthreads();  // sums and scales visible
   const int tile_r0 = m0 + wm * WTM;
   const int cg = lane & 7;  // 8-column group
   const int gcol = n0 + wn * WTN + 8 * cg;
   const bool vec_ok = (N % 8 == 0) && (gcol + 8 <= N);
   float sb[8];
-  if (out) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sb[e] = gcol + e < N ? scale_b[gcol + e] * output_scale : 0.0f;
-  }
+  for (int e = 0; e < 8; ++e) sb[e] = s_sb[wn * WTN + 8 * cg + e];
 #pragma unroll 4
-  for (int it = 0; it < WTM * 8 / 64; ++it) {
-    const int row = 8 * it + (lane >> 3);
+  for (int it = 0; it < WTM * 8 / 64 / kGroups; ++it) {
+    const int row = (WTM / kGroups) * grp + 8 * it + (lane >> 3);
     const int grow = tile_r0 + row;
     if (grow >= M) continue;
     const int4 v0 = *reinterpret_cast<const int4*>(stage + row * kRowStride + cg * 32);
@@ -420,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
       }
     }
     if (out) {
-      const float sa = scale_a[grow];
+      const float sa = s_sa[wm * WTM + row];
       float f[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] = (static_cast<float>(v[e]) * sa) * sb[e];

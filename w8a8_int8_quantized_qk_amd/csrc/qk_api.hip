@@ -15,6 +15,10 @@ bool known_input_dtype(int dt) { return dt == QK_F32 || dt == QK_BF16 || dt == Q
 
 int status_of(hipError_t e) { return e == hipSuccess ? QK_OK : static_cast<int>(e); }
 
+bool workspace_ok(const void* ws, size_t bytes, int n) {
+  return ws && aligned(ws, 256) && bytes >= qk::gemv_workspace_bytes(n);
+}
+
 int check_rows(int m, int k, const void* src, const void* q, const void* scale, int dtype) {
   if (m < 0 || k < 0) return QK_ERR_INVALID_VALUE;
   if (!known_input_dtype(dtype)) return QK_ERR_INVALID_VALUE;
@@ -49,15 +53,15 @@ int gemm_common(int m, int n, int k, const int8_t* a, const int8_t* b, int32_t* 
   } else {
     gemv = m <= qk::kGemvMaxRows && b_layout == QK_B_KN;
   }
-
-  qk::GemmArgs g{m, n, k, a, b, c, scale_a, scale_b, output_scale, out, out_dtype, b_layout,
-                 workspace, workspace_bytes};
   if (gemv) {
-    if (!workspace || !aligned(workspace, 256) || workspace_bytes < qk::gemv_workspace_bytes(n))
-      return QK_ERR_WORKSPACE;
+    if (!workspace_ok(workspace, workspace_bytes, n)) return QK_ERR_WORKSPACE;
+    qk::GemvArgs g{m, n, k, a, -1, b, c, scale_a, scale_b, output_scale, out, out_dtype, nullptr,
+                   nullptr, workspace};
     return status_of(qk::launch_gemv(g, stream));
   }
   if (!qk::gemm_mfma_supported(m, n, k)) return QK_ERR_UNSUPPORTED;
+  qk::GemmArgs g{m, n, k, a, b, c, scale_a, scale_b, output_scale, out, out_dtype, b_layout,
+                 nullptr, 0};
   return status_of(qk::launch_gemm_mfma(g, stream));
 }
 
@@ -105,7 +109,7 @@ int qk_silu_mul_quant_per_token(int m, int d, const void* h, int h_dtype, int8_t
 
 size_t qk_gemm_workspace_size(int m, int n, int k) {
   (void)k;
-  if (m <= 0 || n <= 0 || m > qk::kGemvMaxM) return 0;
+  if (m <= 0 || n <= 0 || m > qk::kGemvMaxM) return 0;  // the tiled kernel needs none
   return qk::gemv_workspace_bytes(n);
 }
 
@@ -123,6 +127,53 @@ int qk_gemm_i8_scaled_ex(int m, int n, int k, const int8_t* a, const int8_t* b, 
                          size_t workspace_bytes, int kernel, hipStream_t stream) {
   return gemm_common(m, n, k, a, b, c, scale_a, scale_b, output_scale, out, out_dtype, b_layout,
                      workspace, workspace_bytes, kernel, stream);
+}
+
+int qk_linear_w8a8(int m, int n, int k, const void* x, int x_dtype, const int8_t* b,
+                   const float* scale_b, float output_scale, void* out, int out_dtype,
+                   int b_layout, int8_t* q_out, float* scale_out, void* workspace,
+                   size_t workspace_bytes, int kernel, hipStream_t stream) {
+  if (m < 0 || n < 0 || k < 0 || k > QK_MAX_K) return QK_ERR_INVALID_VALUE;
+  if (!known_input_dtype(x_dtype)) return QK_ERR_INVALID_VALUE;
+  if (b_layout != QK_B_KN && b_layout != QK_B_NK) return QK_ERR_INVALID_VALUE;
+  if (kernel != QK_KERNEL_AUTO && kernel != QK_KERNEL_MFMA && kernel != QK_KERNEL_GEMV)
+    return QK_ERR_INVALID_VALUE;
+  if (out_dtype != QK_F32 && out_dtype != QK_BF16) return QK_ERR_INVALID_VALUE;
+  if (k % 16 != 0) return QK_ERR_UNSUPPORTED;
+  if (m == 0 || n == 0) return QK_OK;
+  if (!out || !scale_b || (k > 0 && (!x || !b))) return QK_ERR_INVALID_VALUE;
+  if (!aligned(b, 16) || !aligned(x, x_dtype == QK_F32 ? 4 : 2)) return QK_ERR_UNSUPPORTED;
+  if (!aligned(out, out_dtype == QK_BF16 ? 2 : 4)) return QK_ERR_UNSUPPORTED;
+  if (q_out && !aligned(q_out, 16)) return QK_ERR_UNSUPPORTED;
+  if (scale_out && !aligned(scale_out, 4)) return QK_ERR_UNSUPPORTED;
+
+  bool fused;
+  if (kernel == QK_KERNEL_GEMV) {
+    if (m > qk::kGemvMaxM || b_layout != QK_B_KN) return QK_ERR_UNSUPPORTED;
+    fused = true;
+  } else if (kernel == QK_KERNEL_MFMA) {
+    fused = false;
+  } else {
+    fused = m <= qk::kGemvMaxRows && b_layout == QK_B_KN;
+  }
+  if (fused && !aligned(x, 16)) {
+    if (kernel == QK_KERNEL_GEMV) return QK_ERR_UNSUPPORTED;
+    fused = false;  // the fused launch reads x with 128-bit loads
+  }
+  if (fused) {
+    if (!workspace_ok(workspace, workspace_bytes, n)) return QK_ERR_WORKSPACE;
+    qk::GemvArgs g{m, n, k, x, x_dtype, b, nullptr, nullptr, scale_b, output_scale, out,
+                   out_dtype, q_out, scale_out, workspace};
+    return status_of(qk::launch_gemv(g, stream));
+  }
+  // two launches: quantization into q_out / scale_out, then the tiled GEMM
+  if (!q_out || !scale_out) return QK_ERR_INVALID_VALUE;
+  if (!qk::gemm_mfma_supported(m, n, k)) return QK_ERR_UNSUPPORTED;
+  hipError_t e = qk::launch_quant_rows(m, k, x, x_dtype, q_out, scale_out, stream);
+  if (e != hipSuccess) return status_of(e);
+  qk::GemmArgs g{m, n, k, q_out, b, nullptr, scale_out, scale_b, output_scale, out, out_dtype,
+                 b_layout, nullptr, 0};
+  return status_of(qk::launch_gemm_mfma(g, stream));
 }
 
 }  // extern "C"

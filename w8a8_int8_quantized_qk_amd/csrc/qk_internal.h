@@ -57,10 +57,26 @@ hipError_t launch_silu_quant_rows(int m, int d, const void* h, int dtype, int8_t
 bool gemm_mfma_supported(int m, int n, int k);
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
 
-// Split-K decode GEMV for m <= kGemvMaxRows per launch (gemv.hip).
+// Split-K decode GEMV (gemv.hip): m <= kGemvMaxRows rows per launch, larger m
+// in row groups; exact INT32 partial sums in a self-cleaning workspace.
 constexpr int kGemvMaxRows = 8;
-constexpr int kGemvMaxM = 16;  // larger m is split into row groups of kGemvMaxRows
+constexpr int kGemvMaxM = 16;
+struct GemvArgs {
+  int m, n, k;
+  const void* a;   // int8 codes [m][k] (x_dtype == -1) or activations of x_dtype
+  int x_dtype;
+  const int8_t* b;  // [k][n]
+  int32_t* c;
+  const float* scale_a;  // codes' scales (x_dtype == -1)
+  const float* scale_b;
+  float output_scale;
+  void* out;
+  int out_dtype;
+  int8_t* q_out;   // optional codes written by the fused path
+  float* s_out;    // optional scales written by the fused path
+  void* workspace; // gemv_workspace_bytes(n), zero before the first call
+};
 size_t gemv_workspace_bytes(int n);
-hipError_t launch_gemv(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_gemv(const GemvArgs& g, hipStream_t stream);
 
 }  // namespace qk

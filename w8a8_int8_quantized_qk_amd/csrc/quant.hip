@@ -25,71 +25,18 @@
 //
 // Rows too long for the register cache, or not 16-byte aligned, take a
 // two-pass kernel that re-reads the row (and recomputes silu * up).
-#include "qk_internal.h"
+#include "quant_math.h"
 
 namespace qk {
 namespace {
 
+using qm::Elem;
+using qm::code_of;
+using qm::pack4;
+using qm::row_scale;
+
 constexpr int kBlock = 256;    // threads per row
 constexpr int kMaxUnits = 8;   // 16-byte input units cached per thread
-
-template <int DT>
-struct Elem;
-template <>
-struct Elem<QK_F32> {
-  static constexpr int kBytes = 4;
-  static constexpr int kPerUnit = 4;
-  __device__ static void unpack(const uint4 v, float* f) {
-    f[0] = __uint_as_float(v.x);
-    f[1] = __uint_as_float(v.y);
-    f[2] = __uint_as_float(v.z);
-    f[3] = __uint_as_float(v.w);
-  }
-  __device__ static float load(const void* p, size_t i) {
-    return static_cast<const float*>(p)[i];
-  }
-};
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-template <>
-struct Elem<QK_BF16> {
-  static constexpr int kBytes = 2;
-  static constexpr int kPerUnit = 8;
-  __device__ static void unpack(const uint4 v, float* f) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = bf16_lo(w[i]);
-      f[2 * i + 1] = bf16_hi(w[i]);
-    }
-  }
-  __device__ static float load(const void* p, size_t i) {
-    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
-  }
-};
-
-__device__ __forceinline__ float f16_bits(uint32_t b) {
-  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
-}
-
-template <>
-struct Elem<QK_F16> {
-  static constexpr int kBytes = 2;
-  static constexpr int kPerUnit = 8;
-  __device__ static void unpack(const uint4 v, float* f) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = f16_bits(w[i] & 0xffffu);
-      f[2 * i + 1] = f16_bits(w[i] >> 16);
-    }
-  }
-  __device__ static float load(const void* p, size_t i) {
-    return f16_bits(static_cast<const uint16_t*>(p)[i]);
-  }
-};
 
 // e^x in binary32 by a fixed sequence so that results are reproducible bit
 // for bit: x = n ln2 + r with n = rint(x / ln 2) and r reduced in two fused
@@ -120,38 +67,6 @@ __device__ __forceinline__ float silu_times(float g, float u) {
   const float t = 1.0f + e;
   const float sg = g / t;  // IEEE division (correctly rounded build)
   return sg * u;
-}
-
-// clamp(rint(x / s), -127, 127) with x / s formed from r = RN(1 / s).
-__device__ __forceinline__ int code_of(float x, float s, float r) {
-  const float y = x * r;
-  const float e = __builtin_fmaf(-y, s, x);
-  float q = __builtin_fmaf(e, r, y);
-  q = __builtin_rintf(q);
-  q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
-  return static_cast<int>(q);
-}
-
-__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
-  return (static_cast<uint32_t>(a) & 0xffu) | ((static_cast<uint32_t>(b) & 0xffu) << 8) |
-         ((static_cast<uint32_t>(c) & 0xffu) << 16) | (static_cast<uint32_t>(d) << 24);
-}
-
-__device__ __forceinline__ float block_max(float v) {
-  __shared__ float part[kBlock / 64];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = part[0];
-#pragma unroll
-  for (int w = 1; w < kBlock / 64; ++w) r = __builtin_fmaxf(r, part[w]);
-  return r;
-}
-
-__device__ __forceinline__ void row_scale(float amax, float& s, float& r) {
-  s = __builtin_fmaxf(amax, 1e-12f) / 127.0f;
-  r = 1.0f / s;
 }
 
 // Register-cached path: the row (k elements, k % kPerUnit == 0) is split into
@@ -188,7 +103,7 @@ __global__ __launch_bounds__(kBlock) void quant_rows_cached(const void* __restri
       for (int e = 0; e < P; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j][e]));
     }
   }
-  amax = block_max(amax);
+  amax = qm::block_max<kBlock>(amax);
   float s, r;
   row_scale(amax, s, r);
   if (threadIdx.x == 0) scale[row] = s;
@@ -230,7 +145,7 @@ __global__ __launch_bounds__(kBlock) void quant_rows_twopass(const void* __restr
   };
   float amax = 0.0f;
   for (int j = threadIdx.x; j < k; j += kBlock) amax = __builtin_fmaxf(amax, __builtin_fabsf(value(j)));
-  amax = block_max(amax);
+  amax = qm::block_max<kBlock>(amax);
   float s, r;
   row_scale(amax, s, r);
   if (threadIdx.x == 0) scale[row] = s;

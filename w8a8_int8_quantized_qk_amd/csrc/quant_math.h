@@ -1,0 +1,114 @@
+// Per-token quantization arithmetic shared by the quantization kernels and the
+// fused decode GEMV (device code only).
+//
+// scale = max(row absmax, 1e-12) / 127 and code = clamp(rint(x / scale),
+// -127, 127) in binary32 ("kernels: fused silu_and_mul + dynamic per-token FP8
+// quantization", Algorithm; symmetric [-127, 127] codes from "Skill: Write an
+// INT8 Quantized Kernel", Inputs).  x / scale is formed from r = 1 / scale
+// (correctly rounded) as y = x * r, e = fma(-y, scale, x), y' = fma(e, r, y):
+// by Markstein's theorem (P. Markstein, IBM J. Res. Dev. 34(1), 1990; Muller
+// et al., Handbook of Floating-Point Arithmetic, division with fma) y' is the
+// correctly rounded quotient whenever the residual does not underflow, which
+// holds for every element whose code can be nonzero (|x / scale| >= 1/2
+// implies |x| >= 3.9e-15).
+#pragma once
+
+#include "qk_internal.h"
+
+namespace qk {
+namespace qm {
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<QK_F32> {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerUnit = 4;
+  __device__ static void unpack(const uint4 v, float* f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  __device__ static float load(const void* p, size_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <>
+struct Elem<QK_BF16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerUnit = 8;
+  __device__ static void unpack(const uint4 v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(w[i]);
+      f[2 * i + 1] = bf16_hi(w[i]);
+    }
+  }
+  __device__ static float load(const void* p, size_t i) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+  }
+};
+
+__device__ __forceinline__ float f16_bits(uint32_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+}
+
+template <>
+struct Elem<QK_F16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerUnit = 8;
+  __device__ static void unpack(const uint4 v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = f16_bits(w[i] & 0xffffu);
+      f[2 * i + 1] = f16_bits(w[i] >> 16);
+    }
+  }
+  __device__ static float load(const void* p, size_t i) {
+    return f16_bits(static_cast<const uint16_t*>(p)[i]);
+  }
+};
+
+// clamp(rint(x / s), -127, 127) with x / s formed from r = RN(1 / s).
+__device__ __forceinline__ int code_of(float x, float s, float r) {
+  const float y = x * r;
+  const float e = __builtin_fmaf(-y, s, x);
+  float q = __builtin_fmaf(e, r, y);
+  q = __builtin_rintf(q);
+  q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
+  return static_cast<int>(q);
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+  return (static_cast<uint32_t>(a) & 0xffu) | ((static_cast<uint32_t>(b) & 0xffu) << 8) |
+         ((static_cast<uint32_t>(c) & 0xffu) << 16) | (static_cast<uint32_t>(d) << 24);
+}
+
+template <int kBlock>
+__device__ __forceinline__ float block_max(float v) {
+  __shared__ float part[kBlock / 64];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = part[0];
+#pragma unroll
+  for (int w = 1; w < kBlock / 64; ++w) r = __builtin_fmaxf(r, part[w]);
+  return r;
+}
+
+__device__ __forceinline__ void row_scale(float amax, float& s, float& r) {
+  s = __builtin_fmaxf(amax, 1e-12f) / 127.0f;
+  r = 1.0f / s;
+}
+
+
+}  // namespace qm
+}  // namespace qk
