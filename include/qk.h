@@ -121,8 +121,9 @@ int qk_silu_mul_quant_per_token(int m, int d, const void *h, int h_dtype, int8_t
                                 float *scale, hipStream_t stream);
 
 /* Bytes of workspace qk_gemm_i8_scaled / qk_linear_w8a8 need for this shape
- * (0 if none).  The decode kernel (m <= 16) adds exact INT32 split-K partial
- * sums there and counts arriving workgroups; the tiled kernel needs none. */
+ * (0 if none).  The decode kernel (m <= 16) keeps one 64-bit word per output
+ * element of a row group there, holding the exact split-K partial sum and the
+ * number of contributions so far; the tiled kernel needs none. */
 size_t qk_gemm_workspace_size(int m, int n, int k);
 
 /*

@@ -13,28 +13,36 @@
 //     block of the weight.  Lane (cg, half) of wave w loads 16 contiguous
 //     bytes (columns 16 cg .. 16 cg + 15) of the four rows of row quad
 //     2 w + half of each 64-row round: every wave-wide load instruction reads
-//     two contiguous 512-byte row segments.  A lane issues the loads of all
-//     eight rounds (32 x 128-bit) before using any.
+//     two contiguous 512-byte row segments.  Weight loads are nontemporal
+//     (each byte is used once).  A lane keeps several rounds of loads in
+//     flight ahead of the round it multiplies (software pipeline).  Only one
+//     round is issued before the quantization: a CU accepts a limited number
+//     of outstanding loads, and waves stalled issuing weight loads would hold
+//     up the quantization and with it every multiply.
 //   * The four rows of a lane are transposed in registers (v_perm_b32) into
 //     sixteen 4-byte columns and multiplied with the matching four activation
 //     codes by v_dot4_i32_i8 (exact INT32).  Codes come from LDS.
-//   * Partial sums are reduced across the two half-waves by a lane swap,
-//     across the eight waves with LDS atomics, and across the K-slice
-//     workgroups with device-scope INT32 atomic adds into a workspace:
-//     integer addition is exact in any order, so the result is the same bits
-//     as one sequential sum.  Each lane waits for its adds to complete, then
-//     one lane per workgroup counts the arrival (acquire-release, device
-//     scope).  The last workgroup of a column tile reads the sums, applies
-//     the dequant epilogue, and returns its workspace words and counter to
-//     zero for the next call.
+//   * Partial sums are reduced across the 16 half-waves with LDS adds, laid
+//     out so that the lanes of one add touch consecutive words.  Across the
+//     K-slice workgroups
+//     each (row, column) has one 64-bit workspace word holding
+//     (contributions so far) * 2^40 + (their exact sum); a workgroup adds
+//     2^40 + its partial with one returning device-scope atomic.  The partial
+//     sums of any subset of the k range stay within +-2^31, so the two fields
+//     never interfere, and integer addition is exact in any order.  The lane
+//     whose add returns a count of splits - 1 holds the last contribution: it
+//     forms the total, applies the dequant epilogue for that column, and
+//     returns the word to zero for the next call.  No counters, fences or
+//     last-workgroup pass are needed.
 //   * Activation codes are either given (int8 a, scale_a), or the kernel
 //     quantizes the m activation rows itself from fp32/bf16/fp16 input with
 //     the same arithmetic as the quantization kernels: every workgroup
 //     reduces the whole row to the same bit-identical scale and encodes its
 //     own k slice; one workgroup per slice writes the codes out when asked.
-//     The activation loads are issued first and the weight loads right
-//     after, so the quantization overlaps the weight stream.  The decode
-//     linear is then a single launch.
+//     Every wave issues its activation (or code) loads before any wave issues
+//     weight loads, and they are used in straight-line code, so the
+//     quantization waits only for them and overlaps the weight stream.  The decode linear is then a single
+//     launch.
 #include "quant_math.h"
 
 namespace qk {
@@ -46,10 +54,19 @@ constexpr int kCols = 512;      // output columns per workgroup: 32 lanes x 16 b
 constexpr int kRowsK = 512;     // k rows per workgroup (one split-K slice)
 constexpr int kRounds = kRowsK / 64;  // a round: 16 row quads = 8 waves x 2 half-waves
 constexpr int kXUnits = 2;      // 16-byte activation units a lane keeps in registers
+constexpr int kCountShift = 40; // workspace word: count << 40 | sum (two's complement)
+static_assert(kCols == kThreads, "one output column per thread in the reduction");
 
-// rounds whose weight loads a lane keeps in flight (4 x 16 bytes each)
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// rounds of weight loads (4 x 16 bytes per lane each) kept in flight ahead of
+// the round being multiplied; more rows need more accumulator registers
 template <int MR>
-constexpr int unroll_for() { return MR <= 2 ? 8 : (MR == 4 ? 4 : 2); }
+constexpr int prefetch_for() { return MR <= 2 ? kRounds - 1 : (MR == 4 ? 4 : 2); }
+// rounds issued before the quantization: a CU accepts only so many
+// outstanding loads, and a wave stalled issuing weight loads could not reach
+// the quantization (and with it every wave's first multiply)
+constexpr int kEarlyRounds = 1;
 
 __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
                                              uint32_t* col) {
@@ -68,6 +85,27 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Workgroup-wide max of MR values at once (one barrier).
+template <int MR>
+__device__ __forceinline__ void block_max_rows(float (&v)[MR]) {
+  __shared__ float part[MR][kWaves];
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v[m] = __builtin_fmaxf(v[m], __shfl_xor(v[m], off, 64));
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) part[m][threadIdx.x >> 6] = v[m];
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    float r = part[m][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = __builtin_fmaxf(r, part[m][w]);
+    v[m] = r;
+  }
+}
+
 // XDT < 0: `a` holds int8 codes [M][K] and scale_a their scales.
 // XDT >= 0: `a` holds activations [M][K] of that dtype (16-byte aligned rows,
 // K % 16 == 0), quantized here.
@@ -76,13 +114,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const void* __restrict__ a, const int8_t* __restrict__ w, int32_t* __restrict__ c,
     const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
     void* __restrict__ out, int out_dtype, int M, int N, int K, int8_t* __restrict__ q_out,
-    float* __restrict__ s_out, int32_t* __restrict__ ws_acc, int32_t* __restrict__ ws_cnt,
-    int col_tiles, int splits) {
-  constexpr int U = unroll_for<MR>();
-  __shared__ int32_t q_lds[MR][kRowsK / 4];  // codes of this k slice, 4 per word
+    float* __restrict__ s_out, unsigned long long* __restrict__ ws, int col_tiles, int splits) {
+  constexpr int PD = prefetch_for<MR>();
+  static_assert(PD >= kEarlyRounds && PD < kRounds, "prefetch distance");
+  constexpr int kSliceWords = kRowsK / 4;            // code words of one row's k slice
+  constexpr int kCodeWords = MR * kSliceWords;
+  constexpr int kCodeRegs = (kCodeWords + kThreads - 1) / kThreads;
+  __shared__ int32_t q_lds[MR][kSliceWords];  // codes of this k slice, 4 per word
   __shared__ float s_row[MR];
-  __shared__ int red[MR][kCols];
-  __shared__ int last_flag;
+  __shared__ int red[MR][kCols];  // column 16 cg + j of a row at j * 32 + cg
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -95,120 +135,195 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   const int quad = 2 * wave + (lane >> 5);   // row quad within a 64-row round
   const int gn = n0 + 16 * cg;
 
-  for (int idx = t; idx < MR * kCols; idx += kThreads) red[idx / kCols][idx % kCols] = 0;
+  using E = qm::Elem<XDT < 0 ? QK_F32 : XDT>;
+  constexpr int P = E::kPerUnit;
 
-  // weight loads of U rounds; rows past K (zero codes) and columns past N
-  // (never stored) read clamped, valid addresses instead of branching
-  uint32_t wr[U][4][4];
-  auto load_batch = [&](int round0) {
+  if (K == 0) {
+    // empty reduction: acc = 0 (one workgroup per column tile, no workspace);
+    // the scale of an empty row is the guard's
+    const int n = n0 + t;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int m = 0; m < MR; ++m) {
+      if (m >= M) continue;
+      float s_m, r_m;
+      if constexpr (XDT < 0) {
+        s_m = scale_a ? scale_a[m] : 0.0f;
+      } else {
+        qm::row_scale(0.0f, s_m, r_m);
+        if (blockIdx.x == 0 && t == 0 && s_out) s_out[m] = s_m;
+      }
+      if (n >= N) continue;
+      const size_t o_idx = static_cast<size_t>(m) * N + n;
+      if (c) c[o_idx] = 0;
+      if (out) {
+        const float f = (0.0f * s_m) * (scale_b[n] * output_scale);
+        if (out_dtype == QK_BF16)
+          static_cast<uint16_t*>(out)[o_idx] = to_bf16(f);
+        else
+          static_cast<float*>(out)[o_idx] = f;
+      }
+    }
+    return;
+  }
+
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int k = min(k0 + (round0 + u) * 64 + 4 * quad + r, K - 1);
-        const int8_t* row = w + static_cast<size_t>(k) * N;
-        if constexpr (N16) {
-          const uint4 v = *reinterpret_cast<const uint4*>(row + min(gn, N - 16));
-          wr[u][r][0] = v.x;
-          wr[u][r][1] = v.y;
-          wr[u][r][2] = v.z;
-          wr[u][r][3] = v.w;
-        } else {
+  for (int m = 0; m < MR; ++m) red[m][t] = 0;
+
+  // weight loads of one round (all loop indices below are compile-time after
+  // unrolling, so wr stays in registers); rows past K (zero codes) and
+  // columns past N (never stored) read clamped, valid addresses instead of
+  // branching
+  uint32_t wr[kRounds][4][4];
+  auto load_round = [&](int round) {
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            uint32_t x = 0;
+    for (int r = 0; r < 4; ++r) {
+      const int k = min(k0 + round * 64 + 4 * quad + r, K - 1);
+      const int8_t* row = w + static_cast<size_t>(k) * N;
+      if constexpr (N16) {
+        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(row + min(gn, N - 16)));
+        wr[round][r][0] = v.x;
+        wr[round][r][1] = v.y;
+        wr[round][r][2] = v.z;
+        wr[round][r][3] = v.w;
+      } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              x |= static_cast<uint32_t>(static_cast<uint8_t>(row[min(gn + 4 * q4 + e, N - 1)])) << (8 * e);
-            wr[u][r][q4] = x;
-          }
+        for (int q4 = 0; q4 < 4; ++q4) {
+          uint32_t x = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            x |= static_cast<uint32_t>(static_cast<uint8_t>(row[min(gn + 4 * q4 + e, N - 1)])) << (8 * e);
+          wr[round][r][q4] = x;
         }
       }
     }
   };
 
-  // ---- activation loads first, then the weight, so the activation work
-  //      below overlaps the weight stream ----
-  using E = qm::Elem<XDT < 0 ? QK_F32 : XDT>;
-  constexpr int P = E::kPerUnit;
+  // ---- activation (or code) loads first, then the weight (K > 0 from here) ----
   const int units = K / P;  // 16-byte activation units per row (fused path)
-  uint4 xr[MR][kXUnits];
   const bool x_in_regs = units <= kThreads * kXUnits;
+  uint4 xr[MR][kXUnits];
+  int32_t cr[kCodeRegs];
   if constexpr (XDT >= 0) {
-    if (x_in_regs && units > 0) {
+    if (x_in_regs) {
 #pragma unroll
       for (int m = 0; m < MR; ++m)
 #pragma unroll
         for (int j = 0; j < kXUnits; ++j) {
           const int mm = min(m, M - 1);
-          const int u = min(t + kThreads * j, units - 1);
+          const int u = min(t + kThreads * j, units - 1);  // duplicates add nothing to a max
           xr[m][j] = *reinterpret_cast<const uint4*>(
               static_cast<const char*>(a) + (static_cast<size_t>(mm) * K + static_cast<size_t>(u) * P) * E::kBytes);
         }
     }
+  } else {
+    const int8_t* q = static_cast<const int8_t*>(a);
+#pragma unroll
+    for (int j = 0; j < kCodeRegs; ++j) {
+      const int idx = t + kThreads * j;
+      const int m = idx / kSliceWords;
+      const int k = k0 + 4 * (idx % kSliceWords);
+      cr[j] = (idx < kCodeWords && m < M && k < K)
+                  ? *reinterpret_cast<const int32_t*>(q + static_cast<size_t>(m) * K + k)
+                  : 0;
+    }
+    if (t < MR) s_row[t] = (t < M && scale_a) ? scale_a[t] : 0.0f;
   }
-  if (K > 0) load_batch(0);
+  // A CU serves its loads in issue order: without this barrier the later
+  // waves' activation loads would queue behind the earlier waves' weight
+  // loads.  (Execution barrier only; nothing needs to be visible yet.)
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int round = 0; round < kEarlyRounds; ++round) load_round(round);
 
   // ---- codes of rows k0 .. k0 + 511 into LDS ----
   if constexpr (XDT < 0) {
-    const int8_t* q = static_cast<const int8_t*>(a);
-    for (int idx = t; idx < MR * (kRowsK / 4); idx += kThreads) {
-      const int m = idx / (kRowsK / 4);
-      const int k = k0 + 4 * (idx % (kRowsK / 4));
-      q_lds[m][idx % (kRowsK / 4)] =
-          (m < M && k < K) ? *reinterpret_cast<const int32_t*>(q + static_cast<size_t>(m) * K + k) : 0;
+#pragma unroll
+    for (int j = 0; j < kCodeRegs; ++j) {
+      const int idx = t + kThreads * j;
+      if (idx < kCodeWords) q_lds[idx / kSliceWords][idx % kSliceWords] = cr[j];
     }
-    if (t < MR) s_row[t] = (t < M && scale_a) ? scale_a[t] : 0.0f;
+  } else if (x_in_regs) {
+    // the scale needs the whole row: every workgroup reduces it (identical bits)
+    float amax[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      amax[m] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kXUnits; ++j) {
+        float v[P];
+        E::unpack(xr[m][j], v);
+#pragma unroll
+        for (int e = 0; e < P; ++e) amax[m] = __builtin_fmaxf(amax[m], __builtin_fabsf(v[e]));
+      }
+    }
+    block_max_rows<MR>(amax);
+    const int u_lo = k0 / P;
+    const int u_hi = min(units, (k0 + kRowsK) / P);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      float s, r;
+      qm::row_scale(amax[m], s, r);
+      if (t == 0) s_row[m] = s;
+      if (blockIdx.x == 0 && t == 0 && s_out && m < M) s_out[m] = s;
+      // words of the slice past K have no unit: zero (disjoint from the writers below)
+      if (t < kSliceWords && k0 + 4 * t >= K) q_lds[m][t] = 0;
+#pragma unroll
+      for (int j = 0; j < kXUnits; ++j) {
+        const int u = t + kThreads * j;
+        if (u < u_lo || u >= u_hi) continue;
+        float v[P];
+        E::unpack(xr[m][j], v);
+#pragma unroll
+        for (int e4 = 0; e4 < P / 4; ++e4) {
+          const uint32_t word =
+              m < M ? qm::pack4(qm::code_of(v[4 * e4], s, r), qm::code_of(v[4 * e4 + 1], s, r),
+                                qm::code_of(v[4 * e4 + 2], s, r), qm::code_of(v[4 * e4 + 3], s, r))
+                    : 0u;  // padding rows
+          const int kw = u * (P / 4) + e4;  // codes of elements 4 kw .. 4 kw + 3
+          q_lds[m][kw - k0 / 4] = static_cast<int32_t>(word);
+          if (ct == 0 && q_out && m < M)  // one workgroup per k slice writes the codes
+            *reinterpret_cast<uint32_t*>(q_out + static_cast<size_t>(m) * K + 4 * kw) = word;
+        }
+      }
+    }
   } else {
+    // rows too long to hold in registers: re-read them (from L2) per pass
     for (int m = 0; m < MR; ++m) {
       if (m >= M) {  // padding rows: zero codes
-        for (int idx = t; idx < kRowsK / 4; idx += kThreads) q_lds[m][idx] = 0;
+        if (t < kSliceWords) q_lds[m][t] = 0;
         continue;
       }
       const char* xrow = static_cast<const char*>(a) + static_cast<size_t>(m) * K * E::kBytes;
-      auto unit = [&](int j, int u) -> uint4 {  // unit u of this row, from registers if held
-        if (x_in_regs) return xr[m][j];
+      auto unit = [&](int u) -> uint4 {
         return *reinterpret_cast<const uint4*>(xrow + static_cast<size_t>(u) * 16);
       };
-      // the scale needs the whole row: every workgroup reduces it (identical bits)
       float amax = 0.0f;
-      for (int u0 = 0; u0 < units; u0 += kThreads * kXUnits) {
+      for (int u = t; u < units; u += kThreads) {
+        float v[P];
+        E::unpack(unit(u), v);
 #pragma unroll
-        for (int j = 0; j < kXUnits; ++j) {
-          const int u = min(u0 + t + kThreads * j, units - 1);  // duplicates add nothing to a max
-          float v[P];
-          E::unpack(unit(j, u), v);
-#pragma unroll
-          for (int e = 0; e < P; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[e]));
-        }
+        for (int e = 0; e < P; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[e]));
       }
       amax = qm::block_max<kThreads>(amax);
       float s, r;
       qm::row_scale(amax, s, r);
       if (t == 0) s_row[m] = s;
       if (blockIdx.x == 0 && t == 0 && s_out) s_out[m] = s;
-      // codes of this workgroup's k slice only
-      for (int idx = t; idx < kRowsK / 4; idx += kThreads) q_lds[m][idx] = 0;
-      __syncthreads();
+      if (t < kSliceWords && k0 + 4 * t >= K) q_lds[m][t] = 0;
       const int u_lo = k0 / P;
       const int u_hi = min(units, (k0 + kRowsK) / P);
-      for (int u0 = 0; u0 < units; u0 += kThreads * kXUnits) {
+      for (int u = u_lo + t; u < u_hi; u += kThreads) {
+        float v[P];
+        E::unpack(unit(u), v);
 #pragma unroll
-        for (int j = 0; j < kXUnits; ++j) {
-          const int u = u0 + t + kThreads * j;
-          if (u < u_lo || u >= u_hi) continue;
-          float v[P];
-          E::unpack(unit(j, u), v);
-#pragma unroll
-          for (int e4 = 0; e4 < P / 4; ++e4) {
-            const uint32_t word =
-                qm::pack4(qm::code_of(v[4 * e4], s, r), qm::code_of(v[4 * e4 + 1], s, r),
-                          qm::code_of(v[4 * e4 + 2], s, r), qm::code_of(v[4 * e4 + 3], s, r));
-            const int kw = u * (P / 4) + e4;  // codes of elements 4 kw .. 4 kw + 3
-            q_lds[m][kw - k0 / 4] = static_cast<int32_t>(word);
-            if (ct == 0 && q_out)  // one workgroup per k slice writes the codes
-              *reinterpret_cast<uint32_t*>(q_out + static_cast<size_t>(m) * K + 4 * kw) = word;
-          }
+        for (int e4 = 0; e4 < P / 4; ++e4) {
+          const uint32_t word =
+              qm::pack4(qm::code_of(v[4 * e4], s, r), qm::code_of(v[4 * e4 + 1], s, r),
+                        qm::code_of(v[4 * e4 + 2], s, r), qm::code_of(v[4 * e4 + 3], s, r));
+          const int kw = u * (P / 4) + e4;
+          q_lds[m][kw - k0 / 4] = static_cast<int32_t>(word);
+          if (ct == 0 && q_out)
+            *reinterpret_cast<uint32_t*>(q_out + static_cast<size_t>(m) * K + 4 * kw) = word;
         }
       }
       __syncthreads();  // block_max reuses its LDS between rows
@@ -223,74 +338,73 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[m][j] = 0;
 
-  for (int round0 = 0; K > 0 && round0 < kRounds; round0 += U) {
-    if (round0 > 0) load_batch(round0);
+  // software pipeline: round `round` is multiplied while rounds up to
+  // round + PD are in flight
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      uint32_t col[16];
+  for (int round = 0; round < kRounds; ++round) {
+    if (round == 0) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        transpose4x4(wr[u][0][q4], wr[u][1][q4], wr[u][2][q4], wr[u][3][q4], &col[4 * q4]);
-      const int kw = (round0 + u) * 16 + quad;
+      for (int q = kEarlyRounds; q <= PD; ++q) load_round(q);
+    } else if (round + PD < kRounds) {
+      load_round(round + PD);
+    }
+    uint32_t col[16];
 #pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        const int qd = q_lds[m][kw];
+    for (int q4 = 0; q4 < 4; ++q4)
+      transpose4x4(wr[round][0][q4], wr[round][1][q4], wr[round][2][q4], wr[round][3][q4], &col[4 * q4]);
+    const int kw = round * 16 + quad;
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          acc[m][j] = __builtin_amdgcn_sdot4(static_cast<int>(col[j]), qd, acc[m][j], false);
-      }
+    for (int m = 0; m < MR; ++m) {
+      const int qd = q_lds[m][kw];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        acc[m][j] = __builtin_amdgcn_sdot4(static_cast<int>(col[j]), qd, acc[m][j], false);
     }
   }
 
-  // ---- reduce within the workgroup: the two half-waves, then LDS ----
+  // ---- reduce within the workgroup with LDS adds: for a fixed j the 32
+  //      column groups hit 32 consecutive words (no bank conflicts) ----
 #pragma unroll
   for (int m = 0; m < MR; ++m)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int v = acc[m][j] + __shfl_xor(acc[m][j], 32, 64);
-      if (lane < 32) atomicAdd(&red[m][16 * cg + j], v);
-    }
+    for (int j = 0; j < 16; ++j) atomicAdd(&red[m][j * 32 + cg], acc[m][j]);
   __syncthreads();
 
-  // ---- across the split-K workgroups: exact INT32 adds into the workspace ----
-  for (int idx = t; idx < MR * kCols; idx += kThreads) {
-    const int m = idx / kCols;
-    const int n = n0 + idx % kCols;
-    if (m < M && n < N)
-      __hip_atomic_fetch_add(&ws_acc[static_cast<size_t>(m) * N + n], red[m][idx % kCols],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // ---- across the split-K workgroups: one returning 64-bit add per (row,
+  //      column) carrying the arrival count and the exact partial sum ----
+  const int n = n0 + t;
+  if (n >= N) return;
+  const int slot = (t & 15) * 32 + (t >> 4);  // where column t of the tile was reduced
+  unsigned long long prev[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    if (m >= M) continue;
+    const unsigned long long add =
+        (1ull << kCountShift) + static_cast<unsigned long long>(static_cast<long long>(red[m][slot]));
+    prev[m] = __hip_atomic_fetch_add(&ws[static_cast<size_t>(m) * N + n], add, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
   }
-  // every lane's adds have completed before the workgroup's arrival is counted
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (t == 0) {
-    const int prev =
-        __hip_atomic_fetch_add(&ws_cnt[ct], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = prev == splits - 1;
-  }
-  __syncthreads();
-  if (!last_flag) return;
-
-  // ---- last workgroup of this column tile: epilogue, workspace back to zero ----
-  __atomic_thread_fence(__ATOMIC_ACQUIRE);
-  for (int idx = t; idx < M * kCols; idx += kThreads) {
-    const int m = idx / kCols;
-    const int n = n0 + idx % kCols;
-    if (n >= N) continue;
-    int32_t* p = &ws_acc[static_cast<size_t>(m) * N + n];
-    const int v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const size_t o = static_cast<size_t>(m) * N + n;
-    if (c) c[o] = v;
+  const float sb = out ? scale_b[n] * output_scale : 0.0f;
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    if (m >= M) continue;
+    const long long o = static_cast<long long>(prev[m]);
+    const long long count = (o + (1ll << (kCountShift - 1))) >> kCountShift;
+    if (count != splits - 1) continue;
+    // last contribution: total = earlier sum + this partial; word back to zero
+    const int v = static_cast<int>(o - (count << kCountShift)) + red[m][slot];
+    __hip_atomic_store(&ws[static_cast<size_t>(m) * N + n], 0ull, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    const size_t o_idx = static_cast<size_t>(m) * N + n;
+    if (c) c[o_idx] = v;
     if (out) {
-      const float f = (static_cast<float>(v) * s_row[m]) * (scale_b[n] * output_scale);
+      const float f = (static_cast<float>(v) * s_row[m]) * sb;
       if (out_dtype == QK_BF16)
-        static_cast<uint16_t*>(out)[o] = to_bf16(f);
+        static_cast<uint16_t*>(out)[o_idx] = to_bf16(f);
       else
-        static_cast<float*>(out)[o] = f;
+        static_cast<float*>(out)[o_idx] = f;
     }
   }
-  if (t == 0) __hip_atomic_store(&ws_cnt[ct], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int MR, int XDT>
@@ -308,16 +422,15 @@ hipError_t launch_mr(const GemvArgs& g, int row0, int rows, hipStream_t stream) 
   float* s_out = g.s_out ? g.s_out + row0 : nullptr;
   const int col_tiles = (g.n + kCols - 1) / kCols;
   const int splits = g.k > 0 ? (g.k + kRowsK - 1) / kRowsK : 1;
-  int32_t* ws_acc = static_cast<int32_t*>(g.workspace);
-  int32_t* ws_cnt = ws_acc + static_cast<size_t>(kGemvMaxRows) * g.n;
+  auto* ws = static_cast<unsigned long long*>(g.workspace);
   const dim3 grid(static_cast<unsigned>(col_tiles) * static_cast<unsigned>(splits));
   if (g.n % 16 == 0 && reinterpret_cast<uintptr_t>(g.b) % 16 == 0)
     return launch(gemv_kernel<MR, XDT, true>, grid, dim3(kThreads), 0, stream, a, g.b, c, sa,
                   g.scale_b, g.output_scale, out, g.out_dtype, rows, g.n, g.k, q_out, s_out,
-                  ws_acc, ws_cnt, col_tiles, splits);
+                  ws, col_tiles, splits);
   return launch(gemv_kernel<MR, XDT, false>, grid, dim3(kThreads), 0, stream, a, g.b, c, sa,
                 g.scale_b, g.output_scale, out, g.out_dtype, rows, g.n, g.k, q_out, s_out,
-                ws_acc, ws_cnt, col_tiles, splits);
+                ws, col_tiles, splits);
 }
 
 template <int XDT>
@@ -341,8 +454,7 @@ hipError_t launch_rows(const GemvArgs& g, hipStream_t stream) {
 }  // namespace
 
 size_t gemv_workspace_bytes(int n) {
-  const size_t col_tiles = (static_cast<size_t>(n) + kCols - 1) / kCols;
-  const size_t bytes = (static_cast<size_t>(kGemvMaxRows) * n + col_tiles) * sizeof(int32_t);
+  const size_t bytes = static_cast<size_t>(kGemvMaxRows) * static_cast<size_t>(n) * 8;
   return (bytes + 255) / 256 * 256;
 }
 

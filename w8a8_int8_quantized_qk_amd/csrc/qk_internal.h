@@ -58,7 +58,8 @@ bool gemm_mfma_supported(int m, int n, int k);
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
 
 // Split-K decode GEMV (gemv.hip): m <= kGemvMaxRows rows per launch, larger m
-// in row groups; exact INT32 partial sums in a self-cleaning workspace.
+// in row groups; exact partial sums with arrival counts in a self-cleaning
+// workspace of 64-bit words.
 constexpr int kGemvMaxRows = 8;
 constexpr int kGemvMaxM = 16;
 struct GemvArgs {
