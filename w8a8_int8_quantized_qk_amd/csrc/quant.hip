@@ -5,11 +5,12 @@
 // INT8 Quantized Kernel", Inputs):
 //   scale = max(row absmax, 1e-12) / 127, code = clamp(rint(x / scale), -127, 127).
 //
-// One workgroup (4 wave64s) per row.  Each lane loads its 16-byte units with
-// 128-bit loads and keeps the widened values in registers, so the row is read
-// from HBM exactly once: the page's second pass, which re-reads the input and
-// recomputes the activation, is not needed.  The absmax is reduced across the
-// wave with cross-lane max steps and across the four waves through LDS.
+// Rows of up to 128 16-byte units take one wave each (absmax by cross-lane
+// max steps only); rows of up to 2048 units take one workgroup of four waves
+// each (cross-lane steps, then LDS).  Either way each lane loads its units
+// with 128-bit loads and keeps the widened values in registers, so the row is
+// read from HBM exactly once: the page's second pass, which re-reads the
+// input and recomputes the activation, is not needed.
 //
 // Division: x / scale must be the correctly rounded binary32 quotient (it
 // decides the integer code).  Instead of one full IEEE division per element,
@@ -35,8 +36,8 @@ using qm::code_of;
 using qm::pack4;
 using qm::row_scale;
 
-constexpr int kBlock = 256;    // threads per row
-constexpr int kMaxUnits = 8;   // 16-byte input units cached per thread
+constexpr int kBlock = 256;    // threads per workgroup
+constexpr int kMaxUnits = 8;   // 16-byte input units cached per lane
 
 // e^x in binary32 by a fixed sequence so that results are reproducible bit
 // for bit: x = n ln2 + r with n = rint(x / ln 2) and r reduced in two fused
@@ -69,10 +70,97 @@ __device__ __forceinline__ float silu_times(float g, float u) {
   return sg * u;
 }
 
-// Register-cached path: the row (k elements, k % kPerUnit == 0) is split into
-// 16-byte units; lane t holds units t, t + 256, ... (at most kMaxUnits).
-// For SILU the source row has 2k elements: gate units then up units.
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+// Codes of one 16-byte unit of P values, stored as P bytes.  Nontemporal:
+// the codes are not read again by this kernel, and streaming them out keeps
+// them from piling up as dirty cache lines to be written back at the end.
+template <int P>
+__device__ __forceinline__ void store_codes(int8_t* dst, const float (&v)[P], float s, float r) {
+  int c[P];
+#pragma unroll
+  for (int e = 0; e < P; ++e) c[e] = code_of(v[e], s, r);
+  if constexpr (P == 8) {
+    v2u w;
+    w.x = pack4(c[0], c[1], c[2], c[3]);
+    w.y = pack4(c[4], c[5], c[6], c[7]);
+    __builtin_nontemporal_store(w, reinterpret_cast<v2u*>(dst));
+  } else {
+    __builtin_nontemporal_store(pack4(c[0], c[1], c[2], c[3]), reinterpret_cast<uint32_t*>(dst));
+  }
+}
+
+// One 16-byte unit of the input, read once (nontemporal).
+__device__ __forceinline__ uint4 load_unit(const char* p) {
+  const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+
+// The P values of unit u of a row (for SILU: silu(gate) * up, the up half
+// starting k elements after the gate half).
 template <int DT, bool SILU>
+__device__ __forceinline__ void unit_values(const char* base, int k, int u,
+                                            float (&v)[Elem<DT>::kPerUnit]) {
+  using E = Elem<DT>;
+  E::unpack(load_unit(base + static_cast<size_t>(u) * 16), v);
+  if constexpr (SILU) {
+    const uint4 raw_up = load_unit(base + static_cast<size_t>(k) * E::kBytes + static_cast<size_t>(u) * 16);
+    float up[E::kPerUnit];
+    E::unpack(raw_up, up);
+#pragma unroll
+    for (int e = 0; e < E::kPerUnit; ++e) v[e] = silu_times(v[e], up[e]);
+  }
+}
+
+// Short rows (up to 128 units): one wave per row, four rows per workgroup.
+// Lane l holds units l, l + 64 (UPL of them) in registers; the absmax needs
+// only cross-lane steps within the wave (no LDS, no barrier).
+template <int DT, bool SILU, int UPL>
+__global__ __launch_bounds__(kBlock) void quant_rows_wave(const void* __restrict__ src,
+                                                         int8_t* __restrict__ q,
+                                                         float* __restrict__ scale, int m, int k) {
+  using E = Elem<DT>;
+  constexpr int P = E::kPerUnit;
+  const int units = k / P;
+  const int lane = threadIdx.x & 63;
+  const size_t row = static_cast<size_t>(blockIdx.x) * (kBlock / 64) + (threadIdx.x >> 6);
+  if (row >= static_cast<size_t>(m)) return;  // whole waves leave; no barriers below
+  const char* base =
+      static_cast<const char*>(src) + row * static_cast<size_t>(SILU ? 2 : 1) * k * E::kBytes;
+
+  float v[UPL][P];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+    const int u = lane + 64 * j;
+    if (u < units) {
+      unit_values<DT, SILU>(base, k, u, v[j]);
+#pragma unroll
+      for (int e = 0; e < P; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j][e]));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off, 64));
+  float s, r;
+  row_scale(amax, s, r);
+  if (lane == 0) scale[row] = s;
+
+  int8_t* qrow = q + row * static_cast<size_t>(k);
+#pragma unroll
+  for (int j = 0; j < UPL; ++j) {
+    const int u = lane + 64 * j;
+    if (u < units) store_codes<P>(qrow + static_cast<size_t>(u) * P, v[j], s, r);
+  }
+}
+
+// Longer rows: one workgroup (4 waves) per row.  Lane t holds units
+// t, t + 256, ... (UPT of them) in registers, so the row is read from HBM
+// exactly once: the page's second pass, which re-reads the input and
+// recomputes the activation, is not needed.  (Many short-lived waves with a
+// few loads each keep more of the chip's memory pipeline busy than fewer
+// waves with many: measured faster than one wave per row at 512 units.)
+template <int DT, bool SILU, int UPT>
 __global__ __launch_bounds__(kBlock) void quant_rows_cached(const void* __restrict__ src,
                                                            int8_t* __restrict__ q,
                                                            float* __restrict__ scale, int k) {
@@ -83,22 +171,13 @@ __global__ __launch_bounds__(kBlock) void quant_rows_cached(const void* __restri
   const char* base =
       static_cast<const char*>(src) + row * static_cast<size_t>(SILU ? 2 : 1) * k * E::kBytes;
 
-  float v[kMaxUnits][P];
+  float v[UPT][P];
   float amax = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kMaxUnits; ++j) {
+  for (int j = 0; j < UPT; ++j) {
     const int u = threadIdx.x + j * kBlock;
     if (u < units) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(base + static_cast<size_t>(u) * 16);
-      E::unpack(raw, v[j]);
-      if constexpr (SILU) {
-        const uint4 raw_up = *reinterpret_cast<const uint4*>(
-            base + static_cast<size_t>(k) * E::kBytes + static_cast<size_t>(u) * 16);
-        float up[P];
-        E::unpack(raw_up, up);
-#pragma unroll
-        for (int e = 0; e < P; ++e) v[j][e] = silu_times(v[j][e], up[e]);
-      }
+      unit_values<DT, SILU>(base, k, u, v[j]);
 #pragma unroll
       for (int e = 0; e < P; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j][e]));
     }
@@ -110,22 +189,9 @@ __global__ __launch_bounds__(kBlock) void quant_rows_cached(const void* __restri
 
   int8_t* qrow = q + row * static_cast<size_t>(k);
 #pragma unroll
-  for (int j = 0; j < kMaxUnits; ++j) {
+  for (int j = 0; j < UPT; ++j) {
     const int u = threadIdx.x + j * kBlock;
-    if (u < units) {
-      int c[P];
-#pragma unroll
-      for (int e = 0; e < P; ++e) c[e] = code_of(v[j][e], s, r);
-      if constexpr (P == 8) {
-        uint2 w;
-        w.x = pack4(c[0], c[1], c[2], c[3]);
-        w.y = pack4(c[4], c[5], c[6], c[7]);
-        *reinterpret_cast<uint2*>(qrow + static_cast<size_t>(u) * 8) = w;
-      } else {
-        *reinterpret_cast<uint32_t*>(qrow + static_cast<size_t>(u) * 4) =
-            pack4(c[0], c[1], c[2], c[3]);
-      }
-    }
+    if (u < units) store_codes<P>(qrow + static_cast<size_t>(u) * P, v[j], s, r);
   }
 }
 
@@ -159,9 +225,22 @@ hipError_t dispatch(int m, int k, const void* src, int8_t* q, float* scale, hipS
   const bool aligned = (reinterpret_cast<uintptr_t>(src) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(q) % E::kPerUnit == 0) &&
                        (k % E::kPerUnit == 0);
-  const bool fits = k / E::kPerUnit <= kMaxUnits * kBlock;
-  if (aligned && fits)
-    return launch(quant_rows_cached<DT, SILU>, dim3(m), dim3(kBlock), 0, stream, src, q, scale, k);
+  const int units = k / E::kPerUnit;
+  if (aligned && units <= 128) {
+    const dim3 grid((static_cast<unsigned>(m) + kBlock / 64 - 1) / (kBlock / 64));
+    if (units <= 64)
+      return launch(quant_rows_wave<DT, SILU, 1>, grid, dim3(kBlock), 0, stream, src, q, scale, m, k);
+    return launch(quant_rows_wave<DT, SILU, 2>, grid, dim3(kBlock), 0, stream, src, q, scale, m, k);
+  }
+  if (aligned && units <= kBlock * kMaxUnits) {
+    if (units <= kBlock)
+      return launch(quant_rows_cached<DT, SILU, 1>, dim3(m), dim3(kBlock), 0, stream, src, q, scale, k);
+    if (units <= kBlock * 2)
+      return launch(quant_rows_cached<DT, SILU, 2>, dim3(m), dim3(kBlock), 0, stream, src, q, scale, k);
+    if (units <= kBlock * 4)
+      return launch(quant_rows_cached<DT, SILU, 4>, dim3(m), dim3(kBlock), 0, stream, src, q, scale, k);
+    return launch(quant_rows_cached<DT, SILU, 8>, dim3(m), dim3(kBlock), 0, stream, src, q, scale, k);
+  }
   return launch(quant_rows_twopass<DT, SILU>, dim3(m), dim3(kBlock), 0, stream, src, q, scale, k);
 }
 
