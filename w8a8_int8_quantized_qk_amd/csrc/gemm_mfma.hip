@@ -8,10 +8,12 @@
 //   out[i][j] = ((float)acc * scale_a[i]) * (scale_b[j] * output_scale)   (optional)
 //
 // Design for gfx950:
-//   * Workgroup tile 256 (M) x 128 (N), k slice 128 bytes.  Four wave64s in a
-//     2 x 2 grid each own a 128 x 64 sub-tile computed with
+//   * Workgroup tile 256 (M) x 128 (N), k slice 128 bytes, eight wave64s (two
+//     per SIMD).  The waves form two groups of four: each group covers the
+//     whole tile as four 128 x 64 sub-tiles computed with
 //     v_mfma_i32_32x32x32_i8 (4 x 2 instructions per 32-deep k step, 128
-//     INT32 accumulators per lane).  M=2048, N=4096 is 256 tiles: one per CU.
+//     INT32 accumulators per lane), group g multiplying k steps 2g and 2g + 1
+//     of every slice.  M=2048, N=4096 is 256 tiles: one per CU.
 //   * Operands go from global memory straight into LDS with 128-bit
 //     global_load_lds (no register staging): lane l of a wave writes LDS
 //     bytes [16 l, 16 l + 16) above the wave's base address, so each lane
@@ -35,11 +37,16 @@
 //   * Workgroups are dispatched to the 8 XCDs round robin; tiles are renumbered
 //     so the ones running together on one XCD form a compact 4 x 8 block that
 //     shares A rows and B columns in that XCD's L2.
-//   * The epilogue converts each accumulator to binary32 in registers,
-//     multiplies by the per-token and per-channel scales, and stores fp32 or
-//     bf16 (round to nearest even); raw accumulators are stored when asked.
+//   * Epilogue without a row-major staging pass: the two wave groups swap
+//     half of their partial sums through LDS as 16-byte chunks, then each
+//     lane transposes 4 x 4 blocks across its lane quad (DPP) so that it holds
+//     4 consecutive columns of one row, applies the per-token and per-channel
+//     scales in binary32 and stores fp32 or bf16 (round to nearest even), or
+//     the raw accumulators, with nontemporal stores.
 //   * Operands are addressed with 32-bit offsets (m*k, n*k < 2^32).
 #include "qk_internal.h"
+
+#include <type_traits>
 
 namespace qk {
 namespace {
@@ -58,6 +65,8 @@ constexpr int WTM = 128;       // wave tile rows
 constexpr int WTN = 64;        // wave tile columns
 constexpr int FM = WTM / 32;   // 32x32 fragments per wave along M
 constexpr int FN = WTN / 32;   // ... along N
+constexpr int kSubTiles = (BM / WTM) * (BN / WTN);  // wave sub-tiles per workgroup tile
+static_assert(kSubTiles * kGroups == kWaves, "every wave owns one (sub-tile, k group)");
 constexpr int kStages = 3;     // LDS k slices in flight
 constexpr int A_STAGE = BM * BK;
 constexpr int B_STAGE = BN * BK;
@@ -201,6 +210,32 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// 4 x 4 transpose across each quad of lanes: lane i of the quad holds x[k]
+// = element (k, i) of a 4 x 4 block; afterwards y[k] = element (i, k).  Two
+// butterfly steps (partner lane i ^ 1, then i ^ 2), each exchanging the
+// off-diagonal 2 x 2 blocks with DPP quad permutations.
+__device__ __forceinline__ void quad_transpose(int x0, int x1, int x2, int x3, int i, int* y) {
+  // quad_perm(1, 0, 3, 2) = 0xB1: read lane i ^ 1; quad_perm(2, 3, 0, 1) = 0x4E: read lane i ^ 2
+  const bool odd = i & 1;
+  const int p0 = __builtin_amdgcn_mov_dpp(x0, 0xB1, 0xF, 0xF, false);
+  const int p1 = __builtin_amdgcn_mov_dpp(x1, 0xB1, 0xF, 0xF, false);
+  const int p2 = __builtin_amdgcn_mov_dpp(x2, 0xB1, 0xF, 0xF, false);
+  const int p3 = __builtin_amdgcn_mov_dpp(x3, 0xB1, 0xF, 0xF, false);
+  const int a0 = odd ? p1 : x0;
+  const int a1 = odd ? x1 : p0;
+  const int a2 = odd ? p3 : x2;
+  const int a3 = odd ? x3 : p2;
+  const bool hi = i & 2;
+  const int r0 = __builtin_amdgcn_mov_dpp(a0, 0x4E, 0xF, 0xF, false);
+  const int r1 = __builtin_amdgcn_mov_dpp(a1, 0x4E, 0xF, 0xF, false);
+  const int r2 = __builtin_amdgcn_mov_dpp(a2, 0x4E, 0xF, 0xF, false);
+  const int r3 = __builtin_amdgcn_mov_dpp(a3, 0x4E, 0xF, 0xF, false);
+  y[0] = hi ? r2 : a0;
+  y[1] = hi ? r3 : a1;
+  y[2] = hi ? a2 : r0;
+  y[3] = hi ? a3 : r1;
+}
+
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
 // 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  Global-to-LDS loads complete on
 // this counter, so this is how a wave knows its DMA into LDS has landed.
@@ -239,10 +274,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
   const int n0 = tn * BN;
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int grp = (t >> 6) / 4;       // which k steps of a slice this wave multiplies
-  const int wsub = (t >> 6) % 4;      // which 128 x 64 sub-tile it owns
-  const int wm = wsub >> 1;
-  const int wn = wsub & 1;
+  const int grp = (t >> 6) / kSubTiles;  // which k steps of a slice this wave multiplies
+  const int wsub = (t >> 6) % kSubTiles;  // which 128 x 64 sub-tile it owns
+  const int wm = wsub / (BN / WTN);
+  const int wn = wsub % (BN / WTN);
 
   auto a_lds = [&](int s) { return smem + (s % kStages) * STAGE; };
   auto b_lds = [&](int s) { return smem + (s % kStages) * STAGE + A_STAGE; };
@@ -379,105 +414,124 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
   }
 
   // ---- epilogue ----
-  // The two wave groups' INT32 tiles are summed in LDS (row stride padded by
-  // 16 bytes): group 1 stages its accumulators, group 0 adds its own and
-  // writes the sum back in place (each element has the same owner lane in
-  // both groups).  Then all eight waves stream the 128 x 64 sub-tiles out row
-  // by row: eight lanes cover one row's 64 columns, each converting 8
-  // accumulators with the per-token and per-channel scales and writing 16
-  // (bf16) or 32 (fp32) contiguous bytes.
-  constexpr int kRowStride = WTN * 4 + 16;
-  static_assert(4 * WTM * kRowStride + 4 * (BM + BN) <= kStages * STAGE,
-                "epilogue staging fits in LDS");
+  // The two wave groups hold partial sums of the same 128 x 64 sub-tile.
+  // Group g finishes fragment rows i in [2g, 2g + 2): it hands the other
+  // group's fragments over through LDS as 16-byte chunks (4 accumulator
+  // registers), adds the chunks it receives, and stores straight from
+  // registers.  A fragment's register r of lane l is element
+  // (8 (r / 4) + 4 (l / 32) + r % 4, l % 32); a 4 x 4 transpose across each
+  // lane quad (DPP) turns the four registers 4q .. 4q + 3 into four
+  // consecutive columns of one row, so every lane writes 8 (bf16) or 16 (fp32)
+  // contiguous bytes.  Output stores are nontemporal: nothing here reads them.
+  constexpr int kHalfM = FM / kGroups;  // fragment rows finished per group
+  constexpr int kChunkBytes = kHalfM * FN * 4 * 64 * 16;  // one group's hand-over
+  static_assert(2 * kSubTiles * kChunkBytes + 4 * (BM + BN) <= kStages * STAGE,
+                "epilogue hand-over fits in LDS");
   __syncthreads();  // every wave is done with the k slices
-  char* stage = smem + wsub * (WTM * kRowStride);
-  float* s_sa = reinterpret_cast<float*>(smem + 4 * WTM * kRowStride);
+  float* s_sa = reinterpret_cast<float*>(smem + 2 * kSubTiles * kChunkBytes);
   float* s_sb = s_sa + BM;
   if (out) {
-    if (t < BM) s_sa[t] = m0 + t < M ? scale_a[m0 + t] : 0.0f;
-    else if (t - BM < BN) s_sb[t - BM] = n0 + t - BM < N ? scale_b[n0 + t - BM] * output_scale : 0.0f;
+    for (int idx = t; idx < BM + BN; idx += kThreads) {
+      if (idx < BM)
+        s_sa[idx] = m0 + idx < M ? scale_a[m0 + idx] : 0.0f;
+      else
+        s_sb[idx - BM] = n0 + idx - BM < N ? scale_b[n0 + idx - BM] * output_scale : 0.0f;
+    }
   }
-  auto stage_at = [&](int i, int j, int r) -> int* {
-    const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    const int col = j * 32 + (lane & 31);
-    return reinterpret_cast<int*>(stage + row * kRowStride + col * 4);
+  // hand-over region written for group `to` of this sub-tile
+  auto chunk_at = [&](int to, int ii, int j, int q) -> int4* {
+    return reinterpret_cast<int4*>(smem + (wsub * 2 + to) * kChunkBytes +
+                                   (((ii * FN + j) * 4 + q) * 64 + lane) * 16);
   };
-  if (grp == 1) {
+  auto give = [&](auto i_off) {  // fragments i_off .. i_off + kHalfM - 1 go to the other group
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) *stage_at(i, j, r) = acc[i][j][r];
-  }
-  __syncthreads();
-  if (grp == 0) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int ii = 0; ii < kHalfM; ++ii)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int* p = stage_at(i, j, r);
-          *p = *p + acc[i][j][r];
+        for (int q = 0; q < 4; ++q) {
+          const v16i& v = acc[i_off + ii][j];
+          *chunk_at(1 - grp, ii, j, q) = make_int4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
         }
-  }
-  __syncthreads();  // sums and scales visible
-  const int tile_r0 = m0 + wm * WTM;
-  const int cg = lane & 7;  // 8-column group
-  const int gcol = n0 + wn * WTN + 8 * cg;
-  const bool vec_ok = (N % 8 == 0) && (gcol + 8 <= N);
-  float sb[8];
+  };
+  auto take = [&](auto i_off) {  // add the other group's sums for my fragments
 #pragma unroll
-  for (int e = 0; e < 8; ++e) sb[e] = s_sb[wn * WTN + 8 * cg + e];
-#pragma unroll 4
-  for (int it = 0; it < WTM * 8 / 64 / kGroups; ++it) {
-    const int row = (WTM / kGroups) * grp + 8 * it + (lane >> 3);
-    const int grow = tile_r0 + row;
-    if (grow >= M) continue;
-    const int4 v0 = *reinterpret_cast<const int4*>(stage + row * kRowStride + cg * 32);
-    const int4 v1 = *reinterpret_cast<const int4*>(stage + row * kRowStride + cg * 32 + 16);
-    const int v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    const size_t base = static_cast<size_t>(grow) * N + gcol;
-    if (c) {
-      if (vec_ok) {
-        *reinterpret_cast<int4*>(c + base) = v0;
-        *reinterpret_cast<int4*>(c + base + 4) = v1;
-      } else {
-        for (int e = 0; e < 8; ++e)
-          if (gcol + e < N) c[base + e] = v[e];
-      }
-    }
-    if (out) {
-      const float sa = s_sa[wm * WTM + row];
-      float f[8];
+    for (int ii = 0; ii < kHalfM; ++ii)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = (static_cast<float>(v[e]) * sa) * sb[e];
-      if (out_dtype == QK_BF16) {
-        uint16_t* o = static_cast<uint16_t*>(out) + base;
-        if (vec_ok) {
-          uint4 w;
-          w.x = to_bf16(f[0]) | (static_cast<uint32_t>(to_bf16(f[1])) << 16);
-          w.y = to_bf16(f[2]) | (static_cast<uint32_t>(to_bf16(f[3])) << 16);
-          w.z = to_bf16(f[4]) | (static_cast<uint32_t>(to_bf16(f[5])) << 16);
-          w.w = to_bf16(f[6]) | (static_cast<uint32_t>(to_bf16(f[7])) << 16);
-          *reinterpret_cast<uint4*>(o) = w;
-        } else {
-          for (int e = 0; e < 8; ++e)
-            if (gcol + e < N) o[e] = to_bf16(f[e]);
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int4 v = *chunk_at(grp, ii, j, q);
+          acc[i_off + ii][j][4 * q] += v.x;
+          acc[i_off + ii][j][4 * q + 1] += v.y;
+          acc[i_off + ii][j][4 * q + 2] += v.z;
+          acc[i_off + ii][j][4 * q + 3] += v.w;
         }
-      } else {
-        float* o = static_cast<float*>(out) + base;
-        if (vec_ok) {
-          *reinterpret_cast<float4*>(o) = make_float4(f[0], f[1], f[2], f[3]);
-          *reinterpret_cast<float4*>(o + 4) = make_float4(f[4], f[5], f[6], f[7]);
-        } else {
-          for (int e = 0; e < 8; ++e)
-            if (gcol + e < N) o[e] = f[e];
+  };
+  if (grp == 0) give(std::integral_constant<int, kHalfM>{}); else give(std::integral_constant<int, 0>{});
+  __syncthreads();  // hand-over and scales visible
+  if (grp == 0) take(std::integral_constant<int, 0>{}); else take(std::integral_constant<int, kHalfM>{});
+
+  const int quad_i = lane & 3;          // row within the 4-row group after the transpose
+  const int col4 = 4 * ((lane & 31) >> 2);  // first of the lane's 4 columns in a fragment
+  auto finish = [&](auto i_off) {
+#pragma unroll
+    for (int ii = 0; ii < kHalfM; ++ii)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int lcol = wn * WTN + j * 32 + col4;  // tile-local column
+        const int gcol = n0 + lcol;
+        float sb4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sb4[e] = out ? s_sb[lcol + e] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          int v[4];
+          quad_transpose(acc[i_off + ii][j][4 * q], acc[i_off + ii][j][4 * q + 1],
+                         acc[i_off + ii][j][4 * q + 2], acc[i_off + ii][j][4 * q + 3], quad_i, v);
+          const int lrow = wm * WTM + (i_off + ii) * 32 + 8 * q + 4 * (lane >> 5) + quad_i;
+          const int grow = m0 + lrow;
+          if (grow >= M) continue;
+          const size_t base = static_cast<size_t>(grow) * N + gcol;
+          const bool vec_ok = (N % 4 == 0) && (gcol + 4 <= N);
+          if (c) {
+            if (vec_ok) {
+              __builtin_nontemporal_store(v4i{v[0], v[1], v[2], v[3]}, reinterpret_cast<v4i*>(c + base));
+            } else {
+              for (int e = 0; e < 4; ++e)
+                if (gcol + e < N) c[base + e] = v[e];
+            }
+          }
+          if (out) {
+            const float sa = s_sa[lrow];
+            float f[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[e] = (static_cast<float>(v[e]) * sa) * sb4[e];
+            if (out_dtype == QK_BF16) {
+              uint16_t* o = static_cast<uint16_t*>(out) + base;
+              if (vec_ok) {
+                const v2i w = {static_cast<int>(to_bf16(f[0]) | (static_cast<uint32_t>(to_bf16(f[1])) << 16)),
+                               static_cast<int>(to_bf16(f[2]) | (static_cast<uint32_t>(to_bf16(f[3])) << 16))};
+                __builtin_nontemporal_store(w, reinterpret_cast<v2i*>(o));
+              } else {
+                for (int e = 0; e < 4; ++e)
+                  if (gcol + e < N) o[e] = to_bf16(f[e]);
+              }
+            } else {
+              float* o = static_cast<float*>(out) + base;
+              if (vec_ok) {
+                typedef float v4f __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store(v4f{f[0], f[1], f[2], f[3]}, reinterpret_cast<v4f*>(o));
+              } else {
+                for (int e = 0; e < 4; ++e)
+                  if (gcol + e < N) o[e] = f[e];
+              }
+            }
+          }
         }
       }
-    }
-  }
+  };
+  if (grp == 0) finish(std::integral_constant<int, 0>{}); else finish(std::integral_constant<int, kHalfM>{});
 }
 
 template <int MODE>
