@@ -32,8 +32,11 @@ if ROOT not in sys.path:
 
 INT8_PEAK_TOPS = 5000.0     # MI355X dense INT8 MFMA, published
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_prefill_outliers_traffic.txt")
-GEMM_SRC = os.path.join(ROOT, "w8a8_int8_quantized_qk_amd", "csrc", "gemm_mfma.hip")
+CSRC = os.path.join(ROOT, "w8a8_int8_quantized_qk_amd", "csrc")
+GEMM_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_mfma_prefill_outliers_traffic.txt"),
+                os.path.join(CSRC, "gemm_mfma.hip"))
+GEMV_TRAFFIC = (os.path.join(ROOT, "profiles", "gemv_decode_m1_traffic.txt"),
+                os.path.join(CSRC, "gemv.hip"))
 
 
 def _args():
@@ -57,15 +60,17 @@ def _sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic_from_profile():
-    """HBM bytes per GEMM launch from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def _traffic_from_profile(which):
+    """Memory bytes per launch (L2 fetches + writes, scaled by a plain copy's
+    counts) from the committed counter summary, if it was taken on the current
+    kernel source; else None."""
+    summary, src = which
+    if not os.path.exists(summary):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(summary).read()
     m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != _sha(GEMM_SRC):
+    if not m or not t or m.group(1) != _sha(src):
         return None
     return float(t.group(1))
 
@@ -160,7 +165,7 @@ def main():
     ops = 2.0 * m * n * k
     tops = ops / (ms_per_step * 1e-3) / 1e12
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
-    traffic = _traffic_from_profile()
+    traffic = _traffic_from_profile(GEMM_TRAFFIC)
 
     result = {
         "metric": "INT8 TOPS (quant+GEMM) at M=2048,K=N=4096; HBM GB/s at decode M=1",
@@ -219,7 +224,8 @@ def main():
                          "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "avg_launch_us": round(dms * 1e3, 3),
-                         "algorithmic_bytes_per_launch": dbytes, "traffic": None},
+                         "algorithmic_bytes_per_launch": dbytes,
+                         "traffic": _traffic_from_profile(GEMV_TRAFFIC)},
         }
 
     if args.copy_calibration:
