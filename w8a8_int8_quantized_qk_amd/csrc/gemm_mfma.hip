@@ -108,39 +108,47 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 }
 
 // DMA of a k-contiguous tile of ROWS rows x 128 bytes (global rows clamped to
-// rows_valid - 1, k offset clamped into the row).
+// rows_valid - 1, k offset clamped into the row): instruction i of this
+// wave's share (1 KiB = 8 rows each).
+template <int ROWS>
+constexpr int rowk_ops() { return ROWS * BK / 1024 / kWaves; }
+template <int ROWS>
+__device__ __forceinline__ void dma_rowk_one(const int8_t* __restrict__ g, char* lds,
+                                             int rows_valid, int K, int r0, int k0, int i) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int blk = wave * rowk_ops<ROWS>() + i;
+  const int row = blk * 8 + (lane >> 3);
+  const int lchunk = (lane & 7) ^ ((row & 7) ^ ((row >> 2) & 7));
+  const uint32_t gr = static_cast<uint32_t>(min(r0 + row, rows_valid - 1));
+  const uint32_t gk = static_cast<uint32_t>(min(k0 + 16 * lchunk, K - 16));
+  lds_dma16(g + (gr * static_cast<uint32_t>(K) + gk), lds_addr(lds + blk * 1024));
+}
 template <int ROWS>
 __device__ __forceinline__ void dma_rowk(const int8_t* __restrict__ g, char* lds, int rows_valid,
                                          int K, int r0, int k0) {
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  constexpr int kPerWave = ROWS * BK / 1024 / kWaves;
 #pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int blk = wave * kPerWave + i;  // 1 KiB = 8 rows
-    const int row = blk * 8 + (lane >> 3);
-    const int lchunk = (lane & 7) ^ ((row & 7) ^ ((row >> 2) & 7));
-    const uint32_t gr = static_cast<uint32_t>(min(r0 + row, rows_valid - 1));
-    const uint32_t gk = static_cast<uint32_t>(min(k0 + 16 * lchunk, K - 16));
-    lds_dma16(g + (gr * static_cast<uint32_t>(K) + gk), lds_addr(lds + blk * 1024));
-  }
+  for (int i = 0; i < rowk_ops<ROWS>(); ++i) dma_rowk_one<ROWS>(g, lds, rows_valid, K, r0, k0, i);
 }
 
-// DMA of a [K][N] weight tile: 128 k rows x 128 bytes of n.
-__device__ __forceinline__ void dma_kn(const int8_t* __restrict__ b, char* lds, int N, int K,
-                                       int n0, int k0) {
+// DMA of a [K][N] weight tile: 128 k rows x 128 bytes of n; instruction i of
+// this wave's share.
+constexpr int kn_ops() { return BK * BN / 1024 / kWaves; }
+__device__ __forceinline__ void dma_kn_one(const int8_t* __restrict__ b, char* lds, int N, int K,
+                                           int n0, int k0, int i) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  constexpr int kPerWave = BK * BN / 1024 / kWaves;
+  const int blk = wave * kn_ops() + i;
+  const int k = blk * 8 + (lane >> 3);
+  const int lchunk = (lane & 7) ^ (k & 7);
+  const uint32_t gk = static_cast<uint32_t>(min(k0 + k, K - 1));
+  const uint32_t gn = static_cast<uint32_t>(min(n0 + 16 * lchunk, N - 16));
+  lds_dma16(b + (gk * static_cast<uint32_t>(N) + gn), lds_addr(lds + blk * 1024));
+}
+__device__ __forceinline__ void dma_kn(const int8_t* __restrict__ b, char* lds, int N, int K,
+                                       int n0, int k0) {
 #pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int blk = wave * kPerWave + i;
-    const int k = blk * 8 + (lane >> 3);
-    const int lchunk = (lane & 7) ^ (k & 7);
-    const uint32_t gk = static_cast<uint32_t>(min(k0 + k, K - 1));
-    const uint32_t gn = static_cast<uint32_t>(min(n0 + 16 * lchunk, N - 16));
-    lds_dma16(b + (gk * static_cast<uint32_t>(N) + gn), lds_addr(lds + blk * 1024));
-  }
+  for (int i = 0; i < kn_ops(); ++i) dma_kn_one(b, lds, N, K, n0, k0, i);
 }
 
 // ---- register-staged [K][N] weight (N not a multiple of 16) ----
@@ -293,11 +301,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
     if constexpr (MODE == kBknDma) dma_kn(b, b_lds(s), N, K, n0, s * BK);
   };
   constexpr int kFetchOps = BM * BK / 1024 / kWaves + (kRegB ? 0 : BN * BK / 1024 / kWaves);
+  // one DMA instruction of slice s: parts [0, kOpsA) are A, the rest B
+  constexpr int kOpsA = rowk_ops<BM>();
+  auto fetch_part = [&](int s, int part) {
+    if (part < kOpsA) {
+      dma_rowk_one<BM>(a, a_lds(s), M, K, m0, s * BK, part);
+    } else if constexpr (MODE == kBnkDma) {
+      dma_rowk_one<BN>(b, b_lds(s), N, K, n0, s * BK, part - kOpsA);
+    } else if constexpr (MODE == kBknDma) {
+      dma_kn_one(b, b_lds(s), N, K, n0, s * BK, part - kOpsA);
+    }
+  };
 
   // fragment reads: A (and [N][K] / register-staged B) with 128-bit reads;
   // a DMA'd [K][N] B with two transpose reads per lane
   const int a_row = wm * WTM + (lane & 31);
   const int b_row = wn * WTN + (lane & 31);
+  // single-fragment reads for the interleaved schedule
+  auto read_a = [&](const char* As, int kk, int i) -> v4i {
+    return *reinterpret_cast<const v4i*>(As + rowk_offset(a_row + i * 32, 2 * kk + (lane >> 5)));
+  };
+  // B fragment j: a [K][N] weight takes two transpose reads (half 0 and 1)
+  auto read_b_tr = [&](const char* Bs, int kk, int j, int h) -> v2i {
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
+    const int kr = 32 * kk + 16 * (g >> 1) + (i16 >> 1) + 8 * h;
+    const int cb = (wn * WTN + j * 32 + 16 * (g & 1)) >> 4;
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i*)(Bs + kn_offset(kr, cb) + 8 * (i16 & 1)));
+  };
+  auto read_b_rowk = [&](const char* Bs, int kk, int j) -> v4i {
+    return *reinterpret_cast<const v4i*>(Bs + rowk_offset(b_row + j * 32, 2 * kk + (lane >> 5)));
+  };
   auto read_frags = [&](const char* As, const char* Bs, int kk, v4i* fa, v4i* fb) {
     const int chunk = 2 * kk + (lane >> 5);
 #pragma unroll
@@ -373,43 +408,119 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
   //   step 2nd: wait for this wave's DMA of slice kt + 1, barrier (all DMA
   //             landed, all reads of slice kt done), then 8 MFMAs interleaved
   //             with the reads of slice kt + 1's first step.
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 2 < KT) fetch(kt + 2);
-    if constexpr (kRegB) {
-      if (kt + 1 < KT) breg.load(b, N, K, n0, (kt + 1) * BK);
-    }
-    const char* As = a_lds(kt);
-    const char* Bs = b_lds(kt);
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
-      const int cur = st & 1;
-      const int nxt = cur ^ 1;
-      if (st + 1 < kSteps) {
-        read_frags(As, Bs, kSteps * grp + st + 1, af[nxt], bf[nxt]);
-      } else if (kt + 1 < KT) {
-        if constexpr (kRegB) {
-          wait_vmcnt<0>();
-          breg.store(b_lds(kt + 1));
-        } else {
-          if (kt + 2 < KT) wait_vmcnt<kFetchOps>(); else wait_vmcnt<0>();
+  if constexpr (kRegB) {
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + 2 < KT) fetch(kt + 2);
+      if constexpr (kRegB) {
+        if (kt + 1 < KT) breg.load(b, N, K, n0, (kt + 1) * BK);
+      }
+      const char* As = a_lds(kt);
+      const char* Bs = b_lds(kt);
+  #pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        const int cur = st & 1;
+        const int nxt = cur ^ 1;
+        if (st + 1 < kSteps) {
+          read_frags(As, Bs, kSteps * grp + st + 1, af[nxt], bf[nxt]);
+        } else if (kt + 1 < KT) {
+          if constexpr (kRegB) {
+            wait_vmcnt<0>();
+            breg.store(b_lds(kt + 1));
+          } else {
+            if (kt + 2 < KT) wait_vmcnt<kFetchOps>(); else wait_vmcnt<0>();
+          }
+          __syncthreads();
+          if (KTAIL && kt + 1 == KT - 1) zero_tail(kt + 1);
+          read_frags(a_lds(kt + 1), b_lds(kt + 1), kSteps * grp, af[nxt], bf[nxt]);
         }
-        __syncthreads();
-        if (KTAIL && kt + 1 == KT - 1) zero_tail(kt + 1);
-        read_frags(a_lds(kt + 1), b_lds(kt + 1), kSteps * grp, af[nxt], bf[nxt]);
+  #pragma unroll
+        for (int i = 0; i < FM; ++i)
+  #pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[cur][j], acc[i][j], 0,
+                                                              0, 0);
+        // issue order: two LDS reads, one MFMA, ... then the remaining MFMAs
+  #pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
+    }
+  } else {
+    // DMA modes: the slice's DMA instructions are spread through the MFMA
+    // stream (one after every few MFMAs) instead of issued together: a CU
+    // accepts its loads at a limited rate, and a wave waiting to issue one
+    // cannot issue its MFMAs either.  Step 0 issues parts [0, kSplit) of
+    // slice kt + 2, step 1 (after the barrier) the rest.
+    static_assert(FM == 4 && FN == 2 && kSteps == 2, "interleave pattern below");
+    constexpr int kSplit = kFetchOps / 2;
+    for (int kt = 0; kt < KT; ++kt) {
+      const bool prefetch = kt + 2 < KT;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int st = 0; st < kSteps; ++st) {
+        const int cur = st & 1;
+        const int nxt = cur ^ 1;
+        const char* As = a_lds(kt);
+        const char* Bs = b_lds(kt);
+        // the next step's fragments are read unconditionally (after the last
+        // slice they come from a valid, unused LDS slice and are not used):
+        // no branches around LDS reads, so their waits stay exact
+        int kk_next = kSteps * grp + st + 1;
+        if (st + 1 == kSteps) {
+          if (kt + 1 < KT) {
+            if (prefetch) wait_vmcnt<kSplit>(); else wait_vmcnt<0>();
+            __syncthreads();
+            if (KTAIL && kt + 1 == KT - 1) zero_tail(kt + 1);
+          }
+          As = a_lds(kt + 1);
+          Bs = b_lds(kt + 1);
+          kk_next = kSteps * grp;
+        }
+        const int part0 = st * kSplit;
+        auto mfma = [&](int i, int j) {
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[cur][j], acc[i][j], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        auto dma = [&](int q) {
+          if (prefetch && q < kSplit) fetch_part(kt + 2, part0 + q);
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        v2i blo[FN], bhi[FN];
+        mfma(0, 0);
+        af[nxt][0] = read_a(As, kk_next, 0);
+        mfma(0, 1);
+        af[nxt][1] = read_a(As, kk_next, 1);
+        dma(0);
+        mfma(1, 0);
+        af[nxt][2] = read_a(As, kk_next, 2);
+        mfma(1, 1);
+        af[nxt][3] = read_a(As, kk_next, 3);
+        dma(1);
+        mfma(2, 0);
+        if constexpr (MODE == kBknDma) {
+          blo[0] = read_b_tr(Bs, kk_next, 0, 0);
+          mfma(2, 1);
+          bhi[0] = read_b_tr(Bs, kk_next, 0, 1);
+          dma(2);
+          mfma(3, 0);
+          blo[1] = read_b_tr(Bs, kk_next, 1, 0);
+          mfma(3, 1);
+          bhi[1] = read_b_tr(Bs, kk_next, 1, 1);
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[cur][j], acc[i][j], 0,
-                                                            0, 0);
-      // issue order: two LDS reads, one MFMA, ... then the remaining MFMAs
+          for (int j = 0; j < FN; ++j) bf[nxt][j] = v4i{blo[j].x, blo[j].y, bhi[j].x, bhi[j].y};
+        } else {
+          bf[nxt][0] = read_b_rowk(Bs, kk_next, 0);
+          mfma(2, 1);
+          dma(2);
+          mfma(3, 0);
+          bf[nxt][1] = read_b_rowk(Bs, kk_next, 1);
+          mfma(3, 1);
+        }
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        for (int q = 3; q < kSplit; ++q) dma(q);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
   }
 
