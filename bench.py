@@ -7,6 +7,9 @@ measured in the same run: HBM GB/s of the decode linear at M = 1 (X bf16
 [1, 4096], W int8 [4096, 14336]; bytes = W + s_ch + X + out per call).
 
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
+Before the W warmup steps the captured steps are replayed for --settle-seconds
+(default 0.2 s): after idling, the GPU takes tens of milliseconds to reach its
+steady clock, and a short warmup would time that ramp instead.
 Each step uses the next of R buffer sets (R x ~59 MB > the 256 MB Infinity
 Cache plus L2), so weights and activations come from HBM, not cache.  Steps
 are captured in HIP graphs and replayed, so the GPU is not left waiting for
@@ -45,6 +48,9 @@ def _args():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--ring", type=int, default=8, help="buffer sets cycled through")
+    p.add_argument("--settle-seconds", type=float, default=0.2,
+                   help="replay the captured steps this long before the warmup steps: the GPU "
+                        "takes tens of milliseconds to reach its steady clock after idling")
     p.add_argument("--decode-calls", type=int, default=400)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target duration of the CPU oracle baseline sample")
@@ -121,6 +127,10 @@ def main():
                 for i in range(n % R):
                     singles[i].replay()
 
+        t_settle = time.perf_counter()
+        while time.perf_counter() - t_settle < args.settle_seconds:
+            run(8 * R)
+            torch.cuda.synchronize()
         run(warmup)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -192,6 +202,7 @@ def main():
         "step_frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
         "quant_kernel_us": round(quant_ms * 1e3, 3),
         "wall_s_timed_region": round(wall, 4),
+        "settle_s_before_warmup": args.settle_seconds,
     }
 
     # ---------------- decode: M = 1 linear (second metric) ----------------
