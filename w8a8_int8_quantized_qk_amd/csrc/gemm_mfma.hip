@@ -44,6 +44,7 @@
 //     scales in binary32 and stores fp32 or bf16 (round to nearest even), or
 //     the raw accumulators, with nontemporal stores.
 //   * Operands are addressed with 32-bit offsets (m*k, n*k < 2^32).
+#include "lds_dma.h"
 #include "qk_internal.h"
 
 #include <type_traits>
@@ -86,25 +87,6 @@ __device__ __forceinline__ int rowk_offset(int row, int chunk) {
 // [k][n] weight tile: 128-byte rows of n
 __device__ __forceinline__ int kn_offset(int k, int chunk) {
   return k * BN + ((chunk ^ (k & 7)) << 4);
-}
-
-// One 128-bit global-to-LDS load: this lane's 16 bytes at g go to LDS byte
-// lds_base + 16 * lane (lds_base is the wave-uniform LDS address in m0).
-// Written as inline assembly so that the compiler does not treat every later
-// LDS read as possibly aliasing the transfer (which makes it wait for all
-// outstanding loads before each read); completion is tracked explicitly with
-// wait_vmcnt before the barrier that publishes the slice.  The instruction
-// has no register results.  m0 is written here and nowhere else in the kernel.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds_base)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  return __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p)));
 }
 
 // DMA of a k-contiguous tile of ROWS rows x 128 bytes (global rows clamped to
@@ -242,15 +224,6 @@ __device__ __forceinline__ void quad_transpose(int x0, int x1, int x2, int x3, i
   y[1] = hi ? r3 : a1;
   y[2] = hi ? a2 : r0;
   y[3] = hi ? a3 : r1;
-}
-
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  Global-to-LDS loads complete on
-// this counter, so this is how a wave knows its DMA into LDS has landed.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 constexpr int kGroupM = 4;
