@@ -11,9 +11,13 @@
 //   * Workgroup tile 256 (M) x 128 (N), k slice 128 bytes, eight wave64s (two
 //     per SIMD).  The waves form two groups of four: each group covers the
 //     whole tile as four 128 x 64 sub-tiles computed with
-//     v_mfma_i32_32x32x32_i8 (4 x 2 instructions per 32-deep k step, 128
-//     INT32 accumulators per lane), group g multiplying k steps 2g and 2g + 1
+//     v_mfma_i32_16x16x64_i8 (8 x 4 instructions per 64-deep k step, 128
+//     INT32 accumulators per lane), group g multiplying bytes [64 g, 64 g + 64)
 //     of every slice.  M=2048, N=4096 is 256 tiles: one per CU.
+//   * 16x16x64 rather than 32x32x32: the chip runs power-limited here, and on
+//     this workload's operands the same MACs issued as 16x16x64 draw less
+//     power per MAC (a pure MFMA loop measured 24% faster at equal work; with
+//     all-zero operands both shapes run at the same rate).
 //   * Operands go from global memory straight into LDS with 128-bit
 //     global_load_lds (no register staging): lane l of a wave writes LDS
 //     bytes [16 l, 16 l + 16) above the wave's base address, so each lane
@@ -21,13 +25,14 @@
 //     slices (3 x 48 KiB) let slice s + 2 stream in while slice s is
 //     multiplied; one barrier per slice.
 //   * A (and a weight stored [N][K]) is kept k-contiguous, 128-byte rows with
-//     the 16-byte chunk index XORed by (row & 7) ^ ((row >> 2) & 7): the eight
-//     lanes served together by a 128-bit LDS read see eight distinct chunks.
+//     the 16-byte chunk index XORed by (row >> 1) & 7: the 16 lanes served
+//     together by a 128-bit fragment read (16 consecutive rows, one chunk)
+//     hit 16 distinct 16-byte bank groups.
 //   * A weight stored [K][N] (n contiguous) stays [k][n] in LDS (chunk index
-//     XORed by k & 7) and is read with ds_read_b64_tr_b8: a 16-lane group
-//     reads an 8 (k) x 16 (n) byte block and lane j receives column j's eight
-//     k values, which is the k-contiguous MFMA operand; two such reads give
-//     the 16 bytes of a lane.  No VALU transposes are needed.
+//     XORed by (k & 7) ^ ((k >> 4) & 1)) and is read with ds_read_b64_tr_b8: a
+//     16-lane group reads an 8 (k) x 16 (n) byte block and lane j receives
+//     column j's eight k values, which is the k-contiguous MFMA operand; two
+//     such reads give the 16 bytes of a lane.  No VALU transposes are needed.
 //   * For a [K][N] weight whose N is not a multiple of 16, B falls back to
 //     register staging (dword or byte loads, 4 x 4 byte transposes with
 //     v_perm_b32, LDS writes in the [n][k] layout).
@@ -54,7 +59,6 @@ namespace {
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;   // 8: two per SIMD
@@ -64,8 +68,8 @@ constexpr int BN = 128;
 constexpr int BK = 128;
 constexpr int WTM = 128;       // wave tile rows
 constexpr int WTN = 64;        // wave tile columns
-constexpr int FM = WTM / 32;   // 32x32 fragments per wave along M
-constexpr int FN = WTN / 32;   // ... along N
+constexpr int FM = WTM / 16;   // 16x16 fragments per wave along M
+constexpr int FN = WTN / 16;   // ... along N
 constexpr int kSubTiles = (BM / WTM) * (BN / WTN);  // wave sub-tiles per workgroup tile
 static_assert(kSubTiles * kGroups == kWaves, "every wave owns one (sub-tile, k group)");
 constexpr int kStages = 3;     // LDS k slices in flight
@@ -81,12 +85,14 @@ enum BMode {
 };
 
 // k-contiguous tiles (A, [N][K] weight): 128-byte rows
+__device__ __forceinline__ int rowk_swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int rowk_offset(int row, int chunk) {
-  return row * BK + ((chunk ^ ((row & 7) ^ ((row >> 2) & 7))) << 4);
+  return row * BK + ((chunk ^ rowk_swz(row)) << 4);
 }
 // [k][n] weight tile: 128-byte rows of n
+__device__ __forceinline__ int kn_swz(int k) { return (k & 7) ^ ((k >> 4) & 1); }
 __device__ __forceinline__ int kn_offset(int k, int chunk) {
-  return k * BN + ((chunk ^ (k & 7)) << 4);
+  return k * BN + ((chunk ^ kn_swz(k)) << 4);
 }
 
 // DMA of a k-contiguous tile of ROWS rows x 128 bytes (global rows clamped to
@@ -101,7 +107,7 @@ __device__ __forceinline__ void dma_rowk_one(const int8_t* __restrict__ g, char*
   const int lane = threadIdx.x & 63;
   const int blk = wave * rowk_ops<ROWS>() + i;
   const int row = blk * 8 + (lane >> 3);
-  const int lchunk = (lane & 7) ^ ((row & 7) ^ ((row >> 2) & 7));
+  const int lchunk = (lane & 7) ^ rowk_swz(row);
   const uint32_t gr = static_cast<uint32_t>(min(r0 + row, rows_valid - 1));
   const uint32_t gk = static_cast<uint32_t>(min(k0 + 16 * lchunk, K - 16));
   lds_dma16(g + (gr * static_cast<uint32_t>(K) + gk), lds_addr(lds + blk * 1024));
@@ -122,7 +128,7 @@ __device__ __forceinline__ void dma_kn_one(const int8_t* __restrict__ b, char* l
   const int lane = threadIdx.x & 63;
   const int blk = wave * kn_ops() + i;
   const int k = blk * 8 + (lane >> 3);
-  const int lchunk = (lane & 7) ^ (k & 7);
+  const int lchunk = (lane & 7) ^ kn_swz(k);
   const uint32_t gk = static_cast<uint32_t>(min(k0 + k, K - 1));
   const uint32_t gn = static_cast<uint32_t>(min(n0 + 16 * lchunk, N - 16));
   lds_dma16(b + (gk * static_cast<uint32_t>(N) + gn), lds_addr(lds + blk * 1024));
@@ -291,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
       if (q < kOpsA) {
         const int blk = wave * kOpsA + q;
         const int row = blk * 8 + (lane >> 3);
-        const int lchunk = (lane & 7) ^ ((row & 7) ^ ((row >> 2) & 7));
+        const int lchunk = (lane & 7) ^ rowk_swz(row);
         const uint32_t gr = static_cast<uint32_t>(min(m0 + row, M - 1));
         part_src[q] = a + (gr * static_cast<uint32_t>(K) + 16 * lchunk);
         part_lds[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(blk * 1024));
@@ -299,7 +305,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
       } else if constexpr (MODE == kBnkDma) {
         const int blk = wave * rowk_ops<BN>() + (q - kOpsA);
         const int row = blk * 8 + (lane >> 3);
-        const int lchunk = (lane & 7) ^ ((row & 7) ^ ((row >> 2) & 7));
+        const int lchunk = (lane & 7) ^ rowk_swz(row);
         const uint32_t gr = static_cast<uint32_t>(min(n0 + row, N - 1));
         part_src[q] = b + (gr * static_cast<uint32_t>(K) + 16 * lchunk);
         part_lds[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(A_STAGE + blk * 1024));
@@ -307,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
       } else {
         const int blk = wave * kn_ops() + (q - kOpsA);
         const int k = blk * 8 + (lane >> 3);
-        const int lchunk = (lane & 7) ^ (k & 7);
+        const int lchunk = (lane & 7) ^ kn_swz(k);
         const uint32_t gn = static_cast<uint32_t>(min(n0 + 16 * lchunk, N - 16));
         part_src[q] = b + (static_cast<uint32_t>(k) * static_cast<uint32_t>(N) + gn);
         part_lds[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(A_STAGE + blk * 1024));
@@ -328,58 +334,43 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
     }
   };
 
-  // fragment reads: A (and [N][K] / register-staged B) with 128-bit reads;
-  // a DMA'd [K][N] B with two transpose reads per lane
-  const int a_row = wm * WTM + (lane & 31);
-  const int b_row = wn * WTN + (lane & 31);
-  // single-fragment reads for the interleaved schedule
-  auto read_a = [&](const char* As, int kk, int i) -> v4i {
-    return *reinterpret_cast<const v4i*>(As + rowk_offset(a_row + i * 32, 2 * kk + (lane >> 5)));
+  // Fragments of v_mfma_i32_16x16x64_i8: lane l holds 16 k-consecutive bytes,
+  // k = 16 (l / 16) .. + 15 of the wave group's 64-byte k step, of row l % 16
+  // (A) or column l % 16 (B) of the fragment.  A (and [N][K] / register-staged
+  // B) take one 128-bit read; a DMA'd [K][N] B takes two transpose reads.
+  const int kchunk = 4 * grp + (lane >> 4);  // the lane's 16-byte chunk of a slice row
+  const int a_row = wm * WTM + (lane & 15);
+  const int b_row = wn * WTN + (lane & 15);
+  auto read_a = [&](const char* As, int i) -> v4i {
+    return *reinterpret_cast<const v4i*>(As + rowk_offset(a_row + i * 16, kchunk));
   };
-  // B fragment j: a [K][N] weight takes two transpose reads (half 0 and 1)
-  auto read_b_tr = [&](const char* Bs, int kk, int j, int h) -> v2i {
-    const int g = lane >> 4;
+  // B fragment j of a [K][N] weight: transpose read h covers k rows 8h .. 8h + 7
+  // of the lane's 16
+  auto read_b_tr = [&](const char* Bs, int j, int h) -> v2i {
     const int i16 = lane & 15;
-    const int kr = 32 * kk + 16 * (g >> 1) + (i16 >> 1) + 8 * h;
-    const int cb = (wn * WTN + j * 32 + 16 * (g & 1)) >> 4;
+    const int kr = 64 * grp + 16 * (lane >> 4) + (i16 >> 1) + 8 * h;
+    const int cb = (wn * WTN + j * 16) >> 4;
     return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
         (__attribute__((address_space(3))) v2i*)(Bs + kn_offset(kr, cb) + 8 * (i16 & 1)));
   };
-  auto read_b_rowk = [&](const char* Bs, int kk, int j) -> v4i {
-    return *reinterpret_cast<const v4i*>(Bs + rowk_offset(b_row + j * 32, 2 * kk + (lane >> 5)));
+  auto read_b_rowk = [&](const char* Bs, int j) -> v4i {
+    return *reinterpret_cast<const v4i*>(Bs + rowk_offset(b_row + j * 16, kchunk));
   };
-  auto read_frags = [&](const char* As, const char* Bs, int kk, v4i* fa, v4i* fb) {
-    const int chunk = 2 * kk + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-      fa[i] = *reinterpret_cast<const v4i*>(As + rowk_offset(a_row + i * 32, chunk));
+  auto read_b = [&](const char* Bs, int j) -> v4i {
     if constexpr (MODE == kBknDma) {
-      const int g = lane >> 4;        // 16-lane group
-      const int i16 = lane & 15;
-      const int kr = 32 * kk + 16 * (g >> 1) + (i16 >> 1);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int cb = (wn * WTN + j * 32 + 16 * (g & 1)) >> 4;  // chunk of 16 columns
-        const int half = 8 * (i16 & 1);
-        const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i*)(Bs + kn_offset(kr, cb) + half));
-        const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i*)(Bs + kn_offset(kr + 8, cb) + half));
-        fb[j] = v4i{lo.x, lo.y, hi.x, hi.y};
-      }
+      const v2i lo = read_b_tr(Bs, j, 0);
+      const v2i hi = read_b_tr(Bs, j, 1);
+      return v4i{lo.x, lo.y, hi.x, hi.y};
     } else {
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        fb[j] = *reinterpret_cast<const v4i*>(Bs + rowk_offset(b_row + j * 32, chunk));
+      return read_b_rowk(Bs, j);
     }
   };
 
-  v16i acc[FM][FN];
+  v4i acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v16i{};
-
+    for (int j = 0; j < FN; ++j) acc[i][j] = v4i{};
 
   const int KT = (K + BK - 1) / BK;
 
@@ -396,8 +387,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
     __syncthreads();
   };
 
-  constexpr int kSteps = BK / 32 / kGroups;  // MFMA steps per wave per slice
-  v4i af[2][FM], bf[2][FN];
+  v4i fa[FM], fb[FN];  // fragments of the slice being multiplied
   if (KT > 0) {
     fetch(0);
     if constexpr (kRegB) breg.load(b, N, K, n0, 0);
@@ -410,147 +400,188 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
     }
     __syncthreads();
     if (KTAIL && KT == 1) zero_tail(0);
-    read_frags(a_lds(0), b_lds(0), kSteps * grp, af[0], bf[0]);
+    // the DMA schedule below reads fragments A 4..7 and B 2..3 of a slice
+    // while it multiplies the others
+    constexpr int kFirstA = kRegB ? FM : FM / 2;
+    constexpr int kFirstB = kRegB ? FN : FN / 2;
+#pragma unroll
+    for (int i = 0; i < kFirstA; ++i) fa[i] = read_a(a_lds(0), i);
+#pragma unroll
+    for (int j = 0; j < kFirstB; ++j) fb[j] = read_b(b_lds(0), j);
   }
 
-  // Software pipeline, one k slice per iteration.  A slice has 4 MFMA steps
-  // of 32 k; wave group g multiplies steps 2g and 2g + 1 (both groups cover
-  // the same output sub-tiles, their sums are added at the end).  Per slice:
-  //   top:      issue the DMA of slice kt + 2 (its LDS slice was last read in
-  //             iteration kt - 1, before that iteration's barrier);
-  //   step 1st: 8 MFMAs on the fragments in registers, interleaved with the
-  //             LDS reads of the second step's fragments;
-  //   step 2nd: wait for this wave's DMA of slice kt + 1, barrier (all DMA
-  //             landed, all reads of slice kt done), then 8 MFMAs interleaved
-  //             with the reads of slice kt + 1's first step.
   if constexpr (kRegB) {
+    // register-staged weight (N not a multiple of 16): one slice per
+    // iteration, the next slice's B staged through registers
     for (int kt = 0; kt < KT; ++kt) {
       if (kt + 2 < KT) fetch(kt + 2);
-      if constexpr (kRegB) {
-        if (kt + 1 < KT) breg.load(b, N, K, n0, (kt + 1) * BK);
-      }
-      const char* As = a_lds(kt);
-      const char* Bs = b_lds(kt);
-  #pragma unroll
-      for (int st = 0; st < kSteps; ++st) {
-        const int cur = st & 1;
-        const int nxt = cur ^ 1;
-        if (st + 1 < kSteps) {
-          read_frags(As, Bs, kSteps * grp + st + 1, af[nxt], bf[nxt]);
-        } else if (kt + 1 < KT) {
-          if constexpr (kRegB) {
-            wait_vmcnt<0>();
-            breg.store(b_lds(kt + 1));
-          } else {
-            if (kt + 2 < KT) wait_vmcnt<kFetchOps>(); else wait_vmcnt<0>();
-          }
-          __syncthreads();
-          if (KTAIL && kt + 1 == KT - 1) zero_tail(kt + 1);
-          read_frags(a_lds(kt + 1), b_lds(kt + 1), kSteps * grp, af[nxt], bf[nxt]);
-        }
-  #pragma unroll
-        for (int i = 0; i < FM; ++i)
-  #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[cur][j], acc[i][j], 0,
-                                                              0, 0);
-        // issue order: two LDS reads, one MFMA, ... then the remaining MFMAs
-  #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (kt + 1 < KT) breg.load(b, N, K, n0, (kt + 1) * BK);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      if (kt + 1 < KT) {
+        wait_vmcnt<0>();
+        breg.store(b_lds(kt + 1));
+        __syncthreads();
+        if (KTAIL && kt + 1 == KT - 1) zero_tail(kt + 1);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[i] = read_a(a_lds(kt + 1), i);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[j] = read_b_rowk(b_lds(kt + 1), j);
       }
     }
   } else {
-    // DMA modes: the slice's DMA instructions are spread through the MFMA
-    // stream (one after every few MFMAs) instead of issued together: a CU
+    // DMA modes, one k slice per iteration in two phases, every instruction's
+    // place pinned by sched_barrier:
+    //   phase 0: MFMAs of A 0..3 x B 0..1, interleaved with the LDS reads of
+    //            this slice's A 4..7 and B 2..3 and DMA parts [0, kSplit) of
+    //            slice kt + 2 (its LDS slice was last read in iteration kt - 2);
+    //   barrier: this wave's DMA of slice kt + 1 has landed (vmcnt), then all
+    //            waves' (s_barrier);
+    //   phase 1: the other 24 MFMAs, interleaved with the reads of slice
+    //            kt + 1's A 0..3 and B 0..1 (each into a fragment that has
+    //            just been used for the last time) and the remaining DMA
+    //            parts.
+    // The DMA instructions are spread through the MFMA stream because a CU
     // accepts its loads at a limited rate, and a wave waiting to issue one
-    // cannot issue its MFMAs either.  Step 0 issues parts [0, kSplit) of
-    // slice kt + 2, step 1 (after the barrier) the rest.
-    static_assert(FM == 4 && FN == 2 && kSteps == 2, "interleave pattern below");
+    // cannot issue its MFMAs either.
+    static_assert(FM == 8 && FN == 4, "interleave pattern below");
     constexpr int kSplit = kFetchOps / 2;
+    static_assert(kFetchOps == 2 * kSplit && kSplit >= 3, "three DMA slots per phase");
     for (int kt = 0; kt < KT; ++kt) {
       const bool prefetch = kt + 2 < KT;
-#pragma unroll
-      for (int st = 0; st < kSteps; ++st) {
-        const int cur = st & 1;
-        const int nxt = cur ^ 1;
+      auto mfma = [&](int i, int j) {
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto dma = [&](int part) {
+        if (prefetch) fetch_part(kt + 2, part);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // ---- phase 0 ----
+      {
         const char* As = a_lds(kt);
         const char* Bs = b_lds(kt);
-        // the next step's fragments are read unconditionally (after the last
-        // slice they come from a valid, unused LDS slice and are not used):
-        // no branches around LDS reads, so their waits stay exact
-        int kk_next = kSteps * grp + st + 1;
-        if (st + 1 == kSteps) {
-          if (kt + 1 < KT) {
-            if (prefetch) wait_vmcnt<kSplit>(); else wait_vmcnt<0>();
-            __syncthreads();
-            if (KTAIL && kt + 1 == KT - 1) zero_tail(kt + 1);
-          }
-          As = a_lds(kt + 1);
-          Bs = b_lds(kt + 1);
-          kk_next = kSteps * grp;
-        }
-        const int part0 = st * kSplit;
-        auto mfma = [&](int i, int j) {
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[cur][j], acc[i][j], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        };
-        auto dma = [&](int q) {
-          if (prefetch && q < kSplit) fetch_part(kt + 2, part0 + q);
-          __builtin_amdgcn_sched_barrier(0);
-        };
-        v2i blo[FN], bhi[FN];
+        v2i lo[2], hi[2];
         mfma(0, 0);
-        af[nxt][0] = read_a(As, kk_next, 0);
+        fa[4] = read_a(As, 4);
         mfma(0, 1);
-        af[nxt][1] = read_a(As, kk_next, 1);
+        fa[5] = read_a(As, 5);
         dma(0);
         mfma(1, 0);
-        af[nxt][2] = read_a(As, kk_next, 2);
+        fa[6] = read_a(As, 6);
         mfma(1, 1);
-        af[nxt][3] = read_a(As, kk_next, 3);
+        fa[7] = read_a(As, 7);
         dma(1);
-        mfma(2, 0);
         if constexpr (MODE == kBknDma) {
-          blo[0] = read_b_tr(Bs, kk_next, 0, 0);
+          mfma(2, 0);
+          lo[0] = read_b_tr(Bs, 2, 0);
           mfma(2, 1);
-          bhi[0] = read_b_tr(Bs, kk_next, 0, 1);
+          hi[0] = read_b_tr(Bs, 2, 1);
           dma(2);
           mfma(3, 0);
-          blo[1] = read_b_tr(Bs, kk_next, 1, 0);
+          lo[1] = read_b_tr(Bs, 3, 0);
           mfma(3, 1);
-          bhi[1] = read_b_tr(Bs, kk_next, 1, 1);
-#pragma unroll
-          for (int j = 0; j < FN; ++j) bf[nxt][j] = v4i{blo[j].x, blo[j].y, bhi[j].x, bhi[j].y};
+          hi[1] = read_b_tr(Bs, 3, 1);
+          fb[2] = v4i{lo[0].x, lo[0].y, hi[0].x, hi[0].y};
+          fb[3] = v4i{lo[1].x, lo[1].y, hi[1].x, hi[1].y};
         } else {
-          bf[nxt][0] = read_b_rowk(Bs, kk_next, 0);
+          mfma(2, 0);
+          fb[2] = read_b_rowk(Bs, 2);
           mfma(2, 1);
           dma(2);
           mfma(3, 0);
-          bf[nxt][1] = read_b_rowk(Bs, kk_next, 1);
+          fb[3] = read_b_rowk(Bs, 3);
           mfma(3, 1);
         }
 #pragma unroll
         for (int q = 3; q < kSplit; ++q) dma(q);
+      }
+      // ---- barrier for slice kt + 1 ----
+      if (kt + 1 < KT) {
+        if (prefetch) wait_vmcnt<kSplit>(); else wait_vmcnt<0>();
+        __syncthreads();
+        if (KTAIL && kt + 1 == KT - 1) zero_tail(kt + 1);
+      }
+      // ---- phase 1 ----
+      {
+        // after the last slice these reads come from a valid, unused LDS
+        // slice and are not used: no branches around LDS reads, so the
+        // compiler's waits for them stay exact
+        const char* As = a_lds(kt + 1);
+        const char* Bs = b_lds(kt + 1);
+        v4i na[4], nb[2];
+        v2i lo[2], hi[2];
+        mfma(0, 2);
+        mfma(0, 3);
+        na[0] = read_a(As, 0);
+        mfma(1, 2);
+        dma(kSplit + 0);
+        mfma(1, 3);
+        na[1] = read_a(As, 1);
+        mfma(2, 2);
+        mfma(2, 3);
+        na[2] = read_a(As, 2);
+        mfma(3, 2);
+        dma(kSplit + 1);
+        mfma(3, 3);
+        na[3] = read_a(As, 3);
+        mfma(4, 0);
+        mfma(5, 0);
+        dma(kSplit + 2);
+        mfma(6, 0);
+        mfma(7, 0);
+        if constexpr (MODE == kBknDma) {
+          lo[0] = read_b_tr(Bs, 0, 0);
+          mfma(4, 1);
+          hi[0] = read_b_tr(Bs, 0, 1);
+          mfma(5, 1);
+          mfma(6, 1);
+          mfma(7, 1);
+          lo[1] = read_b_tr(Bs, 1, 0);
+          mfma(4, 2);
+          hi[1] = read_b_tr(Bs, 1, 1);
+          nb[0] = v4i{lo[0].x, lo[0].y, hi[0].x, hi[0].y};
+          nb[1] = v4i{lo[1].x, lo[1].y, hi[1].x, hi[1].y};
+        } else {
+          nb[0] = read_b_rowk(Bs, 0);
+          mfma(4, 1);
+          mfma(5, 1);
+          mfma(6, 1);
+          mfma(7, 1);
+          nb[1] = read_b_rowk(Bs, 1);
+          mfma(4, 2);
+        }
+        mfma(5, 2);
+        mfma(6, 2);
+        mfma(7, 2);
+        mfma(4, 3);
+        mfma(5, 3);
+        mfma(6, 3);
+        mfma(7, 3);
+#pragma unroll
+        for (int q = kSplit + 3; q < kFetchOps; ++q) dma(q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = na[i];
+        fb[0] = nb[0];
+        fb[1] = nb[1];
       }
     }
   }
 
   // ---- epilogue ----
   // The two wave groups hold partial sums of the same 128 x 64 sub-tile.
-  // Group g finishes fragment rows i in [2g, 2g + 2): it hands the other
-  // group's fragments over through LDS as 16-byte chunks (4 accumulator
-  // registers), adds the chunks it receives, and stores straight from
-  // registers.  A fragment's register r of lane l is element
-  // (8 (r / 4) + 4 (l / 32) + r % 4, l % 32); a 4 x 4 transpose across each
-  // lane quad (DPP) turns the four registers 4q .. 4q + 3 into four
-  // consecutive columns of one row, so every lane writes 8 (bf16) or 16 (fp32)
-  // contiguous bytes.  Output stores are nontemporal: nothing here reads them.
+  // Group g finishes fragment rows i in [4g, 4g + 4): it hands the other
+  // group's fragments over through LDS as 16-byte chunks (the 4 accumulator
+  // registers of a lane) and adds the chunks it receives.  A fragment's
+  // register r of lane l is element (4 (l / 16) + r, l % 16); a 4 x 4
+  // transpose across each lane quad (DPP) gives every lane four consecutive
+  // columns of one row for the staging below.  Output stores are
+  // nontemporal: nothing here reads them.
   constexpr int kHalfM = FM / kGroups;  // fragment rows finished per group
-  constexpr int kChunkBytes = kHalfM * FN * 4 * 64 * 16;  // one group's hand-over
+  constexpr int kChunkBytes = kHalfM * FN * 64 * 16;  // one group's hand-over
   static_assert(2 * kSubTiles * kChunkBytes + 4 * (BM + BN) <= kStages * STAGE,
                 "epilogue hand-over fits in LDS");
   __syncthreads();  // every wave is done with the k slices
@@ -565,99 +596,134 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
     }
   }
   // hand-over region written for group `to` of this sub-tile
-  auto chunk_at = [&](int to, int ii, int j, int q) -> int4* {
-    return reinterpret_cast<int4*>(smem + (wsub * 2 + to) * kChunkBytes +
-                                   (((ii * FN + j) * 4 + q) * 64 + lane) * 16);
+  auto chunk_at = [&](int to, int ii, int j) -> v4i* {
+    return reinterpret_cast<v4i*>(smem + (wsub * 2 + to) * kChunkBytes +
+                                  ((ii * FN + j) * 64 + lane) * 16);
   };
   auto give = [&](auto i_off) {  // fragments i_off .. i_off + kHalfM - 1 go to the other group
 #pragma unroll
     for (int ii = 0; ii < kHalfM; ++ii)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const v16i& v = acc[i_off + ii][j];
-          *chunk_at(1 - grp, ii, j, q) = make_int4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-        }
+      for (int j = 0; j < FN; ++j) *chunk_at(1 - grp, ii, j) = acc[i_off + ii][j];
   };
   auto take = [&](auto i_off) {  // add the other group's sums for my fragments
 #pragma unroll
     for (int ii = 0; ii < kHalfM; ++ii)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int4 v = *chunk_at(grp, ii, j, q);
-          acc[i_off + ii][j][4 * q] += v.x;
-          acc[i_off + ii][j][4 * q + 1] += v.y;
-          acc[i_off + ii][j][4 * q + 2] += v.z;
-          acc[i_off + ii][j][4 * q + 3] += v.w;
-        }
+      for (int j = 0; j < FN; ++j) acc[i_off + ii][j] += *chunk_at(grp, ii, j);
   };
   if (grp == 0) give(std::integral_constant<int, kHalfM>{}); else give(std::integral_constant<int, 0>{});
   __syncthreads();  // hand-over and scales visible
   if (grp == 0) take(std::integral_constant<int, 0>{}); else take(std::integral_constant<int, kHalfM>{});
 
-  const int quad_i = lane & 3;          // row within the 4-row group after the transpose
-  const int col4 = 4 * ((lane & 31) >> 2);  // first of the lane's 4 columns in a fragment
-  auto finish = [&](auto i_off) {
+  // Each wave now holds the final sums of a 64 x 64 block: rows
+  // [16 i_off, 16 i_off + 64) of its sub-tile.  It stages them row-major in
+  // LDS (the hand-over region, free after this barrier) and reads them back
+  // row-contiguous, so that every store instruction writes whole 128-byte
+  // row segments.
+  __syncthreads();
+  constexpr int kFinRows = kHalfM * 16;
+  constexpr int kStageBytes = kFinRows * WTN * 4;
+  static_assert(kWaves * kStageBytes <= 2 * kSubTiles * kChunkBytes, "staging fits in the hand-over region");
+  int* stage = reinterpret_cast<int*>(smem + (t >> 6) * kStageBytes);
+  // 16-byte chunk q (columns 4q .. 4q + 3) of staged row r; the XOR keeps the
+  // transposed writes and both read patterns below free of bank conflicts
+  auto stage_at = [&](int r, int q) -> v4i* {
+    return reinterpret_cast<v4i*>(stage + r * WTN + ((q ^ (((r & 3) << 2) | (r & 1))) << 2));
+  };
+  const int quad_i = lane & 3;  // row within the 4-row group after the transpose
+  auto stage_out = [&](auto i_off) {
 #pragma unroll
     for (int ii = 0; ii < kHalfM; ++ii)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int lcol = wn * WTN + j * 32 + col4;  // tile-local column
-        const int gcol = n0 + lcol;
-        float sb4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sb4[e] = out ? s_sb[lcol + e] : 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          int v[4];
-          quad_transpose(acc[i_off + ii][j][4 * q], acc[i_off + ii][j][4 * q + 1],
-                         acc[i_off + ii][j][4 * q + 2], acc[i_off + ii][j][4 * q + 3], quad_i, v);
-          const int lrow = wm * WTM + (i_off + ii) * 32 + 8 * q + 4 * (lane >> 5) + quad_i;
-          const int grow = m0 + lrow;
-          if (grow >= M) continue;
-          const size_t base = static_cast<size_t>(grow) * N + gcol;
-          const bool vec_ok = (N % 4 == 0) && (gcol + 4 <= N);
-          if (c) {
-            if (vec_ok) {
-              __builtin_nontemporal_store(v4i{v[0], v[1], v[2], v[3]}, reinterpret_cast<v4i*>(c + base));
-            } else {
-              for (int e = 0; e < 4; ++e)
-                if (gcol + e < N) c[base + e] = v[e];
-            }
-          }
-          if (out) {
-            const float sa = s_sa[lrow];
-            float f[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) f[e] = (static_cast<float>(v[e]) * sa) * sb4[e];
-            if (out_dtype == QK_BF16) {
-              uint16_t* o = static_cast<uint16_t*>(out) + base;
-              if (vec_ok) {
-                const v2i w = {static_cast<int>(to_bf16(f[0]) | (static_cast<uint32_t>(to_bf16(f[1])) << 16)),
-                               static_cast<int>(to_bf16(f[2]) | (static_cast<uint32_t>(to_bf16(f[3])) << 16))};
-                __builtin_nontemporal_store(w, reinterpret_cast<v2i*>(o));
-              } else {
-                for (int e = 0; e < 4; ++e)
-                  if (gcol + e < N) o[e] = to_bf16(f[e]);
-              }
-            } else {
-              float* o = static_cast<float*>(out) + base;
-              if (vec_ok) {
-                typedef float v4f __attribute__((ext_vector_type(4)));
-                __builtin_nontemporal_store(v4f{f[0], f[1], f[2], f[3]}, reinterpret_cast<v4f*>(o));
-              } else {
-                for (int e = 0; e < 4; ++e)
-                  if (gcol + e < N) o[e] = f[e];
-              }
-            }
-          }
-        }
+        int v[4];
+        quad_transpose(acc[i_off + ii][j][0], acc[i_off + ii][j][1], acc[i_off + ii][j][2],
+                       acc[i_off + ii][j][3], quad_i, v);
+        *stage_at(ii * 16 + 4 * (lane >> 4) + quad_i, 4 * j + ((lane & 15) >> 2)) =
+            v4i{v[0], v[1], v[2], v[3]};
       }
   };
-  if (grp == 0) finish(std::integral_constant<int, 0>{}); else finish(std::integral_constant<int, kHalfM>{});
+  if (grp == 0) stage_out(std::integral_constant<int, 0>{}); else stage_out(std::integral_constant<int, kHalfM>{});
+
+  const int lrow0 = wm * WTM + (grp == 0 ? 0 : kFinRows);  // tile-local first row of the block
+  const int lcol0 = wn * WTN;
+  // raw accumulators and fp32: 4 columns (16 bytes) per lane, 4 rows per pass
+  auto store4 = [&](auto is_c) {
+    const int q = lane & 15;
+    const int lcol = lcol0 + 4 * q;
+    const int gcol = n0 + lcol;
+    float sb4[4];
+    if constexpr (!decltype(is_c)::value) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sb4[e] = s_sb[lcol + e];
+    }
+#pragma unroll 4
+    for (int pass = 0; pass < kFinRows / 4; ++pass) {
+      const int r = 4 * pass + (lane >> 4);
+      const int grow = m0 + lrow0 + r;
+      const v4i v = *stage_at(r, q);
+      if (grow >= M) continue;
+      const size_t base = static_cast<size_t>(grow) * N + gcol;
+      if constexpr (decltype(is_c)::value) {
+        int32_t* o = c + base;
+        if (gcol + 4 <= N && reinterpret_cast<uintptr_t>(o) % 16 == 0) {
+          __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(o));
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (gcol + e < N) o[e] = v[e];
+        }
+      } else {
+        typedef float v4f __attribute__((ext_vector_type(4)));
+        const float sa = s_sa[lrow0 + r];
+        v4f f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = (static_cast<float>(v[e]) * sa) * sb4[e];
+        float* o = static_cast<float*>(out) + base;
+        if (gcol + 4 <= N && reinterpret_cast<uintptr_t>(o) % 16 == 0) {
+          __builtin_nontemporal_store(f, reinterpret_cast<v4f*>(o));
+        } else {
+          for (int e = 0; e < 4; ++e)
+            if (gcol + e < N) o[e] = f[e];
+        }
+      }
+    }
+  };
+  // bf16: 8 columns (16 bytes) per lane, 8 rows per pass
+  auto store_bf16 = [&]() {
+    const int q2 = lane & 7;
+    const int lcol = lcol0 + 8 * q2;
+    const int gcol = n0 + lcol;
+    float sb8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sb8[e] = s_sb[lcol + e];
+#pragma unroll 4
+    for (int pass = 0; pass < kFinRows / 8; ++pass) {
+      const int r = 8 * pass + (lane >> 3);
+      const int grow = m0 + lrow0 + r;
+      const v4i v0 = *stage_at(r, 2 * q2);
+      const v4i v1 = *stage_at(r, 2 * q2 + 1);
+      if (grow >= M) continue;
+      const float sa = s_sa[lrow0 + r];
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        h[e] = to_bf16((static_cast<float>(e < 4 ? v0[e] : v1[e - 4]) * sa) * sb8[e]);
+      uint16_t* o = static_cast<uint16_t*>(out) + static_cast<size_t>(grow) * N + gcol;
+      if (gcol + 8 <= N && reinterpret_cast<uintptr_t>(o) % 16 == 0) {
+        const v4i w = {static_cast<int>(h[0] | (h[1] << 16)), static_cast<int>(h[2] | (h[3] << 16)),
+                       static_cast<int>(h[4] | (h[5] << 16)), static_cast<int>(h[6] | (h[7] << 16))};
+        __builtin_nontemporal_store(w, reinterpret_cast<v4i*>(o));
+      } else {
+        for (int e = 0; e < 8; ++e)
+          if (gcol + e < N) o[e] = static_cast<uint16_t>(h[e]);
+      }
+    }
+  };
+  if (c) store4(std::true_type{});
+  if (out) {
+    if (out_dtype == QK_BF16) store_bf16(); else store4(std::false_type{});
+  }
 }
 
 template <int MODE>
