@@ -266,6 +266,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
   const int wm = wsub / (BN / WTN);
   const int wn = wsub % (BN / WTN);
 
+  // this thread's per-token or per-channel scale of the tile, loaded now so
+  // that its latency hides behind the main loop; the epilogue stages it to LDS
+  static_assert(BM + BN <= kThreads, "one scale per thread");
+  float scale_reg = 0.0f;
+  if (out) {
+    if (t < BM) {
+      if (m0 + t < M) scale_reg = scale_a[m0 + t];
+    } else if (t < BM + BN) {
+      if (n0 + t - BM < N) scale_reg = scale_b[n0 + t - BM];  // times output_scale later
+    }
+  }
+
   auto a_lds = [&](int s) { return smem + (s % kStages) * STAGE; };
   auto b_lds = [&](int s) { return smem + (s % kStages) * STAGE + A_STAGE; };
 
@@ -587,14 +599,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
   __syncthreads();  // every wave is done with the k slices
   float* s_sa = reinterpret_cast<float*>(smem + 2 * kSubTiles * kChunkBytes);
   float* s_sb = s_sa + BM;
-  if (out) {
-    for (int idx = t; idx < BM + BN; idx += kThreads) {
-      if (idx < BM)
-        s_sa[idx] = m0 + idx < M ? scale_a[m0 + idx] : 0.0f;
-      else
-        s_sb[idx - BM] = n0 + idx - BM < N ? scale_b[n0 + idx - BM] * output_scale : 0.0f;
-    }
-  }
+  if (out && t < BM + BN) s_sa[t] = t < BM ? scale_reg : scale_reg * output_scale;  // s_sb follows s_sa
   // hand-over region written for group `to` of this sub-tile
   auto chunk_at = [&](int to, int ii, int j) -> v4i* {
     return reinterpret_cast<v4i*>(smem + (wsub * 2 + to) * kChunkBytes +

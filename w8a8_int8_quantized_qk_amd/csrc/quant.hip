@@ -73,9 +73,10 @@ __device__ __forceinline__ float silu_times(float g, float u) {
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
-// Codes of one 16-byte unit of P values, stored as P bytes.  Nontemporal:
-// the codes are not read again by this kernel, and streaming them out keeps
-// them from piling up as dirty cache lines to be written back at the end.
+// Codes of one 16-byte unit of P values, stored as P bytes.  Ordinary
+// stores: the GEMM that consumes the codes usually runs next and finds them
+// in the caches (measured on the prefill step: 0.4 us faster than
+// nontemporal stores, although the quantization alone is slower).
 template <int P>
 __device__ __forceinline__ void store_codes(int8_t* dst, const float (&v)[P], float s, float r) {
   int c[P];
@@ -85,9 +86,9 @@ __device__ __forceinline__ void store_codes(int8_t* dst, const float (&v)[P], fl
     v2u w;
     w.x = pack4(c[0], c[1], c[2], c[3]);
     w.y = pack4(c[4], c[5], c[6], c[7]);
-    __builtin_nontemporal_store(w, reinterpret_cast<v2u*>(dst));
+    *reinterpret_cast<v2u*>(dst) = w;
   } else {
-    __builtin_nontemporal_store(pack4(c[0], c[1], c[2], c[3]), reinterpret_cast<uint32_t*>(dst));
+    *reinterpret_cast<uint32_t*>(dst) = pack4(c[0], c[1], c[2], c[3]);
   }
 }
 
