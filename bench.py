@@ -61,22 +61,27 @@ def _args():
     return p.parse_args()
 
 
-def _sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def _code_sha(path):
+    """SHA-256 prefix of a kernel source with comments and blank lines removed,
+    so that a comment edit does not orphan counter data taken on that code."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def _traffic_from_profile(which):
     """Memory bytes per launch (L2 fetches + writes, scaled by a plain copy's
     counts) from the committed counter summary, if it was taken on the current
-    kernel source; else None."""
+    kernel code (comments aside); else None."""
     summary, src = which
     if not os.path.exists(summary):
         return None
     text = open(summary).read()
-    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
+    m = re.search(r"kernel_code_sha256_16:\s*([0-9a-f]{16})", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != _sha(src):
+    if not m or not t or m.group(1) != _code_sha(src):
         return None
     return float(t.group(1))
 

@@ -42,12 +42,13 @@
 //   * Workgroups are dispatched to the 8 XCDs round robin; tiles are renumbered
 //     so the ones running together on one XCD form a compact 4 x 8 block that
 //     shares A rows and B columns in that XCD's L2.
-//   * Epilogue without a row-major staging pass: the two wave groups swap
-//     half of their partial sums through LDS as 16-byte chunks, then each
-//     lane transposes 4 x 4 blocks across its lane quad (DPP) so that it holds
-//     4 consecutive columns of one row, applies the per-token and per-channel
-//     scales in binary32 and stores fp32 or bf16 (round to nearest even), or
-//     the raw accumulators, with nontemporal stores.
+//   * Epilogue: the two wave groups swap half of their partial sums through
+//     LDS as 16-byte chunks; each lane transposes 4 x 4 blocks across its
+//     lane quad (DPP) and writes 4 consecutive columns of one row to a
+//     row-major staging block in LDS; the block is read back row-contiguous,
+//     the per-token and per-channel scales are applied in binary32, and fp32
+//     or bf16 (round to nearest even), or the raw accumulators, are stored as
+//     whole 128-byte row segments with nontemporal stores.
 //   * Operands are addressed with 32-bit offsets (m*k, n*k < 2^32).
 #include "lds_dma.h"
 #include "qk_internal.h"
