@@ -122,7 +122,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   constexpr int kCodeRegs = (kCodeWords + kThreads - 1) / kThreads;
   __shared__ int32_t q_lds[MR][kSliceWords];  // codes of this k slice, 4 per word
   __shared__ float s_row[MR];
-  __shared__ int red[MR][kCols];  // column 16 cg + j of a row at j * 32 + cg
+  // per-wave partial sums: column c of row m of wave w at [w][m][c ^ ((c >> 6) & 7)]
+  __shared__ int wsum[kWaves][MR][kCols];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -165,9 +166,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     }
     return;
   }
-
-#pragma unroll
-  for (int m = 0; m < MR; ++m) red[m][t] = 0;
 
   // weight loads of one round (all loop indices below are compile-time after
   // unrolling, so wr stays in registers); rows past K (zero codes) and
@@ -228,6 +226,24 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     }
     if (t < MR) s_row[t] = (t < M && scale_a) ? scale_a[t] : 0.0f;
   }
+  // the slice units this thread encodes: unit su of row m, with
+  // m * kSliceUnits + su = t + kThreads * i, spread over every thread (one
+  // wave per row would serialize the divisions of all rows)
+  constexpr int kSliceUnits = kRowsK / P;
+  constexpr int kEncRegs = (MR * kSliceUnits + kThreads - 1) / kThreads;
+  uint4 er[kEncRegs];
+  if constexpr (XDT >= 0) {
+    if (x_in_regs) {
+#pragma unroll
+      for (int i = 0; i < kEncRegs; ++i) {
+        const int idx = min(t + kThreads * i, MR * kSliceUnits - 1);
+        const int mm = min(idx / kSliceUnits, M - 1);
+        const int u = min(k0 / P + idx % kSliceUnits, units - 1);
+        er[i] = *reinterpret_cast<const uint4*>(
+            static_cast<const char*>(a) + (static_cast<size_t>(mm) * K + static_cast<size_t>(u) * P) * E::kBytes);
+      }
+    }
+  }
   // A CU serves its loads in issue order: without this barrier the later
   // waves' activation loads would queue behind the earlier waves' weight
   // loads.  (Execution barrier only; nothing needs to be visible yet.)
@@ -257,33 +273,39 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
       }
     }
     block_max_rows<MR>(amax);
-    const int u_lo = k0 / P;
-    const int u_hi = min(units, (k0 + kRowsK) / P);
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
       float s, r;
       qm::row_scale(amax[m], s, r);
       if (t == 0) s_row[m] = s;
       if (blockIdx.x == 0 && t == 0 && s_out && m < M) s_out[m] = s;
-      // words of the slice past K have no unit: zero (disjoint from the writers below)
-      if (t < kSliceWords && k0 + 4 * t >= K) q_lds[m][t] = 0;
+    }
 #pragma unroll
-      for (int j = 0; j < kXUnits; ++j) {
-        const int u = t + kThreads * j;
-        if (u < u_lo || u >= u_hi) continue;
-        float v[P];
-        E::unpack(xr[m][j], v);
+    for (int i = 0; i < kEncRegs; ++i) {
+      const int idx = t + kThreads * i;
+      if (idx >= MR * kSliceUnits) continue;
+      const int m = idx / kSliceUnits;
+      const int su = idx % kSliceUnits;
+      const int u = k0 / P + su;
+      float am = amax[0];
 #pragma unroll
-        for (int e4 = 0; e4 < P / 4; ++e4) {
-          const uint32_t word =
-              m < M ? qm::pack4(qm::code_of(v[4 * e4], s, r), qm::code_of(v[4 * e4 + 1], s, r),
-                                qm::code_of(v[4 * e4 + 2], s, r), qm::code_of(v[4 * e4 + 3], s, r))
-                    : 0u;  // padding rows
-          const int kw = u * (P / 4) + e4;  // codes of elements 4 kw .. 4 kw + 3
-          q_lds[m][kw - k0 / 4] = static_cast<int32_t>(word);
-          if (ct == 0 && q_out && m < M)  // one workgroup per k slice writes the codes
-            *reinterpret_cast<uint32_t*>(q_out + static_cast<size_t>(m) * K + 4 * kw) = word;
-        }
+      for (int mm = 1; mm < MR; ++mm) am = m == mm ? amax[mm] : am;
+      float s, r;
+      qm::row_scale(am, s, r);
+      float v[P];
+      E::unpack(er[i], v);
+      // padding rows and units past K (the tail of the last slice): zero words
+      const bool live = m < M && u < units;
+#pragma unroll
+      for (int e4 = 0; e4 < P / 4; ++e4) {
+        const uint32_t word =
+            live ? qm::pack4(qm::code_of(v[4 * e4], s, r), qm::code_of(v[4 * e4 + 1], s, r),
+                             qm::code_of(v[4 * e4 + 2], s, r), qm::code_of(v[4 * e4 + 3], s, r))
+                 : 0u;
+        const int kw = su * (P / 4) + e4;  // codes of elements k0 + 4 kw .. + 3
+        q_lds[m][kw] = static_cast<int32_t>(word);
+        if (ct == 0 && q_out && live)  // one workgroup per k slice writes the codes
+          *reinterpret_cast<uint32_t*>(q_out + static_cast<size_t>(m) * K + k0 + 4 * kw) = word;
       }
     }
   } else {
@@ -362,25 +384,42 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     }
   }
 
-  // ---- reduce within the workgroup with LDS adds: for a fixed j the 32
-  //      column groups hit 32 consecutive words (no bank conflicts) ----
+  // ---- reduce within the workgroup ----
+  // The two half-waves hold the same 512 columns (row quads 2w and 2w + 1):
+  // a lane swap across the halves adds them, lanes < 32 ending with columns
+  // 16 cg + jj and lanes >= 32 with 16 cg + 8 + jj (jj < 8).  Each wave then
+  // stores its partial sums with plain LDS stores, and after one barrier
+  // thread t adds the kWaves partials of column t.  The XOR swizzle keeps
+  // both the stores and the column-major reads free of bank conflicts.
+  auto wsum_slot = [](int col) { return col ^ ((col >> 6) & 7); };
 #pragma unroll
   for (int m = 0; m < MR; ++m)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) atomicAdd(&red[m][j * 32 + cg], acc[m][j]);
+    for (int jj = 0; jj < 8; ++jj) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(acc[m][jj], acc[m][jj + 8], false, false);
+      const int col = 16 * cg + jj + 8 * (lane >> 5);
+      wsum[wave][m][wsum_slot(col)] = static_cast<int>(sw[0]) + static_cast<int>(sw[1]);
+    }
   __syncthreads();
+  int part_sum[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    int v = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) v += wsum[w2][m][wsum_slot(t)];
+    part_sum[m] = v;
+  }
 
   // ---- across the split-K workgroups: one returning 64-bit add per (row,
   //      column) carrying the arrival count and the exact partial sum ----
   const int n = n0 + t;
   if (n >= N) return;
-  const int slot = (t & 15) * 32 + (t >> 4);  // where column t of the tile was reduced
   unsigned long long prev[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     if (m >= M) continue;
     const unsigned long long add =
-        (1ull << kCountShift) + static_cast<unsigned long long>(static_cast<long long>(red[m][slot]));
+        (1ull << kCountShift) + static_cast<unsigned long long>(static_cast<long long>(part_sum[m]));
     prev[m] = __hip_atomic_fetch_add(&ws[static_cast<size_t>(m) * N + n], add, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -392,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const long long count = (o + (1ll << (kCountShift - 1))) >> kCountShift;
     if (count != splits - 1) continue;
     // last contribution: total = earlier sum + this partial; word back to zero
-    const int v = static_cast<int>(o - (count << kCountShift)) + red[m][slot];
+    const int v = static_cast<int>(o - (count << kCountShift)) + part_sum[m];
     __hip_atomic_store(&ws[static_cast<size_t>(m) * N + n], 0ull, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
     const size_t o_idx = static_cast<size_t>(m) * N + n;
