@@ -22,10 +22,11 @@
 //   * The four rows of a lane are transposed in registers (v_perm_b32) into
 //     sixteen 4-byte columns and multiplied with the matching four activation
 //     codes by v_dot4_i32_i8 (exact INT32).  Codes come from LDS.
-//   * Partial sums are reduced across the 16 half-waves with LDS adds, laid
-//     out so that the lanes of one add touch consecutive words.  Across the
-//     K-slice workgroups
-//     each (row, column) has one 64-bit workspace word holding
+//   * Partial sums are reduced across the 16 half-waves: a lane swap
+//     (v_permlane32_swap) adds the two halves of each wave, each wave stores
+//     its sums to LDS, and one thread per column adds the waves' sums.
+//     Across the K-slice workgroups each (row, column) has one 64-bit
+//     workspace word holding
 //     (contributions so far) * 2^40 + (their exact sum); a workgroup adds
 //     2^40 + its partial with one returning device-scope atomic.  The partial
 //     sums of any subset of the k range stay within +-2^31, so the two fields
