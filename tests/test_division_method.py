@@ -19,3 +19,13 @@ def test_markstein_quotient_gives_ieee_codes(tmp_path):
     res = subprocess.run([str(exe), "20000000"], capture_output=True, text=True, timeout=600)
     assert res.returncode == 0, res.stdout + res.stderr
     assert "mismatches 0" in res.stdout
+
+
+def test_scale_division_by_127_is_exact(tmp_path):
+    """Every binary32 row maximum from the 1e-12 guard up gives the IEEE scale."""
+    exe = tmp_path / "scale_division_check"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+                           os.path.join(HERE, "scale_division_check.c"), "-o", str(exe), "-lm"])
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "mismatches 0" in res.stdout

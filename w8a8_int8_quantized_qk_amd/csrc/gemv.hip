@@ -89,21 +89,19 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
 // Workgroup-wide max of MR values at once (one barrier).
 template <int MR>
 __device__ __forceinline__ void block_max_rows(float (&v)[MR]) {
-  __shared__ float part[MR][kWaves];
+  __shared__ uint32_t part[MR][kWaves];
 #pragma unroll
-  for (int m = 0; m < MR; ++m)
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v[m] = __builtin_fmaxf(v[m], __shfl_xor(v[m], off, 64));
+  for (int m = 0; m < MR; ++m) v[m] = qm::wave_max_nonneg(v[m]);
   if ((threadIdx.x & 63) == 0)
 #pragma unroll
-    for (int m = 0; m < MR; ++m) part[m][threadIdx.x >> 6] = v[m];
+    for (int m = 0; m < MR; ++m) part[m][threadIdx.x >> 6] = __float_as_uint(v[m]);
   __syncthreads();
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
-    float r = part[m][0];
+    uint32_t r = part[m][0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = __builtin_fmaxf(r, part[m][w]);
-    v[m] = r;
+    for (int w = 1; w < kWaves; ++w) r = qm::max_u32(r, part[m][w]);
+    v[m] = __uint_as_float(r);
   }
 }
 

@@ -141,8 +141,7 @@ __global__ __launch_bounds__(kBlock) void quant_rows_wave(const void* __restrict
       for (int e = 0; e < P; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j][e]));
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off, 64));
+  amax = qm::wave_max_nonneg(amax);
   float s, r;
   row_scale(amax, s, r);
   if (lane == 0) scale[row] = s;

@@ -91,21 +91,50 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
          ((static_cast<uint32_t>(c) & 0xffu) << 16) | (static_cast<uint32_t>(d) << 24);
 }
 
-template <int kBlock>
-__device__ __forceinline__ float block_max(float v) {
-  __shared__ float part[kBlock / 64];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = part[0];
-#pragma unroll
-  for (int w = 1; w < kBlock / 64; ++w) r = __builtin_fmaxf(r, part[w]);
-  return r;
+// Max over the 64 lanes of a wave of non-negative binary32 values (|x|),
+// left in every lane.  For x >= 0 the unsigned order of the bit patterns is
+// the numeric order, so the max runs on integers (no float canonicalizing):
+// DPP lane exchanges within each 16-lane row (quad partners, then the mirror
+// half-row and row), then lane swaps across rows (v_permlane16_swap) and
+// across the halves of the wave (v_permlane32_swap).
+__device__ __forceinline__ uint32_t max_u32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  uint32_t v = __float_as_uint(x);
+  v = max_u32(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false)));   // quad_perm 1,0,3,2
+  v = max_u32(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false)));   // quad_perm 2,3,0,1
+  v = max_u32(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x141, 0xF, 0xF, false)));  // row_half_mirror
+  v = max_u32(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x140, 0xF, 0xF, false)));  // row_mirror
+  const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max_u32(static_cast<uint32_t>(r16[0]), static_cast<uint32_t>(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max_u32(static_cast<uint32_t>(r32[0]), static_cast<uint32_t>(r32[1]));
+  return __uint_as_float(v);
 }
 
+// Workgroup-wide max of non-negative values (|x|), returned to every thread.
+template <int kBlock>
+__device__ __forceinline__ float block_max(float v) {
+  __shared__ uint32_t part[kBlock / 64];
+  v = wave_max_nonneg(v);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = __float_as_uint(v);
+  __syncthreads();
+  uint32_t r = part[0];
+#pragma unroll
+  for (int w = 1; w < kBlock / 64; ++w) r = max_u32(r, part[w]);
+  return __uint_as_float(r);
+}
+
+// s = max(amax, 1e-12f) / 127 (correctly rounded) and r = RN(1 / s).  The
+// division by 127 uses the same correction with the constant RN(1/127): over
+// every binary32 value from 1e-12f to the largest finite one it gives the
+// IEEE quotient (checked exhaustively).  r stays a true division: the code
+// quotients need it correctly rounded.
 __device__ __forceinline__ void row_scale(float amax, float& s, float& r) {
-  s = __builtin_fmaxf(amax, 1e-12f) / 127.0f;
+  constexpr float kInv127 = 0x1.020408p-7f;  // RN(1 / 127)
+  const float a = __builtin_fmaxf(amax, 1e-12f);
+  const float y = a * kInv127;
+  const float e = __builtin_fmaf(-y, 127.0f, a);
+  s = __builtin_fmaf(e, kInv127, y);
   r = 1.0f / s;
 }
 
