@@ -215,6 +215,31 @@ def test_gemm_output_scale(kernel):
 
 
 @pytest.mark.parametrize("kernel", ["mfma", "gemv"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_outputs_aligned_to_their_element_only(kernel, out_dtype):
+    # out and c start one element into their buffers: aligned to the element
+    # size (all the ABI asks) but not to 16 bytes, so the kernels' 16-byte
+    # stores must give way to element stores; the element before each view
+    # stays untouched
+    m = 300 if kernel == "mfma" else 5
+    n, k = 136, 272
+    a, b, sa, sb = _gemm_inputs(m, n, k, "kn", _seed("unaligned", m, n, k, kernel))
+    dt = TORCH_OUT[out_dtype]
+    obuf = torch.full((m * n + 1,), 7, dtype=dt, device=DEV)
+    cbuf = torch.full((m * n + 1,), 7, dtype=torch.int32, device=DEV)
+    out, c = qk.gemm_i8_scaled(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV),
+                               torch.from_numpy(sa).to(DEV), torch.from_numpy(sb).to(DEV),
+                               1.0, dt, "kn", return_acc=True, out=obuf[1:].view(m, n),
+                               c=cbuf[1:].view(m, n), kernel=kernel)
+    assert out.data_ptr() % 16 != 0 and c.data_ptr() % 16 != 0
+    c_ref = oracle.gemm_i32(a, b, oracle.B_KN)
+    what = f"{m}x{n}x{k} {kernel} {out_dtype} element-aligned outputs"
+    assert_equal_exact(host(c), c_ref, f"{what} acc")
+    assert_out_close(host(out), oracle.dequant(c_ref, sa, sb, 1.0), out_dtype, what)
+    assert obuf[0].item() == 7 and cbuf[0].item() == 7, what
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "gemv"])
 def test_gemm_int32_closed_forms(kernel):
     # K * a * b with constant operands: K = 65536 at |q| <= 127, and -128 * -128
     # at the largest K accepted (the largest multiple of 16 below QK_MAX_K)
