@@ -16,9 +16,10 @@
 //     two contiguous 512-byte row segments.  Weight loads are nontemporal
 //     (each byte is used once).  A lane keeps several rounds of loads in
 //     flight ahead of the round it multiplies (software pipeline).  Only one
-//     round is issued before the quantization: a CU accepts a limited number
-//     of outstanding loads, and waves stalled issuing weight loads would hold
-//     up the quantization and with it every multiply.
+//     round (two for more than one row) is issued before the quantization: a
+//     CU accepts a limited number of outstanding loads, and waves stalled
+//     issuing weight loads would hold up the quantization and with it every
+//     multiply.
 //   * The four rows of a lane are transposed in registers (v_perm_b32) into
 //     sixteen 4-byte columns and multiplied with the matching four activation
 //     codes by v_dot4_i32_i8 (exact INT32).  Codes come from LDS.
@@ -66,8 +67,12 @@ template <int MR>
 constexpr int prefetch_for() { return MR <= 2 ? kRounds - 1 : (MR == 4 ? 4 : 2); }
 // rounds issued before the quantization: a CU accepts only so many
 // outstanding loads, and a wave stalled issuing weight loads could not reach
-// the quantization (and with it every wave's first multiply)
-constexpr int kEarlyRounds = 1;
+// the quantization (and with it every wave's first multiply).  With more
+// rows the quantization takes longer and a second round fits under it
+// (measured: 4 rows 16.3 -> 15.9 us, 8 rows 22.4 -> 21.9 us; 1 row best
+// with one).
+template <int MR>
+constexpr int early_rounds_for() { return MR == 1 ? 1 : 2; }
 
 __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
                                              uint32_t* col) {
@@ -115,6 +120,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     void* __restrict__ out, int out_dtype, int M, int N, int K, int8_t* __restrict__ q_out,
     float* __restrict__ s_out, unsigned long long* __restrict__ ws, int col_tiles, int splits) {
   constexpr int PD = prefetch_for<MR>();
+  constexpr int kEarlyRounds = early_rounds_for<MR>();
   static_assert(PD >= kEarlyRounds && PD < kRounds, "prefetch distance");
   constexpr int kSliceWords = kRowsK / 4;            // code words of one row's k slice
   constexpr int kCodeWords = MR * kSliceWords;
