@@ -185,6 +185,34 @@ def test_odd_symmetry():
     assert np.array_equal(q1, -q2)
 
 
+def _all_finite_bf16() -> np.ndarray:
+    """Every finite bf16 value (65,280 patterns: both signs, zero and
+    subnormals included), widened to float32 by placing the bits high."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    exp = (bits >> 7) & 0xFF
+    bits = bits[exp != 0xFF]
+    return (bits << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("amax_bits", [0x0000, 0x0001, 0x0080, 0x2B8C, 0x3C00, 0x3F80, 0x4020,
+                                       0x42FE, 0x447A, 0x477F, 0x5F00, 0x7F7F])
+def test_quantization_of_every_bf16_value_matches_a_float32_numpy_pipeline(amax_bits):
+    # a row of every finite bf16 value with |v| <= amax, plus amax itself, is
+    # quantized by the oracle and by numpy's float32 arithmetic (IEEE
+    # division, rint, clip): IEEE basic operations are correctly rounded, so
+    # the two must agree bit for bit
+    assert _all_finite_bf16().size == 65280
+    amax = np.array([amax_bits << 16], np.uint32).view(np.float32)[0]
+    v = _all_finite_bf16()
+    row = np.concatenate([v[np.abs(v) <= amax], [amax]]).astype(np.float32)
+    q, s = oracle.quant_per_token(row[None, :])
+    s_ref = np.float32(np.maximum(np.float32(amax), np.float32(1e-12)) / np.float32(127.0))
+    with np.errstate(over="ignore"):
+        q_ref = np.clip(np.rint(row / s_ref), -127, 127).astype(np.int8)
+    assert s[0].view(np.uint32) == np.float32(s_ref).view(np.uint32)
+    assert np.array_equal(q[0], q_ref), np.nonzero(q[0] != q_ref)[0][:5]
+
+
 def test_power_of_two_covariance():
     rng = np.random.default_rng(5)
     x = rng.standard_normal((30, 40)).astype(np.float32)
@@ -444,3 +472,46 @@ def test_dequant_entries_is_the_exact_product():
     for e in range(50):
         ex = Fraction(int(c[e])) * Fraction(float(sa[e])) * Fraction(float(sb[e])) / 2
         assert abs(Fraction(float(out[e])) - ex) <= abs(ex) * Fraction(4, 2**53)
+
+
+# --------------------------------------------------------------------------
+# property tests over generated rows (hypothesis)
+# --------------------------------------------------------------------------
+
+from hypothesis import assume, given, settings, strategies as st  # noqa: E402
+from hypothesis.extra import numpy as hnp  # noqa: E402
+
+_ROWS = hnp.arrays(np.float32, st.tuples(st.integers(1, 6), st.integers(1, 48)),
+                   elements=st.floats(width=32, allow_nan=False, allow_infinity=False))
+
+
+@settings(max_examples=300, deadline=None)
+@given(_ROWS)
+def test_generated_rows_range_symmetry_and_row_max(x):
+    q, s = oracle.quant_per_token(x)
+    assert q.min() >= -127 and q.max() <= 127
+    q2, s2 = oracle.quant_per_token(-x)
+    assert np.array_equal(s, s2) and np.array_equal(q, -q2)
+    for i in range(x.shape[0]):
+        a = np.abs(x[i])
+        if a.max() >= np.float32(1e-12):
+            at = a == a.max()
+            assert np.all(q[i][at] == np.sign(x[i][at]).astype(np.int8) * 127)
+
+
+@settings(max_examples=200, deadline=None)
+@given(hnp.arrays(np.float32, st.tuples(st.integers(1, 4), st.integers(1, 32)),
+                  elements=st.floats(-1e6, 1e6, width=32)),
+       st.integers(-40, 40))
+def test_generated_rows_power_of_two_covariance(x, e):
+    # away from the guard and the subnormal range, scaling a row by 2^e scales
+    # its scale by 2^e and leaves every code unchanged
+    a = np.abs(x)
+    nz = a[a > 0]
+    assume(nz.size > 0 and nz.min() >= 2.0 ** -80)
+    assume(np.all(a.max(axis=1) * 2.0 ** min(e, 0) >= 1e-6))
+    q1, s1 = oracle.quant_per_token(x)
+    xe = np.ldexp(x, e).astype(np.float32)
+    qe, se = oracle.quant_per_token(xe)
+    assert np.array_equal(qe, q1)
+    assert np.array_equal(se, np.ldexp(s1, e).astype(np.float32))
