@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
   const int n0 = tn * BN;
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int grp = (t >> 6) / kSubTiles;  // which k steps of a slice this wave multiplies
+  const int grp = (t >> 6) / kSubTiles;  // which 64-byte half of each k slice this wave multiplies
   const int wsub = (t >> 6) % kSubTiles;  // which 128 x 64 sub-tile it owns
   const int wm = wsub / (BN / WTN);
   const int wn = wsub % (BN / WTN);
@@ -450,7 +450,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
     // place pinned by sched_barrier:
     //   phase 0: MFMAs of A 0..3 x B 0..1, interleaved with the LDS reads of
     //            this slice's A 4..7 and B 2..3 and DMA parts [0, kSplit) of
-    //            slice kt + 2 (its LDS slice was last read in iteration kt - 2);
+    //            slice kt + 2 (its LDS stage held slice kt - 1, whose last
+    //            reads, in phase 0 of iteration kt - 1, every wave completed
+    //            before that iteration's barrier);
     //   barrier: this wave's DMA of slice kt + 1 has landed (vmcnt), then all
     //            waves' (s_barrier);
     //   phase 1: the other 24 MFMAs, interleaved with the reads of slice
