@@ -56,6 +56,8 @@ def _args():
                    help="target duration of the CPU oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-other-configs", action="store_true",
+                   help="skip the other workload shapes (8-row decode, gated down, MLP up)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain copy kernel of known size (for counter scaling)")
     return p.parse_args()
@@ -243,6 +245,70 @@ def main():
                          "algorithmic_bytes_per_launch": dbytes,
                          "traffic": _traffic_from_profile(GEMV_TRAFFIC)},
         }
+
+    # ---------------- the other workload shapes (reported, not the metric) ----------------
+    if not args.no_other_configs:
+        others = {}
+        # 8-row decode: the fused linear, HBM-bound like the 1-row one
+        ocfg = wl.WORKLOADS["decode_m8"]
+        om, ok, on = ocfg.m, ocfg.k, ocfg.n
+        ows = torch.zeros(qk.gemm_workspace_size(om, on, ok), dtype=torch.uint8, device=dev)
+        osets = []
+        for r in range(args.ring):
+            d = wl.generate(ocfg, seed=r)
+            osets.append({"x": d["x"].to(dev), "w": torch.from_numpy(d["w"]).to(dev),
+                          "s_ch": torch.from_numpy(d["s_ch"]).to(dev),
+                          "out": torch.empty((om, on), dtype=torch.bfloat16, device=dev)})
+        oms, _ = timed_replays([(lambda bs=b: qk.linear_w8a8(bs["x"], bs["w"], bs["s_ch"], out=bs["out"],
+                                                             workspace=ows)) for b in osets],
+                               200, args.warmup)
+        obytes = ok * on + 4 * on + 2 * om * ok + 2 * om * on
+        others["decode_m8"] = {"m": om, "k": ok, "n": on, "us_per_call": round(oms * 1e3, 3),
+                               "value": round(obytes / (oms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                               "frac_of_hbm_peak": round(obytes / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del osets, ows
+        torch.cuda.empty_cache()
+
+        # gated down-projection and MLP up-projection: quantization + GEMM, and
+        # the GEMM alone; two buffer sets each (both exceed the 256 MB Infinity
+        # Cache already)
+        for name, steps in (("gated_down", 20), ("mlp_up", 8)):
+            gcfg = wl.WORKLOADS[name]
+            gm, gk, gn = gcfg.m, gcfg.k, gcfg.n
+            odt = torch.float32 if gcfg.out_dtype == "f32" else torch.bfloat16
+            gsets = []
+            for r in range(2):
+                d = wl.generate(gcfg, seed=r)
+                bs = {"w": torch.from_numpy(d["w"]).to(dev), "s_ch": torch.from_numpy(d["s_ch"]).to(dev),
+                      "q": torch.empty((gm, gk), dtype=torch.int8, device=dev),
+                      "s": torch.empty((gm,), dtype=torch.float32, device=dev),
+                      "out": torch.empty((gm, gn), dtype=odt, device=dev)}
+                bs["in"] = (d["h"] if gcfg.gated else d["x"]).to(dev)
+                gsets.append(bs)
+                del d
+
+            def quant(bs, gated=gcfg.gated):
+                if gated:
+                    qk.silu_mul_quant_per_token(bs["in"], bs["q"], bs["s"])
+                else:
+                    qk.quant_per_token(bs["in"], bs["q"], bs["s"])
+
+            def gemm(bs):
+                qk.gemm_i8_scaled(bs["q"], bs["w"], bs["s"], bs["s_ch"], out=bs["out"])
+
+            step_ms, _ = timed_replays([(lambda bs=b: (quant(bs), gemm(bs))) for b in gsets], steps, 2)
+            gemm_only_ms, _ = timed_replays([(lambda bs=b: gemm(bs)) for b in gsets], steps, 2)
+            ops = 2 * gm * gn * gk
+            others[name] = {"m": gm, "k": gk, "n": gn, "out_dtype": gcfg.out_dtype,
+                            "quantization": "silu(gate)*up fused" if gcfg.gated else "per-token",
+                            "us_per_step": round(step_ms * 1e3, 2),
+                            "step_tops": round(ops / (step_ms * 1e-3) / 1e12, 1),
+                            "gemm_us": round(gemm_only_ms * 1e3, 2),
+                            "gemm_tops": round(ops / (gemm_only_ms * 1e-3) / 1e12, 1),
+                            "gemm_frac_of_int8_peak": round(ops / (gemm_only_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
+            del gsets
+            torch.cuda.empty_cache()
+        result["other_configs"] = others
 
     if args.copy_calibration:
         nbytes = 256 << 20
