@@ -78,6 +78,14 @@ def _load():
     lib.or_dequant_entries.restype = None
     lib.or_bf16_nearest.argtypes = [I64, P, P]
     lib.or_bf16_nearest.restype = None
+    lib.or_fp8_encode_array.argtypes = [I64, P, P]
+    lib.or_fp8_encode_array.restype = None
+    lib.or_fp8_decode_array.argtypes = [I64, P, P]
+    lib.or_fp8_decode_array.restype = None
+    lib.or_quant_rows_fp8.argtypes = [I64, I64, P, ctypes.c_float, P, P]
+    lib.or_quant_rows_fp8.restype = None
+    lib.or_gemm_fp8.argtypes = [I64, I64, I64, P, P, ctypes.c_int, P]
+    lib.or_gemm_fp8.restype = None
     _lib = lib
     return lib
 
@@ -243,3 +251,69 @@ def linear(x_bits: np.ndarray, dtype: int, w: np.ndarray, scale_b: np.ndarray,
     q, s = quantize_input(x_bits, dtype)
     c = gemm_i32(q, w, layout)
     return q, s, c, dequant(c, s, scale_b, output_scale)
+
+
+# --------------------------------------------------------------------------
+# FP8 path: float8_e4m3fn per-token quantization and the FP8 GEMM
+# --------------------------------------------------------------------------
+
+FP8_MAX = 448.0
+
+
+def fp8_encode(v: np.ndarray) -> np.ndarray:
+    """binary32 -> e4m3fn codes (round to nearest even, saturating at +-448)."""
+    lib = _load()
+    x = _contig(v, np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib.or_fp8_encode_array(x.size, _ptr(x), _ptr(out))
+    return out
+
+
+def fp8_decode(c: np.ndarray) -> np.ndarray:
+    """e4m3fn codes -> their exact values (float64; NaN for S.1111.111)."""
+    lib = _load()
+    cc = _contig(c, np.uint8)
+    out = np.empty(cc.shape, dtype=np.float64)
+    lib.or_fp8_decode_array(cc.size, _ptr(cc), _ptr(out))
+    return out
+
+
+def quant_per_token_fp8(x32: np.ndarray, scale_ub: float = 0.0):
+    """x32: [m, k] float32 -> (e4m3fn codes uint8 [m, k], scale float32 [m]).
+    scale_ub > 0 clamps the scales from above."""
+    lib = _load()
+    x = _contig(x32, np.float32)
+    m, k = x.shape
+    q = np.empty((m, k), dtype=np.uint8)
+    s = np.empty((m,), dtype=np.float32)
+    lib.or_quant_rows_fp8(m, k, _ptr(x), float(scale_ub), _ptr(q), _ptr(s))
+    return q, s
+
+
+def gemm_fp8(a: np.ndarray, b: np.ndarray, layout: int = B_KN) -> np.ndarray:
+    """Exact sums of products of e4m3fn values (float64 [m, n])."""
+    lib = _load()
+    aa = _contig(a, np.uint8)
+    bb = _contig(b, np.uint8)
+    m, k = aa.shape
+    n = bb.shape[1] if layout == B_KN else bb.shape[0]
+    acc = np.empty((m, n), dtype=np.float64)
+    lib.or_gemm_fp8(m, n, k, _ptr(aa), _ptr(bb), layout, _ptr(acc))
+    return acc
+
+
+def dequant_fp8(acc: np.ndarray, scale_a: np.ndarray, scale_b: np.ndarray,
+                output_scale: float = 1.0) -> np.ndarray:
+    """acc * scale_a[row] * scale_b[col] * output_scale in float64."""
+    return (acc * scale_a.astype(np.float64)[:, None] * scale_b.astype(np.float64)[None, :]
+            * float(np.float32(output_scale)))
+
+
+def quantize_input_fp8(x_bits: np.ndarray, dtype: int, scale_ub: float = 0.0):
+    """Widen then quantize per token to e4m3fn: returns (codes, scales)."""
+    return quant_per_token_fp8(widen(x_bits, dtype), scale_ub)
+
+
+def silu_mul_quantize_fp8(h_bits: np.ndarray, dtype: int, scale_ub: float = 0.0):
+    """silu(gate) * up, then per-token e4m3fn quantization: (codes, scales)."""
+    return quant_per_token_fp8(silu_mul(widen(h_bits, dtype)), scale_ub)

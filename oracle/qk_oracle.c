@@ -310,3 +310,117 @@ void or_bf16_nearest(int64_t count, const double *v, uint16_t *out)
     for (int64_t i = 0; i < count; ++i)
         out[i] = bf16_nearest(v[i]);
 }
+
+/* ------------------------------------------------------------------ */
+/* FP8 path [PR]: dynamic per-token quantization to float8_e4m3fn and   */
+/* the FP8 x FP8 GEMM it feeds.                                        */
+/* ------------------------------------------------------------------ */
+
+/* float8_e4m3fn (OCP): sign bit, 4 exponent bits (bias 7), 3 mantissa
+ * bits, no infinities, S.1111.111 is NaN, the largest finite magnitude is
+ * S.1111.110 = 1.75 * 2^8 = 448 (the page's fp8_max), subnormals are
+ * M * 2^-9. */
+double or_fp8_decode(uint8_t c)
+{
+    const int sign = c >> 7;
+    const int e = (c >> 3) & 15;
+    const int m = c & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    /* normal: (1 + m/8) 2^(e-7) = (8 + m) 2^(e-10); subnormal: m 2^-9 */
+    const double v = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+    return sign ? -v : v;
+}
+
+/* Round to nearest, ties to even, saturating at +-448; the sign of zero is
+ * kept; NaN -> S.1111.111.  All arithmetic below is exact in binary64. */
+uint8_t or_fp8_encode(float v)
+{
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v))
+        return sign | 0x7F;
+    const double a = fabs((double)v);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    if (a < 0x1p-6) {
+        /* subnormal range: the nearest multiple of 2^-9 (8 * 2^-9 is the
+         * smallest normal, whose code is 0x08) */
+        const double m = nearbyint(a * 512.0);
+        return sign | (uint8_t)m;
+    }
+    int e;
+    const double f = frexp(a, &e); /* a = f 2^e, f in [0.5, 1) */
+    e -= 1;                         /* a = (2f) 2^e, 2f in [1, 2) */
+    double q = nearbyint((2.0 * f - 1.0) * 8.0);
+    if (q == 8.0) {
+        q = 0.0;
+        e += 1;
+    }
+    if (e > 8 || (e == 8 && q == 7.0))
+        return sign | 0x7E; /* rounds past 448: saturate */
+    return sign | (uint8_t)(((e + 7) << 3) | (int)q);
+}
+
+void or_fp8_encode_array(int64_t count, const float *v, uint8_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = or_fp8_encode(v[i]);
+}
+
+void or_fp8_decode_array(int64_t count, const uint8_t *c, double *out)
+{
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = or_fp8_decode(c[i]);
+}
+
+/* x: [m][k] binary32 -> q: [m][k] e4m3fn codes, scale: [m].
+ * scale = max(absmax, 1e-12) / 448, clamped to scale_ub when scale_ub > 0
+ * [PR: "optionally clamped by scale_ub"]; code = e4m3fn(x / scale) with the
+ * binary32 quotient (the same reading as the INT8 path: a true division). */
+void or_quant_rows_fp8(int64_t m, int64_t k, const float *x, float scale_ub, uint8_t *q,
+                       float *scale)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i) {
+        const float *row = x + i * k;
+        float amax = 0.0f;
+        for (int64_t j = 0; j < k; ++j) {
+            float a = fabsf(row[j]);
+            if (a > amax)
+                amax = a;
+        }
+        float s = fmaxf(amax, 1e-12f) / 448.0f;
+        if (scale_ub > 0.0f && s > scale_ub)
+            s = scale_ub;
+        scale[i] = s;
+        for (int64_t j = 0; j < k; ++j) {
+            float ratio = row[j] / s;
+            q[i * k + j] = or_fp8_encode(ratio);
+        }
+    }
+}
+
+/* acc[i][j] = sum_t value(a[i][t]) * value(B(t, j)) in binary64.  Exact for
+ * k <= 2^17: every product is a multiple of 2^-18 below 2^18 (448^2), so any
+ * partial sum needs at most 18 + 18 + 17 = 53 significant bits. */
+void or_gemm_fp8(int64_t m, int64_t n, int64_t k, const uint8_t *a, const uint8_t *b, int layout,
+                 double *acc)
+{
+    double lut[256];
+    for (int c = 0; c < 256; ++c)
+        lut[c] = or_fp8_decode((uint8_t)c);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < m; ++i) {
+        double *row = acc + i * n;
+        for (int64_t j = 0; j < n; ++j)
+            row[j] = 0.0;
+        for (int64_t kk = 0; kk < k; ++kk) {
+            const double av = lut[a[i * k + kk]];
+            for (int64_t j = 0; j < n; ++j) {
+                const uint8_t bc = layout == OR_B_KN ? b[kk * n + j] : b[j * k + kk];
+                row[j] += av * lut[bc];
+            }
+        }
+    }
+}
