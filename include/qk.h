@@ -6,6 +6,9 @@
  *      silu(gate) * up;
  *   2. an INT8 x INT8 product accumulated in INT32;
  *   3. a dequant epilogue  out = acc * scale_a[row] * scale_b[col] * output_scale.
+ * and the same layer with float8_e4m3fn codes (per-token FP8 quantization
+ * with an optional scale bound, an FP8 x FP8 product accumulated in
+ * binary32, the same epilogue).
  *
  * Sources, cited by page title and section:
  *   "16. Deploying Custom Kernels", C++ Kernel Interface: the GEMM problem
@@ -49,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QK_ABI_VERSION 1
+#define QK_ABI_VERSION 2
 
 /* element types */
 #define QK_F32 0
@@ -190,6 +193,78 @@ int qk_linear_w8a8(int m, int n, int k, const void *x, int x_dtype, const int8_t
                    const float *scale_b, float output_scale, void *out, int out_dtype,
                    int b_layout, int8_t *q_out, float *scale_out, void *workspace,
                    size_t workspace_bytes, int kernel, hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
+/* FP8 path: float8_e4m3fn activations and weights                     */
+/* ------------------------------------------------------------------ */
+/*
+ * float8_e4m3fn (the page's format): sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, no infinities, S.1111.111 is NaN, largest finite 448,
+ * subnormals m * 2^-9.  Codes are passed as uint8_t bytes.
+ */
+
+/*
+ * Per-token dynamic FP8 quantization ("kernels: fused silu_and_mul + dynamic
+ * per-token FP8 quantization", Algorithm: scale from the row absmax over
+ * fp8_max, optionally clamped by scale_ub):
+ *   scale[i] = max(max_j |x[i][j]|, 1e-12f) / 448          (binary32 division)
+ *              then min(scale[i], scale_ub) when scale_ub > 0
+ *   q[i][j]  = e4m3fn(x[i][j] / scale[i])   (binary32 quotient; nearest,
+ *              ties to even; saturating at +-448; the sign of zero kept)
+ *   x        [m][k] of x_dtype (QK_F32, QK_BF16 or QK_F16), read only.
+ *   scale_ub upper bound on the scale; 0 or negative means none.
+ *   q        [m][k] codes, written;  scale [m] float, written.
+ * Errors as qk_quant_per_token; a NaN scale_ub is QK_ERR_INVALID_VALUE.
+ */
+int qk_quant_per_token_fp8(int m, int k, const void *x, int x_dtype, float scale_ub, uint8_t *q,
+                           float *scale, hipStream_t stream);
+
+/*
+ * silu(gate) * up followed by per-token FP8 quantization, one pass over h
+ * (the same page, Purpose and Algorithm; silu exactly as in
+ * qk_silu_mul_quant_per_token).
+ *   h [m][2d] of h_dtype (gate | up);  q [m][d] codes;  scale [m] float.
+ * Errors as qk_quant_per_token_fp8.
+ */
+int qk_silu_mul_quant_per_token_fp8(int m, int d, const void *h, int h_dtype, float scale_ub,
+                                    uint8_t *q, float *scale, hipStream_t stream);
+
+/*
+ * FP8 GEMM with binary32 accumulation and the dequant epilogue (the FP8
+ * codes above fed to the scaled GEMM of "16. Deploying Custom Kernels", C++
+ * Kernel Interface; epilogue of "KV-cache kernels", 02 Scales and
+ * dequantization):
+ *   acc[i][j] = sum_t value(a[i][t]) * value(B(t, j))  (matrix-core binary32
+ *               accumulation: every product exact, sums rounded per 128-deep
+ *               step or finer, so acc is not bit-reproducible across
+ *               implementations)
+ *   c[i][j]   = acc                                 (if c != NULL; binary32)
+ *   out[i][j] = (acc * scale_a[i]) * (scale_b[j] * output_scale)
+ *               (if out != NULL; binary32, stored as fp32 or bf16 RNE)
+ *   a [m][k] codes; b [k][n] (QK_B_KN) or [n][k] (QK_B_NK) codes;
+ *   scale_a [m], scale_b [n] float (NULL only when out is NULL);
+ *   c [m][n] float or NULL; out [m][n] of out_dtype or NULL (not both NULL).
+ * Requirements: 0 <= k <= QK_MAX_K, k % 16 == 0, a and b 16-byte aligned,
+ * m*k and n*k below 2^32 (QK_ERR_UNSUPPORTED otherwise).  No workspace.
+ * NaN codes propagate.
+ */
+int qk_gemm_fp8_scaled(int m, int n, int k, const uint8_t *a, const uint8_t *b, float *c,
+                       const float *scale_a, const float *scale_b, float output_scale, void *out,
+                       int out_dtype, int b_layout, hipStream_t stream);
+
+/*
+ * The FP8 layer: qk_quant_per_token_fp8 of x into q_out / scale_out, then
+ * qk_gemm_fp8_scaled of those codes with the weight (two launches on
+ * `stream`).
+ *   x [m][k] of x_dtype;  b [k][n] or [n][k] codes;  scale_b [n] float;
+ *   out [m][n] of out_dtype;  q_out [m][k] (16-byte aligned) and
+ *   scale_out [m]: required, they hold the codes and scales.
+ * Requirements and errors as the two calls.
+ */
+int qk_linear_fp8(int m, int n, int k, const void *x, int x_dtype, float scale_ub,
+                  const uint8_t *b, const float *scale_b, float output_scale, void *out,
+                  int out_dtype, int b_layout, uint8_t *q_out, float *scale_out,
+                  hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -160,3 +160,54 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(2, 16)
     with pytest.raises(ValueError, match="GPU"):
         qk.quant_per_token(x)
+
+
+def test_fp8_argument_errors_are_reported_before_launch(lib):
+    c = _header_constants()
+    INVALID, UNSUP = c["QK_ERR_INVALID_VALUE"], c["QK_ERR_UNSUPPORTED"]
+    nan = float("nan")
+    q8 = lib.qk_quant_per_token_fp8
+    assert q8(-1, 4, FAKE, 0, 0.0, FAKE, FAKE, NULL) == INVALID
+    assert q8(4, 4, FAKE, 5, 0.0, FAKE, FAKE, NULL) == INVALID
+    assert q8(4, 4, NULL, 0, 0.0, FAKE, FAKE, NULL) == INVALID
+    assert q8(4, 4, FAKE, 0, nan, FAKE, FAKE, NULL) == INVALID        # NaN scale bound
+    assert q8(0, 4, NULL, 0, 0.0, NULL, NULL, NULL) == 0
+    s8 = lib.qk_silu_mul_quant_per_token_fp8
+    assert s8(4, 4, FAKE, 3, 0.0, FAKE, FAKE, NULL) == INVALID
+    assert s8(4, 4, FAKE, 1, nan, FAKE, FAKE, NULL) == INVALID
+    assert s8(0, 4, NULL, 1, 1.0, NULL, NULL, NULL) == 0
+
+    def g8(m, n, k, a=FAKE, b=FAKE, cc=FAKE, sa=FAKE, sb=FAKE, out=FAKE, odt=0, layout=0):
+        return lib.qk_gemm_fp8_scaled(m, n, k, a, b, cc, sa, sb, 1.0, out, odt, layout, NULL)
+
+    assert g8(-1, 4, 16) == INVALID
+    assert g8(4, 4, 131072) == INVALID
+    assert g8(4, 4, 24) == UNSUP
+    assert g8(4, 4, 16, cc=NULL, out=NULL) == INVALID
+    assert g8(4, 4, 16, odt=2) == INVALID
+    assert g8(4, 4, 16, layout=3) == INVALID
+    assert g8(4, 4, 16, a=NULL) == INVALID
+    assert g8(4, 4, 16, sb=NULL) == INVALID
+    assert g8(4, 4, 16, b=FAKE_ODD) == UNSUP
+    assert g8(0, 4, 16, a=NULL, b=NULL) == 0
+
+    def l8(m, n, k, x=FAKE, xdt=1, ub=0.0, b=FAKE, sb=FAKE, out=FAKE, odt=1, q=FAKE, s=FAKE):
+        return lib.qk_linear_fp8(m, n, k, x, xdt, ub, b, sb, 1.0, out, odt, 0, q, s, NULL)
+
+    assert l8(-1, 4, 16) == INVALID
+    assert l8(4, 4, 16, xdt=9) == INVALID
+    assert l8(4, 4, 16, ub=nan) == INVALID
+    assert l8(4, 4, 16, q=NULL) == INVALID                 # codes buffer is required
+    assert l8(4, 4, 16, s=NULL) == INVALID
+    assert l8(4, 4, 16, q=FAKE_ODD) == UNSUP
+    assert l8(4, 4, 24) == UNSUP
+    assert l8(0, 4, 16, x=NULL, b=NULL, q=NULL, s=NULL) == 0
+
+
+def test_fp8_binding_rejects_wrong_dtypes():
+    import torch
+    with pytest.raises(ValueError, match="GPU"):
+        qk.quant_per_token_fp8(torch.zeros(2, 16))
+    with pytest.raises(ValueError, match="GPU"):
+        qk.gemm_fp8_scaled(torch.zeros(2, 16, dtype=torch.float8_e4m3fn),
+                           torch.zeros(16, 4, dtype=torch.float8_e4m3fn), out_dtype=None)

@@ -11,6 +11,10 @@ Layer (per-token dynamic INT8 activations, per-channel INT8 weights):
   q, s     = quant_per_token(x)                 # or silu_mul_quant_per_token(h)
   out      = gemm_i8_scaled(q, w, s, s_ch)       # INT32 accumulate + dequant
   out      = linear_w8a8(x, w, s_ch)             # both steps
+and its FP8 (float8_e4m3fn) counterpart:
+  q, s     = quant_per_token_fp8(x, scale_ub)   # or silu_mul_quant_per_token_fp8(h)
+  out      = gemm_fp8_scaled(q, w8, s, s_ch)     # binary32 accumulate + dequant
+  out      = linear_fp8(x, w8, s_ch)
 """
 from __future__ import annotations
 
@@ -20,7 +24,7 @@ import threading
 
 import torch
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 F32, BF16, F16 = 0, 1, 2
 B_KN, B_NK = 0, 1
 KERNEL_AUTO, KERNEL_MFMA, KERNEL_GEMV = 0, 1, 2
@@ -37,7 +41,8 @@ _KERNELS = {"auto": KERNEL_AUTO, "mfma": KERNEL_MFMA, "gemv": KERNEL_GEMV}
 EXPORTED = (
     "qk_abi_version", "qk_status_string", "qk_build_info", "qk_quant_per_token",
     "qk_silu_mul_quant_per_token", "qk_gemm_workspace_size", "qk_gemm_i8_scaled",
-    "qk_gemm_i8_scaled_ex", "qk_linear_w8a8",
+    "qk_gemm_i8_scaled_ex", "qk_linear_w8a8", "qk_quant_per_token_fp8",
+    "qk_silu_mul_quant_per_token_fp8", "qk_gemm_fp8_scaled", "qk_linear_fp8",
 )
 
 
@@ -74,6 +79,14 @@ def _declare(lib):
     lib.qk_gemm_i8_scaled_ex.restype = I
     lib.qk_linear_w8a8.argtypes = [I, I, I, P, I, P, P, F, P, I, I, P, P, P, ctypes.c_size_t, I, P]
     lib.qk_linear_w8a8.restype = I
+    lib.qk_quant_per_token_fp8.argtypes = [I, I, P, I, F, P, P, P]
+    lib.qk_quant_per_token_fp8.restype = I
+    lib.qk_silu_mul_quant_per_token_fp8.argtypes = [I, I, P, I, F, P, P, P]
+    lib.qk_silu_mul_quant_per_token_fp8.restype = I
+    lib.qk_gemm_fp8_scaled.argtypes = [I, I, I, P, P, P, P, P, F, P, I, I, P]
+    lib.qk_gemm_fp8_scaled.restype = I
+    lib.qk_linear_fp8.argtypes = [I, I, I, P, I, F, P, P, F, P, I, I, P, P, P]
+    lib.qk_linear_fp8.restype = I
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -307,3 +320,134 @@ def gated_linear_w8a8(h: torch.Tensor, w: torch.Tensor, s_ch: torch.Tensor,
     """silu(gate) * up with per-token quantization, then the INT8 GEMM."""
     q, s = silu_mul_quant_per_token(h)
     return gemm_i8_scaled(q, w, s, s_ch, output_scale, out_dtype, b_layout, kernel=kernel)
+
+
+# ---- FP8 (float8_e4m3fn) path ----
+_FP8_CODE_DTYPES = (torch.float8_e4m3fn, torch.uint8)
+
+
+def _need_codes(t: torch.Tensor, name: str, ndim=None, device=None):
+    _need(t, name, ndim=ndim, device=device)
+    if t.dtype not in _FP8_CODE_DTYPES:
+        raise TypeError(f"{name} must be torch.float8_e4m3fn (or its uint8 bytes), got {t.dtype}")
+
+
+def _fp8_rows(src: torch.Tensor, name: str, silu: bool, scale_ub: float, q, scale):
+    _need(src, name, ndim=2)
+    if src.dtype not in _IN_DTYPES:
+        raise TypeError(f"{name} dtype {src.dtype} not supported")
+    m, k = src.shape
+    if silu:
+        if k % 2:
+            raise ValueError(f"{name} must have an even number of columns (gate | up)")
+        k //= 2
+    q = torch.empty((m, k), dtype=torch.float8_e4m3fn, device=src.device) if q is None else q
+    scale = torch.empty((m,), dtype=torch.float32, device=src.device) if scale is None else scale
+    _need_codes(q, "q", 2, src.device)
+    _need(scale, "scale", torch.float32, 1, src.device)
+    if tuple(q.shape) != (m, k) or scale.shape[0] != m:
+        raise ValueError(f"q must be [m, {'d' if silu else 'k'}] and scale [m]")
+    fn = library().qk_silu_mul_quant_per_token_fp8 if silu else library().qk_quant_per_token_fp8
+    _check(fn(m, k, _ptr(src), _IN_DTYPES[src.dtype], float(scale_ub), _ptr(q), _ptr(scale),
+              _stream(src.device)))
+    return q, scale
+
+
+def quant_per_token_fp8(x: torch.Tensor, scale_ub: float = 0.0, q: torch.Tensor | None = None,
+                        scale: torch.Tensor | None = None):
+    """Per-token float8_e4m3fn codes and fp32 scales of x [m, k]; scale_ub > 0
+    bounds the scales from above (codes then saturate at +-448)."""
+    return _fp8_rows(x, "x", False, scale_ub, q, scale)
+
+
+def silu_mul_quant_per_token_fp8(h: torch.Tensor, scale_ub: float = 0.0,
+                                 q: torch.Tensor | None = None,
+                                 scale: torch.Tensor | None = None):
+    """FP8 codes and scales of silu(h[:, :d]) * h[:, d:] for h [m, 2d]."""
+    return _fp8_rows(h, "h", True, scale_ub, q, scale)
+
+
+def gemm_fp8_scaled(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor | None = None,
+                    scale_b: torch.Tensor | None = None, output_scale: float = 1.0,
+                    out_dtype: torch.dtype | None = torch.bfloat16, b_layout: str = "kn",
+                    return_acc: bool = False, out: torch.Tensor | None = None,
+                    c: torch.Tensor | None = None):
+    """FP8 GEMM with binary32 accumulation and the dequant epilogue.
+
+    a [m, k] and b [k, n] ("kn") or [n, k] ("nk") float8_e4m3fn codes; scale_a
+    [m], scale_b [n] fp32.  Returns out, (out, c) with the raw fp32
+    accumulators when return_acc, or c alone when out_dtype is None.
+    """
+    _need_codes(a, "a", 2)
+    dev = a.device
+    _need_codes(b, "b", 2, dev)
+    layout = _LAYOUTS[b_layout]
+    m, k = a.shape
+    n, kb = (b.shape[1], b.shape[0]) if layout == B_KN else (b.shape[0], b.shape[1])
+    if kb != k:
+        raise ValueError(f"inner dimensions differ: a has k={k}, b has {kb}")
+    want_out = out is not None or out_dtype is not None
+    if want_out:
+        out_dtype = out.dtype if out is not None else out_dtype
+        if out_dtype not in _OUT_DTYPES:
+            raise TypeError(f"out dtype {out_dtype} not supported")
+        if out is None:
+            out = torch.empty((m, n), dtype=out_dtype, device=dev)
+        _need(out, "out", out_dtype, 2, dev)
+        _need(scale_a, "scale_a", torch.float32, 1, dev)
+        _need(scale_b, "scale_b", torch.float32, 1, dev)
+        if scale_a.shape[0] != m or scale_b.shape[0] != n or tuple(out.shape) != (m, n):
+            raise ValueError("scale_a must be [m], scale_b [n], out [m, n]")
+    if return_acc or not want_out:
+        if c is None:
+            c = torch.empty((m, n), dtype=torch.float32, device=dev)
+        _need(c, "c", torch.float32, 2, dev)
+    else:
+        c = None
+    _check(library().qk_gemm_fp8_scaled(
+        m, n, k, _ptr(a), _ptr(b), _ptr(c), _ptr(scale_a if want_out else None),
+        _ptr(scale_b if want_out else None), float(output_scale), _ptr(out if want_out else None),
+        _OUT_DTYPES[out_dtype] if want_out else F32, layout, _stream(dev)))
+    if not want_out:
+        return c
+    return (out, c) if return_acc else out
+
+
+def linear_fp8(x: torch.Tensor, w: torch.Tensor, s_ch: torch.Tensor, scale_ub: float = 0.0,
+               out_dtype: torch.dtype = torch.bfloat16, b_layout: str = "kn",
+               output_scale: float = 1.0, out: torch.Tensor | None = None,
+               q: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+               return_codes: bool = False):
+    """The FP8 layer: per-token FP8 quantization of x, FP8 GEMM, dequant."""
+    _need(x, "x", ndim=2)
+    if x.dtype not in _IN_DTYPES:
+        raise TypeError(f"x dtype {x.dtype} not supported")
+    dev = x.device
+    _need_codes(w, "w", 2, dev)
+    _need(s_ch, "s_ch", torch.float32, 1, dev)
+    layout = _LAYOUTS[b_layout]
+    m, k = x.shape
+    n, kb = (w.shape[1], w.shape[0]) if layout == B_KN else (w.shape[0], w.shape[1])
+    if kb != k:
+        raise ValueError(f"inner dimensions differ: x has k={k}, w has {kb}")
+    if out_dtype not in _OUT_DTYPES:
+        raise TypeError(f"out dtype {out_dtype} not supported")
+    out = torch.empty((m, n), dtype=out_dtype, device=dev) if out is None else out
+    _need(out, "out", out_dtype, 2, dev)
+    q = torch.empty((m, k), dtype=torch.float8_e4m3fn, device=dev) if q is None else q
+    scale = torch.empty((m,), dtype=torch.float32, device=dev) if scale is None else scale
+    _need_codes(q, "q", 2, dev)
+    _need(scale, "scale", torch.float32, 1, dev)
+    _check(library().qk_linear_fp8(
+        m, n, k, _ptr(x), _IN_DTYPES[x.dtype], float(scale_ub), _ptr(w), _ptr(s_ch),
+        float(output_scale), _ptr(out), _OUT_DTYPES[out_dtype], layout, _ptr(q), _ptr(scale),
+        _stream(dev)))
+    return (out, q, scale) if return_codes else out
+
+
+def gated_linear_fp8(h: torch.Tensor, w: torch.Tensor, s_ch: torch.Tensor, scale_ub: float = 0.0,
+                     out_dtype: torch.dtype = torch.bfloat16, b_layout: str = "kn",
+                     output_scale: float = 1.0):
+    """silu(gate) * up with per-token FP8 quantization, then the FP8 GEMM."""
+    q, s = silu_mul_quant_per_token_fp8(h, scale_ub)
+    return gemm_fp8_scaled(q, w, s, s_ch, output_scale, out_dtype, b_layout)

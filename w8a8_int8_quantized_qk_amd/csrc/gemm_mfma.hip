@@ -50,203 +50,20 @@
 //     or bf16 (round to nearest even), or the raw accumulators, are stored as
 //     whole 128-byte row segments with nontemporal stores.
 //   * Operands are addressed with 32-bit offsets (m*k, n*k < 2^32).
-#include "lds_dma.h"
-#include "qk_internal.h"
-
-#include <type_traits>
+#include "gemm_tile.h"
 
 namespace qk {
 namespace {
 
-typedef int v2i __attribute__((ext_vector_type(2)));
-typedef int v4i __attribute__((ext_vector_type(4)));
+using namespace tile;
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;   // 8: two per SIMD
 constexpr int kGroups = 2;              // wave groups splitting each k slice
-constexpr int BM = 256;
-constexpr int BN = 128;
-constexpr int BK = 128;
 constexpr int WTM = 128;       // wave tile rows
 constexpr int WTN = 64;        // wave tile columns
 constexpr int FM = WTM / 16;   // 16x16 fragments per wave along M
 constexpr int FN = WTN / 16;   // ... along N
 constexpr int kSubTiles = (BM / WTM) * (BN / WTN);  // wave sub-tiles per workgroup tile
 static_assert(kSubTiles * kGroups == kWaves, "every wave owns one (sub-tile, k group)");
-constexpr int kStages = 3;     // LDS k slices in flight
-constexpr int A_STAGE = BM * BK;
-constexpr int B_STAGE = BN * BK;
-constexpr int STAGE = A_STAGE + B_STAGE;
-
-enum BMode {
-  kBnkDma = 0,    // weight [N][K], DMA, read like A
-  kBknDma = 1,    // weight [K][N], N % 16 == 0: DMA into [k][n], transpose reads
-  kBknReg4 = 2,   // weight [K][N], N % 4 == 0: dword loads, register transpose
-  kBknReg1 = 3,   // weight [K][N], other N: byte loads, register transpose
-};
-
-// k-contiguous tiles (A, [N][K] weight): 128-byte rows
-__device__ __forceinline__ int rowk_swz(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int rowk_offset(int row, int chunk) {
-  return row * BK + ((chunk ^ rowk_swz(row)) << 4);
-}
-// [k][n] weight tile: 128-byte rows of n
-__device__ __forceinline__ int kn_swz(int k) { return (k & 7) ^ ((k >> 4) & 1); }
-__device__ __forceinline__ int kn_offset(int k, int chunk) {
-  return k * BN + ((chunk ^ kn_swz(k)) << 4);
-}
-
-// DMA of a k-contiguous tile of ROWS rows x 128 bytes (global rows clamped to
-// rows_valid - 1, k offset clamped into the row): instruction i of this
-// wave's share (1 KiB = 8 rows each).
-template <int ROWS>
-constexpr int rowk_ops() { return ROWS * BK / 1024 / kWaves; }
-template <int ROWS>
-__device__ __forceinline__ void dma_rowk_one(const int8_t* __restrict__ g, char* lds,
-                                             int rows_valid, int K, int r0, int k0, int i) {
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int blk = wave * rowk_ops<ROWS>() + i;
-  const int row = blk * 8 + (lane >> 3);
-  const int lchunk = (lane & 7) ^ rowk_swz(row);
-  const uint32_t gr = static_cast<uint32_t>(min(r0 + row, rows_valid - 1));
-  const uint32_t gk = static_cast<uint32_t>(min(k0 + 16 * lchunk, K - 16));
-  lds_dma16(g + (gr * static_cast<uint32_t>(K) + gk), lds_addr(lds + blk * 1024));
-}
-template <int ROWS>
-__device__ __forceinline__ void dma_rowk(const int8_t* __restrict__ g, char* lds, int rows_valid,
-                                         int K, int r0, int k0) {
-#pragma unroll
-  for (int i = 0; i < rowk_ops<ROWS>(); ++i) dma_rowk_one<ROWS>(g, lds, rows_valid, K, r0, k0, i);
-}
-
-// DMA of a [K][N] weight tile: 128 k rows x 128 bytes of n; instruction i of
-// this wave's share.
-constexpr int kn_ops() { return BK * BN / 1024 / kWaves; }
-__device__ __forceinline__ void dma_kn_one(const int8_t* __restrict__ b, char* lds, int N, int K,
-                                           int n0, int k0, int i) {
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int blk = wave * kn_ops() + i;
-  const int k = blk * 8 + (lane >> 3);
-  const int lchunk = (lane & 7) ^ kn_swz(k);
-  const uint32_t gk = static_cast<uint32_t>(min(k0 + k, K - 1));
-  const uint32_t gn = static_cast<uint32_t>(min(n0 + 16 * lchunk, N - 16));
-  lds_dma16(b + (gk * static_cast<uint32_t>(N) + gn), lds_addr(lds + blk * 1024));
-}
-__device__ __forceinline__ void dma_kn(const int8_t* __restrict__ b, char* lds, int N, int K,
-                                       int n0, int k0) {
-#pragma unroll
-  for (int i = 0; i < kn_ops(); ++i) dma_kn_one(b, lds, N, K, n0, k0, i);
-}
-
-// ---- register-staged [K][N] weight (N not a multiple of 16) ----
-__device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
-                                             uint32_t& c0, uint32_t& c1, uint32_t& c2,
-                                             uint32_t& c3) {
-  // input: a..d are rows k0..k3, byte j = column j; output cj = column j, byte i = row ki
-  const uint32_t t0 = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
-  const uint32_t t1 = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
-  const uint32_t t2 = __builtin_amdgcn_perm(d, c, 0x05010400u);  // c0 d0 c1 d1
-  const uint32_t t3 = __builtin_amdgcn_perm(d, c, 0x07030602u);  // c2 d2 c3 d3
-  c0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);               // a0 b0 c0 d0
-  c1 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);               // a1 b1 c1 d1
-  c2 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);               // a2 b2 c2 d2
-  c3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);               // a3 b3 c3 d3
-}
-
-template <bool N4>
-struct KnRegTile {
-  uint32_t v[16];  // v[r] = columns 4cg..4cg+3 of k row 16rg + r; thread = (cg, rg) = (t%32, t/32)
-
-  __device__ __forceinline__ void load(const int8_t* __restrict__ b, int N, int K, int n0, int k0) {
-    const int t = threadIdx.x;
-    if (t >= 256) return;  // waves 0-3 stage the 128 x 128 tile
-    const int gn = n0 + 4 * (t & 31);
-    const int kb = k0 + 16 * (t >> 5);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint32_t gk = static_cast<uint32_t>(min(kb + r, K - 1));
-      if constexpr (N4) {
-        const uint32_t gnc = static_cast<uint32_t>(min(gn, N - 4));
-        v[r] = *reinterpret_cast<const uint32_t*>(b + (gk * static_cast<uint32_t>(N) + gnc));
-      } else {
-        const int8_t* row = b + gk * static_cast<uint32_t>(N);
-        uint32_t w = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          w |= static_cast<uint32_t>(static_cast<uint8_t>(row[min(gn + j, N - 1)])) << (8 * j);
-        v[r] = w;
-      }
-    }
-  }
-  // written as k-contiguous [n][k] rows (read like A)
-  __device__ __forceinline__ void store(char* lds) const {
-    const int t = threadIdx.x;
-    if (t >= 256) return;
-    const int cg = t & 31;
-    const int rg = t >> 5;
-    uint32_t col[4][4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      transpose4x4(v[4 * d], v[4 * d + 1], v[4 * d + 2], v[4 * d + 3], col[0][d], col[1][d],
-                   col[2][d], col[3][d]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint4*>(lds + rowk_offset(4 * cg + j, rg)) =
-          make_uint4(col[j][0], col[j][1], col[j][2], col[j][3]);
-  }
-};
-
-struct NoRegTile {
-  __device__ __forceinline__ void load(const int8_t*, int, int, int, int) {}
-  __device__ __forceinline__ void store(char*) const {}
-};
-
-__device__ __forceinline__ uint16_t to_bf16(float f) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
-}
-
-// 4 x 4 transpose across each quad of lanes: lane i of the quad holds x[k]
-// = element (k, i) of a 4 x 4 block; afterwards y[k] = element (i, k).  Two
-// butterfly steps (partner lane i ^ 1, then i ^ 2), each exchanging the
-// off-diagonal 2 x 2 blocks with DPP quad permutations.
-__device__ __forceinline__ void quad_transpose(int x0, int x1, int x2, int x3, int i, int* y) {
-  // quad_perm(1, 0, 3, 2) = 0xB1: read lane i ^ 1; quad_perm(2, 3, 0, 1) = 0x4E: read lane i ^ 2
-  const bool odd = i & 1;
-  const int p0 = __builtin_amdgcn_mov_dpp(x0, 0xB1, 0xF, 0xF, false);
-  const int p1 = __builtin_amdgcn_mov_dpp(x1, 0xB1, 0xF, 0xF, false);
-  const int p2 = __builtin_amdgcn_mov_dpp(x2, 0xB1, 0xF, 0xF, false);
-  const int p3 = __builtin_amdgcn_mov_dpp(x3, 0xB1, 0xF, 0xF, false);
-  const int a0 = odd ? p1 : x0;
-  const int a1 = odd ? x1 : p0;
-  const int a2 = odd ? p3 : x2;
-  const int a3 = odd ? x3 : p2;
-  const bool hi = i & 2;
-  const int r0 = __builtin_amdgcn_mov_dpp(a0, 0x4E, 0xF, 0xF, false);
-  const int r1 = __builtin_amdgcn_mov_dpp(a1, 0x4E, 0xF, 0xF, false);
-  const int r2 = __builtin_amdgcn_mov_dpp(a2, 0x4E, 0xF, 0xF, false);
-  const int r3 = __builtin_amdgcn_mov_dpp(a3, 0x4E, 0xF, 0xF, false);
-  y[0] = hi ? r2 : a0;
-  y[1] = hi ? r3 : a1;
-  y[2] = hi ? a2 : r0;
-  y[3] = hi ? a3 : r1;
-}
-
-constexpr int kGroupM = 4;
-
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int T = tiles_m * tiles_n;
-  int b = blockIdx.x;
-  if (T % 8 == 0) b = (b % 8) * (T / 8) + b / 8;
-  const int group_tiles = kGroupM * tiles_n;
-  const int g = b / group_tiles;
-  const int first_m = g * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int r = b - g * group_tiles;
-  tm = first_m + r % gm;
-  tn = r / gm;
-}
 
 template <int MODE, bool KTAIL>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
@@ -633,104 +450,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
   constexpr int kFinRows = kHalfM * 16;
   constexpr int kStageBytes = kFinRows * WTN * 4;
   static_assert(kWaves * kStageBytes <= 2 * kSubTiles * kChunkBytes, "staging fits in the hand-over region");
+  static_assert(WTN == kStageCols, "staging rows are one wave tile wide");
   int* stage = reinterpret_cast<int*>(smem + (t >> 6) * kStageBytes);
-  // 16-byte chunk q (columns 4q .. 4q + 3) of staged row r; the XOR keeps the
-  // transposed writes and both read patterns below free of bank conflicts
-  auto stage_at = [&](int r, int q) -> v4i* {
-    return reinterpret_cast<v4i*>(stage + r * WTN + ((q ^ (((r & 3) << 2) | (r & 1))) << 2));
-  };
-  const int quad_i = lane & 3;  // row within the 4-row group after the transpose
   auto stage_out = [&](auto i_off) {
 #pragma unroll
     for (int ii = 0; ii < kHalfM; ++ii)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        int v[4];
-        quad_transpose(acc[i_off + ii][j][0], acc[i_off + ii][j][1], acc[i_off + ii][j][2],
-                       acc[i_off + ii][j][3], quad_i, v);
-        *stage_at(ii * 16 + 4 * (lane >> 4) + quad_i, 4 * j + ((lane & 15) >> 2)) =
-            v4i{v[0], v[1], v[2], v[3]};
-      }
+      for (int j = 0; j < FN; ++j) stage_fragment(stage, lane, ii, j, acc[i_off + ii][j]);
   };
   if (grp == 0) stage_out(std::integral_constant<int, 0>{}); else stage_out(std::integral_constant<int, kHalfM>{});
 
   const int lrow0 = wm * WTM + (grp == 0 ? 0 : kFinRows);  // tile-local first row of the block
   const int lcol0 = wn * WTN;
-  // raw accumulators and fp32: 4 columns (16 bytes) per lane, 4 rows per pass
-  auto store4 = [&](auto is_c) {
-    const int q = lane & 15;
-    const int lcol = lcol0 + 4 * q;
-    const int gcol = n0 + lcol;
-    float sb4[4];
-    if constexpr (!decltype(is_c)::value) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sb4[e] = s_sb[lcol + e];
-    }
-#pragma unroll 4
-    for (int pass = 0; pass < kFinRows / 4; ++pass) {
-      const int r = 4 * pass + (lane >> 4);
-      const int grow = m0 + lrow0 + r;
-      const v4i v = *stage_at(r, q);
-      if (grow >= M) continue;
-      const size_t base = static_cast<size_t>(grow) * N + gcol;
-      if constexpr (decltype(is_c)::value) {
-        int32_t* o = c + base;
-        if (gcol + 4 <= N && reinterpret_cast<uintptr_t>(o) % 16 == 0) {
-          __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(o));
-        } else {
-          for (int e = 0; e < 4; ++e)
-            if (gcol + e < N) o[e] = v[e];
-        }
-      } else {
-        typedef float v4f __attribute__((ext_vector_type(4)));
-        const float sa = s_sa[lrow0 + r];
-        v4f f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = (static_cast<float>(v[e]) * sa) * sb4[e];
-        float* o = static_cast<float*>(out) + base;
-        if (gcol + 4 <= N && reinterpret_cast<uintptr_t>(o) % 16 == 0) {
-          __builtin_nontemporal_store(f, reinterpret_cast<v4f*>(o));
-        } else {
-          for (int e = 0; e < 4; ++e)
-            if (gcol + e < N) o[e] = f[e];
-        }
-      }
-    }
-  };
-  // bf16: 8 columns (16 bytes) per lane, 8 rows per pass
-  auto store_bf16 = [&]() {
-    const int q2 = lane & 7;
-    const int lcol = lcol0 + 8 * q2;
-    const int gcol = n0 + lcol;
-    float sb8[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sb8[e] = s_sb[lcol + e];
-#pragma unroll 4
-    for (int pass = 0; pass < kFinRows / 8; ++pass) {
-      const int r = 8 * pass + (lane >> 3);
-      const int grow = m0 + lrow0 + r;
-      const v4i v0 = *stage_at(r, 2 * q2);
-      const v4i v1 = *stage_at(r, 2 * q2 + 1);
-      if (grow >= M) continue;
-      const float sa = s_sa[lrow0 + r];
-      uint32_t h[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        h[e] = to_bf16((static_cast<float>(e < 4 ? v0[e] : v1[e - 4]) * sa) * sb8[e]);
-      uint16_t* o = static_cast<uint16_t*>(out) + static_cast<size_t>(grow) * N + gcol;
-      if (gcol + 8 <= N && reinterpret_cast<uintptr_t>(o) % 16 == 0) {
-        const v4i w = {static_cast<int>(h[0] | (h[1] << 16)), static_cast<int>(h[2] | (h[3] << 16)),
-                       static_cast<int>(h[4] | (h[5] << 16)), static_cast<int>(h[6] | (h[7] << 16))};
-        __builtin_nontemporal_store(w, reinterpret_cast<v4i*>(o));
-      } else {
-        for (int e = 0; e < 8; ++e)
-          if (gcol + e < N) o[e] = static_cast<uint16_t>(h[e]);
-      }
-    }
-  };
-  if (c) store4(std::true_type{});
+  if (c) store4<kFinRows, false, true>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, c);
   if (out) {
-    if (out_dtype == QK_BF16) store_bf16(); else store4(std::false_type{});
+    if (out_dtype == QK_BF16)
+      store_bf16<kFinRows, false>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, out);
+    else
+      store4<kFinRows, false, false>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, out);
   }
 }
 

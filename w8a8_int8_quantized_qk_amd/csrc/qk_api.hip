@@ -176,4 +176,66 @@ int qk_linear_w8a8(int m, int n, int k, const void* x, int x_dtype, const int8_t
   return status_of(qk::launch_gemm_mfma(g, stream));
 }
 
+int qk_quant_per_token_fp8(int m, int k, const void* x, int x_dtype, float scale_ub, uint8_t* q,
+                           float* scale, hipStream_t stream) {
+  const int rc = check_rows(m, k, x, q, scale, x_dtype);
+  if (rc != QK_OK) return rc;
+  if (scale_ub != scale_ub) return QK_ERR_INVALID_VALUE;  // NaN bound
+  if (m == 0) return QK_OK;
+  return status_of(qk::launch_quant_rows_fp8(m, k, x, x_dtype, q, scale, scale_ub, stream));
+}
+
+int qk_silu_mul_quant_per_token_fp8(int m, int d, const void* h, int h_dtype, float scale_ub,
+                                    uint8_t* q, float* scale, hipStream_t stream) {
+  const int rc = check_rows(m, d, h, q, scale, h_dtype);
+  if (rc != QK_OK) return rc;
+  if (scale_ub != scale_ub) return QK_ERR_INVALID_VALUE;
+  if (m == 0) return QK_OK;
+  if (static_cast<long long>(d) * 2 > 0x7fffffffLL) return QK_ERR_UNSUPPORTED;
+  return status_of(qk::launch_silu_quant_rows_fp8(m, d, h, h_dtype, q, scale, scale_ub, stream));
+}
+
+int qk_gemm_fp8_scaled(int m, int n, int k, const uint8_t* a, const uint8_t* b, float* c,
+                       const float* scale_a, const float* scale_b, float output_scale, void* out,
+                       int out_dtype, int b_layout, hipStream_t stream) {
+  if (m < 0 || n < 0 || k < 0 || k > QK_MAX_K) return QK_ERR_INVALID_VALUE;
+  if (b_layout != QK_B_KN && b_layout != QK_B_NK) return QK_ERR_INVALID_VALUE;
+  if (k % 16 != 0) return QK_ERR_UNSUPPORTED;
+  if (m == 0 || n == 0) return QK_OK;
+  if (!c && !out) return QK_ERR_INVALID_VALUE;
+  if (out && out_dtype != QK_F32 && out_dtype != QK_BF16) return QK_ERR_INVALID_VALUE;
+  if (k > 0 && (!a || !b)) return QK_ERR_INVALID_VALUE;
+  if (out && (!scale_a || !scale_b)) return QK_ERR_INVALID_VALUE;
+  if (!aligned(a, 16) || !aligned(b, 16)) return QK_ERR_UNSUPPORTED;
+  if (c && !aligned(c, 4)) return QK_ERR_UNSUPPORTED;
+  if (out && !aligned(out, out_dtype == QK_BF16 ? 2 : 4)) return QK_ERR_UNSUPPORTED;
+  if (!qk::gemm_mfma_supported(m, n, k)) return QK_ERR_UNSUPPORTED;
+  qk::GemmFp8Args g{m, n, k, a, b, c, scale_a, scale_b, output_scale, out, out_dtype, b_layout};
+  return status_of(qk::launch_gemm_fp8(g, stream));
+}
+
+int qk_linear_fp8(int m, int n, int k, const void* x, int x_dtype, float scale_ub,
+                  const uint8_t* b, const float* scale_b, float output_scale, void* out,
+                  int out_dtype, int b_layout, uint8_t* q_out, float* scale_out,
+                  hipStream_t stream) {
+  if (m < 0 || n < 0 || k < 0 || k > QK_MAX_K) return QK_ERR_INVALID_VALUE;
+  if (!known_input_dtype(x_dtype)) return QK_ERR_INVALID_VALUE;
+  if (b_layout != QK_B_KN && b_layout != QK_B_NK) return QK_ERR_INVALID_VALUE;
+  if (out_dtype != QK_F32 && out_dtype != QK_BF16) return QK_ERR_INVALID_VALUE;
+  if (scale_ub != scale_ub) return QK_ERR_INVALID_VALUE;
+  if (k % 16 != 0) return QK_ERR_UNSUPPORTED;
+  if (m == 0 || n == 0) return QK_OK;
+  if (!out || !scale_b || !q_out || !scale_out || (k > 0 && (!x || !b)))
+    return QK_ERR_INVALID_VALUE;
+  if (!aligned(b, 16) || !aligned(q_out, 16) || !aligned(scale_out, 4)) return QK_ERR_UNSUPPORTED;
+  if (!aligned(x, x_dtype == QK_F32 ? 4 : 2)) return QK_ERR_UNSUPPORTED;
+  if (!aligned(out, out_dtype == QK_BF16 ? 2 : 4)) return QK_ERR_UNSUPPORTED;
+  if (!qk::gemm_mfma_supported(m, n, k)) return QK_ERR_UNSUPPORTED;
+  hipError_t e = qk::launch_quant_rows_fp8(m, k, x, x_dtype, q_out, scale_out, scale_ub, stream);
+  if (e != hipSuccess) return status_of(e);
+  qk::GemmFp8Args g{m, n, k, q_out, b, nullptr, scale_out, scale_b, output_scale, out, out_dtype,
+                    b_layout};
+  return status_of(qk::launch_gemm_fp8(g, stream));
+}
+
 }  // extern "C"

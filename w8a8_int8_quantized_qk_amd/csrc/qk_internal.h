@@ -51,11 +51,32 @@ hipError_t launch_quant_rows(int m, int k, const void* x, int dtype, int8_t* q, 
 // silu(gate) * up then per-token quantization, one workgroup per row (quant.hip).
 hipError_t launch_silu_quant_rows(int m, int d, const void* h, int dtype, int8_t* q,
                                   float* scale, hipStream_t stream);
+// The same two with float8_e4m3fn codes and the optional scale bound.
+hipError_t launch_quant_rows_fp8(int m, int k, const void* x, int dtype, uint8_t* q, float* scale,
+                                 float scale_ub, hipStream_t stream);
+hipError_t launch_silu_quant_rows_fp8(int m, int d, const void* h, int dtype, uint8_t* q,
+                                      float* scale, float scale_ub, hipStream_t stream);
 
 // LDS-tiled INT8 MFMA GEMM with fused epilogue (gemm_mfma.hip).  Operands
 // are addressed with 32-bit offsets: m*k and n*k must stay below 2^32.
 bool gemm_mfma_supported(int m, int n, int k);
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
+
+// FP8 (e4m3fn) MFMA GEMM with binary32 accumulation and the fused epilogue
+// (gemm_fp8.hip); the same tiles, layouts and size limits as the INT8 one.
+struct GemmFp8Args {
+  int m, n, k;
+  const uint8_t* a;  // e4m3fn codes [m][k]
+  const uint8_t* b;  // e4m3fn codes [k][n] or [n][k]
+  float* c;          // raw binary32 accumulators [m][n] or nullptr
+  const float* scale_a;
+  const float* scale_b;
+  float output_scale;
+  void* out;
+  int out_dtype;  // QK_F32 | QK_BF16 (ignored when out == nullptr)
+  int b_layout;   // QK_B_KN | QK_B_NK
+};
+hipError_t launch_gemm_fp8(const GemmFp8Args& g, hipStream_t stream);
 
 // Split-K decode GEMV (gemv.hip): m <= kGemvMaxRows rows per launch, larger m
 // in row groups; exact partial sums with arrival counts in a self-cleaning

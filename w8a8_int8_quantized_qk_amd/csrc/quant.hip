@@ -1,9 +1,12 @@
-// Per-token dynamic INT8 quantization for gfx950, plain and fused with silu(gate) * up.
+// Per-token dynamic quantization for gfx950, to INT8 or FP8 codes, plain and
+// fused with silu(gate) * up.
 //
 // Method ("kernels: fused silu_and_mul + dynamic per-token FP8 quantization",
 // Purpose and Algorithm; symmetric [-127, 127] codes from "Skill: Write an
 // INT8 Quantized Kernel", Inputs):
-//   scale = max(row absmax, 1e-12) / 127, code = clamp(rint(x / scale), -127, 127).
+//   INT8: scale = max(row absmax, 1e-12) / 127, code = clamp(rint(x / scale), -127, 127);
+//   FP8:  scale = min(max(row absmax, 1e-12) / 448, scale_ub if > 0),
+//         code = e4m3fn(x / scale), nearest even, saturating at +-448.
 //
 // Rows of up to 128 16-byte units take one wave each (absmax by cross-lane
 // max steps only); rows of up to 2048 units take one workgroup of four waves
@@ -35,6 +38,27 @@ using qm::Elem;
 using qm::code_of;
 using qm::pack4;
 using qm::row_scale;
+
+enum Fmt { kI8 = 0, kF8 = 1 };
+
+// the row's scale s and r = RN(1 / s)
+template <int FMT>
+__device__ __forceinline__ void scale_of(float amax, float scale_ub, float& s, float& r) {
+  if constexpr (FMT == kI8)
+    row_scale(amax, s, r);
+  else
+    qm::row_scale_fp8(amax, scale_ub, s, r);
+}
+
+// the code byte of one value
+template <int FMT>
+__device__ __forceinline__ int8_t code_byte(float x, float s, float r) {
+  if constexpr (FMT == kI8) {
+    return static_cast<int8_t>(code_of(x, s, r));
+  } else {
+    return static_cast<int8_t>(__builtin_amdgcn_cvt_pk_fp8_f32(qm::fp8_ratio(x, s, r), 0.0f, 0, false) & 0xff);
+  }
+}
 
 constexpr int kBlock = 256;    // threads per workgroup
 constexpr int kMaxUnits = 8;   // 16-byte input units cached per lane
@@ -77,18 +101,26 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 // stores: the GEMM that consumes the codes usually runs next and finds them
 // in the caches (measured on the prefill step: 0.4 us faster than
 // nontemporal stores, although the quantization alone is slower).
-template <int P>
+template <int FMT, int P>
 __device__ __forceinline__ void store_codes(int8_t* dst, const float (&v)[P], float s, float r) {
-  int c[P];
+  uint32_t w[P / 4];
+  if constexpr (FMT == kI8) {
+    int c[P];
 #pragma unroll
-  for (int e = 0; e < P; ++e) c[e] = code_of(v[e], s, r);
-  if constexpr (P == 8) {
-    v2u w;
-    w.x = pack4(c[0], c[1], c[2], c[3]);
-    w.y = pack4(c[4], c[5], c[6], c[7]);
-    *reinterpret_cast<v2u*>(dst) = w;
+    for (int e = 0; e < P; ++e) c[e] = code_of(v[e], s, r);
+#pragma unroll
+    for (int i = 0; i < P / 4; ++i) w[i] = pack4(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
   } else {
-    *reinterpret_cast<uint32_t*>(dst) = pack4(c[0], c[1], c[2], c[3]);
+    float f[P];
+#pragma unroll
+    for (int e = 0; e < P; ++e) f[e] = qm::fp8_ratio(v[e], s, r);
+#pragma unroll
+    for (int i = 0; i < P / 4; ++i) w[i] = qm::pack4_fp8(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
+  }
+  if constexpr (P == 8) {
+    *reinterpret_cast<v2u*>(dst) = v2u{w[0], w[1]};
+  } else {
+    *reinterpret_cast<uint32_t*>(dst) = w[0];
   }
 }
 
@@ -117,10 +149,11 @@ __device__ __forceinline__ void unit_values(const char* base, int k, int u,
 // Short rows (up to 128 units): one wave per row, four rows per workgroup.
 // Lane l holds units l, l + 64 (UPL of them) in registers; the absmax needs
 // only cross-lane steps within the wave (no LDS, no barrier).
-template <int DT, bool SILU, int UPL>
+template <int DT, bool SILU, int FMT, int UPL>
 __global__ __launch_bounds__(kBlock) void quant_rows_wave(const void* __restrict__ src,
                                                          int8_t* __restrict__ q,
-                                                         float* __restrict__ scale, int m, int k) {
+                                                         float* __restrict__ scale, float scale_ub,
+                                                         int m, int k) {
   using E = Elem<DT>;
   constexpr int P = E::kPerUnit;
   const int units = k / P;
@@ -143,14 +176,14 @@ __global__ __launch_bounds__(kBlock) void quant_rows_wave(const void* __restrict
   }
   amax = qm::wave_max_nonneg(amax);
   float s, r;
-  row_scale(amax, s, r);
+  scale_of<FMT>(amax, scale_ub, s, r);
   if (lane == 0) scale[row] = s;
 
   int8_t* qrow = q + row * static_cast<size_t>(k);
 #pragma unroll
   for (int j = 0; j < UPL; ++j) {
     const int u = lane + 64 * j;
-    if (u < units) store_codes<P>(qrow + static_cast<size_t>(u) * P, v[j], s, r);
+    if (u < units) store_codes<FMT, P>(qrow + static_cast<size_t>(u) * P, v[j], s, r);
   }
 }
 
@@ -160,10 +193,11 @@ __global__ __launch_bounds__(kBlock) void quant_rows_wave(const void* __restrict
 // recomputes the activation, is not needed.  (Many short-lived waves with a
 // few loads each keep more of the chip's memory pipeline busy than fewer
 // waves with many: measured faster than one wave per row at 512 units.)
-template <int DT, bool SILU, int UPT>
+template <int DT, bool SILU, int FMT, int UPT>
 __global__ __launch_bounds__(kBlock) void quant_rows_cached(const void* __restrict__ src,
                                                            int8_t* __restrict__ q,
-                                                           float* __restrict__ scale, int k) {
+                                                           float* __restrict__ scale,
+                                                           float scale_ub, int k) {
   using E = Elem<DT>;
   constexpr int P = E::kPerUnit;
   const int units = k / P;
@@ -184,23 +218,24 @@ __global__ __launch_bounds__(kBlock) void quant_rows_cached(const void* __restri
   }
   amax = qm::block_max<kBlock>(amax);
   float s, r;
-  row_scale(amax, s, r);
+  scale_of<FMT>(amax, scale_ub, s, r);
   if (threadIdx.x == 0) scale[row] = s;
 
   int8_t* qrow = q + row * static_cast<size_t>(k);
 #pragma unroll
   for (int j = 0; j < UPT; ++j) {
     const int u = threadIdx.x + j * kBlock;
-    if (u < units) store_codes<P>(qrow + static_cast<size_t>(u) * P, v[j], s, r);
+    if (u < units) store_codes<FMT, P>(qrow + static_cast<size_t>(u) * P, v[j], s, r);
   }
 }
 
 // Two-pass path for any k and alignment: pass 1 reduces the absmax, pass 2
 // re-reads (and for SILU recomputes) each value and writes its code.
-template <int DT, bool SILU>
+template <int DT, bool SILU, int FMT>
 __global__ __launch_bounds__(kBlock) void quant_rows_twopass(const void* __restrict__ src,
                                                             int8_t* __restrict__ q,
-                                                            float* __restrict__ scale, int k) {
+                                                            float* __restrict__ scale,
+                                                            float scale_ub, int k) {
   using E = Elem<DT>;
   const size_t row = blockIdx.x;
   const size_t first = row * static_cast<size_t>(SILU ? 2 : 1) * k;
@@ -213,14 +248,15 @@ __global__ __launch_bounds__(kBlock) void quant_rows_twopass(const void* __restr
   for (int j = threadIdx.x; j < k; j += kBlock) amax = __builtin_fmaxf(amax, __builtin_fabsf(value(j)));
   amax = qm::block_max<kBlock>(amax);
   float s, r;
-  row_scale(amax, s, r);
+  scale_of<FMT>(amax, scale_ub, s, r);
   if (threadIdx.x == 0) scale[row] = s;
   int8_t* qrow = q + row * static_cast<size_t>(k);
-  for (int j = threadIdx.x; j < k; j += kBlock) qrow[j] = static_cast<int8_t>(code_of(value(j), s, r));
+  for (int j = threadIdx.x; j < k; j += kBlock) qrow[j] = code_byte<FMT>(value(j), s, r);
 }
 
-template <int DT, bool SILU>
-hipError_t dispatch(int m, int k, const void* src, int8_t* q, float* scale, hipStream_t stream) {
+template <int DT, bool SILU, int FMT>
+hipError_t dispatch(int m, int k, const void* src, int8_t* q, float* scale, float scale_ub,
+                    hipStream_t stream) {
   using E = Elem<DT>;
   const bool aligned = (reinterpret_cast<uintptr_t>(src) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(q) % E::kPerUnit == 0) &&
@@ -229,28 +265,36 @@ hipError_t dispatch(int m, int k, const void* src, int8_t* q, float* scale, hipS
   if (aligned && units <= 128) {
     const dim3 grid((static_cast<unsigned>(m) + kBlock / 64 - 1) / (kBlock / 64));
     if (units <= 64)
-      return launch(quant_rows_wave<DT, SILU, 1>, grid, dim3(kBlock), 0, stream, src, q, scale, m, k);
-    return launch(quant_rows_wave<DT, SILU, 2>, grid, dim3(kBlock), 0, stream, src, q, scale, m, k);
+      return launch(quant_rows_wave<DT, SILU, FMT, 1>, grid, dim3(kBlock), 0, stream, src, q, scale,
+                    scale_ub, m, k);
+    return launch(quant_rows_wave<DT, SILU, FMT, 2>, grid, dim3(kBlock), 0, stream, src, q, scale,
+                  scale_ub, m, k);
   }
   if (aligned && units <= kBlock * kMaxUnits) {
+    const dim3 grid(m);
     if (units <= kBlock)
-      return launch(quant_rows_cached<DT, SILU, 1>, dim3(m), dim3(kBlock), 0, stream, src, q, scale, k);
+      return launch(quant_rows_cached<DT, SILU, FMT, 1>, grid, dim3(kBlock), 0, stream, src, q,
+                    scale, scale_ub, k);
     if (units <= kBlock * 2)
-      return launch(quant_rows_cached<DT, SILU, 2>, dim3(m), dim3(kBlock), 0, stream, src, q, scale, k);
+      return launch(quant_rows_cached<DT, SILU, FMT, 2>, grid, dim3(kBlock), 0, stream, src, q,
+                    scale, scale_ub, k);
     if (units <= kBlock * 4)
-      return launch(quant_rows_cached<DT, SILU, 4>, dim3(m), dim3(kBlock), 0, stream, src, q, scale, k);
-    return launch(quant_rows_cached<DT, SILU, 8>, dim3(m), dim3(kBlock), 0, stream, src, q, scale, k);
+      return launch(quant_rows_cached<DT, SILU, FMT, 4>, grid, dim3(kBlock), 0, stream, src, q,
+                    scale, scale_ub, k);
+    return launch(quant_rows_cached<DT, SILU, FMT, 8>, grid, dim3(kBlock), 0, stream, src, q,
+                  scale, scale_ub, k);
   }
-  return launch(quant_rows_twopass<DT, SILU>, dim3(m), dim3(kBlock), 0, stream, src, q, scale, k);
+  return launch(quant_rows_twopass<DT, SILU, FMT>, dim3(m), dim3(kBlock), 0, stream, src, q, scale,
+                scale_ub, k);
 }
 
-template <bool SILU>
+template <bool SILU, int FMT>
 hipError_t dispatch_dtype(int m, int k, const void* src, int dtype, int8_t* q, float* scale,
-                          hipStream_t stream) {
+                          float scale_ub, hipStream_t stream) {
   switch (dtype) {
-    case QK_F32: return dispatch<QK_F32, SILU>(m, k, src, q, scale, stream);
-    case QK_BF16: return dispatch<QK_BF16, SILU>(m, k, src, q, scale, stream);
-    case QK_F16: return dispatch<QK_F16, SILU>(m, k, src, q, scale, stream);
+    case QK_F32: return dispatch<QK_F32, SILU, FMT>(m, k, src, q, scale, scale_ub, stream);
+    case QK_BF16: return dispatch<QK_BF16, SILU, FMT>(m, k, src, q, scale, scale_ub, stream);
+    case QK_F16: return dispatch<QK_F16, SILU, FMT>(m, k, src, q, scale, scale_ub, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -259,12 +303,24 @@ hipError_t dispatch_dtype(int m, int k, const void* src, int dtype, int8_t* q, f
 
 hipError_t launch_quant_rows(int m, int k, const void* x, int dtype, int8_t* q, float* scale,
                              hipStream_t stream) {
-  return dispatch_dtype<false>(m, k, x, dtype, q, scale, stream);
+  return dispatch_dtype<false, kI8>(m, k, x, dtype, q, scale, 0.0f, stream);
 }
 
 hipError_t launch_silu_quant_rows(int m, int d, const void* h, int dtype, int8_t* q,
                                   float* scale, hipStream_t stream) {
-  return dispatch_dtype<true>(m, d, h, dtype, q, scale, stream);
+  return dispatch_dtype<true, kI8>(m, d, h, dtype, q, scale, 0.0f, stream);
+}
+
+hipError_t launch_quant_rows_fp8(int m, int k, const void* x, int dtype, uint8_t* q, float* scale,
+                                 float scale_ub, hipStream_t stream) {
+  return dispatch_dtype<false, kF8>(m, k, x, dtype, reinterpret_cast<int8_t*>(q), scale, scale_ub,
+                                    stream);
+}
+
+hipError_t launch_silu_quant_rows_fp8(int m, int d, const void* h, int dtype, uint8_t* q,
+                                      float* scale, float scale_ub, hipStream_t stream) {
+  return dispatch_dtype<true, kF8>(m, d, h, dtype, reinterpret_cast<int8_t*>(q), scale, scale_ub,
+                                   stream);
 }
 
 }  // namespace qk

@@ -138,6 +138,45 @@ __device__ __forceinline__ void row_scale(float amax, float& s, float& r) {
   r = 1.0f / s;
 }
 
+// ---- FP8 (float8_e4m3fn) codes ----
+// "kernels: fused silu_and_mul + dynamic per-token FP8 quantization",
+// Algorithm: scale = max(absmax, 1e-12) / 448 (the format's largest finite
+// value), optionally clamped from above by scale_ub; the code is the e4m3fn
+// value nearest x / scale (ties to even), saturating at +-448.
+
+// s = max(amax, 1e-12f) / 448 (IEEE division, once per row), then
+// min(s, scale_ub) when scale_ub > 0; r = RN(1 / s).
+__device__ __forceinline__ void row_scale_fp8(float amax, float scale_ub, float& s, float& r) {
+  s = __builtin_fmaxf(amax, 1e-12f) / 448.0f;
+  if (scale_ub > 0.0f && s > scale_ub) s = scale_ub;
+  r = 1.0f / s;
+}
+
+// x / s, correctly rounded (the same correction as code_of), clamped to
+// [-448, 448].  With scale_ub the quotient can exceed the binary32 range:
+// y is first clamped to +-1024, which leaves every y that can round to a
+// finite code unchanged and keeps the residual step finite; a clamped y gives
+// a quotient beyond 1000 in magnitude, which saturates like the true one.
+// The residual is formed negated, e' = y s - x, and the quotient as
+// y - e' r: the same values as x - y s and y + e r for every nonzero x, but
+// for x = -0 the sums are -0 + -0 rather than +0 + -0, so the quotient keeps
+// the sign of zero (the codes of +0 and -0 differ).
+__device__ __forceinline__ float fp8_ratio(float x, float s, float r) {
+  float y = x * r;
+  y = __builtin_amdgcn_fmed3f(y, -1024.0f, 1024.0f);
+  const float en = __builtin_fmaf(y, s, -x);
+  const float q = __builtin_fmaf(-en, r, y);
+  return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f);
+}
+
+// Four codes packed little-endian (a in byte 0).  v_cvt_pk_fp8_f32 converts
+// to OCP e4m3fn on gfx950, rounding to nearest even; its inputs are already
+// within +-448, so no value reaches the overflow encodings.
+__device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
 
 }  // namespace qm
 }  // namespace qk

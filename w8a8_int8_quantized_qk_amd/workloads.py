@@ -20,8 +20,10 @@ float32; for the outlier workload, the column set (drawn without replacement)
 is multiplied by 50 in float32; X is cast to bf16/fp16 by round-to-nearest-
 even (torch); W is uniform on the integers [-127, 127]; the per-channel
 scales are uniform on [1e-3, 1e-2] in float32.  The gated workload draws H in
-place of X.  These shapes and distributions follow the workloads the pages
-describe (decode GEMV vs prefill GEMM, outlier channels, fused gated MLP).
+place of X.  For the FP8 layer the weight is drawn instead as N(0, 1) x 100,
+clipped to +-448 and cast to float8_e4m3fn by torch.  These shapes and
+distributions follow the workloads the pages describe (decode GEMV vs prefill
+GEMM, outlier channels, fused gated MLP).
 """
 from __future__ import annotations
 
@@ -92,12 +94,23 @@ def random_weight(rng: np.random.Generator, k: int, n: int) -> np.ndarray:
     return rng.integers(-127, 128, size=(k, n), dtype=np.int8)
 
 
+def random_weight_fp8(rng: np.random.Generator, k: int, n: int) -> np.ndarray:
+    """float8_e4m3fn weight codes [k, n] as uint8: N(0, 1) draws times 100 in
+    float32, clipped to +-448 and cast by torch (round to nearest even)."""
+    w = rng.standard_normal((k, n), dtype=np.float32) * np.float32(100.0)
+    t = torch.from_numpy(np.clip(w, -448.0, 448.0)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
 def random_channel_scales(rng: np.random.Generator, n: int) -> np.ndarray:
     return rng.uniform(1e-3, 1e-2, n).astype(np.float32)
 
 
-def generate(name_or_workload, seed: int = 0) -> dict:
-    """Inputs of a named workload: {'x' or 'h': torch CPU, 'w': int8 [K,N], 's_ch': f32 [N]}."""
+def generate(name_or_workload, seed: int = 0, weight: str = "i8") -> dict:
+    """Inputs of a named workload: {'x' or 'h': torch CPU, 'w': [K,N], 's_ch': f32 [N]}.
+
+    weight "i8" draws int8 codes, "fp8" float8_e4m3fn codes (uint8 bytes); the
+    activations are the same either way."""
     wl = WORKLOADS[name_or_workload] if isinstance(name_or_workload, str) else name_or_workload
     rng = np.random.default_rng(seed)
     out = {"workload": wl}
@@ -106,7 +119,12 @@ def generate(name_or_workload, seed: int = 0) -> dict:
     else:
         out["x"] = random_activations(rng, wl.m, wl.k, wl.x_dtype, wl.outlier_cols,
                                       wl.outlier_mult)
-    out["w"] = random_weight(rng, wl.k, wl.n)
+    if weight == "fp8":
+        out["w"] = random_weight_fp8(rng, wl.k, wl.n)
+    elif weight == "i8":
+        out["w"] = random_weight(rng, wl.k, wl.n)
+    else:
+        raise ValueError(f"weight must be 'i8' or 'fp8', got {weight!r}")
     out["s_ch"] = random_channel_scales(rng, wl.n)
     return out
 
