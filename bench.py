@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 
 INT8_PEAK_TOPS = 5000.0     # MI355X dense INT8 MFMA, published
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA, published
 CSRC = os.path.join(ROOT, "w8a8_int8_quantized_qk_amd", "csrc")
 GEMM_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_mfma_prefill_outliers_traffic.txt"),
                 os.path.join(CSRC, "gemm_mfma.hip"))
@@ -308,6 +309,35 @@ def main():
                             "gemm_frac_of_int8_peak": round(ops / (gemm_only_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
             del gsets
             torch.cuda.empty_cache()
+        # the FP8 layer at the prefill shape: per-token e4m3fn quantization +
+        # FP8 GEMM (binary32 accumulation), same activations, e4m3fn weights
+        fsets = []
+        for r in range(args.ring):
+            d = wl.generate(wcfg, seed=r, weight="fp8")
+            fsets.append({"x": d["x"].to(dev), "w": torch.from_numpy(d["w"]).to(dev).view(torch.float8_e4m3fn),
+                          "s_ch": torch.from_numpy(d["s_ch"]).to(dev),
+                          "q": torch.empty((m, k), dtype=torch.float8_e4m3fn, device=dev),
+                          "s": torch.empty((m,), dtype=torch.float32, device=dev),
+                          "out": torch.empty((m, n), dtype=torch.bfloat16, device=dev)})
+
+        def fquant(bs):
+            qk.quant_per_token_fp8(bs["x"], 0.0, bs["q"], bs["s"])
+
+        def fgemm(bs):
+            qk.gemm_fp8_scaled(bs["q"], bs["w"], bs["s"], bs["s_ch"], out=bs["out"])
+
+        fstep_ms, _ = timed_replays([(lambda bs=b: (fquant(bs), fgemm(bs))) for b in fsets], args.steps, args.warmup)
+        fgemm_ms, _ = timed_replays([(lambda bs=b: fgemm(bs)) for b in fsets], args.steps, args.warmup)
+        fops = 2.0 * m * n * k
+        others["fp8_prefill"] = {
+            "m": m, "k": k, "n": n, "x_dtype": "bf16", "w": "e4m3fn [K,N]", "out_dtype": "bf16",
+            "us_per_step": round(fstep_ms * 1e3, 2),
+            "step_tflops": round(fops / (fstep_ms * 1e-3) / 1e12, 1),
+            "gemm_us": round(fgemm_ms * 1e3, 2),
+            "gemm_tflops": round(fops / (fgemm_ms * 1e-3) / 1e12, 1),
+            "gemm_frac_of_fp8_peak": round(fops / (fgemm_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}
+        del fsets
+        torch.cuda.empty_cache()
         result["other_configs"] = others
 
     if args.copy_calibration:

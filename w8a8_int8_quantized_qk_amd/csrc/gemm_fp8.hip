@@ -97,8 +97,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_mfma_kernel(
   };
   constexpr int kFetchOps = BM * BK / 1024 / kWaves + (kRegB ? 0 : BN * BK / 1024 / kWaves);
   constexpr int kOpsA = rowk_ops<BM>();
+  constexpr bool kFixedParts = !KTAIL && !kRegB;
+  const uint32_t lds_smem = lds_addr(smem);
+  using Parts = std::conditional_t<kFixedParts, FixedParts<MODE == kBnkDma ? kBnkDma : kBknDma>,
+                                   NoParts>;
+  Parts parts;
+  if constexpr (kFixedParts) {
+    static_assert(Parts::kOps == kFetchOps, "one DMA instruction per part");
+    parts.init(a, b, M, N, K, m0, n0);
+  }
   auto fetch_part = [&](int s, int part) {
-    if (part < kOpsA) {
+    if constexpr (kFixedParts) {
+      parts.issue(lds_smem, s, part);
+    } else if (part < kOpsA) {
       dma_rowk_one<BM>(a, a_lds(s), M, K, m0, s * BK, part);
     } else if constexpr (MODE == kBnkDma) {
       dma_rowk_one<BN>(b, b_lds(s), N, K, n0, s * BK, part - kOpsA);
@@ -117,22 +128,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_mfma_kernel(
     const v4i hi = *reinterpret_cast<const v4i*>(As + rowk_offset(a_row + i * 16, c1));
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   };
-  // transpose read of a [k][n] weight: k rows 16 ch + 8 h .. + 7 of
-  // fragment column block j; lane i16 of a 16-lane group receives column
-  // i16's eight bytes
-  auto read_b_tr = [&](const char* Bs, int j, int ch, int h) -> v2i {
+  // Transpose reads of a [k][n] weight: a read covers k rows kr .. kr + 7
+  // (kr = 16 ch + 8 h + (i16 >> 1) for lane i16 of a 16-lane group) of
+  // fragment column block j, and lane i16 receives column i16's eight bytes.
+  // The row swizzle kn_swz(kr) = (i16 >> 1) ^ (ch & 1) is the same for the
+  // lane's chunks c0 and c1 = c0 + 4 and both halves h, so the four reads
+  // of a fragment share one per-lane base and differ by constants
+  // (64 rows for c1, 8 rows for h).
+  int b_tr_base[FN];
+  {
     const int i16 = lane & 15;
-    const int kr = 16 * ch + (i16 >> 1) + 8 * h;
-    const int cb = (wn * WTN + j * 16) >> 4;
+    const int kr0 = 16 * c0 + (i16 >> 1);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      b_tr_base[j] = kn_offset(kr0, (wn * WTN + j * 16) >> 4) + 8 * (i16 & 1);
+  }
+  auto read_b_tr = [&](const char* Bs, int j, int row_off) -> v2i {
     return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-        (__attribute__((address_space(3))) v2i*)(Bs + kn_offset(kr, cb) + 8 * (i16 & 1)));
+        (__attribute__((address_space(3))) v2i*)(Bs + b_tr_base[j] + row_off * BN));
   };
   auto read_b = [&](const char* Bs, int j) -> v8i {
     if constexpr (MODE == kBknDma) {
-      const v2i p0 = read_b_tr(Bs, j, c0, 0);
-      const v2i p1 = read_b_tr(Bs, j, c0, 1);
-      const v2i p2 = read_b_tr(Bs, j, c1, 0);
-      const v2i p3 = read_b_tr(Bs, j, c1, 1);
+      const v2i p0 = read_b_tr(Bs, j, 0);
+      const v2i p1 = read_b_tr(Bs, j, 8);
+      const v2i p2 = read_b_tr(Bs, j, 64);
+      const v2i p3 = read_b_tr(Bs, j, 72);
       return v8i{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
     } else {
       const v4i lo = *reinterpret_cast<const v4i*>(Bs + rowk_offset(b_row + j * 16, c0));
@@ -208,21 +228,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_mfma_kernel(
     }
   } else {
     // DMA modes, one k slice per iteration in two phases:
-    //   phase 0: MFMAs of A 0..1 x B 0..3 with DMA parts [0, kSplit) of slice
-    //            kt + 2 in between (its LDS stage held slice kt - 1, whose
-    //            fragments every wave read before the barrier of iteration
-    //            kt - 1);
+    //   phase 0: the first kPhase0 MFMAs (A-fragment-major order) with DMA
+    //            parts [0, kSplit) of slice kt + 2 in between (its LDS stage
+    //            held slice kt - 1, whose fragments every wave read before
+    //            the barrier of iteration kt - 1);
     //   barrier: this wave's DMA of slice kt + 1 has landed (vmcnt), then all
     //            waves' (s_barrier);
-    //   phase 1: MFMAs of A 2..3 x B 0..3 with the reads of slice kt + 1's
-    //            fragments into the second register set and the remaining
-    //            DMA parts in between.
+    //   phase 1: the other MFMAs with the reads of slice kt + 1's fragments
+    //            into the second register set spread between them, and the
+    //            remaining DMA parts.
+    constexpr int kPhase0 = 8;
+    constexpr int kPhase1 = FM * FN - kPhase0;
+    constexpr int kReads = FM + FN;
     constexpr int kSplit = kFetchOps / 2;
     static_assert(kFetchOps == 2 * kSplit, "DMA parts split evenly over the two phases");
+    static_assert(kPhase0 >= kSplit && kPhase1 >= kFetchOps - kSplit, "one DMA part per MFMA slot");
     for (int kt = 0; kt < KT; ++kt) {
       const bool prefetch = kt + 2 < KT;
-      auto mfma = [&](int i, int j) {
-        acc[i][j] = mfma_f8(fa[i], fb[j], acc[i][j]);
+      auto mfma = [&](int q) {
+        acc[q / FN][q % FN] = mfma_f8(fa[q / FN], fb[q % FN], acc[q / FN][q % FN]);
         __builtin_amdgcn_sched_barrier(0);
       };
       auto dma = [&](int part) {
@@ -231,8 +255,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_mfma_kernel(
       };
       // ---- phase 0 ----
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        mfma(q >> 2, q & 3);
+      for (int q = 0; q < kPhase0; ++q) {
+        mfma(q);
         if (q < kSplit) dma(q);
       }
       // ---- barrier for slice kt + 1 ----
@@ -249,12 +273,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_mfma_kernel(
         const char* Bs = b_lds(kt + 1);
         v8i na[FM], nb[FN];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          mfma(2 + (q >> 2), q & 3);
-          if (q < FM) {
-            na[q] = read_a(As, q);
-          } else {
-            nb[q - FM] = read_b(Bs, q - FM);
+        for (int q = 0; q < kPhase1; ++q) {
+          mfma(kPhase0 + q);
+#pragma unroll
+          for (int r = q * kReads / kPhase1; r < (q + 1) * kReads / kPhase1; ++r) {
+            if (r < FM)
+              na[r] = read_a(As, r);
+            else
+              nb[r - FM] = read_b(Bs, r - FM);
           }
           __builtin_amdgcn_sched_barrier(0);
           if (q < kFetchOps - kSplit) dma(kSplit + q);

@@ -116,45 +116,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
   // part's stride (BK bytes along k) and the stage offset.
   constexpr int kOpsA = rowk_ops<BM>();
   constexpr bool kFixedParts = !KTAIL && !kRegB;
-  const int8_t* part_src[kFetchOps];
-  uint32_t part_lds[kFetchOps];  // wave-uniform (m0 operand)
-  size_t part_stride[kFetchOps];
   const uint32_t lds_smem = lds_addr(smem);
+  using Parts = std::conditional_t<kFixedParts, FixedParts<MODE == kBnkDma ? kBnkDma : kBknDma>,
+                                   NoParts>;
+  Parts parts;
   if constexpr (kFixedParts) {
-    const int wave = t >> 6;
-#pragma unroll
-    for (int q = 0; q < kFetchOps; ++q) {
-      if (q < kOpsA) {
-        const int blk = wave * kOpsA + q;
-        const int row = blk * 8 + (lane >> 3);
-        const int lchunk = (lane & 7) ^ rowk_swz(row);
-        const uint32_t gr = static_cast<uint32_t>(min(m0 + row, M - 1));
-        part_src[q] = a + (gr * static_cast<uint32_t>(K) + 16 * lchunk);
-        part_lds[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(blk * 1024));
-        part_stride[q] = BK;
-      } else if constexpr (MODE == kBnkDma) {
-        const int blk = wave * rowk_ops<BN>() + (q - kOpsA);
-        const int row = blk * 8 + (lane >> 3);
-        const int lchunk = (lane & 7) ^ rowk_swz(row);
-        const uint32_t gr = static_cast<uint32_t>(min(n0 + row, N - 1));
-        part_src[q] = b + (gr * static_cast<uint32_t>(K) + 16 * lchunk);
-        part_lds[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(A_STAGE + blk * 1024));
-        part_stride[q] = BK;
-      } else {
-        const int blk = wave * kn_ops() + (q - kOpsA);
-        const int k = blk * 8 + (lane >> 3);
-        const int lchunk = (lane & 7) ^ kn_swz(k);
-        const uint32_t gn = static_cast<uint32_t>(min(n0 + 16 * lchunk, N - 16));
-        part_src[q] = b + (static_cast<uint32_t>(k) * static_cast<uint32_t>(N) + gn);
-        part_lds[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(A_STAGE + blk * 1024));
-        part_stride[q] = static_cast<size_t>(BK) * N;
-      }
-    }
+    static_assert(Parts::kOps == kFetchOps, "one DMA instruction per part");
+    parts.init(a, b, M, N, K, m0, n0);
   }
   auto fetch_part = [&](int s, int part) {
     if constexpr (kFixedParts) {
-      lds_dma16(part_src[part] + static_cast<size_t>(s) * part_stride[part],
-                lds_smem + static_cast<uint32_t>((s % kStages) * STAGE) + part_lds[part]);
+      parts.issue(lds_smem, s, part);
     } else if (part < kOpsA) {
       dma_rowk_one<BM>(a, a_lds(s), M, K, m0, s * BK, part);
     } else if constexpr (MODE == kBnkDma) {

@@ -88,6 +88,61 @@ __device__ __forceinline__ void dma_kn(const int8_t* __restrict__ b, char* lds, 
   for (int i = 0; i < kn_ops(); ++i) dma_kn_one(b, lds, N, K, n0, k0, i);
 }
 
+// Source addresses and LDS slots of one thread's DMA instructions of a k
+// slice (A parts first, then the weight's), formed once per kernel: slice s
+// adds s times the part's stride (BK bytes along k) and its stage offset.
+// Valid when no clamp changes from slice to slice: K a multiple of BK and a
+// DMA'd weight (MODE kBnkDma or kBknDma).
+template <int MODE>
+struct FixedParts {
+  static constexpr int kOpsA = rowk_ops<BM>();
+  static constexpr int kOps = kOpsA + (MODE == kBnkDma ? rowk_ops<BN>() : kn_ops());
+  const int8_t* src[kOps];
+  uint32_t lds[kOps];  // wave-uniform (m0 operand)
+  size_t stride[kOps];
+
+  __device__ __forceinline__ void init(const int8_t* __restrict__ a, const int8_t* __restrict__ b,
+                                       int M, int N, int K, int m0, int n0) {
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < kOps; ++q) {
+      if (q < kOpsA) {
+        const int blk = wave * kOpsA + q;
+        const int row = blk * 8 + (lane >> 3);
+        const int lchunk = (lane & 7) ^ rowk_swz(row);
+        const uint32_t gr = static_cast<uint32_t>(min(m0 + row, M - 1));
+        src[q] = a + (gr * static_cast<uint32_t>(K) + 16 * lchunk);
+        lds[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(blk * 1024));
+        stride[q] = BK;
+      } else if constexpr (MODE == kBnkDma) {
+        const int blk = wave * rowk_ops<BN>() + (q - kOpsA);
+        const int row = blk * 8 + (lane >> 3);
+        const int lchunk = (lane & 7) ^ rowk_swz(row);
+        const uint32_t gr = static_cast<uint32_t>(min(n0 + row, N - 1));
+        src[q] = b + (gr * static_cast<uint32_t>(K) + 16 * lchunk);
+        lds[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(A_STAGE + blk * 1024));
+        stride[q] = BK;
+      } else {
+        const int blk = wave * kn_ops() + (q - kOpsA);
+        const int k = blk * 8 + (lane >> 3);
+        const int lchunk = (lane & 7) ^ kn_swz(k);
+        const uint32_t gn = static_cast<uint32_t>(min(n0 + 16 * lchunk, N - 16));
+        src[q] = b + (static_cast<uint32_t>(k) * static_cast<uint32_t>(N) + gn);
+        lds[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(A_STAGE + blk * 1024));
+        stride[q] = static_cast<size_t>(BK) * N;
+      }
+    }
+  }
+  // DMA part `part` of slice s into its stage of the LDS ring at lds_smem
+  __device__ __forceinline__ void issue(uint32_t lds_smem, int s, int part) const {
+    lds_dma16(src[part] + static_cast<size_t>(s) * stride[part],
+              lds_smem + static_cast<uint32_t>((s % kStages) * STAGE) + lds[part]);
+  }
+};
+
+struct NoParts {};
+
 // ---- register-staged [K][N] weight (N not a multiple of 16) ----
 __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
                                              uint32_t& c0, uint32_t& c1, uint32_t& c2,
