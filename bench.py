@@ -38,9 +38,11 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA, published
 CSRC = os.path.join(ROOT, "w8a8_int8_quantized_qk_amd", "csrc")
 GEMM_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_mfma_prefill_outliers_traffic.txt"),
-                os.path.join(CSRC, "gemm_mfma.hip"))
+                [os.path.join(CSRC, f) for f in ("gemm_mfma.hip", "gemm_tile.h", "lds_dma.h")])
 GEMV_TRAFFIC = (os.path.join(ROOT, "profiles", "gemv_decode_m1_traffic.txt"),
-                os.path.join(CSRC, "gemv.hip"))
+                [os.path.join(CSRC, f) for f in ("gemv.hip", "quant_math.h", "lds_dma.h")])
+FP8_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_fp8_prefill_outliers_traffic.txt"),
+               [os.path.join(CSRC, f) for f in ("gemm_fp8.hip", "gemm_tile.h", "lds_dma.h")])
 
 
 def _args():
@@ -57,6 +59,7 @@ def _args():
                    help="target duration of the CPU oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-fp8", action="store_true", help="skip the FP8 layer at the prefill shape")
     p.add_argument("--no-other-configs", action="store_true",
                    help="skip the other workload shapes (8-row decode, gated down, MLP up)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -64,27 +67,30 @@ def _args():
     return p.parse_args()
 
 
-def _code_sha(path):
-    """SHA-256 prefix of a kernel source with comments and blank lines removed,
-    so that a comment edit does not orphan counter data taken on that code."""
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
-    code = "\n".join(ln for ln in lines if ln.strip())
-    return hashlib.sha256(code.encode()).hexdigest()[:16]
+def _code_sha(paths):
+    """SHA-256 prefix of a kernel's source files (concatenated in order) with
+    comments and blank lines removed, so that a comment edit does not orphan
+    counter data taken on that code."""
+    code = []
+    for path in paths:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
+        code.append("\n".join(ln for ln in lines if ln.strip()))
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def _traffic_from_profile(which):
     """Memory bytes per launch (L2 fetches + writes, scaled by a plain copy's
     counts) from the committed counter summary, if it was taken on the current
     kernel code (comments aside); else None."""
-    summary, src = which
+    summary, srcs = which
     if not os.path.exists(summary):
         return None
     text = open(summary).read()
     m = re.search(r"kernel_code_sha256_16:\s*([0-9a-f]{16})", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != _code_sha(src):
+    if not m or not t or m.group(1) != _code_sha(srcs):
         return None
     return float(t.group(1))
 
@@ -247,6 +253,48 @@ def main():
                          "traffic": _traffic_from_profile(GEMV_TRAFFIC)},
         }
 
+    # ---------------- the FP8 layer at the prefill shape ----------------
+    # per-token e4m3fn quantization + FP8 GEMM (binary32 accumulation): the
+    # same activations, e4m3fn weights
+    if not args.no_fp8:
+        fsets = []
+        for r in range(args.ring):
+            d = wl.generate(wcfg, seed=r, weight="fp8")
+            fsets.append({"x": d["x"].to(dev), "w": torch.from_numpy(d["w"]).to(dev).view(torch.float8_e4m3fn),
+                          "s_ch": torch.from_numpy(d["s_ch"]).to(dev),
+                          "q": torch.empty((m, k), dtype=torch.float8_e4m3fn, device=dev),
+                          "s": torch.empty((m,), dtype=torch.float32, device=dev),
+                          "out": torch.empty((m, n), dtype=torch.bfloat16, device=dev)})
+
+        def fquant(bs):
+            qk.quant_per_token_fp8(bs["x"], 0.0, bs["q"], bs["s"])
+
+        def fgemm(bs):
+            qk.gemm_fp8_scaled(bs["q"], bs["w"], bs["s"], bs["s_ch"], out=bs["out"])
+
+        fstep_ms, _ = timed_replays([(lambda bs=b: (fquant(bs), fgemm(bs))) for b in fsets], args.steps, args.warmup)
+        fgemm_ms, _ = timed_replays([(lambda bs=b: fgemm(bs)) for b in fsets], args.steps, args.warmup)
+        fquant_ms, _ = timed_replays([(lambda bs=b: fquant(bs)) for b in fsets], args.steps, args.warmup)
+        fops = 2.0 * m * n * k
+        ftf = fops / (fgemm_ms * 1e-3) / 1e12
+        result["fp8_prefill"] = {
+            "metric": "FP8 TFLOP/s (quant+GEMM) at M=2048,K=N=4096",
+            "workload": "prefill_outliers with e4m3fn weights", "m": m, "k": k, "n": n,
+            "x_dtype": "bf16", "w": "e4m3fn [K,N]", "out_dtype": "bf16",
+            "value": round(fops / (fstep_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(fstep_ms, 5),
+            "step": "qk_quant_per_token_fp8 + qk_gemm_fp8_scaled, replayed from HIP graphs",
+            "quant_kernel_us": round(fquant_ms * 1e3, 3),
+            "roofline": {"bound": "mfma", "kernel": "gemm_fp8_mfma_kernel",
+                         "achieved": round(ftf, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ftf / FP8_PEAK_TFLOPS, 4),
+                         "traffic": _traffic_from_profile(FP8_TRAFFIC),
+                         "avg_launch_us": round(fgemm_ms * 1e3, 3),
+                         "algorithmic_flops_per_launch": fops},
+        }
+        del fsets
+        torch.cuda.empty_cache()
+
     # ---------------- the other workload shapes (reported, not the metric) ----------------
     if not args.no_other_configs:
         others = {}
@@ -309,35 +357,6 @@ def main():
                             "gemm_frac_of_int8_peak": round(ops / (gemm_only_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
             del gsets
             torch.cuda.empty_cache()
-        # the FP8 layer at the prefill shape: per-token e4m3fn quantization +
-        # FP8 GEMM (binary32 accumulation), same activations, e4m3fn weights
-        fsets = []
-        for r in range(args.ring):
-            d = wl.generate(wcfg, seed=r, weight="fp8")
-            fsets.append({"x": d["x"].to(dev), "w": torch.from_numpy(d["w"]).to(dev).view(torch.float8_e4m3fn),
-                          "s_ch": torch.from_numpy(d["s_ch"]).to(dev),
-                          "q": torch.empty((m, k), dtype=torch.float8_e4m3fn, device=dev),
-                          "s": torch.empty((m,), dtype=torch.float32, device=dev),
-                          "out": torch.empty((m, n), dtype=torch.bfloat16, device=dev)})
-
-        def fquant(bs):
-            qk.quant_per_token_fp8(bs["x"], 0.0, bs["q"], bs["s"])
-
-        def fgemm(bs):
-            qk.gemm_fp8_scaled(bs["q"], bs["w"], bs["s"], bs["s_ch"], out=bs["out"])
-
-        fstep_ms, _ = timed_replays([(lambda bs=b: (fquant(bs), fgemm(bs))) for b in fsets], args.steps, args.warmup)
-        fgemm_ms, _ = timed_replays([(lambda bs=b: fgemm(bs)) for b in fsets], args.steps, args.warmup)
-        fops = 2.0 * m * n * k
-        others["fp8_prefill"] = {
-            "m": m, "k": k, "n": n, "x_dtype": "bf16", "w": "e4m3fn [K,N]", "out_dtype": "bf16",
-            "us_per_step": round(fstep_ms * 1e3, 2),
-            "step_tflops": round(fops / (fstep_ms * 1e-3) / 1e12, 1),
-            "gemm_us": round(fgemm_ms * 1e3, 2),
-            "gemm_tflops": round(fops / (fgemm_ms * 1e-3) / 1e12, 1),
-            "gemm_frac_of_fp8_peak": round(fops / (fgemm_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}
-        del fsets
-        torch.cuda.empty_cache()
         result["other_configs"] = others
 
     if args.copy_calibration:
