@@ -86,6 +86,10 @@ def _load():
     lib.or_quant_rows_fp8.restype = None
     lib.or_gemm_fp8.argtypes = [I64, I64, I64, P, P, ctypes.c_int, P]
     lib.or_gemm_fp8.restype = None
+    lib.or_gemm_i8_grouped.argtypes = [I64, I64, I64, I64, P, P, ctypes.c_int, P, P]
+    lib.or_gemm_i8_grouped.restype = None
+    lib.or_dequant_grouped.argtypes = [I64, I64, P, P, ctypes.c_float, P]
+    lib.or_dequant_grouped.restype = None
     _lib = lib
     return lib
 
@@ -317,3 +321,37 @@ def quantize_input_fp8(x_bits: np.ndarray, dtype: int, scale_ub: float = 0.0):
 def silu_mul_quantize_fp8(h_bits: np.ndarray, dtype: int, scale_ub: float = 0.0):
     """silu(gate) * up, then per-token e4m3fn quantization: (codes, scales)."""
     return quant_per_token_fp8(silu_mul(widen(h_bits, dtype)), scale_ub)
+
+
+# --------------------------------------------------------------------------
+# Per-group weight scales: "KV-cache kernels", 02 Scales and dequantization
+# and 03 Where scales come from (one scale per group of 64-128 channels),
+# with the groups along the reduction dimension k.
+# --------------------------------------------------------------------------
+
+def gemm_i8_grouped(a: np.ndarray, b: np.ndarray, scale_b: np.ndarray, group: int,
+                    layout: int = B_KN) -> np.ndarray:
+    """sum over k-groups g of scale_b[g, col] * (exact integer partial of group g),
+    float64 [m, n]; scale_b is [ceil(k / group), n] float32."""
+    lib = _load()
+    aa = _contig(a, np.int8)
+    bb = _contig(b, np.int8)
+    m, k = aa.shape
+    n = bb.shape[1] if layout == B_KN else bb.shape[0]
+    sb = _contig(scale_b, np.float32)
+    if group < 1 or sb.shape != ((k + group - 1) // group, n):
+        raise ValueError("scale_b must be [ceil(k / group), n]")
+    acc = np.empty((m, n), dtype=np.float64)
+    lib.or_gemm_i8_grouped(m, n, k, group, _ptr(aa), _ptr(bb), layout, _ptr(sb), _ptr(acc))
+    return acc
+
+
+def dequant_grouped(acc: np.ndarray, scale_a: np.ndarray, output_scale: float = 1.0) -> np.ndarray:
+    """acc * scale_a[row] * output_scale in float64."""
+    lib = _load()
+    ac = _contig(acc, np.float64)
+    sa = _contig(scale_a, np.float32)
+    m, n = ac.shape
+    out = np.empty((m, n), dtype=np.float64)
+    lib.or_dequant_grouped(m, n, _ptr(ac), _ptr(sa), float(output_scale), _ptr(out))
+    return out

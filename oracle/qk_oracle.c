@@ -22,6 +22,11 @@
  *   [DAY25]    "KV-cache kernels" (a quantization lesson), 02 Scales and
  *              dequantization -- int8 dot products accumulate in int32 and
  *              the result is multiplied by the activation and weight scales.
+ *   [DAY25-G]  the same lesson, 02 Scales and dequantization and 03 Where
+ *              scales come from -- one weight scale per small group of
+ *              channels (every 64-128), applied after the load; here the
+ *              groups run along the reduction dimension k, so a group's
+ *              integer partial sum is scaled before the groups are added.
  *   [PR]       "kernels: fused silu_and_mul + dynamic per-token FP8
  *              quantization", Purpose and Algorithm -- one scale per token
  *              from the row absmax, scale = max(absmax, 1e-12) / qmax, the
@@ -423,4 +428,42 @@ void or_gemm_fp8(int64_t m, int64_t n, int64_t k, const uint8_t *a, const uint8_
             }
         }
     }
+}
+
+/* ------------------------------------------------------------------ */
+/* Per-group weight scales [DAY25-G]                                   */
+/* ------------------------------------------------------------------ */
+
+/* acc[i][j] = sum over groups g of scale_b[g][j] * P_g[i][j], where
+ * P_g[i][j] = sum of a[i][t] * B(t, j) over t in [g * group, (g + 1) * group)
+ * (the last group ends at k), an exact integer; scale_b is [ceil(k / group)][n].
+ * Each product P_g * scale is exact in binary64 (|P_g| < 2^31, a binary32
+ * scale has 24 significant bits); the sum over groups is binary64. */
+void or_gemm_i8_grouped(int64_t m, int64_t n, int64_t k, int64_t group, const int8_t *a,
+                        const int8_t *b, int layout, const float *scale_b, double *acc)
+{
+    const int64_t groups = (k + group - 1) / group;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t j = 0; j < n; ++j) {
+            double sum = 0.0;
+            for (int64_t g = 0; g < groups; ++g) {
+                int64_t partial = 0;
+                const int64_t end = (g + 1) * group < k ? (g + 1) * group : k;
+                for (int64_t kk = g * group; kk < end; ++kk)
+                    partial += (int64_t)a[i * k + kk] * (int64_t)weight_at(b, layout, n, k, kk, j);
+                sum += (double)partial * (double)scale_b[g * n + j];
+            }
+            acc[i * n + j] = sum;
+        }
+    }
+}
+
+/* out[i][j] = acc[i][j] * scale_a[i] * output_scale in binary64 */
+void or_dequant_grouped(int64_t m, int64_t n, const double *acc, const float *scale_a,
+                        float output_scale, double *out)
+{
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j)
+            out[i * n + j] = acc[i * n + j] * (double)scale_a[i] * (double)output_scale;
 }
