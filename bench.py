@@ -42,7 +42,9 @@ GEMM_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_mfma_prefill_outliers_traff
 GEMV_TRAFFIC = (os.path.join(ROOT, "profiles", "gemv_decode_m1_traffic.txt"),
                 [os.path.join(CSRC, f) for f in ("gemv.hip", "quant_math.h", "lds_dma.h")])
 FP8_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_fp8_prefill_outliers_traffic.txt"),
-               [os.path.join(CSRC, f) for f in ("gemm_fp8.hip", "gemm_tile.h", "lds_dma.h")])
+               [os.path.join(CSRC, f) for f in ("gemm_slice.hip", "gemm_tile.h", "lds_dma.h")])
+GROUPED_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_grouped128_prefill_outliers_traffic.txt"),
+                   [os.path.join(CSRC, f) for f in ("gemm_slice.hip", "gemm_tile.h", "lds_dma.h")])
 
 
 def _args():
@@ -60,6 +62,8 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8 layer at the prefill shape")
+    p.add_argument("--no-grouped", action="store_true",
+                   help="skip the INT8 GEMM with per-group weight scales at the prefill shape")
     p.add_argument("--no-other-configs", action="store_true",
                    help="skip the other workload shapes (8-row decode, gated down, MLP up)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -293,6 +297,50 @@ def main():
                          "algorithmic_flops_per_launch": fops},
         }
         del fsets
+        torch.cuda.empty_cache()
+
+    # ---------------- INT8 with per-group weight scales at the prefill shape ----------------
+    # per-token INT8 quantization + the GEMM whose weight carries one scale per
+    # group of 128 (and 64) consecutive k of each column
+    if not args.no_grouped:
+        gsets = []
+        for r in range(args.ring):
+            d = wl.generate(wcfg, seed=r)
+            grng = np.random.default_rng(1000 + r)
+            gsets.append({"x": d["x"].to(dev), "w": torch.from_numpy(d["w"]).to(dev),
+                          "sg128": torch.from_numpy(wl.random_group_scales(grng, k // 128, n)).to(dev),
+                          "sg64": torch.from_numpy(wl.random_group_scales(grng, k // 64, n)).to(dev),
+                          "q": torch.empty((m, k), dtype=torch.int8, device=dev),
+                          "s": torch.empty((m,), dtype=torch.float32, device=dev),
+                          "out": torch.empty((m, n), dtype=torch.bfloat16, device=dev)})
+        grouped = {}
+        for group in (128, 64):
+            def ggemm(bs, group=group):
+                qk.gemm_i8_grouped(bs["q"], bs["w"], bs["s"], bs[f"sg{group}"], group, out=bs["out"])
+
+            def gstep(bs, group=group):
+                qk.quant_per_token(bs["x"], bs["q"], bs["s"])
+                ggemm(bs, group)
+
+            gstep_ms, _ = timed_replays([(lambda bs=b: gstep(bs)) for b in gsets], args.steps, args.warmup)
+            ggemm_ms, _ = timed_replays([(lambda bs=b: ggemm(bs)) for b in gsets], args.steps, args.warmup)
+            gops = 2.0 * m * n * k
+            gt = gops / (ggemm_ms * 1e-3) / 1e12
+            grouped[f"group_{group}"] = {
+                "value": round(gops / (gstep_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
+                "ms_per_step": round(gstep_ms, 5),
+                "roofline": {"bound": "mfma", "kernel": f"gemm_slice_kernel (INT8, groups of {group})",
+                             "achieved": round(gt, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                             "frac": round(gt / INT8_PEAK_TOPS, 4),
+                             "traffic": _traffic_from_profile(GROUPED_TRAFFIC) if group == 128 else None,
+                             "avg_launch_us": round(ggemm_ms * 1e3, 3),
+                             "algorithmic_ops_per_launch": gops,
+                             "valu_wave_instructions_per_launch": 2 * m * n * (k // group) // 64}}
+        result["grouped_prefill"] = {
+            "metric": "INT8 TOPS (quant+GEMM) with per-group weight scales at M=2048,K=N=4096",
+            "workload": "prefill_outliers with group scales [K/G, N]", "m": m, "k": k, "n": n,
+            "step": "qk_quant_per_token + qk_gemm_i8_grouped, replayed from HIP graphs", **grouped}
+        del gsets
         torch.cuda.empty_cache()
 
     # ---------------- the other workload shapes (reported, not the metric) ----------------

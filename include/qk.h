@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QK_ABI_VERSION 2
+#define QK_ABI_VERSION 3
 
 /* element types */
 #define QK_F32 0
@@ -265,6 +265,33 @@ int qk_linear_fp8(int m, int n, int k, const void *x, int x_dtype, float scale_u
                   const uint8_t *b, const float *scale_b, float output_scale, void *out,
                   int out_dtype, int b_layout, uint8_t *q_out, float *scale_out,
                   hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
+/* INT8 GEMM with per-group weight scales                              */
+/* ------------------------------------------------------------------ */
+/*
+ * The weight carries one scale per group of `group` consecutive k of each
+ * output column ("KV-cache kernels", 02 Scales and dequantization and 03
+ * Where scales come from: one scale per group of 64-128 channels, the
+ * accuracy lever against outlier channels), so the scale applies to each
+ * group's integer partial sum before the groups are added:
+ *   P_g[i][j] = sum_{t in group g} a[i][t] * B(t, j)          (exact, INT32)
+ *   acc[i][j] = sum_g scale_b[g][j] * P_g[i][j]               (binary32:
+ *               each P_g converted exactly, one fused multiply-add per group)
+ *   c[i][j]   = acc                                 (if c != NULL; binary32)
+ *   out[i][j] = (acc * scale_a[i]) * output_scale   (if out != NULL; fp32 or
+ *               bf16 rounded to nearest even)
+ *   a [m][k] int8; b [k][n] (QK_B_KN) or [n][k] (QK_B_NK) int8;
+ *   scale_b [k / group][n] float (n contiguous); scale_a [m] float (NULL
+ *   only when out is NULL); c [m][n] float or NULL; out [m][n] of out_dtype
+ *   or NULL (not both NULL).
+ * Requirements: group 64 or 128 and k a multiple of it, k <= QK_MAX_K, a and
+ * b 16-byte aligned, m*k and n*k below 2^32 (QK_ERR_UNSUPPORTED otherwise).
+ * No workspace.
+ */
+int qk_gemm_i8_grouped(int m, int n, int k, int group, const int8_t *a, const int8_t *b, float *c,
+                       const float *scale_a, const float *scale_b, float output_scale, void *out,
+                       int out_dtype, int b_layout, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -211,3 +211,21 @@ def test_fp8_binding_rejects_wrong_dtypes():
     with pytest.raises(ValueError, match="GPU"):
         qk.gemm_fp8_scaled(torch.zeros(2, 16, dtype=torch.float8_e4m3fn),
                            torch.zeros(16, 4, dtype=torch.float8_e4m3fn), out_dtype=None)
+
+
+def test_grouped_argument_errors_are_reported_before_launch(lib):
+    c = _header_constants()
+    INVALID, UNSUP = c["QK_ERR_INVALID_VALUE"], c["QK_ERR_UNSUPPORTED"]
+
+    def gg(m, n, k, group=128, a=FAKE, b=FAKE, cc=FAKE, sa=FAKE, sb=FAKE, out=FAKE, odt=0, layout=0):
+        return lib.qk_gemm_i8_grouped(m, n, k, group, a, b, cc, sa, sb, 1.0, out, odt, layout, NULL)
+
+    assert gg(-1, 4, 128) == INVALID
+    assert gg(4, 4, 256, group=32) == UNSUP      # groups of 64 or 128 only
+    assert gg(4, 4, 192, group=128) == UNSUP     # k a multiple of the group
+    assert gg(4, 4, 128, sb=NULL) == INVALID
+    assert gg(4, 4, 128, sa=NULL) == INVALID     # out needs the token scales
+    assert gg(4, 4, 128, cc=NULL, out=NULL) == INVALID
+    assert gg(4, 4, 128, layout=5) == INVALID
+    assert gg(4, 4, 128, a=FAKE_ODD) == UNSUP
+    assert gg(0, 4, 128, a=NULL, b=NULL) == 0

@@ -24,7 +24,7 @@ import threading
 
 import torch
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 F32, BF16, F16 = 0, 1, 2
 B_KN, B_NK = 0, 1
 KERNEL_AUTO, KERNEL_MFMA, KERNEL_GEMV = 0, 1, 2
@@ -43,6 +43,7 @@ EXPORTED = (
     "qk_silu_mul_quant_per_token", "qk_gemm_workspace_size", "qk_gemm_i8_scaled",
     "qk_gemm_i8_scaled_ex", "qk_linear_w8a8", "qk_quant_per_token_fp8",
     "qk_silu_mul_quant_per_token_fp8", "qk_gemm_fp8_scaled", "qk_linear_fp8",
+    "qk_gemm_i8_grouped",
 )
 
 
@@ -87,6 +88,8 @@ def _declare(lib):
     lib.qk_gemm_fp8_scaled.restype = I
     lib.qk_linear_fp8.argtypes = [I, I, I, P, I, F, P, P, F, P, I, I, P, P, P]
     lib.qk_linear_fp8.restype = I
+    lib.qk_gemm_i8_grouped.argtypes = [I, I, I, I, P, P, P, P, P, F, P, I, I, P]
+    lib.qk_gemm_i8_grouped.restype = I
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -451,3 +454,56 @@ def gated_linear_fp8(h: torch.Tensor, w: torch.Tensor, s_ch: torch.Tensor, scale
     """silu(gate) * up with per-token FP8 quantization, then the FP8 GEMM."""
     q, s = silu_mul_quant_per_token_fp8(h, scale_ub)
     return gemm_fp8_scaled(q, w, s, s_ch, output_scale, out_dtype, b_layout)
+
+
+# ---- INT8 GEMM with per-group weight scales ----
+
+def gemm_i8_grouped(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor | None,
+                    scale_b: torch.Tensor, group: int, output_scale: float = 1.0,
+                    out_dtype: torch.dtype | None = torch.bfloat16, b_layout: str = "kn",
+                    return_acc: bool = False, out: torch.Tensor | None = None,
+                    c: torch.Tensor | None = None):
+    """INT8 GEMM whose weight carries one scale per group of `group` (64 or
+    128) consecutive k of each output column.
+
+    a [m, k] int8; b [k, n] ("kn") or [n, k] ("nk") int8; scale_a [m] fp32;
+    scale_b [k / group, n] fp32.  acc = sum_g scale_b[g] * (INT32 partial of
+    group g) in binary32; out = acc * scale_a * output_scale.  Returns out,
+    (out, c) with the binary32 accumulators when return_acc, or c alone when
+    out_dtype is None.
+    """
+    _need(a, "a", torch.int8, 2)
+    dev = a.device
+    _need(b, "b", torch.int8, 2, dev)
+    layout = _LAYOUTS[b_layout]
+    m, k = a.shape
+    n, kb = (b.shape[1], b.shape[0]) if layout == B_KN else (b.shape[0], b.shape[1])
+    if kb != k:
+        raise ValueError(f"inner dimensions differ: a has k={k}, b has {kb}")
+    _need(scale_b, "scale_b", torch.float32, 2, dev)
+    if group <= 0 or k % group or tuple(scale_b.shape) != (k // group, n):
+        raise ValueError("scale_b must be [k / group, n] with k a multiple of group")
+    want_out = out is not None or out_dtype is not None
+    if want_out:
+        out_dtype = out.dtype if out is not None else out_dtype
+        if out_dtype not in _OUT_DTYPES:
+            raise TypeError(f"out dtype {out_dtype} not supported")
+        if out is None:
+            out = torch.empty((m, n), dtype=out_dtype, device=dev)
+        _need(out, "out", out_dtype, 2, dev)
+        _need(scale_a, "scale_a", torch.float32, 1, dev)
+        if scale_a.shape[0] != m or tuple(out.shape) != (m, n):
+            raise ValueError("scale_a must be [m], out [m, n]")
+    if return_acc or not want_out:
+        if c is None:
+            c = torch.empty((m, n), dtype=torch.float32, device=dev)
+        _need(c, "c", torch.float32, 2, dev)
+    else:
+        c = None
+    _check(library().qk_gemm_i8_grouped(
+        m, n, k, int(group), _ptr(a), _ptr(b), _ptr(c), _ptr(scale_a if want_out else None),
+        _ptr(scale_b), float(output_scale), _ptr(out if want_out else None),
+        _OUT_DTYPES[out_dtype] if want_out else F32, layout, _stream(dev)))
+    if not want_out:
+        return c
+    return (out, c) if return_acc else out

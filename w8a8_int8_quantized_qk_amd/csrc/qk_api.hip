@@ -210,7 +210,8 @@ int qk_gemm_fp8_scaled(int m, int n, int k, const uint8_t* a, const uint8_t* b, 
   if (c && !aligned(c, 4)) return QK_ERR_UNSUPPORTED;
   if (out && !aligned(out, out_dtype == QK_BF16 ? 2 : 4)) return QK_ERR_UNSUPPORTED;
   if (!qk::gemm_mfma_supported(m, n, k)) return QK_ERR_UNSUPPORTED;
-  qk::GemmFp8Args g{m, n, k, a, b, c, scale_a, scale_b, output_scale, out, out_dtype, b_layout};
+  qk::SliceGemmArgs g{m, n, k, reinterpret_cast<const int8_t*>(a), reinterpret_cast<const int8_t*>(b),
+                      c, scale_a, scale_b, output_scale, out, out_dtype, b_layout};
   return status_of(qk::launch_gemm_fp8(g, stream));
 }
 
@@ -233,9 +234,31 @@ int qk_linear_fp8(int m, int n, int k, const void* x, int x_dtype, float scale_u
   if (!qk::gemm_mfma_supported(m, n, k)) return QK_ERR_UNSUPPORTED;
   hipError_t e = qk::launch_quant_rows_fp8(m, k, x, x_dtype, q_out, scale_out, scale_ub, stream);
   if (e != hipSuccess) return status_of(e);
-  qk::GemmFp8Args g{m, n, k, q_out, b, nullptr, scale_out, scale_b, output_scale, out, out_dtype,
-                    b_layout};
+  qk::SliceGemmArgs g{m, n, k, reinterpret_cast<const int8_t*>(q_out),
+                      reinterpret_cast<const int8_t*>(b), nullptr, scale_out, scale_b, output_scale,
+                      out, out_dtype, b_layout};
   return status_of(qk::launch_gemm_fp8(g, stream));
+}
+
+int qk_gemm_i8_grouped(int m, int n, int k, int group, const int8_t* a, const int8_t* b, float* c,
+                       const float* scale_a, const float* scale_b, float output_scale, void* out,
+                       int out_dtype, int b_layout, hipStream_t stream) {
+  if (m < 0 || n < 0 || k < 0 || k > QK_MAX_K) return QK_ERR_INVALID_VALUE;
+  if (b_layout != QK_B_KN && b_layout != QK_B_NK) return QK_ERR_INVALID_VALUE;
+  if (group != 64 && group != 128) return QK_ERR_UNSUPPORTED;
+  if (k % group != 0) return QK_ERR_UNSUPPORTED;
+  if (m == 0 || n == 0) return QK_OK;
+  if (!c && !out) return QK_ERR_INVALID_VALUE;
+  if (out && out_dtype != QK_F32 && out_dtype != QK_BF16) return QK_ERR_INVALID_VALUE;
+  if (k > 0 && (!a || !b || !scale_b)) return QK_ERR_INVALID_VALUE;
+  if (out && !scale_a) return QK_ERR_INVALID_VALUE;
+  if (!aligned(a, 16) || !aligned(b, 16) || (scale_b && !aligned(scale_b, 4)))
+    return QK_ERR_UNSUPPORTED;
+  if (c && !aligned(c, 4)) return QK_ERR_UNSUPPORTED;
+  if (out && !aligned(out, out_dtype == QK_BF16 ? 2 : 4)) return QK_ERR_UNSUPPORTED;
+  if (!qk::gemm_mfma_supported(m, n, k)) return QK_ERR_UNSUPPORTED;
+  qk::SliceGemmArgs g{m, n, k, a, b, c, scale_a, scale_b, output_scale, out, out_dtype, b_layout};
+  return status_of(qk::launch_gemm_i8_grouped(g, group, stream));
 }
 
 }  // extern "C"

@@ -62,21 +62,25 @@ hipError_t launch_silu_quant_rows_fp8(int m, int d, const void* h, int dtype, ui
 bool gemm_mfma_supported(int m, int n, int k);
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
 
-// FP8 (e4m3fn) MFMA GEMM with binary32 accumulation and the fused epilogue
-// (gemm_fp8.hip); the same tiles, layouts and size limits as the INT8 one.
-struct GemmFp8Args {
+// GEMMs whose waves multiply whole k slices (gemm_slice.hip): the FP8
+// (e4m3fn) GEMM and the INT8 GEMM with per-group weight scales, both with
+// binary32 accumulation and the fused epilogue; the same tiles, layouts and
+// size limits as the INT8 GEMM.
+struct SliceGemmArgs {
   int m, n, k;
-  const uint8_t* a;  // e4m3fn codes [m][k]
-  const uint8_t* b;  // e4m3fn codes [k][n] or [n][k]
-  float* c;          // raw binary32 accumulators [m][n] or nullptr
+  const int8_t* a;  // [m][k] codes (e4m3fn bytes or int8)
+  const int8_t* b;  // [k][n] or [n][k] codes
+  float* c;         // raw binary32 accumulators [m][n] or nullptr
   const float* scale_a;
-  const float* scale_b;
+  const float* scale_b;  // FP8: [n]; grouped INT8: [k / group][n]
   float output_scale;
   void* out;
   int out_dtype;  // QK_F32 | QK_BF16 (ignored when out == nullptr)
   int b_layout;   // QK_B_KN | QK_B_NK
 };
-hipError_t launch_gemm_fp8(const GemmFp8Args& g, hipStream_t stream);
+hipError_t launch_gemm_fp8(const SliceGemmArgs& g, hipStream_t stream);
+// group 64 or 128; k a multiple of group
+hipError_t launch_gemm_i8_grouped(const SliceGemmArgs& g, int group, hipStream_t stream);
 
 // Split-K decode GEMV (gemv.hip): m <= kGemvMaxRows rows per launch, larger m
 // in row groups; exact partial sums with arrival counts in a self-cleaning

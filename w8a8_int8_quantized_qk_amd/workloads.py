@@ -21,7 +21,8 @@ is multiplied by 50 in float32; X is cast to bf16/fp16 by round-to-nearest-
 even (torch); W is uniform on the integers [-127, 127]; the per-channel
 scales are uniform on [1e-3, 1e-2] in float32.  The gated workload draws H in
 place of X.  For the FP8 layer the weight is drawn instead as N(0, 1) x 100,
-clipped to +-448 and cast to float8_e4m3fn by torch.  These shapes and
+clipped to +-448 and cast to float8_e4m3fn by torch; per-group weight scales
+are uniform on [1e-3, 1e-2] like the per-channel ones.  These shapes and
 distributions follow the workloads the pages describe (decode GEMV vs prefill
 GEMM, outlier channels, fused gated MLP).
 """
@@ -104,6 +105,11 @@ def random_weight_fp8(rng: np.random.Generator, k: int, n: int) -> np.ndarray:
 
 def random_channel_scales(rng: np.random.Generator, n: int) -> np.ndarray:
     return rng.uniform(1e-3, 1e-2, n).astype(np.float32)
+
+
+def random_group_scales(rng: np.random.Generator, groups: int, n: int) -> np.ndarray:
+    """Per-group weight scales [groups, n], uniform on [1e-3, 1e-2] in float32."""
+    return rng.uniform(1e-3, 1e-2, (groups, n)).astype(np.float32)
 
 
 def generate(name_or_workload, seed: int = 0, weight: str = "i8") -> dict:
