@@ -355,3 +355,43 @@ def dequant_grouped(acc: np.ndarray, scale_a: np.ndarray, output_scale: float = 
     out = np.empty((m, n), dtype=np.float64)
     lib.or_dequant_grouped(m, n, _ptr(ac), _ptr(sa), float(output_scale), _ptr(out))
     return out
+
+
+# --------------------------------------------------------------------------
+# MoE grouped GEMM ("dynquant-kernels", What is in here: one launch for all
+# experts): the rows of a are grouped by expert, rows [offsets[e],
+# offsets[e + 1]) going to expert e's weight and per-channel scales.  The
+# oracle is the per-expert GEMM of this module applied expert by expert.
+# --------------------------------------------------------------------------
+
+def _check_offsets(offsets: np.ndarray, experts: int, m_total: int) -> np.ndarray:
+    off = np.asarray(offsets, dtype=np.int64)
+    if off.shape != (experts + 1,) or off[0] != 0 or off[-1] != m_total or np.any(np.diff(off) < 0):
+        raise ValueError("offsets must be [experts + 1], nondecreasing, from 0 to the row count")
+    return off
+
+
+def moe_gemm_i32(a: np.ndarray, w: np.ndarray, offsets: np.ndarray, layout: int = B_KN) -> np.ndarray:
+    """Exact int32 accumulators: rows of expert e times w[e] ([k, n] if B_KN, [n, k] if B_NK)."""
+    experts = w.shape[0]
+    off = _check_offsets(offsets, experts, a.shape[0])
+    n = w.shape[2] if layout == B_KN else w.shape[1]
+    c = np.zeros((a.shape[0], n), dtype=np.int32)
+    for e in range(experts):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 > r0:
+            c[r0:r1] = gemm_i32(a[r0:r1], w[e], layout)
+    return c
+
+
+def moe_dequant(c: np.ndarray, scale_a: np.ndarray, scale_b: np.ndarray, offsets: np.ndarray,
+                output_scale: float = 1.0) -> np.ndarray:
+    """acc * scale_a[row] * scale_b[expert of row, col] * output_scale in float64."""
+    experts = scale_b.shape[0]
+    off = _check_offsets(offsets, experts, c.shape[0])
+    out = np.zeros(c.shape, dtype=np.float64)
+    for e in range(experts):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 > r0:
+            out[r0:r1] = dequant(c[r0:r1], scale_a[r0:r1], scale_b[e], output_scale)
+    return out
