@@ -62,6 +62,7 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8 layer at the prefill shape")
+    p.add_argument("--no-moe", action="store_true", help="skip the MoE grouped GEMM")
     p.add_argument("--no-grouped", action="store_true",
                    help="skip the INT8 GEMM with per-group weight scales at the prefill shape")
     p.add_argument("--no-other-configs", action="store_true",
@@ -341,6 +342,58 @@ def main():
             "workload": "prefill_outliers with group scales [K/G, N]", "m": m, "k": k, "n": n,
             "step": "qk_quant_per_token + qk_gemm_i8_grouped, replayed from HIP graphs", **grouped}
         del gsets
+        torch.cuda.empty_cache()
+
+    # ---------------- MoE grouped GEMM: all experts in one launch ----------------
+    if not args.no_moe:
+        msets = []
+        for r in range(2):  # the weights (470 MB per set) exceed the Infinity Cache already
+            d = wl.generate_moe(seed=r)
+            msets.append({"x": d["x"].to(dev), "w": torch.from_numpy(d["w"]).to(dev),
+                          "s_ch": torch.from_numpy(d["s_ch"]).to(dev),
+                          "off": torch.from_numpy(d["offsets"]).to(dev), "off_host": d["offsets"],
+                          "q": torch.empty((d["rows"], d["k"]), dtype=torch.int8, device=dev),
+                          "s": torch.empty((d["rows"],), dtype=torch.float32, device=dev),
+                          "out": torch.empty((d["rows"], d["n"]), dtype=torch.bfloat16, device=dev)})
+        mrows, mk, mn, mexp = d["rows"], d["k"], d["n"], d["experts"]
+        del d
+
+        def mgemm(bs):
+            qk.moe_gemm_i8_scaled(bs["q"], bs["w"], bs["off"], bs["s"], bs["s_ch"], out=bs["out"])
+
+        def mstep(bs):
+            qk.quant_per_token(bs["x"], bs["q"], bs["s"])
+            mgemm(bs)
+
+        def per_expert(bs):  # the same work as one GEMM launch per expert
+            o = bs["off_host"]
+            for e in range(mexp):
+                r0, r1 = int(o[e]), int(o[e + 1])
+                if r1 > r0:
+                    qk.gemm_i8_scaled(bs["q"][r0:r1], bs["w"][e], bs["s"][r0:r1], bs["s_ch"][e],
+                                      out=bs["out"][r0:r1], kernel="mfma")
+
+        msteps = max(4, args.steps // 10)
+        mstep_ms, _ = timed_replays([(lambda bs=b: mstep(bs)) for b in msets], msteps, 2)
+        mgemm_ms, _ = timed_replays([(lambda bs=b: mgemm(bs)) for b in msets], msteps, 2)
+        mper_ms, _ = timed_replays([(lambda bs=b: per_expert(bs)) for b in msets], msteps, 2)
+        mops = 2.0 * mrows * mn * mk
+        mt = mops / (mgemm_ms * 1e-3) / 1e12
+        result["moe_up"] = {
+            "metric": "INT8 TOPS (quant+MoE GEMM), 8 experts, 2048 tokens x top-2, 4096 -> 14336",
+            "experts": mexp, "rows": mrows, "k": mk, "n": mn,
+            "rows_per_expert": [int(x) for x in np.diff(msets[0]["off_host"])],
+            "value": round(mops / (mstep_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
+            "ms_per_step": round(mstep_ms, 5),
+            "step": "qk_quant_per_token + qk_moe_gemm_i8_scaled (one launch for all experts)",
+            "one_launch_per_expert_us": round(mper_ms * 1e3, 2),
+            "roofline": {"bound": "mfma", "kernel": "gemm_i8_moe_kernel",
+                         "achieved": round(mt, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                         "frac": round(mt / INT8_PEAK_TOPS, 4), "traffic": None,
+                         "avg_launch_us": round(mgemm_ms * 1e3, 3),
+                         "algorithmic_ops_per_launch": mops},
+        }
+        del msets
         torch.cuda.empty_cache()
 
     # ---------------- the other workload shapes (reported, not the metric) ----------------

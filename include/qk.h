@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QK_ABI_VERSION 3
+#define QK_ABI_VERSION 4
 
 /* element types */
 #define QK_F32 0
@@ -292,6 +292,40 @@ int qk_linear_fp8(int m, int n, int k, const void *x, int x_dtype, float scale_u
 int qk_gemm_i8_grouped(int m, int n, int k, int group, const int8_t *a, const int8_t *b, float *c,
                        const float *scale_a, const float *scale_b, float output_scale, void *out,
                        int out_dtype, int b_layout, hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
+/* MoE grouped GEMM                                                     */
+/* ------------------------------------------------------------------ */
+/* Largest expert count of one qk_moe_gemm_i8_scaled call. */
+#define QK_MOE_MAX_EXPERTS 256
+
+/*
+ * The INT8 GEMM and dequant epilogue for all experts of a mixture-of-experts
+ * layer in one launch ("dynquant-kernels", What is in here: MoE grouped GEMM,
+ * one launch for all experts, not one per expert):
+ *   rows [expert_offsets[e], expert_offsets[e + 1]) of a are expert e's;
+ *   for each such row i:  acc[i][j] = sum_t a[i][t] * B_e(t, j)   (exact, INT32)
+ *                         out[i][j] = ((float)acc * scale_a[i]) *
+ *                                     (scale_b[e][j] * output_scale)
+ *   c[i][j] = acc (if c != NULL).
+ *   expert_offsets  DEVICE array of experts + 1 int, nondecreasing, [0] = 0,
+ *                   [experts] = m (the routing's row counts as prefix sums).
+ *                   Values are clamped to [0, m] inside the kernel: invalid
+ *                   offsets give unspecified results but no access out of
+ *                   bounds.  Rows outside every expert's range are not written.
+ *   a        [m][k] int8 codes, rows grouped by expert.
+ *   b        [experts][k][n] (QK_B_KN) or [experts][n][k] (QK_B_NK) int8.
+ *   scale_a  [m] float;  scale_b [experts][n] float (both may be NULL only
+ *            when out is NULL).
+ *   c        [m][n] int32 or NULL;  out [m][n] of out_dtype or NULL (not both).
+ * Requirements: 1 <= experts <= QK_MOE_MAX_EXPERTS, k % 16 == 0, a and b
+ * 16-byte aligned, m*k and n*k below 2^32.  No workspace; the grid is
+ * sized from m and experts, so the call needs no host copy of the offsets.
+ */
+int qk_moe_gemm_i8_scaled(int experts, int m, int n, int k, const int *expert_offsets,
+                          const int8_t *a, const int8_t *b, int32_t *c, const float *scale_a,
+                          const float *scale_b, float output_scale, void *out, int out_dtype,
+                          int b_layout, hipStream_t stream);
 
 #ifdef __cplusplus
 }

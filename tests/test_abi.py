@@ -229,3 +229,22 @@ def test_grouped_argument_errors_are_reported_before_launch(lib):
     assert gg(4, 4, 128, layout=5) == INVALID
     assert gg(4, 4, 128, a=FAKE_ODD) == UNSUP
     assert gg(0, 4, 128, a=NULL, b=NULL) == 0
+
+
+def test_moe_argument_errors_are_reported_before_launch(lib):
+    c = _header_constants()
+    INVALID, UNSUP = c["QK_ERR_INVALID_VALUE"], c["QK_ERR_UNSUPPORTED"]
+    assert c["QK_MOE_MAX_EXPERTS"] == qk.MOE_MAX_EXPERTS
+
+    def mm(e, m, n, k, off=FAKE, a=FAKE, b=FAKE, cc=FAKE, sa=FAKE, sb=FAKE, out=FAKE, odt=0, layout=0):
+        return lib.qk_moe_gemm_i8_scaled(e, m, n, k, off, a, b, cc, sa, sb, 1.0, out, odt, layout, NULL)
+
+    assert mm(0, 4, 4, 16) == INVALID
+    assert mm(qk.MOE_MAX_EXPERTS + 1, 4, 4, 16) == INVALID
+    assert mm(2, -1, 4, 16) == INVALID
+    assert mm(2, 4, 4, 24) == UNSUP
+    assert mm(2, 4, 4, 16, off=NULL) == INVALID
+    assert mm(2, 4, 4, 16, sb=NULL) == INVALID
+    assert mm(2, 4, 4, 16, cc=NULL, out=NULL) == INVALID
+    assert mm(2, 4, 4, 16, b=FAKE_ODD) == UNSUP
+    assert mm(2, 0, 4, 16, off=NULL, a=NULL) == 0

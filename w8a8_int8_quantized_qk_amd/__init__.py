@@ -24,7 +24,7 @@ import threading
 
 import torch
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 F32, BF16, F16 = 0, 1, 2
 B_KN, B_NK = 0, 1
 KERNEL_AUTO, KERNEL_MFMA, KERNEL_GEMV = 0, 1, 2
@@ -43,7 +43,7 @@ EXPORTED = (
     "qk_silu_mul_quant_per_token", "qk_gemm_workspace_size", "qk_gemm_i8_scaled",
     "qk_gemm_i8_scaled_ex", "qk_linear_w8a8", "qk_quant_per_token_fp8",
     "qk_silu_mul_quant_per_token_fp8", "qk_gemm_fp8_scaled", "qk_linear_fp8",
-    "qk_gemm_i8_grouped",
+    "qk_gemm_i8_grouped", "qk_moe_gemm_i8_scaled",
 )
 
 
@@ -90,6 +90,8 @@ def _declare(lib):
     lib.qk_linear_fp8.restype = I
     lib.qk_gemm_i8_grouped.argtypes = [I, I, I, I, P, P, P, P, P, F, P, I, I, P]
     lib.qk_gemm_i8_grouped.restype = I
+    lib.qk_moe_gemm_i8_scaled.argtypes = [I, I, I, I, P, P, P, P, P, P, F, P, I, I, P]
+    lib.qk_moe_gemm_i8_scaled.restype = I
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -503,6 +505,63 @@ def gemm_i8_grouped(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor | No
     _check(library().qk_gemm_i8_grouped(
         m, n, k, int(group), _ptr(a), _ptr(b), _ptr(c), _ptr(scale_a if want_out else None),
         _ptr(scale_b), float(output_scale), _ptr(out if want_out else None),
+        _OUT_DTYPES[out_dtype] if want_out else F32, layout, _stream(dev)))
+    if not want_out:
+        return c
+    return (out, c) if return_acc else out
+
+
+# ---- MoE grouped GEMM ----
+MOE_MAX_EXPERTS = 256
+
+
+def moe_gemm_i8_scaled(a: torch.Tensor, w: torch.Tensor, offsets: torch.Tensor,
+                       scale_a: torch.Tensor | None = None, scale_b: torch.Tensor | None = None,
+                       output_scale: float = 1.0, out_dtype: torch.dtype | None = torch.bfloat16,
+                       b_layout: str = "kn", return_acc: bool = False,
+                       out: torch.Tensor | None = None, c: torch.Tensor | None = None):
+    """All experts' INT8 GEMMs in one launch.
+
+    a [m, k] int8 codes, rows grouped by expert; w [experts, k, n] ("kn") or
+    [experts, n, k] ("nk") int8; offsets int32 [experts + 1] on the GPU (row
+    ranges, nondecreasing from 0 to m); scale_a [m], scale_b [experts, n]
+    fp32.  Returns out, (out, c) with the raw int32 accumulators, or c alone
+    when out_dtype is None.
+    """
+    _need(a, "a", torch.int8, 2)
+    dev = a.device
+    _need(w, "w", torch.int8, 3, dev)
+    _need(offsets, "offsets", torch.int32, 1, dev)
+    layout = _LAYOUTS[b_layout]
+    experts = w.shape[0]
+    m, k = a.shape
+    n, kb = (w.shape[2], w.shape[1]) if layout == B_KN else (w.shape[1], w.shape[2])
+    if kb != k:
+        raise ValueError(f"inner dimensions differ: a has k={k}, w has {kb}")
+    if offsets.shape[0] != experts + 1:
+        raise ValueError("offsets must have experts + 1 entries")
+    want_out = out is not None or out_dtype is not None
+    if want_out:
+        out_dtype = out.dtype if out is not None else out_dtype
+        if out_dtype not in _OUT_DTYPES:
+            raise TypeError(f"out dtype {out_dtype} not supported")
+        if out is None:
+            out = torch.empty((m, n), dtype=out_dtype, device=dev)
+        _need(out, "out", out_dtype, 2, dev)
+        _need(scale_a, "scale_a", torch.float32, 1, dev)
+        _need(scale_b, "scale_b", torch.float32, 2, dev)
+        if scale_a.shape[0] != m or tuple(scale_b.shape) != (experts, n) or tuple(out.shape) != (m, n):
+            raise ValueError("scale_a must be [m], scale_b [experts, n], out [m, n]")
+    if return_acc or not want_out:
+        if c is None:
+            c = torch.empty((m, n), dtype=torch.int32, device=dev)
+        _need(c, "c", torch.int32, 2, dev)
+    else:
+        c = None
+    _check(library().qk_moe_gemm_i8_scaled(
+        experts, m, n, k, _ptr(offsets), _ptr(a), _ptr(w), _ptr(c),
+        _ptr(scale_a if want_out else None), _ptr(scale_b if want_out else None),
+        float(output_scale), _ptr(out if want_out else None),
         _OUT_DTYPES[out_dtype] if want_out else F32, layout, _stream(dev)))
     if not want_out:
         return c

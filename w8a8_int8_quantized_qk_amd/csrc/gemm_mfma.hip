@@ -65,16 +65,15 @@ constexpr int FN = WTN / 16;   // ... along N
 constexpr int kSubTiles = (BM / WTM) * (BN / WTN);  // wave sub-tiles per workgroup tile
 static_assert(kSubTiles * kGroups == kWaves, "every wave owns one (sub-tile, k group)");
 
+// One workgroup's 256 x 128 output tile (tm, tn) of an M x N x K product.
 template <int MODE, bool KTAIL>
-__global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
+__device__ __forceinline__ void gemm_i8_tile(
     const int8_t* __restrict__ a, const int8_t* __restrict__ b, int32_t* __restrict__ c,
     const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
-    void* __restrict__ out, int out_dtype, int M, int N, int K, int tiles_m, int tiles_n) {
+    void* __restrict__ out, int out_dtype, int M, int N, int K, int tm, int tn) {
   constexpr bool kRegB = MODE == kBknReg4 || MODE == kBknReg1;
   __shared__ __attribute__((aligned(1024))) char smem[kStages * STAGE];
 
-  int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM;
   const int n0 = tn * BN;
   const int t = threadIdx.x;
@@ -443,6 +442,85 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
   }
 }
 
+template <int MODE, bool KTAIL>
+__global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
+    const int8_t* __restrict__ a, const int8_t* __restrict__ b, int32_t* __restrict__ c,
+    const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
+    void* __restrict__ out, int out_dtype, int M, int N, int K, int tiles_m, int tiles_n) {
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  gemm_i8_tile<MODE, KTAIL>(a, b, c, scale_a, scale_b, output_scale, out, out_dtype, M, N, K, tm,
+                            tn);
+}
+
+// MoE grouped GEMM ("dynquant-kernels", What is in here: one launch for all
+// experts): rows [offsets[e], offsets[e + 1]) of a belong to expert e, whose
+// weight is b + e * expert_stride and per-channel scales scale_b + e * N.
+// The grid is an upper bound on the tiles (the offsets live on the device);
+// every workgroup reads the offsets, counts each expert's tiles
+// (ceil(rows / BM) * tiles_n) with a block-wide prefix sum, and takes the
+// tile its index falls on, or leaves when the index is past the last one.
+// The XCD renumbering runs over the real tile count, so the surplus
+// workgroups, all at the end of the grid, do not unbalance the XCDs.
+// Offsets are clamped to [0, M]: invalid ones give unspecified results but
+// no access out of bounds.
+constexpr int kMoeMaxExperts = QK_MOE_MAX_EXPERTS;
+template <int MODE, bool KTAIL>
+__global__ __launch_bounds__(kThreads, 1) void gemm_i8_moe_kernel(
+    const int8_t* __restrict__ a, const int8_t* __restrict__ b, int32_t* __restrict__ c,
+    const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
+    void* __restrict__ out, int out_dtype, int M, int N, int K, int tiles_n,
+    const int* __restrict__ offsets, int experts, long long expert_stride) {
+  static_assert(kMoeMaxExperts <= kThreads && kMoeMaxExperts % 64 == 0, "one thread per expert");
+  __shared__ int s_wave_sum[kMoeMaxExperts / 64];
+  __shared__ int s_pick[2];  // the workgroup's expert and that expert's first tile
+  const int t = threadIdx.x;
+  int tiles = 0, row0 = 0, row1 = 0;
+  if (t < experts) {
+    row0 = min(max(offsets[t], 0), M);
+    row1 = min(max(offsets[t + 1], 0), M);
+    tiles = row1 > row0 ? ((row1 - row0 + BM - 1) / BM) * tiles_n : 0;
+  }
+  // inclusive prefix sum of the tile counts: within each wave, then across
+  // the (at most four) waves
+  int incl = tiles;
+  if (t < kMoeMaxExperts) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if ((t & 63) >= d) incl += v;
+    }
+    if ((t & 63) == 63) s_wave_sum[t >> 6] = incl;
+  }
+  if (t == 0) s_pick[0] = -1;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kMoeMaxExperts / 64; ++w) {
+    if (w < (t >> 6)) before += s_wave_sum[w];
+    total += s_wave_sum[w];
+  }
+  const int v = xcd_order(blockIdx.x, total);  // meaningful for blockIdx.x < total
+  const int excl = before + incl - tiles;
+  if (t < experts && tiles > 0 && v >= excl && v < excl + tiles) {
+    s_pick[0] = t;
+    s_pick[1] = excl;
+  }
+  __syncthreads();
+  const int e = s_pick[0];
+  if (static_cast<int>(blockIdx.x) >= total || e < 0) return;  // whole workgroup: past the last tile
+  const int r0 = min(max(offsets[e], 0), M);
+  const int Me = min(max(offsets[e + 1], 0), M) - r0;
+  int tm, tn;
+  group_order(v - s_pick[1], (Me + BM - 1) / BM, tiles_n, tm, tn);
+  const size_t row_off = static_cast<size_t>(r0);
+  void* out_e = out ? static_cast<char*>(out) + row_off * N * (out_dtype == QK_BF16 ? 2 : 4) : nullptr;
+  gemm_i8_tile<MODE, KTAIL>(a + row_off * K, b + e * expert_stride, c ? c + row_off * N : nullptr,
+                            scale_a ? scale_a + row_off : nullptr,
+                            scale_b ? scale_b + static_cast<size_t>(e) * N : nullptr, output_scale,
+                            out_e, out_dtype, Me, N, K, tm, tn);
+}
+
 template <int MODE>
 hipError_t launch_mode(const GemmArgs& g, dim3 grid, int tiles_m, int tiles_n,
                        hipStream_t stream) {
@@ -455,7 +533,34 @@ hipError_t launch_mode(const GemmArgs& g, dim3 grid, int tiles_m, int tiles_n,
                 tiles_n);
 }
 
+template <int MODE>
+hipError_t launch_moe_mode(const GemmArgs& g, const int* offsets, int experts, dim3 grid,
+                           int tiles_n, hipStream_t stream) {
+  const long long stride = static_cast<long long>(g.k) * g.n;
+  if (g.k % BK != 0)
+    return launch(gemm_i8_moe_kernel<MODE, true>, grid, dim3(kThreads), 0, stream, g.a, g.b, g.c,
+                  g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k, tiles_n,
+                  offsets, experts, stride);
+  return launch(gemm_i8_moe_kernel<MODE, false>, grid, dim3(kThreads), 0, stream, g.a, g.b, g.c,
+                g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k, tiles_n,
+                offsets, experts, stride);
+}
+
 }  // namespace
+
+int moe_max_experts() { return kMoeMaxExperts; }
+
+hipError_t launch_gemm_moe(const GemmArgs& g, const int* offsets, int experts, hipStream_t stream) {
+  // at most floor(m / BM) + experts tile rows over all experts
+  const int tiles_n = (g.n + BN - 1) / BN;
+  const long long tiles = (static_cast<long long>(g.m) / BM + experts) * tiles_n;
+  if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(tiles));
+  if (g.b_layout == QK_B_NK) return launch_moe_mode<kBnkDma>(g, offsets, experts, grid, tiles_n, stream);
+  if (g.n % 16 == 0) return launch_moe_mode<kBknDma>(g, offsets, experts, grid, tiles_n, stream);
+  if (g.n % 4 == 0) return launch_moe_mode<kBknReg4>(g, offsets, experts, grid, tiles_n, stream);
+  return launch_moe_mode<kBknReg1>(g, offsets, experts, grid, tiles_n, stream);
+}
 
 bool gemm_mfma_supported(int m, int n, int k) {
   return static_cast<unsigned long long>(m) * k < (1ull << 32) &&

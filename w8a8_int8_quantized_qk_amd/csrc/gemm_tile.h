@@ -238,10 +238,16 @@ __device__ __forceinline__ void quad_transpose(int x0, int x1, int x2, int x3, i
 
 constexpr int kGroupM = 4;
 
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int T = tiles_m * tiles_n;
-  int b = blockIdx.x;
-  if (T % 8 == 0) b = (b % 8) * (T / 8) + b / 8;
+// Tile b of T workgroups, renumbered so that the ones dispatched together to
+// one XCD (b, b + 8, ... run on the same XCD) are consecutive.
+__device__ __forceinline__ int xcd_order(int b, int T) {
+  return T % 8 == 0 ? (b % 8) * (T / 8) + b / 8 : b;
+}
+
+// (tm, tn) of tile b of a tiles_m x tiles_n grid: groups of kGroupM tile rows,
+// column-major inside a group, so that consecutive tiles share A rows and B
+// columns.
+__device__ __forceinline__ void group_order(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int group_tiles = kGroupM * tiles_n;
   const int g = b / group_tiles;
   const int first_m = g * kGroupM;
@@ -249,6 +255,10 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   const int r = b - g * group_tiles;
   tm = first_m + r % gm;
   tn = r / gm;
+}
+
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  group_order(xcd_order(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
 // ---- LDS-staged epilogue ----

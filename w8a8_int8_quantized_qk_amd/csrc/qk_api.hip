@@ -261,4 +261,28 @@ int qk_gemm_i8_grouped(int m, int n, int k, int group, const int8_t* a, const in
   return status_of(qk::launch_gemm_i8_grouped(g, group, stream));
 }
 
+int qk_moe_gemm_i8_scaled(int experts, int m, int n, int k, const int* expert_offsets,
+                          const int8_t* a, const int8_t* b, int32_t* c, const float* scale_a,
+                          const float* scale_b, float output_scale, void* out, int out_dtype,
+                          int b_layout, hipStream_t stream) {
+  if (experts < 1 || experts > qk::moe_max_experts()) return QK_ERR_INVALID_VALUE;
+  if (m < 0 || n < 0 || k < 0 || k > QK_MAX_K) return QK_ERR_INVALID_VALUE;
+  if (b_layout != QK_B_KN && b_layout != QK_B_NK) return QK_ERR_INVALID_VALUE;
+  if (k % 16 != 0) return QK_ERR_UNSUPPORTED;
+  if (m == 0 || n == 0) return QK_OK;
+  if (!expert_offsets || (!c && !out)) return QK_ERR_INVALID_VALUE;
+  if (out && out_dtype != QK_F32 && out_dtype != QK_BF16) return QK_ERR_INVALID_VALUE;
+  if (k > 0 && (!a || !b)) return QK_ERR_INVALID_VALUE;
+  if (out && (!scale_a || !scale_b)) return QK_ERR_INVALID_VALUE;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(expert_offsets, 4)) return QK_ERR_UNSUPPORTED;
+  if (c && !aligned(c, 4)) return QK_ERR_UNSUPPORTED;
+  if (out && !aligned(out, out_dtype == QK_BF16 ? 2 : 4)) return QK_ERR_UNSUPPORTED;
+  if (!qk::gemm_mfma_supported(m, n, k)) return QK_ERR_UNSUPPORTED;
+  // k % 16 == 0 keeps every expert's weight (k n bytes apart) and every row
+  // group's codes 16-byte aligned
+  qk::GemmArgs g{m, n, k, a, b, c, scale_a, scale_b, output_scale, out, out_dtype, b_layout,
+                 nullptr, 0};
+  return status_of(qk::launch_gemm_moe(g, expert_offsets, experts, stream));
+}
+
 }  // extern "C"

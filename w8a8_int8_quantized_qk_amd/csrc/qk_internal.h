@@ -61,6 +61,11 @@ hipError_t launch_silu_quant_rows_fp8(int m, int d, const void* h, int dtype, ui
 // are addressed with 32-bit offsets: m*k and n*k must stay below 2^32.
 bool gemm_mfma_supported(int m, int n, int k);
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
+// The same kernel over experts (gemm_mfma.hip): rows [offsets[e],
+// offsets[e + 1]) of a (device array of experts + 1 ints) use weight
+// b + e * k * n and per-channel scales scale_b + e * n; one launch.
+int moe_max_experts();
+hipError_t launch_gemm_moe(const GemmArgs& g, const int* offsets, int experts, hipStream_t stream);
 
 // GEMMs whose waves multiply whole k slices (gemm_slice.hip): the FP8
 // (e4m3fn) GEMM and the INT8 GEMM with per-group weight scales, both with

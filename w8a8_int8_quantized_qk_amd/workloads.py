@@ -22,7 +22,9 @@ even (torch); W is uniform on the integers [-127, 127]; the per-channel
 scales are uniform on [1e-3, 1e-2] in float32.  The gated workload draws H in
 place of X.  For the FP8 layer the weight is drawn instead as N(0, 1) x 100,
 clipped to +-448 and cast to float8_e4m3fn by torch; per-group weight scales
-are uniform on [1e-3, 1e-2] like the per-channel ones.  These shapes and
+are uniform on [1e-3, 1e-2] like the per-channel ones.  The MoE workload
+(generate_moe: 8 experts, 2048 tokens routed to 2 each, 4096 -> 14336) draws
+its per-expert row counts as multinomial(4096, Dirichlet(2)).  These shapes and
 distributions follow the workloads the pages describe (decode GEMV vs prefill
 GEMM, outlier channels, fused gated MLP).
 """
@@ -110,6 +112,30 @@ def random_channel_scales(rng: np.random.Generator, n: int) -> np.ndarray:
 def random_group_scales(rng: np.random.Generator, groups: int, n: int) -> np.ndarray:
     """Per-group weight scales [groups, n], uniform on [1e-3, 1e-2] in float32."""
     return rng.uniform(1e-3, 1e-2, (groups, n)).astype(np.float32)
+
+
+def moe_offsets(rng: np.random.Generator, rows: int, experts: int, alpha: float = 2.0) -> np.ndarray:
+    """Synthetic routing: row counts per expert ~ multinomial(rows, p) with
+    p ~ Dirichlet(alpha) (uneven, some experts busier than others), returned
+    as offsets [experts + 1] (int32, prefix sums from 0 to rows)."""
+    p = rng.dirichlet(np.full(experts, alpha))
+    counts = rng.multinomial(rows, p)
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+def generate_moe(seed: int = 0, experts: int = 8, tokens: int = 2048, top_k: int = 2,
+                 k: int = 4096, n: int = 14336) -> dict:
+    """The MoE up-projection workload: tokens x top_k routed rows, grouped by
+    expert, of bf16 activations [rows, k]; int8 weights [experts, k, n];
+    per-channel scales [experts, n]; offsets [experts + 1]."""
+    rng = np.random.default_rng(seed)
+    rows = tokens * top_k
+    offsets = moe_offsets(rng, rows, experts)
+    x = random_activations(rng, rows, k, "bf16")
+    w = rng.integers(-127, 128, size=(experts, k, n), dtype=np.int8)
+    s_ch = rng.uniform(1e-3, 1e-2, (experts, n)).astype(np.float32)
+    return {"x": x, "w": w, "s_ch": s_ch, "offsets": offsets, "experts": experts, "rows": rows,
+            "k": k, "n": n}
 
 
 def generate(name_or_workload, seed: int = 0, weight: str = "i8") -> dict:
