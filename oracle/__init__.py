@@ -90,6 +90,14 @@ def _load():
     lib.or_gemm_i8_grouped.restype = None
     lib.or_dequant_grouped.argtypes = [I64, I64, P, P, ctypes.c_float, P]
     lib.or_dequant_grouped.restype = None
+    lib.or_quant_static.argtypes = [I64, P, ctypes.c_float, P]
+    lib.or_quant_static.restype = None
+    lib.or_quant_static_fp8.argtypes = [I64, P, ctypes.c_float, P]
+    lib.or_quant_static_fp8.restype = None
+    lib.or_quant_rows_asym.argtypes = [I64, I64, P, P, P, P]
+    lib.or_quant_rows_asym.restype = None
+    lib.or_gemm_asym.argtypes = [I64, I64, I64, P, P, P, ctypes.c_int, P]
+    lib.or_gemm_asym.restype = I64
     _lib = lib
     return lib
 
@@ -395,3 +403,56 @@ def moe_dequant(c: np.ndarray, scale_a: np.ndarray, scale_b: np.ndarray, offsets
         if r1 > r0:
             out[r0:r1] = dequant(c[r0:r1], scale_a[r0:r1], scale_b[e], output_scale)
     return out
+
+
+# --------------------------------------------------------------------------
+# Static per-tensor scale ("kernels: fused silu_and_mul + dynamic per-token
+# FP8 quantization", Purpose: silu_and_mul_quant takes one pre-calibrated
+# scale) and asymmetric per-token quantization ("Skill: Write an INT8
+# Quantized Kernel", Inputs: a nonzero zero point instead of the symmetric
+# range).
+# --------------------------------------------------------------------------
+
+def quant_static(x32: np.ndarray, scale: float) -> np.ndarray:
+    """clamp(rint(x / scale), -127, 127) with one binary32 scale."""
+    lib = _load()
+    x = _contig(x32, np.float32)
+    q = np.empty(x.shape, dtype=np.int8)
+    lib.or_quant_static(x.size, _ptr(x), float(np.float32(scale)), _ptr(q))
+    return q
+
+
+def quant_static_fp8(x32: np.ndarray, scale: float) -> np.ndarray:
+    """e4m3fn(x / scale) with one binary32 scale."""
+    lib = _load()
+    x = _contig(x32, np.float32)
+    q = np.empty(x.shape, dtype=np.uint8)
+    lib.or_quant_static_fp8(x.size, _ptr(x), float(np.float32(scale)), _ptr(q))
+    return q
+
+
+def quant_per_token_asym(x32: np.ndarray):
+    """x32 [m, k] -> (codes int8 [m, k], scales float32 [m], zero points int32 [m])."""
+    lib = _load()
+    x = _contig(x32, np.float32)
+    m, k = x.shape
+    q = np.empty((m, k), dtype=np.int8)
+    s = np.empty(m, dtype=np.float32)
+    z = np.empty(m, dtype=np.int32)
+    lib.or_quant_rows_asym(m, k, _ptr(x), _ptr(q), _ptr(s), _ptr(z))
+    return q, s, z
+
+
+def gemm_asym(a: np.ndarray, zp: np.ndarray, b: np.ndarray, layout: int = B_KN) -> np.ndarray:
+    """Exact int32 sums of (a[i, t] - zp[i]) * B(t, j)."""
+    lib = _load()
+    aa = _contig(a, np.int8)
+    bb = _contig(b, np.int8)
+    z = _contig(zp, np.int32)
+    m, k = aa.shape
+    n = bb.shape[1] if layout == B_KN else bb.shape[0]
+    c = np.empty((m, n), dtype=np.int32)
+    ovf = lib.or_gemm_asym(m, n, k, _ptr(aa), _ptr(z), _ptr(bb), layout, _ptr(c))
+    if ovf:
+        raise OverflowError(f"{ovf} accumulators exceed int32")
+    return c

@@ -27,6 +27,12 @@
  *              channels (every 64-128), applied after the load; here the
  *              groups run along the reduction dimension k, so a group's
  *              integer partial sum is scaled before the groups are added.
+ *   [PR-S]     the same page, Purpose: silu_and_mul_quant quantizes with one
+ *              pre-calibrated (static, per-tensor) scale.
+ *   [ASYM]     "Skill: Write an INT8 Quantized Kernel", Inputs -- the
+ *              asymmetric alternative to the symmetric range: a nonzero zero
+ *              point.  Reading: per token, the range [min(row min, 0),
+ *              max(row max, 0)] maps onto [-128, 127].
  *   [PR]       "kernels: fused silu_and_mul + dynamic per-token FP8
  *              quantization", Purpose and Algorithm -- one scale per token
  *              from the row absmax, scale = max(absmax, 1e-12) / qmax, the
@@ -466,4 +472,89 @@ void or_dequant_grouped(int64_t m, int64_t n, const double *acc, const float *sc
     for (int64_t i = 0; i < m; ++i)
         for (int64_t j = 0; j < n; ++j)
             out[i * n + j] = acc[i * n + j] * (double)scale_a[i] * (double)output_scale;
+}
+
+/* ------------------------------------------------------------------ */
+/* Static per-tensor scale [PR-S]                                      */
+/* ------------------------------------------------------------------ */
+
+/* code = clamp(rint(x / scale), -127, 127), one scale for every element */
+void or_quant_static(int64_t count, const float *x, float scale, int8_t *q)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        float r = nearbyintf(x[i] / scale);
+        if (r > 127.0f)
+            r = 127.0f;
+        if (r < -127.0f)
+            r = -127.0f;
+        q[i] = (int8_t)r;
+    }
+}
+
+/* code = e4m3fn(x / scale) */
+void or_quant_static_fp8(int64_t count, const float *x, float scale, uint8_t *q)
+{
+    for (int64_t i = 0; i < count; ++i)
+        q[i] = or_fp8_encode(x[i] / scale);
+}
+
+/* ------------------------------------------------------------------ */
+/* Asymmetric per-token quantization [ASYM]                            */
+/* ------------------------------------------------------------------ */
+
+/* lo = min(row min, 0), hi = max(row max, 0);
+ * scale = max(hi - lo, 1e-12) / 255                (binary32 operations);
+ * zp = clamp(rint(-lo / scale) - 128, -128, 127);
+ * code = clamp(rint(x / scale) + zp, -128, 127), so x ~ (code - zp) * scale
+ * and x = 0 has the exact code zp. */
+void or_quant_rows_asym(int64_t m, int64_t k, const float *x, int8_t *q, float *scale,
+                        int32_t *zp)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i) {
+        const float *row = x + i * k;
+        float lo = 0.0f, hi = 0.0f;
+        for (int64_t j = 0; j < k; ++j) {
+            if (row[j] < lo)
+                lo = row[j];
+            if (row[j] > hi)
+                hi = row[j];
+        }
+        const float s = fmaxf(hi - lo, 1e-12f) / 255.0f;
+        float z = nearbyintf(-lo / s) - 128.0f;
+        if (z > 127.0f)
+            z = 127.0f;
+        if (z < -128.0f)
+            z = -128.0f;
+        scale[i] = s;
+        zp[i] = (int32_t)z;
+        for (int64_t j = 0; j < k; ++j) {
+            float r = nearbyintf(row[j] / s) + z;
+            if (r > 127.0f)
+                r = 127.0f;
+            if (r < -128.0f)
+                r = -128.0f;
+            q[i * k + j] = (int8_t)r;
+        }
+    }
+}
+
+/* acc[i][j] = sum_t (a[i][t] - zp[i]) * B(t, j), exact; returns the number of
+ * results outside int32. */
+int64_t or_gemm_asym(int64_t m, int64_t n, int64_t k, const int8_t *a, const int32_t *zp,
+                     const int8_t *b, int layout, int32_t *c)
+{
+    int64_t overflow = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : overflow)
+    for (int64_t i = 0; i < m; ++i) {
+        for (int64_t j = 0; j < n; ++j) {
+            int64_t acc = 0;
+            for (int64_t kk = 0; kk < k; ++kk)
+                acc += ((int64_t)a[i * k + kk] - zp[i]) * (int64_t)weight_at(b, layout, n, k, kk, j);
+            if (acc > INT32_MAX || acc < INT32_MIN)
+                ++overflow;
+            c[i * n + j] = (int32_t)acc;
+        }
+    }
+    return overflow;
 }
