@@ -63,6 +63,8 @@ def _args():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8 layer at the prefill shape")
     p.add_argument("--no-moe", action="store_true", help="skip the MoE grouped GEMM")
+    p.add_argument("--no-static-asym", action="store_true",
+                   help="skip the static and asymmetric variants")
     p.add_argument("--no-grouped", action="store_true",
                    help="skip the INT8 GEMM with per-group weight scales at the prefill shape")
     p.add_argument("--no-other-configs", action="store_true",
@@ -342,6 +344,64 @@ def main():
             "workload": "prefill_outliers with group scales [K/G, N]", "m": m, "k": k, "n": n,
             "step": "qk_quant_per_token + qk_gemm_i8_grouped, replayed from HIP graphs", **grouped}
         del gsets
+        torch.cuda.empty_cache()
+
+    # ---------------- static and asymmetric variants at the prefill shape ----------------
+    if not args.no_static_asym:
+        vsets = []
+        for r in range(args.ring):
+            d = wl.generate(wcfg, seed=r)
+            w_dev = torch.from_numpy(d["w"]).to(dev)
+            amax = float(d["x"].float().abs().max())
+            vsets.append({"x": d["x"].to(dev), "w": w_dev, "s_ch": torch.from_numpy(d["s_ch"]).to(dev),
+                          "wsum": qk.weight_colsum(w_dev),
+                          "s_static": torch.tensor([amax / 127.0], dtype=torch.float32, device=dev),
+                          "q": torch.empty((m, k), dtype=torch.int8, device=dev),
+                          "out": torch.empty((m, n), dtype=torch.bfloat16, device=dev)})
+        torch.cuda.synchronize()
+
+        def vstatic(bs):
+            qk.quant_static(bs["x"], bs["s_static"], q=bs["q"])
+
+        def vasym_q(bs):
+            bs["qa"] = qk.quant_per_token_asym(bs["x"])
+
+        for bs in vsets:
+            vasym_q(bs)
+
+        def vasym_gemm(bs):
+            q, s, z = bs["qa"]
+            qk.library().qk_gemm_i8_asym(m, n, k, qk._ptr(q), qk._ptr(z), qk._ptr(bs["w"]),
+                                         qk._ptr(bs["wsum"]), None, qk._ptr(s), qk._ptr(bs["s_ch"]),
+                                         1.0, qk._ptr(bs["out"]), qk.BF16, qk.B_KN,
+                                         qk._stream(dev))
+
+        st_ms, _ = timed_replays([(lambda bs=b: vstatic(bs)) for b in vsets], args.steps, args.warmup)
+        aq_ms, _ = timed_replays([(lambda bs=b: qk.library().qk_quant_per_token_asym(
+            m, k, qk._ptr(bs["x"]), qk.BF16, qk._ptr(bs["qa"][0]), qk._ptr(bs["qa"][1]),
+            qk._ptr(bs["qa"][2]), qk._stream(dev))) for b in vsets], args.steps, args.warmup)
+        ag_ms, _ = timed_replays([(lambda bs=b: vasym_gemm(bs)) for b in vsets], args.steps, args.warmup)
+        qbytes = m * k * 2 + m * k
+        aops = 2.0 * m * n * k
+        agt = aops / (ag_ms * 1e-3) / 1e12
+        result["static_asym_prefill"] = {
+            "workload": "prefill_outliers", "m": m, "k": k, "n": n,
+            "static_quant": {"us": round(st_ms * 1e3, 3), "unit": "GB/s",
+                             "value": round(qbytes / (st_ms * 1e-3) / 1e9, 1),
+                             "roofline": {"bound": "hbm", "achieved": round(qbytes / (st_ms * 1e-3) / 1e9, 1),
+                                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                          "frac": round(qbytes / (st_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                          "traffic": None, "algorithmic_bytes_per_launch": qbytes}},
+            "asym_quant": {"us": round(aq_ms * 1e3, 3), "unit": "GB/s",
+                           "value": round((qbytes + 8 * m) / (aq_ms * 1e-3) / 1e9, 1)},
+            "asym_gemm": {"us": round(ag_ms * 1e3, 3), "unit": "TOPS", "value": round(agt, 2),
+                          "roofline": {"bound": "mfma", "kernel": "gemm_i8_asym_kernel",
+                                       "achieved": round(agt, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                                       "frac": round(agt / INT8_PEAK_TOPS, 4), "traffic": None,
+                                       "avg_launch_us": round(ag_ms * 1e3, 3),
+                                       "algorithmic_ops_per_launch": aops}},
+        }
+        del vsets
         torch.cuda.empty_cache()
 
     # ---------------- MoE grouped GEMM: all experts in one launch ----------------

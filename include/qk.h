@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QK_ABI_VERSION 4
+#define QK_ABI_VERSION 5
 
 /* element types */
 #define QK_F32 0
@@ -326,6 +326,73 @@ int qk_moe_gemm_i8_scaled(int experts, int m, int n, int k, const int *expert_of
                           const int8_t *a, const int8_t *b, int32_t *c, const float *scale_a,
                           const float *scale_b, float output_scale, void *out, int out_dtype,
                           int b_layout, hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
+/* Static (per-tensor) quantization                                    */
+/* ------------------------------------------------------------------ */
+/*
+ * Quantization with one pre-calibrated scale for the whole tensor ("kernels:
+ * fused silu_and_mul + dynamic per-token FP8 quantization", Purpose:
+ * silu_and_mul_quant takes a global scale), read from DEVICE memory:
+ *   INT8:  q[i][j] = clamp(rint(x[i][j] / *scale), -127, 127)
+ *   FP8:   q[i][j] = e4m3fn(x[i][j] / *scale)   (nearest even, saturating)
+ * (binary32 quotient; the _silu_mul_ forms quantize silu(gate) * up of
+ * h [m][2d] as qk_silu_mul_quant_per_token does).
+ *   scale  one float on the device, > 0 (not checked; a zero or negative
+ *          scale gives unspecified codes).
+ * Errors as qk_quant_per_token.
+ */
+int qk_quant_static(int m, int k, const void *x, int x_dtype, const float *scale, int8_t *q,
+                    hipStream_t stream);
+int qk_silu_mul_quant_static(int m, int d, const void *h, int h_dtype, const float *scale,
+                             int8_t *q, hipStream_t stream);
+int qk_quant_static_fp8(int m, int k, const void *x, int x_dtype, const float *scale, uint8_t *q,
+                        hipStream_t stream);
+int qk_silu_mul_quant_static_fp8(int m, int d, const void *h, int h_dtype, const float *scale,
+                                 uint8_t *q, hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
+/* Asymmetric (zero-point) activations                                 */
+/* ------------------------------------------------------------------ */
+/* Largest k of the asymmetric GEMM: the zero-point term keeps the INT32
+ * result within range (2 * 65535 * 128 * 127 < 2^31). */
+#define QK_MAX_K_ASYM 65535
+
+/*
+ * Per-token asymmetric INT8 quantization ("Skill: Write an INT8 Quantized
+ * Kernel", Inputs: the asymmetric alternative, a nonzero zero point):
+ *   lo = min(min_j x[i][j], 0), hi = max(max_j x[i][j], 0)
+ *   scale[i]      = max(hi - lo, 1e-12f) / 255                 (binary32)
+ *   zero_point[i] = clamp(rint(-lo / scale[i]) - 128, -128, 127)
+ *   q[i][j]       = clamp(rint(x[i][j] / scale[i]) + zero_point[i], -128, 127)
+ * so x ~ (q - zero_point) * scale, and 0 has the exact code zero_point.
+ *   q [m][k] int8, scale [m] float, zero_point [m] int32 (all written).
+ * Errors as qk_quant_per_token (NULL zero_point with m > 0 is invalid).
+ */
+int qk_quant_per_token_asym(int m, int k, const void *x, int x_dtype, int8_t *q, float *scale,
+                            int32_t *zero_point, hipStream_t stream);
+
+/* Column sums of an INT8 weight, wsum[j] = sum_t B(t, j) (int32), for the
+ * zero-point term of qk_gemm_i8_asym; computed once per weight.
+ * b [k][n] (QK_B_KN) or [n][k] (QK_B_NK); wsum [n]. */
+int qk_weight_colsum(int k, int n, const int8_t *b, int b_layout, int32_t *wsum,
+                     hipStream_t stream);
+
+/*
+ * INT8 GEMM of asymmetric activations with the dequant epilogue:
+ *   acc[i][j] = sum_t (a[i][t] - zero_point[i]) * B(t, j)
+ *             = sum_t a[i][t] * B(t, j) - zero_point[i] * wsum[j]   (exact INT32)
+ *   c[i][j]   = acc (if c != NULL)
+ *   out[i][j] = ((float)acc * scale_a[i]) * (scale_b[j] * output_scale)
+ *   zero_point [m] int32, wsum [n] int32 = qk_weight_colsum of b; other
+ *   arguments as qk_gemm_i8_scaled (the tiled kernel for every m).
+ * Requirements: 0 <= k <= QK_MAX_K_ASYM, k % 16 == 0, a and b 16-byte
+ * aligned, m*k and n*k below 2^32.
+ */
+int qk_gemm_i8_asym(int m, int n, int k, const int8_t *a, const int32_t *zero_point,
+                    const int8_t *b, const int32_t *wsum, int32_t *c, const float *scale_a,
+                    const float *scale_b, float output_scale, void *out, int out_dtype,
+                    int b_layout, hipStream_t stream);
 
 #ifdef __cplusplus
 }

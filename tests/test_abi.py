@@ -248,3 +248,33 @@ def test_moe_argument_errors_are_reported_before_launch(lib):
     assert mm(2, 4, 4, 16, cc=NULL, out=NULL) == INVALID
     assert mm(2, 4, 4, 16, b=FAKE_ODD) == UNSUP
     assert mm(2, 0, 4, 16, off=NULL, a=NULL) == 0
+
+
+def test_static_and_asym_argument_errors_are_reported_before_launch(lib):
+    c = _header_constants()
+    INVALID, UNSUP = c["QK_ERR_INVALID_VALUE"], c["QK_ERR_UNSUPPORTED"]
+    assert c["QK_MAX_K_ASYM"] == qk.MAX_K_ASYM
+    for name in ("qk_quant_static", "qk_silu_mul_quant_static", "qk_quant_static_fp8",
+                 "qk_silu_mul_quant_static_fp8"):
+        fn = getattr(lib, name)
+        assert fn(-1, 4, FAKE, 0, FAKE, FAKE, NULL) == INVALID
+        assert fn(4, 4, FAKE, 9, FAKE, FAKE, NULL) == INVALID
+        assert fn(4, 4, FAKE, 0, NULL, FAKE, NULL) == INVALID      # no scale
+        assert fn(0, 4, NULL, 0, NULL, NULL, NULL) == 0
+    aq = lib.qk_quant_per_token_asym
+    assert aq(4, 4, FAKE, 0, FAKE, FAKE, NULL, NULL) == INVALID   # no zero-point buffer
+    assert aq(0, 4, NULL, 0, NULL, NULL, NULL, NULL) == 0
+    assert lib.qk_weight_colsum(16, 4, FAKE, 3, FAKE, NULL) == INVALID
+    assert lib.qk_weight_colsum(16, 4, FAKE, 0, NULL, NULL) == INVALID
+    assert lib.qk_weight_colsum(16, 0, NULL, 0, NULL, NULL) == 0
+
+    def ag(m, n, k, zp=FAKE, ws=FAKE, a=FAKE, b=FAKE, cc=FAKE, sa=FAKE, sb=FAKE, out=FAKE):
+        return lib.qk_gemm_i8_asym(m, n, k, a, zp, b, ws, cc, sa, sb, 1.0, out, 0, 0, NULL)
+
+    assert ag(4, 4, qk.MAX_K_ASYM + 17) == INVALID
+    assert ag(4, 4, 24) == UNSUP
+    assert ag(4, 4, 16, zp=NULL) == INVALID
+    assert ag(4, 4, 16, ws=NULL) == INVALID
+    assert ag(4, 4, 16, sa=NULL) == INVALID
+    assert ag(4, 4, 16, a=FAKE_ODD) == UNSUP
+    assert ag(0, 4, 16, a=NULL, b=NULL) == 0

@@ -24,7 +24,7 @@ import threading
 
 import torch
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 F32, BF16, F16 = 0, 1, 2
 B_KN, B_NK = 0, 1
 KERNEL_AUTO, KERNEL_MFMA, KERNEL_GEMV = 0, 1, 2
@@ -43,7 +43,9 @@ EXPORTED = (
     "qk_silu_mul_quant_per_token", "qk_gemm_workspace_size", "qk_gemm_i8_scaled",
     "qk_gemm_i8_scaled_ex", "qk_linear_w8a8", "qk_quant_per_token_fp8",
     "qk_silu_mul_quant_per_token_fp8", "qk_gemm_fp8_scaled", "qk_linear_fp8",
-    "qk_gemm_i8_grouped", "qk_moe_gemm_i8_scaled",
+    "qk_gemm_i8_grouped", "qk_moe_gemm_i8_scaled", "qk_quant_static", "qk_silu_mul_quant_static",
+    "qk_quant_static_fp8", "qk_silu_mul_quant_static_fp8", "qk_quant_per_token_asym",
+    "qk_weight_colsum", "qk_gemm_i8_asym",
 )
 
 
@@ -92,6 +94,16 @@ def _declare(lib):
     lib.qk_gemm_i8_grouped.restype = I
     lib.qk_moe_gemm_i8_scaled.argtypes = [I, I, I, I, P, P, P, P, P, P, F, P, I, I, P]
     lib.qk_moe_gemm_i8_scaled.restype = I
+    for name in ("qk_quant_static", "qk_silu_mul_quant_static", "qk_quant_static_fp8",
+                 "qk_silu_mul_quant_static_fp8"):
+        getattr(lib, name).argtypes = [I, I, P, I, P, P, P]
+        getattr(lib, name).restype = I
+    lib.qk_quant_per_token_asym.argtypes = [I, I, P, I, P, P, P, P]
+    lib.qk_quant_per_token_asym.restype = I
+    lib.qk_weight_colsum.argtypes = [I, I, P, I, P, P]
+    lib.qk_weight_colsum.restype = I
+    lib.qk_gemm_i8_asym.argtypes = [I, I, I, P, P, P, P, P, P, P, F, P, I, I, P]
+    lib.qk_gemm_i8_asym.restype = I
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -563,6 +575,101 @@ def moe_gemm_i8_scaled(a: torch.Tensor, w: torch.Tensor, offsets: torch.Tensor,
         _ptr(scale_a if want_out else None), _ptr(scale_b if want_out else None),
         float(output_scale), _ptr(out if want_out else None),
         _OUT_DTYPES[out_dtype] if want_out else F32, layout, _stream(dev)))
+    if not want_out:
+        return c
+    return (out, c) if return_acc else out
+
+
+# ---- static (per-tensor) quantization ----
+
+def quant_static(x: torch.Tensor, scale: torch.Tensor, fp8: bool = False, silu: bool = False,
+                 q: torch.Tensor | None = None) -> torch.Tensor:
+    """Codes of x [m, k] (or of silu(h[:, :d]) * h[:, d:] when silu) with one
+    scale for the whole tensor (a one-element fp32 GPU tensor): INT8
+    clamp(rint(x / s), -127, 127), or float8_e4m3fn x / s when fp8."""
+    _need(x, "x", ndim=2)
+    if x.dtype not in _IN_DTYPES:
+        raise TypeError(f"x dtype {x.dtype} not supported")
+    _need(scale, "scale", torch.float32, None, x.device)
+    if scale.numel() != 1:
+        raise ValueError("scale must hold one value")
+    m, k = x.shape
+    if silu:
+        if k % 2:
+            raise ValueError("h must have an even number of columns (gate | up)")
+        k //= 2
+    qdt = torch.float8_e4m3fn if fp8 else torch.int8
+    q = torch.empty((m, k), dtype=qdt, device=x.device) if q is None else q
+    if fp8:
+        _need_codes(q, "q", 2, x.device)
+    else:
+        _need(q, "q", torch.int8, 2, x.device)
+    if tuple(q.shape) != (m, k):
+        raise ValueError("q has the wrong shape")
+    name = ("qk_silu_mul_quant_static" if silu else "qk_quant_static") + ("_fp8" if fp8 else "")
+    _check(getattr(library(), name)(m, k, _ptr(x), _IN_DTYPES[x.dtype], _ptr(scale), _ptr(q),
+                                    _stream(x.device)))
+    return q
+
+
+# ---- asymmetric (zero-point) activations ----
+MAX_K_ASYM = 65535
+
+
+def quant_per_token_asym(x: torch.Tensor):
+    """Asymmetric per-token INT8 codes of x [m, k]: (q int8, scale fp32 [m], zero_point int32 [m])."""
+    _need(x, "x", ndim=2)
+    if x.dtype not in _IN_DTYPES:
+        raise TypeError(f"x dtype {x.dtype} not supported")
+    m, k = x.shape
+    q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    scale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    zp = torch.empty((m,), dtype=torch.int32, device=x.device)
+    _check(library().qk_quant_per_token_asym(m, k, _ptr(x), _IN_DTYPES[x.dtype], _ptr(q),
+                                             _ptr(scale), _ptr(zp), _stream(x.device)))
+    return q, scale, zp
+
+
+def weight_colsum(w: torch.Tensor, b_layout: str = "kn") -> torch.Tensor:
+    """int32 column sums of an INT8 weight ([k, n] "kn" or [n, k] "nk")."""
+    _need(w, "w", torch.int8, 2)
+    layout = _LAYOUTS[b_layout]
+    k, n = (w.shape[0], w.shape[1]) if layout == B_KN else (w.shape[1], w.shape[0])
+    wsum = torch.empty((n,), dtype=torch.int32, device=w.device)
+    _check(library().qk_weight_colsum(k, n, _ptr(w), layout, _ptr(wsum), _stream(w.device)))
+    return wsum
+
+
+def gemm_i8_asym(a: torch.Tensor, zero_point: torch.Tensor, b: torch.Tensor, wsum: torch.Tensor,
+                 scale_a: torch.Tensor | None = None, scale_b: torch.Tensor | None = None,
+                 output_scale: float = 1.0, out_dtype: torch.dtype | None = torch.bfloat16,
+                 b_layout: str = "kn", return_acc: bool = False):
+    """INT8 GEMM of asymmetric activations: acc = sum (a - zero_point[row]) * B,
+    out = acc * scale_a * scale_b * output_scale."""
+    _need(a, "a", torch.int8, 2)
+    dev = a.device
+    _need(b, "b", torch.int8, 2, dev)
+    _need(zero_point, "zero_point", torch.int32, 1, dev)
+    _need(wsum, "wsum", torch.int32, 1, dev)
+    layout = _LAYOUTS[b_layout]
+    m, k = a.shape
+    n, kb = (b.shape[1], b.shape[0]) if layout == B_KN else (b.shape[0], b.shape[1])
+    if kb != k or zero_point.shape[0] != m or wsum.shape[0] != n:
+        raise ValueError("shapes differ: a [m, k], zero_point [m], b [k, n], wsum [n]")
+    want_out = out_dtype is not None
+    out = None
+    if want_out:
+        if out_dtype not in _OUT_DTYPES:
+            raise TypeError(f"out dtype {out_dtype} not supported")
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+        _need(scale_a, "scale_a", torch.float32, 1, dev)
+        _need(scale_b, "scale_b", torch.float32, 1, dev)
+    c = torch.empty((m, n), dtype=torch.int32, device=dev) if (return_acc or not want_out) else None
+    _check(library().qk_gemm_i8_asym(
+        m, n, k, _ptr(a), _ptr(zero_point), _ptr(b), _ptr(wsum), _ptr(c),
+        _ptr(scale_a if want_out else None), _ptr(scale_b if want_out else None),
+        float(output_scale), _ptr(out), _OUT_DTYPES[out_dtype] if want_out else F32, layout,
+        _stream(dev)))
     if not want_out:
         return c
     return (out, c) if return_acc else out

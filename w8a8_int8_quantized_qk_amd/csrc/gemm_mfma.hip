@@ -66,11 +66,15 @@ constexpr int kSubTiles = (BM / WTM) * (BN / WTN);  // wave sub-tiles per workgr
 static_assert(kSubTiles * kGroups == kWaves, "every wave owns one (sub-tile, k group)");
 
 // One workgroup's 256 x 128 output tile (tm, tn) of an M x N x K product.
-template <int MODE, bool KTAIL>
+// ASYM: the activations carry per-row zero points zp_a, and the epilogue
+// subtracts zp_a[row] * wsum[col] (wsum: the weight's column sums) from the
+// INT32 accumulators before storing or scaling them.
+template <int MODE, bool KTAIL, bool ASYM = false>
 __device__ __forceinline__ void gemm_i8_tile(
     const int8_t* __restrict__ a, const int8_t* __restrict__ b, int32_t* __restrict__ c,
     const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
-    void* __restrict__ out, int out_dtype, int M, int N, int K, int tm, int tn) {
+    void* __restrict__ out, int out_dtype, int M, int N, int K, int tm, int tn,
+    const int32_t* __restrict__ zp_a = nullptr, const int32_t* __restrict__ wsum = nullptr) {
   constexpr bool kRegB = MODE == kBknReg4 || MODE == kBknReg1;
   __shared__ __attribute__((aligned(1024))) char smem[kStages * STAGE];
 
@@ -92,6 +96,14 @@ __device__ __forceinline__ void gemm_i8_tile(
       if (m0 + t < M) scale_reg = scale_a[m0 + t];
     } else if (t < BM + BN) {
       if (n0 + t - BM < N) scale_reg = scale_b[n0 + t - BM];  // times output_scale later
+    }
+  }
+  int corr_reg = 0;  // this thread's row zero point or column sum (ASYM)
+  if constexpr (ASYM) {
+    if (t < BM) {
+      if (m0 + t < M) corr_reg = zp_a[m0 + t];
+    } else if (t < BM + BN) {
+      if (n0 + t - BM < N) corr_reg = wsum[n0 + t - BM];
     }
   }
 
@@ -385,12 +397,15 @@ __device__ __forceinline__ void gemm_i8_tile(
   // nontemporal: nothing here reads them.
   constexpr int kHalfM = FM / kGroups;  // fragment rows finished per group
   constexpr int kChunkBytes = kHalfM * FN * 64 * 16;  // one group's hand-over
-  static_assert(2 * kSubTiles * kChunkBytes + 4 * (BM + BN) <= kStages * STAGE,
-                "epilogue hand-over fits in LDS");
+  static_assert(2 * kSubTiles * kChunkBytes + 8 * (BM + BN) <= kStages * STAGE,
+                "epilogue hand-over, scales and zero-point terms fit in LDS");
   __syncthreads();  // every wave is done with the k slices
   float* s_sa = reinterpret_cast<float*>(smem + 2 * kSubTiles * kChunkBytes);
   float* s_sb = s_sa + BM;
   if (out && t < BM + BN) s_sa[t] = t < BM ? scale_reg : scale_reg * output_scale;  // s_sb follows s_sa
+  int* s_zp = reinterpret_cast<int*>(s_sa + BM + BN);  // row zero points, then column sums (ASYM)
+  int* s_ws = s_zp + BM;
+  if (ASYM && t < BM + BN) s_zp[t] = corr_reg;
   // hand-over region written for group `to` of this sub-tile
   auto chunk_at = [&](int to, int ii, int j) -> v4i* {
     return reinterpret_cast<v4i*>(smem + (wsub * 2 + to) * kChunkBytes +
@@ -433,12 +448,16 @@ __device__ __forceinline__ void gemm_i8_tile(
 
   const int lrow0 = wm * WTM + (grp == 0 ? 0 : kFinRows);  // tile-local first row of the block
   const int lcol0 = wn * WTN;
-  if (c) store4<kFinRows, false, true>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, c);
+  if (c)
+    store4<kFinRows, false, true, ASYM>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, c,
+                                        s_zp, s_ws);
   if (out) {
     if (out_dtype == QK_BF16)
-      store_bf16<kFinRows, false>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, out);
+      store_bf16<kFinRows, false, ASYM>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, out,
+                                        s_zp, s_ws);
     else
-      store4<kFinRows, false, false>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, out);
+      store4<kFinRows, false, false, ASYM>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb,
+                                           out, s_zp, s_ws);
   }
 }
 
@@ -521,6 +540,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_moe_kernel(
                             out_e, out_dtype, Me, N, K, tm, tn);
 }
 
+// Asymmetric activations: codes with per-row zero points; the result is
+// sum_t (a[i][t] - zp_a[i]) * B(t, j) = acc - zp_a[i] * wsum[j].
+template <int MODE, bool KTAIL>
+__global__ __launch_bounds__(kThreads, 1) void gemm_i8_asym_kernel(
+    const int8_t* __restrict__ a, const int8_t* __restrict__ b, int32_t* __restrict__ c,
+    const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
+    void* __restrict__ out, int out_dtype, int M, int N, int K, int tiles_m, int tiles_n,
+    const int32_t* __restrict__ zp_a, const int32_t* __restrict__ wsum) {
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  gemm_i8_tile<MODE, KTAIL, true>(a, b, c, scale_a, scale_b, output_scale, out, out_dtype, M, N, K,
+                                  tm, tn, zp_a, wsum);
+}
+
 template <int MODE>
 hipError_t launch_mode(const GemmArgs& g, dim3 grid, int tiles_m, int tiles_n,
                        hipStream_t stream) {
@@ -549,6 +582,33 @@ hipError_t launch_moe_mode(const GemmArgs& g, const int* offsets, int experts, d
 }  // namespace
 
 int moe_max_experts() { return kMoeMaxExperts; }
+
+namespace {
+template <int MODE>
+hipError_t launch_asym_mode(const GemmArgs& g, const int32_t* zp_a, const int32_t* wsum, dim3 grid,
+                            int tiles_m, int tiles_n, hipStream_t stream) {
+  if (g.k % BK != 0)
+    return launch(gemm_i8_asym_kernel<MODE, true>, grid, dim3(kThreads), 0, stream, g.a, g.b, g.c,
+                  g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k, tiles_m,
+                  tiles_n, zp_a, wsum);
+  return launch(gemm_i8_asym_kernel<MODE, false>, grid, dim3(kThreads), 0, stream, g.a, g.b, g.c,
+                g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k, tiles_m,
+                tiles_n, zp_a, wsum);
+}
+}  // namespace
+
+hipError_t launch_gemm_asym(const GemmArgs& g, const int32_t* zp_a, const int32_t* wsum,
+                            hipStream_t stream) {
+  const int tiles_m = (g.m + BM - 1) / BM;
+  const int tiles_n = (g.n + BN - 1) / BN;
+  const long long tiles = static_cast<long long>(tiles_m) * tiles_n;
+  if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(tiles));
+  if (g.b_layout == QK_B_NK) return launch_asym_mode<kBnkDma>(g, zp_a, wsum, grid, tiles_m, tiles_n, stream);
+  if (g.n % 16 == 0) return launch_asym_mode<kBknDma>(g, zp_a, wsum, grid, tiles_m, tiles_n, stream);
+  if (g.n % 4 == 0) return launch_asym_mode<kBknReg4>(g, zp_a, wsum, grid, tiles_m, tiles_n, stream);
+  return launch_asym_mode<kBknReg1>(g, zp_a, wsum, grid, tiles_m, tiles_n, stream);
+}
 
 hipError_t launch_gemm_moe(const GemmArgs& g, const int* offsets, int experts, hipStream_t stream) {
   // at most floor(m / BM) + experts tile rows over all experts

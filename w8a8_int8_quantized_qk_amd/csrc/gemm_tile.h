@@ -294,14 +294,29 @@ __device__ __forceinline__ float acc_value(int v) {
     return static_cast<float>(v);
 }
 
+// Zero-point correction of INT32 accumulators (asymmetric activations):
+// acc - zp[row] * wsum[col], with the tile's zero points and column sums in
+// LDS.  Without CORR the accumulators are used as they are.
+template <bool CORR>
+__device__ __forceinline__ v4i corrected(v4i v, const int* s_zp, const int* s_ws, int lrow, int lcol) {
+  if constexpr (CORR) {
+    const int z = s_zp[lrow];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] -= z * s_ws[lcol + e];
+  }
+  return v;
+}
+
 // Raw accumulators (IS_C: INT32 or binary32 bit patterns to c) or fp32
 // results: 4 columns (16 bytes) per lane, 4 rows per pass.  The block covers
 // tile-local rows [lrow0, lrow0 + kRows) and columns [lcol0, lcol0 + 64) of
-// the tile at (m0, n0); s_sa and s_sb are the tile's row and column scales.
-template <int kRows, bool ACC_F32, bool IS_C>
+// the tile at (m0, n0); s_sa and s_sb are the tile's row and column scales,
+// s_zp and s_ws its zero points and column sums (CORR only).
+template <int kRows, bool ACC_F32, bool IS_C, bool CORR = false>
 __device__ __forceinline__ void store4(int* stage, int lane, int m0, int n0, int lrow0, int lcol0,
                                        int M, int N, const float* s_sa, const float* s_sb,
-                                       void* __restrict__ dst) {
+                                       void* __restrict__ dst, const int* s_zp = nullptr,
+                                       const int* s_ws = nullptr) {
   const int q = lane & 15;
   const int lcol = lcol0 + 4 * q;
   const int gcol = n0 + lcol;
@@ -314,7 +329,7 @@ __device__ __forceinline__ void store4(int* stage, int lane, int m0, int n0, int
   for (int pass = 0; pass < kRows / 4; ++pass) {
     const int r = 4 * pass + (lane >> 4);
     const int grow = m0 + lrow0 + r;
-    const v4i v = *stage_at(stage, r, q);
+    const v4i v = corrected<CORR>(*stage_at(stage, r, q), s_zp, s_ws, lrow0 + r, lcol);
     if (grow >= M) continue;
     const size_t base = static_cast<size_t>(grow) * N + gcol;
     if constexpr (IS_C) {
@@ -343,10 +358,11 @@ __device__ __forceinline__ void store4(int* stage, int lane, int m0, int n0, int
 }
 
 // bf16 results: 8 columns (16 bytes) per lane, 8 rows per pass.
-template <int kRows, bool ACC_F32>
+template <int kRows, bool ACC_F32, bool CORR = false>
 __device__ __forceinline__ void store_bf16(int* stage, int lane, int m0, int n0, int lrow0,
                                            int lcol0, int M, int N, const float* s_sa,
-                                           const float* s_sb, void* __restrict__ out) {
+                                           const float* s_sb, void* __restrict__ out,
+                                           const int* s_zp = nullptr, const int* s_ws = nullptr) {
   const int q2 = lane & 7;
   const int lcol = lcol0 + 8 * q2;
   const int gcol = n0 + lcol;
@@ -357,8 +373,8 @@ __device__ __forceinline__ void store_bf16(int* stage, int lane, int m0, int n0,
   for (int pass = 0; pass < kRows / 8; ++pass) {
     const int r = 8 * pass + (lane >> 3);
     const int grow = m0 + lrow0 + r;
-    const v4i v0 = *stage_at(stage, r, 2 * q2);
-    const v4i v1 = *stage_at(stage, r, 2 * q2 + 1);
+    const v4i v0 = corrected<CORR>(*stage_at(stage, r, 2 * q2), s_zp, s_ws, lrow0 + r, lcol);
+    const v4i v1 = corrected<CORR>(*stage_at(stage, r, 2 * q2 + 1), s_zp, s_ws, lrow0 + r, lcol + 4);
     if (grow >= M) continue;
     const float sa = s_sa[lrow0 + r];
     uint32_t h[8];

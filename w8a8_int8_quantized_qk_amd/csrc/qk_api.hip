@@ -285,4 +285,72 @@ int qk_moe_gemm_i8_scaled(int experts, int m, int n, int k, const int* expert_of
   return status_of(qk::launch_gemm_moe(g, expert_offsets, experts, stream));
 }
 
+static int quant_static_common(int m, int k, const void* x, int x_dtype, const float* scale,
+                               void* q, bool silu, bool fp8, hipStream_t stream) {
+  const int rc = check_rows(m, k, x, q, scale, x_dtype);
+  if (rc != QK_OK || m == 0 || k == 0) return rc;
+  if (silu && static_cast<long long>(k) * 2 > 0x7fffffffLL) return QK_ERR_UNSUPPORTED;
+  return status_of(qk::launch_quant_static(m, k, x, x_dtype, silu, fp8, scale,
+                                           static_cast<int8_t*>(q), stream));
+}
+
+int qk_quant_static(int m, int k, const void* x, int x_dtype, const float* scale, int8_t* q,
+                    hipStream_t stream) {
+  return quant_static_common(m, k, x, x_dtype, scale, q, false, false, stream);
+}
+
+int qk_silu_mul_quant_static(int m, int d, const void* h, int h_dtype, const float* scale,
+                             int8_t* q, hipStream_t stream) {
+  return quant_static_common(m, d, h, h_dtype, scale, q, true, false, stream);
+}
+
+int qk_quant_static_fp8(int m, int k, const void* x, int x_dtype, const float* scale, uint8_t* q,
+                        hipStream_t stream) {
+  return quant_static_common(m, k, x, x_dtype, scale, q, false, true, stream);
+}
+
+int qk_silu_mul_quant_static_fp8(int m, int d, const void* h, int h_dtype, const float* scale,
+                                 uint8_t* q, hipStream_t stream) {
+  return quant_static_common(m, d, h, h_dtype, scale, q, true, true, stream);
+}
+
+int qk_quant_per_token_asym(int m, int k, const void* x, int x_dtype, int8_t* q, float* scale,
+                            int32_t* zero_point, hipStream_t stream) {
+  const int rc = check_rows(m, k, x, q, scale, x_dtype);
+  if (rc != QK_OK) return rc;
+  if (m > 0 && !zero_point) return QK_ERR_INVALID_VALUE;
+  if (m == 0) return QK_OK;
+  return status_of(qk::launch_quant_rows_asym(m, k, x, x_dtype, q, scale, zero_point, stream));
+}
+
+int qk_weight_colsum(int k, int n, const int8_t* b, int b_layout, int32_t* wsum, hipStream_t stream) {
+  if (k < 0 || n < 0 || k > QK_MAX_K) return QK_ERR_INVALID_VALUE;
+  if (b_layout != QK_B_KN && b_layout != QK_B_NK) return QK_ERR_INVALID_VALUE;
+  if (n == 0) return QK_OK;
+  if (!wsum || (k > 0 && !b)) return QK_ERR_INVALID_VALUE;
+  return status_of(qk::launch_weight_colsum(k, n, b, b_layout, wsum, stream));
+}
+
+int qk_gemm_i8_asym(int m, int n, int k, const int8_t* a, const int32_t* zero_point,
+                    const int8_t* b, const int32_t* wsum, int32_t* c, const float* scale_a,
+                    const float* scale_b, float output_scale, void* out, int out_dtype,
+                    int b_layout, hipStream_t stream) {
+  if (m < 0 || n < 0 || k < 0 || k > QK_MAX_K_ASYM) return QK_ERR_INVALID_VALUE;
+  if (b_layout != QK_B_KN && b_layout != QK_B_NK) return QK_ERR_INVALID_VALUE;
+  if (k % 16 != 0) return QK_ERR_UNSUPPORTED;
+  if (m == 0 || n == 0) return QK_OK;
+  if (!c && !out) return QK_ERR_INVALID_VALUE;
+  if (!zero_point || !wsum) return QK_ERR_INVALID_VALUE;
+  if (out && out_dtype != QK_F32 && out_dtype != QK_BF16) return QK_ERR_INVALID_VALUE;
+  if (k > 0 && (!a || !b)) return QK_ERR_INVALID_VALUE;
+  if (out && (!scale_a || !scale_b)) return QK_ERR_INVALID_VALUE;
+  if (!aligned(a, 16) || !aligned(b, 16)) return QK_ERR_UNSUPPORTED;
+  if (c && !aligned(c, 4)) return QK_ERR_UNSUPPORTED;
+  if (out && !aligned(out, out_dtype == QK_BF16 ? 2 : 4)) return QK_ERR_UNSUPPORTED;
+  if (!qk::gemm_mfma_supported(m, n, k)) return QK_ERR_UNSUPPORTED;
+  qk::GemmArgs g{m, n, k, a, b, c, scale_a, scale_b, output_scale, out, out_dtype, b_layout,
+                 nullptr, 0};
+  return status_of(qk::launch_gemm_asym(g, zero_point, wsum, stream));
+}
+
 }  // extern "C"

@@ -56,6 +56,16 @@ hipError_t launch_quant_rows_fp8(int m, int k, const void* x, int dtype, uint8_t
                                  float scale_ub, hipStream_t stream);
 hipError_t launch_silu_quant_rows_fp8(int m, int d, const void* h, int dtype, uint8_t* q,
                                       float* scale, float scale_ub, hipStream_t stream);
+// Asymmetric per-token INT8 codes with zero points (quant.hip).
+hipError_t launch_quant_rows_asym(int m, int k, const void* x, int dtype, int8_t* q, float* scale,
+                                  int32_t* zp, hipStream_t stream);
+// Static (per-tensor) quantization with a device scalar scale, INT8 or FP8,
+// plain or silu-fused (quant_static.hip).
+hipError_t launch_quant_static(int m, int k, const void* x, int dtype, bool silu, bool fp8,
+                               const float* scale, int8_t* q, hipStream_t stream);
+// Column sums of an INT8 weight (quant_static.hip): wsum[j] = sum_t B(t, j).
+hipError_t launch_weight_colsum(int k, int n, const int8_t* b, int b_layout, int32_t* wsum,
+                                hipStream_t stream);
 
 // LDS-tiled INT8 MFMA GEMM with fused epilogue (gemm_mfma.hip).  Operands
 // are addressed with 32-bit offsets: m*k and n*k must stay below 2^32.
@@ -65,6 +75,10 @@ hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
 // offsets[e + 1]) of a (device array of experts + 1 ints) use weight
 // b + e * k * n and per-channel scales scale_b + e * n; one launch.
 int moe_max_experts();
+// The same kernel for asymmetric activations (gemm_mfma.hip): the epilogue
+// subtracts zp_a[row] * wsum[col] from the INT32 accumulators.
+hipError_t launch_gemm_asym(const GemmArgs& g, const int32_t* zp_a, const int32_t* wsum,
+                            hipStream_t stream);
 hipError_t launch_gemm_moe(const GemmArgs& g, const int* offsets, int experts, hipStream_t stream);
 
 // GEMMs whose waves multiply whole k slices (gemm_slice.hip): the FP8

@@ -1,12 +1,16 @@
 // Per-token dynamic quantization for gfx950, to INT8 or FP8 codes, plain and
-// fused with silu(gate) * up.
+// fused with silu(gate) * up, and asymmetric (zero-point) INT8 codes.
 //
 // Method ("kernels: fused silu_and_mul + dynamic per-token FP8 quantization",
 // Purpose and Algorithm; symmetric [-127, 127] codes from "Skill: Write an
 // INT8 Quantized Kernel", Inputs):
 //   INT8: scale = max(row absmax, 1e-12) / 127, code = clamp(rint(x / scale), -127, 127);
 //   FP8:  scale = min(max(row absmax, 1e-12) / 448, scale_ub if > 0),
-//         code = e4m3fn(x / scale), nearest even, saturating at +-448.
+//         code = e4m3fn(x / scale), nearest even, saturating at +-448;
+//   asymmetric INT8 ("Skill: Write an INT8 Quantized Kernel", Inputs: a
+//         nonzero zero point): lo = min(row min, 0), hi = max(row max, 0),
+//         scale = max(hi - lo, 1e-12) / 255, zp = clamp(rint(-lo / scale) -
+//         128, -128, 127), code = clamp(rint(x / scale) + zp, -128, 127).
 //
 // Rows of up to 128 16-byte units take one wave each (absmax by cross-lane
 // max steps only); rows of up to 2048 units take one workgroup of four waves
@@ -38,61 +42,75 @@ using qm::Elem;
 using qm::code_of;
 using qm::pack4;
 using qm::row_scale;
+using qm::silu_times;
 
-enum Fmt { kI8 = 0, kF8 = 1 };
+enum Fmt { kI8 = 0, kF8 = 1, kI8Asym = 2 };
 
-// the row's scale s and r = RN(1 / s)
+// Per-lane row statistics: the absmax (symmetric formats) or hi = max(x, 0)
+// and nlo = max(-x, 0) (asymmetric); all non-negative.
+struct Stats {
+  float a = 0.0f;
+  float b = 0.0f;
+};
 template <int FMT>
-__device__ __forceinline__ void scale_of(float amax, float scale_ub, float& s, float& r) {
-  if constexpr (FMT == kI8)
-    row_scale(amax, s, r);
+__device__ __forceinline__ void accumulate(Stats& st, float v) {
+  if constexpr (FMT == kI8Asym) {
+    st.a = __builtin_fmaxf(st.a, v);
+    st.b = __builtin_fmaxf(st.b, -v);
+  } else {
+    st.a = __builtin_fmaxf(st.a, __builtin_fabsf(v));
+  }
+}
+template <int FMT>
+__device__ __forceinline__ void wave_reduce(Stats& st) {
+  st.a = qm::wave_max_nonneg(st.a);
+  if constexpr (FMT == kI8Asym) st.b = qm::wave_max_nonneg(st.b);
+}
+template <int FMT, int kBlock>
+__device__ __forceinline__ void block_reduce(Stats& st) {
+  if constexpr (FMT == kI8Asym)
+    qm::block_max2<kBlock>(st.a, st.b);
   else
-    qm::row_scale_fp8(amax, scale_ub, s, r);
+    st.a = qm::block_max<kBlock>(st.a);
+}
+
+// The row's scale s, r = RN(1 / s), and (asymmetric) the zero point.
+struct RowQ {
+  float s, r, zp;
+};
+template <int FMT>
+__device__ __forceinline__ RowQ row_params(const Stats& st, float scale_ub) {
+  RowQ p{0.0f, 0.0f, 0.0f};
+  if constexpr (FMT == kI8)
+    row_scale(st.a, p.s, p.r);
+  else if constexpr (FMT == kF8)
+    qm::row_scale_fp8(st.a, scale_ub, p.s, p.r);
+  else
+    qm::row_scale_asym(st.a, st.b, p.s, p.r, p.zp);
+  return p;
 }
 
 // the code byte of one value
 template <int FMT>
-__device__ __forceinline__ int8_t code_byte(float x, float s, float r) {
+__device__ __forceinline__ int8_t code_byte(float x, const RowQ& p) {
   if constexpr (FMT == kI8) {
-    return static_cast<int8_t>(code_of(x, s, r));
+    return static_cast<int8_t>(code_of(x, p.s, p.r));
+  } else if constexpr (FMT == kI8Asym) {
+    return static_cast<int8_t>(qm::code_of_asym(x, p.s, p.r, p.zp));
   } else {
-    return static_cast<int8_t>(__builtin_amdgcn_cvt_pk_fp8_f32(qm::fp8_ratio(x, s, r), 0.0f, 0, false) & 0xff);
+    return static_cast<int8_t>(__builtin_amdgcn_cvt_pk_fp8_f32(qm::fp8_ratio(x, p.s, p.r), 0.0f, 0, false) & 0xff);
   }
+}
+
+// the row's outputs: scale, and the zero point for the asymmetric format
+template <int FMT>
+__device__ __forceinline__ void store_row_params(const RowQ& p, float* scale, int32_t* zp, size_t row) {
+  scale[row] = p.s;
+  if constexpr (FMT == kI8Asym) zp[row] = static_cast<int32_t>(p.zp);
 }
 
 constexpr int kBlock = 256;    // threads per workgroup
 constexpr int kMaxUnits = 8;   // 16-byte input units cached per lane
-
-// e^x in binary32 by a fixed sequence so that results are reproducible bit
-// for bit: x = n ln2 + r with n = rint(x / ln 2) and r reduced in two fused
-// steps (ln 2 split into a 16-bit head and a tail), e^r by the degree-7
-// Taylor polynomial in Horner form (coefficients: the binary32 values nearest
-// 1/j!), then the exact scaling by 2^n.  Inputs above 88 give +inf, below -87
-// give 0, so every finite result is a normal number.
-__device__ __forceinline__ float exp_fixed(float x) {
-  if (x > 88.0f) return __builtin_inff();
-  if (x < -87.0f) return 0.0f;
-  const float n = __builtin_rintf(x * 0x1.715476p+0f);
-  float r = __builtin_fmaf(-n, 0x1.62e400p-1f, x);
-  r = __builtin_fmaf(-n, 0x1.7f7d1cp-20f, r);
-  float p = 0x1.a01a02p-13f;                 // 1/7!
-  p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);  // 1/6!
-  p = __builtin_fmaf(p, r, 0x1.111112p-7f);   // 1/5!
-  p = __builtin_fmaf(p, r, 0x1.555556p-5f);   // 1/4!
-  p = __builtin_fmaf(p, r, 0x1.555556p-3f);   // 1/3!
-  p = __builtin_fmaf(p, r, 0.5f);             // 1/2!
-  p = __builtin_fmaf(p, r, 1.0f);             // 1/1!
-  p = __builtin_fmaf(p, r, 1.0f);             // 1/0!
-  return __builtin_amdgcn_ldexpf(p, static_cast<int>(n));
-}
-
-// silu(g) * u = (g / (1 + e^-g)) * u, each operation rounded once.
-__device__ __forceinline__ float silu_times(float g, float u) {
-  const float e = exp_fixed(-g);
-  const float t = 1.0f + e;
-  const float sg = g / t;  // IEEE division (correctly rounded build)
-  return sg * u;
-}
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
@@ -102,12 +120,14 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 // in the caches (measured on the prefill step: 0.4 us faster than
 // nontemporal stores, although the quantization alone is slower).
 template <int FMT, int P>
-__device__ __forceinline__ void store_codes(int8_t* dst, const float (&v)[P], float s, float r) {
+__device__ __forceinline__ void store_codes(int8_t* dst, const float (&v)[P], const RowQ& p) {
   uint32_t w[P / 4];
-  if constexpr (FMT == kI8) {
+  const float s = p.s, r = p.r;
+  if constexpr (FMT == kI8 || FMT == kI8Asym) {
     int c[P];
 #pragma unroll
-    for (int e = 0; e < P; ++e) c[e] = code_of(v[e], s, r);
+    for (int e = 0; e < P; ++e)
+      c[e] = FMT == kI8 ? code_of(v[e], s, r) : qm::code_of_asym(v[e], s, r, p.zp);
 #pragma unroll
     for (int i = 0; i < P / 4; ++i) w[i] = pack4(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
   } else {
@@ -153,7 +173,7 @@ template <int DT, bool SILU, int FMT, int UPL>
 __global__ __launch_bounds__(kBlock) void quant_rows_wave(const void* __restrict__ src,
                                                          int8_t* __restrict__ q,
                                                          float* __restrict__ scale, float scale_ub,
-                                                         int m, int k) {
+                                                         int32_t* __restrict__ zp, int m, int k) {
   using E = Elem<DT>;
   constexpr int P = E::kPerUnit;
   const int units = k / P;
@@ -164,26 +184,25 @@ __global__ __launch_bounds__(kBlock) void quant_rows_wave(const void* __restrict
       static_cast<const char*>(src) + row * static_cast<size_t>(SILU ? 2 : 1) * k * E::kBytes;
 
   float v[UPL][P];
-  float amax = 0.0f;
+  Stats st;
 #pragma unroll
   for (int j = 0; j < UPL; ++j) {
     const int u = lane + 64 * j;
     if (u < units) {
       unit_values<DT, SILU>(base, k, u, v[j]);
 #pragma unroll
-      for (int e = 0; e < P; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j][e]));
+      for (int e = 0; e < P; ++e) accumulate<FMT>(st, v[j][e]);
     }
   }
-  amax = qm::wave_max_nonneg(amax);
-  float s, r;
-  scale_of<FMT>(amax, scale_ub, s, r);
-  if (lane == 0) scale[row] = s;
+  wave_reduce<FMT>(st);
+  const RowQ p = row_params<FMT>(st, scale_ub);
+  if (lane == 0) store_row_params<FMT>(p, scale, zp, row);
 
   int8_t* qrow = q + row * static_cast<size_t>(k);
 #pragma unroll
   for (int j = 0; j < UPL; ++j) {
     const int u = lane + 64 * j;
-    if (u < units) store_codes<FMT, P>(qrow + static_cast<size_t>(u) * P, v[j], s, r);
+    if (u < units) store_codes<FMT, P>(qrow + static_cast<size_t>(u) * P, v[j], p);
   }
 }
 
@@ -197,7 +216,8 @@ template <int DT, bool SILU, int FMT, int UPT>
 __global__ __launch_bounds__(kBlock) void quant_rows_cached(const void* __restrict__ src,
                                                            int8_t* __restrict__ q,
                                                            float* __restrict__ scale,
-                                                           float scale_ub, int k) {
+                                                           float scale_ub, int32_t* __restrict__ zp,
+                                                           int k) {
   using E = Elem<DT>;
   constexpr int P = E::kPerUnit;
   const int units = k / P;
@@ -206,26 +226,25 @@ __global__ __launch_bounds__(kBlock) void quant_rows_cached(const void* __restri
       static_cast<const char*>(src) + row * static_cast<size_t>(SILU ? 2 : 1) * k * E::kBytes;
 
   float v[UPT][P];
-  float amax = 0.0f;
+  Stats st;
 #pragma unroll
   for (int j = 0; j < UPT; ++j) {
     const int u = threadIdx.x + j * kBlock;
     if (u < units) {
       unit_values<DT, SILU>(base, k, u, v[j]);
 #pragma unroll
-      for (int e = 0; e < P; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j][e]));
+      for (int e = 0; e < P; ++e) accumulate<FMT>(st, v[j][e]);
     }
   }
-  amax = qm::block_max<kBlock>(amax);
-  float s, r;
-  scale_of<FMT>(amax, scale_ub, s, r);
-  if (threadIdx.x == 0) scale[row] = s;
+  block_reduce<FMT, kBlock>(st);
+  const RowQ p = row_params<FMT>(st, scale_ub);
+  if (threadIdx.x == 0) store_row_params<FMT>(p, scale, zp, row);
 
   int8_t* qrow = q + row * static_cast<size_t>(k);
 #pragma unroll
   for (int j = 0; j < UPT; ++j) {
     const int u = threadIdx.x + j * kBlock;
-    if (u < units) store_codes<FMT, P>(qrow + static_cast<size_t>(u) * P, v[j], s, r);
+    if (u < units) store_codes<FMT, P>(qrow + static_cast<size_t>(u) * P, v[j], p);
   }
 }
 
@@ -235,7 +254,8 @@ template <int DT, bool SILU, int FMT>
 __global__ __launch_bounds__(kBlock) void quant_rows_twopass(const void* __restrict__ src,
                                                             int8_t* __restrict__ q,
                                                             float* __restrict__ scale,
-                                                            float scale_ub, int k) {
+                                                            float scale_ub, int32_t* __restrict__ zp,
+                                                            int k) {
   using E = Elem<DT>;
   const size_t row = blockIdx.x;
   const size_t first = row * static_cast<size_t>(SILU ? 2 : 1) * k;
@@ -244,19 +264,18 @@ __global__ __launch_bounds__(kBlock) void quant_rows_twopass(const void* __restr
     if constexpr (SILU) return silu_times(x, E::load(src, first + k + j));
     return x;
   };
-  float amax = 0.0f;
-  for (int j = threadIdx.x; j < k; j += kBlock) amax = __builtin_fmaxf(amax, __builtin_fabsf(value(j)));
-  amax = qm::block_max<kBlock>(amax);
-  float s, r;
-  scale_of<FMT>(amax, scale_ub, s, r);
-  if (threadIdx.x == 0) scale[row] = s;
+  Stats st;
+  for (int j = threadIdx.x; j < k; j += kBlock) accumulate<FMT>(st, value(j));
+  block_reduce<FMT, kBlock>(st);
+  const RowQ p = row_params<FMT>(st, scale_ub);
+  if (threadIdx.x == 0) store_row_params<FMT>(p, scale, zp, row);
   int8_t* qrow = q + row * static_cast<size_t>(k);
-  for (int j = threadIdx.x; j < k; j += kBlock) qrow[j] = code_byte<FMT>(value(j), s, r);
+  for (int j = threadIdx.x; j < k; j += kBlock) qrow[j] = code_byte<FMT>(value(j), p);
 }
 
 template <int DT, bool SILU, int FMT>
 hipError_t dispatch(int m, int k, const void* src, int8_t* q, float* scale, float scale_ub,
-                    hipStream_t stream) {
+                    int32_t* zp, hipStream_t stream) {
   using E = Elem<DT>;
   const bool aligned = (reinterpret_cast<uintptr_t>(src) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(q) % E::kPerUnit == 0) &&
@@ -266,35 +285,35 @@ hipError_t dispatch(int m, int k, const void* src, int8_t* q, float* scale, floa
     const dim3 grid((static_cast<unsigned>(m) + kBlock / 64 - 1) / (kBlock / 64));
     if (units <= 64)
       return launch(quant_rows_wave<DT, SILU, FMT, 1>, grid, dim3(kBlock), 0, stream, src, q, scale,
-                    scale_ub, m, k);
+                    scale_ub, zp, m, k);
     return launch(quant_rows_wave<DT, SILU, FMT, 2>, grid, dim3(kBlock), 0, stream, src, q, scale,
-                  scale_ub, m, k);
+                  scale_ub, zp, m, k);
   }
   if (aligned && units <= kBlock * kMaxUnits) {
     const dim3 grid(m);
     if (units <= kBlock)
       return launch(quant_rows_cached<DT, SILU, FMT, 1>, grid, dim3(kBlock), 0, stream, src, q,
-                    scale, scale_ub, k);
+                    scale, scale_ub, zp, k);
     if (units <= kBlock * 2)
       return launch(quant_rows_cached<DT, SILU, FMT, 2>, grid, dim3(kBlock), 0, stream, src, q,
-                    scale, scale_ub, k);
+                    scale, scale_ub, zp, k);
     if (units <= kBlock * 4)
       return launch(quant_rows_cached<DT, SILU, FMT, 4>, grid, dim3(kBlock), 0, stream, src, q,
-                    scale, scale_ub, k);
+                    scale, scale_ub, zp, k);
     return launch(quant_rows_cached<DT, SILU, FMT, 8>, grid, dim3(kBlock), 0, stream, src, q,
-                  scale, scale_ub, k);
+                  scale, scale_ub, zp, k);
   }
   return launch(quant_rows_twopass<DT, SILU, FMT>, dim3(m), dim3(kBlock), 0, stream, src, q, scale,
-                scale_ub, k);
+                scale_ub, zp, k);
 }
 
 template <bool SILU, int FMT>
 hipError_t dispatch_dtype(int m, int k, const void* src, int dtype, int8_t* q, float* scale,
-                          float scale_ub, hipStream_t stream) {
+                          float scale_ub, int32_t* zp, hipStream_t stream) {
   switch (dtype) {
-    case QK_F32: return dispatch<QK_F32, SILU, FMT>(m, k, src, q, scale, scale_ub, stream);
-    case QK_BF16: return dispatch<QK_BF16, SILU, FMT>(m, k, src, q, scale, scale_ub, stream);
-    case QK_F16: return dispatch<QK_F16, SILU, FMT>(m, k, src, q, scale, scale_ub, stream);
+    case QK_F32: return dispatch<QK_F32, SILU, FMT>(m, k, src, q, scale, scale_ub, zp, stream);
+    case QK_BF16: return dispatch<QK_BF16, SILU, FMT>(m, k, src, q, scale, scale_ub, zp, stream);
+    case QK_F16: return dispatch<QK_F16, SILU, FMT>(m, k, src, q, scale, scale_ub, zp, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -303,24 +322,29 @@ hipError_t dispatch_dtype(int m, int k, const void* src, int dtype, int8_t* q, f
 
 hipError_t launch_quant_rows(int m, int k, const void* x, int dtype, int8_t* q, float* scale,
                              hipStream_t stream) {
-  return dispatch_dtype<false, kI8>(m, k, x, dtype, q, scale, 0.0f, stream);
+  return dispatch_dtype<false, kI8>(m, k, x, dtype, q, scale, 0.0f, nullptr, stream);
 }
 
 hipError_t launch_silu_quant_rows(int m, int d, const void* h, int dtype, int8_t* q,
                                   float* scale, hipStream_t stream) {
-  return dispatch_dtype<true, kI8>(m, d, h, dtype, q, scale, 0.0f, stream);
+  return dispatch_dtype<true, kI8>(m, d, h, dtype, q, scale, 0.0f, nullptr, stream);
 }
 
 hipError_t launch_quant_rows_fp8(int m, int k, const void* x, int dtype, uint8_t* q, float* scale,
                                  float scale_ub, hipStream_t stream) {
   return dispatch_dtype<false, kF8>(m, k, x, dtype, reinterpret_cast<int8_t*>(q), scale, scale_ub,
-                                    stream);
+                                    nullptr, stream);
 }
 
 hipError_t launch_silu_quant_rows_fp8(int m, int d, const void* h, int dtype, uint8_t* q,
                                       float* scale, float scale_ub, hipStream_t stream) {
   return dispatch_dtype<true, kF8>(m, d, h, dtype, reinterpret_cast<int8_t*>(q), scale, scale_ub,
-                                   stream);
+                                   nullptr, stream);
+}
+
+hipError_t launch_quant_rows_asym(int m, int k, const void* x, int dtype, int8_t* q, float* scale,
+                                  int32_t* zp, hipStream_t stream) {
+  return dispatch_dtype<false, kI8Asym>(m, k, x, dtype, q, scale, 0.0f, zp, stream);
 }
 
 }  // namespace qk

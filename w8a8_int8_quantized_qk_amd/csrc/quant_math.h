@@ -91,6 +91,37 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
          ((static_cast<uint32_t>(c) & 0xffu) << 16) | (static_cast<uint32_t>(d) << 24);
 }
 
+// e^x in binary32 by a fixed sequence so that results are reproducible bit
+// for bit: x = n ln2 + r with n = rint(x / ln 2) and r reduced in two fused
+// steps (ln 2 split into a 16-bit head and a tail), e^r by the degree-7
+// Taylor polynomial in Horner form (coefficients: the binary32 values nearest
+// 1/j!), then the exact scaling by 2^n.  Inputs above 88 give +inf, below -87
+// give 0, so every finite result is a normal number.
+__device__ __forceinline__ float exp_fixed(float x) {
+  if (x > 88.0f) return __builtin_inff();
+  if (x < -87.0f) return 0.0f;
+  const float n = __builtin_rintf(x * 0x1.715476p+0f);
+  float r = __builtin_fmaf(-n, 0x1.62e400p-1f, x);
+  r = __builtin_fmaf(-n, 0x1.7f7d1cp-20f, r);
+  float p = 0x1.a01a02p-13f;                 // 1/7!
+  p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);  // 1/6!
+  p = __builtin_fmaf(p, r, 0x1.111112p-7f);   // 1/5!
+  p = __builtin_fmaf(p, r, 0x1.555556p-5f);   // 1/4!
+  p = __builtin_fmaf(p, r, 0x1.555556p-3f);   // 1/3!
+  p = __builtin_fmaf(p, r, 0.5f);             // 1/2!
+  p = __builtin_fmaf(p, r, 1.0f);             // 1/1!
+  p = __builtin_fmaf(p, r, 1.0f);             // 1/0!
+  return __builtin_amdgcn_ldexpf(p, static_cast<int>(n));
+}
+
+// silu(g) * u = (g / (1 + e^-g)) * u, each operation rounded once.
+__device__ __forceinline__ float silu_times(float g, float u) {
+  const float e = exp_fixed(-g);
+  const float t = 1.0f + e;
+  const float sg = g / t;  // IEEE division (correctly rounded build)
+  return sg * u;
+}
+
 // Max over the 64 lanes of a wave of non-negative binary32 values (|x|),
 // left in every lane.  For x >= 0 the unsigned order of the bit patterns is
 // the numeric order, so the max runs on integers (no float canonicalizing):
@@ -122,6 +153,62 @@ __device__ __forceinline__ float block_max(float v) {
 #pragma unroll
   for (int w = 1; w < kBlock / 64; ++w) r = max_u32(r, part[w]);
   return __uint_as_float(r);
+}
+
+// Workgroup-wide max of two non-negative values at once (one barrier).
+template <int kBlock>
+__device__ __forceinline__ void block_max2(float& a, float& b) {
+  __shared__ uint32_t part2[2][kBlock / 64];
+  a = wave_max_nonneg(a);
+  b = wave_max_nonneg(b);
+  if ((threadIdx.x & 63) == 0) {
+    part2[0][threadIdx.x >> 6] = __float_as_uint(a);
+    part2[1][threadIdx.x >> 6] = __float_as_uint(b);
+  }
+  __syncthreads();
+  uint32_t ra = part2[0][0], rb = part2[1][0];
+#pragma unroll
+  for (int w = 1; w < kBlock / 64; ++w) {
+    ra = max_u32(ra, part2[0][w]);
+    rb = max_u32(rb, part2[1][w]);
+  }
+  a = __uint_as_float(ra);
+  b = __uint_as_float(rb);
+}
+
+// clamp(rint(x / s), -127, 127) for a caller-given scale s, which may be
+// small enough for x * r to overflow: the first product is clamped to +-256
+// (every quotient that can round inside [-127, 127] is unchanged; a clamped
+// one saturates like the true quotient), which keeps the correction finite.
+__device__ __forceinline__ int code_of_bounded(float x, float s, float r) {
+  float y = x * r;
+  y = __builtin_amdgcn_fmed3f(y, -256.0f, 256.0f);
+  const float e = __builtin_fmaf(-y, s, x);
+  float q = __builtin_fmaf(e, r, y);
+  q = __builtin_rintf(q);
+  q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
+  return static_cast<int>(q);
+}
+
+// Asymmetric codes: clamp(rint(x / s) + zp, -128, 127) with the exact
+// quotient (|x / s| <= 255 by construction of s, so no overflow).
+__device__ __forceinline__ int code_of_asym(float x, float s, float r, float zp) {
+  const float y = x * r;
+  const float e = __builtin_fmaf(-y, s, x);
+  float q = __builtin_fmaf(e, r, y);
+  q = __builtin_rintf(q) + zp;
+  q = __builtin_fminf(__builtin_fmaxf(q, -128.0f), 127.0f);
+  return static_cast<int>(q);
+}
+
+// Asymmetric row parameters from hi = max(row max, 0) and nlo = -min(row
+// min, 0): s = max(hi + nlo, 1e-12f) / 255 (= hi - lo), r = RN(1 / s),
+// zp = clamp(rint(nlo / s) - 128, -128, 127), IEEE divisions (once per row).
+__device__ __forceinline__ void row_scale_asym(float hi, float nlo, float& s, float& r, float& zp) {
+  s = __builtin_fmaxf(hi + nlo, 1e-12f) / 255.0f;
+  r = 1.0f / s;
+  zp = __builtin_rintf(nlo / s) - 128.0f;
+  zp = __builtin_fminf(__builtin_fmaxf(zp, -128.0f), 127.0f);
 }
 
 // s = max(amax, 1e-12f) / 127 (correctly rounded) and r = RN(1 / s).  The

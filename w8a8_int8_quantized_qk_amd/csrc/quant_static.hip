@@ -1,0 +1,191 @@
+// Static (per-tensor) quantization and weight column sums for gfx950.
+//
+// Static scale ("kernels: fused silu_and_mul + dynamic per-token FP8
+// quantization", Purpose: silu_and_mul_quant quantizes with one
+// pre-calibrated scale for the whole tensor):
+//   INT8: code = clamp(rint(x / scale), -127, 127);   FP8: code = e4m3fn(x / scale)
+// optionally of silu(gate) * up.  No row reduction, so the kernel streams:
+// each thread converts 16-byte units (a row's units are contiguous), reading
+// the input once and writing the codes once.  The scale comes from device
+// memory (a calibration result need not visit the host); every thread forms
+// r = RN(1 / scale) itself, and the exact quotient by the same correction as
+// the dynamic kernels.
+//
+// Weight column sums, wsum[j] = sum_t B(t, j), once per weight: the
+// zero-point correction of the asymmetric GEMM.
+#include "quant_math.h"
+
+namespace qk {
+namespace {
+
+using qm::Elem;
+using qm::silu_times;
+
+constexpr int kBlock = 256;
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+template <bool FP8>
+__device__ __forceinline__ uint32_t codes4(float a, float b, float c, float d, float s, float r) {
+  if constexpr (FP8) {
+    return qm::pack4_fp8(qm::fp8_ratio(a, s, r), qm::fp8_ratio(b, s, r), qm::fp8_ratio(c, s, r),
+                         qm::fp8_ratio(d, s, r));
+  } else {
+    return qm::pack4(qm::code_of_bounded(a, s, r), qm::code_of_bounded(b, s, r),
+                     qm::code_of_bounded(c, s, r), qm::code_of_bounded(d, s, r));
+  }
+}
+
+// One thread per 16-byte unit of P values (rows of k / P units; for SILU the
+// up half of row i starts k elements after its gate half).
+template <int DT, bool SILU, bool FP8>
+__global__ __launch_bounds__(kBlock) void quant_static_units(const void* __restrict__ src,
+                                                             int8_t* __restrict__ q,
+                                                             const float* __restrict__ scale,
+                                                             long long units, int units_per_row,
+                                                             int k) {
+  using E = Elem<DT>;
+  constexpr int P = E::kPerUnit;
+  const float s = *scale;
+  const float r = 1.0f / s;
+  for (long long u = static_cast<long long>(blockIdx.x) * kBlock + threadIdx.x; u < units;
+       u += static_cast<long long>(gridDim.x) * kBlock) {
+    const long long row = u / units_per_row;
+    const int cu = static_cast<int>(u - row * units_per_row);
+    const char* base =
+        static_cast<const char*>(src) + row * static_cast<long long>(SILU ? 2 : 1) * k * E::kBytes;
+    float v[P];
+    const v4u raw = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(base + cu * 16));
+    E::unpack(make_uint4(raw.x, raw.y, raw.z, raw.w), v);
+    if constexpr (SILU) {
+      const v4u rup = __builtin_nontemporal_load(
+          reinterpret_cast<const v4u*>(base + static_cast<long long>(k) * E::kBytes + cu * 16));
+      float up[P];
+      E::unpack(make_uint4(rup.x, rup.y, rup.z, rup.w), up);
+#pragma unroll
+      for (int e = 0; e < P; ++e) v[e] = silu_times(v[e], up[e]);
+    }
+    int8_t* dst = q + row * k + static_cast<long long>(cu) * P;
+    if constexpr (P == 8) {
+      *reinterpret_cast<v2u*>(dst) =
+          v2u{codes4<FP8>(v[0], v[1], v[2], v[3], s, r), codes4<FP8>(v[4], v[5], v[6], v[7], s, r)};
+    } else {
+      *reinterpret_cast<uint32_t*>(dst) = codes4<FP8>(v[0], v[1], v[2], v[3], s, r);
+    }
+  }
+}
+
+// Any k or alignment: one thread per element.
+template <int DT, bool SILU, bool FP8>
+__global__ __launch_bounds__(kBlock) void quant_static_elems(const void* __restrict__ src,
+                                                             int8_t* __restrict__ q,
+                                                             const float* __restrict__ scale,
+                                                             long long count, int k) {
+  using E = Elem<DT>;
+  const float s = *scale;
+  const float r = 1.0f / s;
+  for (long long i = static_cast<long long>(blockIdx.x) * kBlock + threadIdx.x; i < count;
+       i += static_cast<long long>(gridDim.x) * kBlock) {
+    const long long row = i / k;
+    const long long j = i - row * k;
+    const long long first = row * static_cast<long long>(SILU ? 2 : 1) * k;
+    float x = E::load(src, first + j);
+    if constexpr (SILU) x = silu_times(x, E::load(src, first + k + j));
+    if constexpr (FP8) {
+      q[i] = static_cast<int8_t>(
+          __builtin_amdgcn_cvt_pk_fp8_f32(qm::fp8_ratio(x, s, r), 0.0f, 0, false) & 0xff);
+    } else {
+      q[i] = static_cast<int8_t>(qm::code_of_bounded(x, s, r));
+    }
+  }
+}
+
+unsigned grid_for(long long items) {
+  const long long blocks = (items + kBlock - 1) / kBlock;
+  return static_cast<unsigned>(blocks < 65536 ? (blocks > 0 ? blocks : 1) : 65536);
+}
+
+template <int DT, bool SILU, bool FP8>
+hipError_t dispatch_static(int m, int k, const void* src, const float* scale, int8_t* q,
+                           hipStream_t stream) {
+  using E = Elem<DT>;
+  const bool aligned = reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(q) % E::kPerUnit == 0 && k % E::kPerUnit == 0;
+  if (aligned) {
+    const int upr = k / E::kPerUnit;
+    const long long units = static_cast<long long>(m) * upr;
+    return launch(quant_static_units<DT, SILU, FP8>, dim3(grid_for(units)), dim3(kBlock), 0, stream,
+                  src, q, scale, units, upr, k);
+  }
+  const long long count = static_cast<long long>(m) * k;
+  return launch(quant_static_elems<DT, SILU, FP8>, dim3(grid_for(count)), dim3(kBlock), 0, stream,
+                src, q, scale, count, k);
+}
+
+template <bool SILU, bool FP8>
+hipError_t static_dtype(int m, int k, const void* src, int dtype, const float* scale, int8_t* q,
+                        hipStream_t stream) {
+  switch (dtype) {
+    case QK_F32: return dispatch_static<QK_F32, SILU, FP8>(m, k, src, scale, q, stream);
+    case QK_BF16: return dispatch_static<QK_BF16, SILU, FP8>(m, k, src, scale, q, stream);
+    case QK_F16: return dispatch_static<QK_F16, SILU, FP8>(m, k, src, scale, q, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// [K][N] weight: a workgroup sums 64 columns, thread (c, g) the rows
+// t = g, g + 4, ... of column c (a wave reads 64 consecutive bytes of a row),
+// then the four partial sums of each column are added through LDS.
+__global__ __launch_bounds__(kBlock) void colsum_kn(const int8_t* __restrict__ b, int k, int n,
+                                                    int32_t* __restrict__ wsum) {
+  __shared__ int part[kBlock / 64][64];
+  const int c = threadIdx.x & 63;
+  const int g = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + c;
+  int acc = 0;
+  if (j < n)
+    for (int t = g; t < k; t += kBlock / 64) acc += b[static_cast<size_t>(t) * n + j];
+  part[g][c] = acc;
+  __syncthreads();
+  if (g == 0 && j < n) {
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) total += part[w][c];
+    wsum[j] = total;
+  }
+}
+__global__ __launch_bounds__(kBlock) void colsum_nk(const int8_t* __restrict__ b, int k, int n,
+                                                    int32_t* __restrict__ wsum) {
+  const int j = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (j >= n) return;  // whole waves leave
+  const int8_t* row = b + static_cast<size_t>(j) * k;
+  int acc = 0;
+  for (int t = lane; t < k; t += 64) acc += row[t];
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) acc += __shfl_xor(acc, d);
+  if (lane == 0) wsum[j] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_quant_static(int m, int k, const void* x, int dtype, bool silu, bool fp8,
+                               const float* scale, int8_t* q, hipStream_t stream) {
+  if (silu) {
+    return fp8 ? static_dtype<true, true>(m, k, x, dtype, scale, q, stream)
+               : static_dtype<true, false>(m, k, x, dtype, scale, q, stream);
+  }
+  return fp8 ? static_dtype<false, true>(m, k, x, dtype, scale, q, stream)
+             : static_dtype<false, false>(m, k, x, dtype, scale, q, stream);
+}
+
+hipError_t launch_weight_colsum(int k, int n, const int8_t* b, int b_layout, int32_t* wsum,
+                                hipStream_t stream) {
+  if (b_layout == QK_B_KN)
+    return launch(colsum_kn, dim3((n + 63) / 64), dim3(kBlock), 0, stream, b, k, n, wsum);
+  return launch(colsum_nk, dim3((n + kBlock / 64 - 1) / (kBlock / 64)), dim3(kBlock), 0, stream, b,
+                k, n, wsum);
+}
+
+}  // namespace qk
