@@ -94,7 +94,7 @@ __device__ __forceinline__ RowQ row_params(const Stats& st, float scale_ub) {
 template <int FMT>
 __device__ __forceinline__ int8_t code_byte(float x, const RowQ& p) {
   if constexpr (FMT == kI8) {
-    return static_cast<int8_t>(code_of(x, p.s, p.r));
+    return static_cast<int8_t>(qm::code_word_dynamic(x, p.s, p.r) & 0xffu);
   } else if constexpr (FMT == kI8Asym) {
     return static_cast<int8_t>(qm::code_of_asym(x, p.s, p.r, p.zp));
   } else {
@@ -123,11 +123,17 @@ template <int FMT, int P>
 __device__ __forceinline__ void store_codes(int8_t* dst, const float (&v)[P], const RowQ& p) {
   uint32_t w[P / 4];
   const float s = p.s, r = p.r;
-  if constexpr (FMT == kI8 || FMT == kI8Asym) {
+  if constexpr (FMT == kI8) {
+    uint32_t c[P];
+#pragma unroll
+    for (int e = 0; e < P; ++e) c[e] = qm::code_word_dynamic(v[e], s, r);
+#pragma unroll
+    for (int i = 0; i < P / 4; ++i)
+      w[i] = qm::pack4_low_bytes(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
+  } else if constexpr (FMT == kI8Asym) {
     int c[P];
 #pragma unroll
-    for (int e = 0; e < P; ++e)
-      c[e] = FMT == kI8 ? code_of(v[e], s, r) : qm::code_of_asym(v[e], s, r, p.zp);
+    for (int e = 0; e < P; ++e) c[e] = qm::code_of_asym(v[e], s, r, p.zp);
 #pragma unroll
     for (int i = 0; i < P / 4; ++i) w[i] = pack4(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
   } else {

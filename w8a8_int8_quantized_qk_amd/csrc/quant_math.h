@@ -86,6 +86,28 @@ __device__ __forceinline__ int code_of(float x, float s, float r) {
   return static_cast<int>(q);
 }
 
+// The code of x / s for a row's own dynamic scale, as the low byte of the
+// returned word.  The quotient is exact (as in code_of); adding 1.5 * 2^23
+// rounds it to an integer, ties to even (the sum's unit in the last place is
+// 1, and 1.5 * 2^23 is even), and leaves that integer in the low mantissa
+// bits: the word is 0x4B400000 + code, whose low byte is the code's two's
+// complement byte.  No clamp is needed: s is the correctly rounded
+// max(amax, 1e-12) / 127, so |x / s| <= 127 (1 + 2^-23) for every |x| <=
+// amax, which rounds to at most 127.
+__device__ __forceinline__ uint32_t code_word_dynamic(float x, float s, float r) {
+  const float y = x * r;
+  const float e = __builtin_fmaf(-y, s, x);
+  const float q = __builtin_fmaf(e, r, y);
+  return __float_as_uint(q + 12582912.0f);
+}
+
+// Four code words' low bytes packed little-endian (a in byte 0).
+__device__ __forceinline__ uint32_t pack4_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // bytes: a0 b0 0 0
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x04000c0cu);  // bytes: 0 0 c0 d0
+  return ab | cd;
+}
+
 __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
   return (static_cast<uint32_t>(a) & 0xffu) | ((static_cast<uint32_t>(b) & 0xffu) << 8) |
          ((static_cast<uint32_t>(c) & 0xffu) << 16) | (static_cast<uint32_t>(d) << 24);
