@@ -45,6 +45,12 @@ FP8_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_fp8_prefill_outliers_traffic
                [os.path.join(CSRC, f) for f in ("gemm_slice.hip", "gemm_tile.h", "lds_dma.h")])
 GROUPED_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_grouped128_prefill_outliers_traffic.txt"),
                    [os.path.join(CSRC, f) for f in ("gemm_slice.hip", "gemm_tile.h", "lds_dma.h")])
+MOE_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_moe_up_traffic.txt"),
+               [os.path.join(CSRC, f) for f in ("gemm_mfma.hip", "gemm_tile.h", "lds_dma.h")])
+ASYM_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_asym_prefill_outliers_traffic.txt"),
+                [os.path.join(CSRC, f) for f in ("gemm_mfma.hip", "gemm_tile.h", "lds_dma.h")])
+STATIC_TRAFFIC = (os.path.join(ROOT, "profiles", "quant_static_prefill_outliers_traffic.txt"),
+                  [os.path.join(CSRC, f) for f in ("quant_static.hip", "quant_math.h")])
 
 
 def _args():
@@ -63,6 +69,8 @@ def _args():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8 layer at the prefill shape")
     p.add_argument("--no-moe", action="store_true", help="skip the MoE grouped GEMM")
+    p.add_argument("--moe-per-expert", action="store_true",
+                   help="also time the MoE work as one plain GEMM launch per expert")
     p.add_argument("--no-static-asym", action="store_true",
                    help="skip the static and asymmetric variants")
     p.add_argument("--no-grouped", action="store_true",
@@ -391,13 +399,15 @@ def main():
                              "roofline": {"bound": "hbm", "achieved": round(qbytes / (st_ms * 1e-3) / 1e9, 1),
                                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                           "frac": round(qbytes / (st_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                          "traffic": None, "algorithmic_bytes_per_launch": qbytes}},
+                                          "traffic": _traffic_from_profile(STATIC_TRAFFIC),
+                                          "algorithmic_bytes_per_launch": qbytes}},
             "asym_quant": {"us": round(aq_ms * 1e3, 3), "unit": "GB/s",
                            "value": round((qbytes + 8 * m) / (aq_ms * 1e-3) / 1e9, 1)},
             "asym_gemm": {"us": round(ag_ms * 1e3, 3), "unit": "TOPS", "value": round(agt, 2),
                           "roofline": {"bound": "mfma", "kernel": "gemm_i8_asym_kernel",
                                        "achieved": round(agt, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
-                                       "frac": round(agt / INT8_PEAK_TOPS, 4), "traffic": None,
+                                       "frac": round(agt / INT8_PEAK_TOPS, 4),
+                                       "traffic": _traffic_from_profile(ASYM_TRAFFIC),
                                        "avg_launch_us": round(ag_ms * 1e3, 3),
                                        "algorithmic_ops_per_launch": aops}},
         }
@@ -436,7 +446,9 @@ def main():
         msteps = max(4, args.steps // 10)
         mstep_ms, _ = timed_replays([(lambda bs=b: mstep(bs)) for b in msets], msteps, 2)
         mgemm_ms, _ = timed_replays([(lambda bs=b: mgemm(bs)) for b in msets], msteps, 2)
-        mper_ms, _ = timed_replays([(lambda bs=b: per_expert(bs)) for b in msets], msteps, 2)
+        mper_ms = None
+        if args.moe_per_expert:  # launches the plain GEMM at the experts' shapes
+            mper_ms, _ = timed_replays([(lambda bs=b: per_expert(bs)) for b in msets], msteps, 2)
         mops = 2.0 * mrows * mn * mk
         mt = mops / (mgemm_ms * 1e-3) / 1e12
         result["moe_up"] = {
@@ -446,10 +458,10 @@ def main():
             "value": round(mops / (mstep_ms * 1e-3) / 1e12, 2), "unit": "TOPS",
             "ms_per_step": round(mstep_ms, 5),
             "step": "qk_quant_per_token + qk_moe_gemm_i8_scaled (one launch for all experts)",
-            "one_launch_per_expert_us": round(mper_ms * 1e3, 2),
+            "one_launch_per_expert_us": round(mper_ms * 1e3, 2) if mper_ms is not None else None,
             "roofline": {"bound": "mfma", "kernel": "gemm_i8_moe_kernel",
                          "achieved": round(mt, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
-                         "frac": round(mt / INT8_PEAK_TOPS, 4), "traffic": None,
+                         "frac": round(mt / INT8_PEAK_TOPS, 4), "traffic": _traffic_from_profile(MOE_TRAFFIC),
                          "avg_launch_us": round(mgemm_ms * 1e3, 3),
                          "algorithmic_ops_per_launch": mops},
         }

@@ -101,13 +101,28 @@ def test_asym_quant_edge_rows(dtype, k):
 
 
 @pytest.mark.parametrize("layout", ["kn", "nk"])
-@pytest.mark.parametrize("k,n", [(16, 3), (4096, 14336), (1000 * 16, 37)])
+@pytest.mark.parametrize("k,n", [(16, 3), (4096, 14336), (1000 * 16, 37), (1300, 260), (513, 1024),
+                                 (1, 4), (65535, 8)])
 def test_weight_colsum(layout, k, n):
     rng = np.random.default_rng(_seed("cs", layout, k, n))
     w = rng.integers(-128, 128, (k, n), dtype=np.int8)
     wd = torch.from_numpy(w if layout == "kn" else np.ascontiguousarray(w.T)).to(DEV)
     assert_equal_exact(host(qk.weight_colsum(wd, layout)), w.astype(np.int64).sum(0).astype(np.int32),
                        f"colsum {layout} {k}x{n}")
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_weight_colsum_unaligned(offset):
+    """A weight whose first byte is not 4-byte aligned (n a multiple of 4)."""
+    k, n = 700, 520
+    rng = np.random.default_rng(_seed("cs-unaligned", offset))
+    w = rng.integers(-128, 128, (k, n), dtype=np.int8)
+    flat = torch.zeros(k * n + 16, dtype=torch.int8, device=DEV)
+    wd = flat[offset:offset + k * n].view(k, n)
+    wd.copy_(torch.from_numpy(w).to(DEV))
+    assert wd.data_ptr() % 4 == offset
+    assert_equal_exact(host(qk.weight_colsum(wd, "kn")), w.astype(np.int64).sum(0).astype(np.int32),
+                       f"colsum unaligned +{offset}")
 
 
 @pytest.mark.parametrize("m,n,k,layout", [

@@ -134,25 +134,49 @@ hipError_t static_dtype(int m, int k, const void* src, int dtype, const float* s
   }
 }
 
-// [K][N] weight: a workgroup sums 64 columns, thread (c, g) the rows
-// t = g, g + 4, ... of column c (a wave reads 64 consecutive bytes of a row),
-// then the four partial sums of each column are added through LDS.
+// [K][N] weight: workgroup (x, y) sums rows [y * kColsumRows, ...) of
+// columns [256 x, 256 x + 256): each lane reads 4 consecutive columns of a
+// row as one dword (a wave reads 1 KB of a row), the four waves take every
+// fourth row, their partial sums meet in LDS, and one integer atomic per
+// column adds the workgroup's sum into wsum (zeroed first).  Integer
+// addition makes the order irrelevant: the result is exact.
+constexpr int kColsumRows = 512;
+__global__ __launch_bounds__(kBlock) void colsum_zero(int32_t* __restrict__ wsum, int n) {
+  const int j = blockIdx.x * kBlock + threadIdx.x;
+  if (j < n) wsum[j] = 0;
+}
 __global__ __launch_bounds__(kBlock) void colsum_kn(const int8_t* __restrict__ b, int k, int n,
                                                     int32_t* __restrict__ wsum) {
-  __shared__ int part[kBlock / 64][64];
-  const int c = threadIdx.x & 63;
-  const int g = threadIdx.x >> 6;
-  const int j = blockIdx.x * 64 + c;
-  int acc = 0;
-  if (j < n)
-    for (int t = g; t < k; t += kBlock / 64) acc += b[static_cast<size_t>(t) * n + j];
-  part[g][c] = acc;
-  __syncthreads();
-  if (g == 0 && j < n) {
-    int total = 0;
+  __shared__ int part[kBlock / 64][256];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int j0 = blockIdx.x * 256 + 4 * lane;  // this lane's first column
+  const int t0 = blockIdx.y * kColsumRows;
+  const int t1 = min(t0 + kColsumRows, k);
+  int acc[4] = {0, 0, 0, 0};
+  if (j0 + 3 < n && ((n | static_cast<int>(reinterpret_cast<uintptr_t>(b))) & 3) == 0) {
+    for (int t = t0 + w; t < t1; t += kBlock / 64) {
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(b + static_cast<size_t>(t) * n + j0);
 #pragma unroll
-    for (int w = 0; w < kBlock / 64; ++w) total += part[w][c];
-    wsum[j] = total;
+      for (int e = 0; e < 4; ++e) acc[e] += static_cast<int8_t>(v >> (8 * e));
+    }
+  } else {
+    for (int t = t0 + w; t < t1; t += kBlock / 64)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j0 + e < n) acc[e] += b[static_cast<size_t>(t) * n + j0 + e];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) part[w][4 * lane + e] = acc[e];
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      int total = 0;
+#pragma unroll
+      for (int q = 0; q < kBlock / 64; ++q) total += part[q][4 * lane + e];
+      if (j0 + e < n) atomicAdd(wsum + j0 + e, total);
+    }
   }
 }
 __global__ __launch_bounds__(kBlock) void colsum_nk(const int8_t* __restrict__ b, int k, int n,
@@ -182,8 +206,13 @@ hipError_t launch_quant_static(int m, int k, const void* x, int dtype, bool silu
 
 hipError_t launch_weight_colsum(int k, int n, const int8_t* b, int b_layout, int32_t* wsum,
                                 hipStream_t stream) {
-  if (b_layout == QK_B_KN)
-    return launch(colsum_kn, dim3((n + 63) / 64), dim3(kBlock), 0, stream, b, k, n, wsum);
+  if (b_layout == QK_B_KN) {
+    hipError_t e = launch(colsum_zero, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, stream, wsum, n);
+    if (e != hipSuccess) return e;
+    if (k == 0) return hipSuccess;
+    return launch(colsum_kn, dim3((n + 255) / 256, (k + kColsumRows - 1) / kColsumRows), dim3(kBlock),
+                  0, stream, b, k, n, wsum);
+  }
   return launch(colsum_nk, dim3((n + kBlock / 64 - 1) / (kBlock / 64)), dim3(kBlock), 0, stream, b,
                 k, n, wsum);
 }
