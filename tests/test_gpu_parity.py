@@ -209,6 +209,18 @@ def test_gemm_decode_kernel(m, n, k, out_dtype):
     _run_gemm_case(m, n, k, "kn", "gemv", out_dtype)
 
 
+# decode kernel with 4..8 rows per launch on the matrix cores (n % 16 == 0;
+# 3 rows take the v_dot4 kernel):
+# every row count, ragged column tiles and k splits, a single k split with
+# its tail past k, 64 splits, and 9..16 rows as two launches
+@pytest.mark.parametrize("m,n,k", [(3, 16, 16), (4, 272, 1040), (5, 4112, 3088), (6, 256, 1024),
+                                   (7, 528, 2064), (8, 14336, 1024), (8, 48, 65536),
+                                   (12, 512, 1024), (16, 256, 2048)])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_decode_kernel_matrix_core_rows(m, n, k, out_dtype):
+    _run_gemm_case(m, n, k, "kn", "gemv", out_dtype)
+
+
 @pytest.mark.parametrize("kernel", ["auto", "mfma", "gemv"])
 def test_gemm_output_scale(kernel):
     _run_gemm_case(4, 96, 64, "kn", kernel, "f32", output_scale=-0.375)
@@ -390,6 +402,24 @@ def test_linear_entry_point(m, k, n, x_dtype, kernel):
     out2 = qk.linear_w8a8(x.to(DEV), torch.from_numpy(w).to(DEV), torch.from_numpy(s_ch).to(DEV),
                           TORCH_OUT[out_dtype], kernel=kernel)
     assert np.array_equal(host(out2).view(np.uint8), host(out).view(np.uint8))
+
+
+# the fused decode launch with 4..8 rows: rows held in registers, and rows
+# too long for them (re-read per pass: k > 4096 for f32, > 8192 for bf16/f16)
+@pytest.mark.parametrize("m,k,n", [(4, 1040, 272), (8, 4096, 528), (6, 4112, 64), (5, 8208, 80)])
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16", "f16"])
+def test_linear_decode_matrix_core_rows(m, k, n, x_dtype):
+    rng = np.random.default_rng(_seed("lin-mc", m, k, n, x_dtype))
+    x = wl.random_activations(rng, m, k, x_dtype, outlier_cols=max(1, k // 100))
+    w = wl.random_weight(rng, k, n)
+    s_ch = wl.random_channel_scales(rng, n)
+    out, q, s = qk.linear_w8a8(x.to(DEV), torch.from_numpy(w).to(DEV), torch.from_numpy(s_ch).to(DEV),
+                               torch.bfloat16, kernel="gemv", return_codes=True)
+    q_ref, s_ref, c_ref, out_ref = oracle.linear(wl.bits(x), DTYPE_CODE[x_dtype], w, s_ch)
+    what = f"linear {m}x{k}x{n} {x_dtype} gemv"
+    assert_equal_exact(host(s), s_ref, f"{what} scale")
+    assert_equal_exact(host(q), q_ref, f"{what} codes")
+    assert_out_close(host(out), out_ref, "bf16", what)
 
 
 @pytest.mark.parametrize("name", ["decode_m1", "decode_m8"])

@@ -6,9 +6,13 @@
 // dequantization).  The shape is the one "dynquant-kernels", What is in here,
 // calls the memory-bound decode GEMV, and "KV-cache kernels", 04 What changes
 // in the kernel's shape, is the reason for a tiling of its own: with one to
-// eight tokens the matrix cores would idle while the weight streams in.
+// eight tokens a GEMM tile would be almost all padding while the weight
+// streams in.  One to three rows take dot-product instructions
+// (gemv_kernel); four to eight take MFMAs with the rows padded to 16
+// (gemv_mfma_kernel, further down), where the dot products' VALU work would
+// outlast the weight's arrival.
 //
-// Design:
+// Design of gemv_kernel:
 //   * Split-K: a workgroup (8 wave64s, two per SIMD) owns a 512 (k) x 512 (n)
 //     block of the weight.  Lane (cg, half) of wave w loads 16 contiguous
 //     bytes (columns 16 cg .. 16 cg + 15) of the four rows of row quad
@@ -46,6 +50,7 @@
 //     quantization waits only for them and overlaps the weight stream.  The decode linear is then a single
 //     launch.
 #include "quant_math.h"
+
 
 namespace qk {
 namespace {
@@ -110,6 +115,185 @@ __device__ __forceinline__ void block_max_rows(float (&v)[MR]) {
   }
 }
 
+// The k slice's activation codes, staged into LDS: int8 codes with their
+// scales (XDT < 0), or activations of dtype XDT quantized here (every
+// workgroup reduces whole rows to the same bit-identical scales and encodes
+// its own slice; q_w, when given, receives this slice's codes).  Rows M..MR-1
+// and k past K get zero codes.  `early` issues the first weight loads: it
+// runs after every wave has issued its activation loads and before the
+// quantization (K > 0).
+template <int MR, int XDT, int ROWSK, typename Early>
+__device__ __forceinline__ void stage_codes(const void* __restrict__ a,
+                                            const float* __restrict__ scale_a, int M, int K,
+                                            int k0, int8_t* __restrict__ q_w,
+                                            float* __restrict__ s_out,
+                                            int32_t (&q_lds)[MR][ROWSK / 4], float (&s_row)[MR],
+                                            Early&& early) {
+  constexpr int kSliceWords = ROWSK / 4;  // code words of one row's k slice
+  constexpr int kCodeWords = MR * kSliceWords;
+  constexpr int kCodeRegs = (kCodeWords + kThreads - 1) / kThreads;
+  using E = qm::Elem<XDT < 0 ? QK_F32 : XDT>;
+  constexpr int P = E::kPerUnit;
+  const int t = threadIdx.x;
+
+  const int units = K / P;  // 16-byte activation units per row (fused path)
+  const bool x_in_regs = units <= kThreads * kXUnits;
+  uint4 xr[MR][kXUnits];
+  int32_t cr[kCodeRegs];
+  if constexpr (XDT >= 0) {
+    if (x_in_regs) {
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int j = 0; j < kXUnits; ++j) {
+          const int mm = min(m, M - 1);
+          const int u = min(t + kThreads * j, units - 1);  // duplicates add nothing to a max
+          xr[m][j] = *reinterpret_cast<const uint4*>(
+              static_cast<const char*>(a) + (static_cast<size_t>(mm) * K + static_cast<size_t>(u) * P) * E::kBytes);
+        }
+    }
+  } else {
+    const int8_t* q = static_cast<const int8_t*>(a);
+#pragma unroll
+    for (int j = 0; j < kCodeRegs; ++j) {
+      const int idx = t + kThreads * j;
+      const int m = idx / kSliceWords;
+      const int k = k0 + 4 * (idx % kSliceWords);
+      cr[j] = (idx < kCodeWords && m < M && k < K)
+                  ? *reinterpret_cast<const int32_t*>(q + static_cast<size_t>(m) * K + k)
+                  : 0;
+    }
+    if (t < MR) s_row[t] = (t < M && scale_a) ? scale_a[t] : 0.0f;
+  }
+  // the slice units this thread encodes: unit su of row m, with
+  // m * kSliceUnits + su = t + kThreads * i, spread over every thread (one
+  // wave per row would serialize the divisions of all rows)
+  constexpr int kSliceUnits = ROWSK / P;
+  constexpr int kEncRegs = (MR * kSliceUnits + kThreads - 1) / kThreads;
+  uint4 er[kEncRegs];
+  if constexpr (XDT >= 0) {
+    if (x_in_regs) {
+#pragma unroll
+      for (int i = 0; i < kEncRegs; ++i) {
+        const int idx = min(t + kThreads * i, MR * kSliceUnits - 1);
+        const int mm = min(idx / kSliceUnits, M - 1);
+        const int u = min(k0 / P + idx % kSliceUnits, units - 1);
+        er[i] = *reinterpret_cast<const uint4*>(
+            static_cast<const char*>(a) + (static_cast<size_t>(mm) * K + static_cast<size_t>(u) * P) * E::kBytes);
+      }
+    }
+  }
+  // A CU serves its loads in issue order: without this barrier the later
+  // waves' activation loads would queue behind the earlier waves' weight
+  // loads.  (Execution barrier only; nothing needs to be visible yet.)
+  __builtin_amdgcn_s_barrier();
+  early();
+
+  // ---- codes of rows k0 .. k0 + 511 into LDS ----
+  if constexpr (XDT < 0) {
+#pragma unroll
+    for (int j = 0; j < kCodeRegs; ++j) {
+      const int idx = t + kThreads * j;
+      if (idx < kCodeWords) q_lds[idx / kSliceWords][idx % kSliceWords] = cr[j];
+    }
+  } else if (x_in_regs) {
+    // the scale needs the whole row: every workgroup reduces it (identical bits)
+    float amax[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      amax[m] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kXUnits; ++j) {
+        float v[P];
+        E::unpack(xr[m][j], v);
+#pragma unroll
+        for (int e = 0; e < P; ++e) amax[m] = __builtin_fmaxf(amax[m], __builtin_fabsf(v[e]));
+      }
+    }
+    block_max_rows<MR>(amax);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      float s, r;
+      qm::row_scale(amax[m], s, r);
+      if (t == 0) s_row[m] = s;
+      if (blockIdx.x == 0 && t == 0 && s_out && m < M) s_out[m] = s;
+    }
+#pragma unroll
+    for (int i = 0; i < kEncRegs; ++i) {
+      const int idx = t + kThreads * i;
+      if (idx >= MR * kSliceUnits) continue;
+      const int m = idx / kSliceUnits;
+      const int su = idx % kSliceUnits;
+      const int u = k0 / P + su;
+      float am = amax[0];
+#pragma unroll
+      for (int mm = 1; mm < MR; ++mm) am = m == mm ? amax[mm] : am;
+      float s, r;
+      qm::row_scale(am, s, r);
+      float v[P];
+      E::unpack(er[i], v);
+      // padding rows and units past K (the tail of the last slice): zero words
+      const bool live = m < M && u < units;
+#pragma unroll
+      for (int e4 = 0; e4 < P / 4; ++e4) {
+        const uint32_t word =
+            live ? qm::pack4(qm::code_of(v[4 * e4], s, r), qm::code_of(v[4 * e4 + 1], s, r),
+                             qm::code_of(v[4 * e4 + 2], s, r), qm::code_of(v[4 * e4 + 3], s, r))
+                 : 0u;
+        const int kw = su * (P / 4) + e4;  // codes of elements k0 + 4 kw .. + 3
+        q_lds[m][kw] = static_cast<int32_t>(word);
+        if (q_w && live)  // one workgroup per k slice writes the codes
+          *reinterpret_cast<uint32_t*>(q_w + static_cast<size_t>(m) * K + k0 + 4 * kw) = word;
+      }
+    }
+  } else {
+    // rows too long to hold in registers: re-read them (from L2) per pass
+    for (int m = 0; m < MR; ++m) {
+      if (m >= M) {  // padding rows: zero codes
+        for (int wd = t; wd < kSliceWords; wd += kThreads) q_lds[m][wd] = 0;
+        continue;
+      }
+      const char* xrow = static_cast<const char*>(a) + static_cast<size_t>(m) * K * E::kBytes;
+      auto unit = [&](int u) -> uint4 {
+        return *reinterpret_cast<const uint4*>(xrow + static_cast<size_t>(u) * 16);
+      };
+      float amax = 0.0f;
+      for (int u = t; u < units; u += kThreads) {
+        float v[P];
+        E::unpack(unit(u), v);
+#pragma unroll
+        for (int e = 0; e < P; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[e]));
+      }
+      amax = qm::block_max<kThreads>(amax);
+      float s, r;
+      qm::row_scale(amax, s, r);
+      if (t == 0) s_row[m] = s;
+      if (blockIdx.x == 0 && t == 0 && s_out) s_out[m] = s;
+      for (int wd = t; wd < kSliceWords; wd += kThreads)
+        if (k0 + 4 * wd >= K) q_lds[m][wd] = 0;
+      const int u_lo = k0 / P;
+      const int u_hi = min(units, (k0 + ROWSK) / P);
+      for (int u = u_lo + t; u < u_hi; u += kThreads) {
+        float v[P];
+        E::unpack(unit(u), v);
+#pragma unroll
+        for (int e4 = 0; e4 < P / 4; ++e4) {
+          const uint32_t word =
+              qm::pack4(qm::code_of(v[4 * e4], s, r), qm::code_of(v[4 * e4 + 1], s, r),
+                        qm::code_of(v[4 * e4 + 2], s, r), qm::code_of(v[4 * e4 + 3], s, r));
+          const int kw = u * (P / 4) + e4;
+          q_lds[m][kw - k0 / 4] = static_cast<int32_t>(word);
+          if (q_w)
+            *reinterpret_cast<uint32_t*>(q_w + static_cast<size_t>(m) * K + 4 * kw) = word;
+        }
+      }
+      __syncthreads();  // block_max reuses its LDS between rows
+    }
+  }
+  __syncthreads();
+
+}
+
 // XDT < 0: `a` holds int8 codes [M][K] and scale_a their scales.
 // XDT >= 0: `a` holds activations [M][K] of that dtype (16-byte aligned rows,
 // K % 16 == 0), quantized here.
@@ -122,10 +306,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   constexpr int PD = prefetch_for<MR>();
   constexpr int kEarlyRounds = early_rounds_for<MR>();
   static_assert(PD >= kEarlyRounds && PD < kRounds, "prefetch distance");
-  constexpr int kSliceWords = kRowsK / 4;            // code words of one row's k slice
-  constexpr int kCodeWords = MR * kSliceWords;
-  constexpr int kCodeRegs = (kCodeWords + kThreads - 1) / kThreads;
-  __shared__ int32_t q_lds[MR][kSliceWords];  // codes of this k slice, 4 per word
+  __shared__ int32_t q_lds[MR][kRowsK / 4];  // codes of this k slice, 4 per word
   __shared__ float s_row[MR];
   // per-wave partial sums: column c of row m of wave w at [w][m][c ^ ((c >> 6) & 7)]
   __shared__ int wsum[kWaves][MR][kCols];
@@ -140,9 +321,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   const int cg = lane & 31;                  // 16-column group
   const int quad = 2 * wave + (lane >> 5);   // row quad within a 64-row round
   const int gn = n0 + 16 * cg;
-
-  using E = qm::Elem<XDT < 0 ? QK_F32 : XDT>;
-  constexpr int P = E::kPerUnit;
 
   if (K == 0) {
     // empty reduction: acc = 0 (one workgroup per column tile, no workspace);
@@ -202,161 +380,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   };
 
   // ---- activation (or code) loads first, then the weight (K > 0 from here) ----
-  const int units = K / P;  // 16-byte activation units per row (fused path)
-  const bool x_in_regs = units <= kThreads * kXUnits;
-  uint4 xr[MR][kXUnits];
-  int32_t cr[kCodeRegs];
-  if constexpr (XDT >= 0) {
-    if (x_in_regs) {
+  stage_codes<MR, XDT, kRowsK>(a, scale_a, M, K, k0, ct == 0 ? q_out : nullptr, s_out, q_lds, s_row,
+                               [&] {
 #pragma unroll
-      for (int m = 0; m < MR; ++m)
-#pragma unroll
-        for (int j = 0; j < kXUnits; ++j) {
-          const int mm = min(m, M - 1);
-          const int u = min(t + kThreads * j, units - 1);  // duplicates add nothing to a max
-          xr[m][j] = *reinterpret_cast<const uint4*>(
-              static_cast<const char*>(a) + (static_cast<size_t>(mm) * K + static_cast<size_t>(u) * P) * E::kBytes);
-        }
-    }
-  } else {
-    const int8_t* q = static_cast<const int8_t*>(a);
-#pragma unroll
-    for (int j = 0; j < kCodeRegs; ++j) {
-      const int idx = t + kThreads * j;
-      const int m = idx / kSliceWords;
-      const int k = k0 + 4 * (idx % kSliceWords);
-      cr[j] = (idx < kCodeWords && m < M && k < K)
-                  ? *reinterpret_cast<const int32_t*>(q + static_cast<size_t>(m) * K + k)
-                  : 0;
-    }
-    if (t < MR) s_row[t] = (t < M && scale_a) ? scale_a[t] : 0.0f;
-  }
-  // the slice units this thread encodes: unit su of row m, with
-  // m * kSliceUnits + su = t + kThreads * i, spread over every thread (one
-  // wave per row would serialize the divisions of all rows)
-  constexpr int kSliceUnits = kRowsK / P;
-  constexpr int kEncRegs = (MR * kSliceUnits + kThreads - 1) / kThreads;
-  uint4 er[kEncRegs];
-  if constexpr (XDT >= 0) {
-    if (x_in_regs) {
-#pragma unroll
-      for (int i = 0; i < kEncRegs; ++i) {
-        const int idx = min(t + kThreads * i, MR * kSliceUnits - 1);
-        const int mm = min(idx / kSliceUnits, M - 1);
-        const int u = min(k0 / P + idx % kSliceUnits, units - 1);
-        er[i] = *reinterpret_cast<const uint4*>(
-            static_cast<const char*>(a) + (static_cast<size_t>(mm) * K + static_cast<size_t>(u) * P) * E::kBytes);
-      }
-    }
-  }
-  // A CU serves its loads in issue order: without this barrier the later
-  // waves' activation loads would queue behind the earlier waves' weight
-  // loads.  (Execution barrier only; nothing needs to be visible yet.)
-  __builtin_amdgcn_s_barrier();
-#pragma unroll
-  for (int round = 0; round < kEarlyRounds; ++round) load_round(round);
-
-  // ---- codes of rows k0 .. k0 + 511 into LDS ----
-  if constexpr (XDT < 0) {
-#pragma unroll
-    for (int j = 0; j < kCodeRegs; ++j) {
-      const int idx = t + kThreads * j;
-      if (idx < kCodeWords) q_lds[idx / kSliceWords][idx % kSliceWords] = cr[j];
-    }
-  } else if (x_in_regs) {
-    // the scale needs the whole row: every workgroup reduces it (identical bits)
-    float amax[MR];
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      amax[m] = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kXUnits; ++j) {
-        float v[P];
-        E::unpack(xr[m][j], v);
-#pragma unroll
-        for (int e = 0; e < P; ++e) amax[m] = __builtin_fmaxf(amax[m], __builtin_fabsf(v[e]));
-      }
-    }
-    block_max_rows<MR>(amax);
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      float s, r;
-      qm::row_scale(amax[m], s, r);
-      if (t == 0) s_row[m] = s;
-      if (blockIdx.x == 0 && t == 0 && s_out && m < M) s_out[m] = s;
-    }
-#pragma unroll
-    for (int i = 0; i < kEncRegs; ++i) {
-      const int idx = t + kThreads * i;
-      if (idx >= MR * kSliceUnits) continue;
-      const int m = idx / kSliceUnits;
-      const int su = idx % kSliceUnits;
-      const int u = k0 / P + su;
-      float am = amax[0];
-#pragma unroll
-      for (int mm = 1; mm < MR; ++mm) am = m == mm ? amax[mm] : am;
-      float s, r;
-      qm::row_scale(am, s, r);
-      float v[P];
-      E::unpack(er[i], v);
-      // padding rows and units past K (the tail of the last slice): zero words
-      const bool live = m < M && u < units;
-#pragma unroll
-      for (int e4 = 0; e4 < P / 4; ++e4) {
-        const uint32_t word =
-            live ? qm::pack4(qm::code_of(v[4 * e4], s, r), qm::code_of(v[4 * e4 + 1], s, r),
-                             qm::code_of(v[4 * e4 + 2], s, r), qm::code_of(v[4 * e4 + 3], s, r))
-                 : 0u;
-        const int kw = su * (P / 4) + e4;  // codes of elements k0 + 4 kw .. + 3
-        q_lds[m][kw] = static_cast<int32_t>(word);
-        if (ct == 0 && q_out && live)  // one workgroup per k slice writes the codes
-          *reinterpret_cast<uint32_t*>(q_out + static_cast<size_t>(m) * K + k0 + 4 * kw) = word;
-      }
-    }
-  } else {
-    // rows too long to hold in registers: re-read them (from L2) per pass
-    for (int m = 0; m < MR; ++m) {
-      if (m >= M) {  // padding rows: zero codes
-        if (t < kSliceWords) q_lds[m][t] = 0;
-        continue;
-      }
-      const char* xrow = static_cast<const char*>(a) + static_cast<size_t>(m) * K * E::kBytes;
-      auto unit = [&](int u) -> uint4 {
-        return *reinterpret_cast<const uint4*>(xrow + static_cast<size_t>(u) * 16);
-      };
-      float amax = 0.0f;
-      for (int u = t; u < units; u += kThreads) {
-        float v[P];
-        E::unpack(unit(u), v);
-#pragma unroll
-        for (int e = 0; e < P; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[e]));
-      }
-      amax = qm::block_max<kThreads>(amax);
-      float s, r;
-      qm::row_scale(amax, s, r);
-      if (t == 0) s_row[m] = s;
-      if (blockIdx.x == 0 && t == 0 && s_out) s_out[m] = s;
-      if (t < kSliceWords && k0 + 4 * t >= K) q_lds[m][t] = 0;
-      const int u_lo = k0 / P;
-      const int u_hi = min(units, (k0 + kRowsK) / P);
-      for (int u = u_lo + t; u < u_hi; u += kThreads) {
-        float v[P];
-        E::unpack(unit(u), v);
-#pragma unroll
-        for (int e4 = 0; e4 < P / 4; ++e4) {
-          const uint32_t word =
-              qm::pack4(qm::code_of(v[4 * e4], s, r), qm::code_of(v[4 * e4 + 1], s, r),
-                        qm::code_of(v[4 * e4 + 2], s, r), qm::code_of(v[4 * e4 + 3], s, r));
-          const int kw = u * (P / 4) + e4;
-          q_lds[m][kw - k0 / 4] = static_cast<int32_t>(word);
-          if (ct == 0 && q_out)
-            *reinterpret_cast<uint32_t*>(q_out + static_cast<size_t>(m) * K + 4 * kw) = word;
-        }
-      }
-      __syncthreads();  // block_max reuses its LDS between rows
-    }
-  }
-  __syncthreads();
+                                 for (int round = 0; round < kEarlyRounds; ++round) load_round(round);
+                               });
 
   // ---- multiply the streamed weight with the codes ----
   int acc[MR][16];
@@ -451,6 +479,254 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   }
 }
 
+// Four to eight rows: the products on the matrix cores.  With v_dot4 the
+// VALU work grows with the row count (eight rows: 1024 dot instructions per
+// wave, more than the weight's arrival time); one v_mfma_i32_16x16x64_i8
+// multiplies 64 k of 16 columns by up to 16 rows (rows 8..15 are zero
+// here), so the multiply no longer grows with m.
+//   * Each lane loads CB bytes (CB consecutive columns) per weight row, so a
+//     workgroup covers 16 CB columns and, at the same 256 KB per workgroup,
+//     16384 / CB k rows (16 B: 256 columns x 1024 k; 4 B: 64 columns x 4096
+//     k, where one workgroup holds a column's whole k range and no split-K
+//     settlement is needed for k <= 4096).
+//   * Wave w multiplies k rows kWaveRows w .. kWaveRows (w + 1) - 1 of the
+//     block in 64-deep steps.  Lane (p = lane % 16, g = lane / 16) loads
+//     columns CB p .. CB p + CB - 1 of the 16 rows 16 g .. 16 g + 15 of a
+//     step: every wave-wide load reads four contiguous 16 CB-byte row
+//     segments.
+//   * 4 x 4 byte transposes turn a lane's 16 rows x CB columns into CB
+//     16-byte column operands (byte t = row 16 g + t).  MFMA j takes column
+//     CB p + j from lane p, and from every lane the 16 activation codes of its
+//     row p (from LDS) at the same k, 16 g .. 16 g + 15: A and B pair the same
+//     k in every byte, so each output is an exact INT32 dot product whatever
+//     order the instruction sums in.
+//   * Output of MFMA j: lane (p, g) holds rows 4 g .. 4 g + 3 of column
+//     CB p + j.  The eight waves' partial sums meet in LDS; each thread then
+//     owns CB / 4 rows of one column and either writes them (one k split) or
+//     settles them through the workspace as gemv_kernel does.
+//   Measured at 8 x 4096 x 14336: 16-byte loads (4 splits) 17.2 us per call,
+//   8-byte (2 splits) 17.8, 4-byte (no split) 28.3; the split-K settlement
+//   costs ~3.5 us of the 17.2 (v_dot4 kernel: 21.9 us).
+constexpr int kMEarlyBytes = 128;  // weight bytes per lane issued before the quantization
+
+template <int CB>
+struct MfmaTiling {
+  static constexpr int kCols = 16 * CB;            // columns per workgroup
+  static constexpr int kRowsK = 16384 / CB;        // k rows per workgroup (256 KB of weight)
+  static constexpr int kWaveRows = kRowsK / kWaves;
+  static constexpr int kSteps = kWaveRows / 64;    // 64-deep MFMA steps per wave
+  static constexpr int kRowsPerThread = CB / 4;    // rows of one column each thread settles
+  static_assert(CB == 4 || CB == 8 || CB == 16, "load width");
+  static_assert(8 * kCols == kThreads * kRowsPerThread, "one (row, column) per thread and row");
+};
+
+template <int CB>
+struct WeightLoad;
+template <>
+struct WeightLoad<16> {
+  static __device__ __forceinline__ void get(const int8_t* src, uint32_t* d) {
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(src));
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+  }
+};
+template <>
+struct WeightLoad<8> {
+  typedef unsigned v2u __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ void get(const int8_t* src, uint32_t* d) {
+    const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(src));
+    d[0] = v.x; d[1] = v.y;
+  }
+};
+template <>
+struct WeightLoad<4> {
+  static __device__ __forceinline__ void get(const int8_t* src, uint32_t* d) {
+    d[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src));
+  }
+};
+
+template <int XDT, int CB>
+__global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(
+    const void* __restrict__ a, const int8_t* __restrict__ w, int32_t* __restrict__ c,
+    const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
+    void* __restrict__ out, int out_dtype, int M, int N, int K, int8_t* __restrict__ q_out,
+    float* __restrict__ s_out, unsigned long long* __restrict__ ws, int col_tiles, int splits) {
+  using T = MfmaTiling<CB>;
+  constexpr int MR = 8;
+  constexpr int D = CB / 4;  // dwords per lane per weight row
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  __shared__ int32_t q_lds[MR][T::kRowsK / 4];
+  __shared__ float s_row[MR];
+  // partial sums of wave w: row m, column col at [w][m][slot(m, col)]
+  __shared__ int wsum[kWaves][MR][T::kCols];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int p = lane & 15;
+  const int g = lane >> 4;
+  const int ct = blockIdx.x % col_tiles;
+  const int ks = blockIdx.x / col_tiles;
+  const int n0 = ct * T::kCols;
+  const int k0 = ks * T::kRowsK;
+  // columns past N (never stored) and rows past K (zero codes) read
+  // clamped, valid addresses; N % 16 == 0 here
+  const int gn = min(n0 + CB * p, N - CB);
+
+  uint32_t wr[T::kSteps][16][D];
+  auto load_row = [&](int st, int tt) {
+    const int k = min(k0 + T::kWaveRows * wave + 64 * st + 16 * g + tt, K - 1);
+    WeightLoad<CB>::get(w + static_cast<size_t>(k) * N + gn, wr[st][tt]);
+  };
+  constexpr int kEarly = kMEarlyBytes / CB;  // loads, in (step, row) order
+  static_assert(kEarly <= 16 * T::kSteps, "early loads");
+
+  stage_codes<MR, XDT, T::kRowsK>(a, scale_a, M, K, k0, ct == 0 ? q_out : nullptr, s_out, q_lds,
+                                  s_row, [&] {
+#pragma unroll
+                                    for (int e = 0; e < kEarly; ++e) load_row(e / 16, e % 16);
+                                  });
+#pragma unroll
+  for (int e = kEarly; e < 16 * T::kSteps; ++e) load_row(e / 16, e % 16);
+
+  v4i acc[CB];
+#pragma unroll
+  for (int j = 0; j < CB; ++j) acc[j] = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int st = 0; st < T::kSteps; ++st) {
+    // codes of row p at k = kWaveRows w + 64 st + 16 g .. + 15 of the block
+    const v4i av = p < MR ? *reinterpret_cast<const v4i*>(
+                                &q_lds[p & (MR - 1)][(T::kWaveRows * wave + 64 * st + 16 * g) / 4])
+                          : v4i{0, 0, 0, 0};
+    uint32_t col[4][CB];  // [4-row batch][column]: bytes = rows 4 b .. 4 b + 3
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int q4 = 0; q4 < D; ++q4)
+        transpose4x4(wr[st][4 * b][q4], wr[st][4 * b + 1][q4], wr[st][4 * b + 2][q4],
+                     wr[st][4 * b + 3][q4], &col[b][4 * q4]);
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const v4i bv = v4i{static_cast<int>(col[0][j]), static_cast<int>(col[1][j]),
+                         static_cast<int>(col[2][j]), static_cast<int>(col[3][j])};
+      acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc[j], 0, 0, 0);
+    }
+  }
+
+  // ---- reduce within the workgroup ----
+  // slot: the column's CB-block index XORed into its low bits, and bit 4
+  // flipped for rows 4..7, so that the 32 lanes of a store (columns CB p + j
+  // of two row groups) and 64 consecutive columns of a read hit distinct
+  // banks
+  auto slot = [](int m, int col) { return col ^ ((col / CB) & (CB - 1)) ^ ((m & 4) << 2); };
+  if (g < 2) {
+#pragma unroll
+    for (int j = 0; j < CB; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * g + i;
+        wsum[wave][m][slot(m, CB * p + j)] = acc[j][i];
+      }
+  }
+  __syncthreads();
+  constexpr int R = T::kRowsPerThread;
+  const int colx = t % T::kCols;
+  const int m0 = R * (t / T::kCols);  // rows m0 .. m0 + R - 1
+  int part_sum[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int m = m0 + i;
+    int v = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) v += wsum[w2][m][slot(m, colx)];
+    part_sum[i] = v;
+  }
+
+  const int n = n0 + colx;
+  if (n >= N) return;
+  const float sb = out ? scale_b[n] * output_scale : 0.0f;
+  auto finish = [&](int m, int v) {
+    const size_t o_idx = static_cast<size_t>(m) * N + n;
+    if (c) c[o_idx] = v;
+    if (out) {
+      const float f = (static_cast<float>(v) * s_row[m]) * sb;
+      if (out_dtype == QK_BF16)
+        static_cast<uint16_t*>(out)[o_idx] = to_bf16(f);
+      else
+        static_cast<float*>(out)[o_idx] = f;
+    }
+  };
+  if (splits == 1) {  // the whole k range is here
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      if (m0 + i < M) finish(m0 + i, part_sum[i]);
+    return;
+  }
+  // ---- across the split-K workgroups (as in gemv_kernel) ----
+  unsigned long long prev[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int m = m0 + i;
+    if (m >= M) continue;
+    const unsigned long long add =
+        (1ull << kCountShift) + static_cast<unsigned long long>(static_cast<long long>(part_sum[i]));
+    prev[i] = __hip_atomic_fetch_add(&ws[static_cast<size_t>(m) * N + n], add, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int m = m0 + i;
+    if (m >= M) continue;
+    const long long o = static_cast<long long>(prev[i]);
+    const long long count = (o + (1ll << (kCountShift - 1))) >> kCountShift;
+    if (count != splits - 1) continue;
+    __hip_atomic_store(&ws[static_cast<size_t>(m) * N + n], 0ull, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    finish(m, static_cast<int>(o - (count << kCountShift)) + part_sum[i]);
+  }
+}
+
+// Row-group pointers of one launch.
+struct RowGroup {
+  const void* a;
+  int32_t* c;
+  const float* sa;
+  void* out;
+  int8_t* q_out;
+  float* s_out;
+};
+
+template <int XDT>
+RowGroup row_group(const GemvArgs& g, int row0) {
+  const size_t xsz = XDT == QK_F32 ? 4 : (XDT < 0 ? 1 : 2);
+  RowGroup r;
+  r.a = static_cast<const char*>(g.a) + static_cast<size_t>(row0) * g.k * xsz;
+  r.c = g.c ? g.c + static_cast<size_t>(row0) * g.n : nullptr;
+  r.sa = g.scale_a ? g.scale_a + row0 : nullptr;
+  r.out = nullptr;
+  if (g.out) {
+    const size_t esz = g.out_dtype == QK_BF16 ? 2 : 4;
+    r.out = static_cast<char*>(g.out) + static_cast<size_t>(row0) * g.n * esz;
+  }
+  r.q_out = g.q_out ? g.q_out + static_cast<size_t>(row0) * g.k : nullptr;
+  r.s_out = g.s_out ? g.s_out + row0 : nullptr;
+  return r;
+}
+
+constexpr int kMfmaLoadBytes = 16;
+
+template <int XDT>
+hipError_t launch_mfma(const GemvArgs& g, int row0, int rows, hipStream_t stream) {
+  using T = MfmaTiling<kMfmaLoadBytes>;
+  const RowGroup r = row_group<XDT>(g, row0);
+  const int col_tiles = (g.n + T::kCols - 1) / T::kCols;
+  const int splits = (g.k + T::kRowsK - 1) / T::kRowsK;
+  auto* ws = static_cast<unsigned long long*>(g.workspace);
+  const dim3 grid(static_cast<unsigned>(col_tiles) * static_cast<unsigned>(splits));
+  return launch(gemv_mfma_kernel<XDT, kMfmaLoadBytes>, grid, dim3(kThreads), 0, stream, r.a, g.b, r.c, r.sa,
+                g.scale_b, g.output_scale, r.out, g.out_dtype, rows, g.n, g.k, r.q_out, r.s_out,
+                ws, col_tiles, splits);
+}
+
 template <int MR, int XDT>
 hipError_t launch_mr(const GemvArgs& g, int row0, int rows, hipStream_t stream) {
   const size_t xsz = XDT == QK_F32 ? 4 : (XDT < 0 ? 1 : 2);
@@ -482,7 +758,11 @@ hipError_t launch_rows(const GemvArgs& g, hipStream_t stream) {
   for (int row0 = 0; row0 < g.m; row0 += kGemvMaxRows) {
     const int rows = g.m - row0 < kGemvMaxRows ? g.m - row0 : kGemvMaxRows;
     hipError_t e;
-    if (rows == 1)
+    const bool mfma_ok =
+        g.k > 0 && g.n >= 16 && g.n % 16 == 0 && reinterpret_cast<uintptr_t>(g.b) % 16 == 0;
+    if (rows >= 4 && mfma_ok)  // measured: v_dot4 ahead at 3 rows, level at 4, behind from 5
+      e = launch_mfma<XDT>(g, row0, rows, stream);
+    else if (rows == 1)
       e = launch_mr<1, XDT>(g, row0, rows, stream);
     else if (rows == 2)
       e = launch_mr<2, XDT>(g, row0, rows, stream);
