@@ -113,7 +113,7 @@ def _traffic_from_profile(which):
 def main():
     args = _args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for "
               f"--gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
