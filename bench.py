@@ -491,6 +491,43 @@ def main():
         del osets, ows
         torch.cuda.empty_cache()
 
+        # one GPU's share under 8-way column (tensor) parallelism: the 1-row
+        # decode and the prefill with N / 8 output columns (weights from a ring
+        # larger than the Infinity Cache: 48 x 7.3 MB and 8 x 2.1 MB + inputs)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0)
+        shard = {}
+        for sname, (sm, sk, sn, nsets, ssteps) in (("decode_m1_n1792", (1, 4096, 1792, 48, 480)),
+                                                     ("prefill_n512", (2048, 4096, 512, 8, 80))):
+            ssets = []
+            for r in range(nsets):
+                if sm == 1:
+                    x = torch.randn((sm, sk), generator=gen, device=dev).to(torch.bfloat16)
+                else:  # the prefill activations, outlier columns included
+                    x = wl.generate(wcfg, seed=r)["x"].to(dev)
+                ssets.append({"x": x,
+                              "w": torch.randint(-127, 128, (sk, sn), generator=gen, device=dev,
+                                                 dtype=torch.int8),
+                              "s_ch": torch.empty(sn, device=dev).uniform_(1e-3, 1e-2, generator=gen),
+                              "out": torch.empty((sm, sn), dtype=torch.bfloat16, device=dev)})
+            sws = torch.zeros(qk.gemm_workspace_size(sm, sn, sk), dtype=torch.uint8, device=dev)
+            sms, _ = timed_replays([(lambda bs=b: qk.linear_w8a8(bs["x"], bs["w"], bs["s_ch"],
+                                                                 out=bs["out"], workspace=sws))
+                                    for b in ssets], ssteps, args.warmup)
+            if sm == 1:
+                sbytes = sk * sn + 4 * sn + 2 * sk + 2 * sn
+                shard[sname] = {"m": sm, "k": sk, "n": sn, "us_per_call": round(sms * 1e3, 3),
+                                "value": round(sbytes / (sms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                                "frac_of_hbm_peak": round(sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            else:
+                sops = 2.0 * sm * sn * sk
+                shard[sname] = {"m": sm, "k": sk, "n": sn, "us_per_step": round(sms * 1e3, 3),
+                                "value": round(sops / (sms * 1e-3) / 1e12, 1), "unit": "TOPS",
+                                "step": "quantization + GEMM (qk_linear_w8a8)"}
+            del ssets, sws
+            torch.cuda.empty_cache()
+        others["tp8_column_shard"] = shard
+
         # gated down-projection and MLP up-projection: quantization + GEMM, and
         # the GEMM alone; two buffer sets each (both exceed the 256 MB Infinity
         # Cache already)

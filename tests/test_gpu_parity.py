@@ -221,6 +221,16 @@ def test_gemm_decode_kernel_matrix_core_rows(m, n, k, out_dtype):
     _run_gemm_case(m, n, k, "kn", "gemv", out_dtype)
 
 
+# decode kernel with 1-2 rows on narrow weights (fewer than 128 workgroups at
+# 512-row k slices): 128-row slices, ragged last slice, unaligned widths, and
+# the 8-way column shard of the decode shape
+@pytest.mark.parametrize("m,n,k", [(1, 1792, 4096), (2, 300, 1040), (1, 16, 65536), (2, 4112, 3088),
+                                   (1, 77, 528)])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_decode_kernel_narrow_weights(m, n, k, out_dtype):
+    _run_gemm_case(m, n, k, "kn", "gemv", out_dtype)
+
+
 @pytest.mark.parametrize("kernel", ["auto", "mfma", "gemv"])
 def test_gemm_output_scale(kernel):
     _run_gemm_case(4, 96, 64, "kn", kernel, "f32", output_scale=-0.375)
@@ -405,9 +415,11 @@ def test_linear_entry_point(m, k, n, x_dtype, kernel):
     assert np.array_equal(host(out2).view(np.uint8), host(out).view(np.uint8))
 
 
-# the fused decode launch with 4..8 rows: rows held in registers, and rows
-# too long for them (re-read per pass: k > 4096 for f32, > 8192 for bf16/f16)
-@pytest.mark.parametrize("m,k,n", [(4, 1040, 272), (8, 4096, 528), (6, 4112, 64), (5, 8208, 80)])
+# the fused decode launch with 4..8 rows (and 1-2 rows on narrow weights):
+# rows held in registers, and rows too long for them (re-read per pass:
+# k > 4096 for f32, > 8192 for bf16/f16)
+@pytest.mark.parametrize("m,k,n", [(4, 1040, 272), (8, 4096, 528), (6, 4112, 64), (5, 8208, 80),
+                                   (1, 4096, 1792), (2, 8208, 64), (1, 1040, 300)])
 @pytest.mark.parametrize("x_dtype", ["f32", "bf16", "f16"])
 def test_linear_decode_matrix_core_rows(m, k, n, x_dtype):
     rng = np.random.default_rng(_seed("lin-mc", m, k, n, x_dtype))

@@ -14,7 +14,8 @@
 //
 // Design of gemv_kernel:
 //   * Split-K: a workgroup (8 wave64s, two per SIMD) owns a 512 (k) x 512 (n)
-//     block of the weight.  Lane (cg, half) of wave w loads 16 contiguous
+//     block of the weight (128 x 512 for narrow weights, so that there are
+//     enough workgroups).  Lane (cg, half) of wave w loads 16 contiguous
 //     bytes (columns 16 cg .. 16 cg + 15) of the four rows of row quad
 //     2 w + half of each 64-row round: every wave-wide load instruction reads
 //     two contiguous 512-byte row segments.  Weight loads are nontemporal
@@ -58,8 +59,13 @@ namespace {
 constexpr int kThreads = 512;   // 8 waves: two per SIMD
 constexpr int kWaves = kThreads / 64;
 constexpr int kCols = 512;      // output columns per workgroup: 32 lanes x 16 bytes
-constexpr int kRowsK = 512;     // k rows per workgroup (one split-K slice)
+constexpr int kRowsK = 512;     // k rows per workgroup (one split-K slice), usually
 constexpr int kRounds = kRowsK / 64;  // a round: 16 row quads = 8 waves x 2 half-waves
+// Narrow weights (few column tiles) take slices of kNarrowRounds rounds, so
+// that more k splits keep enough workgroups streaming: 1 x 4096 x 1792 makes
+// 32 workgroups with 512-row slices and 128 with 128-row ones.
+constexpr int kNarrowRounds = 2;
+constexpr int kMinWorkgroups = 128;
 constexpr int kXUnits = 2;      // 16-byte activation units a lane keeps in registers
 constexpr int kCountShift = 40; // workspace word: count << 40 | sum (two's complement)
 static_assert(kCols == kThreads, "one output column per thread in the reduction");
@@ -68,16 +74,20 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // rounds of weight loads (4 x 16 bytes per lane each) kept in flight ahead of
 // the round being multiplied; more rows need more accumulator registers
-template <int MR>
-constexpr int prefetch_for() { return MR <= 2 ? kRounds - 1 : (MR == 4 ? 4 : 2); }
+template <int MR, int ROUNDS>
+constexpr int prefetch_for() {
+  return (MR <= 2 ? ROUNDS - 1 : (MR == 4 ? 4 : 2)) < ROUNDS - 1
+             ? (MR <= 2 ? ROUNDS - 1 : (MR == 4 ? 4 : 2))
+             : ROUNDS - 1;
+}
 // rounds issued before the quantization: a CU accepts only so many
 // outstanding loads, and a wave stalled issuing weight loads could not reach
 // the quantization (and with it every wave's first multiply).  With more
 // rows the quantization takes longer and a second round fits under it
 // (measured: 4 rows 16.3 -> 15.9 us, 8 rows 22.4 -> 21.9 us; 1 row best
 // with one).
-template <int MR>
-constexpr int early_rounds_for() { return MR == 1 ? 1 : 2; }
+template <int MR, int ROUNDS>
+constexpr int early_rounds_for() { return MR == 1 || ROUNDS <= 2 ? 1 : 2; }
 
 __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
                                              uint32_t* col) {
@@ -297,14 +307,16 @@ __device__ __forceinline__ void stage_codes(const void* __restrict__ a,
 // XDT < 0: `a` holds int8 codes [M][K] and scale_a their scales.
 // XDT >= 0: `a` holds activations [M][K] of that dtype (16-byte aligned rows,
 // K % 16 == 0), quantized here.
-template <int MR, int XDT, bool N16>
+template <int MR, int XDT, bool N16, int ROUNDS>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const void* __restrict__ a, const int8_t* __restrict__ w, int32_t* __restrict__ c,
     const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
     void* __restrict__ out, int out_dtype, int M, int N, int K, int8_t* __restrict__ q_out,
     float* __restrict__ s_out, unsigned long long* __restrict__ ws, int col_tiles, int splits) {
-  constexpr int PD = prefetch_for<MR>();
-  constexpr int kEarlyRounds = early_rounds_for<MR>();
+  constexpr int kRowsK = 64 * ROUNDS;  // this instance's k slice
+  constexpr int kRounds = ROUNDS;
+  constexpr int PD = prefetch_for<MR, ROUNDS>();
+  constexpr int kEarlyRounds = early_rounds_for<MR, ROUNDS>();
   static_assert(PD >= kEarlyRounds && PD < kRounds, "prefetch distance");
   __shared__ int32_t q_lds[MR][kRowsK / 4];  // codes of this k slice, 4 per word
   __shared__ float s_row[MR];
@@ -727,30 +739,31 @@ hipError_t launch_mfma(const GemvArgs& g, int row0, int rows, hipStream_t stream
                 ws, col_tiles, splits);
 }
 
-template <int MR, int XDT>
-hipError_t launch_mr(const GemvArgs& g, int row0, int rows, hipStream_t stream) {
-  const size_t xsz = XDT == QK_F32 ? 4 : (XDT < 0 ? 1 : 2);
-  const void* a = static_cast<const char*>(g.a) + static_cast<size_t>(row0) * g.k * xsz;
-  int32_t* c = g.c ? g.c + static_cast<size_t>(row0) * g.n : nullptr;
-  const float* sa = g.scale_a ? g.scale_a + row0 : nullptr;
-  void* out = nullptr;
-  if (g.out) {
-    const size_t esz = g.out_dtype == QK_BF16 ? 2 : 4;
-    out = static_cast<char*>(g.out) + static_cast<size_t>(row0) * g.n * esz;
-  }
-  int8_t* q_out = g.q_out ? g.q_out + static_cast<size_t>(row0) * g.k : nullptr;
-  float* s_out = g.s_out ? g.s_out + row0 : nullptr;
+template <int MR, int XDT, int ROUNDS>
+hipError_t launch_rounds(const GemvArgs& g, int row0, int rows, hipStream_t stream) {
+  const RowGroup r = row_group<XDT>(g, row0);
   const int col_tiles = (g.n + kCols - 1) / kCols;
-  const int splits = g.k > 0 ? (g.k + kRowsK - 1) / kRowsK : 1;
+  const int splits = g.k > 0 ? (g.k + 64 * ROUNDS - 1) / (64 * ROUNDS) : 1;
   auto* ws = static_cast<unsigned long long*>(g.workspace);
   const dim3 grid(static_cast<unsigned>(col_tiles) * static_cast<unsigned>(splits));
   if (g.n % 16 == 0 && reinterpret_cast<uintptr_t>(g.b) % 16 == 0)
-    return launch(gemv_kernel<MR, XDT, true>, grid, dim3(kThreads), 0, stream, a, g.b, c, sa,
-                  g.scale_b, g.output_scale, out, g.out_dtype, rows, g.n, g.k, q_out, s_out,
-                  ws, col_tiles, splits);
-  return launch(gemv_kernel<MR, XDT, false>, grid, dim3(kThreads), 0, stream, a, g.b, c, sa,
-                g.scale_b, g.output_scale, out, g.out_dtype, rows, g.n, g.k, q_out, s_out,
-                ws, col_tiles, splits);
+    return launch(gemv_kernel<MR, XDT, true, ROUNDS>, grid, dim3(kThreads), 0, stream, r.a, g.b,
+                  r.c, r.sa, g.scale_b, g.output_scale, r.out, g.out_dtype, rows, g.n, g.k, r.q_out,
+                  r.s_out, ws, col_tiles, splits);
+  return launch(gemv_kernel<MR, XDT, false, ROUNDS>, grid, dim3(kThreads), 0, stream, r.a, g.b,
+                r.c, r.sa, g.scale_b, g.output_scale, r.out, g.out_dtype, rows, g.n, g.k, r.q_out,
+                r.s_out, ws, col_tiles, splits);
+}
+
+template <int MR, int XDT>
+hipError_t launch_mr(const GemvArgs& g, int row0, int rows, hipStream_t stream) {
+  if constexpr (MR <= 2) {
+    const long long wide = static_cast<long long>((g.n + kCols - 1) / kCols) *
+                           ((g.k + kRowsK - 1) / kRowsK);
+    if (g.k > kRowsK && wide < kMinWorkgroups)
+      return launch_rounds<MR, XDT, kNarrowRounds>(g, row0, rows, stream);
+  }
+  return launch_rounds<MR, XDT, kRounds>(g, row0, rows, stream);
 }
 
 template <int XDT>
