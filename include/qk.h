@@ -66,7 +66,8 @@ extern "C" {
 /* GEMM kernel choice for qk_gemm_i8_scaled_ex */
 #define QK_KERNEL_AUTO 0 /* by shape: decode GEMV for m <= 8, MFMA tiles otherwise */
 #define QK_KERNEL_MFMA 1 /* LDS-tiled INT8 MFMA kernel, any m */
-#define QK_KERNEL_GEMV 2 /* split-K decode GEMV: m <= 16, [k][n] weight */
+#define QK_KERNEL_GEMV 2 /* split-K decode GEMV: m <= 16, [k][n] weight (per launch of up
+                          * to 8 rows: dot products for 1-3, matrix cores for 4-8) */
 
 /* status codes */
 #define QK_OK 0
