@@ -265,10 +265,13 @@ def test_gemm_outputs_aligned_to_their_element_only(kernel, out_dtype):
 def test_gemm_int32_closed_forms(kernel):
     # K * a * b with constant operands: K = 65536 at |q| <= 127, and -128 * -128
     # at the largest K accepted (the largest multiple of 16 below QK_MAX_K)
-    # (the decode kernel with 2 rows takes dot products, with 8 the matrix cores)
+    # (the decode kernel with 2 rows takes dot products, with 8 the matrix cores;
+    # at k <= 4096 the latter packs two rows' split-K sums into one word, whose
+    # fields are sized for -128 * -128 over whole 1024-row splits)
     kmax = 131056
     for m in ((2, 8) if kernel == "gemv" else (2,)):
-        for k, av, bv in ((65536, 127, 127), (65536, 127, -127), (kmax, -128, -128)):
+        for k, av, bv in ((65536, 127, 127), (65536, 127, -127), (kmax, -128, -128),
+                          (4096, -128, -128), (4096, -128, 127), (3072, 127, -128), (1024, -128, -128)):
             a = torch.full((m, k), av, dtype=torch.int8, device=DEV)
             b = torch.full((k, 64), bv, dtype=torch.int8, device=DEV)
             c = qk.gemm_i8_scaled(a, b, out_dtype=None, kernel=kernel)
