@@ -11,6 +11,8 @@ bound.  Each case prints its shape in the assertion message.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -24,7 +26,8 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 TORCH_OUT = {"f32": torch.float32, "bf16": torch.bfloat16}
 U = 2.0 ** -24
-CASES = 16
+# QK_SWEEP_CASES widens the sweep (the default keeps the suite short)
+CASES = int(os.environ.get("QK_SWEEP_CASES", "16"))
 
 
 @pytest.fixture(scope="module", autouse=True)
