@@ -6,8 +6,8 @@ boundaries instead (ragged rows and columns, k tails, every layout and
 output type, m on both sides of the decode/tiled split), so that a shape
 class nobody thought of still meets the same bar: codes, scales, zero points
 and INT32 accumulators bit-exact, fp32 outputs within 1e-6 relative and bf16
-within one ulp of the exact result, per-group results within the grouped
-bound.  Each case prints its shape in the assertion message.
+within one ulp of the exact result, per-group and FP8 results within their
+derived bounds.  Each case prints its shape in the assertion message.
 """
 from __future__ import annotations
 
@@ -197,3 +197,36 @@ def test_asym_gemm_random_shapes(case):
                         qk.weight_colsum(bd, layout), out_dtype=None, b_layout=layout)
     assert_equal_exact(host(c), oracle.gemm_asym(a, zp, b_kn, oracle.B_KN),
                        f"asym gemm {m}x{n}x{k} {layout}")
+
+
+@pytest.mark.parametrize("case", range(CASES // 2))
+def test_fp8_random_shapes(case):
+    """FP8 quantization (codes and scales exact) and the FP8 GEMM (within the
+    bound the FP8 tests derive from the matrix cores' accumulation)."""
+    from tests.test_gpu_fp8 import _acc_bound, _check_acc, _check_out
+
+    rng = _rng("fp8", case)
+    m = _dim(rng, 1, 400)
+    n = _dim(rng, 1, 400)
+    k = _dim(rng, 16, 1500, 16)
+    layout = "kn" if rng.random() < 0.6 else "nk"
+    dtype = str(rng.choice(["f32", "bf16", "f16"]))
+    scale_ub = float(rng.choice([0.0, 0.0, 0.002]))
+    x = wl.random_activations(rng, m, k, dtype, outlier_cols=max(1, k // 100))
+    q, s = qk.quant_per_token_fp8(x.to(DEV), scale_ub)
+    q_ref, s_ref = oracle.quantize_input_fp8(wl.bits(x), DTYPE_CODE[dtype], scale_ub)
+    what = f"fp8 {m}x{n}x{k} {layout} {dtype} ub={scale_ub}"
+    assert_equal_exact(host(s), s_ref, f"{what} scale")
+    assert_equal_exact(host(q.view(torch.uint8)), q_ref, f"{what} codes")
+    b_kn = wl.random_weight_fp8(rng, k, n)
+    b = b_kn if layout == "kn" else np.ascontiguousarray(b_kn.T)
+    sb = wl.random_channel_scales(rng, n)
+    out_dtype = str(rng.choice(["f32", "bf16"]))
+    out, c = qk.gemm_fp8_scaled(q, torch.from_numpy(b).to(DEV).view(torch.float8_e4m3fn), s,
+                                torch.from_numpy(sb).to(DEV), 1.0, TORCH_OUT[out_dtype], layout,
+                                return_acc=True)
+    exact = oracle.gemm_fp8(q_ref, b_kn)
+    bound, _ = _acc_bound(q_ref, b_kn)
+    _check_acc(host(c), exact, bound, f"{what} acc")
+    _check_out(host(out), oracle.dequant_fp8(exact, s_ref, sb, 1.0), bound, s_ref, sb, 1.0,
+               out_dtype, f"{what} out")
