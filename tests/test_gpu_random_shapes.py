@@ -1,4 +1,4 @@
-"""Seeded random shapes through the INT8 entry points, against the oracle.
+"""Seeded random shapes through the INT8 and FP8 entry points, against the oracle.
 
 The grids of the other GPU test files pick shapes by hand around each
 kernel's tiles; here a fixed-seed generator draws them across those
