@@ -51,6 +51,8 @@ ASYM_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_asym_prefill_outliers_traff
                 [os.path.join(CSRC, f) for f in ("gemm_mfma.hip", "gemm_tile.h", "lds_dma.h")])
 STATIC_TRAFFIC = (os.path.join(ROOT, "profiles", "quant_static_prefill_outliers_traffic.txt"),
                   [os.path.join(CSRC, f) for f in ("quant_static.hip", "quant_math.h")])
+GEMV_M8_TRAFFIC = (os.path.join(ROOT, "profiles", "gemv_mfma_decode_m8_traffic.txt"),
+                   [os.path.join(CSRC, f) for f in ("gemv.hip", "quant_math.h", "lds_dma.h")])
 
 
 def _args():
@@ -485,9 +487,15 @@ def main():
                                                              workspace=ows)) for b in osets],
                                200, args.warmup)
         obytes = ok * on + 4 * on + 2 * om * ok + 2 * om * on
+        ogbs = obytes / (oms * 1e-3) / 1e9
         others["decode_m8"] = {"m": om, "k": ok, "n": on, "us_per_call": round(oms * 1e3, 3),
-                               "value": round(obytes / (oms * 1e-3) / 1e9, 1), "unit": "GB/s",
-                               "frac_of_hbm_peak": round(obytes / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                               "value": round(ogbs, 1), "unit": "GB/s",
+                               "frac_of_hbm_peak": round(ogbs / HBM_PEAK_GBS, 4),
+                               "roofline": {"bound": "hbm", "kernel": "gemv_mfma_kernel (fused quantization)",
+                                            "achieved": round(ogbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                            "frac": round(ogbs / HBM_PEAK_GBS, 4),
+                                            "algorithmic_bytes_per_launch": obytes,
+                                            "traffic": _traffic_from_profile(GEMV_M8_TRAFFIC)}}
         del osets, ows
         torch.cuda.empty_cache()
 
