@@ -459,6 +459,41 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   //      column) carrying the arrival count and the exact partial sum ----
   const int n = n0 + t;
   if (n >= N) return;
+  auto finish = [&](int m, int v) {
+    const size_t o_idx = static_cast<size_t>(m) * N + n;
+    if (c) c[o_idx] = v;
+    if (out) {
+      const float f = (static_cast<float>(v) * s_row[m]) * (scale_b[n] * output_scale);
+      if (out_dtype == QK_BF16)
+        static_cast<uint16_t*>(out)[o_idx] = to_bf16(f);
+      else
+        static_cast<float*>(out)[o_idx] = f;
+    }
+  };
+  if constexpr (MR == 2) {
+    // Two rows share one word while splits * kRowsK <= 4096: bits 56-63
+    // count the arrivals, bits 28-55 and 0-27 hold, for rows 1 and 0, the sum
+    // of (partial + B) with B = 2^14 kRowsK >= |partial|, so each biased term
+    // lies in [0, 2 B] and all of them together stay below 2 B splits <= 2^27:
+    // no field carries into the next, and subtracting count * B recovers the
+    // exact earlier sum.  (Half the returning atomics of two words.)
+    constexpr long long kB = 16384ll * kRowsK;
+    constexpr unsigned long long kF = (1ull << 28) - 1;
+    if (static_cast<long long>(splits) * kRowsK <= 4096) {
+      const unsigned long long add =
+          (1ull << 56) + static_cast<unsigned long long>(part_sum[0] + kB) +
+          (static_cast<unsigned long long>(part_sum[1] + kB) << 28);
+      const unsigned long long o = __hip_atomic_fetch_add(&ws[n], add, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+      const long long count = static_cast<long long>(o >> 56);
+      if (count != splits - 1) return;
+      __hip_atomic_store(&ws[n], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      finish(0, static_cast<int>(static_cast<long long>(o & kF) - count * kB) + part_sum[0]);
+      if (M > 1)
+        finish(1, static_cast<int>(static_cast<long long>((o >> 28) & kF) - count * kB) + part_sum[1]);
+      return;
+    }
+  }
   unsigned long long prev[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
@@ -489,6 +524,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
         static_cast<float*>(out)[o_idx] = f;
     }
   }
+  (void)finish;
 }
 
 // Four to eight rows: the products on the matrix cores.  With v_dot4 the
