@@ -4,8 +4,10 @@ The GPU kernels settle split-K partial sums with returning 64-bit atomic adds
 and let the arrival whose add returns the last-but-one count finish the
 column.  Two encodings are used:
   * one row per word: count * 2^40 + sum (two's complement, wrapping at 2^64);
-  * two rows per word (at most 4 arrivals of at most 1024 k each): count * 2^56
-    + sum(p_hi + 2^24) * 2^28 + sum(p_lo + 2^24).
+  * two rows per word: count * 2^56 + sum(p_hi + B) * 2^28 + sum(p_lo + B),
+    with B = 2^24 for at most 4 arrivals of at most 1024 k each (matrix-core
+    kernel), and B = 2^14 * slice rows for splits * slice rows <= 4096
+    (dot-product kernel: 8 slices of 512 rows, or 32 of 128).
 These tests replay every arrival order with partial sums at the extremes the
 kernels allow and check that the decoding recovers the exact totals, i.e.
 that no field ever carries into another.  (The kernels' own results are
@@ -32,8 +34,8 @@ def settle_one_row(partials):
     raise AssertionError("no arrival saw the last count")
 
 
-def settle_two_rows(pairs):
-    kb, kf = 1 << 24, (1 << 28) - 1
+def settle_two_rows(pairs, kb=1 << 24):
+    kf = (1 << 28) - 1
     word = 0
     splits = len(pairs)
     for lo, hi in pairs:
@@ -84,3 +86,20 @@ def test_two_row_fields_never_carry():
     b = 1 << 24
     assert 4 * (b + b) < (1 << 28)
     assert 4 < (1 << 8)  # the count field (bits 56..63) holds up to 4 arrivals
+
+
+def test_two_row_words_dot_product_kernel_slices():
+    # B = 2^14 * slice rows; splits * slice rows <= 4096
+    rng = np.random.default_rng(13)
+    for slice_rows, splits in ((512, 8), (128, 32), (512, 1), (128, 9)):
+        b = 16384 * slice_rows
+        assert 2 * b * splits <= 1 << 27
+        for vals in ([b] * splits, [-b] * splits):
+            pairs = [(v, -v) for v in vals]
+            assert settle_two_rows(pairs, b) == (sum(vals), -sum(vals))
+        for _ in range(500):
+            lo = [int(v) for v in rng.integers(-b, b + 1, splits)]
+            hi = [int(v) for v in rng.integers(-b, b + 1, splits)]
+            order = rng.permutation(splits)
+            pairs = [(lo[i], hi[i]) for i in order]
+            assert settle_two_rows(pairs, b) == (sum(lo), sum(hi))
