@@ -40,7 +40,8 @@
 //     whose add returns a count of splits - 1 holds the last contribution: it
 //     forms the total, applies the dequant epilogue for that column, and
 //     returns the word to zero for the next call.  No counters, fences or
-//     last-workgroup pass are needed.
+//     last-workgroup pass are needed.  (With two rows and a short k range
+//     both rows share one word; the settlement code states the field bounds.)
 //   * Activation codes are either given (int8 a, scale_a), or the kernel
 //     quantizes the m activation rows itself from fp32/bf16/fp16 input with
 //     the same arithmetic as the quantization kernels: every workgroup
@@ -48,8 +49,8 @@
 //     own k slice; one workgroup per slice writes the codes out when asked.
 //     Every wave issues its activation (or code) loads before any wave issues
 //     weight loads, and they are used in straight-line code, so the
-//     quantization waits only for them and overlaps the weight stream.  The decode linear is then a single
-//     launch.
+//     quantization waits only for them and overlaps the weight stream.  The
+//     decode linear is then a single launch.
 #include "quant_math.h"
 
 
