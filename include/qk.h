@@ -127,7 +127,11 @@ int qk_silu_mul_quant_per_token(int m, int d, const void *h, int h_dtype, int8_t
 /* Bytes of workspace qk_gemm_i8_scaled / qk_linear_w8a8 need for this shape
  * (0 if none).  The decode kernel (m <= 16) keeps one 64-bit word per output
  * element of a row group there, holding the exact split-K partial sum and the
- * number of contributions so far; the tiled kernel needs none. */
+ * number of contributions so far.  The tiled kernel uses it when the output
+ * has fewer than 128 tiles of 256 x 128 ([k][n] weight, n % 16 == 0,
+ * k % 128 == 0, k >= 2048): it then splits k, stores each slice's INT32
+ * partial sums there and adds them in a second launch (exact, the same bits
+ * on every run); with a smaller workspace, or none, it runs unsplit. */
 size_t qk_gemm_workspace_size(int m, int n, int k);
 
 /*
@@ -153,8 +157,9 @@ size_t qk_gemm_workspace_size(int m, int n, int k);
  *            filled before its first use by this library; every call
  *            returns it to all zeros when it completes, so one buffer serves
  *            all calls issued in order on a stream.  Calls that can run at
- *            the same time must not share one.  May be NULL when the size is 0
- *            (QK_ERR_WORKSPACE otherwise).
+ *            the same time must not share one.  May be NULL when the size is 0;
+ *            otherwise a missing or short workspace is QK_ERR_WORKSPACE on
+ *            the decode path, while the tiled GEMM then runs unsplit.
  * Requirements: 0 <= k <= QK_MAX_K and k % 16 == 0; a, b 16-byte aligned;
  * for the tiled (m > 8) kernel m*k and n*k below 2^32 (QK_ERR_UNSUPPORTED
  * otherwise).  k == 0 gives acc = 0.
@@ -185,7 +190,7 @@ int qk_gemm_i8_scaled_ex(int m, int n, int k, const int8_t *a, const int8_t *b, 
  *            codes and scales if given.  Required otherwise: they hold the
  *            intermediate between the two launches.
  *   workspace / workspace_bytes: as for qk_gemm_i8_scaled (used by the
- *            fused decode launch).
+ *            fused decode launch, and by the tiled GEMM to split k).
  *   kernel   QK_KERNEL_AUTO, QK_KERNEL_GEMV (fused, m <= 16) or
  *            QK_KERNEL_MFMA (quantization launch + tiled GEMM).
  * Requirements and errors as qk_quant_per_token and qk_gemm_i8_scaled.

@@ -482,3 +482,55 @@ def test_hip_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(again.view(torch.int16), ref_d.view(torch.int16))
     assert not ws.any()
+
+
+# --------------------------------------------------------------------------
+# split-K of the tiled GEMM for outputs with few tiles (the workspace holds
+# the INT32 partial sums; the reduction adds them in order and clears them)
+# --------------------------------------------------------------------------
+
+SPLIT_SHAPES = [(2048, 512, 4096), (300, 256, 2048), (513, 144, 3200), (17, 4096, 2048),
+                (1024, 1024, 8192), (512, 512, 8192)]
+
+
+@pytest.mark.parametrize("m,n,k", SPLIT_SHAPES)
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_split_k(m, n, k, out_dtype):
+    assert qk.gemm_workspace_size(m, n, k) >= 2 * m * n * 4  # the plan splits these
+    _run_gemm_case(m, n, k, "kn", "mfma", out_dtype, output_scale=0.75)
+
+
+@pytest.mark.parametrize("m,n,k,layout", [(2048, 512, 4096, "nk"), (2048, 512, 4112, "kn"),
+                                          (300, 200, 2048, "kn")])
+def test_gemm_unsplit_shapes_with_workspace(m, n, k, layout):
+    # [N][K] weights, k % 128 != 0 and n % 16 != 0 run unsplit
+    _run_gemm_case(m, n, k, layout, "mfma", "bf16")
+
+
+def test_gemm_split_k_closed_forms_and_workspace_left_zero():
+    m, n = 600, 384
+    for k, av, bv in ((8192, -128, -128), (4096, 127, -128), (2048, -127, 127), (131072 - 128, -128, -128)):
+        ws = torch.zeros(qk.gemm_workspace_size(m, n, k), dtype=torch.uint8, device=DEV)
+        assert ws.numel() > 0
+        a = torch.full((m, k), av, dtype=torch.int8, device=DEV)
+        b = torch.full((k, n), bv, dtype=torch.int8, device=DEV)
+        c = qk.gemm_i8_scaled(a, b, out_dtype=None, kernel="mfma", workspace=ws)
+        assert bool((c == k * av * bv).all()), (k, av, bv)
+        torch.cuda.synchronize()
+        assert not ws.any(), "the split-K reduction leaves the workspace zero"
+
+
+def test_gemm_split_k_then_decode_share_a_workspace():
+    # a split-K GEMM and a decode GEMM in turn on one workspace: both exact
+    rng = np.random.default_rng(_seed("split-share"))
+    ws = torch.zeros(max(qk.gemm_workspace_size(2048, 512, 4096), qk.gemm_workspace_size(8, 4096, 4096)),
+                     dtype=torch.uint8, device=DEV)
+    for _ in range(2):
+        for (m, n, k, kernel) in ((2048, 512, 4096, "mfma"), (8, 4096, 4096, "gemv"), (2, 512, 4096, "gemv")):
+            a = rng.integers(-128, 128, size=(m, k), dtype=np.int8)
+            b = rng.integers(-128, 128, size=(k, n), dtype=np.int8)
+            c = qk.gemm_i8_scaled(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV), out_dtype=None,
+                                  kernel=kernel, workspace=ws)
+            assert_equal_exact(host(c), oracle.gemm_i32(a, b), f"{m}x{n}x{k} {kernel} shared workspace")
+    torch.cuda.synchronize()
+    assert not ws.any()

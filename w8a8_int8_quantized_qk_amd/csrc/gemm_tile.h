@@ -49,9 +49,12 @@ __device__ __forceinline__ int kn_offset(int k, int chunk) {
 // wave's share (1 KiB = 8 rows each).
 template <int ROWS>
 constexpr int rowk_ops() { return ROWS * BK / 1024 / kWaves; }
+// Row-major [rows][K] operand; ld, when given, is the row stride (a k range
+// of a longer row), else K.
 template <int ROWS>
 __device__ __forceinline__ void dma_rowk_one(const int8_t* __restrict__ g, char* lds,
-                                             int rows_valid, int K, int r0, int k0, int i) {
+                                             int rows_valid, int K, int r0, int k0, int i,
+                                             int ld = -1) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int blk = wave * rowk_ops<ROWS>() + i;
@@ -59,13 +62,14 @@ __device__ __forceinline__ void dma_rowk_one(const int8_t* __restrict__ g, char*
   const int lchunk = (lane & 7) ^ rowk_swz(row);
   const uint32_t gr = static_cast<uint32_t>(min(r0 + row, rows_valid - 1));
   const uint32_t gk = static_cast<uint32_t>(min(k0 + 16 * lchunk, K - 16));
-  lds_dma16(g + (gr * static_cast<uint32_t>(K) + gk), lds_addr(lds + blk * 1024));
+  lds_dma16(g + (gr * static_cast<uint32_t>(ld < 0 ? K : ld) + gk), lds_addr(lds + blk * 1024));
 }
 template <int ROWS>
 __device__ __forceinline__ void dma_rowk(const int8_t* __restrict__ g, char* lds, int rows_valid,
-                                         int K, int r0, int k0) {
+                                         int K, int r0, int k0, int ld = -1) {
 #pragma unroll
-  for (int i = 0; i < rowk_ops<ROWS>(); ++i) dma_rowk_one<ROWS>(g, lds, rows_valid, K, r0, k0, i);
+  for (int i = 0; i < rowk_ops<ROWS>(); ++i)
+    dma_rowk_one<ROWS>(g, lds, rows_valid, K, r0, k0, i, ld);
 }
 
 // DMA of a [K][N] weight tile: 128 k rows x 128 bytes of n; instruction i of
@@ -101,8 +105,9 @@ struct FixedParts {
   uint32_t lds[kOps];  // wave-uniform (m0 operand)
   size_t stride[kOps];
 
+  // lda: A's row stride when A is a k range of longer rows (else K)
   __device__ __forceinline__ void init(const int8_t* __restrict__ a, const int8_t* __restrict__ b,
-                                       int M, int N, int K, int m0, int n0) {
+                                       int M, int N, int K, int m0, int n0, int lda = -1) {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -112,7 +117,7 @@ struct FixedParts {
         const int row = blk * 8 + (lane >> 3);
         const int lchunk = (lane & 7) ^ rowk_swz(row);
         const uint32_t gr = static_cast<uint32_t>(min(m0 + row, M - 1));
-        src[q] = a + (gr * static_cast<uint32_t>(K) + 16 * lchunk);
+        src[q] = a + (gr * static_cast<uint32_t>(lda < 0 ? K : lda) + 16 * lchunk);
         lds[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(blk * 1024));
         stride[q] = BK;
       } else if constexpr (MODE == kBnkDma) {

@@ -60,8 +60,10 @@ int gemm_common(int m, int n, int k, const int8_t* a, const int8_t* b, int32_t* 
     return status_of(qk::launch_gemv(g, stream));
   }
   if (!qk::gemm_mfma_supported(m, n, k)) return QK_ERR_UNSUPPORTED;
+  // the workspace, when given, lets an output with few tiles split k
+  const bool ws = workspace && aligned(workspace, 256);
   qk::GemmArgs g{m, n, k, a, b, c, scale_a, scale_b, output_scale, out, out_dtype, b_layout,
-                 nullptr, 0};
+                 ws ? workspace : nullptr, ws ? workspace_bytes : 0};
   return status_of(qk::launch_gemm_mfma(g, stream));
 }
 
@@ -108,9 +110,12 @@ int qk_silu_mul_quant_per_token(int m, int d, const void* h, int h_dtype, int8_t
 }
 
 size_t qk_gemm_workspace_size(int m, int n, int k) {
-  (void)k;
-  if (m <= 0 || n <= 0 || m > qk::kGemvMaxM) return 0;  // the tiled kernel needs none
-  return qk::gemv_workspace_bytes(n);
+  if (m <= 0 || n <= 0 || k < 0) return 0;
+  // the decode kernel's words (m <= 16), and the tiled kernel's split-K
+  // partial sums when the output has few tiles ([K][N] weight)
+  const size_t gemv = m <= qk::kGemvMaxM ? qk::gemv_workspace_bytes(n) : 0;
+  const size_t split = qk::splitk_plan(m, n, k, QK_B_KN).bytes;
+  return gemv > split ? gemv : split;
 }
 
 int qk_gemm_i8_scaled(int m, int n, int k, const int8_t* a, const int8_t* b, int32_t* c,
@@ -171,8 +176,9 @@ int qk_linear_w8a8(int m, int n, int k, const void* x, int x_dtype, const int8_t
   if (!qk::gemm_mfma_supported(m, n, k)) return QK_ERR_UNSUPPORTED;
   hipError_t e = qk::launch_quant_rows(m, k, x, x_dtype, q_out, scale_out, stream);
   if (e != hipSuccess) return status_of(e);
+  const bool ws = workspace && aligned(workspace, 256);
   qk::GemmArgs g{m, n, k, q_out, b, nullptr, scale_out, scale_b, output_scale, out, out_dtype,
-                 b_layout, nullptr, 0};
+                 b_layout, ws ? workspace : nullptr, ws ? workspace_bytes : 0};
   return status_of(qk::launch_gemm_mfma(g, stream));
 }
 

@@ -30,6 +30,15 @@ hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds_by
       typed);
 }
 
+// Split-K plan of the tiled INT8 GEMM (gemm_mfma.hip): splits > 1 when the
+// output has few tiles; `bytes` of workspace hold the INT32 partial sums.
+struct SplitKPlan {
+  int splits;
+  int kslice;
+  size_t bytes;
+};
+SplitKPlan splitk_plan(int m, int n, int k, int b_layout);
+
 struct GemmArgs {
   int m, n, k;
   const int8_t* a;
@@ -41,7 +50,7 @@ struct GemmArgs {
   void* out;
   int out_dtype;  // QK_F32 | QK_BF16 (ignored when out == nullptr)
   int b_layout;   // QK_B_KN | QK_B_NK
-  void* workspace;
+  void* workspace;         // optional: the split-K partial sums (zero before and after)
   size_t workspace_bytes;
 };
 
