@@ -520,6 +520,44 @@ def test_gemm_split_k_closed_forms_and_workspace_left_zero():
         assert not ws.any(), "the split-K reduction leaves the workspace zero"
 
 
+def test_hip_graph_replays_of_split_k_match_eager():
+    # a split-K GEMM and the decode linear captured on one workspace, replayed
+    # with eager split-K work in between; the reduction clears the partial
+    # sums with stores (no memset nodes in the graph)
+    rng = np.random.default_rng(_seed("split-graph"))
+    m, n, k = 512, 512, 8192
+    a = torch.from_numpy(rng.integers(-128, 128, size=(m, k), dtype=np.int8)).to(DEV)
+    b = torch.from_numpy(rng.integers(-128, 128, size=(k, n), dtype=np.int8)).to(DEV)
+    sa = torch.from_numpy(rng.uniform(1e-4, 1e-1, m).astype(np.float32)).to(DEV)
+    sb = torch.from_numpy(rng.uniform(1e-3, 1e-2, n).astype(np.float32)).to(DEV)
+    dec = wl.generate("decode_m8")
+    xd, wd, sd = dec["x"].to(DEV), torch.from_numpy(dec["w"]).to(DEV), torch.from_numpy(dec["s_ch"]).to(DEV)
+    ws = torch.zeros(max(qk.gemm_workspace_size(m, n, k), qk.gemm_workspace_size(8, wd.shape[1], wd.shape[0])),
+                     dtype=torch.uint8, device=DEV)
+    ref_s = qk.gemm_i8_scaled(a, b, sa, sb, kernel="mfma", workspace=ws).clone()
+    ref_d = qk.linear_w8a8(xd, wd, sd, workspace=ws).clone()
+    out_s = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    out_d = torch.empty((8, wd.shape[1]), dtype=torch.bfloat16, device=DEV)
+    stream = torch.cuda.Stream(DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        qk.gemm_i8_scaled(a, b, sa, sb, out=out_s, kernel="mfma", workspace=ws)
+        qk.linear_w8a8(xd, wd, sd, out=out_d, workspace=ws)
+    for rep in range(4):
+        out_s.zero_()
+        out_d.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_s.view(torch.int16), ref_s.view(torch.int16)), rep
+        assert torch.equal(out_d.view(torch.int16), ref_d.view(torch.int16)), rep
+        again = qk.gemm_i8_scaled(a, b, sa, sb, kernel="mfma", workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16), ref_s.view(torch.int16))
+    assert not ws.any()
+    c_ref = oracle.gemm_i32(host(a), host(b))
+    assert_out_close(host(ref_s), oracle.dequant(c_ref, host(sa), host(sb)), "bf16", "split-K graph")
+
+
 def test_gemm_split_k_then_decode_share_a_workspace():
     # a split-K GEMM and a decode GEMM in turn on one workspace: both exact
     rng = np.random.default_rng(_seed("split-share"))
