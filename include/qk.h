@@ -129,9 +129,10 @@ int qk_silu_mul_quant_per_token(int m, int d, const void *h, int h_dtype, int8_t
  * element of a row group there, holding the exact split-K partial sum and the
  * number of contributions so far.  The tiled kernel uses it when the output
  * has fewer than 128 tiles of 256 x 128 ([k][n] weight, n % 16 == 0,
- * k % 128 == 0, k >= 2048): it then splits k, stores each slice's INT32
- * partial sums there and adds them in a second launch (exact, the same bits
- * on every run); with a smaller workspace, or none, it runs unsplit. */
+ * k % 128 == 0, k >= 2048) and the k time saved outweighs the partial sums'
+ * round trip: it then splits k, stores each slice's INT32 partial sums there
+ * and adds them in a second launch (exact, the same bits on every run); with
+ * a smaller workspace, or none, it runs unsplit. */
 size_t qk_gemm_workspace_size(int m, int n, int k);
 
 /*

@@ -688,17 +688,25 @@ SplitKPlan splitk_plan(int m, int n, int k, int b_layout) {
   if (m <= 0 || b_layout != QK_B_KN || n % 16 != 0 || k % BK != 0 || k < 2048) return p;
   const long long tiles = static_cast<long long>((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   if (tiles >= 128) return p;
-  const int want = static_cast<int>((256 + tiles - 1) / tiles);  // about one round of the CUs
+  const int want = static_cast<int>(256 / tiles);  // (slice, tile) workgroups in one round
   // at least 1024 k per split: a tile's fixed cost (prologue, k-group hand-over,
-  // stores) is ~8 slices' worth, and each split adds its partial sums' write,
-  // read and clearing (measured: 2048 x 512 x 4096 with 512-k splits 34.2 us
-  // against 33.4 unsplit)
+  // stores) is ~8 slices' worth (measured: 2048 x 512 x 4096 with 512-k
+  // splits 34.2 us against 33.4 unsplit)
   const int splits = min(want, k / 1024);
   if (splits < 2) return p;
   const int kt = k / BK;
   const int per = (kt + splits - 1) / splits;
-  p.kslice = per * BK;
-  p.splits = (kt + per - 1) / per;
+  const int kslice = per * BK;
+  const int nsplit = (kt + per - 1) / per;
+  // worth it only when the loop time saved outweighs the partial sums' round
+  // trip (written, read, cleared); fitted to eight measured shapes: ~6.2 ns per
+  // k of a tile's loop, ~3.3 ps per partial-sum element (e.g. 2048 x 1024 x
+  // 4096 split 4 ways measured 39.5 against 33.6 us unsplit, and is refused)
+  const double saved_us = 6.2e-3 * (k - kslice);
+  const double cost_us = 3.3e-6 * nsplit * static_cast<double>(m) * n;
+  if (saved_us < 1.25 * cost_us) return p;
+  p.splits = nsplit;
+  p.kslice = kslice;
   p.bytes = (static_cast<size_t>(p.splits) * m * n * 4 + 255) / 256 * 256;
   return p;
 }
