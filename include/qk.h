@@ -128,8 +128,8 @@ int qk_silu_mul_quant_per_token(int m, int d, const void *h, int h_dtype, int8_t
  * (0 if none).  The decode kernel (m <= 16) keeps one 64-bit word per output
  * element of a row group there, holding the exact split-K partial sum and the
  * number of contributions so far.  The tiled kernel uses it when the output
- * has fewer than 128 tiles of 256 x 128 ([k][n] weight, n % 16 == 0,
- * k % 128 == 0, k >= 2048) and the k time saved outweighs the partial sums'
+ * has fewer than 128 tiles of 256 x 128 (n % 16 == 0, k % 128 == 0,
+ * k >= 2048) and the k time saved outweighs the partial sums'
  * round trip: it then splits k, stores each slice's INT32 partial sums there
  * and adds them in a second launch (exact, the same bits on every run); with
  * a smaller workspace, or none, it runs unsplit. */

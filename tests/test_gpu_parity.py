@@ -500,10 +500,16 @@ def test_gemm_split_k(m, n, k, out_dtype):
     _run_gemm_case(m, n, k, "kn", "mfma", out_dtype, output_scale=0.75)
 
 
-@pytest.mark.parametrize("m,n,k,layout", [(2048, 512, 4096, "nk"), (2048, 512, 4112, "kn"),
-                                          (300, 200, 2048, "kn")])
+@pytest.mark.parametrize("m,n,k", [(2048, 512, 4096), (513, 144, 3200), (512, 512, 8192)])
+def test_gemm_split_k_nk_weight(m, n, k):
+    # the [N][K] layout splits too (B's row stride passed like A's)
+    _run_gemm_case(m, n, k, "nk", "mfma", "bf16")
+
+
+@pytest.mark.parametrize("m,n,k,layout", [(2048, 512, 4112, "kn"), (300, 200, 2048, "kn"),
+                                          (300, 200, 2048, "nk"), (2048, 1024, 4096, "kn")])
 def test_gemm_unsplit_shapes_with_workspace(m, n, k, layout):
-    # [N][K] weights, k % 128 != 0 and n % 16 != 0 run unsplit
+    # k % 128 != 0, n % 16 != 0, and a shape whose split would not pay, run unsplit
     _run_gemm_case(m, n, k, layout, "mfma", "bf16")
 
 

@@ -75,7 +75,7 @@ __device__ __forceinline__ void gemm_i8_tile(
     const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
     void* __restrict__ out, int out_dtype, int M, int N, int K, int tm, int tn,
     const int32_t* __restrict__ zp_a = nullptr, const int32_t* __restrict__ wsum = nullptr,
-    int lda = -1) {
+    int lda = -1, int ldb = -1) {
   constexpr bool kRegB = MODE == kBknReg4 || MODE == kBknReg1;
   __shared__ __attribute__((aligned(1024))) char smem[kStages * STAGE];
 
@@ -118,7 +118,7 @@ __device__ __forceinline__ void gemm_i8_tile(
   // issue the global reads of k slice s (DMA: straight into its LDS slice)
   auto fetch = [&](int s) {
     dma_rowk<BM>(a, a_lds(s), M, K, m0, s * BK, lda);
-    if constexpr (MODE == kBnkDma) dma_rowk<BN>(b, b_lds(s), N, K, n0, s * BK);
+    if constexpr (MODE == kBnkDma) dma_rowk<BN>(b, b_lds(s), N, K, n0, s * BK, ldb);
     if constexpr (MODE == kBknDma) dma_kn(b, b_lds(s), N, K, n0, s * BK);
   };
   constexpr int kFetchOps = BM * BK / 1024 / kWaves + (kRegB ? 0 : BN * BK / 1024 / kWaves);
@@ -134,7 +134,7 @@ __device__ __forceinline__ void gemm_i8_tile(
   Parts parts;
   if constexpr (kFixedParts) {
     static_assert(Parts::kOps == kFetchOps, "one DMA instruction per part");
-    parts.init(a, b, M, N, K, m0, n0, lda);
+    parts.init(a, b, M, N, K, m0, n0, lda, ldb);
   }
   auto fetch_part = [&](int s, int part) {
     if constexpr (kFixedParts) {
@@ -142,7 +142,7 @@ __device__ __forceinline__ void gemm_i8_tile(
     } else if (part < kOpsA) {
       dma_rowk_one<BM>(a, a_lds(s), M, K, m0, s * BK, part, lda);
     } else if constexpr (MODE == kBnkDma) {
-      dma_rowk_one<BN>(b, b_lds(s), N, K, n0, s * BK, part - kOpsA);
+      dma_rowk_one<BN>(b, b_lds(s), N, K, n0, s * BK, part - kOpsA, ldb);
     } else if constexpr (MODE == kBknDma) {
       dma_kn_one(b, b_lds(s), N, K, n0, s * BK, part - kOpsA);
     }
@@ -632,6 +632,7 @@ namespace {
 // stores its raw INT32 partial sums to slice s of the workspace; a second
 // kernel adds the slices in order (exact, and the same bits on every run),
 // returns the workspace to zero, and applies the epilogue.
+template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_splitk_kernel(
     const int8_t* __restrict__ a, const int8_t* __restrict__ b, int32_t* __restrict__ part,
     int M, int N, int K, int tiles_m, int tiles_n, int kslice) {
@@ -641,10 +642,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_splitk_kernel(
   int tm, tn;
   group_order(xcd_order(t, tiles), tiles_m, tiles_n, tm, tn);
   const int k0 = s * kslice;
-  gemm_i8_tile<kBknDma, false>(a + k0, b + static_cast<size_t>(k0) * N,
-                               part + static_cast<size_t>(s) * M * N, nullptr, nullptr, 1.0f,
-                               nullptr, QK_F32, M, N, min(kslice, K - k0), tm, tn, nullptr,
-                               nullptr, K);
+  // a [K][N] weight's k range starts k0 rows down; a [N][K] one's k0 bytes in
+  const int8_t* bk = MODE == kBknDma ? b + static_cast<size_t>(k0) * N : b + k0;
+  gemm_i8_tile<MODE, false>(a + k0, bk, part + static_cast<size_t>(s) * M * N, nullptr, nullptr,
+                            1.0f, nullptr, QK_F32, M, N, min(kslice, K - k0), tm, tn, nullptr,
+                            nullptr, K, K);
 }
 
 // Four consecutive outputs of one row per thread (N % 16 == 0).
@@ -685,7 +687,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
 
 SplitKPlan splitk_plan(int m, int n, int k, int b_layout) {
   SplitKPlan p{1, k, 0};
-  if (m <= 0 || b_layout != QK_B_KN || n % 16 != 0 || k % BK != 0 || k < 2048) return p;
+  if (m <= 0 || (b_layout != QK_B_KN && b_layout != QK_B_NK) || n % 16 != 0 || k % BK != 0 ||
+      k < 2048)
+    return p;
   const long long tiles = static_cast<long long>((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   if (tiles >= 128) return p;
   const int want = static_cast<int>(256 / tiles);  // (slice, tile) workgroups in one round
@@ -717,9 +721,12 @@ hipError_t launch_splitk(const GemmArgs& g, const SplitKPlan& p, hipStream_t str
   const int tiles_m = (g.m + BM - 1) / BM;
   const int tiles_n = (g.n + BN - 1) / BN;
   auto* part = static_cast<int32_t*>(g.workspace);
-  hipError_t e = launch(gemm_i8_splitk_kernel, dim3(static_cast<unsigned>(p.splits * tiles_m * tiles_n)),
-                        dim3(kThreads), 0, stream, g.a, g.b, part, g.m, g.n, g.k, tiles_m, tiles_n,
-                        p.kslice);
+  const dim3 grid(static_cast<unsigned>(p.splits * tiles_m * tiles_n));
+  hipError_t e = g.b_layout == QK_B_NK
+                     ? launch(gemm_i8_splitk_kernel<kBnkDma>, grid, dim3(kThreads), 0, stream, g.a,
+                              g.b, part, g.m, g.n, g.k, tiles_m, tiles_n, p.kslice)
+                     : launch(gemm_i8_splitk_kernel<kBknDma>, grid, dim3(kThreads), 0, stream, g.a,
+                              g.b, part, g.m, g.n, g.k, tiles_m, tiles_n, p.kslice);
   if (e != hipSuccess) return e;
   const long long quads = static_cast<long long>(g.m) * g.n / 4;
   const long long blocks = (quads + 255) / 256;

@@ -105,9 +105,11 @@ struct FixedParts {
   uint32_t lds[kOps];  // wave-uniform (m0 operand)
   size_t stride[kOps];
 
-  // lda: A's row stride when A is a k range of longer rows (else K)
+  // lda, ldb: the row strides of A and of a [N][K] B when they are a k range
+  // of longer rows (else K)
   __device__ __forceinline__ void init(const int8_t* __restrict__ a, const int8_t* __restrict__ b,
-                                       int M, int N, int K, int m0, int n0, int lda = -1) {
+                                       int M, int N, int K, int m0, int n0, int lda = -1,
+                                       int ldb = -1) {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -125,7 +127,7 @@ struct FixedParts {
         const int row = blk * 8 + (lane >> 3);
         const int lchunk = (lane & 7) ^ rowk_swz(row);
         const uint32_t gr = static_cast<uint32_t>(min(n0 + row, N - 1));
-        src[q] = b + (gr * static_cast<uint32_t>(K) + 16 * lchunk);
+        src[q] = b + (gr * static_cast<uint32_t>(ldb < 0 ? K : ldb) + 16 * lchunk);
         lds[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(A_STAGE + blk * 1024));
         stride[q] = BK;
       } else {
