@@ -60,6 +60,8 @@ def _args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--repeats", type=int, default=5,
+                   help="timed blocks of exactly --steps steps each; the median is reported")
     p.add_argument("--ring", type=int, default=8, help="buffer sets cycled through")
     p.add_argument("--settle-seconds", type=float, default=0.2,
                    help="replay the captured steps this long before the warmup steps: the GPU "
@@ -112,6 +114,55 @@ def _traffic_from_profile(which):
     return float(t.group(1))
 
 
+def _sclk_now():
+    """Current shader clock in MHz from the amdgpu driver's sysfs table (the
+    level marked '*'), or None where it cannot be read."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(path).read().splitlines():
+                if line.rstrip().endswith("*"):
+                    mhz = re.search(r"(\d+)\s*[Mm]hz", line)
+                    if mhz:
+                        return int(mhz.group(1))
+        except OSError:
+            continue
+    return None
+
+
+class _ClockSampler:
+    """Samples the shader clock every ~2 ms in a thread while a timed region runs."""
+
+    def __init__(self):
+        import threading
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = _sclk_now()
+            if v is None:
+                return
+            self.samples.append(v)
+            self._stop.wait(0.002)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1],
+                "samples": len(v), "source": "sysfs pp_dpm_sclk during the timed repeats"}
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -130,10 +181,13 @@ def main():
     qk.library()
     stream = torch.cuda.Stream(dev)  # default priority (capture needs a non-default stream)
 
-    def timed_replays(step_fns, k_steps, warmup):
+    def timed_replays(step_fns, k_steps, warmup, repeats=None, stats=None):
         """Capture one HIP graph per buffer set (one step each) plus one graph of
-        a whole ring, then run exactly k_steps steps by replay and time them with
-        HIP events on the replay stream.  Returns (ms per step, wall seconds)."""
+        a whole ring, then run `repeats` timed blocks of exactly k_steps steps by
+        replay, each timed with HIP events on the replay stream.  Returns (median
+        ms per step, wall seconds of the median block); `stats`, when given,
+        receives every block's ms per step and their min / median / max."""
+        repeats = args.repeats if repeats is None else repeats
         R = len(step_fns)
         with torch.cuda.stream(stream):
             for f in step_fns:  # eager warm-up: first-use setup stays out of capture
@@ -164,15 +218,25 @@ def main():
             torch.cuda.synchronize()
         run(warmup)
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record(stream)
-        run(k_steps)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return e0.elapsed_time(e1) / k_steps, wall
+        blocks = []
+        for _ in range(max(1, repeats)):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e0.record(stream)
+            run(k_steps)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            blocks.append((e0.elapsed_time(e1) / k_steps, time.perf_counter() - t0))
+        order = sorted(blocks)
+        ms, wall = order[len(order) // 2]
+        if stats is not None:
+            stats.update({"repeats": len(blocks), "steps_each": k_steps,
+                          "ms_per_step_each": [round(b[0], 6) for b in blocks],
+                          "min_ms": round(order[0][0], 6), "median_ms": round(ms, 6),
+                          "max_ms": round(order[-1][0], 6)})
+        return ms, wall
 
     # ---------------- prefill: quant + GEMM (headline) ----------------
     wcfg = wl.WORKLOADS["prefill_outliers"]
@@ -200,9 +264,13 @@ def main():
     def quant_fn(bs):
         return lambda: qk.quant_per_token(bs["x"], bs["q"], bs["s"])
 
-    ms_per_step, wall = timed_replays([step_fn(b) for b in sets], args.steps, args.warmup)
-    gemm_ms, _ = timed_replays([gemm_fn(b) for b in sets], args.steps, args.warmup)
-    quant_ms, _ = timed_replays([quant_fn(b) for b in sets], args.steps, args.warmup)
+    step_stats, gemm_stats, quant_stats = {}, {}, {}
+    with _ClockSampler() as sclk:
+        ms_per_step, wall = timed_replays([step_fn(b) for b in sets], args.steps, args.warmup,
+                                          stats=step_stats)
+    gemm_ms, _ = timed_replays([gemm_fn(b) for b in sets], args.steps, args.warmup, stats=gemm_stats)
+    quant_ms, _ = timed_replays([quant_fn(b) for b in sets], args.steps, args.warmup,
+                                stats=quant_stats)
     ops = 2.0 * m * n * k
     tops = ops / (ms_per_step * 1e-3) / 1e12
     gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
@@ -228,9 +296,19 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "gemm_i8_mfma_kernel",
                      "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                      "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": traffic, "avg_launch_us": round(gemm_ms * 1e3, 3),
+                     "traffic": traffic,
+                     "traffic_source": ("rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of this kernel "
+                                        "code, copy-kernel scaled, from "
+                                        "profiles/gemm_mfma_prefill_outliers_traffic.txt"
+                                        if traffic is not None else
+                                        "none: no counter summary taken on this kernel code"),
+                     "avg_launch_us": round(gemm_ms * 1e3, 3),
                      "algorithmic_ops_per_launch": ops},
         "step_frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+        "timing": {"step": step_stats, "gemm": gemm_stats, "quant": quant_stats,
+                   "rule": "each block times exactly --steps replayed steps with HIP events; "
+                           "value and ms_per_step are the median block"},
+        "sclk": sclk.summary(),
         "quant_kernel_us": round(quant_ms * 1e3, 3),
         "wall_s_timed_region": round(wall, 4),
         "settle_s_before_warmup": args.settle_seconds,
@@ -240,7 +318,7 @@ def main():
     if not args.no_decode:
         dcfg = wl.WORKLOADS["decode_m1"]
         dm, dk, dn = dcfg.m, dcfg.k, dcfg.n
-        ws = torch.zeros(qk.gemm_workspace_size(dm, dn, dk), dtype=torch.uint8, device=dev)
+        ws = qk.new_workspace(qk.gemm_workspace_size(dm, dn, dk), dev)
         dsets = []
         for r in range(args.ring):
             d = wl.generate(dcfg, seed=r)
@@ -253,7 +331,9 @@ def main():
         def dstep_fn(bs):
             return lambda: qk.linear_w8a8(bs["x"], bs["w"], bs["s_ch"], out=bs["out"], workspace=ws)
 
-        dms, _ = timed_replays([dstep_fn(b) for b in dsets], args.decode_calls, args.warmup)
+        dstats = {}
+        dms, _ = timed_replays([dstep_fn(b) for b in dsets], args.decode_calls, args.warmup,
+                               stats=dstats)
         dbytes = dk * dn + 4 * dn + 2 * dm * dk + 2 * dm * dn
         gbs = dbytes / (dms * 1e-3) / 1e9
         result["decode"] = {
@@ -261,6 +341,7 @@ def main():
             "workload": "decode_m1", "m": dm, "k": dk, "n": dn,
             "value": round(gbs, 1), "unit": "GB/s",
             "us_per_call": round(dms * 1e3, 3), "algorithmic_bytes_per_call": dbytes,
+            "timing": dstats,
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "roofline": {"bound": "hbm", "kernel": "gemv_kernel (fused quantization)",
                          "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -476,7 +557,7 @@ def main():
         # 8-row decode: the fused linear, HBM-bound like the 1-row one
         ocfg = wl.WORKLOADS["decode_m8"]
         om, ok, on = ocfg.m, ocfg.k, ocfg.n
-        ows = torch.zeros(qk.gemm_workspace_size(om, on, ok), dtype=torch.uint8, device=dev)
+        ows = qk.new_workspace(qk.gemm_workspace_size(om, on, ok), dev)
         osets = []
         for r in range(args.ring):
             d = wl.generate(ocfg, seed=r)
@@ -518,7 +599,7 @@ def main():
                                                  dtype=torch.int8),
                               "s_ch": torch.empty(sn, device=dev).uniform_(1e-3, 1e-2, generator=gen),
                               "out": torch.empty((sm, sn), dtype=torch.bfloat16, device=dev)})
-            sws = torch.zeros(qk.gemm_workspace_size(sm, sn, sk), dtype=torch.uint8, device=dev)
+            sws = qk.new_workspace(qk.gemm_workspace_size(sm, sn, sk), dev)
             sms, _ = timed_replays([(lambda bs=b: qk.linear_w8a8(bs["x"], bs["w"], bs["s_ch"],
                                                                  out=bs["out"], workspace=sws))
                                     for b in ssets], ssteps, args.warmup)

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QK_ABI_VERSION 5
+#define QK_ABI_VERSION 6
 
 /* element types */
 #define QK_F32 0
@@ -136,6 +136,29 @@ int qk_silu_mul_quant_per_token(int m, int d, const void *h, int h_dtype, int8_t
 size_t qk_gemm_workspace_size(int m, int n, int k);
 
 /*
+ * Prepares a workspace for the calls that take one: enqueues, on `stream`, a
+ * kernel that sets all `workspace_bytes` bytes to zero (a kernel, not a
+ * memset, so that the call may be captured in a HIP graph).  The caller
+ * allocates and owns the workspace ("16. Deploying Custom Kernels", C++
+ * Kernel Interface: caller-owned buffers, a status return); the library
+ * keeps it zero from then on:
+ *   - call it once on a new workspace before its first use (memory from an
+ *     allocator holds arbitrary bytes);
+ *   - every call that uses the workspace and returns QK_OK leaves it all
+ *     zeros when its work completes, so later calls issued in order on one
+ *     stream need no further initialization;
+ *   - after a call returns a HIP launch error (a status below 1000 other
+ *     than QK_OK), part of its work may have run: call this again before the
+ *     workspace is reused.  Host-detected errors (QK_ERR_*) enqueue nothing
+ *     and leave the workspace as it was.
+ *   workspace        device memory, 256-byte aligned (NULL only with 0 bytes).
+ *   workspace_bytes  any size; usually qk_gemm_workspace_size(m, n, k).
+ * Errors: NULL with workspace_bytes > 0 (QK_ERR_INVALID_VALUE); misaligned
+ * (QK_ERR_WORKSPACE).
+ */
+int qk_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * INT8 GEMM with INT32 accumulation and the dequant epilogue
  * ("16. Deploying Custom Kernels", C++ Kernel Interface and Python Bindings
  * for the first nine arguments; "KV-cache kernels", 02 Scales and
@@ -154,13 +177,14 @@ size_t qk_gemm_workspace_size(int m, int n, int k);
  *   out      [m][n] of out_dtype (QK_F32 or QK_BF16) or NULL; c and out may
  *            not both be NULL.
  *   workspace / workspace_bytes: device memory of at least
- *            qk_gemm_workspace_size(m, n, k) bytes, 256-byte aligned, zero
- *            filled before its first use by this library; every call
- *            returns it to all zeros when it completes, so one buffer serves
- *            all calls issued in order on a stream.  Calls that can run at
- *            the same time must not share one.  May be NULL when the size is 0;
- *            otherwise a missing or short workspace is QK_ERR_WORKSPACE on
- *            the decode path, while the tiled GEMM then runs unsplit.
+ *            qk_gemm_workspace_size(m, n, k) bytes, 256-byte aligned, set up
+ *            by qk_workspace_init before its first use; every successful
+ *            call returns it to all zeros when it completes, so one buffer
+ *            serves all calls issued in order on a stream.  Calls that can
+ *            run at the same time must not share one.  May be NULL when the
+ *            size is 0; otherwise a missing or short workspace is
+ *            QK_ERR_WORKSPACE on the decode path, while the tiled GEMM then
+ *            runs unsplit.
  * Requirements: 0 <= k <= QK_MAX_K and k % 16 == 0; a, b 16-byte aligned;
  * for the tiled (m > 8) kernel m*k and n*k below 2^32 (QK_ERR_UNSUPPORTED
  * otherwise).  k == 0 gives acc = 0.
@@ -184,7 +208,9 @@ int qk_gemm_i8_scaled_ex(int m, int n, int k, const int8_t *a, const int8_t *b, 
  * qk_gemm_i8_scaled with scale_a = the per-token scales).
  *   x        [m][k] of x_dtype (QK_F32, QK_BF16, QK_F16).
  *   b        [k][n] (QK_B_KN) or [n][k] (QK_B_NK) int8; scale_b [n] float.
- *   out      [m][n] of out_dtype (QK_F32 or QK_BF16).
+ *   out      [m][n] of out_dtype (QK_F32 or QK_BF16), or NULL.
+ *   c_out    [m][n] int32 raw accumulators, or NULL; c_out and out may not
+ *            both be NULL.
  *   q_out, scale_out: [m][k] int8 codes and [m] scales.  Optional when the
  *            call runs as one fused decode launch (m <= 8, [k][n] weight,
  *            x 16-byte aligned, kernel AUTO or GEMV); then they receive the
@@ -198,8 +224,8 @@ int qk_gemm_i8_scaled_ex(int m, int n, int k, const int8_t *a, const int8_t *b, 
  */
 int qk_linear_w8a8(int m, int n, int k, const void *x, int x_dtype, const int8_t *b,
                    const float *scale_b, float output_scale, void *out, int out_dtype,
-                   int b_layout, int8_t *q_out, float *scale_out, void *workspace,
-                   size_t workspace_bytes, int kernel, hipStream_t stream);
+                   int b_layout, int8_t *q_out, float *scale_out, int32_t *c_out,
+                   void *workspace, size_t workspace_bytes, int kernel, hipStream_t stream);
 
 /* ------------------------------------------------------------------ */
 /* FP8 path: float8_e4m3fn activations and weights                     */

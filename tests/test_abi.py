@@ -133,9 +133,9 @@ def test_quant_argument_errors_are_reported_before_launch(lib):
 
 
 def _linear(lib, m, n, k, x=FAKE, xdt=1, b=FAKE, sb=FAKE, out=FAKE, odt=1, layout=0, q=NULL,
-            s=NULL, ws=NULL, ws_bytes=0, kernel=0):
-    return lib.qk_linear_w8a8(m, n, k, x, xdt, b, sb, 1.0, out, odt, layout, q, s, ws, ws_bytes,
-                              kernel, NULL)
+            s=NULL, cc=NULL, ws=NULL, ws_bytes=0, kernel=0):
+    return lib.qk_linear_w8a8(m, n, k, x, xdt, b, sb, 1.0, out, odt, layout, q, s, cc, ws,
+                              ws_bytes, kernel, NULL)
 
 
 def test_linear_argument_errors_are_reported_before_launch(lib):
@@ -145,14 +145,25 @@ def test_linear_argument_errors_are_reported_before_launch(lib):
     assert _linear(lib, 4, 4, 16, xdt=7) == INVALID
     assert _linear(lib, 4, 4, 16, odt=2) == INVALID
     assert _linear(lib, 4, 4, 24) == UNSUP
-    assert _linear(lib, 4, 4, 16, out=NULL) == INVALID
+    assert _linear(lib, 4, 4, 16, out=NULL) == INVALID      # neither out nor c_out
     assert _linear(lib, 4, 4, 16, sb=NULL) == INVALID
+    assert _linear(lib, 4, 4, 16, cc=FAKE_ODD) == UNSUP
+    assert _linear(lib, 4, 4, 16, out=NULL, sb=NULL, cc=FAKE, odt=9) == c["QK_ERR_WORKSPACE"]
     assert _linear(lib, 4, 4, 16, b=FAKE_ODD) == UNSUP
     assert _linear(lib, 64, 4, 16) == INVALID              # tiled path needs q and scale
     assert _linear(lib, 4, 4, 16, layout=1) == INVALID     # [n][k] weight: tiled path too
     assert _linear(lib, 17, 4, 16, kernel=2) == UNSUP
     assert _linear(lib, 4, 4, 16) == c["QK_ERR_WORKSPACE"]  # fused decode launch needs one
     assert _linear(lib, 0, 4, 16, x=NULL, b=NULL) == 0
+
+
+def test_workspace_init_argument_errors_are_reported_before_launch(lib):
+    c = _header_constants()
+    size_t = ctypes.c_size_t
+    assert lib.qk_workspace_init(NULL, size_t(0), NULL) == 0          # nothing to prepare
+    assert lib.qk_workspace_init(FAKE, size_t(0), NULL) == 0
+    assert lib.qk_workspace_init(NULL, size_t(256), NULL) == c["QK_ERR_INVALID_VALUE"]
+    assert lib.qk_workspace_init(ctypes.c_void_p(0x100010), size_t(256), NULL) == c["QK_ERR_WORKSPACE"]
 
 
 def test_binding_rejects_cpu_tensors():

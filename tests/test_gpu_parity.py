@@ -305,8 +305,7 @@ def test_gemm_repeatable_and_workspace_left_zero():
     w = torch.from_numpy(d["w"]).to(DEV)
     s_ch = torch.from_numpy(d["s_ch"]).to(DEV)
     q, s = qk.quant_per_token(x)
-    ws = torch.zeros(qk.gemm_workspace_size(8, w.shape[1], w.shape[0]), dtype=torch.uint8,
-                     device=DEV)
+    ws = qk.new_workspace(qk.gemm_workspace_size(8, w.shape[1], w.shape[0]), DEV)
     outs = [qk.gemm_i8_scaled(q, w, s, s_ch, return_acc=True, kernel="gemv", workspace=ws)
             for _ in range(3)]
     torch.cuda.synchronize()
@@ -332,20 +331,33 @@ def test_gemm_on_a_side_stream():
 # the named workloads, end to end, in the launch configuration of bench.py
 # --------------------------------------------------------------------------
 
-def _sample_entries(m, n, rng, count=4096):
-    rows = np.concatenate([rng.integers(0, m, count), [0, m - 1, m - 1, 0]])
-    cols = np.concatenate([rng.integers(0, n, count), [0, n - 1, 0, n - 1]])
-    return rows.astype(np.int64), cols.astype(np.int64)
+def _compare_rows_in_chunks(name, q_ref, s_ref, w_host, s_ch, c_dev, out_dev, out_dtype,
+                            max_elems=1 << 26):
+    """Every INT32 accumulator and every output of a GEMM against the oracle,
+    a block of rows at a time so that host memory stays bounded (the MLP
+    up-projection's 8192 x 28672 accumulators are 940 MB)."""
+    m, n = c_dev.shape
+    rows = max(1, max_elems // n)
+    for r0 in range(0, m, rows):
+        r1 = min(m, r0 + rows)
+        c_ref = oracle.gemm_i32(q_ref[r0:r1], w_host)
+        assert_equal_exact(host(c_dev[r0:r1]), c_ref, f"{name} acc rows {r0}..{r1 - 1}")
+        assert_out_close(host(out_dev[r0:r1]), oracle.dequant(c_ref, s_ref[r0:r1], s_ch),
+                         out_dtype, f"{name} out rows {r0}..{r1 - 1}")
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "decode_m1", "decode_m8", "prefill_outliers",
                                   "gated_down", "mlp_up"])
 def test_workload_end_to_end(name):
+    # The named workloads at their full sizes, in the launch configuration
+    # bench.py times (quantization kernel, then the GEMM the shape selects):
+    # codes, scales, every INT32 accumulator and every output element
+    # against the oracle.
     d = wl.generate(name)
     w_cfg = d["workload"]
-    w_host = d["w"]
+    w_host, s_ch_host = d["w"], d["s_ch"]
     w = torch.from_numpy(w_host).to(DEV)
-    s_ch = torch.from_numpy(d["s_ch"]).to(DEV)
+    s_ch = torch.from_numpy(s_ch_host).to(DEV)
     if w_cfg.gated:
         q, s = qk.silu_mul_quant_per_token(d["h"].to(DEV))
         q_ref, s_ref = oracle.silu_mul_quantize(wl.bits(d["h"]), DTYPE_CODE[w_cfg.x_dtype])
@@ -354,39 +366,16 @@ def test_workload_end_to_end(name):
         q_ref, s_ref = oracle.quantize_input(wl.bits(d["x"]), DTYPE_CODE[w_cfg.x_dtype])
     assert_equal_exact(host(s), s_ref, f"{name} scale")
     assert_equal_exact(host(q), q_ref, f"{name} codes")
+    del d
 
     out = qk.gemm_i8_scaled(q, w, s, s_ch, out_dtype=TORCH_OUT[w_cfg.out_dtype])
     out_acc, c = qk.gemm_i8_scaled(q, w, s, s_ch, out_dtype=TORCH_OUT[w_cfg.out_dtype],
                                    return_acc=True)
-    out_h = host(out)
-    assert np.array_equal(out_h.view(np.uint8), host(out_acc).view(np.uint8))
-    c_h = host(c)
-    m, n = w_cfg.m, w_cfg.n
-    rng = np.random.default_rng(_seed("e2e", name))
-    if m * n * w_cfg.k <= 2**28:
-        c_ref = oracle.gemm_i32(q_ref, w_host)
-        assert_equal_exact(c_h, c_ref, f"{name} acc")
-        assert_out_close(out_h, oracle.dequant(c_ref, s_ref, d["s_ch"]), w_cfg.out_dtype, name)
-        return
-    # full rows at a few positions (tile edges included) ...
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, m - 1], rng.integers(0, m, 7)]))
-    rows = rows[rows < m]
-    c_rows = oracle.gemm_i32(q_ref[rows], w_host)
-    assert_equal_exact(c_h[rows], c_rows, f"{name} acc rows")
-    assert_out_close(out_h[rows], oracle.dequant(c_rows, s_ref[rows], d["s_ch"]),
-                     w_cfg.out_dtype, f"{name} rows")
-    # ... and scattered single entries
-    r, cc = _sample_entries(m, n, rng)
-    c_ent = oracle.gemm_entries(q_ref, w_host, r, cc)
-    assert_equal_exact(c_h[r, cc], c_ent, f"{name} acc entries")
-    assert_out_close(out_h[r, cc], oracle.dequant_entries(c_ent, s_ref[r], d["s_ch"][cc]),
-                     w_cfg.out_dtype, f"{name} entries")
-    # and a property over every entry: |out| is bounded by |acc| s_a s_b (1 + 1e-6)
-    bound = np.abs(c_h.astype(np.float64)) * s_ref[:, None].astype(np.float64) \
-        * d["s_ch"][None, :].astype(np.float64)
-    outf = torch.from_numpy(out_h.view(np.int16)).view(torch.bfloat16).float().numpy() \
-        if w_cfg.out_dtype == "bf16" else out_h
-    assert np.all(np.abs(outf.astype(np.float64)) <= bound * (1 + 2.0 ** -7) + 1e-30)
+    # the two launches (with and without the accumulator output) agree bit for bit
+    assert torch.equal(out.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32),
+                       out_acc.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32))
+    del out_acc, q, s
+    _compare_rows_in_chunks(name, q_ref, s_ref, w_host, s_ch_host, c, out, w_cfg.out_dtype)
 
 
 # --------------------------------------------------------------------------
@@ -440,13 +429,40 @@ def test_linear_decode_matrix_core_rows(m, k, n, x_dtype):
 
 @pytest.mark.parametrize("name", ["decode_m1", "decode_m8"])
 def test_linear_decode_workloads(name):
+    # the fused single-launch decode linear at the full decode shapes: codes,
+    # scales and every INT32 accumulator bit-exact, every output within the bar
     d = wl.generate(name)
     wcfg = d["workload"]
-    out = qk.linear_w8a8(d["x"].to(DEV), torch.from_numpy(d["w"]).to(DEV),
-                         torch.from_numpy(d["s_ch"]).to(DEV), TORCH_OUT[wcfg.out_dtype])
+    out, q, s, c = qk.linear_w8a8(d["x"].to(DEV), torch.from_numpy(d["w"]).to(DEV),
+                                  torch.from_numpy(d["s_ch"]).to(DEV), TORCH_OUT[wcfg.out_dtype],
+                                  return_codes=True, return_acc=True)
     q_ref, s_ref, c_ref, out_ref = oracle.linear(wl.bits(d["x"]), DTYPE_CODE[wcfg.x_dtype], d["w"],
                                                  d["s_ch"])
+    assert_equal_exact(host(s), s_ref, f"{name} scale")
+    assert_equal_exact(host(q), q_ref, f"{name} codes")
+    assert_equal_exact(host(c), c_ref, f"{name} acc")
     assert_out_close(host(out), out_ref, wcfg.out_dtype, name)
+    # the launch bench.py times (no optional outputs) writes the same outputs
+    out2 = qk.linear_w8a8(d["x"].to(DEV), torch.from_numpy(d["w"]).to(DEV),
+                          torch.from_numpy(d["s_ch"]).to(DEV), TORCH_OUT[wcfg.out_dtype])
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+
+
+@pytest.mark.parametrize("m,k,n,kernel", [(1, 4096, 1000, "gemv"), (8, 4096, 2048, "gemv"),
+                                          (3, 1024, 272, "gemv"), (300, 1024, 512, "mfma")])
+def test_linear_accumulator_output(m, k, n, kernel):
+    # c_out of the whole-layer call: raw INT32 accumulators, alone or beside out
+    rng = np.random.default_rng(_seed("lin-acc", m, k, n))
+    x = wl.random_activations(rng, m, k, "bf16", outlier_cols=max(1, k // 100))
+    w = wl.random_weight(rng, k, n)
+    s_ch = wl.random_channel_scales(rng, n)
+    xd, wd, sd = x.to(DEV), torch.from_numpy(w).to(DEV), torch.from_numpy(s_ch).to(DEV)
+    q_ref, s_ref, c_ref, out_ref = oracle.linear(wl.bits(x), oracle.BF16, w, s_ch)
+    c_only = qk.linear_w8a8(xd, wd, sd, out_dtype=None, kernel=kernel)
+    assert_equal_exact(host(c_only), c_ref, f"{m}x{k}x{n} {kernel} c only")
+    out, c = qk.linear_w8a8(xd, wd, sd, torch.float32, kernel=kernel, return_acc=True)
+    assert_equal_exact(host(c), c_ref, f"{m}x{k}x{n} {kernel} c")
+    assert_out_close(host(out), out_ref, "f32", f"{m}x{k}x{n} {kernel} out")
 
 
 def test_hip_graph_replays_match_eager():
@@ -456,7 +472,7 @@ def test_hip_graph_replays_match_eager():
     pre = wl.generate(wl.Workload("pre_small", 300, 1024, 512, "bf16", "bf16", outlier_cols=10))
     xd, wd, sd = dec["x"].to(DEV), torch.from_numpy(dec["w"]).to(DEV), torch.from_numpy(dec["s_ch"]).to(DEV)
     xp, wp, sp = pre["x"].to(DEV), torch.from_numpy(pre["w"]).to(DEV), torch.from_numpy(pre["s_ch"]).to(DEV)
-    ws = torch.zeros(qk.gemm_workspace_size(8, wd.shape[1], wd.shape[0]), dtype=torch.uint8, device=DEV)
+    ws = qk.new_workspace(qk.gemm_workspace_size(8, wd.shape[1], wd.shape[0]), DEV)
     out_d = torch.empty((8, wd.shape[1]), dtype=torch.bfloat16, device=DEV)
     q = torch.empty((300, 1024), dtype=torch.int8, device=DEV)
     s = torch.empty((300,), dtype=torch.float32, device=DEV)
@@ -513,17 +529,94 @@ def test_gemm_unsplit_shapes_with_workspace(m, n, k, layout):
     _run_gemm_case(m, n, k, layout, "mfma", "bf16")
 
 
-def test_gemm_split_k_closed_forms_and_workspace_left_zero():
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+def test_gemm_split_k_closed_forms_and_workspace_left_zero(layout):
     m, n = 600, 384
     for k, av, bv in ((8192, -128, -128), (4096, 127, -128), (2048, -127, 127), (131072 - 128, -128, -128)):
-        ws = torch.zeros(qk.gemm_workspace_size(m, n, k), dtype=torch.uint8, device=DEV)
+        ws = qk.new_workspace(qk.gemm_workspace_size(m, n, k), DEV)
         assert ws.numel() > 0
         a = torch.full((m, k), av, dtype=torch.int8, device=DEV)
-        b = torch.full((k, n), bv, dtype=torch.int8, device=DEV)
-        c = qk.gemm_i8_scaled(a, b, out_dtype=None, kernel="mfma", workspace=ws)
-        assert bool((c == k * av * bv).all()), (k, av, bv)
+        b = torch.full((k, n) if layout == "kn" else (n, k), bv, dtype=torch.int8, device=DEV)
+        c = qk.gemm_i8_scaled(a, b, out_dtype=None, kernel="mfma", workspace=ws, b_layout=layout)
+        assert bool((c == k * av * bv).all()), (k, av, bv, layout)
         torch.cuda.synchronize()
         assert not ws.any(), "the split-K reduction leaves the workspace zero"
+    # a [N][K] weight whose columns differ, at the largest k: the row stride of
+    # B is k, so a wrong stride mixes columns
+    k = 131072 - 128
+    ws = qk.new_workspace(qk.gemm_workspace_size(m, n, k), DEV)
+    a = torch.full((m, k), -128, dtype=torch.int8, device=DEV)
+    col_vals = torch.arange(n, device=DEV, dtype=torch.int32) % 255 - 127
+    b = col_vals.to(torch.int8)[:, None].expand(n, k).contiguous()
+    if layout == "kn":
+        b = b.t().contiguous()
+    c = qk.gemm_i8_scaled(a, b, out_dtype=None, kernel="mfma", workspace=ws, b_layout=layout)
+    want = (col_vals.to(torch.int64) * (-128 * k)).to(torch.int32)
+    assert torch.equal(c, want[None, :].expand(m, n)), layout
+    torch.cuda.synchronize()
+    assert not ws.any()
+
+
+def test_workspace_init_prepares_dirty_memory():
+    # a workspace straight from the allocator holds arbitrary bytes:
+    # qk_workspace_init zeroes it with the library's own kernel, after which
+    # the decode kernel's settlement and split-K are exact and leave it zero
+    rng = np.random.default_rng(_seed("dirty-ws"))
+    nbytes = max(qk.gemm_workspace_size(2048, 512, 4096), qk.gemm_workspace_size(8, 14336, 4096))
+    for size in (1000, 4096 + 48, nbytes):  # sizes that are not multiples of 16 or 256 too
+        buf = torch.empty(size + 512, dtype=torch.uint8, device=DEV).fill_(0xA5)
+        ws = buf[:size]
+        qk.workspace_init(ws)
+        torch.cuda.synchronize()
+        assert not ws.any(), size
+        assert bool((buf[size:] == 0xA5).all()), "init writes nothing past the workspace"
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    ws.copy_(torch.from_numpy(rng.integers(0, 256, nbytes, dtype=np.uint8)).to(DEV))
+    qk.workspace_init(ws)
+    for m, n, k, kernel in ((2048, 512, 4096, "mfma"), (8, 14336, 4096, "gemv"), (1, 4096, 4096, "gemv"),
+                            (2, 512, 4096, "gemv")):
+        a = rng.integers(-128, 128, size=(m, k), dtype=np.int8)
+        b = rng.integers(-128, 128, size=(k, n), dtype=np.int8)
+        c = qk.gemm_i8_scaled(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV), out_dtype=None,
+                              kernel=kernel, workspace=ws)
+        assert_equal_exact(host(c), oracle.gemm_i32(a, b), f"{m}x{n}x{k} {kernel} after init")
+    torch.cuda.synchronize()
+    assert not ws.any()
+
+
+@pytest.mark.parametrize("case", ["prefill_outliers", "split_k", "moe"])
+def test_tiled_kernels_repeat_bit_identical(case):
+    # the tiled GEMM (k-group hand-over through LDS), the split-K pair of
+    # launches and the MoE launch, three runs each on the same inputs: every
+    # accumulator and output identical
+    rng = np.random.default_rng(_seed("rep3", case))
+    if case == "prefill_outliers":
+        d = wl.generate(case)
+        q, s = qk.quant_per_token(d["x"].to(DEV))
+        w, s_ch = torch.from_numpy(d["w"]).to(DEV), torch.from_numpy(d["s_ch"]).to(DEV)
+        run = lambda: qk.gemm_i8_scaled(q, w, s, s_ch, return_acc=True)
+    elif case == "split_k":
+        m, n, k = 2048, 512, 4096
+        assert qk.gemm_workspace_size(m, n, k) > 0
+        q = torch.from_numpy(rng.integers(-127, 128, size=(m, k), dtype=np.int8)).to(DEV)
+        w = torch.from_numpy(rng.integers(-127, 128, size=(k, n), dtype=np.int8)).to(DEV)
+        s = torch.from_numpy(rng.uniform(1e-3, 1e-1, m).astype(np.float32)).to(DEV)
+        s_ch = torch.from_numpy(wl.random_channel_scales(rng, n)).to(DEV)
+        run = lambda: qk.gemm_i8_scaled(q, w, s, s_ch, return_acc=True, kernel="mfma")
+    else:
+        experts, m, n, k = 8, 4096, 2048, 1024
+        counts = rng.multinomial(m, rng.dirichlet(np.full(experts, 2.0)))
+        offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(DEV)
+        q = torch.from_numpy(rng.integers(-127, 128, size=(m, k), dtype=np.int8)).to(DEV)
+        w = torch.from_numpy(rng.integers(-127, 128, size=(experts, k, n), dtype=np.int8)).to(DEV)
+        s = torch.from_numpy(rng.uniform(1e-3, 1e-1, m).astype(np.float32)).to(DEV)
+        s_ch = torch.from_numpy(rng.uniform(1e-3, 1e-2, (experts, n)).astype(np.float32)).to(DEV)
+        run = lambda: qk.moe_gemm_i8_scaled(q, w, offsets, s, s_ch, return_acc=True)
+    first_out, first_c = run()
+    for _ in range(2):
+        out, c = run()
+        assert torch.equal(c, first_c), case
+        assert torch.equal(out.view(torch.int16), first_out.view(torch.int16)), case
 
 
 def test_hip_graph_replays_of_split_k_match_eager():
@@ -538,8 +631,7 @@ def test_hip_graph_replays_of_split_k_match_eager():
     sb = torch.from_numpy(rng.uniform(1e-3, 1e-2, n).astype(np.float32)).to(DEV)
     dec = wl.generate("decode_m8")
     xd, wd, sd = dec["x"].to(DEV), torch.from_numpy(dec["w"]).to(DEV), torch.from_numpy(dec["s_ch"]).to(DEV)
-    ws = torch.zeros(max(qk.gemm_workspace_size(m, n, k), qk.gemm_workspace_size(8, wd.shape[1], wd.shape[0])),
-                     dtype=torch.uint8, device=DEV)
+    ws = qk.new_workspace(max(qk.gemm_workspace_size(m, n, k), qk.gemm_workspace_size(8, wd.shape[1], wd.shape[0])), DEV)
     ref_s = qk.gemm_i8_scaled(a, b, sa, sb, kernel="mfma", workspace=ws).clone()
     ref_d = qk.linear_w8a8(xd, wd, sd, workspace=ws).clone()
     out_s = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
@@ -567,8 +659,7 @@ def test_hip_graph_replays_of_split_k_match_eager():
 def test_gemm_split_k_then_decode_share_a_workspace():
     # a split-K GEMM and a decode GEMM in turn on one workspace: both exact
     rng = np.random.default_rng(_seed("split-share"))
-    ws = torch.zeros(max(qk.gemm_workspace_size(2048, 512, 4096), qk.gemm_workspace_size(8, 4096, 4096)),
-                     dtype=torch.uint8, device=DEV)
+    ws = qk.new_workspace(max(qk.gemm_workspace_size(2048, 512, 4096), qk.gemm_workspace_size(8, 4096, 4096)), DEV)
     for _ in range(2):
         for (m, n, k, kernel) in ((2048, 512, 4096, "mfma"), (8, 4096, 4096, "gemv"), (2, 512, 4096, "gemv")):
             a = rng.integers(-128, 128, size=(m, k), dtype=np.int8)

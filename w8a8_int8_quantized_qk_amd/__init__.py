@@ -24,7 +24,7 @@ import threading
 
 import torch
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 F32, BF16, F16 = 0, 1, 2
 B_KN, B_NK = 0, 1
 KERNEL_AUTO, KERNEL_MFMA, KERNEL_GEMV = 0, 1, 2
@@ -40,7 +40,8 @@ _KERNELS = {"auto": KERNEL_AUTO, "mfma": KERNEL_MFMA, "gemv": KERNEL_GEMV}
 
 EXPORTED = (
     "qk_abi_version", "qk_status_string", "qk_build_info", "qk_quant_per_token",
-    "qk_silu_mul_quant_per_token", "qk_gemm_workspace_size", "qk_gemm_i8_scaled",
+    "qk_silu_mul_quant_per_token", "qk_gemm_workspace_size", "qk_workspace_init",
+    "qk_gemm_i8_scaled",
     "qk_gemm_i8_scaled_ex", "qk_linear_w8a8", "qk_quant_per_token_fp8",
     "qk_silu_mul_quant_per_token_fp8", "qk_gemm_fp8_scaled", "qk_linear_fp8",
     "qk_gemm_i8_grouped", "qk_moe_gemm_i8_scaled", "qk_quant_static", "qk_silu_mul_quant_static",
@@ -75,12 +76,15 @@ def _declare(lib):
     lib.qk_silu_mul_quant_per_token.restype = I
     lib.qk_gemm_workspace_size.argtypes = [I, I, I]
     lib.qk_gemm_workspace_size.restype = ctypes.c_size_t
+    lib.qk_workspace_init.argtypes = [P, ctypes.c_size_t, P]
+    lib.qk_workspace_init.restype = I
     gemm = [I, I, I, P, P, P, P, P, F, P, I, I, P, ctypes.c_size_t]
     lib.qk_gemm_i8_scaled.argtypes = gemm + [P]
     lib.qk_gemm_i8_scaled.restype = I
     lib.qk_gemm_i8_scaled_ex.argtypes = gemm + [I, P]
     lib.qk_gemm_i8_scaled_ex.restype = I
-    lib.qk_linear_w8a8.argtypes = [I, I, I, P, I, P, P, F, P, I, I, P, P, P, ctypes.c_size_t, I, P]
+    lib.qk_linear_w8a8.argtypes = [I, I, I, P, I, P, P, F, P, I, I, P, P, P, P, ctypes.c_size_t,
+                                   I, P]
     lib.qk_linear_w8a8.restype = I
     lib.qk_quant_per_token_fp8.argtypes = [I, I, P, I, F, P, P, P]
     lib.qk_quant_per_token_fp8.restype = I
@@ -216,20 +220,48 @@ def gemm_workspace_size(m: int, n: int, k: int) -> int:
 _workspaces: dict = {}
 
 
-def workspace_for(device: torch.device, stream_handle: int, nbytes: int) -> torch.Tensor | None:
-    """A zero-filled workspace of at least nbytes for one (device, stream).
+def workspace_init(ws: torch.Tensor, stream=None):
+    """Zero a workspace with libqk's own kernel (qk_workspace_init), on `stream`
+    (default: the current stream of its device)."""
+    _need(ws, "workspace")
+    stream = torch.cuda.current_stream(ws.device) if stream is None else stream
+    _check(library().qk_workspace_init(_ptr(ws), ws.numel() * ws.element_size(),
+                                       ctypes.c_void_p(stream.cuda_stream)))
+    return ws
 
-    libqk leaves the workspace zero after every call, so one buffer serves all
-    calls issued in order on that stream.
+
+def new_workspace(nbytes: int, device, stream=None) -> torch.Tensor | None:
+    """A workspace of nbytes (256-byte aligned device memory from torch's
+    allocator) prepared by qk_workspace_init; None when nbytes is 0."""
+    if nbytes == 0:
+        return None
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace_init(ws, stream)
+
+
+def workspace_for(device: torch.device, stream_handle: int, nbytes: int) -> torch.Tensor | None:
+    """A prepared workspace of at least nbytes for one (device, stream).
+
+    libqk leaves the workspace zero after every successful call, so one buffer
+    serves all calls issued in order on that stream.
     """
     if nbytes == 0:
         return None
     key = (device, stream_handle)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        ws = new_workspace(nbytes, device)
         _workspaces[key] = ws
     return ws
+
+
+def _check_ws(status: int, device, stream_handle: int):
+    """_check for calls that used a cached workspace: after a HIP launch error
+    part of the call may have run, so the workspace is dropped (the next call
+    prepares a fresh one)."""
+    if status != QK_OK and status < 1000:
+        _workspaces.pop((device, stream_handle), None)
+    _check(status)
 
 
 def gemm_i8_scaled(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor | None = None,
@@ -275,42 +307,57 @@ def gemm_i8_scaled(a: torch.Tensor, b: torch.Tensor, scale_a: torch.Tensor | Non
     if workspace is None:
         workspace = workspace_for(dev, stream.cuda_stream, gemm_workspace_size(m, n, k))
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(library().qk_gemm_i8_scaled_ex(
+    _check_ws(library().qk_gemm_i8_scaled_ex(
         m, n, k, _ptr(a), _ptr(b), _ptr(c), _ptr(scale_a if want_out else None),
         _ptr(scale_b if want_out else None), float(output_scale), _ptr(out if want_out else None),
         _OUT_DTYPES[out_dtype] if want_out else F32, layout, _ptr(workspace), ws_bytes,
-        _KERNELS[kernel], ctypes.c_void_p(stream.cuda_stream)))
+        _KERNELS[kernel], ctypes.c_void_p(stream.cuda_stream)), dev, stream.cuda_stream)
     if not want_out:
         return c
     return (out, c) if return_acc else out
 
 
 def linear_w8a8(x: torch.Tensor, w: torch.Tensor, s_ch: torch.Tensor,
-                out_dtype: torch.dtype = torch.bfloat16, b_layout: str = "kn",
+                out_dtype: torch.dtype | None = torch.bfloat16, b_layout: str = "kn",
                 output_scale: float = 1.0, kernel: str = "auto", out: torch.Tensor | None = None,
                 q: torch.Tensor | None = None, scale: torch.Tensor | None = None,
-                return_codes: bool = False, workspace: torch.Tensor | None = None):
+                return_codes: bool = False, workspace: torch.Tensor | None = None,
+                return_acc: bool = False, c: torch.Tensor | None = None):
     """The whole layer in one call: per-token quantization of x, INT8 GEMM, dequant.
 
     Decode shapes (m <= 8, [k, n] weight) run as one fused launch.  Otherwise
     the codes and scales go through q / scale (allocated when not given).
-    Returns out, or (out, q, scale) when return_codes.
+    Returns out; with return_codes also q and scale, with return_acc also the
+    raw int32 accumulators c (in that order: out, q, scale, c).  out_dtype
+    None (and no out) writes only c.
     """
     _need(x, "x", ndim=2)
     if x.dtype not in _IN_DTYPES:
         raise TypeError(f"x dtype {x.dtype} not supported")
     dev = x.device
     _need(w, "w", torch.int8, 2, dev)
-    _need(s_ch, "s_ch", torch.float32, 1, dev)
     layout = _LAYOUTS[b_layout]
     m, k = x.shape
     n, kb = (w.shape[1], w.shape[0]) if layout == B_KN else (w.shape[0], w.shape[1])
     if kb != k:
         raise ValueError(f"inner dimensions differ: x has k={k}, w has {kb}")
-    if out_dtype not in _OUT_DTYPES:
-        raise TypeError(f"out dtype {out_dtype} not supported")
-    out = torch.empty((m, n), dtype=out_dtype, device=dev) if out is None else out
-    _need(out, "out", out_dtype, 2, dev)
+    want_out = out is not None or out_dtype is not None
+    if want_out:
+        out_dtype = out.dtype if out is not None else out_dtype
+        if out_dtype not in _OUT_DTYPES:
+            raise TypeError(f"out dtype {out_dtype} not supported")
+        out = torch.empty((m, n), dtype=out_dtype, device=dev) if out is None else out
+        _need(out, "out", out_dtype, 2, dev)
+        _need(s_ch, "s_ch", torch.float32, 1, dev)
+        if tuple(out.shape) != (m, n) or s_ch.shape[0] != n:
+            raise ValueError("out must be [m, n] and s_ch [n]")
+    if return_acc or not want_out:
+        c = torch.empty((m, n), dtype=torch.int32, device=dev) if c is None else c
+        _need(c, "c", torch.int32, 2, dev)
+        if tuple(c.shape) != (m, n):
+            raise ValueError("c must be [m, n]")
+    else:
+        c = None
     fused = (m <= 8 and layout == B_KN and kernel != "mfma") or kernel == "gemv"
     if (return_codes or not fused) and q is None:
         q = torch.empty((m, k), dtype=torch.int8, device=dev)
@@ -324,11 +371,18 @@ def linear_w8a8(x: torch.Tensor, w: torch.Tensor, s_ch: torch.Tensor,
     if workspace is None:
         workspace = workspace_for(dev, stream.cuda_stream, gemm_workspace_size(m, n, k))
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(library().qk_linear_w8a8(
-        m, n, k, _ptr(x), _IN_DTYPES[x.dtype], _ptr(w), _ptr(s_ch), float(output_scale),
-        _ptr(out), _OUT_DTYPES[out_dtype], layout, _ptr(q), _ptr(scale), _ptr(workspace),
-        ws_bytes, _KERNELS[kernel], ctypes.c_void_p(stream.cuda_stream)))
-    return (out, q, scale) if return_codes else out
+    _check_ws(library().qk_linear_w8a8(
+        m, n, k, _ptr(x), _IN_DTYPES[x.dtype], _ptr(w), _ptr(s_ch if want_out else None),
+        float(output_scale), _ptr(out if want_out else None),
+        _OUT_DTYPES[out_dtype] if want_out else F32, layout, _ptr(q), _ptr(scale), _ptr(c),
+        _ptr(workspace), ws_bytes, _KERNELS[kernel], ctypes.c_void_p(stream.cuda_stream)),
+        dev, stream.cuda_stream)
+    res = (out,) if want_out else ()
+    if return_codes:
+        res += (q, scale)
+    if return_acc or not want_out:
+        res += (c,)
+    return res[0] if len(res) == 1 else res
 
 
 def gated_linear_w8a8(h: torch.Tensor, w: torch.Tensor, s_ch: torch.Tensor,

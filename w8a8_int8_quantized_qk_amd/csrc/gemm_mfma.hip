@@ -730,9 +730,14 @@ hipError_t launch_splitk(const GemmArgs& g, const SplitKPlan& p, hipStream_t str
   if (e != hipSuccess) return e;
   const long long quads = static_cast<long long>(g.m) * g.n / 4;
   const long long blocks = (quads + 255) / 256;
-  return launch(splitk_reduce_kernel, dim3(static_cast<unsigned>(blocks < 16384 ? blocks : 16384)),
-                dim3(256), 0, stream, part, p.splits, quads, g.n, g.c, g.scale_a, g.scale_b,
-                g.output_scale, g.out, g.out_dtype);
+  e = launch(splitk_reduce_kernel, dim3(static_cast<unsigned>(blocks < 16384 ? blocks : 16384)),
+             dim3(256), 0, stream, part, p.splits, quads, g.n, g.c, g.scale_a, g.scale_b,
+             g.output_scale, g.out, g.out_dtype);
+  // the partial sums are already enqueued: without the reduction nothing
+  // would clear them, so try to return the workspace to zero (the caller is
+  // told to re-initialize it after a launch error in any case)
+  if (e != hipSuccess) (void)launch_zero_fill(part, p.bytes, stream);
+  return e;
 }
 
 }  // namespace

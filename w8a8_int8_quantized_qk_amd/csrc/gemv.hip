@@ -74,9 +74,14 @@ static_assert(kCols == kThreads, "one output column per thread in the reduction"
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // rounds of weight loads (4 x 16 bytes per lane each) kept in flight ahead of
-// the round being multiplied; more rows need more accumulator registers
-template <int MR, int ROUNDS>
+// the round being multiplied; more rows need more accumulator registers.  A
+// weight whose width is not a multiple of 16 is read byte by byte (64 loads
+// per lane and round, each its own register until the bytes are combined),
+// so with 4 or more rows only one round is kept in flight: two overflow the
+// 256 registers.
+template <int MR, int ROUNDS, bool N16>
 constexpr int prefetch_for() {
+  if (!N16 && MR >= 4) return 1;
   return (MR <= 2 ? ROUNDS - 1 : (MR == 4 ? 4 : 2)) < ROUNDS - 1
              ? (MR <= 2 ? ROUNDS - 1 : (MR == 4 ? 4 : 2))
              : ROUNDS - 1;
@@ -86,9 +91,11 @@ constexpr int prefetch_for() {
 // the quantization (and with it every wave's first multiply).  With more
 // rows the quantization takes longer and a second round fits under it
 // (measured: 4 rows 16.3 -> 15.9 us, 8 rows 22.4 -> 21.9 us; 1 row best
-// with one).
-template <int MR, int ROUNDS>
-constexpr int early_rounds_for() { return MR == 1 || ROUNDS <= 2 ? 1 : 2; }
+// with one).  Never more than the rounds kept in flight.
+template <int MR, int ROUNDS, bool N16>
+constexpr int early_rounds_for() {
+  return MR == 1 || ROUNDS <= 2 || prefetch_for<MR, ROUNDS, N16>() < 2 ? 1 : 2;
+}
 
 __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
                                              uint32_t* col) {
@@ -316,8 +323,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     float* __restrict__ s_out, unsigned long long* __restrict__ ws, int col_tiles, int splits) {
   constexpr int kRowsK = 64 * ROUNDS;  // this instance's k slice
   constexpr int kRounds = ROUNDS;
-  constexpr int PD = prefetch_for<MR, ROUNDS>();
-  constexpr int kEarlyRounds = early_rounds_for<MR, ROUNDS>();
+  constexpr int PD = prefetch_for<MR, ROUNDS, N16>();
+  constexpr int kEarlyRounds = early_rounds_for<MR, ROUNDS, N16>();
   static_assert(PD >= kEarlyRounds && PD < kRounds, "prefetch distance");
   __shared__ int32_t q_lds[MR][kRowsK / 4];  // codes of this k slice, 4 per word
   __shared__ float s_row[MR];

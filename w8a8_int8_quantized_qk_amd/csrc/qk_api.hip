@@ -7,6 +7,34 @@
 #define QK_STR2(x) #x
 #define QK_STR(x) QK_STR2(x)
 
+namespace qk {
+namespace {
+
+// 16 bytes per lane, grid-stride; the last (bytes % 16) bytes one per thread
+// of the first workgroup.
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* __restrict__ p, size_t n16,
+                                                        unsigned char* __restrict__ tail,
+                                                        unsigned ntail) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * 256;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return hipSuccess;
+  const size_t n16 = bytes / 16;
+  const unsigned ntail = static_cast<unsigned>(bytes % 16);
+  const size_t want = (n16 + 255) / 256;
+  const unsigned blocks = static_cast<unsigned>(want == 0 ? 1 : (want < 4096 ? want : 4096));
+  return launch(zero_fill_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<uint4*>(p), n16,
+                static_cast<unsigned char*>(p) + n16 * 16, ntail);
+}
+
+}  // namespace qk
+
 namespace {
 
 bool aligned(const void* p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; }
@@ -67,6 +95,70 @@ int gemm_common(int m, int n, int k, const int8_t* a, const int8_t* b, int32_t* 
   return status_of(qk::launch_gemm_mfma(g, stream));
 }
 
+// Host checks of the whole-layer call (both entry points).  On QK_OK, *noop
+// tells that there is nothing to do (m or n is 0) and *fused which path runs:
+// the single decode launch or quantization + tiled GEMM.
+int linear_check(int m, int n, int k, const void* x, int x_dtype, const int8_t* b,
+                 const float* scale_b, const void* out, int out_dtype, int b_layout,
+                 const int8_t* q_out, const float* scale_out, const int32_t* c_out, int kernel,
+                 bool* fused, bool* noop) {
+  if (m < 0 || n < 0 || k < 0 || k > QK_MAX_K) return QK_ERR_INVALID_VALUE;
+  if (!known_input_dtype(x_dtype)) return QK_ERR_INVALID_VALUE;
+  if (b_layout != QK_B_KN && b_layout != QK_B_NK) return QK_ERR_INVALID_VALUE;
+  if (kernel != QK_KERNEL_AUTO && kernel != QK_KERNEL_MFMA && kernel != QK_KERNEL_GEMV)
+    return QK_ERR_INVALID_VALUE;
+  if (out && out_dtype != QK_F32 && out_dtype != QK_BF16) return QK_ERR_INVALID_VALUE;
+  if (k % 16 != 0) return QK_ERR_UNSUPPORTED;
+  *noop = m == 0 || n == 0;
+  if (*noop) return QK_OK;
+  if (!out && !c_out) return QK_ERR_INVALID_VALUE;
+  if ((out && !scale_b) || (k > 0 && (!x || !b))) return QK_ERR_INVALID_VALUE;
+  if (!aligned(b, 16) || !aligned(x, x_dtype == QK_F32 ? 4 : 2)) return QK_ERR_UNSUPPORTED;
+  if (out && !aligned(out, out_dtype == QK_BF16 ? 2 : 4)) return QK_ERR_UNSUPPORTED;
+  if (c_out && !aligned(c_out, 4)) return QK_ERR_UNSUPPORTED;
+  if (q_out && !aligned(q_out, 16)) return QK_ERR_UNSUPPORTED;
+  if (scale_out && !aligned(scale_out, 4)) return QK_ERR_UNSUPPORTED;
+
+  if (kernel == QK_KERNEL_GEMV) {
+    if (m > qk::kGemvMaxM || b_layout != QK_B_KN) return QK_ERR_UNSUPPORTED;
+    *fused = true;
+  } else if (kernel == QK_KERNEL_MFMA) {
+    *fused = false;
+  } else {
+    *fused = m <= qk::kGemvMaxRows && b_layout == QK_B_KN;
+  }
+  if (*fused && !aligned(x, 16)) {
+    if (kernel == QK_KERNEL_GEMV) return QK_ERR_UNSUPPORTED;
+    *fused = false;  // the fused launch reads x with 128-bit loads
+  }
+  if (!*fused) {
+    // two launches: the codes and scales go through q_out / scale_out
+    if (!q_out || !scale_out) return QK_ERR_INVALID_VALUE;
+    if (!qk::gemm_mfma_supported(m, n, k)) return QK_ERR_UNSUPPORTED;
+  }
+  return QK_OK;
+}
+
+// Enqueues a checked whole-layer call; the workspace (valid and large enough
+// for the decode launch when `fused`) lets the tiled GEMM split k when its
+// partial sums fit.
+int linear_launch(int m, int n, int k, const void* x, int x_dtype, const int8_t* b,
+                  const float* scale_b, float output_scale, void* out, int out_dtype,
+                  int b_layout, int8_t* q_out, float* scale_out, int32_t* c_out, bool fused,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (fused) {
+    qk::GemvArgs g{m, n, k, x, x_dtype, b, c_out, nullptr, scale_b, output_scale, out,
+                   out_dtype, q_out, scale_out, workspace};
+    return status_of(qk::launch_gemv(g, stream));
+  }
+  hipError_t e = qk::launch_quant_rows(m, k, x, x_dtype, q_out, scale_out, stream);
+  if (e != hipSuccess) return status_of(e);
+  const bool ws = workspace && aligned(workspace, 256);
+  qk::GemmArgs g{m, n, k, q_out, b, c_out, scale_out, scale_b, output_scale, out, out_dtype,
+                 b_layout, ws ? workspace : nullptr, ws ? workspace_bytes : 0};
+  return status_of(qk::launch_gemm_mfma(g, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -112,10 +204,18 @@ int qk_silu_mul_quant_per_token(int m, int d, const void* h, int h_dtype, int8_t
 size_t qk_gemm_workspace_size(int m, int n, int k) {
   if (m <= 0 || n <= 0 || k < 0) return 0;
   // the decode kernel's words (m <= 16), and the tiled kernel's split-K
-  // partial sums when the output has few tiles ([K][N] weight)
+  // partial sums when the output has few tiles (the plan is the same for
+  // either weight layout)
   const size_t gemv = m <= qk::kGemvMaxM ? qk::gemv_workspace_bytes(n) : 0;
   const size_t split = qk::splitk_plan(m, n, k, QK_B_KN).bytes;
   return gemv > split ? gemv : split;
+}
+
+int qk_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (workspace_bytes == 0) return QK_OK;
+  if (!workspace) return QK_ERR_INVALID_VALUE;
+  if (!aligned(workspace, 256)) return QK_ERR_WORKSPACE;
+  return status_of(qk::launch_zero_fill(workspace, workspace_bytes, stream));
 }
 
 int qk_gemm_i8_scaled(int m, int n, int k, const int8_t* a, const int8_t* b, int32_t* c,
@@ -136,50 +236,15 @@ int qk_gemm_i8_scaled_ex(int m, int n, int k, const int8_t* a, const int8_t* b, 
 
 int qk_linear_w8a8(int m, int n, int k, const void* x, int x_dtype, const int8_t* b,
                    const float* scale_b, float output_scale, void* out, int out_dtype,
-                   int b_layout, int8_t* q_out, float* scale_out, void* workspace,
-                   size_t workspace_bytes, int kernel, hipStream_t stream) {
-  if (m < 0 || n < 0 || k < 0 || k > QK_MAX_K) return QK_ERR_INVALID_VALUE;
-  if (!known_input_dtype(x_dtype)) return QK_ERR_INVALID_VALUE;
-  if (b_layout != QK_B_KN && b_layout != QK_B_NK) return QK_ERR_INVALID_VALUE;
-  if (kernel != QK_KERNEL_AUTO && kernel != QK_KERNEL_MFMA && kernel != QK_KERNEL_GEMV)
-    return QK_ERR_INVALID_VALUE;
-  if (out_dtype != QK_F32 && out_dtype != QK_BF16) return QK_ERR_INVALID_VALUE;
-  if (k % 16 != 0) return QK_ERR_UNSUPPORTED;
-  if (m == 0 || n == 0) return QK_OK;
-  if (!out || !scale_b || (k > 0 && (!x || !b))) return QK_ERR_INVALID_VALUE;
-  if (!aligned(b, 16) || !aligned(x, x_dtype == QK_F32 ? 4 : 2)) return QK_ERR_UNSUPPORTED;
-  if (!aligned(out, out_dtype == QK_BF16 ? 2 : 4)) return QK_ERR_UNSUPPORTED;
-  if (q_out && !aligned(q_out, 16)) return QK_ERR_UNSUPPORTED;
-  if (scale_out && !aligned(scale_out, 4)) return QK_ERR_UNSUPPORTED;
-
-  bool fused;
-  if (kernel == QK_KERNEL_GEMV) {
-    if (m > qk::kGemvMaxM || b_layout != QK_B_KN) return QK_ERR_UNSUPPORTED;
-    fused = true;
-  } else if (kernel == QK_KERNEL_MFMA) {
-    fused = false;
-  } else {
-    fused = m <= qk::kGemvMaxRows && b_layout == QK_B_KN;
-  }
-  if (fused && !aligned(x, 16)) {
-    if (kernel == QK_KERNEL_GEMV) return QK_ERR_UNSUPPORTED;
-    fused = false;  // the fused launch reads x with 128-bit loads
-  }
-  if (fused) {
-    if (!workspace_ok(workspace, workspace_bytes, n)) return QK_ERR_WORKSPACE;
-    qk::GemvArgs g{m, n, k, x, x_dtype, b, nullptr, nullptr, scale_b, output_scale, out,
-                   out_dtype, q_out, scale_out, workspace};
-    return status_of(qk::launch_gemv(g, stream));
-  }
-  // two launches: quantization into q_out / scale_out, then the tiled GEMM
-  if (!q_out || !scale_out) return QK_ERR_INVALID_VALUE;
-  if (!qk::gemm_mfma_supported(m, n, k)) return QK_ERR_UNSUPPORTED;
-  hipError_t e = qk::launch_quant_rows(m, k, x, x_dtype, q_out, scale_out, stream);
-  if (e != hipSuccess) return status_of(e);
-  const bool ws = workspace && aligned(workspace, 256);
-  qk::GemmArgs g{m, n, k, q_out, b, nullptr, scale_out, scale_b, output_scale, out, out_dtype,
-                 b_layout, ws ? workspace : nullptr, ws ? workspace_bytes : 0};
-  return status_of(qk::launch_gemm_mfma(g, stream));
+                   int b_layout, int8_t* q_out, float* scale_out, int32_t* c_out,
+                   void* workspace, size_t workspace_bytes, int kernel, hipStream_t stream) {
+  bool fused = false, noop = false;
+  const int rc = linear_check(m, n, k, x, x_dtype, b, scale_b, out, out_dtype, b_layout, q_out,
+                              scale_out, c_out, kernel, &fused, &noop);
+  if (rc != QK_OK || noop) return rc;
+  if (fused && !workspace_ok(workspace, workspace_bytes, n)) return QK_ERR_WORKSPACE;
+  return linear_launch(m, n, k, x, x_dtype, b, scale_b, output_scale, out, out_dtype, b_layout,
+                       q_out, scale_out, c_out, fused, workspace, workspace_bytes, stream);
 }
 
 int qk_quant_per_token_fp8(int m, int k, const void* x, int x_dtype, float scale_ub, uint8_t* q,

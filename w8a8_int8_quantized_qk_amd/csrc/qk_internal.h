@@ -54,6 +54,11 @@ struct GemmArgs {
   size_t workspace_bytes;
 };
 
+// Sets `bytes` bytes at p (16-byte aligned) to zero with a kernel on `stream`
+// (qk_api.hip); used to prepare workspaces and to clear partial sums after a
+// failed launch.
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
+
 // Per-token quantization, one workgroup per row (quant.hip).
 hipError_t launch_quant_rows(int m, int k, const void* x, int dtype, int8_t* q, float* scale,
                              hipStream_t stream);
