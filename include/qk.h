@@ -74,6 +74,7 @@ extern "C" {
 #define QK_ERR_INVALID_VALUE 1001 /* negative size, NULL pointer, unknown enum */
 #define QK_ERR_UNSUPPORTED 1002   /* a size or alignment this library does not handle */
 #define QK_ERR_WORKSPACE 1003     /* workspace missing, misaligned or too small */
+#define QK_ERR_SCRATCH_LIMIT 1004 /* qk_linear_w8a8_noalloc: more scratch needed than it has */
 
 /* Largest reduction length accepted: 131071 * 128 * 128 < 2^31, so no int32
  * accumulator can overflow even for -128 operands ("Skill: Write an INT8
@@ -226,6 +227,36 @@ int qk_linear_w8a8(int m, int n, int k, const void *x, int x_dtype, const int8_t
                    const float *scale_b, float output_scale, void *out, int out_dtype,
                    int b_layout, int8_t *q_out, float *scale_out, int32_t *c_out,
                    void *workspace, size_t workspace_bytes, int kernel, hipStream_t stream);
+
+/* Bytes of device scratch the library holds per GPU for
+ * qk_linear_w8a8_noalloc (16 MiB). */
+#define QK_SCRATCH_BYTES 16777216
+
+/*
+ * qk_linear_w8a8 for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The same layer and arguments without the workspace: in its place the call
+ * uses QK_SCRATCH_BYTES of static device memory inside the library (one copy
+ * per GPU, held until the process ends), and it calls no allocator.  The
+ * caller still passes x, b, scale_b and the outputs (and q_out / scale_out
+ * where qk_linear_w8a8 requires them).
+ *   - The fused decode launch needs 64 bytes of scratch per output column:
+ *     n > QK_SCRATCH_BYTES / 64 = 262144 on that path is QK_ERR_SCRATCH_LIMIT
+ *     (nothing is enqueued).  The tiled GEMM splits k only when its partial
+ *     sums fit in the scratch and otherwise runs unsplit; results are the
+ *     same bits either way.
+ *   - All calls on one GPU share its scratch, which keeps the last call's
+ *     contents (all zeros after a successful call): calls that can overlap on
+ *     one GPU (other streams, other host threads) race and must be ordered by
+ *     the caller.  The first call on a GPU, and the first after a call that
+ *     returned a HIP launch error, clear the scratch with a kernel on `stream`
+ *     before using it.
+ * Requirements and errors otherwise as qk_linear_w8a8.
+ */
+int qk_linear_w8a8_noalloc(int m, int n, int k, const void *x, int x_dtype, const int8_t *b,
+                           const float *scale_b, float output_scale, void *out, int out_dtype,
+                           int b_layout, int8_t *q_out, float *scale_out, int32_t *c_out,
+                           int kernel, hipStream_t stream);
 
 /* ------------------------------------------------------------------ */
 /* FP8 path: float8_e4m3fn activations and weights                     */

@@ -157,6 +157,27 @@ def test_linear_argument_errors_are_reported_before_launch(lib):
     assert _linear(lib, 0, 4, 16, x=NULL, b=NULL) == 0
 
 
+def test_noalloc_linear_errors_are_reported_before_launch(lib):
+    c = _header_constants()
+    assert c["QK_SCRATCH_BYTES"] == qk.SCRATCH_BYTES
+
+    def na(m, n, k, out=FAKE, q=NULL, s=NULL, cc=NULL, kernel=0, layout=0):
+        return lib.qk_linear_w8a8_noalloc(m, n, k, FAKE, 1, FAKE, FAKE, 1.0, out, 1, layout, q, s,
+                                          cc, kernel, NULL)
+
+    assert na(-1, 4, 16) == c["QK_ERR_INVALID_VALUE"]
+    assert na(4, 4, 24) == c["QK_ERR_UNSUPPORTED"]
+    assert na(4, 4, 16, out=NULL) == c["QK_ERR_INVALID_VALUE"]
+    assert na(64, 4, 16) == c["QK_ERR_INVALID_VALUE"]          # tiled path needs q and scale
+    # the decode launch needs 64 bytes of scratch per column: beyond the static
+    # scratch it is refused before anything is enqueued
+    cols = qk.SCRATCH_BYTES // 64
+    assert na(1, cols + 16, 16) == c["QK_ERR_SCRATCH_LIMIT"]
+    assert na(1, cols + 16, 16, kernel=2) == c["QK_ERR_SCRATCH_LIMIT"]
+    assert na(0, 4, 16) == 0
+    assert qk.status_string(c["QK_ERR_SCRATCH_LIMIT"]).startswith("QK_ERR_SCRATCH_LIMIT")
+
+
 def test_workspace_init_argument_errors_are_reported_before_launch(lib):
     c = _header_constants()
     size_t = ctypes.c_size_t

@@ -29,6 +29,7 @@ F32, BF16, F16 = 0, 1, 2
 B_KN, B_NK = 0, 1
 KERNEL_AUTO, KERNEL_MFMA, KERNEL_GEMV = 0, 1, 2
 QK_OK = 0
+SCRATCH_BYTES = 16777216  # static scratch of qk_linear_w8a8_noalloc, per GPU
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqk.so")
@@ -42,7 +43,7 @@ EXPORTED = (
     "qk_abi_version", "qk_status_string", "qk_build_info", "qk_quant_per_token",
     "qk_silu_mul_quant_per_token", "qk_gemm_workspace_size", "qk_workspace_init",
     "qk_gemm_i8_scaled",
-    "qk_gemm_i8_scaled_ex", "qk_linear_w8a8", "qk_quant_per_token_fp8",
+    "qk_gemm_i8_scaled_ex", "qk_linear_w8a8", "qk_linear_w8a8_noalloc", "qk_quant_per_token_fp8",
     "qk_silu_mul_quant_per_token_fp8", "qk_gemm_fp8_scaled", "qk_linear_fp8",
     "qk_gemm_i8_grouped", "qk_moe_gemm_i8_scaled", "qk_quant_static", "qk_silu_mul_quant_static",
     "qk_quant_static_fp8", "qk_silu_mul_quant_static_fp8", "qk_quant_per_token_asym",
@@ -86,6 +87,8 @@ def _declare(lib):
     lib.qk_linear_w8a8.argtypes = [I, I, I, P, I, P, P, F, P, I, I, P, P, P, P, ctypes.c_size_t,
                                    I, P]
     lib.qk_linear_w8a8.restype = I
+    lib.qk_linear_w8a8_noalloc.argtypes = [I, I, I, P, I, P, P, F, P, I, I, P, P, P, I, P]
+    lib.qk_linear_w8a8_noalloc.restype = I
     lib.qk_quant_per_token_fp8.argtypes = [I, I, P, I, F, P, P, P]
     lib.qk_quant_per_token_fp8.restype = I
     lib.qk_silu_mul_quant_per_token_fp8.argtypes = [I, I, P, I, F, P, P, P]

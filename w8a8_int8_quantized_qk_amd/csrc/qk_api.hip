@@ -1,6 +1,7 @@
 // C ABI of libqk: argument validation, kernel choice by shape, launches on the
 // caller's stream.  Declarations and the contract of each call are in qk.h.
 #include <cstdint>
+#include <mutex>
 
 #include "qk_internal.h"
 
@@ -159,6 +160,52 @@ int linear_launch(int m, int n, int k, const void* x, int x_dtype, const int8_t*
   return status_of(qk::launch_gemm_mfma(g, stream));
 }
 
+// ---- static scratch of qk_linear_w8a8_noalloc ----
+// The memory the no-allocation entry point uses in place of a caller's
+// workspace: a file-scope device array, one copy per GPU, held until the
+// process ends.  Its name is a host-side stand-in in host code, so the device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is ever passed to kernels.  The first call
+// on a device, and the first call after a failed launch, clear it on the
+// caller's stream before using it (a kernel, so that a captured call stays
+// valid); every successful call leaves it all zeros again.
+constexpr size_t kScratchBytes = QK_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  void* ptr = nullptr;    // device address of `scratch` on this device
+  bool needs_clear = true;
+};
+std::mutex g_scratch_mutex;
+ScratchSlot g_scratch[kMaxDevices];
+
+hipError_t scratch_for_call(hipStream_t stream, int* dev, void** ptr) {
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return e;
+  if (*dev < 0 || *dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  ScratchSlot& slot = g_scratch[*dev];
+  if (!slot.ptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    slot.ptr = p;
+  }
+  if (slot.needs_clear) {
+    e = qk::launch_zero_fill(slot.ptr, kScratchBytes, stream);
+    if (e != hipSuccess) return e;
+    slot.needs_clear = false;
+  }
+  *ptr = slot.ptr;
+  return hipSuccess;
+}
+
+void scratch_mark_dirty(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  g_scratch[dev].needs_clear = true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,6 +223,10 @@ const char* qk_status_string(int status) {
     case QK_ERR_WORKSPACE:
       return "QK_ERR_WORKSPACE: workspace missing, misaligned, or smaller than "
              "qk_gemm_workspace_size()";
+    case QK_ERR_SCRATCH_LIMIT:
+      return "QK_ERR_SCRATCH_LIMIT: the call needs more than the QK_SCRATCH_BYTES of static "
+             "scratch that qk_linear_w8a8_noalloc uses (the decode launch needs 64 bytes per "
+             "output column)";
     default: return hipGetErrorString(static_cast<hipError_t>(status));
   }
 }
@@ -245,6 +296,27 @@ int qk_linear_w8a8(int m, int n, int k, const void* x, int x_dtype, const int8_t
   if (fused && !workspace_ok(workspace, workspace_bytes, n)) return QK_ERR_WORKSPACE;
   return linear_launch(m, n, k, x, x_dtype, b, scale_b, output_scale, out, out_dtype, b_layout,
                        q_out, scale_out, c_out, fused, workspace, workspace_bytes, stream);
+}
+
+int qk_linear_w8a8_noalloc(int m, int n, int k, const void* x, int x_dtype, const int8_t* b,
+                           const float* scale_b, float output_scale, void* out, int out_dtype,
+                           int b_layout, int8_t* q_out, float* scale_out, int32_t* c_out,
+                           int kernel, hipStream_t stream) {
+  bool fused = false, noop = false;
+  const int rc = linear_check(m, n, k, x, x_dtype, b, scale_b, out, out_dtype, b_layout, q_out,
+                              scale_out, c_out, kernel, &fused, &noop);
+  if (rc != QK_OK || noop) return rc;
+  // the decode launch needs its words; the tiled GEMM splits k only when its
+  // partial sums fit, and otherwise runs unsplit
+  if (fused && qk::gemv_workspace_bytes(n) > kScratchBytes) return QK_ERR_SCRATCH_LIMIT;
+  int dev = 0;
+  void* ptr = nullptr;
+  hipError_t e = scratch_for_call(stream, &dev, &ptr);
+  if (e != hipSuccess) return status_of(e);
+  const int st = linear_launch(m, n, k, x, x_dtype, b, scale_b, output_scale, out, out_dtype,
+                               b_layout, q_out, scale_out, c_out, fused, ptr, kScratchBytes, stream);
+  if (st != QK_OK) scratch_mark_dirty(dev);  // a launch failed after others may have run
+  return st;
 }
 
 int qk_quant_per_token_fp8(int m, int k, const void* x, int x_dtype, float scale_ub, uint8_t* q,
