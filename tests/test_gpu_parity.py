@@ -203,6 +203,21 @@ def test_gemm_mfma_kernel(m, n, k, layout, out_dtype):
     _run_gemm_case(m, n, k, layout, "mfma", out_dtype)
 
 
+# outputs with at least one 256 x 256 tile per CU take the 256 x 256 tile
+# kernel: exact multiples, ragged rows and columns, k tails past a 64-byte
+# slice (k % 64 != 0), one slice, and slices fewer than the four LDS stages
+WIDE_SHAPES = [(4096, 4096, 256), (4000, 4112, 208), (4096, 4096, 16), (4096, 4096, 48),
+               (4096, 4096, 64), (4096, 4096, 128), (4096, 4096, 192), (3900, 4352, 1040),
+               (8192, 2048, 320), (256, 65536, 96)]
+
+
+@pytest.mark.parametrize("m,n,k", WIDE_SHAPES)
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+def test_gemm_wide_tiles(m, n, k, layout):
+    assert ((m + 255) // 256) * ((n + 255) // 256) >= 256  # the shape selects the 256 x 256 tiles
+    _run_gemm_case(m, n, k, layout, "mfma", "bf16" if k % 128 else "f32", output_scale=0.5)
+
+
 @pytest.mark.parametrize("m,n,k", [s for s in GEMM_SHAPES if s[0] <= 16])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_gemm_decode_kernel(m, n, k, out_dtype):

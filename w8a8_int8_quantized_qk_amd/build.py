@@ -21,7 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqk.so")
-SOURCES = ["qk_api.hip", "quant.hip", "quant_static.hip", "gemm_mfma.hip", "gemm_slice.hip", "gemv.hip"]
+SOURCES = ["qk_api.hip", "quant.hip", "quant_static.hip", "gemm_mfma.hip", "gemm_wide.hip",
+           "gemm_slice.hip", "gemv.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

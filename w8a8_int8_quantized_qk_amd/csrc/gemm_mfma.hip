@@ -248,24 +248,26 @@ __device__ __forceinline__ void gemm_i8_tile(
     }
   } else {
     // DMA modes, one k slice per iteration in two phases, every instruction's
-    // place pinned by sched_barrier:
-    //   phase 0: MFMAs of A 0..3 x B 0..1, interleaved with the LDS reads of
-    //            this slice's A 4..7 and B 2..3 and DMA parts [0, kSplit) of
-    //            slice kt + 2 (its LDS stage held slice kt - 1, whose last
-    //            reads, in phase 0 of iteration kt - 1, every wave completed
-    //            before that iteration's barrier);
+    // place pinned by sched_barrier and every fragment read several MFMAs
+    // ahead of its first use:
+    //   phase 0: MFMAs of A 0..3 x B 0..1 (fragments read in the previous
+    //            iteration); this slice's A 4..7 and B 2..3 are read in its
+    //            first half, so the barrier's wait for LDS reads finds them
+    //            done, and DMA parts [0, kSplit) of slice kt + 2 follow (its
+    //            LDS stage held slice kt - 1, whose last reads every wave
+    //            completed before the previous iteration's barrier);
     //   barrier: this wave's DMA of slice kt + 1 has landed (vmcnt), then all
     //            waves' (s_barrier);
-    //   phase 1: the other 24 MFMAs, interleaved with the reads of slice
-    //            kt + 1's A 0..3 and B 0..1 (each into a fragment that has
-    //            just been used for the last time) and the remaining DMA
-    //            parts.
+    //   phase 1: A 4..7 x B 0 and B 1 (then slice kt + 1's B 0..1 are read
+    //            into the freed registers), A 0..3 x B 2..3 (each A register
+    //            refilled with slice kt + 1's fragment after its last MFMA),
+    //            A 4..7 x B 2..3, with the remaining DMA parts in between.
     // The DMA instructions are spread through the MFMA stream because a CU
     // accepts its loads at a limited rate, and a wave waiting to issue one
     // cannot issue its MFMAs either.
     static_assert(FM == 8 && FN == 4, "interleave pattern below");
     constexpr int kSplit = kFetchOps / 2;
-    static_assert(kFetchOps == 2 * kSplit && kSplit >= 3, "three DMA slots per phase");
+    static_assert(kFetchOps == 2 * kSplit && kSplit == 3, "three DMA slots per phase");
     for (int kt = 0; kt < KT; ++kt) {
       const bool prefetch = kt + 2 < KT;
       auto mfma = [&](int i, int j) {
@@ -276,44 +278,50 @@ __device__ __forceinline__ void gemm_i8_tile(
         if (prefetch) fetch_part(kt + 2, part);
         __builtin_amdgcn_sched_barrier(0);
       };
+      auto sb = [] { __builtin_amdgcn_sched_barrier(0); };
       // ---- phase 0 ----
       {
         const char* As = a_lds(kt);
         const char* Bs = b_lds(kt);
-        v2i lo[2], hi[2];
-        mfma(0, 0);
         fa[4] = read_a(As, 4);
-        mfma(0, 1);
+        sb();
+        mfma(0, 0);
         fa[5] = read_a(As, 5);
-        dma(0);
-        mfma(1, 0);
+        sb();
         fa[6] = read_a(As, 6);
-        mfma(1, 1);
+        sb();
+        mfma(0, 1);
         fa[7] = read_a(As, 7);
-        dma(1);
+        sb();
         if constexpr (MODE == kBknDma) {
-          mfma(2, 0);
+          v2i lo[2], hi[2];
           lo[0] = read_b_tr(Bs, 2, 0);
-          mfma(2, 1);
+          sb();
+          mfma(1, 0);
           hi[0] = read_b_tr(Bs, 2, 1);
-          dma(2);
-          mfma(3, 0);
+          sb();
           lo[1] = read_b_tr(Bs, 3, 0);
-          mfma(3, 1);
+          sb();
+          mfma(1, 1);
           hi[1] = read_b_tr(Bs, 3, 1);
+          sb();
           fb[2] = v4i{lo[0].x, lo[0].y, hi[0].x, hi[0].y};
           fb[3] = v4i{lo[1].x, lo[1].y, hi[1].x, hi[1].y};
         } else {
-          mfma(2, 0);
           fb[2] = read_b_rowk(Bs, 2);
-          mfma(2, 1);
-          dma(2);
-          mfma(3, 0);
+          sb();
+          mfma(1, 0);
           fb[3] = read_b_rowk(Bs, 3);
-          mfma(3, 1);
+          sb();
+          mfma(1, 1);
         }
-#pragma unroll
-        for (int q = 3; q < kSplit; ++q) dma(q);
+        dma(0);
+        mfma(2, 0);
+        dma(1);
+        mfma(2, 1);
+        dma(2);
+        mfma(3, 0);
+        mfma(3, 1);
       }
       // ---- barrier for slice kt + 1 ----
       if (kt + 1 < KT) {
@@ -329,27 +337,13 @@ __device__ __forceinline__ void gemm_i8_tile(
         const char* As = a_lds(kt + 1);
         const char* Bs = b_lds(kt + 1);
         v4i na[4], nb[2];
-        v2i lo[2], hi[2];
-        mfma(0, 2);
-        mfma(0, 3);
-        na[0] = read_a(As, 0);
-        mfma(1, 2);
-        dma(kSplit + 0);
-        mfma(1, 3);
-        na[1] = read_a(As, 1);
-        mfma(2, 2);
-        mfma(2, 3);
-        na[2] = read_a(As, 2);
-        mfma(3, 2);
-        dma(kSplit + 1);
-        mfma(3, 3);
-        na[3] = read_a(As, 3);
         mfma(4, 0);
         mfma(5, 0);
-        dma(kSplit + 2);
+        dma(kSplit + 0);
         mfma(6, 0);
         mfma(7, 0);
         if constexpr (MODE == kBknDma) {
+          v2i lo[2], hi[2];
           lo[0] = read_b_tr(Bs, 0, 0);
           mfma(4, 1);
           hi[0] = read_b_tr(Bs, 0, 1);
@@ -357,7 +351,7 @@ __device__ __forceinline__ void gemm_i8_tile(
           mfma(6, 1);
           mfma(7, 1);
           lo[1] = read_b_tr(Bs, 1, 0);
-          mfma(4, 2);
+          mfma(0, 2);
           hi[1] = read_b_tr(Bs, 1, 1);
           nb[0] = v4i{lo[0].x, lo[0].y, hi[0].x, hi[0].y};
           nb[1] = v4i{lo[1].x, lo[1].y, hi[1].x, hi[1].y};
@@ -368,17 +362,29 @@ __device__ __forceinline__ void gemm_i8_tile(
           mfma(6, 1);
           mfma(7, 1);
           nb[1] = read_b_rowk(Bs, 1);
-          mfma(4, 2);
+          mfma(0, 2);
         }
-        mfma(5, 2);
-        mfma(6, 2);
-        mfma(7, 2);
+        mfma(0, 3);
+        na[0] = read_a(As, 0);
+        mfma(1, 2);
+        dma(kSplit + 1);
+        mfma(1, 3);
+        na[1] = read_a(As, 1);
+        mfma(2, 2);
+        mfma(2, 3);
+        na[2] = read_a(As, 2);
+        mfma(3, 2);
+        dma(kSplit + 2);
+        mfma(3, 3);
+        na[3] = read_a(As, 3);
+        mfma(4, 2);
         mfma(4, 3);
+        mfma(5, 2);
         mfma(5, 3);
+        mfma(6, 2);
         mfma(6, 3);
+        mfma(7, 2);
         mfma(7, 3);
-#pragma unroll
-        for (int q = kSplit + 3; q < kFetchOps; ++q) dma(q);
 #pragma unroll
         for (int i = 0; i < 4; ++i) fa[i] = na[i];
         fb[0] = nb[0];
@@ -756,6 +762,7 @@ hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream) {
   const SplitKPlan p = splitk_plan(g.m, g.n, g.k, g.b_layout);
   if (p.splits > 1 && g.workspace && g.workspace_bytes >= p.bytes)
     return launch_splitk(g, p, stream);
+  if (gemm_wide_applies(g.m, g.n, g.k, g.b_layout)) return launch_gemm_wide(g, stream);
   if (g.b_layout == QK_B_NK) return launch_mode<kBnkDma>(g, grid, tiles_m, tiles_n, stream);
   if (g.n % 16 == 0) return launch_mode<kBknDma>(g, grid, tiles_m, tiles_n, stream);
   if (g.n % 4 == 0) return launch_mode<kBknReg4>(g, grid, tiles_m, tiles_n, stream);

@@ -1,0 +1,466 @@
+// INT8 x INT8 -> INT32 GEMM with 256 x 256 workgroup tiles, for outputs with
+// many tiles (the large MLP projections), on CDNA4 matrix cores with the
+// dequant epilogue fused.
+//
+// What it computes is the tiled INT8 kernel's ("16. Deploying Custom
+// Kernels", C++ Kernel Interface; "KV-cache kernels", 02 Scales and
+// dequantization; INT32 accumulation from "Skill: Write an INT8 Quantized
+// Kernel", Inputs):
+//   acc[i][j] = sum_t a[i][t] * B(t, j)        exact INT32
+//   c[i][j]   = acc                            (optional)
+//   out[i][j] = ((float)acc * scale_a[i]) * (scale_b[j] * output_scale)   (optional)
+// Re-tiling for the shape class is what "KV-cache kernels", 04 What changes
+// in the kernel's shape, asks for: a larger tile halves the global-to-LDS
+// bytes per multiply-accumulate of the 256 x 128 tile's k-split design.
+//
+// Design for gfx950:
+//   * Workgroup tile 256 (M) x 256 (N), k slices of 64 bytes, four LDS
+//     stages of 32 KiB (A 256 x 64, B 64 x 256), eight wave64s (two per SIMD),
+//     each owning a 128 x 64 sub-tile (2 x 4 of them) over the whole k range
+//     with v_mfma_i32_16x16x64_i8: per slice and wave 8 x 4 instructions, 8
+//     A and 4 B fragment reads, exactly the per-wave work of the 256 x 128
+//     kernel's half slice, with 32 KiB of global-to-LDS transfer per slice
+//     instead of 48 and no k-group hand-over at the end.
+//   * Transfers go global -> LDS with 128-bit global_load_lds (four per wave
+//     and slice), issued for slice kt + 3 while slice kt is multiplied: the
+//     wait before slice kt + 1's fragments covers loads issued two slices
+//     earlier.  One execution barrier per slice, without a memory fence, and
+//     every fragment read several MFMAs ahead of its first use, so neither
+//     the barrier nor an MFMA waits on LDS latency.
+//   * Measured: the loop's time per slice is the same at 1.8 and 2.4 GHz, so
+//     memory, not the matrix cores, paces it: with four stages, each slice's
+//     lines that miss L2 have about two slices' time to arrive.
+//   * A (and a weight stored [N][K]) is kept k-contiguous, 64-byte rows with
+//     the 16-byte chunk index XORed by (row >> 2) & 3: the 16 consecutive
+//     rows a 128-bit fragment read serves together hit 16 distinct 16-byte
+//     bank groups.  A weight stored [K][N] stays [k][n] (256-byte rows, chunk
+//     XORed by (k & 7) | ((k >> 4) & 1) << 3) and is read with
+//     ds_read_b64_tr_b8, which hands each lane its column's k bytes; the 16
+//     rows two lane groups read together land in 16 distinct bank groups.
+//   * Rows past M or N re-read a valid row (never stored); a k tail (K not a
+//     multiple of 64) has its A chunks at k >= K zeroed in LDS before use.
+//   * XCD-aware tile order as in the 256 x 128 kernel.
+//   * Epilogue: each wave stages its 128 x 64 block in two 64-row halves
+//     row-major in LDS and stores whole 128-byte row segments with the
+//     shared store helpers (scales in binary32, bf16 rounded to nearest even).
+#include "gemm_tile.h"
+
+namespace qk {
+namespace {
+
+namespace wide {
+
+using tile::v2i;
+using tile::v4i;
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int BM = 256;
+constexpr int BN = 256;
+constexpr int BK = 64;
+constexpr int kStages = 4;
+constexpr int A_STAGE = BM * BK;          // 16 KiB
+constexpr int B_STAGE = BN * BK;          // 16 KiB
+constexpr int STAGE = A_STAGE + B_STAGE;  // 32 KiB
+constexpr int WTM = 128;                  // wave sub-tile rows
+constexpr int WTN = 64;                   // wave sub-tile columns
+constexpr int FM = WTM / 16;
+constexpr int FN = WTN / 16;
+static_assert((BM / WTM) * (BN / WTN) == kWaves, "one sub-tile per wave");
+constexpr int kOpsA = BM * BK / 1024 / kWaves;  // 1 KiB transfers per wave and slice
+constexpr int kOpsB = BN * BK / 1024 / kWaves;
+constexpr int kOps = kOpsA + kOpsB;
+static_assert(kOpsA == 2 && kOpsB == 2, "two A and two B transfers per wave and slice");
+
+// k-contiguous rows of 64 bytes (A, [N][K] weight)
+__device__ __forceinline__ int rowk_offset(int row, int chunk) {
+  return row * BK + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+// [k][n] weight rows of 256 bytes
+__device__ __forceinline__ int kn_swz(int k) { return (k & 7) | (((k >> 4) & 1) << 3); }
+__device__ __forceinline__ int kn_offset(int k, int chunk) {
+  return k * BN + ((chunk ^ kn_swz(k)) << 4);
+}
+
+// Source address and LDS slot (wave-uniform, for m0) of this thread's
+// transfer `part` of a slice.
+// A part: 16 rows x 64 bytes (lane l: row l / 4, LDS chunk l % 4).  [K][N]
+// weight part: 4 k rows x 256 bytes (lane l: k row l / 16, LDS chunk l % 16).
+// Global rows, columns and k are clamped into the operands (the values
+// there are never used, or meet zero codes).
+template <int MODE>
+__device__ __forceinline__ void part_source(const int8_t* __restrict__ a,
+                                            const int8_t* __restrict__ b, int M, int N, int K,
+                                            int m0, int n0, int k0, int lda, int ldb, int part,
+                                            const int8_t*& src, uint32_t& lds) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  if (part < kOpsA || MODE == tile::kBnkDma) {
+    const bool is_a = part < kOpsA;
+    const int blk = wave * kOpsA + (is_a ? part : part - kOpsA);
+    const int row = blk * 16 + (lane >> 2);
+    const int gchunk = (lane & 3) ^ ((row >> 2) & 3);
+    const uint32_t gr = static_cast<uint32_t>(min((is_a ? m0 : n0) + row, (is_a ? M : N) - 1));
+    const uint32_t gk = static_cast<uint32_t>(min(k0 + 16 * gchunk, K - 16));
+    src = (is_a ? a : b) + (gr * static_cast<uint32_t>(is_a ? lda : ldb) + gk);
+    lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>((is_a ? 0 : A_STAGE) + blk * 1024));
+  } else {
+    const int blk = wave * kOpsB + (part - kOpsA);
+    const int k = blk * 4 + (lane >> 4);
+    const int gchunk = (lane & 15) ^ kn_swz(k);
+    const uint32_t gk = static_cast<uint32_t>(min(k0 + k, K - 1));
+    const uint32_t gn = static_cast<uint32_t>(min(n0 + 16 * gchunk, N - 16));
+    src = b + (gk * static_cast<uint32_t>(N) + gn);
+    lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(A_STAGE + blk * 1024));
+  }
+}
+
+// One workgroup's 256 x 256 output tile (tm, tn).
+template <int MODE, bool KTAIL>
+__device__ __forceinline__ void gemm_wide_tile(
+    const int8_t* __restrict__ a, const int8_t* __restrict__ b, int32_t* __restrict__ c,
+    const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
+    void* __restrict__ out, int out_dtype, int M, int N, int K, int tm, int tn) {
+  static_assert(MODE == tile::kBnkDma || MODE == tile::kBknDma, "DMA weight layouts");
+  constexpr int kStageRows = 64;                         // rows per epilogue pass
+  constexpr int kStageBytes = kStageRows * WTN * 4;      // 16 KiB per wave
+  constexpr int kSmem = kStages * STAGE > kWaves * kStageBytes + 8 * (BM + BN)
+                            ? kStages * STAGE
+                            : kWaves * kStageBytes + 8 * (BM + BN);
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int wm = wave >> 2;  // 2 sub-tiles along M
+  const int wn = wave & 3;   // 4 along N
+
+  // this thread's per-token or per-channel scale, loaded now so that its
+  // latency hides behind the main loop
+  static_assert(BM + BN == kThreads, "one scale per thread");
+  float scale_reg = 0.0f;
+  if (out) {
+    if (t < BM) {
+      if (m0 + t < M) scale_reg = scale_a[m0 + t];
+    } else if (n0 + t - BM < N) {
+      scale_reg = scale_b[n0 + t - BM];  // times output_scale later
+    }
+  }
+
+  // transfer sources and LDS slots, formed once: slice s adds s times the
+  // part's k stride (BK bytes along a row, or BK weight rows)
+  const uint32_t lds_smem = lds_addr(smem);
+  const int8_t* src[kOps];
+  uint32_t slot[kOps];
+#pragma unroll
+  for (int q = 0; q < kOps; ++q)
+    part_source<MODE>(a, b, M, N, K, m0, n0, 0, K, K, q, src[q], slot[q]);
+  auto kstride = [&](int q) -> size_t {
+    return (q < kOpsA || MODE == tile::kBnkDma) ? static_cast<size_t>(BK)
+                                                : static_cast<size_t>(BK) * N;
+  };
+  auto issue = [&](int s, int q) {
+    if constexpr (KTAIL) {
+      // the clamps change in the final slice: form the address again
+      const int8_t* p;
+      uint32_t l;
+      part_source<MODE>(a, b, M, N, K, m0, n0, s * BK, K, K, q, p, l);
+      lds_dma16(p, lds_smem + static_cast<uint32_t>((s % kStages) * STAGE) + l);
+    } else {
+      lds_dma16(src[q] + static_cast<size_t>(s) * kstride(q),
+                lds_smem + static_cast<uint32_t>((s % kStages) * STAGE) + slot[q]);
+    }
+  };
+  auto a_lds = [&](int s) -> const char* { return smem + (s % kStages) * STAGE; };
+  auto b_lds = [&](int s) -> const char* { return smem + (s % kStages) * STAGE + A_STAGE; };
+
+  // Fragments of v_mfma_i32_16x16x64_i8: lane l holds 16 k-consecutive bytes,
+  // k = 16 (l / 16) .. + 15 of the slice, of row l % 16 (A) or column l % 16
+  // (B) of the fragment.
+  const int kchunk = lane >> 4;
+  const int a_row = wm * WTM + (lane & 15);
+  const int b_row = wn * WTN + (lane & 15);
+  auto read_a = [&](const char* As, int i) -> v4i {
+    return *reinterpret_cast<const v4i*>(As + rowk_offset(a_row + i * 16, kchunk));
+  };
+  auto read_b_tr = [&](const char* Bs, int j, int h) -> v2i {
+    const int i16 = lane & 15;
+    const int kr = 16 * (lane >> 4) + (i16 >> 1) + 8 * h;
+    const int cb = wn * (WTN / 16) + j;
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i*)(Bs + kn_offset(kr, cb) + 8 * (i16 & 1)));
+  };
+  auto read_b_rowk = [&](const char* Bs, int j) -> v4i {
+    return *reinterpret_cast<const v4i*>(Bs + rowk_offset(b_row + j * 16, kchunk));
+  };
+  auto read_b = [&](const char* Bs, int j) -> v4i {
+    if constexpr (MODE == tile::kBknDma) {
+      const v2i lo = read_b_tr(Bs, j, 0);
+      const v2i hi = read_b_tr(Bs, j, 1);
+      return v4i{lo.x, lo.y, hi.x, hi.y};
+    } else {
+      return read_b_rowk(Bs, j);
+    }
+  };
+
+  v4i acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v4i{};
+
+  const int KT = (K + BK - 1) / BK;
+
+  // zero the A chunks of the final slice that lie at k >= K, then publish
+  auto zero_tail = [&](int s) {
+    char* Az = smem + (s % kStages) * STAGE;
+    // 256 rows x 4 chunks = 1024 chunks, two per thread
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = t + kThreads * i;
+      const int row = idx >> 2;
+      const int ch = idx & 3;
+      if (s * BK + 16 * ch >= K)
+        *reinterpret_cast<uint4*>(Az + rowk_offset(row, ch)) = make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+  };
+
+  v4i fa[FM], fb[FN];
+  if (KT > 0) {
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+      if (s < KT)
+#pragma unroll
+        for (int q = 0; q < kOps; ++q) issue(s, q);
+    // slice 0 landed: at most the later prologue slices are outstanding
+    if (KT > 2) wait_vmcnt<2 * kOps>(); else if (KT > 1) wait_vmcnt<kOps>(); else wait_vmcnt<0>();
+    __syncthreads();
+    if (KTAIL && KT == 1) zero_tail(0);
+#pragma unroll
+    for (int i = 0; i < FM / 2; ++i) fa[i] = read_a(a_lds(0), i);
+#pragma unroll
+    for (int j = 0; j < FN / 2; ++j) fb[j] = read_b(b_lds(0), j);
+  }
+
+  // An execution barrier without a memory fence: the waits it needs are
+  // explicit (vmcnt for this wave's transfers), and LDS reads issued before it
+  // stay in flight until the MFMA that uses them waits for them.
+  auto barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // One slice per iteration in two phases, every instruction's place pinned
+  // by sched_barrier, each fragment read several MFMAs before its first use:
+  //   phase 0: MFMAs of A 0..3 x B 0..1 (fragments read in the previous
+  //            iteration), interleaved with the reads of this slice's A 4..7,
+  //            then B 2..3;
+  //   barrier: slice kt + 1 has landed (this wave's transfers by vmcnt, every
+  //            wave's by s_barrier).  Every wave has also consumed slice
+  //            kt - 1 by now, so the transfers of slice kt + 3 into its stage
+  //            follow the barrier;
+  //   phase 1: A 4..7 x B 0 and B 1 (then B 0 and B 1 are free and slice
+  //            kt + 1's B 0..1 are read into them), A 0..3 x B 2..3 (each A
+  //            register is read for slice kt + 1 once its last MFMA issued),
+  //            A 4..7 x B 2..3, with the four transfers of slice kt + 3
+  //            spread between.
+  static_assert(FM == 8 && FN == 4, "interleave pattern below");
+  for (int kt = 0; kt < KT; ++kt) {
+    const bool prefetch = kt + 3 < KT;
+    auto mfma = [&](int i, int j) {
+      acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto dma = [&](int q) {
+      if (prefetch) issue(kt + 3, q);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // ---- phase 0 ----
+    {
+      const char* As = a_lds(kt);
+      const char* Bs = b_lds(kt);
+      mfma(0, 0);
+      fa[4] = read_a(As, 4);
+      mfma(0, 1);
+      fa[5] = read_a(As, 5);
+      mfma(1, 0);
+      fa[6] = read_a(As, 6);
+      mfma(1, 1);
+      fa[7] = read_a(As, 7);
+      if constexpr (MODE == tile::kBknDma) {
+        v2i lo[2], hi[2];
+        mfma(2, 0);
+        lo[0] = read_b_tr(Bs, 2, 0);
+        mfma(2, 1);
+        hi[0] = read_b_tr(Bs, 2, 1);
+        mfma(3, 0);
+        lo[1] = read_b_tr(Bs, 3, 0);
+        mfma(3, 1);
+        hi[1] = read_b_tr(Bs, 3, 1);
+        fb[2] = v4i{lo[0].x, lo[0].y, hi[0].x, hi[0].y};
+        fb[3] = v4i{lo[1].x, lo[1].y, hi[1].x, hi[1].y};
+      } else {
+        mfma(2, 0);
+        fb[2] = read_b_rowk(Bs, 2);
+        mfma(2, 1);
+        mfma(3, 0);
+        fb[3] = read_b_rowk(Bs, 3);
+        mfma(3, 1);
+      }
+    }
+    // ---- barrier for slice kt + 1 ----
+    if (kt + 1 < KT) {
+      // outstanding after slice kt + 1: slice kt + 2's transfers, if issued
+      if (kt + 2 < KT) wait_vmcnt<kOps>(); else wait_vmcnt<0>();
+      barrier();
+      if (KTAIL && kt + 1 == KT - 1) zero_tail(kt + 1);
+    }
+    // ---- phase 1 ----
+    {
+      // after the last slice these reads come from a valid, unused stage and
+      // are not used: no branches around LDS reads
+      const char* As = a_lds(kt + 1);
+      const char* Bs = b_lds(kt + 1);
+      v4i na[4], nb[2];
+      mfma(4, 0);
+      mfma(5, 0);
+      dma(0);
+      mfma(6, 0);
+      mfma(7, 0);
+      if constexpr (MODE == tile::kBknDma) {
+        v2i lo[2], hi[2];
+        lo[0] = read_b_tr(Bs, 0, 0);
+        mfma(4, 1);
+        hi[0] = read_b_tr(Bs, 0, 1);
+        mfma(5, 1);
+        dma(1);
+        mfma(6, 1);
+        mfma(7, 1);
+        lo[1] = read_b_tr(Bs, 1, 0);
+        mfma(0, 2);
+        hi[1] = read_b_tr(Bs, 1, 1);
+        nb[0] = v4i{lo[0].x, lo[0].y, hi[0].x, hi[0].y};
+        nb[1] = v4i{lo[1].x, lo[1].y, hi[1].x, hi[1].y};
+      } else {
+        nb[0] = read_b_rowk(Bs, 0);
+        mfma(4, 1);
+        mfma(5, 1);
+        dma(1);
+        mfma(6, 1);
+        mfma(7, 1);
+        nb[1] = read_b_rowk(Bs, 1);
+        mfma(0, 2);
+      }
+      mfma(0, 3);
+      na[0] = read_a(As, 0);
+      mfma(1, 2);
+      dma(2);
+      mfma(1, 3);
+      na[1] = read_a(As, 1);
+      mfma(2, 2);
+      mfma(2, 3);
+      na[2] = read_a(As, 2);
+      mfma(3, 2);
+      dma(3);
+      mfma(3, 3);
+      na[3] = read_a(As, 3);
+      mfma(4, 2);
+      mfma(4, 3);
+      mfma(5, 2);
+      mfma(5, 3);
+      mfma(6, 2);
+      mfma(6, 3);
+      mfma(7, 2);
+      mfma(7, 3);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i] = na[i];
+      fb[0] = nb[0];
+      fb[1] = nb[1];
+    }
+  }
+
+  // ---- epilogue ----
+  // Each wave stages its 128 x 64 block in two 64-row halves, row-major in
+  // LDS (the stages are free once every wave is past the loop), and stores
+  // whole 128-byte row segments.  Output stores are nontemporal.
+  __syncthreads();
+  float* s_sa = reinterpret_cast<float*>(smem + kWaves * kStageBytes);
+  float* s_sb = s_sa + BM;
+  if (out) s_sa[t] = t < BM ? scale_reg : scale_reg * output_scale;  // s_sb follows s_sa
+  int* stage = reinterpret_cast<int*>(smem + wave * kStageBytes);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (half == 1) __syncthreads();  // the first half's rows are read back by now
+    constexpr int kHalfFrags = kStageRows / 16;
+#pragma unroll
+    for (int ii = 0; ii < kHalfFrags; ++ii)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        tile::stage_fragment(stage, lane, ii, j, acc[half * kHalfFrags + ii][j]);
+    __syncthreads();  // staged blocks and scales visible
+    const int lrow0 = wm * WTM + half * kStageRows;
+    const int lcol0 = wn * WTN;
+    if (c)
+      tile::store4<kStageRows, false, true>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, c);
+    if (out) {
+      if (out_dtype == QK_BF16)
+        tile::store_bf16<kStageRows, false>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb,
+                                            out);
+      else
+        tile::store4<kStageRows, false, false>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa,
+                                               s_sb, out);
+    }
+  }
+}
+
+template <int MODE, bool KTAIL>
+__global__ __launch_bounds__(kThreads, 1) void gemm_i8_wide_kernel(
+    const int8_t* __restrict__ a, const int8_t* __restrict__ b, int32_t* __restrict__ c,
+    const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
+    void* __restrict__ out, int out_dtype, int M, int N, int K, int tiles_m, int tiles_n) {
+  int tm, tn;
+  tile::tile_coords(tiles_m, tiles_n, tm, tn);
+  gemm_wide_tile<MODE, KTAIL>(a, b, c, scale_a, scale_b, output_scale, out, out_dtype, M, N, K,
+                              tm, tn);
+}
+
+template <int MODE>
+hipError_t launch_wide_mode(const GemmArgs& g, dim3 grid, int tiles_m, int tiles_n,
+                            hipStream_t stream) {
+  if (g.k % BK != 0)
+    return launch(gemm_i8_wide_kernel<MODE, true>, grid, dim3(kThreads), 0, stream, g.a, g.b,
+                  g.c, g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k,
+                  tiles_m, tiles_n);
+  return launch(gemm_i8_wide_kernel<MODE, false>, grid, dim3(kThreads), 0, stream, g.a, g.b, g.c,
+                g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k, tiles_m,
+                tiles_n);
+}
+
+}  // namespace wide
+}  // namespace
+
+bool gemm_wide_applies(int m, int n, int k, int b_layout) {
+  if (k <= 0 || n < 16) return false;
+  if (b_layout == QK_B_KN && n % 16 != 0) return false;  // DMA of [k][n] rows in 16-byte chunks
+  const long long tiles = static_cast<long long>((m + wide::BM - 1) / wide::BM) *
+                          ((n + wide::BN - 1) / wide::BN);
+  return tiles >= 256;  // at least one 256 x 256 tile per CU
+}
+
+hipError_t launch_gemm_wide(const GemmArgs& g, hipStream_t stream) {
+  const int tiles_m = (g.m + wide::BM - 1) / wide::BM;
+  const int tiles_n = (g.n + wide::BN - 1) / wide::BN;
+  const long long tiles = static_cast<long long>(tiles_m) * tiles_n;
+  if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(tiles));
+  if (g.b_layout == QK_B_NK) return wide::launch_wide_mode<tile::kBnkDma>(g, grid, tiles_m, tiles_n, stream);
+  return wide::launch_wide_mode<tile::kBknDma>(g, grid, tiles_m, tiles_n, stream);
+}
+
+}  // namespace qk

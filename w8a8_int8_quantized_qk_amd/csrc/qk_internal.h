@@ -85,6 +85,10 @@ hipError_t launch_weight_colsum(int k, int n, const int8_t* b, int b_layout, int
 // are addressed with 32-bit offsets: m*k and n*k must stay below 2^32.
 bool gemm_mfma_supported(int m, int n, int k);
 hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
+// The same product with 256 x 256 tiles (gemm_wide.hip), for outputs with at
+// least one such tile per CU; launch_gemm_mfma picks it when it applies.
+bool gemm_wide_applies(int m, int n, int k, int b_layout);
+hipError_t launch_gemm_wide(const GemmArgs& g, hipStream_t stream);
 // The same kernel over experts (gemm_mfma.hip): rows [offsets[e],
 // offsets[e + 1]) of a (device array of experts + 1 ints) use weight
 // b + e * k * n and per-channel scales scale_b + e * n; one launch.
