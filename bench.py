@@ -37,8 +37,12 @@ INT8_PEAK_TOPS = 5000.0     # MI355X dense INT8 MFMA, published
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA, published
 CSRC = os.path.join(ROOT, "w8a8_int8_quantized_qk_amd", "csrc")
-GEMM_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_mfma_prefill_outliers_traffic.txt"),
-                [os.path.join(CSRC, f) for f in ("gemm_mfma.hip", "gemm_tile.h", "lds_dma.h")])
+# the 2048 x 4096 x 4096 GEMM (128 tiles of 256 x 256, fewer than the CUs; k a
+# multiple of 128) runs the 256 x 128 kernel with separate transfer and
+# matrix-core waves
+GEMM_KERNEL = "gemm_i8_spec_kernel"
+GEMM_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_spec_prefill_outliers_traffic.txt"),
+                [os.path.join(CSRC, f) for f in ("gemm_spec.hip", "gemm_tile.h", "lds_dma.h")])
 GEMV_TRAFFIC = (os.path.join(ROOT, "profiles", "gemv_decode_m1_traffic.txt"),
                 [os.path.join(CSRC, f) for f in ("gemv.hip", "quant_math.h", "lds_dma.h")])
 FP8_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_fp8_prefill_outliers_traffic.txt"),
@@ -293,13 +297,13 @@ def main():
                    "w_layout": "[K,N]", "out_dtype": "bf16", "outlier_cols": wcfg.outlier_cols,
                    "ring_sets": args.ring,
                    "step": "qk_quant_per_token + qk_gemm_i8_scaled, replayed from HIP graphs"},
-        "roofline": {"bound": "mfma", "kernel": "gemm_i8_mfma_kernel",
+        "roofline": {"bound": "mfma", "kernel": GEMM_KERNEL,
                      "achieved": round(gemm_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                      "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
                      "traffic": traffic,
                      "traffic_source": ("rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of this kernel "
                                         "code, copy-kernel scaled, from "
-                                        "profiles/gemm_mfma_prefill_outliers_traffic.txt"
+                                        "profiles/" + os.path.basename(GEMM_TRAFFIC[0])
                                         if traffic is not None else
                                         "none: no counter summary taken on this kernel code"),
                      "avg_launch_us": round(gemm_ms * 1e3, 3),

@@ -218,6 +218,22 @@ def test_gemm_wide_tiles(m, n, k, layout):
     _run_gemm_case(m, n, k, layout, "mfma", "bf16" if k % 128 else "f32", output_scale=0.5)
 
 
+# outputs with fewer 256 x 256 tiles than CUs and k a multiple of 128 take
+# the 256 x 128 kernel with separate transfer and matrix-core waves: one
+# tile, one and two slices (fewer than its three LDS stages), as many slices
+# as stages, ragged rows and columns, 16 columns, a few rows
+SPEC_SHAPES = [(256, 128, 128), (300, 272, 256), (2048, 4096, 384), (1000, 1040, 1152),
+               (513, 4096, 640), (7, 16, 256), (40, 2064, 2048)]
+
+
+@pytest.mark.parametrize("m,n,k", SPEC_SHAPES)
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_spec_tiles(m, n, k, layout, out_dtype):
+    assert ((m + 255) // 256) * ((n + 255) // 256) < 256 and k % 128 == 0
+    _run_gemm_case(m, n, k, layout, "mfma", out_dtype, output_scale=0.75)
+
+
 @pytest.mark.parametrize("m,n,k", [s for s in GEMM_SHAPES if s[0] <= 16])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_gemm_decode_kernel(m, n, k, out_dtype):

@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqk.so")
 SOURCES = ["qk_api.hip", "quant.hip", "quant_static.hip", "gemm_mfma.hip", "gemm_wide.hip",
-           "gemm_slice.hip", "gemv.hip"]
+           "gemm_spec.hip", "gemm_slice.hip", "gemv.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -763,6 +763,7 @@ hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream) {
   if (p.splits > 1 && g.workspace && g.workspace_bytes >= p.bytes)
     return launch_splitk(g, p, stream);
   if (gemm_wide_applies(g.m, g.n, g.k, g.b_layout)) return launch_gemm_wide(g, stream);
+  if (gemm_spec_applies(g.m, g.n, g.k, g.b_layout)) return launch_gemm_spec(g, stream);
   if (g.b_layout == QK_B_NK) return launch_mode<kBnkDma>(g, grid, tiles_m, tiles_n, stream);
   if (g.n % 16 == 0) return launch_mode<kBknDma>(g, grid, tiles_m, tiles_n, stream);
   if (g.n % 4 == 0) return launch_mode<kBknReg4>(g, grid, tiles_m, tiles_n, stream);

@@ -1,0 +1,297 @@
+// INT8 x INT8 -> INT32 GEMM on 256 x 128 tiles with transfer waves and
+// matrix-core waves kept apart, dequant epilogue fused.
+//
+// What it computes is the tiled INT8 kernel's ("16. Deploying Custom
+// Kernels", C++ Kernel Interface; "KV-cache kernels", 02 Scales and
+// dequantization; INT32 accumulation from "Skill: Write an INT8 Quantized
+// Kernel", Inputs):
+//   acc[i][j] = sum_t a[i][t] * B(t, j)        exact INT32
+//   c[i][j]   = acc                            (optional)
+//   out[i][j] = ((float)acc * scale_a[i]) * (scale_b[j] * output_scale)   (optional)
+//
+// Design for gfx950 (measured on the 256 x 128 k-group kernel: with the same
+// LDS reads and MFMAs, leaving out the in-loop global-to-LDS instructions
+// made its loop 31% faster, leaving out only the waits for them 6%; a wave
+// held up issuing a transfer cannot issue its MFMAs either):
+//   * Workgroup tile 256 (M) x 128 (N), k slices of 128 bytes, three LDS
+//     stages of 48 KiB (the 256 x 128 kernel's layouts, swizzles and
+//     fragment reads, gemm_tile.h).
+//   * Twelve waves, three per SIMD: waves 0..7 multiply (two per SIMD: one
+//     wave issues a 16x16x64 MFMA only every ~25 cycles, measured, so a
+//     single wave cannot keep a matrix core busy), waves 8..11 only move
+//     data.  Transfer wave d issues 12 of a slice's 48 1-KiB
+//     global_load_lds_dwordx4 (A rows 64 d .. 64 d + 63 and a quarter of the
+//     weight block), waits for them and meets the others at the slice
+//     barrier.  Matrix-core wave w owns a 64 x 64 sub-tile over the whole k
+//     range (three waves per SIMD leave ~168 registers each): per slice two
+//     64-deep steps of 4 x 4 v_mfma_i32_16x16x64_i8, reading the next step's
+//     8 fragments while it multiplies the current one.  No partial sums
+//     cross waves, so there is no k-group hand-over.
+//   * One barrier per slice, between its two steps: before it the transfer
+//     waves have seen slice kt + 1 land; after it they issue slice kt + 2
+//     into the stage of slice kt - 1, whose last fragments the matrix-core
+//     waves read before that barrier (a fenced barrier: their LDS reads are
+//     complete when they arrive).
+//   * Rows past M or N re-read a valid row (never stored).  K must be a
+//     multiple of 128 (the 256 x 128 k-group kernel takes the others).
+//   * Epilogue: each matrix-core wave stages its 64 x 64 block row-major in
+//     LDS and stores it as whole 128-byte row segments, scales in binary32.
+#include "gemm_tile.h"
+
+namespace qk {
+namespace {
+
+namespace spec {
+
+using namespace tile;
+
+constexpr int kMma = 8;                       // matrix-core waves 0..7, two per SIMD
+constexpr int kXfer = 4;                      // transfer waves 8..11, one per SIMD
+constexpr int kSpecThreads = 64 * (kMma + kXfer);
+constexpr int WTM = 64;                       // matrix-core wave sub-tile rows
+constexpr int WTN = 64;                       // ... columns
+constexpr int FM = WTM / 16;
+constexpr int FN = WTN / 16;
+static_assert((BM / WTM) * (BN / WTN) == kMma, "one sub-tile per matrix-core wave");
+constexpr int kPartsA = BM * BK / 1024;        // 32 transfers of A per slice
+constexpr int kPartsB = BN * BK / 1024;        // 16 of the weight
+constexpr int kOps = (kPartsA + kPartsB) / kXfer;  // 12 per transfer wave
+static_assert(kOps * kXfer == kPartsA + kPartsB, "transfers divide over the waves");
+constexpr int kOpsA = kPartsA / kXfer;  // 8 A parts, then 4 weight parts
+
+template <int MODE>
+__device__ __forceinline__ void gemm_spec_tile(
+    const int8_t* __restrict__ a, const int8_t* __restrict__ b, int32_t* __restrict__ c,
+    const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
+    void* __restrict__ out, int out_dtype, int M, int N, int K, int tm, int tn) {
+  static_assert(MODE == kBnkDma || MODE == kBknDma, "DMA weight layouts");
+  constexpr int kStageBytes = WTM * WTN * 4;  // one matrix-core wave's staged block (16 KiB)
+  static_assert(kMma * kStageBytes + 8 * (BM + BN) <= kStages * STAGE, "epilogue fits in LDS");
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * STAGE];
+
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  // wave-uniform for the compiler too, so the two kinds branch, not mask
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+
+  float scale_reg = 0.0f;
+  if (out) {
+    if (t < BM) {
+      if (m0 + t < M) scale_reg = scale_a[m0 + t];
+    } else if (t < BM + BN && n0 + t - BM < N) {
+      scale_reg = scale_b[n0 + t - BM];  // times output_scale later
+    }
+  }
+
+  const int KT = K / BK;  // K % BK == 0
+  auto a_lds = [&](int s) -> const char* { return smem + (s % kStages) * STAGE; };
+  auto b_lds = [&](int s) -> const char* { return smem + (s % kStages) * STAGE + A_STAGE; };
+
+  v4i acc[FM][FN];
+  const int wm = wave >> 1;  // matrix-core wave's 64 x 64 sub-tile
+  const int wn = wave & 1;
+
+  if (wave >= kMma) {
+    // ---------------- transfer wave ----------------
+    const int d = wave - kMma;
+    const uint32_t lds_smem = lds_addr(smem);
+    const int8_t* src[kOps];
+    uint32_t slot[kOps];
+    size_t stride[kOps];
+#pragma unroll
+    for (int q = 0; q < kOps; ++q) {
+      if (q < kOpsA) {  // A block kOpsA d + q: 8 rows of 128 bytes
+        const int blk = kOpsA * d + q;
+        const int row = blk * 8 + (lane >> 3);
+        const int lchunk = (lane & 7) ^ rowk_swz(row);
+        src[q] = a + (static_cast<uint32_t>(min(m0 + row, M - 1)) * static_cast<uint32_t>(K) +
+                      16 * lchunk);
+        slot[q] = static_cast<uint32_t>(blk * 1024);
+        stride[q] = BK;
+      } else if constexpr (MODE == kBnkDma) {  // [N][K] weight block: 8 rows of 128 bytes
+        const int blk = (kOps - kOpsA) * d + (q - kOpsA);
+        const int row = blk * 8 + (lane >> 3);
+        const int lchunk = (lane & 7) ^ rowk_swz(row);
+        src[q] = b + (static_cast<uint32_t>(min(n0 + row, N - 1)) * static_cast<uint32_t>(K) +
+                      16 * lchunk);
+        slot[q] = static_cast<uint32_t>(A_STAGE + blk * 1024);
+        stride[q] = BK;
+      } else {  // [K][N] weight block: 8 k rows of 128 bytes
+        const int blk = (kOps - kOpsA) * d + (q - kOpsA);
+        const int k = blk * 8 + (lane >> 3);
+        const int lchunk = (lane & 7) ^ kn_swz(k);
+        src[q] = b + (static_cast<uint32_t>(k) * static_cast<uint32_t>(N) +
+                      static_cast<uint32_t>(min(n0 + 16 * lchunk, N - 16)));
+        slot[q] = static_cast<uint32_t>(A_STAGE + blk * 1024);
+        stride[q] = static_cast<size_t>(BK) * N;
+      }
+    }
+    auto issue = [&](int s) {
+#pragma unroll
+      for (int q = 0; q < kOps; ++q)
+        lds_dma16(src[q] + static_cast<size_t>(s) * stride[q],
+                  __builtin_amdgcn_readfirstlane(
+                      lds_smem + static_cast<uint32_t>((s % kStages) * STAGE) + slot[q]));
+    };
+    issue(0);
+    if (KT > 1) {
+      issue(1);
+      wait_vmcnt<kOps>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();  // slice 0 in LDS
+    for (int kt = 0; kt < KT; ++kt) {
+      // the stage of slice kt - 1 is free: every matrix-core wave read its
+      // last fragments before the previous barrier
+      const bool more = kt + 2 < KT;
+      if (more) issue(kt + 2);
+      if (kt + 1 < KT) {
+        if (more) wait_vmcnt<kOps>(); else wait_vmcnt<0>();  // slice kt + 1 landed
+        __syncthreads();
+      }
+    }
+  } else {
+    // ---------------- matrix-core wave ----------------
+    const int a_row = wm * WTM + (lane & 15);
+    const int b_row = wn * WTN + (lane & 15);
+    // fragments of 64-deep step g of a slice: lane l holds k = 64 g + 16 (l / 16)
+    // .. + 15 of row (A) or column (B) l % 16 of the fragment
+    auto read_a = [&](const char* As, int i, int g) -> v4i {
+      return *reinterpret_cast<const v4i*>(As + rowk_offset(a_row + i * 16, 4 * g + (lane >> 4)));
+    };
+    auto read_b_tr = [&](const char* Bs, int j, int h, int g) -> v2i {
+      const int i16 = lane & 15;
+      const int kr = 64 * g + 16 * (lane >> 4) + (i16 >> 1) + 8 * h;
+      const int cb = (wn * WTN + j * 16) >> 4;
+      return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) v2i*)(Bs + kn_offset(kr, cb) + 8 * (i16 & 1)));
+    };
+    auto read_b_rowk = [&](const char* Bs, int j, int g) -> v4i {
+      return *reinterpret_cast<const v4i*>(Bs + rowk_offset(b_row + j * 16, 4 * g + (lane >> 4)));
+    };
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = v4i{};
+
+    v4i f0a[FM], f0b[FN], f1a[FM], f1b[FN];
+    auto mfma_step = [&](v4i (&xa)[FM], v4i (&xb)[FN], v4i (&ya)[FM], v4i (&yb)[FN],
+                         const char* As, const char* Bs, int g) {
+      // 16 MFMAs of (xa, xb); after each of the first 12 one read of (ya,
+      // yb): the A fragments, then the weight's
+      v2i lo[FN], hi[FN];
+#pragma unroll
+      for (int n = 0; n < FM * FN; ++n) {
+        const int i = n / FN;
+        const int j = n % FN;
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa[i], xb[j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (n < FM) {
+          ya[n] = read_a(As, n, g);
+        } else if (n < FM + 2 * FN) {
+          const int r = n - FM;
+          if constexpr (MODE == kBknDma) {
+            if (r & 1) hi[r >> 1] = read_b_tr(Bs, r >> 1, 1, g);
+            else lo[r >> 1] = read_b_tr(Bs, r >> 1, 0, g);
+          } else if ((r & 1) == 0) {
+            yb[r >> 1] = read_b_rowk(Bs, r >> 1, g);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (MODE == kBknDma) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) yb[j] = v4i{lo[j].x, lo[j].y, hi[j].x, hi[j].y};
+      }
+    };
+
+    __syncthreads();  // slice 0 in LDS
+    if (KT > 0) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) f0a[i] = read_a(a_lds(0), i, 0);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (MODE == kBknDma) {
+          const v2i lo = read_b_tr(b_lds(0), j, 0, 0);
+          const v2i hi = read_b_tr(b_lds(0), j, 1, 0);
+          f0b[j] = v4i{lo.x, lo.y, hi.x, hi.y};
+        } else {
+          f0b[j] = read_b_rowk(b_lds(0), j, 0);
+        }
+      }
+    }
+    for (int kt = 0; kt < KT; ++kt) {
+      // step 0 of slice kt, reading its step 1
+      mfma_step(f0a, f0b, f1a, f1b, a_lds(kt), b_lds(kt), 1);
+      // slice kt + 1 landed; this wave's reads of slice kt are complete
+      if (kt + 1 < KT) __syncthreads();
+      // step 1 of slice kt, reading step 0 of slice kt + 1 (after the last
+      // slice: a valid, unused stage; not used)
+      mfma_step(f1a, f1b, f0a, f0b, a_lds(kt + 1), b_lds(kt + 1), 0);
+    }
+  }
+
+  // ---- epilogue ----
+  __syncthreads();  // every wave is done with the stages
+  float* s_sa = reinterpret_cast<float*>(smem + kMma * kStageBytes);
+  float* s_sb = s_sa + BM;
+  if (out && t < BM + BN) s_sa[t] = t < BM ? scale_reg : scale_reg * output_scale;
+  int* stage = reinterpret_cast<int*>(smem + (wave & 7) * kStageBytes);
+  if (wave < kMma) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) stage_fragment(stage, lane, i, j, acc[i][j]);
+  }
+  __syncthreads();  // staged blocks and scales visible
+  if (wave < kMma) {
+    const int lrow0 = wm * WTM;
+    const int lcol0 = wn * WTN;
+    if (c) store4<64, false, true>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, c);
+    if (out) {
+      if (out_dtype == QK_BF16)
+        store_bf16<64, false>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, out);
+      else
+        store4<64, false, false>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, out);
+    }
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kSpecThreads, 1) void gemm_i8_spec_kernel(
+    const int8_t* __restrict__ a, const int8_t* __restrict__ b, int32_t* __restrict__ c,
+    const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
+    void* __restrict__ out, int out_dtype, int M, int N, int K, int tiles_m, int tiles_n) {
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  gemm_spec_tile<MODE>(a, b, c, scale_a, scale_b, output_scale, out, out_dtype, M, N, K, tm, tn);
+}
+
+}  // namespace spec
+}  // namespace
+
+bool gemm_spec_applies(int m, int n, int k, int b_layout) {
+  if (k <= 0 || k % tile::BK != 0 || n < 16) return false;
+  if (b_layout == QK_B_KN && n % 16 != 0) return false;  // DMA of [k][n] rows in 16-byte chunks
+  return true;
+}
+
+hipError_t launch_gemm_spec(const GemmArgs& g, hipStream_t stream) {
+  const int tiles_m = (g.m + tile::BM - 1) / tile::BM;
+  const int tiles_n = (g.n + tile::BN - 1) / tile::BN;
+  const long long tiles = static_cast<long long>(tiles_m) * tiles_n;
+  if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(tiles));
+  if (g.b_layout == QK_B_NK)
+    return launch(spec::gemm_i8_spec_kernel<tile::kBnkDma>, grid, dim3(spec::kSpecThreads), 0, stream,
+                  g.a, g.b, g.c, g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m,
+                  g.n, g.k, tiles_m, tiles_n);
+  return launch(spec::gemm_i8_spec_kernel<tile::kBknDma>, grid, dim3(spec::kSpecThreads), 0, stream,
+                g.a, g.b, g.c, g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n,
+                g.k, tiles_m, tiles_n);
+}
+
+}  // namespace qk

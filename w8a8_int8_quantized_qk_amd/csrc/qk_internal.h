@@ -89,6 +89,11 @@ hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
 // least one such tile per CU; launch_gemm_mfma picks it when it applies.
 bool gemm_wide_applies(int m, int n, int k, int b_layout);
 hipError_t launch_gemm_wide(const GemmArgs& g, hipStream_t stream);
+// 256 x 128 tiles with separate transfer and matrix-core waves
+// (gemm_spec.hip), for the outputs the wide kernel does not take; k a
+// multiple of 128, a DMA'd weight layout.
+bool gemm_spec_applies(int m, int n, int k, int b_layout);
+hipError_t launch_gemm_spec(const GemmArgs& g, hipStream_t stream);
 // The same kernel over experts (gemm_mfma.hip): rows [offsets[e],
 // offsets[e + 1]) of a (device array of experts + 1 ints) use weight
 // b + e * k * n and per-channel scales scale_b + e * n; one launch.
