@@ -49,8 +49,10 @@ FP8_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_fp8_prefill_outliers_traffic
                [os.path.join(CSRC, f) for f in ("gemm_slice.hip", "gemm_tile.h", "lds_dma.h")])
 GROUPED_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_grouped128_prefill_outliers_traffic.txt"),
                    [os.path.join(CSRC, f) for f in ("gemm_slice.hip", "gemm_tile.h", "lds_dma.h")])
-MOE_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_moe_up_traffic.txt"),
-               [os.path.join(CSRC, f) for f in ("gemm_mfma.hip", "gemm_tile.h", "lds_dma.h")])
+# the MoE up-projection (4096 routed rows x 14336) takes the 256 x 256 tiles
+MOE_KERNEL = "gemm_i8_wide_moe_kernel"
+MOE_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_wide_moe_up_traffic.txt"),
+               [os.path.join(CSRC, f) for f in ("gemm_wide.hip", "gemm_tile.h", "lds_dma.h")])
 ASYM_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_asym_prefill_outliers_traffic.txt"),
                 [os.path.join(CSRC, f) for f in ("gemm_mfma.hip", "gemm_tile.h", "lds_dma.h")])
 STATIC_TRAFFIC = (os.path.join(ROOT, "profiles", "quant_static_prefill_outliers_traffic.txt"),
@@ -546,7 +548,7 @@ def main():
             "ms_per_step": round(mstep_ms, 5),
             "step": "qk_quant_per_token + qk_moe_gemm_i8_scaled (one launch for all experts)",
             "one_launch_per_expert_us": round(mper_ms * 1e3, 2) if mper_ms is not None else None,
-            "roofline": {"bound": "mfma", "kernel": "gemm_i8_moe_kernel",
+            "roofline": {"bound": "mfma", "kernel": MOE_KERNEL,
                          "achieved": round(mt, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                          "frac": round(mt / INT8_PEAK_TOPS, 4), "traffic": _traffic_from_profile(MOE_TRAFFIC),
                          "avg_launch_us": round(mgemm_ms * 1e3, 3),

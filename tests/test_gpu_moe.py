@@ -57,6 +57,22 @@ def test_moe_against_per_expert_oracle(counts, k, n, layout, out_dtype):
     _run(counts, k, n, layout, seed=len(counts) * 1000 + k + n, out_dtype=out_dtype, osc=0.5)
 
 
+# groups whose dense GEMM of all rows has at least one 256 x 256 tile per CU
+# take the 256 x 256 tile kernel: empty and one-row experts, ragged rows and
+# columns, k tails past a 64-byte slice (k % 64 != 0), both layouts, all rows
+# in one expert
+@pytest.mark.parametrize("counts,k,n,layout", [
+    ([0, 1500, 1, 257, 2338], 256, 4096, "kn"),
+    ([700, 0, 1300, 2100], 208, 4112, "nk"),
+    ([4096], 128, 4096, "kn"),
+    ([1000, 999, 1001, 1096], 320, 4096, "nk"),
+])
+def test_moe_wide_tiles_against_per_expert_oracle(counts, k, n, layout):
+    m = sum(counts)
+    assert (m // 256) * ((n + 255) // 256) >= 256  # the shape selects the 256 x 256 tiles
+    _run(counts, k, n, layout, seed=len(counts) * 1000 + k + n + 7, out_dtype="bf16", osc=0.75)
+
+
 def test_moe_maximum_expert_count():
     rng = np.random.default_rng(7)
     counts = rng.integers(0, 5, qk.MOE_MAX_EXPERTS)
@@ -70,21 +86,24 @@ def test_moe_many_tiles_per_expert():
     _run(np.diff(off).tolist(), 1024, 1024, "kn", seed=10)
 
 
-def test_moe_full_workload_sampled_rows():
+def test_moe_full_workload_every_entry():
+    # the MoE up-projection workload at its full size, in the launch
+    # configuration bench.py times: codes and scales, then every INT32
+    # accumulator and every output element, expert by expert
     d = wl.generate_moe()
     x, w, s_ch, off = d["x"], d["w"], d["s_ch"], d["offsets"]
     q, s = qk.quant_per_token(x.to(DEV))
-    out = qk.moe_gemm_i8_scaled(q, torch.from_numpy(w).to(DEV), torch.from_numpy(off).to(DEV), s,
-                                torch.from_numpy(s_ch).to(DEV))
+    out, c = qk.moe_gemm_i8_scaled(q, torch.from_numpy(w).to(DEV), torch.from_numpy(off).to(DEV),
+                                   s, torch.from_numpy(s_ch).to(DEV), return_acc=True)
     q_ref, s_ref = oracle.quantize_input(wl.bits(x), oracle.BF16)
     assert_equal_exact(host(q), q_ref, "moe workload codes")
-    # the first and last row of every non-empty expert
-    rows, experts = [], []
+    assert_equal_exact(host(s), s_ref, "moe workload scales")
+    c_host, out_host = host(c), host(out)
     for e in range(d["experts"]):
-        if off[e + 1] > off[e]:
-            rows += [int(off[e]), int(off[e + 1]) - 1]
-            experts += [e, e]
-    rows, experts = np.array(rows), np.array(experts)
-    c_ref = np.stack([oracle.gemm_i32(q_ref[r:r + 1], w[e])[0] for r, e in zip(rows, experts)])
-    ref = c_ref.astype(np.float64) * s_ref[rows].astype(np.float64)[:, None] * s_ch[experts].astype(np.float64)
-    assert_out_close(host(out)[rows], ref, "bf16", "moe workload out")
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        c_ref = oracle.gemm_i32(q_ref[r0:r1], w[e])
+        assert_equal_exact(c_host[r0:r1], c_ref, f"moe workload acc expert {e}")
+        assert_out_close(out_host[r0:r1], oracle.dequant(c_ref, s_ref[r0:r1], s_ch[e]), "bf16",
+                         f"moe workload out expert {e}")

@@ -615,7 +615,7 @@ def test_workspace_init_prepares_dirty_memory():
     assert not ws.any()
 
 
-@pytest.mark.parametrize("case", ["prefill_outliers", "split_k", "moe"])
+@pytest.mark.parametrize("case", ["prefill_outliers", "split_k", "moe", "moe_wide"])
 def test_tiled_kernels_repeat_bit_identical(case):
     # the tiled GEMM (k-group hand-over through LDS), the split-K pair of
     # launches and the MoE launch, three runs each on the same inputs: every
@@ -635,7 +635,8 @@ def test_tiled_kernels_repeat_bit_identical(case):
         s_ch = torch.from_numpy(wl.random_channel_scales(rng, n)).to(DEV)
         run = lambda: qk.gemm_i8_scaled(q, w, s, s_ch, return_acc=True, kernel="mfma")
     else:
-        experts, m, n, k = 8, 4096, 2048, 1024
+        # 4096 x 2048 takes the 256 x 128 tiles, 4096 x 4096 the 256 x 256 ones
+        experts, m, n, k = 8, 4096, 2048 if case == "moe" else 4096, 1024
         counts = rng.multinomial(m, rng.dirichlet(np.full(experts, 2.0)))
         offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(DEV)
         q = torch.from_numpy(rng.integers(-127, 128, size=(m, k), dtype=np.int8)).to(DEV)

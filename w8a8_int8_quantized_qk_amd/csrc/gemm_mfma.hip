@@ -482,14 +482,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_mfma_kernel(
 // MoE grouped GEMM ("dynquant-kernels", What is in here: one launch for all
 // experts): rows [offsets[e], offsets[e + 1]) of a belong to expert e, whose
 // weight is b + e * expert_stride and per-channel scales scale_b + e * N.
-// The grid is an upper bound on the tiles (the offsets live on the device);
-// every workgroup reads the offsets, counts each expert's tiles
-// (ceil(rows / BM) * tiles_n) with a block-wide prefix sum, and takes the
-// tile its index falls on, or leaves when the index is past the last one.
-// The XCD renumbering runs over the real tile count, so the surplus
-// workgroups, all at the end of the grid, do not unbalance the XCDs.
-// Offsets are clamped to [0, M]: invalid ones give unspecified results but
-// no access out of bounds.
+// Each workgroup finds its expert and tile with moe_pick (gemm_tile.h).
 constexpr int kMoeMaxExperts = QK_MOE_MAX_EXPERTS;
 template <int MODE, bool KTAIL>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_moe_kernel(
@@ -497,48 +490,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_moe_kernel(
     const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
     void* __restrict__ out, int out_dtype, int M, int N, int K, int tiles_n,
     const int* __restrict__ offsets, int experts, long long expert_stride) {
-  static_assert(kMoeMaxExperts <= kThreads && kMoeMaxExperts % 64 == 0, "one thread per expert");
-  __shared__ int s_wave_sum[kMoeMaxExperts / 64];
-  __shared__ int s_pick[2];  // the workgroup's expert and that expert's first tile
-  const int t = threadIdx.x;
-  int tiles = 0, row0 = 0, row1 = 0;
-  if (t < experts) {
-    row0 = min(max(offsets[t], 0), M);
-    row1 = min(max(offsets[t + 1], 0), M);
-    tiles = row1 > row0 ? ((row1 - row0 + BM - 1) / BM) * tiles_n : 0;
-  }
-  // inclusive prefix sum of the tile counts: within each wave, then across
-  // the (at most four) waves
-  int incl = tiles;
-  if (t < kMoeMaxExperts) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl, d);
-      if ((t & 63) >= d) incl += v;
-    }
-    if ((t & 63) == 63) s_wave_sum[t >> 6] = incl;
-  }
-  if (t == 0) s_pick[0] = -1;
-  __syncthreads();
-  int before = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < kMoeMaxExperts / 64; ++w) {
-    if (w < (t >> 6)) before += s_wave_sum[w];
-    total += s_wave_sum[w];
-  }
-  const int v = xcd_order(blockIdx.x, total);  // meaningful for blockIdx.x < total
-  const int excl = before + incl - tiles;
-  if (t < experts && tiles > 0 && v >= excl && v < excl + tiles) {
-    s_pick[0] = t;
-    s_pick[1] = excl;
-  }
-  __syncthreads();
-  const int e = s_pick[0];
-  if (static_cast<int>(blockIdx.x) >= total || e < 0) return;  // whole workgroup: past the last tile
-  const int r0 = min(max(offsets[e], 0), M);
-  const int Me = min(max(offsets[e + 1], 0), M) - r0;
+  int e, local, r0, Me;
+  if (!moe_pick<BM, kMoeMaxExperts>(offsets, experts, M, tiles_n, e, local, r0, Me)) return;
   int tm, tn;
-  group_order(v - s_pick[1], (Me + BM - 1) / BM, tiles_n, tm, tn);
+  group_order(local, (Me + BM - 1) / BM, tiles_n, tm, tn);
   const size_t row_off = static_cast<size_t>(r0);
   void* out_e = out ? static_cast<char*>(out) + row_off * N * (out_dtype == QK_BF16 ? 2 : 4) : nullptr;
   gemm_i8_tile<MODE, KTAIL>(a + row_off * K, b + e * expert_stride, c ? c + row_off * N : nullptr,
@@ -618,6 +573,7 @@ hipError_t launch_gemm_asym(const GemmArgs& g, const int32_t* zp_a, const int32_
 }
 
 hipError_t launch_gemm_moe(const GemmArgs& g, const int* offsets, int experts, hipStream_t stream) {
+  if (gemm_wide_moe_applies(g.m, g.n, g.k, g.b_layout)) return launch_gemm_wide_moe(g, offsets, experts, stream);
   // at most floor(m / BM) + experts tile rows over all experts
   const int tiles_n = (g.n + BN - 1) / BN;
   const long long tiles = (static_cast<long long>(g.m) / BM + experts) * tiles_n;

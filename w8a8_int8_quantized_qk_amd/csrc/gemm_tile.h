@@ -268,6 +268,65 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   group_order(xcd_order(blockIdx.x, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
+// ---- grouped (MoE) launches ----
+// Rows [offsets[e], offsets[e + 1]) of the activations belong to expert e
+// (offsets clamped to [0, M]: invalid ones give unspecified results but no
+// access out of bounds).  Expert e has ceil(rows / TILE_M) x tiles_n tiles,
+// numbered expert by expert; the grid is an upper bound on their total (the
+// offsets live on the device).  Every workgroup (kThreads threads, one per
+// expert and at most MAX_EXPERTS experts) counts each expert's tiles with a
+// block-wide prefix sum and takes the tile its index falls on: expert e,
+// index `local` within e's tiles, e's first row r0 and row count Me.  The
+// XCD renumbering runs over the real total, so the surplus workgroups, all
+// at the end of the grid, do not unbalance the XCDs.  Returns false (for the
+// whole workgroup) past the last tile.
+template <int TILE_M, int MAX_EXPERTS>
+__device__ __forceinline__ bool moe_pick(const int* __restrict__ offsets, int experts, int M,
+                                         int tiles_n, int& e, int& local, int& r0, int& Me) {
+  static_assert(MAX_EXPERTS <= kThreads && MAX_EXPERTS % 64 == 0, "one thread per expert");
+  __shared__ int s_wave_sum[MAX_EXPERTS / 64];
+  __shared__ int s_pick[2];  // the workgroup's expert and that expert's first tile
+  const int t = threadIdx.x;
+  int tiles = 0;
+  if (t < experts) {
+    const int row0 = min(max(offsets[t], 0), M);
+    const int row1 = min(max(offsets[t + 1], 0), M);
+    tiles = row1 > row0 ? ((row1 - row0 + TILE_M - 1) / TILE_M) * tiles_n : 0;
+  }
+  // inclusive prefix sum of the tile counts: within each wave, then across
+  // the waves
+  int incl = tiles;
+  if (t < MAX_EXPERTS) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if ((t & 63) >= d) incl += v;
+    }
+    if ((t & 63) == 63) s_wave_sum[t >> 6] = incl;
+  }
+  if (t == 0) s_pick[0] = -1;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < MAX_EXPERTS / 64; ++w) {
+    if (w < (t >> 6)) before += s_wave_sum[w];
+    total += s_wave_sum[w];
+  }
+  const int v = xcd_order(blockIdx.x, total);  // meaningful for blockIdx.x < total
+  const int excl = before + incl - tiles;
+  if (t < experts && tiles > 0 && v >= excl && v < excl + tiles) {
+    s_pick[0] = t;
+    s_pick[1] = excl;
+  }
+  __syncthreads();
+  e = s_pick[0];
+  if (static_cast<int>(blockIdx.x) >= total || e < 0) return false;
+  local = v - s_pick[1];
+  r0 = min(max(offsets[e], 0), M);
+  Me = min(max(offsets[e + 1], 0), M) - r0;
+  return true;
+}
+
 // ---- LDS-staged epilogue ----
 // A wave stages a block of kRows x 64 32-bit results row-major in LDS (the
 // operand slices are free by then) and reads it back row-contiguous, so that

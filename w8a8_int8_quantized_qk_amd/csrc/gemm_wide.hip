@@ -430,6 +430,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_wide_kernel(
                               tm, tn);
 }
 
+// The MoE grouped GEMM on 256 x 256 tiles: expert e's rows [offsets[e],
+// offsets[e + 1]) times its weight b + e * expert_stride, with its
+// per-channel scales scale_b + e * N; moe_pick (gemm_tile.h) gives each
+// workgroup its expert and tile.
+template <int MODE, bool KTAIL>
+__global__ __launch_bounds__(kThreads, 1) void gemm_i8_wide_moe_kernel(
+    const int8_t* __restrict__ a, const int8_t* __restrict__ b, int32_t* __restrict__ c,
+    const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
+    void* __restrict__ out, int out_dtype, int M, int N, int K, int tiles_n,
+    const int* __restrict__ offsets, int experts, long long expert_stride) {
+  int e, local, r0, Me;
+  if (!tile::moe_pick<BM, QK_MOE_MAX_EXPERTS>(offsets, experts, M, tiles_n, e, local, r0, Me))
+    return;
+  int tm, tn;
+  tile::group_order(local, (Me + BM - 1) / BM, tiles_n, tm, tn);
+  const size_t row_off = static_cast<size_t>(r0);
+  void* out_e = out ? static_cast<char*>(out) + row_off * N * (out_dtype == QK_BF16 ? 2 : 4) : nullptr;
+  gemm_wide_tile<MODE, KTAIL>(a + row_off * K, b + e * expert_stride, c ? c + row_off * N : nullptr,
+                              scale_a ? scale_a + row_off : nullptr,
+                              scale_b ? scale_b + static_cast<size_t>(e) * N : nullptr,
+                              output_scale, out_e, out_dtype, Me, N, K, tm, tn);
+}
+
+template <int MODE>
+hipError_t launch_wide_moe_mode(const GemmArgs& g, const int* offsets, int experts, dim3 grid,
+                                int tiles_n, hipStream_t stream) {
+  const long long stride = static_cast<long long>(g.k) * g.n;
+  if (g.k % BK != 0)
+    return launch(gemm_i8_wide_moe_kernel<MODE, true>, grid, dim3(kThreads), 0, stream, g.a, g.b,
+                  g.c, g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k,
+                  tiles_n, offsets, experts, stride);
+  return launch(gemm_i8_wide_moe_kernel<MODE, false>, grid, dim3(kThreads), 0, stream, g.a, g.b,
+                g.c, g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k,
+                tiles_n, offsets, experts, stride);
+}
+
 template <int MODE>
 hipError_t launch_wide_mode(const GemmArgs& g, dim3 grid, int tiles_m, int tiles_n,
                             hipStream_t stream) {
@@ -451,6 +487,23 @@ bool gemm_wide_applies(int m, int n, int k, int b_layout) {
   const long long tiles = static_cast<long long>((m + wide::BM - 1) / wide::BM) *
                           ((n + wide::BN - 1) / wide::BN);
   return tiles >= 256;  // at least one 256 x 256 tile per CU
+}
+
+bool gemm_wide_moe_applies(int m, int n, int k, int b_layout) {
+  // the dense GEMM of all rows would take the 256 x 256 tiles
+  return gemm_wide_applies(m, n, k, b_layout);
+}
+
+hipError_t launch_gemm_wide_moe(const GemmArgs& g, const int* offsets, int experts,
+                                hipStream_t stream) {
+  // at most floor(m / BM) + experts tile rows over all experts
+  const int tiles_n = (g.n + wide::BN - 1) / wide::BN;
+  const long long tiles = (static_cast<long long>(g.m) / wide::BM + experts) * tiles_n;
+  if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(tiles));
+  if (g.b_layout == QK_B_NK)
+    return wide::launch_wide_moe_mode<tile::kBnkDma>(g, offsets, experts, grid, tiles_n, stream);
+  return wide::launch_wide_moe_mode<tile::kBknDma>(g, offsets, experts, grid, tiles_n, stream);
 }
 
 hipError_t launch_gemm_wide(const GemmArgs& g, hipStream_t stream) {

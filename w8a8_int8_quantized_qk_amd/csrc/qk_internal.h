@@ -89,6 +89,11 @@ hipError_t launch_gemm_mfma(const GemmArgs& g, hipStream_t stream);
 // least one such tile per CU; launch_gemm_mfma picks it when it applies.
 bool gemm_wide_applies(int m, int n, int k, int b_layout);
 hipError_t launch_gemm_wide(const GemmArgs& g, hipStream_t stream);
+// The MoE grouped GEMM on those tiles (gemm_wide.hip), for groups whose
+// dense GEMM of all rows would take them; launch_gemm_moe picks it.
+bool gemm_wide_moe_applies(int m, int n, int k, int b_layout);
+hipError_t launch_gemm_wide_moe(const GemmArgs& g, const int* offsets, int experts,
+                                hipStream_t stream);
 // 256 x 128 tiles with separate transfer and matrix-core waves
 // (gemm_spec.hip), for the outputs the wide kernel does not take; k a
 // multiple of 128, a DMA'd weight layout.
