@@ -84,11 +84,17 @@ __device__ __forceinline__ void add_scaled(v4f& acc, const v4i& p, float s) {
   asm volatile("" : "+v"(acc));
 }
 
-template <int KIND, int MODE, bool KTAIL>
-__global__ __launch_bounds__(kThreads, 1) void gemm_slice_kernel(
+// XF: four more waves (kXferWaves, gemm_tile.h) issue every global-to-LDS
+// transfer, so that the eight matrix-core waves issue none (K % BK == 0, a
+// DMA'd weight; a wave held up issuing transfers cannot issue MFMAs).  Three
+// waves per SIMD then share its registers.
+template <int KIND, int MODE, bool KTAIL, bool XF = false>
+__global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void gemm_slice_kernel(
     const int8_t* __restrict__ a, const int8_t* __restrict__ b, float* __restrict__ c,
     const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
     void* __restrict__ out, int out_dtype, int M, int N, int K, int tiles_m, int tiles_n) {
+  static_assert(!XF || (!KTAIL && (MODE == kBnkDma || MODE == kBknDma)),
+                "transfer waves: whole slices of a DMA'd weight");
   constexpr bool kRegB = MODE == kBknReg4 || MODE == kBknReg1;
   constexpr int GPS = groups_per_slice<KIND>();
   constexpr bool kGrouped = GPS > 0;
@@ -100,8 +106,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_slice_kernel(
   const int n0 = tn * BN;
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
-  const int wm = wave / (BN / WTN);
+  // wave-uniform for the compiler too, so that the two kinds branch
+  const int wave = XF ? __builtin_amdgcn_readfirstlane(t >> 6) : t >> 6;
+  const int wm = (wave % kWaves) / (BN / WTN);
   const int wn = wave % (BN / WTN);
 
   // epilogue scales: per token, and per channel (FP8) or 1 (group scales
@@ -130,7 +137,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_slice_kernel(
   };
   constexpr int kFetchOps = BM * BK / 1024 / kWaves + (kRegB ? 0 : BN * BK / 1024 / kWaves);
   constexpr int kOpsA = rowk_ops<BM>();
-  constexpr bool kFixedParts = !KTAIL && !kRegB;
+  constexpr bool kFixedParts = !KTAIL && !kRegB && !XF;
   const uint32_t lds_smem = lds_addr(smem);
   using Parts = std::conditional_t<kFixedParts, FixedParts<MODE == kBnkDma ? kBnkDma : kBknDma>,
                                    NoParts>;
@@ -236,8 +243,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_slice_kernel(
     __syncthreads();
   };
 
+  if (XF && wave >= kWaves) {
+    // ---------------- transfer wave ----------------
+    if constexpr (XF) {
+      XferParts<MODE == kBnkDma ? kBnkDma : kBknDma> xparts;
+      xparts.init(a, b, M, N, K, m0, n0, wave - kWaves);
+      xparts.run(lds_smem, KT);
+    }
+  } else {
   v8i fa[FM], fb[FN];  // fragments of the slice being multiplied
-  if (KT > 0) {
+  if (KT > 0 && XF) {
+    load_scales(0, sc);
+    __syncthreads();  // slice 0 in LDS (the transfer waves waited for it)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = read_a(a_lds(0), i);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = read_b(b_lds(0), j);
+  } else if (KT > 0) {
     fetch(0);
     load_scales(0, sc);
     if constexpr (kRegB) breg.load(b, N, K, n0, 0);
@@ -361,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_slice_kernel(
     for (int kt = 0; kt < KT; ++kt) {
       const bool prefetch = kt + 2 < KT;
       auto dma = [&](int part_idx) {
-        if (prefetch) fetch_part(kt + 2, part_idx);
+        if (!XF && prefetch) fetch_part(kt + 2, part_idx);
         __builtin_amdgcn_sched_barrier(0);
       };
       // ---- phase 0 ----
@@ -374,7 +396,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_slice_kernel(
       }
       // ---- barrier for slice kt + 1 ----
       if (kt + 1 < KT) {
-        if (prefetch) wait_vmcnt<kSplit>(); else wait_vmcnt<0>();
+        if constexpr (!XF) {
+          if (prefetch) wait_vmcnt<kSplit>(); else wait_vmcnt<0>();
+        }
         __syncthreads();
         if (KTAIL && kt + 1 == KT - 1) zero_tail(kt + 1);
       }
@@ -413,10 +437,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_slice_kernel(
     }
   }
 
+  }  // matrix-core waves
+
   // ---- epilogue ----
-  // Each wave holds the final sums of its 64 x 64 sub-tile; it stages them
-  // row-major in LDS (the operand slices are free after the barrier) and
-  // stores whole 128-byte row segments with nontemporal stores.
+  // Each matrix-core wave holds the final sums of its 64 x 64 sub-tile; it
+  // stages them row-major in LDS (the operand slices are free after the
+  // barrier) and stores whole 128-byte row segments with nontemporal stores.
   constexpr int kStageBytes = WTM * WTN * 4;
   static_assert(WTN == kStageCols, "staging rows are one wave tile wide");
   static_assert(kWaves * kStageBytes + 4 * (BM + BN) <= kStages * STAGE, "staging fits in LDS");
@@ -424,16 +450,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_slice_kernel(
   float* s_sa = reinterpret_cast<float*>(smem + kWaves * kStageBytes);
   float* s_sb = s_sa + BM;
   if (out && t < BM + BN) s_sa[t] = t < BM ? scale_reg : scale_reg * output_scale;  // s_sb follows s_sa
-  int* stage = reinterpret_cast<int*>(smem + wave * kStageBytes);
+  int* stage = reinterpret_cast<int*>(smem + (wave % kWaves) * kStageBytes);
+  if (!XF || wave < kWaves) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const v4i bits = {__float_as_int(acc[i][j][0]), __float_as_int(acc[i][j][1]),
-                        __float_as_int(acc[i][j][2]), __float_as_int(acc[i][j][3])};
-      stage_fragment(stage, lane, i, j, bits);
-    }
+      for (int j = 0; j < FN; ++j) {
+        const v4i bits = {__float_as_int(acc[i][j][0]), __float_as_int(acc[i][j][1]),
+                          __float_as_int(acc[i][j][2]), __float_as_int(acc[i][j][3])};
+        stage_fragment(stage, lane, i, j, bits);
+      }
+  }
   __syncthreads();  // scales visible (each wave reads back only its own staging)
+  if (XF && wave >= kWaves) return;
 
   const int lrow0 = wm * WTM;
   const int lcol0 = wn * WTN;
@@ -449,6 +478,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_slice_kernel(
 template <int KIND, int MODE>
 hipError_t launch_mode(const SliceGemmArgs& g, dim3 grid, int tiles_m, int tiles_n,
                        hipStream_t stream) {
+  // FP8 with whole slices of a DMA'd weight: transfer waves of their own
+  // (measured 35.3 -> 33.6 us at 2048 x 4096 x 4096).  The group-scale kinds
+  // keep eight waves: with three waves per SIMD their binary32 accumulators,
+  // partials and scales exceed the 168 registers each wave then has, and
+  // the spills made them slower (G = 128: 56.9 -> 74.6 us).
+  if constexpr ((MODE == kBnkDma || MODE == kBknDma) && KIND == kFp8) {
+    if (g.k > 0 && g.k % BK == 0)  // k = 0 has no slice to transfer: the kernel below
+      return launch(gemm_slice_kernel<KIND, MODE, false, true>, grid,
+                    dim3(kThreads + 64 * kXferWaves), 0, stream, g.a, g.b, g.c, g.scale_a,
+                    g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k, tiles_m,
+                    tiles_n);
+  }
   if (g.k % BK != 0)
     return launch(gemm_slice_kernel<KIND, MODE, true>, grid, dim3(kThreads), 0, stream, g.a, g.b,
                   g.c, g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k,

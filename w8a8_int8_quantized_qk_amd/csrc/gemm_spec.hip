@@ -53,11 +53,7 @@ constexpr int WTN = 64;                       // ... columns
 constexpr int FM = WTM / 16;
 constexpr int FN = WTN / 16;
 static_assert((BM / WTM) * (BN / WTN) == kMma, "one sub-tile per matrix-core wave");
-constexpr int kPartsA = BM * BK / 1024;        // 32 transfers of A per slice
-constexpr int kPartsB = BN * BK / 1024;        // 16 of the weight
-constexpr int kOps = (kPartsA + kPartsB) / kXfer;  // 12 per transfer wave
-static_assert(kOps * kXfer == kPartsA + kPartsB, "transfers divide over the waves");
-constexpr int kOpsA = kPartsA / kXfer;  // 8 A parts, then 4 weight parts
+static_assert(kXfer == kXferWaves, "the transfer waves of gemm_tile.h");
 
 template <int MODE>
 __device__ __forceinline__ void gemm_spec_tile(
@@ -95,64 +91,9 @@ __device__ __forceinline__ void gemm_spec_tile(
 
   if (wave >= kMma) {
     // ---------------- transfer wave ----------------
-    const int d = wave - kMma;
-    const uint32_t lds_smem = lds_addr(smem);
-    const int8_t* src[kOps];
-    uint32_t slot[kOps];
-    size_t stride[kOps];
-#pragma unroll
-    for (int q = 0; q < kOps; ++q) {
-      if (q < kOpsA) {  // A block kOpsA d + q: 8 rows of 128 bytes
-        const int blk = kOpsA * d + q;
-        const int row = blk * 8 + (lane >> 3);
-        const int lchunk = (lane & 7) ^ rowk_swz(row);
-        src[q] = a + (static_cast<uint32_t>(min(m0 + row, M - 1)) * static_cast<uint32_t>(K) +
-                      16 * lchunk);
-        slot[q] = static_cast<uint32_t>(blk * 1024);
-        stride[q] = BK;
-      } else if constexpr (MODE == kBnkDma) {  // [N][K] weight block: 8 rows of 128 bytes
-        const int blk = (kOps - kOpsA) * d + (q - kOpsA);
-        const int row = blk * 8 + (lane >> 3);
-        const int lchunk = (lane & 7) ^ rowk_swz(row);
-        src[q] = b + (static_cast<uint32_t>(min(n0 + row, N - 1)) * static_cast<uint32_t>(K) +
-                      16 * lchunk);
-        slot[q] = static_cast<uint32_t>(A_STAGE + blk * 1024);
-        stride[q] = BK;
-      } else {  // [K][N] weight block: 8 k rows of 128 bytes
-        const int blk = (kOps - kOpsA) * d + (q - kOpsA);
-        const int k = blk * 8 + (lane >> 3);
-        const int lchunk = (lane & 7) ^ kn_swz(k);
-        src[q] = b + (static_cast<uint32_t>(k) * static_cast<uint32_t>(N) +
-                      static_cast<uint32_t>(min(n0 + 16 * lchunk, N - 16)));
-        slot[q] = static_cast<uint32_t>(A_STAGE + blk * 1024);
-        stride[q] = static_cast<size_t>(BK) * N;
-      }
-    }
-    auto issue = [&](int s) {
-#pragma unroll
-      for (int q = 0; q < kOps; ++q)
-        lds_dma16(src[q] + static_cast<size_t>(s) * stride[q],
-                  __builtin_amdgcn_readfirstlane(
-                      lds_smem + static_cast<uint32_t>((s % kStages) * STAGE) + slot[q]));
-    };
-    issue(0);
-    if (KT > 1) {
-      issue(1);
-      wait_vmcnt<kOps>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __syncthreads();  // slice 0 in LDS
-    for (int kt = 0; kt < KT; ++kt) {
-      // the stage of slice kt - 1 is free: every matrix-core wave read its
-      // last fragments before the previous barrier
-      const bool more = kt + 2 < KT;
-      if (more) issue(kt + 2);
-      if (kt + 1 < KT) {
-        if (more) wait_vmcnt<kOps>(); else wait_vmcnt<0>();  // slice kt + 1 landed
-        __syncthreads();
-      }
-    }
+    XferParts<MODE> parts;
+    parts.init(a, b, M, N, K, m0, n0, wave - kMma);
+    parts.run(lds_addr(smem), KT);
   } else {
     // ---------------- matrix-core wave ----------------
     const int a_row = wm * WTM + (lane & 15);

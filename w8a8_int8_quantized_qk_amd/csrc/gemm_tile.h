@@ -150,6 +150,87 @@ struct FixedParts {
 
 struct NoParts {};
 
+// Transfer waves' parts, for kernels whose global-to-LDS transfers are issued
+// by kXferWaves waves of their own: transfer wave d (0 .. kXferWaves - 1)
+// issues kXferOps of a slice's 48 1-KiB parts, A blocks kXferOpsA d ..
+// kXferOpsA d + 7 (8 rows of 128 bytes each), then a quarter of the weight
+// block.  Valid for K a multiple of BK and a DMA'd weight.
+constexpr int kXferWaves = 4;
+constexpr int kXferOps = (BM + BN) * BK / 1024 / kXferWaves;  // 12
+constexpr int kXferOpsA = BM * BK / 1024 / kXferWaves;        // 8
+template <int MODE>
+struct XferParts {
+  static_assert(MODE == kBnkDma || MODE == kBknDma, "DMA weight layouts");
+  const int8_t* src[kXferOps];
+  uint32_t slot[kXferOps];
+  size_t stride[kXferOps];
+
+  __device__ __forceinline__ void init(const int8_t* __restrict__ a, const int8_t* __restrict__ b,
+                                       int M, int N, int K, int m0, int n0, int d) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < kXferOps; ++q) {
+      if (q < kXferOpsA) {  // A block kXferOpsA d + q: 8 rows of 128 bytes
+        const int blk = kXferOpsA * d + q;
+        const int row = blk * 8 + (lane >> 3);
+        const int lchunk = (lane & 7) ^ rowk_swz(row);
+        src[q] = a + (static_cast<uint32_t>(min(m0 + row, M - 1)) * static_cast<uint32_t>(K) +
+                      16 * lchunk);
+        slot[q] = static_cast<uint32_t>(blk * 1024);
+        stride[q] = BK;
+      } else if constexpr (MODE == kBnkDma) {  // [N][K] weight block: 8 rows of 128 bytes
+        const int blk = (kXferOps - kXferOpsA) * d + (q - kXferOpsA);
+        const int row = blk * 8 + (lane >> 3);
+        const int lchunk = (lane & 7) ^ rowk_swz(row);
+        src[q] = b + (static_cast<uint32_t>(min(n0 + row, N - 1)) * static_cast<uint32_t>(K) +
+                      16 * lchunk);
+        slot[q] = static_cast<uint32_t>(A_STAGE + blk * 1024);
+        stride[q] = BK;
+      } else {  // [K][N] weight block: 8 k rows of 128 bytes
+        const int blk = (kXferOps - kXferOpsA) * d + (q - kXferOpsA);
+        const int k = blk * 8 + (lane >> 3);
+        const int lchunk = (lane & 7) ^ kn_swz(k);
+        src[q] = b + (static_cast<uint32_t>(k) * static_cast<uint32_t>(N) +
+                      static_cast<uint32_t>(min(n0 + 16 * lchunk, N - 16)));
+        slot[q] = static_cast<uint32_t>(A_STAGE + blk * 1024);
+        stride[q] = static_cast<size_t>(BK) * N;
+      }
+    }
+  }
+  // every part of slice s into its stage of the LDS ring at lds_smem
+  __device__ __forceinline__ void issue(uint32_t lds_smem, int s) const {
+#pragma unroll
+    for (int q = 0; q < kXferOps; ++q)
+      lds_dma16(src[q] + static_cast<size_t>(s) * stride[q],
+                __builtin_amdgcn_readfirstlane(
+                    lds_smem + static_cast<uint32_t>((s % kStages) * STAGE) + slot[q]));
+  }
+  // The transfer wave's whole k loop, matching a consumer that waits at one
+  // barrier after slice 0 has landed and then one per slice kt < KT - 1, by
+  // which slice kt + 1 has landed and every wave has read its last fragments
+  // of slice kt - 1 (whose stage slice kt + 2 then takes).  KT <= 0: no
+  // transfer and no barrier (the operands may be empty).
+  __device__ __forceinline__ void run(uint32_t lds_smem, int KT) const {
+    if (KT <= 0) return;
+    issue(lds_smem, 0);
+    if (KT > 1) {
+      issue(lds_smem, 1);
+      wait_vmcnt<kXferOps>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();  // slice 0 in LDS
+    for (int kt = 0; kt < KT; ++kt) {
+      const bool more = kt + 2 < KT;
+      if (more) issue(lds_smem, kt + 2);
+      if (kt + 1 < KT) {
+        if (more) wait_vmcnt<kXferOps>(); else wait_vmcnt<0>();  // slice kt + 1 landed
+        __syncthreads();
+      }
+    }
+  }
+};
+
 // ---- register-staged [K][N] weight (N not a multiple of 16) ----
 __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
                                              uint32_t& c0, uint32_t& c1, uint32_t& c2,
