@@ -248,6 +248,8 @@ SHAPES = [
     (513, 257, 4096, "nk"),   # [N][K] weight, ragged m and n, 32 slices
     (64, 4096, 4096, "kn"),
     (2048, 128, 4096, "kn"),  # the prefill row count
+    (300, 272, 256, "kn"),    # transfer waves: two slices, fewer than the LDS stages
+    (129, 144, 384, "nk"),    # transfer waves: three slices, ragged m and n
 ]
 
 
