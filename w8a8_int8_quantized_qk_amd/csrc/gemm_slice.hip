@@ -484,7 +484,8 @@ hipError_t launch_mode(const SliceGemmArgs& g, dim3 grid, int tiles_m, int tiles
   // partials and scales exceed the 168 registers each wave then has, and
   // the spills made them slower (G = 128: 56.9 -> 74.6 us).
   if constexpr ((MODE == kBnkDma || MODE == kBknDma) && KIND == kFp8) {
-    if (g.k > 0 && g.k % BK == 0)  // k = 0 has no slice to transfer: the kernel below
+    // k = 0 has no slice to transfer: the kernel below
+    if (g.k > 0 && g.k % BK == 0 && xfer_parts_fit(g.n, g.k))
       return launch(gemm_slice_kernel<KIND, MODE, false, true>, grid,
                     dim3(kThreads + 64 * kXferWaves), 0, stream, g.a, g.b, g.c, g.scale_a,
                     g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k, tiles_m,

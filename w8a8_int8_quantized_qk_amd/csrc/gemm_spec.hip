@@ -14,19 +14,28 @@
 // made its loop 31% faster, leaving out only the waits for them 6%; a wave
 // held up issuing a transfer cannot issue its MFMAs either):
 //   * Workgroup tile 256 (M) x 128 (N), k slices of 128 bytes, three LDS
-//     stages of 48 KiB (the 256 x 128 kernel's layouts, swizzles and
-//     fragment reads, gemm_tile.h).
+//     stages (the 256 x 128 kernel's row layouts, swizzles and fragment
+//     reads, gemm_tile.h) in a split ring: the three A blocks first, then
+//     the three weight blocks.
 //   * Twelve waves, three per SIMD: waves 0..7 multiply (two per SIMD: one
 //     wave issues a 16x16x64 MFMA only every ~25 cycles, measured, so a
 //     single wave cannot keep a matrix core busy), waves 8..11 only move
 //     data.  Transfer wave d issues 12 of a slice's 48 1-KiB
 //     global_load_lds_dwordx4 (A rows 64 d .. 64 d + 63 and a quarter of the
-//     weight block), waits for them and meets the others at the slice
-//     barrier.  Matrix-core wave w owns a 64 x 64 sub-tile over the whole k
-//     range (three waves per SIMD leave ~168 registers each): per slice two
-//     64-deep steps of 4 x 4 v_mfma_i32_16x16x64_i8, reading the next step's
-//     8 fragments while it multiplies the current one.  No partial sums
-//     cross waves, so there is no k-group hand-over.
+//     weight block) from a scalar base plus fixed per-lane offsets, waits for
+//     them and meets the others at the slice barrier.  Matrix-core wave w
+//     owns a 64 x 64 sub-tile over the whole k range (three waves per SIMD
+//     leave ~168 registers each): per slice two 64-deep steps of 4 x 4
+//     v_mfma_i32_16x16x64_i8, reading the next step's 8 fragments while it
+//     multiplies the current one.  No partial sums cross waves, so there is
+//     no k-group hand-over.
+//   * No vector-ALU work in the k loop: on this chip such instructions do
+//     not overlap a wave's MFMAs but add to the SIMD's time (a probe: 4
+//     conversions or FMAs per 16x16x64 MFMA, from the same or another wave,
+//     raise its cycle count from 16.5 to 25-27).  The loop is unrolled over
+//     the three stages so that every fragment read is a base register plus an
+//     immediate offset, and the transfer waves advance their sources in
+//     scalar registers.
 //   * One barrier per slice, between its two steps: before it the transfer
 //     waves have seen slice kt + 1 land; after it they issue slice kt + 2
 //     into the stage of slice kt - 1, whose last fragments the matrix-core
@@ -62,8 +71,11 @@ __device__ __forceinline__ void gemm_spec_tile(
     void* __restrict__ out, int out_dtype, int M, int N, int K, int tm, int tn) {
   static_assert(MODE == kBnkDma || MODE == kBknDma, "DMA weight layouts");
   constexpr int kStageBytes = WTM * WTN * 4;  // one matrix-core wave's staged block (16 KiB)
-  static_assert(kMma * kStageBytes + 8 * (BM + BN) <= kStages * STAGE, "epilogue fits in LDS");
+  static_assert(kMma * kStageBytes <= kStages * STAGE, "epilogue staging fits in the ring");
   __shared__ __attribute__((aligned(1024))) char smem[kStages * STAGE];
+  // per-token scales, then per-channel ones times output_scale; written
+  // before the k loop so that no register holds them across it
+  __shared__ float s_scale[BM + BN];
 
   const int m0 = tm * BM;
   const int n0 = tn * BN;
@@ -72,18 +84,17 @@ __device__ __forceinline__ void gemm_spec_tile(
   // wave-uniform for the compiler too, so the two kinds branch, not mask
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
 
-  float scale_reg = 0.0f;
-  if (out) {
+  if (out && t < BM + BN) {
+    float v = 0.0f;
     if (t < BM) {
-      if (m0 + t < M) scale_reg = scale_a[m0 + t];
-    } else if (t < BM + BN && n0 + t - BM < N) {
-      scale_reg = scale_b[n0 + t - BM];  // times output_scale later
+      if (m0 + t < M) v = scale_a[m0 + t];
+    } else if (n0 + t - BM < N) {
+      v = scale_b[n0 + t - BM] * output_scale;
     }
+    s_scale[t] = v;  // read after the barriers below
   }
 
   const int KT = K / BK;  // K % BK == 0
-  auto a_lds = [&](int s) -> const char* { return smem + (s % kStages) * STAGE; };
-  auto b_lds = [&](int s) -> const char* { return smem + (s % kStages) * STAGE + A_STAGE; };
 
   v4i acc[FM][FN];
   const int wm = wave >> 1;  // matrix-core wave's 64 x 64 sub-tile
@@ -91,27 +102,66 @@ __device__ __forceinline__ void gemm_spec_tile(
 
   if (wave >= kMma) {
     // ---------------- transfer wave ----------------
-    XferParts<MODE> parts;
+    XferParts<MODE, true> parts;
     parts.init(a, b, M, N, K, m0, n0, wave - kMma);
     parts.run(lds_addr(smem), KT);
   } else {
     // ---------------- matrix-core wave ----------------
-    const int a_row = wm * WTM + (lane & 15);
-    const int b_row = wn * WTN + (lane & 15);
-    // fragments of 64-deep step g of a slice: lane l holds k = 64 g + 16 (l / 16)
-    // .. + 15 of row (A) or column (B) l % 16 of the fragment
-    auto read_a = [&](const char* As, int i, int g) -> v4i {
-      return *reinterpret_cast<const v4i*>(As + rowk_offset(a_row + i * 16, 4 * g + (lane >> 4)));
+    // Every fragment read is a per-lane base plus a constant: the loop below
+    // is unrolled over the three stages of the split ring (A stages at
+    // s * A_STAGE, weight stages after them at kStages * A_STAGE + s *
+    // B_STAGE), and a DS instruction's immediate offset reaches 65535 bytes:
+    // one set of A bases serves stages 0 and 1, a second stage 2, and one set
+    // of weight bases all three.  No address arithmetic is left in the loop,
+    // whose vector-ALU issue cycles the MFMAs share.
+    static_assert(kStages == 3, "three stages");
+    static_assert(A_STAGE + 2048 * (FM - 1) < 65536, "A: stage 1 from the stage-0 bases");
+    static_assert(2 * B_STAGE + BN * (64 + 8) < 65536 && 2 * B_STAGE + 2048 * (FN - 1) < 65536,
+                  "weight: every stage from one base");
+    const int c = lane >> 4;     // the lane's 16-byte chunk of a 64-deep step
+    const int i16 = lane & 15;
+    // LDS byte addresses; the empty asm makes each base opaque, so that the
+    // compiler keeps it in its own register instead of deriving one base
+    // from another with offsets beyond the immediate's reach
+    auto opaque = [](uint32_t x) {
+      asm("" : "+v"(x));
+      return x;
     };
-    auto read_b_tr = [&](const char* Bs, int j, int h, int g) -> v2i {
-      const int i16 = lane & 15;
-      const int kr = 64 * g + 16 * (lane >> 4) + (i16 >> 1) + 8 * h;
-      const int cb = (wn * WTN + j * 16) >> 4;
+    const uint32_t lds0 = lds_addr(smem);
+    const uint32_t b_ring = lds0 + kStages * A_STAGE;
+    uint32_t a_base[2][2];    // [set][step g]: A fragment 0; fragment i at + 2048 i
+    uint32_t b_base[FN];      // [j] ([K][N] weight): column block j, k row 16 c + i16 / 2
+    uint32_t bk_base[2];      // [g] ([N][K] weight): fragment 0; fragment j at + 2048 j
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const uint32_t a_off = rowk_offset(wm * WTM + i16, 4 * g + c);
+      a_base[0][g] = opaque(lds0 + a_off);
+      a_base[1][g] = opaque(lds0 + 2 * A_STAGE + a_off);
+      if constexpr (MODE == kBnkDma) bk_base[g] = opaque(b_ring + rowk_offset(wn * WTN + i16, 4 * g + c));
+    }
+    // kn_swz of k rows 64 g + 16 c + i16 / 2 + 8 h is that of 16 c + i16 / 2
+    // for every g and h, so they differ from it by (64 g + 8 h) rows
+    if constexpr (MODE == kBknDma) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        b_base[j] = opaque(b_ring + kn_offset(16 * c + (i16 >> 1), (wn * WTN + j * 16) >> 4) +
+                           8 * (i16 & 1));
+    }
+    typedef __attribute__((address_space(3))) const v4i* lds_v4i;
+    // fragments of 64-deep step g of a slice in stage S: lane l holds k = 64 g
+    // + 16 (l / 16) .. + 15 of row (A) or column (B) l % 16 of the fragment
+    auto read_a = [&](auto S_, int i, int g) -> v4i {
+      constexpr int S = decltype(S_)::value;
+      return *reinterpret_cast<lds_v4i>(a_base[S / 2][g] + (S == 1 ? A_STAGE : 0) + 2048 * i);
+    };
+    auto read_b_tr = [&](auto S_, int j, int h, int g) -> v2i {
+      constexpr int S = decltype(S_)::value;
       return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (__attribute__((address_space(3))) v2i*)(Bs + kn_offset(kr, cb) + 8 * (i16 & 1)));
+          (__attribute__((address_space(3))) v2i*)(b_base[j] + S * B_STAGE + BN * (64 * g + 8 * h)));
     };
-    auto read_b_rowk = [&](const char* Bs, int j, int g) -> v4i {
-      return *reinterpret_cast<const v4i*>(Bs + rowk_offset(b_row + j * 16, 4 * g + (lane >> 4)));
+    auto read_b_rowk = [&](auto S_, int j, int g) -> v4i {
+      constexpr int S = decltype(S_)::value;
+      return *reinterpret_cast<lds_v4i>(bk_base[g] + S * B_STAGE + 2048 * j);
     };
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -119,10 +169,11 @@ __device__ __forceinline__ void gemm_spec_tile(
       for (int j = 0; j < FN; ++j) acc[i][j] = v4i{};
 
     v4i f0a[FM], f0b[FN], f1a[FM], f1b[FN];
-    auto mfma_step = [&](v4i (&xa)[FM], v4i (&xb)[FN], v4i (&ya)[FM], v4i (&yb)[FN],
-                         const char* As, const char* Bs, int g) {
-      // 16 MFMAs of (xa, xb); after each of the first 12 one read of (ya,
-      // yb): the A fragments, then the weight's
+    // 16 MFMAs of (xa, xb); after each of the first 12 one read of (ya, yb)
+    // from step g of stage S: the A fragments, then the weight's
+    auto mfma_step = [&](auto S_, auto G_, v4i (&xa)[FM], v4i (&xb)[FN], v4i (&ya)[FM],
+                         v4i (&yb)[FN]) {
+      constexpr int g = decltype(G_)::value;
       v2i lo[FN], hi[FN];
 #pragma unroll
       for (int n = 0; n < FM * FN; ++n) {
@@ -131,14 +182,14 @@ __device__ __forceinline__ void gemm_spec_tile(
         acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa[i], xb[j], acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (n < FM) {
-          ya[n] = read_a(As, n, g);
+          ya[n] = read_a(S_, n, g);
         } else if (n < FM + 2 * FN) {
           const int r = n - FM;
           if constexpr (MODE == kBknDma) {
-            if (r & 1) hi[r >> 1] = read_b_tr(Bs, r >> 1, 1, g);
-            else lo[r >> 1] = read_b_tr(Bs, r >> 1, 0, g);
+            if (r & 1) hi[r >> 1] = read_b_tr(S_, r >> 1, 1, g);
+            else lo[r >> 1] = read_b_tr(S_, r >> 1, 0, g);
           } else if ((r & 1) == 0) {
-            yb[r >> 1] = read_b_rowk(Bs, r >> 1, g);
+            yb[r >> 1] = read_b_rowk(S_, r >> 1, g);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -148,47 +199,63 @@ __device__ __forceinline__ void gemm_spec_tile(
         for (int j = 0; j < FN; ++j) yb[j] = v4i{lo[j].x, lo[j].y, hi[j].x, hi[j].y};
       }
     };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
 
     __syncthreads();  // slice 0 in LDS
     if (KT > 0) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) f0a[i] = read_a(a_lds(0), i, 0);
+      for (int i = 0; i < FM; ++i) f0a[i] = read_a(S0{}, i, 0);
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         if constexpr (MODE == kBknDma) {
-          const v2i lo = read_b_tr(b_lds(0), j, 0, 0);
-          const v2i hi = read_b_tr(b_lds(0), j, 1, 0);
+          const v2i lo = read_b_tr(S0{}, j, 0, 0);
+          const v2i hi = read_b_tr(S0{}, j, 1, 0);
           f0b[j] = v4i{lo.x, lo.y, hi.x, hi.y};
         } else {
-          f0b[j] = read_b_rowk(b_lds(0), j, 0);
+          f0b[j] = read_b_rowk(S0{}, j, 0);
         }
       }
     }
-    for (int kt = 0; kt < KT; ++kt) {
+    // slice kt, which sits in stage S = kt % 3
+    auto slice = [&](auto S_, int kt) {
+      constexpr int S = decltype(S_)::value;
       // step 0 of slice kt, reading its step 1
-      mfma_step(f0a, f0b, f1a, f1b, a_lds(kt), b_lds(kt), 1);
+      mfma_step(S_, S1{}, f0a, f0b, f1a, f1b);
       // slice kt + 1 landed; this wave's reads of slice kt are complete
       if (kt + 1 < KT) __syncthreads();
       // step 1 of slice kt, reading step 0 of slice kt + 1 (after the last
       // slice: a valid, unused stage; not used)
-      mfma_step(f1a, f1b, f0a, f0b, a_lds(kt + 1), b_lds(kt + 1), 0);
+      mfma_step(std::integral_constant<int, (S + 1) % kStages>{}, S0{}, f1a, f1b, f0a, f0b);
+    };
+    int kt = 0;
+    for (; kt + kStages <= KT; kt += kStages) {
+      slice(S0{}, kt);
+      slice(S1{}, kt + 1);
+      slice(S2{}, kt + 2);
     }
+    if (kt < KT) slice(S0{}, kt);
+    if (kt + 1 < KT) slice(S1{}, kt + 1);
   }
 
   // ---- epilogue ----
   __syncthreads();  // every wave is done with the stages
-  float* s_sa = reinterpret_cast<float*>(smem + kMma * kStageBytes);
-  float* s_sb = s_sa + BM;
-  if (out && t < BM + BN) s_sa[t] = t < BM ? scale_reg : scale_reg * output_scale;
+  const float* s_sa = s_scale;
+  const float* s_sb = s_scale + BM;
   int* stage = reinterpret_cast<int*>(smem + (wave & 7) * kStageBytes);
   if (wave < kMma) {
+    // the lane index again from the exec mask, so that no register keeps it
+    // over the k loop
+    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) stage_fragment(stage, lane, i, j, acc[i][j]);
   }
-  __syncthreads();  // staged blocks and scales visible
+  __syncthreads();  // staged blocks visible
   if (wave < kMma) {
+    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     const int lrow0 = wm * WTM;
     const int lcol0 = wn * WTN;
     if (c) store4<64, false, true>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, c);
@@ -215,7 +282,7 @@ __global__ __launch_bounds__(kSpecThreads, 1) void gemm_i8_spec_kernel(
 }  // namespace
 
 bool gemm_spec_applies(int m, int n, int k, int b_layout) {
-  if (k <= 0 || k % tile::BK != 0 || n < 16) return false;
+  if (k <= 0 || k % tile::BK != 0 || n < 16 || !tile::xfer_parts_fit(n, k)) return false;
   if (b_layout == QK_B_KN && n % 16 != 0) return false;  // DMA of [k][n] rows in 16-byte chunks
   return true;
 }

@@ -150,60 +150,90 @@ struct FixedParts {
 
 struct NoParts {};
 
+// The transfer waves' per-lane source offsets (below 256 rows of K bytes, or
+// 128 k rows of N bytes) fit in 32 bits.
+__host__ __device__ constexpr bool xfer_parts_fit(int n, int k) {
+  return k > 0 && n > 0 && k <= (1 << 24) && n <= (1 << 24);
+}
+
 // Transfer waves' parts, for kernels whose global-to-LDS transfers are issued
 // by kXferWaves waves of their own: transfer wave d (0 .. kXferWaves - 1)
 // issues kXferOps of a slice's 48 1-KiB parts, A blocks kXferOpsA d ..
 // kXferOpsA d + 7 (8 rows of 128 bytes each), then a quarter of the weight
-// block.  Valid for K a multiple of BK and a DMA'd weight.
+// block.  Valid for K a multiple of BK, a DMA'd weight and xfer_parts_fit.
 constexpr int kXferWaves = 4;
 constexpr int kXferOps = (BM + BN) * BK / 1024 / kXferWaves;  // 12
 constexpr int kXferOpsA = BM * BK / 1024 / kXferWaves;        // 8
-template <int MODE>
+//
+// Two layouts of the LDS ring: interleaved (SPLIT false), stage s at
+// s * STAGE holding the A block and then the weight block at A_STAGE; split
+// (SPLIT true), the A blocks of the stages at s * A_STAGE and the weight
+// blocks after all of them, at kStages * A_STAGE + s * B_STAGE, so that the
+// three weight stages lie within one 64 KiB reach of a DS immediate offset.
+template <int MODE, bool SPLIT = false>
 struct XferParts {
   static_assert(MODE == kBnkDma || MODE == kBknDma, "DMA weight layouts");
-  const int8_t* src[kXferOps];
+  static constexpr uint32_t kBSlot0 = SPLIT ? 0 : A_STAGE;  // weight block within its stage
+  // A part's source is a wave-uniform base (the tile's A rows or weight
+  // block at slice 0, advanced per slice in scalar registers) plus this
+  // lane's 32-bit offset, which stays fixed over the k loop; xfer_parts_fit
+  // bounds the offsets.
+  const int8_t* base_a;
+  const int8_t* base_b;
+  size_t stride_b;             // weight bytes per slice (A: BK)
+  uint32_t voff[kXferOps];
   uint32_t slot[kXferOps];
-  size_t stride[kXferOps];
 
   __device__ __forceinline__ void init(const int8_t* __restrict__ a, const int8_t* __restrict__ b,
                                        int M, int N, int K, int m0, int n0, int d) {
-    const int lane = threadIdx.x & 63;
+    // the lane index from the exec mask (the whole wave runs this), not from
+    // threadIdx, which the kernel then need not keep in a register
+    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    base_a = a + static_cast<size_t>(m0) * K;
+    base_b = MODE == kBknDma ? b + n0 : b + static_cast<size_t>(n0) * K;
+    stride_b = MODE == kBknDma ? static_cast<size_t>(BK) * N : BK;
 #pragma unroll
     for (int q = 0; q < kXferOps; ++q) {
       if (q < kXferOpsA) {  // A block kXferOpsA d + q: 8 rows of 128 bytes
         const int blk = kXferOpsA * d + q;
         const int row = blk * 8 + (lane >> 3);
         const int lchunk = (lane & 7) ^ rowk_swz(row);
-        src[q] = a + (static_cast<uint32_t>(min(m0 + row, M - 1)) * static_cast<uint32_t>(K) +
-                      16 * lchunk);
+        voff[q] = static_cast<uint32_t>(min(m0 + row, M - 1) - m0) * static_cast<uint32_t>(K) +
+                  16 * lchunk;
         slot[q] = static_cast<uint32_t>(blk * 1024);
-        stride[q] = BK;
       } else if constexpr (MODE == kBnkDma) {  // [N][K] weight block: 8 rows of 128 bytes
         const int blk = (kXferOps - kXferOpsA) * d + (q - kXferOpsA);
         const int row = blk * 8 + (lane >> 3);
         const int lchunk = (lane & 7) ^ rowk_swz(row);
-        src[q] = b + (static_cast<uint32_t>(min(n0 + row, N - 1)) * static_cast<uint32_t>(K) +
-                      16 * lchunk);
-        slot[q] = static_cast<uint32_t>(A_STAGE + blk * 1024);
-        stride[q] = BK;
-      } else {  // [K][N] weight block: 8 k rows of 128 bytes
+        voff[q] = static_cast<uint32_t>(min(n0 + row, N - 1) - n0) * static_cast<uint32_t>(K) +
+                  16 * lchunk;
+        slot[q] = kBSlot0 + static_cast<uint32_t>(blk * 1024);
+      } else {  // [K][N] weight block: 8 k rows of 128 bytes (n0 <= N - 16)
         const int blk = (kXferOps - kXferOpsA) * d + (q - kXferOpsA);
         const int k = blk * 8 + (lane >> 3);
         const int lchunk = (lane & 7) ^ kn_swz(k);
-        src[q] = b + (static_cast<uint32_t>(k) * static_cast<uint32_t>(N) +
-                      static_cast<uint32_t>(min(n0 + 16 * lchunk, N - 16)));
-        slot[q] = static_cast<uint32_t>(A_STAGE + blk * 1024);
-        stride[q] = static_cast<size_t>(BK) * N;
+        voff[q] = static_cast<uint32_t>(k) * static_cast<uint32_t>(N) +
+                  static_cast<uint32_t>(min(n0 + 16 * lchunk, N - 16) - n0);
+        slot[q] = kBSlot0 + static_cast<uint32_t>(blk * 1024);
       }
     }
   }
+  // offset of part q's stage of slice s in the ring
+  __device__ __forceinline__ static uint32_t stage_offset(int s, int q) {
+    if constexpr (SPLIT)
+      return static_cast<uint32_t>(q < kXferOpsA ? (s % kStages) * A_STAGE
+                                                 : kStages * A_STAGE + (s % kStages) * B_STAGE);
+    else
+      return static_cast<uint32_t>((s % kStages) * STAGE);
+  }
   // every part of slice s into its stage of the LDS ring at lds_smem
   __device__ __forceinline__ void issue(uint32_t lds_smem, int s) const {
+    const int8_t* sa = base_a + static_cast<size_t>(s) * BK;
+    const int8_t* sb = base_b + static_cast<size_t>(s) * stride_b;
 #pragma unroll
     for (int q = 0; q < kXferOps; ++q)
-      lds_dma16(src[q] + static_cast<size_t>(s) * stride[q],
-                __builtin_amdgcn_readfirstlane(
-                    lds_smem + static_cast<uint32_t>((s % kStages) * STAGE) + slot[q]));
+      lds_dma16_split(q < kXferOpsA ? sa : sb, voff[q],
+                      __builtin_amdgcn_readfirstlane(lds_smem + stage_offset(s, q) + slot[q]));
   }
   // The transfer wave's whole k loop, matching a consumer that waits at one
   // barrier after slice 0 has landed and then one per slice kt < KT - 1, by

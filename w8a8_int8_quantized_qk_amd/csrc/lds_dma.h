@@ -21,6 +21,16 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// The same load with its address split into a wave-uniform 64-bit base in
+// scalar registers and this lane's unsigned 32-bit offset: advancing the base
+// is then scalar arithmetic, not a 64-bit vector add per instruction.
+__device__ __forceinline__ void lds_dma16_split(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p)));
