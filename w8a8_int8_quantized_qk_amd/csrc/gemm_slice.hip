@@ -111,20 +111,27 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
   const int wm = (wave % kWaves) / (BN / WTN);
   const int wn = wave % (BN / WTN);
 
-  // epilogue scales: per token, and per channel (FP8) or 1 (group scales
-  // are applied in the main loop); output_scale is multiplied in later
+  // epilogue scales: per token, then per channel (FP8) or 1 (group scales
+  // are applied in the main loop) times output_scale; written to LDS before
+  // the k loop so that no register holds them across it (read after its
+  // barriers)
   static_assert(BM + BN <= kThreads, "one scale per thread");
-  float scale_reg = 1.0f;
-  if (out) {
+  __shared__ float s_scale[BM + BN];
+  if (out && t < BM + BN) {
+    float v = 1.0f;
     if (t < BM) {
-      scale_reg = m0 + t < M ? scale_a[m0 + t] : 0.0f;
-    } else if (!kGrouped && t < BM + BN) {
-      scale_reg = n0 + t - BM < N ? scale_b[n0 + t - BM] : 0.0f;
+      v = m0 + t < M ? scale_a[m0 + t] : 0.0f;
+    } else if (!kGrouped) {
+      v = n0 + t - BM < N ? scale_b[n0 + t - BM] : 0.0f;
     }
+    s_scale[t] = t < BM ? v : v * output_scale;
   }
 
-  auto a_lds = [&](int s) { return smem + (s % kStages) * STAGE; };
-  auto b_lds = [&](int s) { return smem + (s % kStages) * STAGE + A_STAGE; };
+  // the split LDS ring (gemm_tile.h): the three A blocks, then the three
+  // weight blocks, so that one base register reaches a weight fragment in
+  // every stage within a DS instruction's immediate offset
+  auto a_lds = [&](int s) { return smem + (s % kStages) * A_STAGE; };
+  auto b_lds = [&](int s) { return smem + kStages * A_STAGE + (s % kStages) * B_STAGE; };
 
   using RegTile = std::conditional_t<MODE == kBknReg4, KnRegTile<true>,
                                      std::conditional_t<MODE == kBknReg1, KnRegTile<false>, NoRegTile>>;
@@ -139,7 +146,7 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
   constexpr int kOpsA = rowk_ops<BM>();
   constexpr bool kFixedParts = !KTAIL && !kRegB && !XF;
   const uint32_t lds_smem = lds_addr(smem);
-  using Parts = std::conditional_t<kFixedParts, FixedParts<MODE == kBnkDma ? kBnkDma : kBknDma>,
+  using Parts = std::conditional_t<kFixedParts, FixedParts<MODE == kBnkDma ? kBnkDma : kBknDma, true>,
                                    NoParts>;
   Parts parts;
   if constexpr (kFixedParts) {
@@ -161,46 +168,101 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
   // the lane's two 16-byte k chunks of a slice and its fragment row / column
   const int c0 = lane >> 4;
   const int c1 = 4 + (lane >> 4);
-  const int a_row = wm * WTM + (lane & 15);
-  const int b_row = wn * WTN + (lane & 15);
-  auto read_a = [&](const char* As, int i) -> v8i {
-    const v4i lo = *reinterpret_cast<const v4i*>(As + rowk_offset(a_row + i * 16, c0));
-    const v4i hi = *reinterpret_cast<const v4i*>(As + rowk_offset(a_row + i * 16, c1));
-    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  const int i16 = lane & 15;
+  const int a_row = wm * WTM + i16;
+  const int b_row = wn * WTN + i16;
+  // Fragment reads of stage S.  kConstStage: the DMA-mode loop below is
+  // unrolled over the stages and every read is a base register plus a
+  // constant, so the loop issues no address arithmetic (vector-ALU
+  // instructions do not overlap the MFMAs on this chip but add to the
+  // SIMD's time).  The empty asm makes each base opaque, so that the
+  // compiler keeps it in its own register instead of deriving one from
+  // another with offsets past the 16-bit immediate's reach.  With transfer
+  // waves beside them the matrix-core waves have no register to spare for
+  // the bases (the loop then spills), and the register-staged weight's loop
+  // is not unrolled: there the stage is a run-time value and each read's
+  // address is formed from it.
+  constexpr bool kConstStage = !XF && !kRegB;
+  auto opaque = [](uint32_t x) {
+    asm("" : "+v"(x));
+    return x;
   };
-  // Transpose reads of a [k][n] weight: a read covers k rows kr .. kr + 7
-  // (kr = 16 ch + 8 h + (i16 >> 1) for lane i16 of a 16-lane group) of
-  // fragment column block j, and lane i16 receives column i16's eight bytes.
-  // The row swizzle kn_swz(kr) = (i16 >> 1) ^ (ch & 1) is the same for the
-  // lane's chunks c0 and c1 = c0 + 4 and both halves h, so the four reads
-  // of a fragment share one per-lane base and differ by constants
-  // (64 rows for c1, 8 rows for h).
-  int b_tr_base[FN];
-  {
-    const int i16 = lane & 15;
-    const int kr0 = 16 * c0 + (i16 >> 1);
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t b_ring = lds0 + kStages * A_STAGE;
+  // A: chunks c0 and c1 of fragment 0 in stage 0; fragment i at + 2048 i,
+  // stage 1 at + A_STAGE.  Stage 2 lies past the immediate's reach: its
+  // reads add 2 A_STAGE in place (volatile, so that the sum is not hoisted
+  // into two more registers kept over the loop).
+  uint32_t a_base[2] = {0, 0};
+  // [k][n] weight: a transpose read covers k rows kr .. kr + 7 (kr = 16 ch +
+  // 8 h + (i16 >> 1) for lane i16 of a 16-lane group) of fragment column
+  // block j, and lane i16 receives column i16's eight bytes.  The row
+  // swizzle kn_swz(kr) = (i16 >> 1) ^ (ch & 1) is the same for the lane's
+  // chunks c0 and c1 = c0 + 4 and both halves h, so the four reads of a
+  // fragment share one base and differ by 64 rows (c1) and 8 rows (h); the
+  // bases serve all three stages.
+  uint32_t b_base[FN];
+  // [N][K] or register-staged weight: like A, fragment j at + 2048 j
+  uint32_t bk_base[2] = {0, 0};
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      b_tr_base[j] = kn_offset(kr0, (wn * WTN + j * 16) >> 4) + 8 * (i16 & 1);
+  for (int j = 0; j < FN; ++j)
+    b_base[j] = b_ring + kn_offset(16 * c0 + (i16 >> 1), (wn * WTN + j * 16) >> 4) + 8 * (i16 & 1);
+  if constexpr (kConstStage) {
+    a_base[0] = opaque(lds0 + rowk_offset(a_row, c0));
+    a_base[1] = opaque(lds0 + rowk_offset(a_row, c1));
+    if constexpr (MODE == kBknDma) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) b_base[j] = opaque(b_base[j]);
+    } else {
+      bk_base[0] = opaque(b_ring + rowk_offset(b_row, c0));
+      bk_base[1] = opaque(b_ring + rowk_offset(b_row, c1));
+    }
   }
-  auto read_b_tr = [&](const char* Bs, int j, int row_off) -> v2i {
-    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-        (__attribute__((address_space(3))) v2i*)(Bs + b_tr_base[j] + row_off * BN));
+  typedef __attribute__((address_space(3))) const v4i* lds_v4i;
+  auto a_addr = [&](int S, int h, uint32_t off) -> uint32_t {
+    if (S != 2) return a_base[h] + (S == 1 ? A_STAGE : 0) + off;
+    uint32_t r;
+    asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(2 * A_STAGE + off), "v"(a_base[h]));
+    return r;
   };
-  auto read_b_rowk = [&](const char* Bs, int j) -> v8i {
-    const v4i lo = *reinterpret_cast<const v4i*>(Bs + rowk_offset(b_row + j * 16, c0));
-    const v4i hi = *reinterpret_cast<const v4i*>(Bs + rowk_offset(b_row + j * 16, c1));
+  auto read_a = [&](int S, int i) -> v8i {
+    v4i lo, hi;
+    if constexpr (kConstStage) {
+      lo = *reinterpret_cast<lds_v4i>(a_addr(S, 0, 2048 * i));
+      hi = *reinterpret_cast<lds_v4i>(a_addr(S, 1, 2048 * i));
+    } else {
+      const char* As = a_lds(S);
+      lo = *reinterpret_cast<const v4i*>(As + rowk_offset(a_row + i * 16, c0));
+      hi = *reinterpret_cast<const v4i*>(As + rowk_offset(a_row + i * 16, c1));
+    }
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   };
-  auto read_b = [&](const char* Bs, int j) -> v8i {
+  auto read_b_tr = [&](int S, int j, int row_off) -> v2i {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i*)(b_base[j] + S * B_STAGE + row_off * BN));
+  };
+  auto read_b_rowk = [&](int S, int j) -> v8i {
+    v4i lo, hi;
+    if constexpr (kConstStage) {
+      const uint32_t off = S * B_STAGE + 2048 * j;
+      lo = *reinterpret_cast<lds_v4i>(bk_base[0] + off);
+      hi = *reinterpret_cast<lds_v4i>(bk_base[1] + off);
+    } else {
+      const char* Bs = b_lds(S);
+      lo = *reinterpret_cast<const v4i*>(Bs + rowk_offset(b_row + j * 16, c0));
+      hi = *reinterpret_cast<const v4i*>(Bs + rowk_offset(b_row + j * 16, c1));
+    }
+    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  };
+  auto read_b = [&](int S, int j) -> v8i {
     if constexpr (MODE == kBknDma) {
-      const v2i p0 = read_b_tr(Bs, j, 0);
-      const v2i p1 = read_b_tr(Bs, j, 8);
-      const v2i p2 = read_b_tr(Bs, j, 64);
-      const v2i p3 = read_b_tr(Bs, j, 72);
+      const v2i p0 = read_b_tr(S, j, 0);
+      const v2i p1 = read_b_tr(S, j, 8);
+      const v2i p2 = read_b_tr(S, j, 64);
+      const v2i p3 = read_b_tr(S, j, 72);
       return v8i{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
     } else {
-      return read_b_rowk(Bs, j);
+      return read_b_rowk(S, j);
     }
   };
 
@@ -246,7 +308,7 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
   if (XF && wave >= kWaves) {
     // ---------------- transfer wave ----------------
     if constexpr (XF) {
-      XferParts<MODE == kBnkDma ? kBnkDma : kBknDma> xparts;
+      XferParts<MODE == kBnkDma ? kBnkDma : kBknDma, true> xparts;
       xparts.init(a, b, M, N, K, m0, n0, wave - kWaves);
       xparts.run(lds_smem, KT);
     }
@@ -256,9 +318,9 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
     load_scales(0, sc);
     __syncthreads();  // slice 0 in LDS (the transfer waves waited for it)
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fa[i] = read_a(a_lds(0), i);
+    for (int i = 0; i < FM; ++i) fa[i] = read_a(0, i);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) fb[j] = read_b(b_lds(0), j);
+    for (int j = 0; j < FN; ++j) fb[j] = read_b(0, j);
   } else if (KT > 0) {
     fetch(0);
     load_scales(0, sc);
@@ -273,9 +335,9 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
     __syncthreads();
     if (KTAIL && KT == 1) zero_tail(0);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fa[i] = read_a(a_lds(0), i);
+    for (int i = 0; i < FM; ++i) fa[i] = read_a(0, i);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) fb[j] = read_b(b_lds(0), j);
+    for (int j = 0; j < FN; ++j) fb[j] = read_b(0, j);
   }
 
   // ---- one MFMA unit: one fragment pair ----
@@ -354,9 +416,9 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
         __syncthreads();
         if (KTAIL && kt + 1 == KT - 1) zero_tail(kt + 1);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) fa[i] = read_a(a_lds(kt + 1), i);
+        for (int i = 0; i < FM; ++i) fa[i] = read_a((kt + 1) % kStages, i);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) fb[j] = read_b_rowk(b_lds(kt + 1), j);
+        for (int j = 0; j < FN; ++j) fb[j] = read_b_rowk((kt + 1) % kStages, j);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -380,7 +442,9 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
     constexpr int kSplit = kFetchOps / 2;
     static_assert(kFetchOps == 2 * kSplit, "DMA parts split evenly over the two phases");
     static_assert(kPhase0 >= kSplit && kPhase1 >= kFetchOps - kSplit, "one DMA part per unit");
-    for (int kt = 0; kt < KT; ++kt) {
+    // slice kt, in stage S = kt % 3 (a constant in the unrolled loop)
+    auto slice = [&](int S, int kt) __attribute__((always_inline)) {
+      const int SN = (S + 1) % kStages;
       const bool prefetch = kt + 2 < KT;
       auto dma = [&](int part_idx) {
         if (!XF && prefetch) fetch_part(kt + 2, part_idx);
@@ -406,20 +470,18 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
       {
         // after the last slice these reads come from a valid, unused LDS
         // slice and are not used: no branches around LDS reads
-        const char* As = a_lds(kt + 1);
-        const char* Bs = b_lds(kt + 1);
         v8i na2, na3;
 #pragma unroll
         for (int q = 0; q < kPhase1; ++q) {
           unit(kPhase0 + q);
           if (q & 1) {
-            fb[q >> 1] = read_b(Bs, q >> 1);
+            fb[q >> 1] = read_b(SN, q >> 1);
           } else if (q < 4) {
-            fa[q >> 1] = read_a(As, q >> 1);
+            fa[q >> 1] = read_a(SN, q >> 1);
           } else if (q == 4) {
-            na2 = read_a(As, 2);
+            na2 = read_a(SN, 2);
           } else {
-            na3 = read_a(As, 3);
+            na3 = read_a(SN, 3);
           }
           __builtin_amdgcn_sched_barrier(0);
           if (q < kFetchOps - kSplit) dma(kSplit + q);
@@ -434,6 +496,19 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
             for (int h = 0; h < (GPS > 0 ? GPS : 1); ++h) sc[j][h] = scn[j][h];
         }
       }
+    };
+    static_assert(kStages == 3, "three stages");
+    if constexpr (KTAIL || !kConstStage) {
+      for (int kt = 0; kt < KT; ++kt) slice(kt % kStages, kt);
+    } else {
+      int kt = 0;
+      for (; kt + kStages <= KT; kt += kStages) {
+        slice(0, kt);
+        slice(1, kt + 1);
+        slice(2, kt + 2);
+      }
+      if (kt < KT) slice(0, kt);
+      if (kt + 1 < KT) slice(1, kt + 1);
     }
   }
 
@@ -445,12 +520,14 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
   // barrier) and stores whole 128-byte row segments with nontemporal stores.
   constexpr int kStageBytes = WTM * WTN * 4;
   static_assert(WTN == kStageCols, "staging rows are one wave tile wide");
-  static_assert(kWaves * kStageBytes + 4 * (BM + BN) <= kStages * STAGE, "staging fits in LDS");
+  static_assert(kWaves * kStageBytes <= kStages * STAGE, "staging fits in the ring");
   __syncthreads();  // every wave is done with the k slices
-  float* s_sa = reinterpret_cast<float*>(smem + kWaves * kStageBytes);
-  float* s_sb = s_sa + BM;
-  if (out && t < BM + BN) s_sa[t] = t < BM ? scale_reg : scale_reg * output_scale;  // s_sb follows s_sa
+  const float* s_sa = s_scale;
+  const float* s_sb = s_scale + BM;
   int* stage = reinterpret_cast<int*>(smem + (wave % kWaves) * kStageBytes);
+  // the lane index again from the exec mask, so that no register keeps it
+  // over the k loop
+  const int elane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   if (!XF || wave < kWaves) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -458,20 +535,20 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
       for (int j = 0; j < FN; ++j) {
         const v4i bits = {__float_as_int(acc[i][j][0]), __float_as_int(acc[i][j][1]),
                           __float_as_int(acc[i][j][2]), __float_as_int(acc[i][j][3])};
-        stage_fragment(stage, lane, i, j, bits);
+        stage_fragment(stage, elane, i, j, bits);
       }
   }
-  __syncthreads();  // scales visible (each wave reads back only its own staging)
+  __syncthreads();  // each wave reads back only its own staging
   if (XF && wave >= kWaves) return;
 
   const int lrow0 = wm * WTM;
   const int lcol0 = wn * WTN;
-  if (c) store4<WTM, true, true>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, c);
+  if (c) store4<WTM, true, true>(stage, elane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, c);
   if (out) {
     if (out_dtype == QK_BF16)
-      store_bf16<WTM, true>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, out);
+      store_bf16<WTM, true>(stage, elane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, out);
     else
-      store4<WTM, true, false>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, out);
+      store4<WTM, true, false>(stage, elane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, out);
   }
 }
 
@@ -491,7 +568,10 @@ hipError_t launch_mode(const SliceGemmArgs& g, dim3 grid, int tiles_m, int tiles
                     g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k, tiles_m,
                     tiles_n);
   }
-  if (g.k % BK != 0)
+  // whole slices of a DMA'd weight take the fixed transfer parts, whose lane
+  // offsets are 32-bit; the k-tail kernel forms its addresses per slice
+  constexpr bool kDma = MODE == kBnkDma || MODE == kBknDma;
+  if (g.k % BK != 0 || (kDma && !xfer_parts_fit(g.n, g.k)))
     return launch(gemm_slice_kernel<KIND, MODE, true>, grid, dim3(kThreads), 0, stream, g.a, g.b,
                   g.c, g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k,
                   tiles_m, tiles_n);

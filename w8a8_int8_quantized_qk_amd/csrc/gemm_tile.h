@@ -97,13 +97,24 @@ __device__ __forceinline__ void dma_kn(const int8_t* __restrict__ b, char* lds, 
 // adds s times the part's stride (BK bytes along k) and its stage offset.
 // Valid when no clamp changes from slice to slice: K a multiple of BK and a
 // DMA'd weight (MODE kBnkDma or kBknDma).
-template <int MODE>
+//
+// SPLIT false: the interleaved ring (stage s at s * STAGE, the weight block
+// at A_STAGE within it), each source a 64-bit per-lane address.  SPLIT true:
+// the split ring of XferParts below, each source a wave-uniform base in
+// scalar registers (advanced per slice there) plus a fixed 32-bit lane
+// offset (needs xfer_parts_fit; lda and ldb are K).
+template <int MODE, bool SPLIT = false>
 struct FixedParts {
   static constexpr int kOpsA = rowk_ops<BM>();
   static constexpr int kOps = kOpsA + (MODE == kBnkDma ? rowk_ops<BN>() : kn_ops());
-  const int8_t* src[kOps];
+  static constexpr uint32_t kBSlot0 = SPLIT ? 0 : A_STAGE;  // weight block within its stage
+  const int8_t* src[SPLIT ? 1 : kOps];
+  size_t stride[SPLIT ? 1 : kOps];
+  const int8_t* base_a;
+  const int8_t* base_b;
+  size_t stride_b;
+  uint32_t voff[SPLIT ? kOps : 1];
   uint32_t lds[kOps];  // wave-uniform (m0 operand)
-  size_t stride[kOps];
 
   // lda, ldb: the row strides of A and of a [N][K] B when they are a k range
   // of longer rows (else K)
@@ -112,39 +123,61 @@ struct FixedParts {
                                        int ldb = -1) {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
+    const uint32_t la = static_cast<uint32_t>(lda < 0 ? K : lda);
+    const uint32_t lb = static_cast<uint32_t>(ldb < 0 ? K : ldb);
+    if constexpr (SPLIT) {
+      base_a = a + static_cast<size_t>(m0) * la;
+      base_b = MODE == kBknDma ? b + n0 : b + static_cast<size_t>(n0) * lb;
+      stride_b = MODE == kBknDma ? static_cast<size_t>(BK) * N : BK;
+    }
 #pragma unroll
     for (int q = 0; q < kOps; ++q) {
+      uint32_t rel;        // offset from the tile's base (SPLIT)
+      const int8_t* full;  // whole address (interleaved)
       if (q < kOpsA) {
         const int blk = wave * kOpsA + q;
         const int row = blk * 8 + (lane >> 3);
         const int lchunk = (lane & 7) ^ rowk_swz(row);
         const uint32_t gr = static_cast<uint32_t>(min(m0 + row, M - 1));
-        src[q] = a + (gr * static_cast<uint32_t>(lda < 0 ? K : lda) + 16 * lchunk);
+        rel = (gr - m0) * la + 16 * lchunk;
+        full = a + (gr * la + 16 * lchunk);
         lds[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(blk * 1024));
-        stride[q] = BK;
+        if constexpr (!SPLIT) stride[q] = BK;
       } else if constexpr (MODE == kBnkDma) {
         const int blk = wave * rowk_ops<BN>() + (q - kOpsA);
         const int row = blk * 8 + (lane >> 3);
         const int lchunk = (lane & 7) ^ rowk_swz(row);
         const uint32_t gr = static_cast<uint32_t>(min(n0 + row, N - 1));
-        src[q] = b + (gr * static_cast<uint32_t>(ldb < 0 ? K : ldb) + 16 * lchunk);
-        lds[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(A_STAGE + blk * 1024));
-        stride[q] = BK;
+        rel = (gr - n0) * lb + 16 * lchunk;
+        full = b + (gr * lb + 16 * lchunk);
+        lds[q] = __builtin_amdgcn_readfirstlane(kBSlot0 + static_cast<uint32_t>(blk * 1024));
+        if constexpr (!SPLIT) stride[q] = BK;
       } else {
         const int blk = wave * kn_ops() + (q - kOpsA);
         const int k = blk * 8 + (lane >> 3);
         const int lchunk = (lane & 7) ^ kn_swz(k);
         const uint32_t gn = static_cast<uint32_t>(min(n0 + 16 * lchunk, N - 16));
-        src[q] = b + (static_cast<uint32_t>(k) * static_cast<uint32_t>(N) + gn);
-        lds[q] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(A_STAGE + blk * 1024));
-        stride[q] = static_cast<size_t>(BK) * N;
+        rel = static_cast<uint32_t>(k) * static_cast<uint32_t>(N) + (gn - n0);
+        full = b + (static_cast<uint32_t>(k) * static_cast<uint32_t>(N) + gn);
+        lds[q] = __builtin_amdgcn_readfirstlane(kBSlot0 + static_cast<uint32_t>(blk * 1024));
+        if constexpr (!SPLIT) stride[q] = static_cast<size_t>(BK) * N;
       }
+      if constexpr (SPLIT) voff[q] = rel;
+      else src[q] = full;
     }
   }
   // DMA part `part` of slice s into its stage of the LDS ring at lds_smem
   __device__ __forceinline__ void issue(uint32_t lds_smem, int s, int part) const {
-    lds_dma16(src[part] + static_cast<size_t>(s) * stride[part],
-              lds_smem + static_cast<uint32_t>((s % kStages) * STAGE) + lds[part]);
+    if constexpr (SPLIT) {
+      const uint32_t st = static_cast<uint32_t>(
+          part < kOpsA ? (s % kStages) * A_STAGE : kStages * A_STAGE + (s % kStages) * B_STAGE);
+      const int8_t* sbase = part < kOpsA ? base_a + static_cast<size_t>(s) * BK
+                                         : base_b + static_cast<size_t>(s) * stride_b;
+      lds_dma16_split(sbase, voff[part], lds_smem + st + lds[part]);
+    } else {
+      lds_dma16(src[part] + static_cast<size_t>(s) * stride[part],
+                lds_smem + static_cast<uint32_t>((s % kStages) * STAGE) + lds[part]);
+    }
   }
 };
 

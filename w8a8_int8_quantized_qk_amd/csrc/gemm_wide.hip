@@ -82,8 +82,8 @@ __device__ __forceinline__ int kn_offset(int k, int chunk) {
   return k * BN + ((chunk ^ kn_swz(k)) << 4);
 }
 
-// Source address and LDS slot (wave-uniform, for m0) of this thread's
-// transfer `part` of a slice.
+// Source address and LDS slot (wave-uniform, for m0; relative to the stage's
+// block of its operand) of this thread's transfer `part` of a slice.
 // A part: 16 rows x 64 bytes (lane l: row l / 4, LDS chunk l % 4).  [K][N]
 // weight part: 4 k rows x 256 bytes (lane l: k row l / 16, LDS chunk l % 16).
 // Global rows, columns and k are clamped into the operands (the values
@@ -103,7 +103,7 @@ __device__ __forceinline__ void part_source(const int8_t* __restrict__ a,
     const uint32_t gr = static_cast<uint32_t>(min((is_a ? m0 : n0) + row, (is_a ? M : N) - 1));
     const uint32_t gk = static_cast<uint32_t>(min(k0 + 16 * gchunk, K - 16));
     src = (is_a ? a : b) + (gr * static_cast<uint32_t>(is_a ? lda : ldb) + gk);
-    lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>((is_a ? 0 : A_STAGE) + blk * 1024));
+    lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(blk * 1024));
   } else {
     const int blk = wave * kOpsB + (part - kOpsA);
     const int k = blk * 4 + (lane >> 4);
@@ -111,7 +111,7 @@ __device__ __forceinline__ void part_source(const int8_t* __restrict__ a,
     const uint32_t gk = static_cast<uint32_t>(min(k0 + k, K - 1));
     const uint32_t gn = static_cast<uint32_t>(min(n0 + 16 * gchunk, N - 16));
     src = b + (gk * static_cast<uint32_t>(N) + gn);
-    lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(A_STAGE + blk * 1024));
+    lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(blk * 1024));
   }
 }
 
@@ -149,59 +149,95 @@ __device__ __forceinline__ void gemm_wide_tile(
     }
   }
 
-  // transfer sources and LDS slots, formed once: slice s adds s times the
-  // part's k stride (BK bytes along a row, or BK weight rows)
+  // The LDS ring is split: the A blocks of the four stages first (stage s at
+  // s * A_STAGE), then the weight blocks (at kStages * A_STAGE + s * B_STAGE),
+  // so that one base register reaches an operand's block in every stage
+  // within a DS instruction's 16-bit immediate offset.
+  auto stage_a = [](int s) { return static_cast<uint32_t>((s % kStages) * A_STAGE); };
+  auto stage_b = [](int s) {
+    return static_cast<uint32_t>(kStages * A_STAGE + (s % kStages) * B_STAGE);
+  };
+  static_assert((kStages - 1) * A_STAGE + 1024 * (FM - 1) < 65536 &&
+                    (kStages - 1) * B_STAGE + 2048 < 65536 &&
+                    (kStages - 1) * B_STAGE + 1024 * (FN - 1) < 65536,
+                "every stage within the immediate offsets of one base");
+
+  // transfer sources and LDS slots, formed once.  Whole slices (no k tail):
+  // each part is a wave-uniform base (the tile's A rows or weight block at
+  // slice 0, advanced per slice in scalar registers) plus a fixed 32-bit
+  // lane offset (gemm_wide_applies bounds it).  A k tail changes the clamps
+  // in its final slice, so there every slice forms its addresses again.
   const uint32_t lds_smem = lds_addr(smem);
-  const int8_t* src[kOps];
+  const int8_t* const base_a = a + static_cast<size_t>(m0) * K;
+  const int8_t* const base_b = MODE == tile::kBknDma ? b + n0 : b + static_cast<size_t>(n0) * K;
+  const size_t stride_b = MODE == tile::kBknDma ? static_cast<size_t>(BK) * N : BK;
+  uint32_t voff[kOps];
   uint32_t slot[kOps];
 #pragma unroll
-  for (int q = 0; q < kOps; ++q)
-    part_source<MODE>(a, b, M, N, K, m0, n0, 0, K, K, q, src[q], slot[q]);
-  auto kstride = [&](int q) -> size_t {
-    return (q < kOpsA || MODE == tile::kBnkDma) ? static_cast<size_t>(BK)
-                                                : static_cast<size_t>(BK) * N;
-  };
+  for (int q = 0; q < kOps; ++q) {
+    const int8_t* src;
+    part_source<MODE>(a, b, M, N, K, m0, n0, 0, K, K, q, src, slot[q]);
+    voff[q] = static_cast<uint32_t>(src - (q < kOpsA ? base_a : base_b));
+  }
   auto issue = [&](int s, int q) {
+    const uint32_t lds = lds_smem + (q < kOpsA ? stage_a(s) : stage_b(s));
     if constexpr (KTAIL) {
-      // the clamps change in the final slice: form the address again
       const int8_t* p;
       uint32_t l;
       part_source<MODE>(a, b, M, N, K, m0, n0, s * BK, K, K, q, p, l);
-      lds_dma16(p, lds_smem + static_cast<uint32_t>((s % kStages) * STAGE) + l);
+      lds_dma16(p, lds + l);
     } else {
-      lds_dma16(src[q] + static_cast<size_t>(s) * kstride(q),
-                lds_smem + static_cast<uint32_t>((s % kStages) * STAGE) + slot[q]);
+      const int8_t* sbase = q < kOpsA ? base_a + static_cast<size_t>(s) * BK
+                                      : base_b + static_cast<size_t>(s) * stride_b;
+      lds_dma16_split(sbase, voff[q], lds + slot[q]);
     }
   };
-  auto a_lds = [&](int s) -> const char* { return smem + (s % kStages) * STAGE; };
-  auto b_lds = [&](int s) -> const char* { return smem + (s % kStages) * STAGE + A_STAGE; };
 
   // Fragments of v_mfma_i32_16x16x64_i8: lane l holds 16 k-consecutive bytes,
   // k = 16 (l / 16) .. + 15 of the slice, of row l % 16 (A) or column l % 16
-  // (B) of the fragment.
+  // (B) of the fragment.  Every read is a base register plus a constant (the
+  // stage is a template constant below): A fragment i at + 1024 i; the [K][N]
+  // weight's column block j from its own base (kn_swz of k rows 16 (l / 16) +
+  // (l % 16) / 2 + 8 h does not depend on h, so half h is at + 8 rows); the
+  // [N][K] weight's fragment j at + 1024 j.  The empty asm makes each base
+  // opaque, so that the compiler keeps it in its own register instead of
+  // deriving one from another with offsets past the immediate's reach.
+  auto opaque = [](uint32_t x) {
+    asm("" : "+v"(x));
+    return x;
+  };
   const int kchunk = lane >> 4;
-  const int a_row = wm * WTM + (lane & 15);
-  const int b_row = wn * WTN + (lane & 15);
-  auto read_a = [&](const char* As, int i) -> v4i {
-    return *reinterpret_cast<const v4i*>(As + rowk_offset(a_row + i * 16, kchunk));
+  const int i16 = lane & 15;
+  const uint32_t a_base = opaque(lds_smem + rowk_offset(wm * WTM + i16, kchunk));
+  uint32_t b_base[FN];
+  uint32_t bk_base = 0;
+  if constexpr (MODE == tile::kBknDma) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      b_base[j] = opaque(lds_smem + kStages * A_STAGE +
+                         kn_offset(16 * kchunk + (i16 >> 1), wn * (WTN / 16) + j) + 8 * (i16 & 1));
+  } else {
+    bk_base = opaque(lds_smem + kStages * A_STAGE + rowk_offset(wn * WTN + i16, kchunk));
+  }
+  typedef __attribute__((address_space(3))) const v4i* lds_v4i;
+  // stage S of the ring (a constant wherever the loop below is unrolled)
+  auto read_a = [&](int S, int i) -> v4i {
+    return *reinterpret_cast<lds_v4i>(a_base + S * A_STAGE + 1024 * i);
   };
-  auto read_b_tr = [&](const char* Bs, int j, int h) -> v2i {
-    const int i16 = lane & 15;
-    const int kr = 16 * (lane >> 4) + (i16 >> 1) + 8 * h;
-    const int cb = wn * (WTN / 16) + j;
+  auto read_b_tr = [&](int S, int j, int h) -> v2i {
     return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-        (__attribute__((address_space(3))) v2i*)(Bs + kn_offset(kr, cb) + 8 * (i16 & 1)));
+        (__attribute__((address_space(3))) v2i*)(b_base[j] + S * B_STAGE + BN * 8 * h));
   };
-  auto read_b_rowk = [&](const char* Bs, int j) -> v4i {
-    return *reinterpret_cast<const v4i*>(Bs + rowk_offset(b_row + j * 16, kchunk));
+  auto read_b_rowk = [&](int S, int j) -> v4i {
+    return *reinterpret_cast<lds_v4i>(bk_base + S * B_STAGE + 1024 * j);
   };
-  auto read_b = [&](const char* Bs, int j) -> v4i {
+  auto read_b = [&](int S, int j) -> v4i {
     if constexpr (MODE == tile::kBknDma) {
-      const v2i lo = read_b_tr(Bs, j, 0);
-      const v2i hi = read_b_tr(Bs, j, 1);
+      const v2i lo = read_b_tr(S, j, 0);
+      const v2i hi = read_b_tr(S, j, 1);
       return v4i{lo.x, lo.y, hi.x, hi.y};
     } else {
-      return read_b_rowk(Bs, j);
+      return read_b_rowk(S, j);
     }
   };
 
@@ -215,7 +251,7 @@ __device__ __forceinline__ void gemm_wide_tile(
 
   // zero the A chunks of the final slice that lie at k >= K, then publish
   auto zero_tail = [&](int s) {
-    char* Az = smem + (s % kStages) * STAGE;
+    char* Az = smem + stage_a(s);
     // 256 rows x 4 chunks = 1024 chunks, two per thread
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -240,9 +276,9 @@ __device__ __forceinline__ void gemm_wide_tile(
     __syncthreads();
     if (KTAIL && KT == 1) zero_tail(0);
 #pragma unroll
-    for (int i = 0; i < FM / 2; ++i) fa[i] = read_a(a_lds(0), i);
+    for (int i = 0; i < FM / 2; ++i) fa[i] = read_a(0, i);
 #pragma unroll
-    for (int j = 0; j < FN / 2; ++j) fb[j] = read_b(b_lds(0), j);
+    for (int j = 0; j < FN / 2; ++j) fb[j] = read_b(0, j);
   }
 
   // An execution barrier without a memory fence: the waits it needs are
@@ -256,10 +292,11 @@ __device__ __forceinline__ void gemm_wide_tile(
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // One slice per iteration in two phases, every instruction's place pinned
-  // by sched_barrier, each fragment read several MFMAs before its first use:
+  // One slice (in stage S = kt % 4) in two phases, every instruction's place
+  // pinned by sched_barrier, each fragment read several MFMAs before its
+  // first use:
   //   phase 0: MFMAs of A 0..3 x B 0..1 (fragments read in the previous
-  //            iteration), interleaved with the reads of this slice's A 4..7,
+  //            slice), interleaved with the reads of this slice's A 4..7,
   //            then B 2..3;
   //   barrier: slice kt + 1 has landed (this wave's transfers by vmcnt, every
   //            wave's by s_barrier).  Every wave has also consumed slice
@@ -271,7 +308,8 @@ __device__ __forceinline__ void gemm_wide_tile(
   //            A 4..7 x B 2..3, with the four transfers of slice kt + 3
   //            spread between.
   static_assert(FM == 8 && FN == 4, "interleave pattern below");
-  for (int kt = 0; kt < KT; ++kt) {
+  auto slice = [&](int S, int kt) __attribute__((always_inline)) {
+    const int SN = (S + 1) % kStages;
     const bool prefetch = kt + 3 < KT;
     auto mfma = [&](int i, int j) {
       acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
@@ -283,34 +321,32 @@ __device__ __forceinline__ void gemm_wide_tile(
     };
     // ---- phase 0 ----
     {
-      const char* As = a_lds(kt);
-      const char* Bs = b_lds(kt);
       mfma(0, 0);
-      fa[4] = read_a(As, 4);
+      fa[4] = read_a(S, 4);
       mfma(0, 1);
-      fa[5] = read_a(As, 5);
+      fa[5] = read_a(S, 5);
       mfma(1, 0);
-      fa[6] = read_a(As, 6);
+      fa[6] = read_a(S, 6);
       mfma(1, 1);
-      fa[7] = read_a(As, 7);
+      fa[7] = read_a(S, 7);
       if constexpr (MODE == tile::kBknDma) {
         v2i lo[2], hi[2];
         mfma(2, 0);
-        lo[0] = read_b_tr(Bs, 2, 0);
+        lo[0] = read_b_tr(S, 2, 0);
         mfma(2, 1);
-        hi[0] = read_b_tr(Bs, 2, 1);
+        hi[0] = read_b_tr(S, 2, 1);
         mfma(3, 0);
-        lo[1] = read_b_tr(Bs, 3, 0);
+        lo[1] = read_b_tr(S, 3, 0);
         mfma(3, 1);
-        hi[1] = read_b_tr(Bs, 3, 1);
+        hi[1] = read_b_tr(S, 3, 1);
         fb[2] = v4i{lo[0].x, lo[0].y, hi[0].x, hi[0].y};
         fb[3] = v4i{lo[1].x, lo[1].y, hi[1].x, hi[1].y};
       } else {
         mfma(2, 0);
-        fb[2] = read_b_rowk(Bs, 2);
+        fb[2] = read_b_rowk(S, 2);
         mfma(2, 1);
         mfma(3, 0);
-        fb[3] = read_b_rowk(Bs, 3);
+        fb[3] = read_b_rowk(S, 3);
         mfma(3, 1);
       }
     }
@@ -325,8 +361,6 @@ __device__ __forceinline__ void gemm_wide_tile(
     {
       // after the last slice these reads come from a valid, unused stage and
       // are not used: no branches around LDS reads
-      const char* As = a_lds(kt + 1);
-      const char* Bs = b_lds(kt + 1);
       v4i na[4], nb[2];
       mfma(4, 0);
       mfma(5, 0);
@@ -335,41 +369,41 @@ __device__ __forceinline__ void gemm_wide_tile(
       mfma(7, 0);
       if constexpr (MODE == tile::kBknDma) {
         v2i lo[2], hi[2];
-        lo[0] = read_b_tr(Bs, 0, 0);
+        lo[0] = read_b_tr(SN, 0, 0);
         mfma(4, 1);
-        hi[0] = read_b_tr(Bs, 0, 1);
+        hi[0] = read_b_tr(SN, 0, 1);
         mfma(5, 1);
         dma(1);
         mfma(6, 1);
         mfma(7, 1);
-        lo[1] = read_b_tr(Bs, 1, 0);
+        lo[1] = read_b_tr(SN, 1, 0);
         mfma(0, 2);
-        hi[1] = read_b_tr(Bs, 1, 1);
+        hi[1] = read_b_tr(SN, 1, 1);
         nb[0] = v4i{lo[0].x, lo[0].y, hi[0].x, hi[0].y};
         nb[1] = v4i{lo[1].x, lo[1].y, hi[1].x, hi[1].y};
       } else {
-        nb[0] = read_b_rowk(Bs, 0);
+        nb[0] = read_b_rowk(SN, 0);
         mfma(4, 1);
         mfma(5, 1);
         dma(1);
         mfma(6, 1);
         mfma(7, 1);
-        nb[1] = read_b_rowk(Bs, 1);
+        nb[1] = read_b_rowk(SN, 1);
         mfma(0, 2);
       }
       mfma(0, 3);
-      na[0] = read_a(As, 0);
+      na[0] = read_a(SN, 0);
       mfma(1, 2);
       dma(2);
       mfma(1, 3);
-      na[1] = read_a(As, 1);
+      na[1] = read_a(SN, 1);
       mfma(2, 2);
       mfma(2, 3);
-      na[2] = read_a(As, 2);
+      na[2] = read_a(SN, 2);
       mfma(3, 2);
       dma(3);
       mfma(3, 3);
-      na[3] = read_a(As, 3);
+      na[3] = read_a(SN, 3);
       mfma(4, 2);
       mfma(4, 3);
       mfma(5, 2);
@@ -383,6 +417,22 @@ __device__ __forceinline__ void gemm_wide_tile(
       fb[0] = nb[0];
       fb[1] = nb[1];
     }
+  };
+  static_assert(kStages == 4, "four stages");
+  if constexpr (KTAIL) {
+    for (int kt = 0; kt < KT; ++kt) slice(kt % kStages, kt);
+  } else {
+    // unrolled over the four stages, so that each slice's stage is a constant
+    int kt = 0;
+    for (; kt + kStages <= KT; kt += kStages) {
+      slice(0, kt);
+      slice(1, kt + 1);
+      slice(2, kt + 2);
+      slice(3, kt + 3);
+    }
+    if (kt < KT) slice(0, kt);
+    if (kt + 1 < KT) slice(1, kt + 1);
+    if (kt + 2 < KT) slice(2, kt + 2);
   }
 
   // ---- epilogue ----
@@ -482,7 +532,9 @@ hipError_t launch_wide_mode(const GemmArgs& g, dim3 grid, int tiles_m, int tiles
 }  // namespace
 
 bool gemm_wide_applies(int m, int n, int k, int b_layout) {
-  if (k <= 0 || n < 16) return false;
+  // k, n <= 2^24: the transfers' 32-bit lane offsets (256 rows of k bytes,
+  // 64 k rows of n bytes) fit
+  if (k <= 0 || n < 16 || k > (1 << 24) || n > (1 << 24)) return false;
   if (b_layout == QK_B_KN && n % 16 != 0) return false;  // DMA of [k][n] rows in 16-byte chunks
   const long long tiles = static_cast<long long>((m + wide::BM - 1) / wide::BM) *
                           ((n + wide::BN - 1) / wide::BN);
