@@ -33,7 +33,7 @@
 //     each starts from zero (two groups per slice).  The INT32 partial of a
 //     group is exact and below 2^24 in magnitude, so its conversion to
 //     binary32 is exact; it is added into the binary32 accumulator with one
-//     fused multiply-add by the group's scale, issued one MFMA unit later so
+//     fused multiply-add by the group's scale, issued two MFMA units later so
 //     the conversion does not wait for the matrix core.  A lane's four
 //     accumulator registers share one column, so a lane needs one scale per
 //     fragment column and group; the next slice's scales are loaded during
@@ -45,6 +45,11 @@
 //     DMA parts of slice kt + 2 in between, then the barrier, then 8, each
 //     followed by the read of one of slice kt + 1's fragments into registers
 //     already done with, and the remaining DMA parts.
+//   * The LDS ring is split (the three A blocks, then the three weight
+//     blocks) and, without transfer waves, the loop is unrolled over the
+//     stages so that every fragment read is a base register plus a constant:
+//     vector-ALU instructions do not overlap the MFMAs on this chip but add
+//     to the SIMD's time, and the conversions are the only ones left.
 //   * Bytes past K in the final slice are zeroed in LDS for A; the weight
 //     rows or chunks read past K meet those zeros.  A NaN code in an FP8
 //     weight there would still poison the sum, as it would inside K.
@@ -189,11 +194,10 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
   };
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t b_ring = lds0 + kStages * A_STAGE;
-  // A: chunks c0 and c1 of fragment 0 in stage 0; fragment i at + 2048 i,
-  // stage 1 at + A_STAGE.  Stage 2 lies past the immediate's reach: its
-  // reads add 2 A_STAGE in place (volatile, so that the sum is not hoisted
-  // into two more registers kept over the loop).
-  uint32_t a_base[2] = {0, 0};
+  // A: chunks c0 and c1 of fragment 0; fragment i at + 2048 i.  Set 0
+  // serves stages 0 and 1 (stage 1 at + A_STAGE), set 1 stage 2, which lies
+  // past the immediate's reach from set 0.
+  uint32_t a_base[2][2] = {{0, 0}, {0, 0}};
   // [k][n] weight: a transpose read covers k rows kr .. kr + 7 (kr = 16 ch +
   // 8 h + (i16 >> 1) for lane i16 of a 16-lane group) of fragment column
   // block j, and lane i16 receives column i16's eight bytes.  The row
@@ -208,8 +212,11 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
   for (int j = 0; j < FN; ++j)
     b_base[j] = b_ring + kn_offset(16 * c0 + (i16 >> 1), (wn * WTN + j * 16) >> 4) + 8 * (i16 & 1);
   if constexpr (kConstStage) {
-    a_base[0] = opaque(lds0 + rowk_offset(a_row, c0));
-    a_base[1] = opaque(lds0 + rowk_offset(a_row, c1));
+#pragma unroll
+    for (int set = 0; set < 2; ++set) {
+      a_base[set][0] = opaque(lds0 + set * 2 * A_STAGE + rowk_offset(a_row, c0));
+      a_base[set][1] = opaque(lds0 + set * 2 * A_STAGE + rowk_offset(a_row, c1));
+    }
     if constexpr (MODE == kBknDma) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) b_base[j] = opaque(b_base[j]);
@@ -220,10 +227,7 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
   }
   typedef __attribute__((address_space(3))) const v4i* lds_v4i;
   auto a_addr = [&](int S, int h, uint32_t off) -> uint32_t {
-    if (S != 2) return a_base[h] + (S == 1 ? A_STAGE : 0) + off;
-    uint32_t r;
-    asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(2 * A_STAGE + off), "v"(a_base[h]));
-    return r;
+    return a_base[S / 2][h] + (S == 1 ? A_STAGE : 0) + off;
   };
   auto read_a = [&](int S, int i) -> v8i {
     v4i lo, hi;
@@ -349,7 +353,10 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
   constexpr int kUnits = FM * FN;
   static_assert(FM == 4 && FN == 4, "unit order below");
   constexpr int kPartsPerUnit = GPS == 2 ? 2 : 1;
-  v4i part[kPartsPerUnit], prev[kPartsPerUnit];
+  // a unit's partials are scaled kLag units after its MFMAs, by when the
+  // matrix core has written them (no wait states before the conversions)
+  constexpr int kLag = 2;
+  v4i pend[kLag][kPartsPerUnit];  // unit u's partials in pend[u % kLag]
   auto unit_pair = [](int u, int& i, int& j) {
     if (u < 8) {
       i = u / FN;
@@ -362,6 +369,7 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
   auto unit_mfma = [&](int u) {
     int i, j;
     unit_pair(u, i, j);
+    [[maybe_unused]] v4i(&part)[kPartsPerUnit] = pend[u % kLag];
     if constexpr (KIND == kFp8) {
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
     } else if constexpr (KIND == kI8Group128) {
@@ -374,29 +382,30 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
       part[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(hi_half(fa[i]), hi_half(fb[j]), zero, 0, 0, 0);
     }
   };
-  // add the partials of unit u (held in prev[]) with the scales `s`
+  // add the partials of unit u (held in pend[u % kLag]) with the scales `s`
   auto unit_scale = [&](int u, const float (&s)[FN][GPS > 0 ? GPS : 1]) {
     if constexpr (kGrouped) {
       int i, j;
       unit_pair(u, i, j);
 #pragma unroll
-      for (int h = 0; h < kPartsPerUnit; ++h) add_scaled(acc[i][j], prev[h], s[j][h]);
+      for (int h = 0; h < kPartsPerUnit; ++h) add_scaled(acc[i][j], pend[u % kLag][h], s[j][h]);
     }
   };
-  // MFMAs of unit u, then the scaling of unit u - 1 (whose results have had
-  // a unit's time to arrive); unit 0 scales nothing, the slice's last unit
-  // is scaled after the loop over units
+  // the scaling of unit u - kLag, then the MFMAs of unit u into the
+  // partials it freed; the slice's last kLag units are scaled after the
+  // loop over units
   auto unit = [&](int u) {
-    unit_mfma(u);
     if constexpr (kGrouped) {
-      if (u > 0) unit_scale(u - 1, sc);
-#pragma unroll
-      for (int h = 0; h < kPartsPerUnit; ++h) prev[h] = part[h];
+      if (u >= kLag) unit_scale(u - kLag, sc);
     }
+    unit_mfma(u);
     __builtin_amdgcn_sched_barrier(0);
   };
   auto slice_end = [&]() {
-    if constexpr (kGrouped) unit_scale(kUnits - 1, sc);
+    if constexpr (kGrouped) {
+#pragma unroll
+      for (int d = kLag; d >= 1; --d) unit_scale(kUnits - d, sc);
+    }
   };
 
   if constexpr (kRegB) {
