@@ -53,8 +53,10 @@ GROUPED_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_grouped128_prefill_outli
 MOE_KERNEL = "gemm_i8_wide_moe_kernel"
 MOE_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_wide_moe_up_traffic.txt"),
                [os.path.join(CSRC, f) for f in ("gemm_wide.hip", "gemm_tile.h", "lds_dma.h")])
-ASYM_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_asym_prefill_outliers_traffic.txt"),
-                [os.path.join(CSRC, f) for f in ("gemm_mfma.hip", "gemm_tile.h", "lds_dma.h")])
+# the zero-point GEMM at the prefill shape takes the kernel with transfer waves too
+ASYM_KERNEL = "gemm_i8_spec_asym_kernel"
+ASYM_TRAFFIC = (os.path.join(ROOT, "profiles", "gemm_spec_asym_prefill_outliers_traffic.txt"),
+                [os.path.join(CSRC, f) for f in ("gemm_spec.hip", "gemm_tile.h", "lds_dma.h")])
 STATIC_TRAFFIC = (os.path.join(ROOT, "profiles", "quant_static_prefill_outliers_traffic.txt"),
                   [os.path.join(CSRC, f) for f in ("quant_static.hip", "quant_math.h")])
 GEMV_M8_TRAFFIC = (os.path.join(ROOT, "profiles", "gemv_mfma_decode_m8_traffic.txt"),
@@ -493,7 +495,7 @@ def main():
             "asym_quant": {"us": round(aq_ms * 1e3, 3), "unit": "GB/s",
                            "value": round((qbytes + 8 * m) / (aq_ms * 1e-3) / 1e9, 1)},
             "asym_gemm": {"us": round(ag_ms * 1e3, 3), "unit": "TOPS", "value": round(agt, 2),
-                          "roofline": {"bound": "mfma", "kernel": "gemm_i8_asym_kernel",
+                          "roofline": {"bound": "mfma", "kernel": ASYM_KERNEL,
                                        "achieved": round(agt, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                                        "frac": round(agt / INT8_PEAK_TOPS, 4),
                                        "traffic": _traffic_from_profile(ASYM_TRAFFIC),

@@ -128,6 +128,8 @@ def test_weight_colsum_unaligned(offset):
 @pytest.mark.parametrize("m,n,k,layout", [
     (1, 128, 128, "kn"), (7, 200, 272, "kn"), (300, 130, 400, "kn"), (257, 384, 1040, "kn"),
     (513, 257, 4096, "nk"), (2048, 256, 4096, "kn"), (4, 128, 65520, "kn"),
+    # the kernel with transfer waves (k % 128 == 0): ragged rows and columns
+    (300, 272, 1152, "kn"), (129, 144, 384, "nk"),
 ])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_asym_gemm(m, n, k, layout, out_dtype):

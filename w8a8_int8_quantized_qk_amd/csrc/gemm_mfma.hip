@@ -566,6 +566,8 @@ hipError_t launch_gemm_asym(const GemmArgs& g, const int32_t* zp_a, const int32_
   const long long tiles = static_cast<long long>(tiles_m) * tiles_n;
   if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(tiles));
+  // the kernel with transfer waves apart where it applies (as for the plain GEMM)
+  if (gemm_spec_applies(g.m, g.n, g.k, g.b_layout)) return launch_gemm_spec_asym(g, zp_a, wsum, stream);
   if (g.b_layout == QK_B_NK) return launch_asym_mode<kBnkDma>(g, zp_a, wsum, grid, tiles_m, tiles_n, stream);
   if (g.n % 16 == 0) return launch_asym_mode<kBknDma>(g, zp_a, wsum, grid, tiles_m, tiles_n, stream);
   if (g.n % 4 == 0) return launch_asym_mode<kBknReg4>(g, zp_a, wsum, grid, tiles_m, tiles_n, stream);

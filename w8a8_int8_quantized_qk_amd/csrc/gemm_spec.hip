@@ -64,11 +64,16 @@ constexpr int FN = WTN / 16;
 static_assert((BM / WTM) * (BN / WTN) == kMma, "one sub-tile per matrix-core wave");
 static_assert(kXfer == kXferWaves, "the transfer waves of gemm_tile.h");
 
-template <int MODE>
+// ASYM: the activations carry per-row zero points zp_a, and the epilogue
+// subtracts zp_a[row] * wsum[col] (wsum: the weight's column sums) from the
+// INT32 accumulators before storing or scaling them ("KV-cache kernels", 02
+// Scales and dequantization: asymmetric codes with a zero point).
+template <int MODE, bool ASYM>
 __device__ __forceinline__ void gemm_spec_tile(
     const int8_t* __restrict__ a, const int8_t* __restrict__ b, int32_t* __restrict__ c,
     const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
-    void* __restrict__ out, int out_dtype, int M, int N, int K, int tm, int tn) {
+    void* __restrict__ out, int out_dtype, int M, int N, int K, int tm, int tn,
+    const int32_t* __restrict__ zp_a, const int32_t* __restrict__ wsum) {
   static_assert(MODE == kBnkDma || MODE == kBknDma, "DMA weight layouts");
   constexpr int kStageBytes = WTM * WTN * 4;  // one matrix-core wave's staged block (16 KiB)
   static_assert(kMma * kStageBytes <= kStages * STAGE, "epilogue staging fits in the ring");
@@ -76,6 +81,8 @@ __device__ __forceinline__ void gemm_spec_tile(
   // per-token scales, then per-channel ones times output_scale; written
   // before the k loop so that no register holds them across it
   __shared__ float s_scale[BM + BN];
+  // row zero points, then column sums (ASYM)
+  __shared__ int s_corr[ASYM ? BM + BN : 1];
 
   const int m0 = tm * BM;
   const int n0 = tn * BN;
@@ -92,6 +99,17 @@ __device__ __forceinline__ void gemm_spec_tile(
       v = scale_b[n0 + t - BM] * output_scale;
     }
     s_scale[t] = v;  // read after the barriers below
+  }
+  if constexpr (ASYM) {
+    if (t < BM + BN) {
+      int z = 0;
+      if (t < BM) {
+        if (m0 + t < M) z = zp_a[m0 + t];
+      } else if (n0 + t - BM < N) {
+        z = wsum[n0 + t - BM];
+      }
+      s_corr[t] = z;
+    }
   }
 
   const int KT = K / BK;  // K % BK == 0
@@ -258,12 +276,18 @@ __device__ __forceinline__ void gemm_spec_tile(
     const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     const int lrow0 = wm * WTM;
     const int lcol0 = wn * WTN;
-    if (c) store4<64, false, true>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, c);
+    const int* s_zp = s_corr;
+    const int* s_ws = s_corr + BM;
+    if (c)
+      store4<64, false, true, ASYM>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, c, s_zp,
+                                    s_ws);
     if (out) {
       if (out_dtype == QK_BF16)
-        store_bf16<64, false>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, out);
+        store_bf16<64, false, ASYM>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, out, s_zp,
+                                    s_ws);
       else
-        store4<64, false, false>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, out);
+        store4<64, false, false, ASYM>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, out,
+                                       s_zp, s_ws);
     }
   }
 }
@@ -275,7 +299,22 @@ __global__ __launch_bounds__(kSpecThreads, 1) void gemm_i8_spec_kernel(
     void* __restrict__ out, int out_dtype, int M, int N, int K, int tiles_m, int tiles_n) {
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
-  gemm_spec_tile<MODE>(a, b, c, scale_a, scale_b, output_scale, out, out_dtype, M, N, K, tm, tn);
+  gemm_spec_tile<MODE, false>(a, b, c, scale_a, scale_b, output_scale, out, out_dtype, M, N, K,
+                              tm, tn, nullptr, nullptr);
+}
+
+// Asymmetric activations: the result is sum_t (a[i][t] - zp_a[i]) * B(t, j)
+// = acc - zp_a[i] * wsum[j].
+template <int MODE>
+__global__ __launch_bounds__(kSpecThreads, 1) void gemm_i8_spec_asym_kernel(
+    const int8_t* __restrict__ a, const int8_t* __restrict__ b, int32_t* __restrict__ c,
+    const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
+    void* __restrict__ out, int out_dtype, int M, int N, int K, int tiles_m, int tiles_n,
+    const int32_t* __restrict__ zp_a, const int32_t* __restrict__ wsum) {
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  gemm_spec_tile<MODE, true>(a, b, c, scale_a, scale_b, output_scale, out, out_dtype, M, N, K, tm,
+                             tn, zp_a, wsum);
 }
 
 }  // namespace spec
@@ -285,6 +324,22 @@ bool gemm_spec_applies(int m, int n, int k, int b_layout) {
   if (k <= 0 || k % tile::BK != 0 || n < 16 || !tile::xfer_parts_fit(n, k)) return false;
   if (b_layout == QK_B_KN && n % 16 != 0) return false;  // DMA of [k][n] rows in 16-byte chunks
   return true;
+}
+
+hipError_t launch_gemm_spec_asym(const GemmArgs& g, const int32_t* zp_a, const int32_t* wsum,
+                                 hipStream_t stream) {
+  const int tiles_m = (g.m + tile::BM - 1) / tile::BM;
+  const int tiles_n = (g.n + tile::BN - 1) / tile::BN;
+  const long long tiles = static_cast<long long>(tiles_m) * tiles_n;
+  if (tiles > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(tiles));
+  if (g.b_layout == QK_B_NK)
+    return launch(spec::gemm_i8_spec_asym_kernel<tile::kBnkDma>, grid, dim3(spec::kSpecThreads), 0,
+                  stream, g.a, g.b, g.c, g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype,
+                  g.m, g.n, g.k, tiles_m, tiles_n, zp_a, wsum);
+  return launch(spec::gemm_i8_spec_asym_kernel<tile::kBknDma>, grid, dim3(spec::kSpecThreads), 0,
+                stream, g.a, g.b, g.c, g.scale_a, g.scale_b, g.output_scale, g.out, g.out_dtype,
+                g.m, g.n, g.k, tiles_m, tiles_n, zp_a, wsum);
 }
 
 hipError_t launch_gemm_spec(const GemmArgs& g, hipStream_t stream) {

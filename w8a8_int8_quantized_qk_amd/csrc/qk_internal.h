@@ -99,6 +99,8 @@ hipError_t launch_gemm_wide_moe(const GemmArgs& g, const int* offsets, int exper
 // multiple of 128, a DMA'd weight layout.
 bool gemm_spec_applies(int m, int n, int k, int b_layout);
 hipError_t launch_gemm_spec(const GemmArgs& g, hipStream_t stream);
+hipError_t launch_gemm_spec_asym(const GemmArgs& g, const int32_t* zp_a, const int32_t* wsum,
+                                 hipStream_t stream);
 // The same kernel over experts (gemm_mfma.hip): rows [offsets[e],
 // offsets[e + 1]) of a (device array of experts + 1 ints) use weight
 // b + e * k * n and per-channel scales scale_b + e * n; one launch.
