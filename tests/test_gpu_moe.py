@@ -60,12 +60,15 @@ def test_moe_against_per_expert_oracle(counts, k, n, layout, out_dtype):
 # groups whose dense GEMM of all rows has at least one 256 x 256 tile per CU
 # take the 256 x 256 tile kernel: empty and one-row experts, ragged rows and
 # columns, k tails past a 64-byte slice (k % 64 != 0), both layouts, all rows
-# in one expert
+# in one expert.  An expert's last row block of at most 128 rows is a light
+# tile (rows 128 and 128 + 256 light, 129 full, at the boundary).
 @pytest.mark.parametrize("counts,k,n,layout", [
     ([0, 1500, 1, 257, 2338], 256, 4096, "kn"),
     ([700, 0, 1300, 2100], 208, 4112, "nk"),
     ([4096], 128, 4096, "kn"),
     ([1000, 999, 1001, 1096], 320, 4096, "nk"),
+    ([128, 384, 129, 3455], 192, 4096, "kn"),
+    ([128, 384, 129, 3455], 208, 4096, "nk"),
 ])
 def test_moe_wide_tiles_against_per_expert_oracle(counts, k, n, layout):
     m = sum(counts)

@@ -40,6 +40,11 @@
 //   * Rows past M or N re-read a valid row (never stored); a k tail (K not a
 //     multiple of 64) has its A chunks at k >= K zeroed in LDS before use.
 //   * XCD-aware tile order as in the 256 x 128 kernel.
+//   * MoE: an expert's last row block of at most 128 rows is a light tile:
+//     every wave multiplies a 64 x 64 block of the first 128 rows (half the
+//     MFMAs) and only those A rows are transferred (three 1-KiB parts per
+//     wave and slice instead of four).  The loop is paced by its transfers,
+//     so the light tile costs about three quarters of a full one.
 //   * Epilogue: each wave stages its 128 x 64 block in two 64-row halves
 //     row-major in LDS and stores whole 128-byte row segments with the
 //     shared store helpers (scales in binary32, bf16 rounded to nearest even).
@@ -92,12 +97,12 @@ template <int MODE>
 __device__ __forceinline__ void part_source(const int8_t* __restrict__ a,
                                             const int8_t* __restrict__ b, int M, int N, int K,
                                             int m0, int n0, int k0, int lda, int ldb, int part,
-                                            const int8_t*& src, uint32_t& lds) {
+                                            const int8_t*& src, uint32_t& lds, int a_blk = -1) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   if (part < kOpsA || MODE == tile::kBnkDma) {
     const bool is_a = part < kOpsA;
-    const int blk = wave * kOpsA + (is_a ? part : part - kOpsA);
+    const int blk = is_a && a_blk >= 0 ? a_blk : wave * kOpsA + (is_a ? part : part - kOpsA);
     const int row = blk * 16 + (lane >> 2);
     const int gchunk = (lane & 3) ^ ((row >> 2) & 3);
     const uint32_t gr = static_cast<uint32_t>(min((is_a ? m0 : n0) + row, (is_a ? M : N) - 1));
@@ -115,12 +120,16 @@ __device__ __forceinline__ void part_source(const int8_t* __restrict__ a,
   }
 }
 
-// One workgroup's 256 x 256 output tile (tm, tn).
+// One workgroup's 256 x 256 output tile (tm, tn).  light: the tile has at
+// most 128 rows below M (an expert's last row block in the MoE launch); its
+// eight waves then each multiply a 64 x 64 block of the first 128 rows, half
+// the MFMAs of a full tile.
 template <int MODE, bool KTAIL>
 __device__ __forceinline__ void gemm_wide_tile(
     const int8_t* __restrict__ a, const int8_t* __restrict__ b, int32_t* __restrict__ c,
     const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
-    void* __restrict__ out, int out_dtype, int M, int N, int K, int tm, int tn) {
+    void* __restrict__ out, int out_dtype, int M, int N, int K, int tm, int tn,
+    bool light = false) {
   static_assert(MODE == tile::kBnkDma || MODE == tile::kBknDma, "DMA weight layouts");
   constexpr int kStageRows = 64;                         // rows per epilogue pass
   constexpr int kStageBytes = kStageRows * WTN * 4;      // 16 KiB per wave
@@ -190,6 +199,30 @@ __device__ __forceinline__ void gemm_wide_tile(
       const int8_t* sbase = q < kOpsA ? base_a + static_cast<size_t>(s) * BK
                                       : base_b + static_cast<size_t>(s) * stride_b;
       lds_dma16_split(sbase, voff[q], lds + slot[q]);
+    }
+  };
+  // A light tile needs only A rows 0 .. 127: its transfers per slice are one
+  // A part per wave (rows 16 w .. 16 w + 15) and the wave's two weight parts
+  constexpr int kOpsLight = 1 + kOpsB;
+  uint32_t voff_la = 0, slot_la = 0;
+  {
+    const int8_t* src;
+    part_source<MODE>(a, b, M, N, K, m0, n0, 0, K, K, 0, src, slot_la, wave);
+    voff_la = static_cast<uint32_t>(src - base_a);
+  }
+  auto issue_light = [&](int s, int p) {
+    if (p > 0) {
+      issue(s, kOpsA + p - 1);
+      return;
+    }
+    const uint32_t lds = lds_smem + stage_a(s);
+    if constexpr (KTAIL) {
+      const int8_t* src;
+      uint32_t l;
+      part_source<MODE>(a, b, M, N, K, m0, n0, s * BK, K, K, 0, src, l, wave);
+      lds_dma16(src, lds + l);
+    } else {
+      lds_dma16_split(base_a + static_cast<size_t>(s) * BK, voff_la, lds + slot_la);
     }
   };
 
@@ -266,19 +299,30 @@ __device__ __forceinline__ void gemm_wide_tile(
 
   v4i fa[FM], fb[FN];
   if (KT > 0) {
+    if (light) {
 #pragma unroll
-    for (int s = 0; s < 3; ++s)
-      if (s < KT)
+      for (int s = 0; s < 3; ++s)
+        if (s < KT)
 #pragma unroll
-        for (int q = 0; q < kOps; ++q) issue(s, q);
-    // slice 0 landed: at most the later prologue slices are outstanding
-    if (KT > 2) wait_vmcnt<2 * kOps>(); else if (KT > 1) wait_vmcnt<kOps>(); else wait_vmcnt<0>();
+          for (int p = 0; p < kOpsLight; ++p) issue_light(s, p);
+      if (KT > 2) wait_vmcnt<2 * kOpsLight>(); else if (KT > 1) wait_vmcnt<kOpsLight>(); else wait_vmcnt<0>();
+    } else {
+#pragma unroll
+      for (int s = 0; s < 3; ++s)
+        if (s < KT)
+#pragma unroll
+          for (int q = 0; q < kOps; ++q) issue(s, q);
+      // slice 0 landed: at most the later prologue slices are outstanding
+      if (KT > 2) wait_vmcnt<2 * kOps>(); else if (KT > 1) wait_vmcnt<kOps>(); else wait_vmcnt<0>();
+    }
     __syncthreads();
     if (KTAIL && KT == 1) zero_tail(0);
+    if (!light) {
 #pragma unroll
-    for (int i = 0; i < FM / 2; ++i) fa[i] = read_a(0, i);
+      for (int i = 0; i < FM / 2; ++i) fa[i] = read_a(0, i);
 #pragma unroll
-    for (int j = 0; j < FN / 2; ++j) fb[j] = read_b(0, j);
+      for (int j = 0; j < FN / 2; ++j) fb[j] = read_b(0, j);
+    }
   }
 
   // An execution barrier without a memory fence: the waits it needs are
@@ -418,8 +462,82 @@ __device__ __forceinline__ void gemm_wide_tile(
       fb[1] = nb[1];
     }
   };
+  // A light tile: wave w multiplies rows 64 (w / 4) .. + 63 of the tile by
+  // its 64 columns, 16 MFMAs per slice from 4 A and 4 B fragments.  At the
+  // top of slice kt the wave holds kt's fragments (xa, xb); after the barrier
+  // for slice kt + 1 (every wave has also consumed slice kt - 1, whose stage
+  // slice kt + 3 then takes) it reads kt + 1's into (ya, yb) between the
+  // MFMAs, with the three transfers of slice kt + 3.
+  const uint32_t la_base = opaque(lds_smem + rowk_offset(wm * 64 + i16, kchunk));
+  auto lread_a = [&](int S, int i) -> v4i {
+    return *reinterpret_cast<lds_v4i>(la_base + S * A_STAGE + 1024 * i);
+  };
+  v4i xa[4], xb[FN], ya[4], yb[FN];
+  auto lslice = [&](int S, int kt) __attribute__((always_inline)) {
+    const int SN = (S + 1) % kStages;
+    const bool prefetch = kt + 3 < KT;
+    if (kt + 1 < KT) {
+      if (kt + 2 < KT) wait_vmcnt<kOpsLight>(); else wait_vmcnt<0>();
+      barrier();
+      if (KTAIL && kt + 1 == KT - 1) zero_tail(kt + 1);
+    }
+    v2i lo[FN], hi[FN];
+#pragma unroll
+    for (int n = 0; n < 4 * FN; ++n) {
+      const int i = n / FN;
+      const int j = n % FN;
+      acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa[i], xb[j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // after the last slice these reads come from a valid, unused stage
+      if (n < 4) {
+        ya[n] = lread_a(SN, n);
+      } else if (n < 4 + 2 * FN) {
+        const int r = n - 4;
+        if constexpr (MODE == tile::kBknDma) {
+          if (r & 1) hi[r >> 1] = read_b_tr(SN, r >> 1, 1);
+          else lo[r >> 1] = read_b_tr(SN, r >> 1, 0);
+        } else if ((r & 1) == 0) {
+          yb[r >> 1] = read_b_rowk(SN, r >> 1);
+        }
+      }
+      if ((n & 3) == 3 && (n >> 2) < kOpsLight) {
+        if (prefetch) issue_light(kt + 3, n >> 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (MODE == tile::kBknDma) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) yb[j] = v4i{lo[j].x, lo[j].y, hi[j].x, hi[j].y};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xa[i] = ya[i];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) xb[j] = yb[j];
+  };
+
   static_assert(kStages == 4, "four stages");
-  if constexpr (KTAIL) {
+  if (light) {
+    if (KT > 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xa[i] = lread_a(0, i);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) xb[j] = read_b(0, j);
+    }
+    if constexpr (KTAIL) {
+      for (int kt = 0; kt < KT; ++kt) lslice(kt % kStages, kt);
+    } else {
+      int kt = 0;
+      for (; kt + kStages <= KT; kt += kStages) {
+        lslice(0, kt);
+        lslice(1, kt + 1);
+        lslice(2, kt + 2);
+        lslice(3, kt + 3);
+      }
+      if (kt < KT) lslice(0, kt);
+      if (kt + 1 < KT) lslice(1, kt + 1);
+      if (kt + 2 < KT) lslice(2, kt + 2);
+    }
+  } else if constexpr (KTAIL) {
     for (int kt = 0; kt < KT; ++kt) slice(kt % kStages, kt);
   } else {
     // unrolled over the four stages, so that each slice's stage is a constant
@@ -446,6 +564,8 @@ __device__ __forceinline__ void gemm_wide_tile(
   int* stage = reinterpret_cast<int*>(smem + wave * kStageBytes);
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
+    // a light tile's wave holds one 64-row block (rows 64 wm .. + 63)
+    if (half == 1 && light) break;
     if (half == 1) __syncthreads();  // the first half's rows are read back by now
     constexpr int kHalfFrags = kStageRows / 16;
 #pragma unroll
@@ -454,7 +574,7 @@ __device__ __forceinline__ void gemm_wide_tile(
       for (int j = 0; j < FN; ++j)
         tile::stage_fragment(stage, lane, ii, j, acc[half * kHalfFrags + ii][j]);
     __syncthreads();  // staged blocks and scales visible
-    const int lrow0 = wm * WTM + half * kStageRows;
+    const int lrow0 = light ? wm * kStageRows : wm * WTM + half * kStageRows;
     const int lcol0 = wn * WTN;
     if (c)
       tile::store4<kStageRows, false, true>(stage, lane, m0, n0, lrow0, lcol0, M, N, s_sa, s_sb, c);
@@ -495,12 +615,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_wide_moe_kernel(
     return;
   int tm, tn;
   tile::group_order(local, (Me + BM - 1) / BM, tiles_n, tm, tn);
+  // an expert's last row block of at most 128 rows: a light tile
+  const bool light = Me - tm * BM <= BM / 2;
   const size_t row_off = static_cast<size_t>(r0);
   void* out_e = out ? static_cast<char*>(out) + row_off * N * (out_dtype == QK_BF16 ? 2 : 4) : nullptr;
   gemm_wide_tile<MODE, KTAIL>(a + row_off * K, b + e * expert_stride, c ? c + row_off * N : nullptr,
                               scale_a ? scale_a + row_off : nullptr,
                               scale_b ? scale_b + static_cast<size_t>(e) * N : nullptr,
-                              output_scale, out_e, out_dtype, Me, N, K, tm, tn);
+                              output_scale, out_e, out_dtype, Me, N, K, tm, tn, light);
 }
 
 template <int MODE>
