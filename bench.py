@@ -391,7 +391,7 @@ def main():
             "ms_per_step": round(fstep_ms, 5),
             "step": "qk_quant_per_token_fp8 + qk_gemm_fp8_scaled, replayed from HIP graphs",
             "quant_kernel_us": round(fquant_ms * 1e3, 3),
-            "roofline": {"bound": "mfma", "kernel": "gemm_fp8_mfma_kernel",
+            "roofline": {"bound": "mfma", "kernel": "gemm_slice_kernel (FP8)",
                          "achieved": round(ftf, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(ftf / FP8_PEAK_TFLOPS, 4),
                          "traffic": _traffic_from_profile(FP8_TRAFFIC),

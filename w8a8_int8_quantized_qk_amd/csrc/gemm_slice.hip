@@ -46,8 +46,8 @@
 //     followed by the read of one of slice kt + 1's fragments into registers
 //     already done with, and the remaining DMA parts.
 //   * The LDS ring is split (the three A blocks, then the three weight
-//     blocks) and, without transfer waves, the loop is unrolled over the
-//     stages so that every fragment read is a base register plus a constant:
+//     blocks) and the loop is unrolled over the stages so that every
+//     fragment read is a base register plus a constant:
 //     vector-ALU instructions do not overlap the MFMAs on this chip but add
 //     to the SIMD's time, and the conversions are the only ones left.
 //   * Bytes past K in the final slice are zeroed in LDS for A; the weight
@@ -89,17 +89,11 @@ __device__ __forceinline__ void add_scaled(v4f& acc, const v4i& p, float s) {
   asm volatile("" : "+v"(acc));
 }
 
-// XF: four more waves (kXferWaves, gemm_tile.h) issue every global-to-LDS
-// transfer, so that the eight matrix-core waves issue none (K % BK == 0, a
-// DMA'd weight; a wave held up issuing transfers cannot issue MFMAs).  Three
-// waves per SIMD then share its registers.
-template <int KIND, int MODE, bool KTAIL, bool XF = false>
-__global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void gemm_slice_kernel(
+template <int KIND, int MODE, bool KTAIL>
+__global__ __launch_bounds__(kThreads, 1) void gemm_slice_kernel(
     const int8_t* __restrict__ a, const int8_t* __restrict__ b, float* __restrict__ c,
     const float* __restrict__ scale_a, const float* __restrict__ scale_b, float output_scale,
     void* __restrict__ out, int out_dtype, int M, int N, int K, int tiles_m, int tiles_n) {
-  static_assert(!XF || (!KTAIL && (MODE == kBnkDma || MODE == kBknDma)),
-                "transfer waves: whole slices of a DMA'd weight");
   constexpr bool kRegB = MODE == kBknReg4 || MODE == kBknReg1;
   constexpr int GPS = groups_per_slice<KIND>();
   constexpr bool kGrouped = GPS > 0;
@@ -111,9 +105,8 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
   const int n0 = tn * BN;
   const int t = threadIdx.x;
   const int lane = t & 63;
-  // wave-uniform for the compiler too, so that the two kinds branch
-  const int wave = XF ? __builtin_amdgcn_readfirstlane(t >> 6) : t >> 6;
-  const int wm = (wave % kWaves) / (BN / WTN);
+  const int wave = t >> 6;
+  const int wm = wave / (BN / WTN);
   const int wn = wave % (BN / WTN);
 
   // epilogue scales: per token, then per channel (FP8) or 1 (group scales
@@ -149,7 +142,7 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
   };
   constexpr int kFetchOps = BM * BK / 1024 / kWaves + (kRegB ? 0 : BN * BK / 1024 / kWaves);
   constexpr int kOpsA = rowk_ops<BM>();
-  constexpr bool kFixedParts = !KTAIL && !kRegB && !XF;
+  constexpr bool kFixedParts = !KTAIL && !kRegB;
   const uint32_t lds_smem = lds_addr(smem);
   using Parts = std::conditional_t<kFixedParts, FixedParts<MODE == kBnkDma ? kBnkDma : kBknDma, true>,
                                    NoParts>;
@@ -182,12 +175,10 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
   // instructions do not overlap the MFMAs on this chip but add to the
   // SIMD's time).  The empty asm makes each base opaque, so that the
   // compiler keeps it in its own register instead of deriving one from
-  // another with offsets past the 16-bit immediate's reach.  With transfer
-  // waves beside them the matrix-core waves have no register to spare for
-  // the bases (the loop then spills), and the register-staged weight's loop
-  // is not unrolled: there the stage is a run-time value and each read's
-  // address is formed from it.
-  constexpr bool kConstStage = !XF && !kRegB;
+  // another with offsets past the 16-bit immediate's reach.  The
+  // register-staged weight's loop is not unrolled: there the stage is a
+  // run-time value and each read's address is formed from it.
+  constexpr bool kConstStage = !kRegB;
   auto opaque = [](uint32_t x) {
     asm("" : "+v"(x));
     return x;
@@ -309,23 +300,8 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
     __syncthreads();
   };
 
-  if (XF && wave >= kWaves) {
-    // ---------------- transfer wave ----------------
-    if constexpr (XF) {
-      XferParts<MODE == kBnkDma ? kBnkDma : kBknDma, true> xparts;
-      xparts.init(a, b, M, N, K, m0, n0, wave - kWaves);
-      xparts.run(lds_smem, KT);
-    }
-  } else {
   v8i fa[FM], fb[FN];  // fragments of the slice being multiplied
-  if (KT > 0 && XF) {
-    load_scales(0, sc);
-    __syncthreads();  // slice 0 in LDS (the transfer waves waited for it)
-#pragma unroll
-    for (int i = 0; i < FM; ++i) fa[i] = read_a(0, i);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) fb[j] = read_b(0, j);
-  } else if (KT > 0) {
+  if (KT > 0) {
     fetch(0);
     load_scales(0, sc);
     if constexpr (kRegB) breg.load(b, N, K, n0, 0);
@@ -456,7 +432,7 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
       const int SN = (S + 1) % kStages;
       const bool prefetch = kt + 2 < KT;
       auto dma = [&](int part_idx) {
-        if (!XF && prefetch) fetch_part(kt + 2, part_idx);
+        if (prefetch) fetch_part(kt + 2, part_idx);
         __builtin_amdgcn_sched_barrier(0);
       };
       // ---- phase 0 ----
@@ -469,9 +445,7 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
       }
       // ---- barrier for slice kt + 1 ----
       if (kt + 1 < KT) {
-        if constexpr (!XF) {
-          if (prefetch) wait_vmcnt<kSplit>(); else wait_vmcnt<0>();
-        }
+        if (prefetch) wait_vmcnt<kSplit>(); else wait_vmcnt<0>();
         __syncthreads();
         if (KTAIL && kt + 1 == KT - 1) zero_tail(kt + 1);
       }
@@ -521,10 +495,8 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
     }
   }
 
-  }  // matrix-core waves
-
   // ---- epilogue ----
-  // Each matrix-core wave holds the final sums of its 64 x 64 sub-tile; it
+  // Each wave holds the final sums of its 64 x 64 sub-tile; it
   // stages them row-major in LDS (the operand slices are free after the
   // barrier) and stores whole 128-byte row segments with nontemporal stores.
   constexpr int kStageBytes = WTM * WTN * 4;
@@ -533,11 +505,11 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
   __syncthreads();  // every wave is done with the k slices
   const float* s_sa = s_scale;
   const float* s_sb = s_scale + BM;
-  int* stage = reinterpret_cast<int*>(smem + (wave % kWaves) * kStageBytes);
+  int* stage = reinterpret_cast<int*>(smem + wave * kStageBytes);
   // the lane index again from the exec mask, so that no register keeps it
   // over the k loop
   const int elane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  if (!XF || wave < kWaves) {
+  {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -548,7 +520,6 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
       }
   }
   __syncthreads();  // each wave reads back only its own staging
-  if (XF && wave >= kWaves) return;
 
   const int lrow0 = wm * WTM;
   const int lcol0 = wn * WTN;
@@ -564,19 +535,6 @@ __global__ __launch_bounds__(XF ? kThreads + 64 * kXferWaves : kThreads, 1) void
 template <int KIND, int MODE>
 hipError_t launch_mode(const SliceGemmArgs& g, dim3 grid, int tiles_m, int tiles_n,
                        hipStream_t stream) {
-  // FP8 with whole slices of a DMA'd weight: transfer waves of their own
-  // (measured 35.3 -> 33.6 us at 2048 x 4096 x 4096).  The group-scale kinds
-  // keep eight waves: with three waves per SIMD their binary32 accumulators,
-  // partials and scales exceed the 168 registers each wave then has, and
-  // the spills made them slower (G = 128: 56.9 -> 74.6 us).
-  if constexpr ((MODE == kBnkDma || MODE == kBknDma) && KIND == kFp8) {
-    // k = 0 has no slice to transfer: the kernel below
-    if (g.k > 0 && g.k % BK == 0 && xfer_parts_fit(g.n, g.k))
-      return launch(gemm_slice_kernel<KIND, MODE, false, true>, grid,
-                    dim3(kThreads + 64 * kXferWaves), 0, stream, g.a, g.b, g.c, g.scale_a,
-                    g.scale_b, g.output_scale, g.out, g.out_dtype, g.m, g.n, g.k, tiles_m,
-                    tiles_n);
-  }
   // whole slices of a DMA'd weight take the fixed transfer parts, whose lane
   // offsets are 32-bit; the k-tail kernel forms its addresses per slice
   constexpr bool kDma = MODE == kBnkDma || MODE == kBknDma;
