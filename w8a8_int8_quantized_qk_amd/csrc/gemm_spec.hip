@@ -120,7 +120,7 @@ __device__ __forceinline__ void gemm_spec_tile(
 
   if (wave >= kMma) {
     // ---------------- transfer wave ----------------
-    XferParts<MODE, true> parts;
+    XferParts<MODE> parts;
     parts.init(a, b, M, N, K, m0, n0, wave - kMma);
     parts.run(lds_addr(smem), KT);
   } else {

@@ -197,16 +197,13 @@ __host__ __device__ constexpr bool xfer_parts_fit(int n, int k) {
 constexpr int kXferWaves = 4;
 constexpr int kXferOps = (BM + BN) * BK / 1024 / kXferWaves;  // 12
 constexpr int kXferOpsA = BM * BK / 1024 / kXferWaves;        // 8
-//
-// Two layouts of the LDS ring: interleaved (SPLIT false), stage s at
-// s * STAGE holding the A block and then the weight block at A_STAGE; split
-// (SPLIT true), the A blocks of the stages at s * A_STAGE and the weight
-// blocks after all of them, at kStages * A_STAGE + s * B_STAGE, so that the
-// three weight stages lie within one 64 KiB reach of a DS immediate offset.
-template <int MODE, bool SPLIT = false>
+// The parts fill the split LDS ring: the A blocks of the stages at
+// s * A_STAGE and the weight blocks after all of them, at kStages * A_STAGE +
+// s * B_STAGE, so that the three weight stages lie within one 64 KiB reach
+// of a DS immediate offset.
+template <int MODE>
 struct XferParts {
   static_assert(MODE == kBnkDma || MODE == kBknDma, "DMA weight layouts");
-  static constexpr uint32_t kBSlot0 = SPLIT ? 0 : A_STAGE;  // weight block within its stage
   // A part's source is a wave-uniform base (the tile's A rows or weight
   // block at slice 0, advanced per slice in scalar registers) plus this
   // lane's 32-bit offset, which stays fixed over the k loop; xfer_parts_fit
@@ -240,24 +237,21 @@ struct XferParts {
         const int lchunk = (lane & 7) ^ rowk_swz(row);
         voff[q] = static_cast<uint32_t>(min(n0 + row, N - 1) - n0) * static_cast<uint32_t>(K) +
                   16 * lchunk;
-        slot[q] = kBSlot0 + static_cast<uint32_t>(blk * 1024);
+        slot[q] = static_cast<uint32_t>(blk * 1024);
       } else {  // [K][N] weight block: 8 k rows of 128 bytes (n0 <= N - 16)
         const int blk = (kXferOps - kXferOpsA) * d + (q - kXferOpsA);
         const int k = blk * 8 + (lane >> 3);
         const int lchunk = (lane & 7) ^ kn_swz(k);
         voff[q] = static_cast<uint32_t>(k) * static_cast<uint32_t>(N) +
                   static_cast<uint32_t>(min(n0 + 16 * lchunk, N - 16) - n0);
-        slot[q] = kBSlot0 + static_cast<uint32_t>(blk * 1024);
+        slot[q] = static_cast<uint32_t>(blk * 1024);
       }
     }
   }
   // offset of part q's stage of slice s in the ring
   __device__ __forceinline__ static uint32_t stage_offset(int s, int q) {
-    if constexpr (SPLIT)
-      return static_cast<uint32_t>(q < kXferOpsA ? (s % kStages) * A_STAGE
-                                                 : kStages * A_STAGE + (s % kStages) * B_STAGE);
-    else
-      return static_cast<uint32_t>((s % kStages) * STAGE);
+    return static_cast<uint32_t>(q < kXferOpsA ? (s % kStages) * A_STAGE
+                                               : kStages * A_STAGE + (s % kStages) * B_STAGE);
   }
   // every part of slice s into its stage of the LDS ring at lds_smem
   __device__ __forceinline__ void issue(uint32_t lds_smem, int s) const {
