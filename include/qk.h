@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QK_ABI_VERSION 6
+#define QK_ABI_VERSION 7
 
 /* element types */
 #define QK_F32 0
@@ -124,6 +124,19 @@ int qk_quant_per_token(int m, int k, const void *x, int x_dtype, int8_t *q, floa
  */
 int qk_silu_mul_quant_per_token(int m, int d, const void *h, int h_dtype, int8_t *q,
                                 float *scale, hipStream_t stream);
+
+/*
+ * silu(gate) * up alone, in binary32, with exactly the arithmetic of
+ * qk_silu_mul_quant_per_token before its quantization ("kernels: fused
+ * silu_and_mul + dynamic per-token FP8 quantization", Purpose: the
+ * silu_and_mul activation):
+ *   out[i][j] = (g / (1 + exp(-g))) * u,  g = h[i][j], u = h[i][d + j]
+ *   h    [m][2d] of h_dtype (QK_F32, QK_BF16 or QK_F16), gate | up.
+ *   out  [m][d] float, written.
+ * Any alignment.  Errors: m or d negative, NULL pointer with m*d > 0, unknown
+ * dtype (QK_ERR_INVALID_VALUE); 2d above INT_MAX (QK_ERR_UNSUPPORTED).
+ */
+int qk_silu_mul(int m, int d, const void *h, int h_dtype, float *out, hipStream_t stream);
 
 /* Bytes of workspace qk_gemm_i8_scaled / qk_linear_w8a8 need for this shape
  * (0 if none).  The decode kernel (m <= 16) keeps one 64-bit word per output

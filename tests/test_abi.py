@@ -130,6 +130,13 @@ def test_quant_argument_errors_are_reported_before_launch(lib):
     assert lib.qk_quant_per_token(0, 4, NULL, 0, NULL, NULL, NULL) == 0
     assert lib.qk_silu_mul_quant_per_token(4, 4, FAKE, 3, FAKE, FAKE, NULL) == INVALID
     assert lib.qk_silu_mul_quant_per_token(0, 4, NULL, 1, NULL, NULL, NULL) == 0
+    assert lib.qk_silu_mul(-1, 4, FAKE, 1, FAKE, NULL) == INVALID
+    assert lib.qk_silu_mul(4, 4, FAKE, 3, FAKE, NULL) == INVALID
+    assert lib.qk_silu_mul(4, 4, NULL, 1, FAKE, NULL) == INVALID
+    assert lib.qk_silu_mul(4, 4, FAKE, 1, NULL, NULL) == INVALID
+    assert lib.qk_silu_mul(0, 4, NULL, 1, NULL, NULL) == 0
+    assert lib.qk_silu_mul(4, 0, NULL, 1, NULL, NULL) == 0
+    assert lib.qk_silu_mul(4, 0x40000000, FAKE, 1, FAKE, NULL) == c["QK_ERR_UNSUPPORTED"]
 
 
 def _linear(lib, m, n, k, x=FAKE, xdt=1, b=FAKE, sb=FAKE, out=FAKE, odt=1, layout=0, q=NULL,

@@ -24,7 +24,7 @@ import threading
 
 import torch
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 F32, BF16, F16 = 0, 1, 2
 B_KN, B_NK = 0, 1
 KERNEL_AUTO, KERNEL_MFMA, KERNEL_GEMV = 0, 1, 2
@@ -41,7 +41,7 @@ _KERNELS = {"auto": KERNEL_AUTO, "mfma": KERNEL_MFMA, "gemv": KERNEL_GEMV}
 
 EXPORTED = (
     "qk_abi_version", "qk_status_string", "qk_build_info", "qk_quant_per_token",
-    "qk_silu_mul_quant_per_token", "qk_gemm_workspace_size", "qk_workspace_init",
+    "qk_silu_mul_quant_per_token", "qk_silu_mul", "qk_gemm_workspace_size", "qk_workspace_init",
     "qk_gemm_i8_scaled",
     "qk_gemm_i8_scaled_ex", "qk_linear_w8a8", "qk_linear_w8a8_noalloc", "qk_quant_per_token_fp8",
     "qk_silu_mul_quant_per_token_fp8", "qk_gemm_fp8_scaled", "qk_linear_fp8",
@@ -75,6 +75,8 @@ def _declare(lib):
     lib.qk_quant_per_token.restype = I
     lib.qk_silu_mul_quant_per_token.argtypes = [I, I, P, I, P, P, P]
     lib.qk_silu_mul_quant_per_token.restype = I
+    lib.qk_silu_mul.argtypes = [I, I, P, I, P, P]
+    lib.qk_silu_mul.restype = I
     lib.qk_gemm_workspace_size.argtypes = [I, I, I]
     lib.qk_gemm_workspace_size.restype = ctypes.c_size_t
     lib.qk_workspace_init.argtypes = [P, ctypes.c_size_t, P]
@@ -214,6 +216,25 @@ def silu_mul_quant_per_token(h: torch.Tensor, q: torch.Tensor | None = None,
     _check(library().qk_silu_mul_quant_per_token(m, d, _ptr(h), _IN_DTYPES[h.dtype], _ptr(q),
                                                  _ptr(scale), _stream(h.device)))
     return q, scale
+
+
+def silu_mul(h: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """silu(h[:, :d]) * h[:, d:] in fp32 for h [m, 2d], unquantized (the same
+    arithmetic as the fused quantization)."""
+    _need(h, "h", ndim=2)
+    if h.dtype not in _IN_DTYPES:
+        raise TypeError(f"h dtype {h.dtype} not supported")
+    m, two_d = h.shape
+    if two_d % 2:
+        raise ValueError("h must have an even number of columns (gate | up)")
+    d = two_d // 2
+    out = torch.empty((m, d), dtype=torch.float32, device=h.device) if out is None else out
+    _need(out, "out", torch.float32, 2, h.device)
+    if tuple(out.shape) != (m, d):
+        raise ValueError("out must be [m, d]")
+    _check(library().qk_silu_mul(m, d, _ptr(h), _IN_DTYPES[h.dtype], _ptr(out),
+                                 _stream(h.device)))
+    return out
 
 
 def gemm_workspace_size(m: int, n: int, k: int) -> int:

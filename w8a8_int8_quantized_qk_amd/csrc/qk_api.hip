@@ -252,6 +252,14 @@ int qk_silu_mul_quant_per_token(int m, int d, const void* h, int h_dtype, int8_t
   return status_of(qk::launch_silu_quant_rows(m, d, h, h_dtype, q, scale, stream));
 }
 
+int qk_silu_mul(int m, int d, const void* h, int h_dtype, float* out, hipStream_t stream) {
+  if (m < 0 || d < 0 || !known_input_dtype(h_dtype)) return QK_ERR_INVALID_VALUE;
+  if (m == 0 || d == 0) return QK_OK;  // empty tensors may have NULL data pointers
+  if (!h || !out) return QK_ERR_INVALID_VALUE;
+  if (static_cast<long long>(d) * 2 > 0x7fffffffLL) return QK_ERR_UNSUPPORTED;
+  return status_of(qk::launch_silu_mul(m, d, h, h_dtype, out, stream));
+}
+
 size_t qk_gemm_workspace_size(int m, int n, int k) {
   if (m <= 0 || n <= 0 || k < 0) return 0;
   // the decode kernel's words (m <= 16), and the tiled kernel's split-K

@@ -65,6 +65,9 @@ hipError_t launch_quant_rows(int m, int k, const void* x, int dtype, int8_t* q, 
 // silu(gate) * up then per-token quantization, one workgroup per row (quant.hip).
 hipError_t launch_silu_quant_rows(int m, int d, const void* h, int dtype, int8_t* q,
                                   float* scale, hipStream_t stream);
+// silu(gate) * up in binary32, no quantization (quant.hip).
+hipError_t launch_silu_mul(int m, int d, const void* h, int dtype, float* out,
+                           hipStream_t stream);
 // The same two with float8_e4m3fn codes and the optional scale bound.
 hipError_t launch_quant_rows_fp8(int m, int k, const void* x, int dtype, uint8_t* q, float* scale,
                                  float scale_ub, hipStream_t stream);

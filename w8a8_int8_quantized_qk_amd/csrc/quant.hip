@@ -173,7 +173,7 @@ __device__ __forceinline__ void unit_values(const char* base, int k, int u,
     float up[E::kPerUnit];
     E::unpack(raw_up, up);
 #pragma unroll
-    for (int e = 0; e < E::kPerUnit; ++e) v[e] = silu_times(v[e], up[e]);
+    for (int e = 0; e < E::kPerUnit; ++e) v[e] = silu_times<DT != QK_F32>(v[e], up[e]);
   }
 }
 
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(kBlock) void quant_rows_twopass(const void* __restr
   const size_t first = row * static_cast<size_t>(SILU ? 2 : 1) * k;
   auto value = [&](int j) -> float {
     const float x = E::load(src, first + j);
-    if constexpr (SILU) return silu_times(x, E::load(src, first + k + j));
+    if constexpr (SILU) return silu_times<DT != QK_F32>(x, E::load(src, first + k + j));
     return x;
   };
   Stats st;
@@ -318,6 +318,24 @@ hipError_t dispatch(int m, int k, const void* src, int8_t* q, float* scale, floa
                 scale_ub, zp, k);
 }
 
+// silu(gate) * up in binary32 without quantization, one element per thread
+// and iteration: the activation the fused kernels quantize, with the same
+// arithmetic (silu_times), for callers that want it unquantized.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void silu_mul_kernel(const void* __restrict__ src,
+                                                         float* __restrict__ out,
+                                                         long long total, int d) {
+  using E = Elem<DT>;
+  const long long stride = static_cast<long long>(gridDim.x) * kBlock;
+  for (long long i = static_cast<long long>(blockIdx.x) * kBlock + threadIdx.x; i < total;
+       i += stride) {
+    const long long row = i / d;
+    const long long j = i - row * d;
+    const size_t first = static_cast<size_t>(row) * 2 * d;
+    out[i] = silu_times<DT != QK_F32>(E::load(src, first + j), E::load(src, first + d + j));
+  }
+}
+
 template <bool SILU, int FMT>
 hipError_t dispatch_dtype(int m, int k, const void* src, int dtype, int8_t* q, float* scale,
                           float scale_ub, int32_t* zp, hipStream_t stream) {
@@ -339,6 +357,20 @@ hipError_t launch_quant_rows(int m, int k, const void* x, int dtype, int8_t* q, 
 hipError_t launch_silu_quant_rows(int m, int d, const void* h, int dtype, int8_t* q,
                                   float* scale, hipStream_t stream) {
   return dispatch_dtype<true, kI8>(m, d, h, dtype, q, scale, 0.0f, nullptr, stream);
+}
+
+hipError_t launch_silu_mul(int m, int d, const void* h, int dtype, float* out,
+                           hipStream_t stream) {
+  const long long total = static_cast<long long>(m) * d;
+  if (total == 0) return hipSuccess;
+  const long long want = (total + kBlock - 1) / kBlock;
+  const dim3 grid(static_cast<unsigned>(want < 8192 ? want : 8192));
+  switch (dtype) {
+    case QK_F32: return launch(silu_mul_kernel<QK_F32>, grid, dim3(kBlock), 0, stream, h, out, total, d);
+    case QK_BF16: return launch(silu_mul_kernel<QK_BF16>, grid, dim3(kBlock), 0, stream, h, out, total, d);
+    case QK_F16: return launch(silu_mul_kernel<QK_F16>, grid, dim3(kBlock), 0, stream, h, out, total, d);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_quant_rows_fp8(int m, int k, const void* x, int dtype, uint8_t* q, float* scale,

@@ -120,10 +120,9 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
 // steps (ln 2 split into a 16-bit head and a tail), e^r by the degree-7
 // Taylor polynomial in Horner form (coefficients: the binary32 values nearest
 // 1/j!), then the exact scaling by 2^n.  Inputs above 88 give +inf, below -87
-// give 0, so every finite result is a normal number.
-__device__ __forceinline__ float exp_fixed(float x) {
-  if (x > 88.0f) return __builtin_inff();
-  if (x < -87.0f) return 0.0f;
+// give 0, so every finite result is a normal number.  This function is the
+// part for x in [-87, 88]; silu_times applies the two range rules.
+__device__ __forceinline__ float exp_fixed_in_range(float x) {
   const float n = __builtin_rintf(x * 0x1.715476p+0f);
   float r = __builtin_fmaf(-n, 0x1.62e400p-1f, x);
   r = __builtin_fmaf(-n, 0x1.7f7d1cp-20f, r);
@@ -138,11 +137,42 @@ __device__ __forceinline__ float exp_fixed(float x) {
   return __builtin_amdgcn_ldexpf(p, static_cast<int>(n));
 }
 
-// silu(g) * u = (g / (1 + e^-g)) * u, each operation rounded once.
+// g / t for a denominator t >= 1 (or +inf): the hardware reciprocal with
+// one correction step.  v_div_scale_f32 scales both operands so that the
+// reciprocal and the quotient stay clear of the subnormal range; then
+// r ~ 1 / t, y = g r, the exact residual g - y t, the corrected y + residual
+// * r (rescaled by v_div_fmas_f32), and v_div_fixup_f32 for infinite, zero
+// and NaN operands.  Seven instructions against eleven for the IEEE sequence,
+// which first refines r by a Newton step and corrects twice.  One correction
+// from an unrefined reciprocal is not correctly rounded for every pair of
+// binary32 operands, so this serves only 16-bit gates: there t is a function
+// of g, and every one of the 65536 gates of each 16-bit format is checked
+// against IEEE division on the GPU.
+__device__ __forceinline__ float div_one_correction(float g, float t) {
+  bool den_flag, vcc;
+  const float ds = __builtin_amdgcn_div_scalef(g, t, false, &den_flag);
+  const float ns = __builtin_amdgcn_div_scalef(g, t, true, &vcc);
+  const float r = __builtin_amdgcn_rcpf(ds);
+  const float y = ns * r;
+  const float e = __builtin_fmaf(-ds, y, ns);
+  const float q = __builtin_amdgcn_div_fmasf(e, r, y, vcc);
+  return __builtin_amdgcn_div_fixupf(q, t, g);
+}
+
+// silu(g) * u = (g / (1 + e^-g)) * u, each operation rounded once, e^x as
+// exp_fixed_in_range with its range rules, and without branches: x = -g is
+// clamped to [-87, 88] first, which changes no result (below -87 the rule
+// gives e = 0, the clamped x gives e = e^-87 < 2^-125, and 1 + e rounds to
+// exactly 1 either way), and t = +inf replaces 1 + e where x > 88.  A NaN
+// gate needs neither rule: the quotient propagates it.  kNarrow: the gate
+// came from a 16-bit format (the division as div_one_correction, checked
+// for all such gates); otherwise the IEEE division.
+template <bool kNarrow>
 __device__ __forceinline__ float silu_times(float g, float u) {
-  const float e = exp_fixed(-g);
-  const float t = 1.0f + e;
-  const float sg = g / t;  // IEEE division (correctly rounded build)
+  const float x = __builtin_amdgcn_fmed3f(-g, -87.0f, 88.0f);
+  float t = 1.0f + exp_fixed_in_range(x);
+  t = -g > 88.0f ? __builtin_inff() : t;
+  const float sg = kNarrow ? div_one_correction(g, t) : g / t;  // IEEE division (correctly rounded build)
   return sg * u;
 }
 

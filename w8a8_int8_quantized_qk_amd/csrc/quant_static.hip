@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kBlock) void quant_static_units(const void* __restr
       float up[P];
       E::unpack(make_uint4(rup.x, rup.y, rup.z, rup.w), up);
 #pragma unroll
-      for (int e = 0; e < P; ++e) v[e] = silu_times(v[e], up[e]);
+      for (int e = 0; e < P; ++e) v[e] = silu_times<DT != QK_F32>(v[e], up[e]);
     }
     int8_t* dst = q + row * k + static_cast<long long>(cu) * P;
     if constexpr (P == 8) {
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kBlock) void quant_static_elems(const void* __restr
     const long long j = i - row * k;
     const long long first = row * static_cast<long long>(SILU ? 2 : 1) * k;
     float x = E::load(src, first + j);
-    if constexpr (SILU) x = silu_times(x, E::load(src, first + k + j));
+    if constexpr (SILU) x = silu_times<DT != QK_F32>(x, E::load(src, first + k + j));
     if constexpr (FP8) {
       q[i] = static_cast<int8_t>(
           __builtin_amdgcn_cvt_pk_fp8_f32(qm::fp8_ratio(x, s, r), 0.0f, 0, false) & 0xff);
