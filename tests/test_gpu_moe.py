@@ -69,6 +69,10 @@ def test_moe_against_per_expert_oracle(counts, k, n, layout, out_dtype):
     ([1000, 999, 1001, 1096], 320, 4096, "nk"),
     ([128, 384, 129, 3455], 192, 4096, "kn"),
     ([128, 384, 129, 3455], 208, 4096, "nk"),
+    # many experts, light and full last blocks, empty ones, 17 column tiles
+    # (full and light tile counts not multiples of 8: uneven XCD shares)
+    ([0, 129, 128, 1, 300, 0, 640, 385, 127, 2000, 33, 0, 77, 256, 255, 257], 192, 4112, "kn"),
+    ([0, 129, 128, 1, 300, 0, 640, 385, 127, 2000, 33, 0, 77, 256, 255, 257], 128, 4112, "nk"),
 ])
 def test_moe_wide_tiles_against_per_expert_oracle(counts, k, n, layout):
     m = sum(counts)
