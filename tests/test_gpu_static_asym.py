@@ -74,6 +74,35 @@ def test_static_quant_extreme_scales_and_misaligned_input(fp8):
     _check_static(x, "bf16", np.float32(0.01), fp8, False, x_dev=xd, what="misaligned")
 
 
+def test_static_quant_special_values():
+    # infinities, signed zeros, subnormals and quotients at and next to the
+    # half-integers around the +-127 clamp (the kernel clamps the quotient
+    # before rounding it, the oracle after: the same integer)
+    scale = np.float32(0.03125)
+    halves = np.float32([126.5, 127.0, 127.5, 128.5, 300.0, 0.5, 1.5, 2.5]) * scale
+    vals = np.concatenate([halves, -halves, np.nextafter(halves, np.float32(np.inf)),
+                           np.nextafter(halves, np.float32(0)),
+                           np.float32([np.inf, -np.inf, 0.0, -0.0, 1e-45, -1e-45, 3e38, -3e38])])
+    x = np.resize(vals, (4, 64)).astype(np.float32)
+    for dt in ("f32", "bf16"):
+        for fp8 in (False, True):
+            xt = wl.cast(x, dt)
+            _check_static(xt, dt, scale, fp8, False, what=f"specials {dt} fp8={fp8}")
+
+
+def test_static_quant_prefill_shape_and_grid_loop():
+    # the prefill shape bench.py times, and a tensor one grid pass can not
+    # cover (the kernel loops over units in steps of its whole grid)
+    d = wl.generate("prefill_outliers")
+    amax = float(np.abs(oracle.widen(wl.bits(d["x"]), oracle.BF16)).max())
+    _check_static(d["x"], "bf16", np.float32(amax / 127.0), False, False, what="prefill static")
+    del d
+    rng = np.random.default_rng(_seed("stbig"))
+    block = wl.random_activations(rng, 512, 8192, "bf16", outlier_cols=8)
+    x = torch.from_numpy(np.resize(wl.bits(block), (32769, 8192)).view(np.int16)).view(torch.bfloat16)
+    _check_static(x, "bf16", np.float32(0.05), False, False, what="grid loop")
+
+
 def _check_asym(x_cpu, dtype, what=""):
     q, s, z = qk.quant_per_token_asym(x_cpu.to(DEV))
     q_ref, s_ref, z_ref = oracle.quant_per_token_asym(oracle.widen(wl.bits(x_cpu), DTYPE_CODE[dtype]))

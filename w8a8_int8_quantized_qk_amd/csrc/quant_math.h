@@ -244,6 +244,20 @@ __device__ __forceinline__ int code_of_bounded(float x, float s, float r) {
   return static_cast<int>(q);
 }
 
+// The same code as code_of_bounded, as the low byte of the returned word
+// (packed like code_word_dynamic's): the quotient is clamped to [-127, 127]
+// before it is rounded, which gives the same integer (rint and the clamp
+// commute, the bounds being integers), and the rounding adds 1.5 * 2^23.
+// Six instructions instead of eight plus the packing shifts.
+__device__ __forceinline__ uint32_t code_word_bounded(float x, float s, float r) {
+  float y = x * r;
+  y = __builtin_amdgcn_fmed3f(y, -256.0f, 256.0f);
+  const float e = __builtin_fmaf(-y, s, x);
+  float q = __builtin_fmaf(e, r, y);
+  q = __builtin_amdgcn_fmed3f(q, -127.0f, 127.0f);
+  return __float_as_uint(q + 12582912.0f);
+}
+
 // Asymmetric codes: clamp(rint(x / s) + zp, -128, 127) with the exact
 // quotient (|x / s| <= 255 by construction of s, so no overflow).
 __device__ __forceinline__ int code_of_asym(float x, float s, float r, float zp) {

@@ -32,13 +32,20 @@ __device__ __forceinline__ uint32_t codes4(float a, float b, float c, float d, f
     return qm::pack4_fp8(qm::fp8_ratio(a, s, r), qm::fp8_ratio(b, s, r), qm::fp8_ratio(c, s, r),
                          qm::fp8_ratio(d, s, r));
   } else {
-    return qm::pack4(qm::code_of_bounded(a, s, r), qm::code_of_bounded(b, s, r),
-                     qm::code_of_bounded(c, s, r), qm::code_of_bounded(d, s, r));
+    return qm::pack4_low_bytes(qm::code_word_bounded(a, s, r), qm::code_word_bounded(b, s, r),
+                               qm::code_word_bounded(c, s, r), qm::code_word_bounded(d, s, r));
   }
 }
 
-// One thread per 16-byte unit of P values (rows of k / P units; for SILU the
-// up half of row i starts k elements after its gate half).
+constexpr int kUnitsPerThread = 2;
+
+// 16-byte units of P values (rows of k / P units; for SILU the up half of row
+// i starts k elements after its gate half), kUnitsPerThread per thread and
+// iteration: a wave's loads cover 64 consecutive units each, and all of a
+// thread's loads are issued before any unit is converted, so one round of
+// waves keeps the whole tensor's reads in flight.  Without SILU the units of
+// the input and of the codes are both contiguous (unit u at byte 16 u and at
+// code P u), so no row index is needed.
 template <int DT, bool SILU, bool FP8>
 __global__ __launch_bounds__(kBlock) void quant_static_units(const void* __restrict__ src,
                                                              int8_t* __restrict__ q,
@@ -47,31 +54,49 @@ __global__ __launch_bounds__(kBlock) void quant_static_units(const void* __restr
                                                              int k) {
   using E = Elem<DT>;
   constexpr int P = E::kPerUnit;
+  constexpr int U = kUnitsPerThread;
   const float s = *scale;
   const float r = 1.0f / s;
-  for (long long u = static_cast<long long>(blockIdx.x) * kBlock + threadIdx.x; u < units;
-       u += static_cast<long long>(gridDim.x) * kBlock) {
-    const long long row = u / units_per_row;
-    const int cu = static_cast<int>(u - row * units_per_row);
-    const char* base =
-        static_cast<const char*>(src) + row * static_cast<long long>(SILU ? 2 : 1) * k * E::kBytes;
-    float v[P];
-    const v4u raw = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(base + cu * 16));
-    E::unpack(make_uint4(raw.x, raw.y, raw.z, raw.w), v);
-    if constexpr (SILU) {
-      const v4u rup = __builtin_nontemporal_load(
-          reinterpret_cast<const v4u*>(base + static_cast<long long>(k) * E::kBytes + cu * 16));
-      float up[P];
-      E::unpack(make_uint4(rup.x, rup.y, rup.z, rup.w), up);
+  const char* in = static_cast<const char*>(src);
+  const long long stride = static_cast<long long>(gridDim.x) * kBlock;
+  for (long long u0 = static_cast<long long>(blockIdx.x) * kBlock + threadIdx.x; u0 < units;
+       u0 += U * stride) {
+    v4u raw[U], rup[U];
 #pragma unroll
-      for (int e = 0; e < P; ++e) v[e] = silu_times<DT != QK_F32>(v[e], up[e]);
+    for (int j = 0; j < U; ++j) {
+      const long long u = u0 + j * stride;
+      if (u >= units) continue;
+      long long at = u;  // the unit's index in the input, in units
+      if constexpr (SILU) {
+        const long long row = units <= 0x7fffffffLL
+                                  ? static_cast<long long>(static_cast<uint32_t>(u) /
+                                                           static_cast<uint32_t>(units_per_row))
+                                  : u / units_per_row;
+        at = u + row * units_per_row;
+        rup[j] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4u*>(in + (at + units_per_row) * 16));
+      }
+      raw[j] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(in + at * 16));
     }
-    int8_t* dst = q + row * k + static_cast<long long>(cu) * P;
-    if constexpr (P == 8) {
-      *reinterpret_cast<v2u*>(dst) =
-          v2u{codes4<FP8>(v[0], v[1], v[2], v[3], s, r), codes4<FP8>(v[4], v[5], v[6], v[7], s, r)};
-    } else {
-      *reinterpret_cast<uint32_t*>(dst) = codes4<FP8>(v[0], v[1], v[2], v[3], s, r);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const long long u = u0 + j * stride;
+      if (u >= units) continue;
+      float v[P];
+      E::unpack(make_uint4(raw[j].x, raw[j].y, raw[j].z, raw[j].w), v);
+      if constexpr (SILU) {
+        float up[P];
+        E::unpack(make_uint4(rup[j].x, rup[j].y, rup[j].z, rup[j].w), up);
+#pragma unroll
+        for (int e = 0; e < P; ++e) v[e] = silu_times<DT != QK_F32>(v[e], up[e]);
+      }
+      int8_t* dst = q + u * P;
+      if constexpr (P == 8) {
+        *reinterpret_cast<v2u*>(dst) =
+            v2u{codes4<FP8>(v[0], v[1], v[2], v[3], s, r), codes4<FP8>(v[4], v[5], v[6], v[7], s, r)};
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = codes4<FP8>(v[0], v[1], v[2], v[3], s, r);
+      }
     }
   }
 }
@@ -115,8 +140,9 @@ hipError_t dispatch_static(int m, int k, const void* src, const float* scale, in
   if (aligned) {
     const int upr = k / E::kPerUnit;
     const long long units = static_cast<long long>(m) * upr;
-    return launch(quant_static_units<DT, SILU, FP8>, dim3(grid_for(units)), dim3(kBlock), 0, stream,
-                  src, q, scale, units, upr, k);
+    return launch(quant_static_units<DT, SILU, FP8>,
+                  dim3(grid_for((units + kUnitsPerThread - 1) / kUnitsPerThread)), dim3(kBlock), 0,
+                  stream, src, q, scale, units, upr, k);
   }
   const long long count = static_cast<long long>(m) * k;
   return launch(quant_static_elems<DT, SILU, FP8>, dim3(grid_for(count)), dim3(kBlock), 0, stream,
