@@ -122,11 +122,12 @@ def _traffic_from_profile(which):
     return float(t.group(1))
 
 
-def _sclk_now():
-    """Current shader clock in MHz from the amdgpu driver's sysfs table (the
-    level marked '*'), or None where it cannot be read."""
+def _clock_now(table):
+    """Current clock in MHz from the amdgpu driver's sysfs table `table`
+    (pp_dpm_sclk: shader, pp_dpm_mclk: memory; the level marked '*'), or None
+    where it cannot be read."""
     import glob
-    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+    for path in sorted(glob.glob(f"/sys/class/drm/card*/device/{table}")):
         try:
             for line in open(path).read().splitlines():
                 if line.rstrip().endswith("*"):
@@ -139,20 +140,25 @@ def _sclk_now():
 
 
 class _ClockSampler:
-    """Samples the shader clock every ~2 ms in a thread while a timed region runs."""
+    """Samples the shader and memory clocks every ~2 ms in a thread while a
+    timed region runs."""
 
     def __init__(self):
         import threading
-        self.samples = []
+        self.samples = {"pp_dpm_sclk": [], "pp_dpm_mclk": []}
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
 
     def _run(self):
         while not self._stop.is_set():
-            v = _sclk_now()
-            if v is None:
+            got = False
+            for table, vals in self.samples.items():
+                v = _clock_now(table)
+                if v is not None:
+                    vals.append(v)
+                    got = True
+            if not got:
                 return
-            self.samples.append(v)
             self._stop.wait(0.002)
 
     def __enter__(self):
@@ -163,12 +169,12 @@ class _ClockSampler:
         self._stop.set()
         self._thread.join()
 
-    def summary(self):
-        if not self.samples:
+    def summary(self, table="pp_dpm_sclk"):
+        v = sorted(self.samples[table])
+        if not v:
             return None
-        v = sorted(self.samples)
         return {"median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1],
-                "samples": len(v), "source": "sysfs pp_dpm_sclk during the timed repeats"}
+                "samples": len(v), "source": f"sysfs {table} during the timed repeats"}
 
 
 def main():
@@ -316,7 +322,8 @@ def main():
         "timing": {"step": step_stats, "gemm": gemm_stats, "quant": quant_stats,
                    "rule": "each block times exactly --steps replayed steps with HIP events; "
                            "value and ms_per_step are the median block"},
-        "sclk": sclk.summary(),
+        "sclk": sclk.summary("pp_dpm_sclk"),
+        "mclk": sclk.summary("pp_dpm_mclk"),
         "quant_kernel_us": round(quant_ms * 1e3, 3),
         "wall_s_timed_region": round(wall, 4),
         "settle_s_before_warmup": args.settle_seconds,
