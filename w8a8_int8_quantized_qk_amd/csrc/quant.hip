@@ -136,11 +136,13 @@ __device__ __forceinline__ void store_codes(int8_t* dst, const float (&v)[P], co
     for (int i = 0; i < P / 4; ++i)
       w[i] = qm::pack4_low_bytes(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
   } else if constexpr (FMT == kI8Asym) {
-    int c[P];
+    const int zp_off = static_cast<int>(p.zp) - 0x4B400000;
+    uint32_t c[P];
 #pragma unroll
-    for (int e = 0; e < P; ++e) c[e] = qm::code_of_asym(v[e], s, r, p.zp);
+    for (int e = 0; e < P; ++e) c[e] = qm::code_word_asym(v[e], s, r, zp_off);
 #pragma unroll
-    for (int i = 0; i < P / 4; ++i) w[i] = pack4(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
+    for (int i = 0; i < P / 4; ++i)
+      w[i] = qm::pack4_low_bytes(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
   } else {
     float f[P];
 #pragma unroll

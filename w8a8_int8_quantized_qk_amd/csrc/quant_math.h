@@ -269,6 +269,18 @@ __device__ __forceinline__ int code_of_asym(float x, float s, float r, float zp)
   return static_cast<int>(q);
 }
 
+// The same code as code_of_asym as the low byte of the returned word: the
+// exact quotient rounded by adding 1.5 * 2^23 (|x / s| <= 255, so the sum's
+// bits are 0x4B400000 + rint(x / s)), then the zero point added and the clamp
+// to [-128, 127] taken on that integer.  zp_off = zp - 0x4B400000 (per row).
+__device__ __forceinline__ uint32_t code_word_asym(float x, float s, float r, int zp_off) {
+  const float y = x * r;
+  const float e = __builtin_fmaf(-y, s, x);
+  const float q = __builtin_fmaf(e, r, y);
+  const int c = static_cast<int>(__float_as_uint(q + 12582912.0f)) + zp_off;
+  return static_cast<uint32_t>(min(max(c, -128), 127));
+}
+
 // Asymmetric row parameters from hi = max(row max, 0) and nlo = -min(row
 // min, 0): s = max(hi + nlo, 1e-12f) / 255 (= hi - lo), r = RN(1 / s),
 // zp = clamp(rint(nlo / s) - 128, -128, 127), IEEE divisions (once per row).
