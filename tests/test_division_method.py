@@ -9,6 +9,8 @@ half-integer multiples of s where a wrong quotient would change the code.
 import os
 import subprocess
 
+import pytest
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -21,11 +23,13 @@ def test_markstein_quotient_gives_ieee_codes(tmp_path):
     assert "mismatches 0" in res.stdout
 
 
-def test_scale_division_by_127_is_exact(tmp_path):
-    """Every binary32 row maximum from the 1e-12 guard up gives the IEEE scale."""
+@pytest.mark.parametrize("divisor", [127, 255, 448])
+def test_scale_division_by_constant_is_exact(tmp_path, divisor):
+    """Every binary32 row statistic from the 1e-12 guard up gives the IEEE
+    scale: / 127 (INT8), / 255 (asymmetric INT8), / 448 (FP8)."""
     exe = tmp_path / "scale_division_check"
     subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
                            os.path.join(HERE, "scale_division_check.c"), "-o", str(exe), "-lm"])
-    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    res = subprocess.run([str(exe), str(divisor)], capture_output=True, text=True, timeout=600)
     assert res.returncode == 0, res.stdout + res.stderr
-    assert "mismatches 0" in res.stdout
+    assert "mismatches 0" in res.stdout and f"divisor {divisor}," in res.stdout

@@ -82,14 +82,15 @@ __device__ __forceinline__ void block_reduce(Stats& st) {
 // The row's scale s, r = RN(1 / s), and (asymmetric) the zero point.
 struct RowQ {
   float s, r, zp;
+  bool bounded;  // FP8: the scale bound replaced the row's own scale
 };
 template <int FMT>
 __device__ __forceinline__ RowQ row_params(const Stats& st, float scale_ub) {
-  RowQ p{0.0f, 0.0f, 0.0f};
+  RowQ p{0.0f, 0.0f, 0.0f, false};
   if constexpr (FMT == kI8)
     row_scale(st.a, p.s, p.r);
   else if constexpr (FMT == kF8)
-    qm::row_scale_fp8(st.a, scale_ub, p.s, p.r);
+    p.bounded = qm::row_scale_fp8(st.a, scale_ub, p.s, p.r);
   else
     qm::row_scale_asym(st.a, st.b, p.s, p.r, p.zp);
   return p;
@@ -145,8 +146,13 @@ __device__ __forceinline__ void store_codes(int8_t* dst, const float (&v)[P], co
       w[i] = qm::pack4_low_bytes(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
   } else {
     float f[P];
+    if (p.bounded) {  // uniform: one row per wave or workgroup
 #pragma unroll
-    for (int e = 0; e < P; ++e) f[e] = qm::fp8_ratio(v[e], s, r);
+      for (int e = 0; e < P; ++e) f[e] = qm::fp8_ratio(v[e], s, r);
+    } else {
+#pragma unroll
+      for (int e = 0; e < P; ++e) f[e] = qm::fp8_ratio_own(v[e], s, r);
+    }
 #pragma unroll
     for (int i = 0; i < P / 4; ++i) w[i] = qm::pack4_fp8(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
   }

@@ -281,11 +281,23 @@ __device__ __forceinline__ uint32_t code_word_asym(float x, float s, float r, in
   return static_cast<uint32_t>(min(max(c, -128), 127));
 }
 
+// a / d for a >= 1e-12f and a constant divisor d of 255 or 448, by the
+// same correction with the constant c = RN(1 / d): checked against IEEE
+// division for every binary32 a from 1e-12f to the largest finite value, as
+// for 127.  An infinite a (a row holding an infinity) gives a itself, as the
+// division does (the correction would give NaN).
+__device__ __forceinline__ float div_by_const(float a, float d, float c) {
+  const float y = a * c;
+  const float e = __builtin_fmaf(-y, d, a);
+  const float q = __builtin_fmaf(e, c, y);
+  return __builtin_isinf(a) ? a : q;
+}
+
 // Asymmetric row parameters from hi = max(row max, 0) and nlo = -min(row
 // min, 0): s = max(hi + nlo, 1e-12f) / 255 (= hi - lo), r = RN(1 / s),
 // zp = clamp(rint(nlo / s) - 128, -128, 127), IEEE divisions (once per row).
 __device__ __forceinline__ void row_scale_asym(float hi, float nlo, float& s, float& r, float& zp) {
-  s = __builtin_fmaxf(hi + nlo, 1e-12f) / 255.0f;
+  s = div_by_const(__builtin_fmaxf(hi + nlo, 1e-12f), 255.0f, 0x1.010102p-8f);  // RN(1 / 255)
   r = 1.0f / s;
   zp = __builtin_rintf(nlo / s) - 128.0f;
   zp = __builtin_fminf(__builtin_fmaxf(zp, -128.0f), 127.0f);
@@ -311,12 +323,15 @@ __device__ __forceinline__ void row_scale(float amax, float& s, float& r) {
 // value), optionally clamped from above by scale_ub; the code is the e4m3fn
 // value nearest x / scale (ties to even), saturating at +-448.
 
-// s = max(amax, 1e-12f) / 448 (IEEE division, once per row), then
-// min(s, scale_ub) when scale_ub > 0; r = RN(1 / s).
-__device__ __forceinline__ void row_scale_fp8(float amax, float scale_ub, float& s, float& r) {
-  s = __builtin_fmaxf(amax, 1e-12f) / 448.0f;
-  if (scale_ub > 0.0f && s > scale_ub) s = scale_ub;
+// s = max(amax, 1e-12f) / 448 (correctly rounded, by div_by_const), then
+// min(s, scale_ub) when scale_ub > 0; r = RN(1 / s).  Returns whether the
+// bound replaced the row's own scale (then quotients may exceed 448).
+__device__ __forceinline__ bool row_scale_fp8(float amax, float scale_ub, float& s, float& r) {
+  s = div_by_const(__builtin_fmaxf(amax, 1e-12f), 448.0f, 0x1.24924ap-9f);  // RN(1 / 448)
+  const bool bounded = scale_ub > 0.0f && s > scale_ub;
+  if (bounded) s = scale_ub;
   r = 1.0f / s;
+  return bounded;
 }
 
 // x / s, correctly rounded (the same correction as code_of), clamped to
@@ -331,6 +346,16 @@ __device__ __forceinline__ void row_scale_fp8(float amax, float scale_ub, float&
 __device__ __forceinline__ float fp8_ratio(float x, float s, float r) {
   float y = x * r;
   y = __builtin_amdgcn_fmed3f(y, -1024.0f, 1024.0f);
+  const float en = __builtin_fmaf(y, s, -x);
+  const float q = __builtin_fmaf(-en, r, y);
+  return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f);
+}
+
+// fp8_ratio for a row quantized with its own scale s = RN(max(amax, 1e-12)
+// / 448) (no scale bound): every |x| <= amax gives |x * r| < 449, so the
+// first clamp cannot bind and is left out (the same results).
+__device__ __forceinline__ float fp8_ratio_own(float x, float s, float r) {
+  const float y = x * r;
   const float en = __builtin_fmaf(y, s, -x);
   const float q = __builtin_fmaf(-en, r, y);
   return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f);
