@@ -294,8 +294,9 @@ __device__ __forceinline__ float div_by_const(float a, float d, float c) {
 }
 
 // Asymmetric row parameters from hi = max(row max, 0) and nlo = -min(row
-// min, 0): s = max(hi + nlo, 1e-12f) / 255 (= hi - lo), r = RN(1 / s),
-// zp = clamp(rint(nlo / s) - 128, -128, 127), IEEE divisions (once per row).
+// min, 0): s = max(hi + nlo, 1e-12f) / 255 (= hi - lo; correctly rounded,
+// by div_by_const), r = RN(1 / s), zp = clamp(rint(nlo / s) - 128, -128,
+// 127) (IEEE divisions; once per row).
 __device__ __forceinline__ void row_scale_asym(float hi, float nlo, float& s, float& r, float& zp) {
   s = div_by_const(__builtin_fmaxf(hi + nlo, 1e-12f), 255.0f, 0x1.010102p-8f);  // RN(1 / 255)
   r = 1.0f / s;
