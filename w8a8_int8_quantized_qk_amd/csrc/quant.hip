@@ -326,9 +326,36 @@ hipError_t dispatch(int m, int k, const void* src, int8_t* q, float* scale, floa
                 scale_ub, zp, k);
 }
 
-// silu(gate) * up in binary32 without quantization, one element per thread
-// and iteration: the activation the fused kernels quantize, with the same
-// arithmetic (silu_times), for callers that want it unquantized.
+// silu(gate) * up in binary32 without quantization: the activation the fused
+// kernels quantize, with the same arithmetic (silu_times), for callers that
+// want it unquantized.  Rows of whole 16-byte units (16-byte aligned input,
+// d a multiple of the unit) take one unit of gate and one of up per thread
+// and iteration; others one element.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void silu_mul_units_kernel(const void* __restrict__ src,
+                                                               float* __restrict__ out,
+                                                               long long units, int units_per_row) {
+  using E = Elem<DT>;
+  constexpr int P = E::kPerUnit;
+  const char* in = static_cast<const char*>(src);
+  const long long stride = static_cast<long long>(gridDim.x) * kBlock;
+  for (long long u = static_cast<long long>(blockIdx.x) * kBlock + threadIdx.x; u < units;
+       u += stride) {
+    const long long row = u / units_per_row;
+    const long long at = u + row * units_per_row;  // the gate unit; up is units_per_row later
+    float g[P], up[P];
+    E::unpack(load_unit(in + at * 16), g);
+    E::unpack(load_unit(in + (at + units_per_row) * 16), up);
+    float* o = out + u * P;
+#pragma unroll
+    for (int e = 0; e < P; e += 4)
+      *reinterpret_cast<float4*>(o + e) =
+          make_float4(silu_times<DT != QK_F32>(g[e], up[e]), silu_times<DT != QK_F32>(g[e + 1], up[e + 1]),
+                      silu_times<DT != QK_F32>(g[e + 2], up[e + 2]),
+                      silu_times<DT != QK_F32>(g[e + 3], up[e + 3]));
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(kBlock) void silu_mul_kernel(const void* __restrict__ src,
                                                          float* __restrict__ out,
@@ -342,6 +369,20 @@ __global__ __launch_bounds__(kBlock) void silu_mul_kernel(const void* __restrict
     const size_t first = static_cast<size_t>(row) * 2 * d;
     out[i] = silu_times<DT != QK_F32>(E::load(src, first + j), E::load(src, first + d + j));
   }
+}
+
+template <int DT>
+hipError_t launch_silu_mul_dt(int m, int d, const void* h, float* out, hipStream_t stream) {
+  constexpr int P = Elem<DT>::kPerUnit;
+  const long long total = static_cast<long long>(m) * d;
+  const bool units = d % P == 0 && reinterpret_cast<uintptr_t>(h) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(out) % 16 == 0;
+  const long long items = units ? total / P : total;
+  const long long want = (items + kBlock - 1) / kBlock;
+  const dim3 grid(static_cast<unsigned>(want < 8192 ? want : 8192));
+  if (units)
+    return launch(silu_mul_units_kernel<DT>, grid, dim3(kBlock), 0, stream, h, out, items, d / P);
+  return launch(silu_mul_kernel<DT>, grid, dim3(kBlock), 0, stream, h, out, total, d);
 }
 
 template <bool SILU, int FMT>
@@ -369,14 +410,11 @@ hipError_t launch_silu_quant_rows(int m, int d, const void* h, int dtype, int8_t
 
 hipError_t launch_silu_mul(int m, int d, const void* h, int dtype, float* out,
                            hipStream_t stream) {
-  const long long total = static_cast<long long>(m) * d;
-  if (total == 0) return hipSuccess;
-  const long long want = (total + kBlock - 1) / kBlock;
-  const dim3 grid(static_cast<unsigned>(want < 8192 ? want : 8192));
+  if (static_cast<long long>(m) * d == 0) return hipSuccess;
   switch (dtype) {
-    case QK_F32: return launch(silu_mul_kernel<QK_F32>, grid, dim3(kBlock), 0, stream, h, out, total, d);
-    case QK_BF16: return launch(silu_mul_kernel<QK_BF16>, grid, dim3(kBlock), 0, stream, h, out, total, d);
-    case QK_F16: return launch(silu_mul_kernel<QK_F16>, grid, dim3(kBlock), 0, stream, h, out, total, d);
+    case QK_F32: return launch_silu_mul_dt<QK_F32>(m, d, h, out, stream);
+    case QK_BF16: return launch_silu_mul_dt<QK_BF16>(m, d, h, out, stream);
+    case QK_F16: return launch_silu_mul_dt<QK_F16>(m, d, h, out, stream);
     default: return hipErrorInvalidValue;
   }
 }
