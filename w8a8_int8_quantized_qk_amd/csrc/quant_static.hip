@@ -50,8 +50,7 @@ template <int DT, bool SILU, bool FP8>
 __global__ __launch_bounds__(kBlock) void quant_static_units(const void* __restrict__ src,
                                                              int8_t* __restrict__ q,
                                                              const float* __restrict__ scale,
-                                                             long long units, int units_per_row,
-                                                             int k) {
+                                                             long long units, int units_per_row) {
   using E = Elem<DT>;
   constexpr int P = E::kPerUnit;
   constexpr int U = kUnitsPerThread;
@@ -142,7 +141,7 @@ hipError_t dispatch_static(int m, int k, const void* src, const float* scale, in
     const long long units = static_cast<long long>(m) * upr;
     return launch(quant_static_units<DT, SILU, FP8>,
                   dim3(grid_for((units + kUnitsPerThread - 1) / kUnitsPerThread)), dim3(kBlock), 0,
-                  stream, src, q, scale, units, upr, k);
+                  stream, src, q, scale, units, upr);
   }
   const long long count = static_cast<long long>(m) * k;
   return launch(quant_static_elems<DT, SILU, FP8>, dim3(grid_for(count)), dim3(kBlock), 0, stream,
